@@ -1,0 +1,209 @@
+"""fp64 CPU oracle of FreeSolo's long-range branch (FS / FS-L).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module; the GPU library never
+does, and the two share no code.  The arithmetic lives in ``fsl_oracle.c``
+(plain C, fp64, one (sequence, head) per call); this file only marshals numpy
+arrays into it and runs independent (sequence, head) pairs on a thread pool
+(ctypes releases the GIL while the C code runs).
+
+Page: "FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
+Extrapolation" (arXiv 2610.17191), Sec. 3.3 Eqs. 5-9 and App. D.2 Eq. 17.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfsl_oracle.so")
+_SRC = os.path.join(_HERE, "fsl_oracle.c")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (host only)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("d", ctypes.c_int32), ("s", ctypes.c_int32),
+                ("B", ctypes.c_int32), ("P", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("prune", ctypes.c_int32), ("sigma", ctypes.c_double),
+                ("lambda_", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+_lib = None
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.oracle_head.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp, vp, i64, i64, i64,
+                                vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_head.restype = ctypes.c_int
+    lib.oracle_cell_summaries.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp]
+    lib.oracle_cell_summaries.restype = None
+    lib.oracle_available_count.argtypes = [i64, ctypes.c_int32]
+    lib.oracle_available_count.restype = i64
+    lib.oracle_retained.argtypes = [ctypes.POINTER(_Cfg), i64, vp, vp, vp]
+    lib.oracle_retained.restype = i64
+    lib.oracle_cell_score.argtypes = [ctypes.POINTER(_Cfg), vp, vp, ctypes.c_double, i64, i64]
+    lib.oracle_cell_score.restype = ctypes.c_double
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = _bind(build())
+    return _lib
+
+
+class use_library:
+    """Context manager: route this module's calls to another build of the oracle
+    source (the mutation tests use it to run the pins against planted mistakes)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self._saved = _load()
+        _lib = _bind(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+@dataclass(frozen=True)
+class Params:
+    """Method parameters (defaults: the page's hyperparameters, App. A)."""
+    s: int = 32
+    B: int = 128
+    P: int = 64
+    W: int = 8
+    K: int = 4
+    prune: bool = True
+    sigma: float = 4.0
+    lam: float = 1.0
+    eps: float = 1e-8
+
+    def cfg(self, N: int, d: int) -> _Cfg:
+        return _Cfg(N, d, self.s, self.B, self.P, self.W, self.K, int(self.prune),
+                    self.sigma, self.lam, self.eps)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def cell_summaries(k: np.ndarray, prm: Params = Params()):
+    """Eq. 5 for one head: k [N, d] -> (kbar [N//s, d], a [N//s])."""
+    k = _f64(k)
+    N, d = k.shape
+    M = N // prm.s
+    kbar = np.zeros((M, d)); a = np.zeros(M)
+    cfg = prm.cfg(N, d)
+    _load().oracle_cell_summaries(ctypes.byref(cfg), _p(k), _p(kbar), _p(a))
+    return kbar, a
+
+
+def available_count(b_start: int, s: int = 32) -> int:
+    """Eq. 6: |C_i| for a block starting at b_start."""
+    return int(_load().oracle_available_count(b_start, s))
+
+
+def retained(a: np.ndarray, n_avail: int, prm: Params = Params()):
+    """Eq. 8 (or A = C for FS) for one block -> (ids ascending, gap_p)."""
+    a = _f64(a)
+    out = np.full(max(1, n_avail), -1, dtype=np.int32)
+    gap = np.zeros(1)
+    cfg = prm.cfg(len(a) * prm.s, 1)
+    n = _load().oracle_retained(ctypes.byref(cfg), n_avail, _p(a), _p(out), _p(gap))
+    return out[:n].copy(), float(gap[0])
+
+
+def cell_score(q_i, kbar_c, a_c: float, i: int, c: int, prm: Params = Params()) -> float:
+    """Eq. 7 for one (query, cell)."""
+    q_i = _f64(q_i); kbar_c = _f64(kbar_c)
+    cfg = prm.cfg(0, len(q_i))
+    return float(_load().oracle_cell_score(ctypes.byref(cfg), _p(q_i), _p(kbar_c), float(a_c), i, c))
+
+
+def cap_for(N: int, prm: Params) -> int:
+    M = N // prm.s
+    return max(1, min(M, prm.P + prm.W) if prm.prune else M)
+
+
+def head(q, k, v, g=None, prm: Params = Params(), i_lo: int = 0, i_hi: int | None = None,
+         want_scores: bool = False, want_out: bool = True, want_summaries: bool = True):
+    """The whole branch for one (sequence, head); q, k, v [N, d] (any float dtype).
+
+    Returns a dict with kbar, a, retained [NB, cap], n_ret [NB], gap_p [NB],
+    sel [n, K], gap_k [n], out [n, d] and optionally scores [n, cap], for the
+    queries i in [i_lo, i_hi).  Blocks not touched by the range hold -1/NaN.
+    """
+    k = _f64(k)
+    N, d = k.shape
+    q = _f64(q) if q is not None else np.zeros((N, d))
+    v = _f64(v) if v is not None else np.zeros((N, d))
+    g = _f64(g)
+    i_hi = N if i_hi is None else i_hi
+    n = i_hi - i_lo
+    M = N // prm.s
+    NB = (N + prm.B - 1) // prm.B
+    cap = cap_for(N, prm)
+    res = {
+        "kbar": np.zeros((M, d)) if want_summaries else None,
+        "a": np.zeros(M) if want_summaries else None,
+        "retained": np.full((max(NB, 1), cap), -1, dtype=np.int32),
+        "n_ret": np.full(max(NB, 1), -1, dtype=np.int32),
+        "gap_p": np.full(max(NB, 1), np.nan),
+        "sel": np.full((n, prm.K), -1, dtype=np.int32),
+        "gap_k": np.zeros(n),
+        "out": np.zeros((n, d)) if want_out else None,
+        "scores": np.full((n, cap), np.nan) if want_scores else None,
+    }
+    cfg = prm.cfg(N, d)
+    rc = _load().oracle_head(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), i_lo, i_hi, cap,
+                             _p(res["kbar"]), _p(res["a"]), _p(res["retained"]), _p(res["n_ret"]),
+                             _p(res["gap_p"]), _p(res["sel"]), _p(res["gap_k"]), _p(res["out"]),
+                             _p(res["scores"]))
+    if rc != 0:
+        raise ValueError("oracle_head rejected its arguments")
+    return res
+
+
+def batch(q, k, v, g=None, prm: Params = Params(), heads=None, i_lo: int = 0, i_hi: int | None = None,
+          threads: int | None = None, want_out: bool = True):
+    """Run `head` over (b, h) pairs of [batch, H, N, d] arrays on a thread pool.
+
+    `g` is [H, d] or None.  Returns {(b, h): result}.
+    """
+    Bt, H = k.shape[0], k.shape[1]
+    pairs = heads if heads is not None else [(b, h) for b in range(Bt) for h in range(H)]
+
+    def one(p):
+        b, h = p
+        return p, head(None if q is None else q[b, h], k[b, h], None if v is None else v[b, h],
+                       None if g is None else g[h], prm, i_lo, i_hi, want_out=want_out)
+
+    n = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        return dict(ex.map(one, pairs))

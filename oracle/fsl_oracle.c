@@ -1,0 +1,280 @@
+/*
+ * fp64 CPU oracle of FreeSolo's long-range branch (FS and FS-L).
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg; never by the GPU library, with which it shares
+ * no code.  Plain loops, plain definitions, no blocking or reordering: each
+ * step is written so that it can be checked against the page by eye.
+ *
+ * Page: "FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
+ * Extrapolation" (arXiv 2610.17191).
+ *   Sec. 3.3 "Cells"                 Eq. 5  summaries kbar_c, p_c, a_c
+ *   Sec. 3.3 "Query blocks"                 b_i = B floor(i / B)
+ *   Sec. 3.3 "Causal availability"   Eq. 6  C_i = {c : (c+1) s <= b_i}
+ *   Sec. 3.3 "Cell scoring"          Eq. 7  r_ic
+ *   Sec. 3.3 "Query-independent pruning" Eq. 8  A_i = Recent_W u TopP
+ *   Sec. 3.3 "Per-query selection"          T_i, S_i
+ *   Sec. 3.3 "Token readout"         Eq. 9  softmax readout + RMSNorm
+ *   Sec. 2 "Attention"               Eq. 1  softmax readout
+ *   App. D.2 "Why sparse readout..." Eq. 17 RMSNorm with epsilon
+ *
+ * Readings where the page leaves a choice open:
+ *   - ties in TopP and top-K are broken by the smaller cell id (the page asks
+ *     only for "a common deterministic tie rule", App. C "Bounded cache");
+ *   - Recent_W(C) is the min(W, |C|) cells of C with the largest ids;
+ *   - only complete cells (N / s of them, rounded down) have summaries;
+ *   - RMSNorm adds epsilon to the mean square inside the square root, with a
+ *     per-feature gain g (unit gain when g is NULL).
+ */
+#include "fsl_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- Eq. 5: cell summaries ------------------------------------------------ */
+
+void oracle_cell_summaries(const oracle_cfg *cfg, const double *k, double *kbar, double *a)
+{
+    const int64_t M = cfg->N / cfg->s; /* complete cells only */
+    const int32_t d = cfg->d, s = cfg->s;
+    for (int64_t c = 0; c < M; ++c) {
+        /* mean key over I_c = {cs, ..., (c+1)s - 1}, summed in index order */
+        for (int32_t f = 0; f < d; ++f) {
+            double sum = 0.0;
+            for (int64_t j = c * s; j < (c + 1) * s; ++j)
+                sum += k[j * d + f];
+            if (kbar)
+                kbar[c * d + f] = sum / s;
+        }
+        /* largest L2 norm of a key in the cell */
+        double best = 0.0;
+        for (int64_t j = c * s; j < (c + 1) * s; ++j) {
+            double sq = 0.0;
+            for (int32_t f = 0; f < d; ++f)
+                sq += k[j * d + f] * k[j * d + f];
+            const double nrm = sqrt(sq);
+            if (j == c * s || nrm > best)
+                best = nrm;
+        }
+        if (a)
+            a[c] = best;
+    }
+}
+
+/* ---- Eq. 6: causal availability ------------------------------------------- */
+
+int64_t oracle_available_count(int64_t b_start, int32_t s)
+{
+    int64_t n = 0;
+    while ((n + 1) * (int64_t)s <= b_start) /* cell n is available iff (n+1)s <= b_i */
+        ++n;
+    return n;
+}
+
+/* ---- ordering helpers: value descending, then id ascending ---------------- */
+
+typedef struct {
+    double val;
+    int64_t id;
+} keyed;
+
+static int by_value_desc_id_asc(const void *x, const void *y)
+{
+    const keyed *p = (const keyed *)x, *q = (const keyed *)y;
+    if (p->val > q->val) return -1;
+    if (p->val < q->val) return 1;
+    return (p->id < q->id) ? -1 : (p->id > q->id) ? 1 : 0;
+}
+
+static double relative_gap(double x, double y)
+{
+    const double m = fmax(fabs(x), fabs(y));
+    return m > 0.0 ? fabs(x - y) / m : 0.0;
+}
+
+/* ---- Eq. 8: retained set of one query block -------------------------------- */
+
+int64_t oracle_retained(const oracle_cfg *cfg, int64_t n_avail, const double *a,
+                        int32_t *A_out, double *gap_p)
+{
+    if (gap_p)
+        *gap_p = INFINITY;
+    if (!cfg->prune) { /* FS: A_i = C_i */
+        for (int64_t c = 0; c < n_avail; ++c)
+            A_out[c] = (int32_t)c;
+        return n_avail;
+    }
+    char *keep = (char *)calloc((size_t)(n_avail > 0 ? n_avail : 1), 1);
+    keyed *order = (keyed *)malloc(sizeof(keyed) * (size_t)(n_avail > 0 ? n_avail : 1));
+    /* TopP: the P cells of C with the largest a_c */
+    for (int64_t c = 0; c < n_avail; ++c) {
+        order[c].val = a[c];
+        order[c].id = c;
+    }
+    qsort(order, (size_t)n_avail, sizeof(keyed), by_value_desc_id_asc);
+    const int64_t n_top = n_avail < cfg->P ? n_avail : cfg->P;
+    for (int64_t r = 0; r < n_top; ++r)
+        keep[order[r].id] = 1;
+    if (gap_p && cfg->P > 0 && n_avail > cfg->P)
+        *gap_p = relative_gap(order[cfg->P - 1].val, order[cfg->P].val);
+    /* Recent_W: the W most recent cells of C */
+    const int64_t n_recent = n_avail < cfg->W ? n_avail : cfg->W;
+    for (int64_t c = n_avail - n_recent; c < n_avail; ++c)
+        keep[c] = 1;
+    /* the union, ascending */
+    int64_t n = 0;
+    for (int64_t c = 0; c < n_avail; ++c)
+        if (keep[c])
+            A_out[n++] = (int32_t)c;
+    free(order);
+    free(keep);
+    return n;
+}
+
+/* ---- Eq. 7: cell score ------------------------------------------------------ */
+
+double oracle_cell_score(const oracle_cfg *cfg, const double *q_i, const double *kbar_c,
+                         double a_c, int64_t i, int64_t c)
+{
+    double dot = 0.0;
+    for (int32_t f = 0; f < cfg->d; ++f)
+        dot += q_i[f] * kbar_c[f];
+    const double p_c = ((double)c + 0.5) * cfg->s;        /* cell centre, Eq. 5 */
+    const double g = erf(((double)i - p_c) / (2.0 * cfg->sigma)); /* g_h(i - p_c) */
+    return dot / sqrt((double)cfg->d) + cfg->lambda * a_c * g;
+}
+
+/* ---- Eq. 9 / Eq. 1 / Eq. 17: token readout and RMSNorm --------------------- */
+
+static void readout(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
+                    const double *g, const int64_t *T, int64_t nT, double *o)
+{
+    const int32_t d = cfg->d, s = cfg->s;
+    if (nT == 0) { /* S_i empty: both u and o are zero */
+        for (int32_t f = 0; f < d; ++f)
+            o[f] = 0.0;
+        return;
+    }
+    const int64_t nS = nT * s;
+    double *logit = (double *)malloc(sizeof(double) * (size_t)nS);
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)nS);
+    /* S_i: the tokens of the selected cells */
+    int64_t n = 0;
+    for (int64_t t = 0; t < nT; ++t)
+        for (int64_t j = T[t] * s; j < (T[t] + 1) * s; ++j)
+            tok[n++] = j;
+    /* l_ij = q_i . k_j / sqrt(d), NoPE */
+    double mx = -INFINITY;
+    for (int64_t x = 0; x < nS; ++x) {
+        double dot = 0.0;
+        for (int32_t f = 0; f < d; ++f)
+            dot += q_i[f] * k[tok[x] * d + f];
+        logit[x] = dot / sqrt((double)d);
+        if (logit[x] > mx)
+            mx = logit[x];
+    }
+    /* softmax over S_i jointly, then u = sum p_j v_j */
+    double z = 0.0;
+    for (int64_t x = 0; x < nS; ++x) {
+        logit[x] = exp(logit[x] - mx);
+        z += logit[x];
+    }
+    double ms = 0.0;
+    for (int32_t f = 0; f < d; ++f) {
+        double u = 0.0;
+        for (int64_t x = 0; x < nS; ++x)
+            u += logit[x] * v[tok[x] * d + f];
+        u /= z;
+        o[f] = u;
+        ms += u * u;
+    }
+    /* RMSNorm over the d features */
+    ms /= d;
+    const double inv = 1.0 / sqrt(ms + cfg->eps);
+    for (int32_t f = 0; f < d; ++f)
+        o[f] = (g ? g[f] : 1.0) * o[f] * inv;
+    free(tok);
+    free(logit);
+}
+
+/* ---- the whole branch for one (sequence, head) ------------------------------ */
+
+int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const double *v,
+                const double *g, int64_t i_lo, int64_t i_hi, int64_t cap,
+                double *kbar, double *a, int32_t *retained, int32_t *n_ret, double *gap_p,
+                int32_t *sel, double *gap_k, double *out, double *scores)
+{
+    if (cfg->N < 0 || cfg->d <= 0 || cfg->s <= 0 || cfg->B <= 0 || cfg->B % cfg->s != 0 ||
+        cfg->K < 1 || cfg->P < 0 || cfg->W < 0 || cfg->sigma <= 0.0 || cfg->lambda < 0.0 ||
+        cfg->eps < 0.0 || i_lo < 0 || i_hi > cfg->N || i_lo > i_hi)
+        return -1;
+    const int32_t d = cfg->d, K = cfg->K;
+    const int64_t M = cfg->N / cfg->s;
+    double *kb = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1) * d);
+    double *an = (double *)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    oracle_cell_summaries(cfg, k, kb, an);
+    if (kbar)
+        memcpy(kbar, kb, sizeof(double) * (size_t)M * d);
+    if (a)
+        memcpy(a, an, sizeof(double) * (size_t)M);
+
+    int32_t *A = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1));
+    keyed *rank = (keyed *)malloc(sizeof(keyed) * (size_t)(M > 0 ? M : 1));
+    int64_t *T = (int64_t *)malloc(sizeof(int64_t) * (size_t)K);
+    int status = 0;
+    int64_t cur_block = -1, nA = 0;
+
+    for (int64_t i = i_lo; i < i_hi; ++i) {
+        const int64_t blk = i / cfg->B;
+        if (blk != cur_block) { /* the prefix and retained set are fixed within a block */
+            cur_block = blk;
+            const int64_t b_i = (int64_t)cfg->B * blk;
+            const int64_t n_avail = oracle_available_count(b_i, cfg->s);
+            double gp;
+            nA = oracle_retained(cfg, n_avail, an, A, &gp);
+            if (nA > cap) {
+                status = -1;
+                break;
+            }
+            if (retained) {
+                for (int64_t x = 0; x < cap; ++x)
+                    retained[blk * cap + x] = x < nA ? A[x] : -1;
+            }
+            if (n_ret)
+                n_ret[blk] = (int32_t)nA;
+            if (gap_p)
+                gap_p[blk] = gp;
+        }
+        const double *q_i = q + i * d;
+        const int64_t row = i - i_lo;
+        /* Eq. 7 over the retained cells */
+        for (int64_t x = 0; x < nA; ++x) {
+            rank[x].id = A[x];
+            rank[x].val = oracle_cell_score(cfg, q_i, kb + (int64_t)A[x] * d, an[A[x]], i, A[x]);
+            if (scores)
+                scores[row * cap + x] = rank[x].val;
+        }
+        if (scores)
+            for (int64_t x = nA; x < cap; ++x)
+                scores[row * cap + x] = NAN;
+        /* T_i: the min(K, |A_i|) best cells */
+        qsort(rank, (size_t)nA, sizeof(keyed), by_value_desc_id_asc);
+        const int64_t nT = nA < K ? nA : K;
+        for (int64_t t = 0; t < nT; ++t)
+            T[t] = rank[t].id;
+        if (sel)
+            for (int32_t t = 0; t < K; ++t)
+                sel[row * K + t] = t < nT ? (int32_t)T[t] : -1;
+        if (gap_k)
+            gap_k[row] = nA > K ? relative_gap(rank[K - 1].val, rank[K].val) : INFINITY;
+        if (out)
+            readout(cfg, q_i, k, v, g, T, nT, out + row * d);
+    }
+    free(T);
+    free(rank);
+    free(A);
+    free(an);
+    free(kb);
+    return status;
+}

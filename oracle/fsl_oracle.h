@@ -1,0 +1,75 @@
+/*
+ * fp64 CPU oracle of FreeSolo's long-range branch (FS and FS-L).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this code: only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code with the GPU library.
+ *
+ * Source: "FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
+ * Extrapolation" (arXiv 2610.17191), Sec. 3.3 (Eqs. 5-9), Sec. 2 (Eq. 1) and
+ * App. D.2 (Eq. 17).  Every array is fp64 and row-major; one call handles one
+ * (sequence, head) pair.
+ */
+#ifndef FSL_ORACLE_H
+#define FSL_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int64_t N;      /* tokens in the sequence */
+    int32_t d;      /* head dimension */
+    int32_t s;      /* cell size (tokens per cell) */
+    int32_t B;      /* query-block size, a multiple of s */
+    int32_t P;      /* FS-L: cells kept by largest key norm */
+    int32_t W;      /* FS-L: most recent cells kept */
+    int32_t K;      /* cells selected per query */
+    int32_t prune;  /* 1 = FS-L (Eq. 8), 0 = FS (A_i = C_i) */
+    double sigma;   /* sigma_h of the erf prior */
+    double lambda;  /* lambda_h of the erf prior */
+    double eps;     /* RMSNorm epsilon */
+} oracle_cfg;
+
+/* Eq. 5: mean key kbar[c] and largest key norm a[c] of every complete cell. */
+void oracle_cell_summaries(const oracle_cfg *cfg, const double *k, double *kbar, double *a);
+
+/* Eq. 6: number of cells available to a query whose block starts at b_start. */
+int64_t oracle_available_count(int64_t b_start, int32_t s);
+
+/* Eq. 8 (FS-L) or A = C (FS) for one block; ids ascending; returns |A|.
+ * gap_p (may be NULL) receives the relative gap between the P-th and (P+1)-th
+ * key norms of the block's prefix, or +inf when there is no such boundary. */
+int64_t oracle_retained(const oracle_cfg *cfg, int64_t n_avail, const double *a,
+                        int32_t *A_out, double *gap_p);
+
+/* Eq. 7: routing score of cell c for query position i. */
+double oracle_cell_score(const oracle_cfg *cfg, const double *q_i, const double *kbar_c,
+                         double a_c, int64_t i, int64_t c);
+
+/*
+ * The whole branch for one (sequence, head), for queries i in [i_lo, i_hi).
+ *   q, k, v  [N, d];  g [d] or NULL (unit gains)
+ *   kbar [N/s, d], a [N/s]                      cell summaries (optional)
+ *   retained [NB, cap] (-1 padded), n_ret [NB], gap_p [NB]   per query block
+ *       touched by [i_lo, i_hi), indexed by absolute block (optional)
+ *   sel [(i_hi-i_lo), K] selected cells (-1 padded), in (score desc, id asc)
+ *   gap_k [(i_hi-i_lo)] relative gap of the K-th and (K+1)-th scores, or +inf
+ *   out [(i_hi-i_lo), d] long-range output after RMSNorm
+ *   scores [(i_hi-i_lo), cap] scores of the retained cells in ascending id
+ *       order (optional; NaN padded)
+ * cap is the row length of retained/scores: at least |A| of every block.
+ * Returns 0, or -1 when cap is too small or an argument is invalid.
+ */
+int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const double *v,
+                const double *g, int64_t i_lo, int64_t i_hi, int64_t cap,
+                double *kbar, double *a, int32_t *retained, int32_t *n_ret, double *gap_p,
+                int32_t *sel, double *gap_k, double *out, double *scores);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
