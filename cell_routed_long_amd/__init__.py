@@ -1,0 +1,206 @@
+"""Python binding of libfsl.so, the gfx950 implementation of FreeSolo's
+long-range sparse-attention branch (FS / FS-L).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/fsl.h.  PyTorch supplies device
+memory and the current stream.  If the library has not been built, every call
+raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from ._build import LIB_PATH, build  # noqa: F401
+
+FS_OK, FS_ERR_INVALID, FS_ERR_UNSUPPORTED, FS_ERR_WORKSPACE, FS_ERR_STATE, FS_ERR_HIP = range(6)
+FS_F32, FS_BF16 = 0, 1
+FS_MAX_HEADS = 128
+
+
+class FslError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class fs_params(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_int32), ("B", ctypes.c_int32), ("P", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("prune", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class fs_shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int64), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Params:
+    """Method parameters; defaults are the page's (App. A)."""
+    s: int = 32
+    B: int = 128
+    P: int = 64
+    W: int = 8
+    K: int = 4
+    prune: bool = True
+    eps: float = 1e-8
+
+    def c(self) -> fs_params:
+        return fs_params(self.s, self.B, self.P, self.W, self.K, int(self.prune), self.eps)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfsl.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with cell_routed_long_amd.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        P_shape, P_prm = ctypes.POINTER(fs_shape), ctypes.POINTER(fs_params)
+        L.fs_status_string.argtypes = [ctypes.c_int]
+        L.fs_status_string.restype = ctypes.c_char_p
+        L.fs_cell_summaries.argtypes = [P_shape, P_prm, vp, vp, vp, vp]
+        L.fs_prune_workspace_bytes.argtypes = [P_shape, P_prm]
+        L.fs_prune_workspace_bytes.restype = sz
+        L.fs_prune_retained.argtypes = [P_shape, P_prm, vp, vp, vp, vp, sz, vp]
+        L.fs_prefill_workspace_bytes.argtypes = [P_shape, P_prm]
+        L.fs_prefill_workspace_bytes.restype = sz
+        L.fs_longrange_prefill.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+        L.fs_decode_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, P_prm]
+        L.fs_decode_state_bytes.restype = sz
+        L.fs_longrange_decode.argtypes = [P_prm, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                          vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        for name in ("fs_cell_summaries", "fs_prune_retained", "fs_longrange_prefill", "fs_longrange_decode"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fs_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != FS_OK:
+        raise FslError(status, where)
+
+
+# ---------------------------------------------------------------- marshalling --
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FS_F32
+    if t.dtype == torch.bfloat16:
+        return FS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def shape_of(x) -> fs_shape:
+    """fs_shape of a [batch, H, N, d] tensor."""
+    b, H, N, d = x.shape
+    return fs_shape(b, H, N, d, _dtype_code(x))
+
+
+def _floats(vals, H):
+    if isinstance(vals, (int, float)):
+        vals = [float(vals)] * H
+    arr = (ctypes.c_float * H)(*[float(x) for x in vals])
+    return arr
+
+
+# ------------------------------------------------------------- C ABI calls --
+
+def fs_cell_summaries(k, kbar, a, params: Params = Params(), stream=None):
+    """Eq. 5: kbar [b,H,N/s,d] fp32 and a [b,H,N/s] fp32 from k [b,H,N,d]."""
+    sh, prm = shape_of(k), params.c()
+    _check(lib().fs_cell_summaries(ctypes.byref(sh), ctypes.byref(prm), _ptr(k), _ptr(kbar), _ptr(a),
+                                   _stream(stream)), "fs_cell_summaries")
+
+
+def fs_prune_workspace_bytes(sh: fs_shape, params: Params = Params()) -> int:
+    prm = params.c()
+    return int(lib().fs_prune_workspace_bytes(ctypes.byref(sh), ctypes.byref(prm)))
+
+
+def fs_prune_retained(sh: fs_shape, a, retained, n_retained, workspace, params: Params = Params(), stream=None):
+    """Eqs. 6 and 8: retained [b,H,NB,P+W] int32 and n_retained [b,H,NB] int32 from a."""
+    prm = params.c()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().fs_prune_retained(ctypes.byref(sh), ctypes.byref(prm), _ptr(a), _ptr(retained), _ptr(n_retained),
+                                   _ptr(workspace), nbytes, _stream(stream)), "fs_prune_retained")
+
+
+def fs_prefill_workspace_bytes(sh: fs_shape, params: Params = Params()) -> int:
+    prm = params.c()
+    return int(lib().fs_prefill_workspace_bytes(ctypes.byref(sh), ctypes.byref(prm)))
+
+
+def fs_longrange_prefill(q, k, v, sigma_h, lambda_h, gain, out, sel, state, workspace,
+                         params: Params = Params(), stream=None):
+    """The branch over a whole prompt (Eqs. 5-9, 17); see include/fsl.h."""
+    sh, prm = shape_of(k), params.c()
+    H = sh.H
+    sig, lam = _floats(sigma_h, H), _floats(lambda_h, H)
+    st_bytes = 0 if state is None else state.numel() * state.element_size()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().fs_longrange_prefill(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), sig, lam,
+                                      _ptr(gain), _ptr(out), _ptr(sel), _ptr(state), st_bytes, _ptr(workspace),
+                                      ws_bytes, _stream(stream)), "fs_longrange_prefill")
+
+
+def fs_decode_state_bytes(batch: int, H: int, d: int, dtype_code: int, params: Params = Params()) -> int:
+    prm = params.c()
+    return int(lib().fs_decode_state_bytes(batch, H, d, dtype_code, ctypes.byref(prm)))
+
+
+def fs_longrange_decode(state, q, k_new, v_new, sigma_h, lambda_h, gain, out, sel=None,
+                        params: Params = Params(), stream=None):
+    """One decode step for every sequence; q, k_new, v_new, out are [b, H, d]."""
+    prm = params.c()
+    b, H, d = q.shape
+    sig, lam = _floats(sigma_h, H), _floats(lambda_h, H)
+    _check(lib().fs_longrange_decode(ctypes.byref(prm), b, H, d, _dtype_code(q), _ptr(state),
+                                     state.numel() * state.element_size(), _ptr(q), _ptr(k_new), _ptr(v_new), sig,
+                                     lam, _ptr(gain), _ptr(out), _ptr(sel), _stream(stream)), "fs_longrange_decode")
+
+
+# ------------------------------------------------------- allocation helpers --
+
+def prefill(q, k, v, params: Params = Params(), sigma=4.0, lam=1.0, gain=None, want_out=True, want_sel=True,
+            workspace=None, stream=None):
+    """Allocate outputs and workspace with torch and run fs_longrange_prefill.
+
+    Returns (out or None, sel or None, workspace)."""
+    import torch
+    sh = shape_of(k)
+    ws_bytes = fs_prefill_workspace_bytes(sh, params)
+    if ws_bytes == 0:
+        raise FslError(FS_ERR_UNSUPPORTED, "fs_prefill_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
+    out = torch.empty_like(q) if want_out else None
+    sel = torch.empty(k.shape[0], k.shape[1], k.shape[2], params.K, dtype=torch.int32, device=k.device) \
+        if want_sel else None
+    fs_longrange_prefill(q, k, v, sigma, lam, gain, out, sel, None, workspace, params, stream)
+    return out, sel, workspace

@@ -1,0 +1,245 @@
+// C ABI of the long-range branch: argument validation, workspace layout and the
+// launch sequence.  Validation happens entirely on the host and before any HIP
+// call, so a rejected call touches neither the device nor the runtime.
+#include "fsl.h"
+
+#include <cmath>
+#include <cstring>
+
+#include "fsl_internal.h"
+
+#define FSL_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace fsl {
+namespace {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 22; // LDS union bitmap of the readout: N/32 bits <= 16 KB
+constexpr int kMaxRetained = 1024;               // P + W
+constexpr int kMaxK = 8;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+fs_status check_params(const fs_params *p)
+{
+    if (!p)
+        return FS_ERR_INVALID;
+    if (p->s < 1 || p->B < 1 || p->B % p->s != 0 || p->K < 1 || p->P < 0 || p->W < 0 ||
+        (p->prune != 0 && p->prune != 1) || !(p->eps >= 0.0f) || !std::isfinite(p->eps))
+        return FS_ERR_INVALID;
+    if (p->s != 32 || p->B != 128 || p->K > kMaxK || (int64_t)p->P + p->W > kMaxRetained)
+        return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
+fs_status check_shape(const fs_shape *sh)
+{
+    if (!sh)
+        return FS_ERR_INVALID;
+    if (sh->batch < 1 || sh->H < 1 || sh->N < 1 || sh->d < 1 || (sh->dtype != FS_F32 && sh->dtype != FS_BF16))
+        return FS_ERR_INVALID;
+    if ((sh->d != 64 && sh->d != 128) || sh->H > FS_MAX_HEADS || sh->N > kMaxTokens ||
+        (int64_t)sh->batch * sh->H > 65535)
+        return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
+fs_status check_all(const fs_shape *sh, const fs_params *p)
+{
+    fs_status st = check_shape(sh);
+    if (st != FS_OK)
+        return st;
+    return check_params(p);
+}
+
+Geometry geometry(const fs_shape *sh, const fs_params *p)
+{
+    Geometry g;
+    g.bh = sh->batch * sh->H;
+    g.H = sh->H;
+    g.N = sh->N;
+    g.d = sh->d;
+    g.bf16 = sh->dtype == FS_BF16;
+    g.M = sh->N / p->s;
+    g.NB = (int32_t)((sh->N + p->B - 1) / p->B);
+    g.s = p->s;
+    g.B = p->B;
+    g.P = p->P;
+    g.W = p->W;
+    g.K = p->K;
+    g.prune = p->prune;
+    g.cap = p->P + p->W > 0 ? p->P + p->W : 1;
+    g.eps = p->eps;
+    return g;
+}
+
+// Workspace of fs_longrange_prefill, carved in this order (256-byte aligned).
+struct PrefillLayout {
+    size_t kbar, a, death, retained, n_ret, sel, total;
+};
+
+PrefillLayout prefill_layout(const Geometry &g)
+{
+    PrefillLayout L;
+    size_t off = 0;
+    L.kbar = off;
+    off += align_up((size_t)g.bh * g.M * g.d * sizeof(float));
+    L.a = off;
+    off += align_up((size_t)g.bh * g.M * sizeof(float));
+    L.death = off;
+    off += g.prune ? align_up((size_t)g.bh * g.M * sizeof(int32_t)) : 0;
+    L.retained = off;
+    off += g.prune ? align_up((size_t)g.bh * g.NB * g.cap * sizeof(int32_t)) : 0;
+    L.n_ret = off;
+    off += g.prune ? align_up((size_t)g.bh * g.NB * sizeof(int32_t)) : 0;
+    L.sel = off;
+    off += align_up((size_t)g.bh * g.N * g.K * sizeof(int32_t));
+    L.total = off > 0 ? off : kAlign;
+    return L;
+}
+
+fs_status check_heads(int H, const float *sigma_h, const float *lambda_h, HeadConsts *hc)
+{
+    if (!sigma_h || !lambda_h)
+        return FS_ERR_INVALID;
+    std::memset(hc, 0, sizeof(*hc));
+    for (int h = 0; h < H; ++h) {
+        if (!(sigma_h[h] > 0.0f) || !std::isfinite(sigma_h[h]) || !(lambda_h[h] >= 0.0f) ||
+            !std::isfinite(lambda_h[h]))
+            return FS_ERR_INVALID;
+        hc->inv_two_sigma[h] = 1.0f / (2.0f * sigma_h[h]);
+        hc->lambda[h] = lambda_h[h];
+    }
+    return FS_OK;
+}
+
+inline fs_status hip_status(hipError_t e) { return e == hipSuccess ? FS_OK : FS_ERR_HIP; }
+
+} // namespace
+} // namespace fsl
+
+using namespace fsl;
+
+FSL_EXPORT const char *fs_status_string(fs_status status)
+{
+    switch (status) {
+    case FS_OK: return "ok";
+    case FS_ERR_INVALID: return "invalid argument";
+    case FS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FS_ERR_WORKSPACE: return "workspace too small";
+    case FS_ERR_STATE: return "decode state does not match the parameters";
+    case FS_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+FSL_EXPORT fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *prm, const void *k, float *kbar,
+                                       float *a, void *stream)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    const Geometry g = geometry(shape, prm);
+    if (!k || ((!kbar || !a) && g.M > 0)) // no complete cell: nothing to write
+        return FS_ERR_INVALID;
+    return hip_status(launch_cell_summaries(g, k, kbar, a, static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT size_t fs_prune_workspace_bytes(const fs_shape *shape, const fs_params *prm)
+{
+    if (check_all(shape, prm) != FS_OK)
+        return 0;
+    const Geometry g = geometry(shape, prm);
+    return align_up((size_t)g.bh * (g.M > 0 ? g.M : 1) * sizeof(int32_t));
+}
+
+FSL_EXPORT fs_status fs_prune_retained(const fs_shape *shape, const fs_params *prm, const float *a,
+                                       int32_t *retained, int32_t *n_retained, void *workspace,
+                                       size_t workspace_bytes, void *stream)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    if (!prm->prune || !a || !retained || !n_retained || !workspace)
+        return FS_ERR_INVALID;
+    if (workspace_bytes < fs_prune_workspace_bytes(shape, prm))
+        return FS_ERR_WORKSPACE;
+    const Geometry g = geometry(shape, prm);
+    return hip_status(launch_prune(g, a, static_cast<int32_t *>(workspace), retained, n_retained,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm)
+{
+    if (check_all(shape, prm) != FS_OK)
+        return 0;
+    return prefill_layout(geometry(shape, prm)).total;
+}
+
+FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
+                                          const void *v, const float *sigma_h, const float *lambda_h,
+                                          const float *gain, void *out, int32_t *sel, void *state,
+                                          size_t state_bytes, void *workspace, size_t workspace_bytes,
+                                          void *stream)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(shape->H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    if (!k || !workspace || (!out && !sel && !state))
+        return FS_ERR_INVALID;
+    if ((out || sel) && !q)
+        return FS_ERR_INVALID;
+    if (out && !v)
+        return FS_ERR_INVALID;
+    if (state) {
+        (void)state_bytes;
+        return FS_ERR_UNSUPPORTED; // decode state not built by this version
+    }
+    const Geometry g = geometry(shape, prm);
+    const PrefillLayout L = prefill_layout(g);
+    if (workspace_bytes < L.total)
+        return FS_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    float *kbar = reinterpret_cast<float *>(ws + L.kbar);
+    float *a = reinterpret_cast<float *>(ws + L.a);
+    int32_t *death = reinterpret_cast<int32_t *>(ws + L.death);
+    int32_t *retained = reinterpret_cast<int32_t *>(ws + L.retained);
+    int32_t *n_ret = reinterpret_cast<int32_t *>(ws + L.n_ret);
+    int32_t *sel_buf = sel ? sel : reinterpret_cast<int32_t *>(ws + L.sel);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    hipError_t e = launch_cell_summaries(g, k, kbar, a, s);
+    if (e == hipSuccess && g.prune)
+        e = launch_prune(g, a, death, retained, n_ret, s);
+    if (e == hipSuccess)
+        e = launch_score_topk(g, hc, q, kbar, a, g.prune ? retained : nullptr, g.prune ? n_ret : nullptr, sel_buf,
+                              s);
+    if (e == hipSuccess && out)
+        e = launch_readout(g, q, k, v, sel_buf, gain, out, s);
+    return hip_status(e);
+}
+
+FSL_EXPORT size_t fs_decode_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, const fs_params *prm)
+{
+    (void)batch;
+    (void)H;
+    (void)d;
+    (void)dtype;
+    (void)prm;
+    return 0; // streaming decode state not provided by this version
+}
+
+FSL_EXPORT fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
+                                         void *state, size_t state_bytes, const void *q, const void *k_new,
+                                         const void *v_new, const float *sigma_h, const float *lambda_h,
+                                         const float *gain, void *out, int32_t *sel, void *stream)
+{
+    (void)prm; (void)batch; (void)H; (void)d; (void)dtype; (void)state; (void)state_bytes; (void)q;
+    (void)k_new; (void)v_new; (void)sigma_h; (void)lambda_h; (void)gain; (void)out; (void)sel; (void)stream;
+    return FS_ERR_UNSUPPORTED;
+}

@@ -1,0 +1,103 @@
+// Device helpers shared by the gfx950 kernels of the long-range branch.
+//
+// MFMA conventions used throughout (CDNA3/CDNA4 32x32 tiles, wave64):
+//   v_mfma_f32_32x32x16_bf16 : A[32 x 16], B[16 x 32] -> C[32 x 32] fp32
+//   v_mfma_f32_32x32x2_f32   : A[32 x 2],  B[2 x 32]  -> C[32 x 32] fp32
+// Lane l supplies row (l % 32) of A and column (l % 32) of B; its k values are
+// the contiguous group (l / 32) of the instruction's k range.  Accumulator
+// register r of lane l holds C[8 (r / 4) + 4 (l / 32) + (r % 4)][l % 32].
+// The kernels put the query index on the C column, so each lane owns one
+// query and 16 of the 32 rows (cells or tokens); its partner lane l ^ 32 owns
+// the other 16 rows of the same query.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsl {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row (within the 32-row tile) held by accumulator register r of a lane in half `half`.
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// (value desc, id asc): does (v1, i1) rank before (v2, i2)?
+__device__ __forceinline__ bool ranks_before(float v1, int i1, float v2, int i2)
+{
+    return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Insert (v, id) into the sorted list tv/ti of the first K (<= KMAX) entries.
+// Every index is a compile-time constant after unrolling, so the list stays in
+// registers for any run-time K.
+template <int KMAX>
+__device__ __forceinline__ void topk_insert(float (&tv)[KMAX], int (&ti)[KMAX], int K, float v, int id)
+{
+    float thr_v = tv[0];
+    int thr_i = ti[0];
+#pragma unroll
+    for (int j = 1; j < KMAX; ++j)
+        if (j == K - 1) {
+            thr_v = tv[j];
+            thr_i = ti[j];
+        }
+    if (!ranks_before(v, id, thr_v, thr_i))
+        return;
+#pragma unroll
+    for (int j = KMAX - 1; j >= 0; --j) {
+        if (j >= K)
+            continue;
+        const bool above_prev = (j > 0) && ranks_before(v, id, tv[j > 0 ? j - 1 : 0], ti[j > 0 ? j - 1 : 0]);
+        if (above_prev) {
+            tv[j] = tv[j - 1];
+            ti[j] = ti[j - 1];
+        } else if (ranks_before(v, id, tv[j], ti[j])) {
+            tv[j] = v;
+            ti[j] = id;
+        }
+    }
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, kWave); }
+__device__ __forceinline__ int shfl_xor_i(int x, int m) { return __shfl_xor(x, m, kWave); }
+__device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xor(x, m, kWave); }
+
+// Per-head routing constants, passed by value with every launch.
+struct HeadConsts {
+    float inv_two_sigma[128]; // 1 / (2 sigma_h)
+    float lambda[128];        // lambda_h
+};
+
+} // namespace fsl

@@ -1,0 +1,38 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fsl_device.h"
+
+namespace fsl {
+
+// Geometry every kernel shares (derived and validated by the ABI layer).
+struct Geometry {
+    int32_t bh;        // batch * H
+    int32_t H;
+    int64_t N;         // positions per sequence
+    int32_t d;         // head dimension (64 or 128)
+    int32_t bf16;      // 1 = bf16 tensors, 0 = fp32
+    int64_t M;         // complete cells per sequence, N / s
+    int32_t NB;        // query blocks per sequence, ceil(N / B)
+    int32_t s, B, P, W, K, prune;
+    int32_t cap;       // row length of the retained lists, P + W
+    float eps;
+};
+
+hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, hipStream_t st);
+
+// death[c]: first query block whose TopP no longer holds cell c (INT32_MAX: never leaves).
+hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32_t *retained,
+                        int32_t *n_ret, hipStream_t st);
+
+hipError_t launch_score_topk(const Geometry &g, const HeadConsts &hc, const void *q, const float *kbar,
+                             const float *a, const int32_t *retained, const int32_t *n_ret, int32_t *sel,
+                             hipStream_t st);
+
+hipError_t launch_readout(const Geometry &g, const void *q, const void *k, const void *v,
+                          const int32_t *sel, const float *gain, void *out, hipStream_t st);
+
+} // namespace fsl

@@ -1,0 +1,130 @@
+// FS-L retained sets (FreeSolo, Sec. 3.3 "Query-independent pruning", Eq. 8, over
+// the causal prefix of Eq. 6): A_beta = Recent_W(C_beta) u TopP(a_c), C_beta the
+// cells ending at or before the block start beta*B.
+//
+// Instead of replaying the incremental top-P merge block after block (one long
+// serial chain per head), the prefill computes for every cell the block at
+// which it leaves TopP.  A cell c belongs to TopP(C_beta) iff fewer than P cells
+// of C_beta outrank it by (a desc, id asc).  The outranking cells of C_beta only
+// grow with beta, so if e is the P-th outranking cell in id order, c is in
+// TopP(C_beta) exactly for the blocks that contain c and satisfy
+// beta < death(c) = e / (B/s) + 1 (the first block in which e is available).
+// This gives the same sets as the page's Eq. 15 merge (App. C "Bounded cache")
+// with every block independent:
+//   prune_death_kernel: one thread per cell scans the head's norms (staged
+//       through LDS) in id order and stops at its P-th outranking cell;
+//   prune_emit_kernel:  one wave per (head, block) compacts, in id order, the
+//       non-recent cells still alive plus the W most recent cells.
+#include "fsl_internal.h"
+
+#include <climits>
+
+namespace fsl {
+namespace {
+
+constexpr int kDeathThreads = 256;
+constexpr int kTile = 2048; // norms staged per LDS pass
+
+__global__ __launch_bounds__(kDeathThreads) void prune_death_kernel(const float *__restrict__ a,
+                                                                    int32_t *__restrict__ death, int64_t M,
+                                                                    int P, int cells_per_block)
+{
+    __shared__ float tile[kTile];
+    const int64_t head = blockIdx.y;
+    const int64_t c = (int64_t)blockIdx.x * kDeathThreads + threadIdx.x;
+    const float *ah = a + head * M;
+    const float ac = c < M ? ah[c] : 0.0f;
+    int count = 0;
+    int64_t e = -1;
+    bool done = (c >= M) || (P == 0);
+    for (int64_t base = 0; base < M; base += kTile) {
+        const int len = (int)((M - base) < kTile ? (M - base) : kTile);
+        __syncthreads();
+        for (int x = threadIdx.x; x < len; x += kDeathThreads)
+            tile[x] = ah[base + x];
+        __syncthreads();
+        if (!done) {
+            for (int x = 0; x < len; ++x) {
+                const float ax = tile[x];
+                const int64_t cx = base + x;
+                if (ax > ac || (ax == ac && cx < c)) {
+                    if (++count == P) {
+                        e = cx;
+                        done = true;
+                        break;
+                    }
+                }
+            }
+        }
+        if (__syncthreads_count(done ? 1 : 0) == (int)blockDim.x)
+            break;
+    }
+    if (c < M) {
+        int32_t dth;
+        if (P == 0)
+            dth = 0; // never in TopP
+        else if (e < 0)
+            dth = INT32_MAX;
+        else
+            dth = (int32_t)(e / cells_per_block + 1);
+        death[head * M + c] = dth;
+    }
+}
+
+__global__ __launch_bounds__(kWave) void prune_emit_kernel(const int32_t *__restrict__ death,
+                                                           int32_t *__restrict__ retained,
+                                                           int32_t *__restrict__ n_ret, int64_t M, int NB,
+                                                           int cap, int W, int cells_per_block)
+{
+    const int beta = blockIdx.x;
+    const int64_t head = blockIdx.y;
+    const int lane = threadIdx.x;
+    int64_t n_avail = (int64_t)beta * cells_per_block; // |C_beta|, Eq. 6
+    if (n_avail > M)
+        n_avail = M;
+    const int64_t recent0 = n_avail > W ? n_avail - W : 0;
+    const int32_t *dh = death + head * M;
+    int32_t *dst = retained + (head * NB + beta) * (int64_t)cap;
+    int count = 0;
+    // non-recent cells still in TopP, ascending
+    for (int64_t base = 0; base < recent0; base += kWave) {
+        const int64_t c = base + lane;
+        const bool keep = c < recent0 && dh[c] > beta;
+        const uint64_t mask = __ballot(keep);
+        const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+        if (keep && pos < cap)
+            dst[pos] = (int32_t)c;
+        count += __popcll(mask);
+    }
+    if (count > cap - (int)(n_avail - recent0)) // only reachable with non-finite norms
+        count = cap - (int)(n_avail - recent0);
+    // the W most recent cells
+    for (int64_t c = recent0 + lane; c < n_avail; c += kWave)
+        dst[count + (c - recent0)] = (int32_t)c;
+    count += (int)(n_avail - recent0);
+    for (int x = count + lane; x < cap; x += kWave)
+        dst[x] = -1;
+    if (lane == 0)
+        n_ret[head * NB + beta] = count;
+}
+
+} // namespace
+
+hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32_t *retained, int32_t *n_ret,
+                        hipStream_t st)
+{
+    const int cpb = g.B / g.s;
+    if (g.M > 0) {
+        dim3 grid((unsigned)((g.M + kDeathThreads - 1) / kDeathThreads), (unsigned)g.bh);
+        hipLaunchKernelGGL(prune_death_kernel, grid, dim3(kDeathThreads), 0, st, a, death, g.M, g.P, cpb);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    dim3 grid2((unsigned)g.NB, (unsigned)g.bh);
+    hipLaunchKernelGGL(prune_emit_kernel, grid2, dim3(kWave), 0, st, death, retained, n_ret, g.M, g.NB, g.cap, g.W,
+                       cpb);
+    return hipGetLastError();
+}
+
+} // namespace fsl

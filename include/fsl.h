@@ -1,0 +1,161 @@
+/*
+ * fsl.h — C ABI of the MI355X (gfx950) implementation of FreeSolo's long-range
+ * sparse-attention branch (FS and FS-L).
+ *
+ * Page: "FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
+ * Extrapolation" (arXiv 2610.17191), Sec. 3.3 ("Cells", "Query blocks",
+ * "Causal availability", "Cell scoring", "Query-independent pruning",
+ * "Per-query selection", "Token readout", "Inference"), App. C ("Bounded
+ * cache", Eq. 15) and App. D.2 (Eq. 17).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are contiguous, row-major, on the device: q, k, v, out are
+ *     [batch, H, N, d] of the shape's dtype (fp32 or bf16).  Cell summaries
+ *     are fp32; ids are int32.  Cell c holds positions c*s .. c*s+s-1; only the
+ *     floor(N/s) complete cells have summaries; the query block of position i
+ *     is i / B.
+ *   - The caller owns every buffer (inputs, outputs, workspace, decode state).
+ *     The library never allocates or frees device memory and keeps no mutable
+ *     global state.  Outputs are fully overwritten (zero rows, -1 padding).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is enqueued
+ *     on it; no call synchronises.  Decode steps are safe to capture in a HIP
+ *     graph (all position-dependent branching happens on the device).
+ *   - Errors: arguments are checked on the host before anything is enqueued;
+ *     a rejected call enqueues nothing and writes nothing.  A launch failure
+ *     reported by the runtime gives FS_ERR_HIP.  Faults inside kernels surface
+ *     at the caller's next synchronisation, as for any HIP work.
+ *   - Ties in key norm (top-P) and in routing score (top-K) are broken in
+ *     favour of the smaller cell id.
+ */
+#ifndef FSL_H
+#define FSL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FS_OK = 0,
+    FS_ERR_INVALID = 1,      /* NULL required pointer, non-positive size, inconsistent params */
+    FS_ERR_UNSUPPORTED = 2,  /* valid per the method, outside what the kernels implement */
+    FS_ERR_WORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes() */
+    FS_ERR_STATE = 4,        /* decode state of the wrong size, or not built by this library */
+    FS_ERR_HIP = 5           /* the HIP runtime rejected a launch */
+} fs_status;
+
+typedef enum { FS_F32 = 0, FS_BF16 = 1 } fs_dtype;
+
+/* Method parameters (Sec. 3.3; the page's values in App. A are s=32, B=128,
+ * P=64, W=8, K=4).  prune = 1 selects FS-L (Eq. 8), prune = 0 selects FS
+ * (A_i = C_i).  eps is the RMSNorm epsilon of Eq. 17 (the page uses 1e-8).
+ * Kernels support s == 32, B == 128, 1 <= K <= 8, P + W <= 1024; anything
+ * else valid gives FS_ERR_UNSUPPORTED. */
+typedef struct {
+    int32_t s, B, P, W, K, prune;
+    float eps;
+} fs_params;
+
+/* batch sequences x H heads x N positions x d features (d in {64, 128}). */
+typedef struct {
+    int32_t batch, H;
+    int64_t N;
+    int32_t d;
+    fs_dtype dtype;
+} fs_shape;
+
+/* Largest head count accepted (sigma_h and lambda_h travel as launch arguments). */
+#define FS_MAX_HEADS 128
+
+const char *fs_status_string(fs_status status);
+
+/*
+ * Cell summaries, Eq. 5: for every complete cell c < M = floor(N/s) of every
+ * (sequence, head), kbar[c] = (1/s) sum_{j in I_c} k_j and a[c] = max_{j in I_c}
+ * ||k_j||_2 (p_c = (c + 1/2) s is implicit).
+ *   k     [batch, H, N, d]  shape dtype            (input)
+ *   kbar  [batch, H, M, d]  fp32                   (output)
+ *   a     [batch, H, M]     fp32                   (output)
+ * Sums and norms accumulate in fp64 and are rounded once to fp32.
+ */
+fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *prm, const void *k,
+                            float *kbar, float *a, void *stream);
+
+/* Bytes of workspace fs_prune_retained needs (0 on invalid arguments). */
+size_t fs_prune_workspace_bytes(const fs_shape *shape, const fs_params *prm);
+
+/*
+ * FS-L retained sets, Eqs. 6 and 8: for every query block beta of every
+ * (sequence, head), A_beta = Recent_W(C_beta) u TopP_{c in C_beta}(a_c) with
+ * C_beta = {c : (c+1) s <= beta B}.  Requires prm->prune == 1.
+ *   a           [batch, H, M]            fp32, from fs_cell_summaries (input)
+ *   retained    [batch, H, NB, P + W]    int32 cell ids ascending, -1 padded (output)
+ *   n_retained  [batch, H, NB]           int32 |A_beta| (output)
+ *   workspace   fs_prune_workspace_bytes() bytes of device memory (scratch)
+ * NB = ceil(N / B).  Block 0 is always empty.
+ */
+fs_status fs_prune_retained(const fs_shape *shape, const fs_params *prm, const float *a,
+                            int32_t *retained, int32_t *n_retained,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fs_longrange_prefill needs (0 on invalid arguments). */
+size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm);
+
+/*
+ * The long-range branch over a whole prompt (Sec. 3.3 "Inference": prompt
+ * prefill uses the same causal operator), for every query position i:
+ * summaries (Eq. 5), availability (Eq. 6), retention (Eq. 8, FS-L) or the full
+ * prefix (FS), scores r_ic (Eq. 7) with g_h(x) = erf(x / (2 sigma_h)), the
+ * min(K, |A_i|) best cells T_i, and o_i = RMSNorm(softmax(q_i k_S / sqrt(d)) V_S)
+ * over the tokens S_i of T_i (Eq. 9, Eq. 17); o_i = 0 when S_i is empty.
+ *   q, k, v     [batch, H, N, d]   shape dtype (input)
+ *   sigma_h     host [H] fp32, > 0          lambda_h  host [H] fp32, >= 0
+ *   gain        device [H, d] fp32 RMSNorm gains, or NULL for unit gains
+ *   out         [batch, H, N, d]   shape dtype, or NULL (output)
+ *   sel         [batch, H, N, K]   int32 T_i by (score desc, id asc), -1 padded,
+ *               or NULL (output)
+ *   state       decode state to fill for continuing at position N (see
+ *               fs_decode_state_bytes), or NULL
+ *   workspace   fs_prefill_workspace_bytes() bytes of device memory (scratch)
+ * At least one of out, sel, state must be non-NULL.  q and v may be NULL when
+ * out and sel are both NULL (state-only prefill of a long prefix).
+ */
+fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params *prm,
+                               const void *q, const void *k, const void *v,
+                               const float *sigma_h, const float *lambda_h, const float *gain,
+                               void *out, int32_t *sel, void *state, size_t state_bytes,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of one decode state for `batch` sequences x H heads (0 on invalid
+ * arguments).  The state is one flat caller-owned device buffer; copying its
+ * bytes checkpoints the stream exactly. */
+size_t fs_decode_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
+                             const fs_params *prm);
+
+/*
+ * One decode step of the long-range branch for every sequence (Sec. 3.3
+ * "Inference"; App. C "Bounded cache", Eq. 15): with i the stored position,
+ *   (1) if i is a block start, the block's newly eligible cells are merged
+ *       into TopP (Eq. 15), Recent_W advances and cells in neither are evicted;
+ *   (2) k_new, v_new are appended; when position i completes a cell its
+ *       summary (Eq. 5) is formed;
+ *   (3) q is scored against the retained cells (Eq. 7), its top-K selected and
+ *       read out (Eq. 9) with RMSNorm; the position advances to i + 1.
+ *   state        from fs_longrange_prefill (or a copy of one)   (in/out)
+ *   q, k_new, v_new  [batch, H, d]  dtype                       (input)
+ *   sigma_h, lambda_h, gain        as for fs_longrange_prefill
+ *   out          [batch, H, d] dtype (output);  sel [batch, H, K] int32 or NULL
+ */
+fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, int32_t d,
+                              fs_dtype dtype, void *state, size_t state_bytes,
+                              const void *q, const void *k_new, const void *v_new,
+                              const float *sigma_h, const float *lambda_h, const float *gain,
+                              void *out, int32_t *sel, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSL_H */

@@ -1,0 +1,121 @@
+"""CPU checks of the C ABI: the library loads, exports what include/fsl.h declares,
+and rejects bad arguments on the host before anything reaches the GPU (these calls
+never touch the HIP runtime, so they run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import cell_routed_long_amd as fsl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsl.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fsl.LIB_PATH):
+        fsl.build()
+    return fsl.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fs_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_match_header(L):
+    declared = declared_functions()
+    assert {"fs_cell_summaries", "fs_prune_retained", "fs_longrange_prefill", "fs_longrange_decode"} <= set(declared)
+    out = subprocess.run(["nm", "-D", "--defined-only", fsl.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = sorted(set(m for m in re.findall(r" T (\w+)", out.stdout)))
+    assert exported == declared
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings(L):
+    for code in range(6):
+        assert fsl.status_string(code)
+
+
+def shape(b=1, H=2, N=1024, d=64, dtype=fsl.FS_F32):
+    return fsl.fs_shape(b, H, N, d, dtype)
+
+
+def prm(**kw):
+    return fsl.Params(**kw).c()
+
+
+def call_summaries(L, sh, p, k=1, kbar=1, a=1):
+    vp = ctypes.c_void_p
+    return L.fs_cell_summaries(ctypes.byref(sh), ctypes.byref(p), vp(k) if k else None,
+                               vp(kbar) if kbar else None, vp(a) if a else None, None)
+
+
+@pytest.mark.parametrize("sh,p,expect", [
+    (shape(b=0), prm(), fsl.FS_ERR_INVALID),
+    (shape(H=0), prm(), fsl.FS_ERR_INVALID),
+    (shape(N=0), prm(), fsl.FS_ERR_INVALID),
+    (shape(dtype=7), prm(), fsl.FS_ERR_INVALID),
+    (shape(), prm(K=0), fsl.FS_ERR_INVALID),
+    (shape(), prm(P=-1), fsl.FS_ERR_INVALID),
+    (shape(), prm(B=100), fsl.FS_ERR_INVALID),      # B % s != 0
+    (shape(), prm(eps=-1.0), fsl.FS_ERR_INVALID),
+    (shape(d=96), prm(), fsl.FS_ERR_UNSUPPORTED),
+    (shape(H=129), prm(), fsl.FS_ERR_UNSUPPORTED),
+    (shape(), prm(K=9), fsl.FS_ERR_UNSUPPORTED),
+    (shape(), prm(s=16, B=128), fsl.FS_ERR_UNSUPPORTED),
+    (shape(), prm(B=256), fsl.FS_ERR_UNSUPPORTED),
+    (shape(), prm(P=1000, W=100), fsl.FS_ERR_UNSUPPORTED),
+    (shape(N=(1 << 22) + 1), prm(), fsl.FS_ERR_UNSUPPORTED),
+])
+def test_summaries_rejects_bad_arguments(L, sh, p, expect):
+    assert call_summaries(L, sh, p) == expect
+
+
+def test_null_pointers_rejected(L):
+    assert call_summaries(L, shape(), prm(), k=0) == fsl.FS_ERR_INVALID
+    assert call_summaries(L, shape(), prm(), a=0) == fsl.FS_ERR_INVALID
+    assert L.fs_cell_summaries(None, ctypes.byref(prm()), None, None, None, None) == fsl.FS_ERR_INVALID
+
+
+def test_workspace_sizes(L):
+    sh, p = shape(b=4, H=16, N=16384, d=128, dtype=fsl.FS_BF16), prm()
+    ws = fsl.fs_prefill_workspace_bytes(sh, fsl.Params())
+    M, NB = 16384 // 32, 16384 // 128
+    # summaries + norms + per-cell exit blocks + retained lists + counts + selections
+    at_least = 64 * (M * 128 * 4 + M * 4 + M * 4 + NB * 72 * 4 + NB * 4 + 16384 * 4 * 4)
+    assert at_least <= ws <= at_least + 6 * 256
+    assert fsl.fs_prefill_workspace_bytes(shape(d=96), fsl.Params()) == 0
+    assert fsl.fs_prune_workspace_bytes(sh, fsl.Params()) >= 64 * M * 4
+
+
+def test_prefill_validation_before_launch(L):
+    sh, p = shape(), prm()
+    vp = ctypes.c_void_p
+    H = sh.H
+    ones = (ctypes.c_float * H)(*([4.0] * H))
+    lam = (ctypes.c_float * H)(*([1.0] * H))
+    bad_sigma = (ctypes.c_float * H)(*([0.0] * H))
+    ws = fsl.fs_prefill_workspace_bytes(sh, fsl.Params())
+    args = lambda sig, ws_bytes, out=1, q=1: (ctypes.byref(sh), ctypes.byref(p), vp(q) if q else None, vp(1), vp(1),
+                                              sig, lam, None, vp(out) if out else None, None, None, 0, vp(1), ws_bytes,
+                                              None)
+    assert L.fs_longrange_prefill(*args(bad_sigma, ws)) == fsl.FS_ERR_INVALID
+    assert L.fs_longrange_prefill(*args(ones, ws - 1)) == fsl.FS_ERR_WORKSPACE
+    assert L.fs_longrange_prefill(*args(ones, ws, out=0)) == fsl.FS_ERR_INVALID  # nothing requested
+    assert L.fs_longrange_prefill(*args(ones, ws, q=0)) == fsl.FS_ERR_INVALID    # output needs q
+
+
+def test_prune_requires_fsl_mode(L):
+    sh = shape()
+    p = prm(prune=False)
+    vp = ctypes.c_void_p
+    assert L.fs_prune_retained(ctypes.byref(sh), ctypes.byref(p), vp(1), vp(1), vp(1), vp(1), 1 << 20,
+                               None) == fsl.FS_ERR_INVALID
+    p = prm()
+    assert L.fs_prune_retained(ctypes.byref(sh), ctypes.byref(p), vp(1), vp(1), vp(1), vp(1), 0,
+                               None) == fsl.FS_ERR_WORKSPACE

@@ -1,0 +1,182 @@
+"""GPU parity: the gfx950 path through the C ABI against the fp64 oracle, on the
+same seeded inputs.  Selections must match exactly (near-ties excepted, counted),
+outputs within the stated tolerances; see tests/parity_utils.py for the rules."""
+import numpy as np
+import pytest
+
+import cell_routed_long_amd as fsl
+import synth
+from tests import parity_utils as pu
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def gpu_available():
+    return torch.cuda.is_available()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not gpu_available():
+        pytest.skip("needs a GPU")
+    fsl.lib()
+
+
+def run_prefill(w, host, p, sigma=4.0, lam=1.0, gain=None):
+    dq, dk, dv = (pu.to_device(host[x], w.dtype) for x in "qkv")
+    g = None if gain is None else torch.from_numpy(gain).cuda()
+    print(f"[gpu] prefill {w} {p}", flush=True)
+    out, sel, _ = fsl.prefill(dq, dk, dv, p, sigma=sigma, lam=lam, gain=g)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), sel.cpu().numpy()
+
+
+def check(w, p, heads=None, sigma=4.0, lam=1.0, gain=None, max_skip_frac=0.01):
+    host = pu.inputs(w)
+    out, sel = run_prefill(w, host, p, sigma, lam, gain)
+    heads = heads or [(b, h) for b in range(w.batch) for h in range(w.H)]
+    refs = pu.run_oracle(w, host, p, heads, sigma, lam, gain)
+    checked = skipped = 0
+    for (b, h), ref in refs.items():
+        c, s = pu.compare_head(sel[b, h], out[b, h], ref, p, w.dtype, what=f"{w.name or w} b{b} h{h}")
+        checked += c
+        skipped += s
+    print(f"checked {checked} queries, {skipped} near-ties excluded")
+    assert skipped <= max_skip_frac * (checked + skipped)
+    return out, sel
+
+
+# ---------------------------------------------------------------- summaries ----
+
+@pytest.mark.parametrize("w", [
+    synth.WORKLOADS["small_fs_equiv"],
+    synth.WORKLOADS["prefill_4k"],
+    synth.Workload(batch=2, H=3, N=1000, d=128, dtype="bf16", seed=21, needle_frac=0.01),
+    synth.Workload(batch=1, H=2, N=777, d=64, dtype="bf16", seed=22),
+    synth.Workload(batch=1, H=1, N=31, d=128, dtype="f32", seed=23),
+], ids=lambda w: f"b{w.batch}H{w.H}N{w.N}d{w.d}{w.dtype}")
+def test_cell_summaries(w):
+    host = pu.inputs(w)
+    k = pu.to_device(host["k"], w.dtype)
+    M = w.N // 32
+    kbar = torch.empty(w.batch, w.H, M, w.d, dtype=torch.float32, device="cuda")
+    a = torch.empty(w.batch, w.H, M, dtype=torch.float32, device="cuda")
+    print(f"[gpu] summaries {w}", flush=True)
+    fsl.fs_cell_summaries(k, kbar, a)
+    torch.cuda.synchronize()
+    kbar, a = kbar.cpu().numpy(), a.cpu().numpy()
+    import oracle
+    for b in range(w.batch):
+        for h in range(w.H):
+            rk, ra = oracle.cell_summaries(synth.to_f64(host["k"][b, h], w.dtype))
+            # fp64 sums rounded once: the mean is the correctly rounded fp32 of the exact mean
+            np.testing.assert_array_equal(kbar[b, h], rk.astype(np.float32))
+            np.testing.assert_allclose(a[b, h], ra, rtol=1.2e-7, atol=0)
+
+
+# ------------------------------------------------------------------ pruning ----
+
+@pytest.mark.parametrize("w,P,W", [
+    (synth.WORKLOADS["prefill_4k"], 64, 8),
+    (synth.Workload(batch=2, H=2, N=5000, d=64, dtype="f32", seed=31, needle_frac=0.01), 5, 3),
+    (synth.Workload(batch=1, H=2, N=3000, d=128, dtype="bf16", seed=32), 0, 4),
+    (synth.Workload(batch=1, H=2, N=3000, d=128, dtype="bf16", seed=33), 7, 0),
+], ids=["cfg4k", "P5W3", "P0W4", "P7W0"])
+def test_prune_retained(w, P, W):
+    p = fsl.Params(P=P, W=W)
+    host = pu.inputs(w)
+    k = pu.to_device(host["k"], w.dtype)
+    M, NB, cap = w.N // 32, (w.N + 127) // 128, max(1, P + W)
+    kbar = torch.empty(w.batch, w.H, M, w.d, dtype=torch.float32, device="cuda")
+    a = torch.empty(w.batch, w.H, M, dtype=torch.float32, device="cuda")
+    fsl.fs_cell_summaries(k, kbar, a, p)
+    sh = fsl.shape_of(k)
+    ws = torch.empty(fsl.fs_prune_workspace_bytes(sh, p), dtype=torch.uint8, device="cuda")
+    ret = torch.empty(w.batch, w.H, NB, cap, dtype=torch.int32, device="cuda")
+    nret = torch.empty(w.batch, w.H, NB, dtype=torch.int32, device="cuda")
+    print(f"[gpu] prune {w} P={P} W={W}", flush=True)
+    fsl.fs_prune_retained(sh, a, ret, nret, ws, p)
+    torch.cuda.synchronize()
+    ret, nret = ret.cpu().numpy(), nret.cpu().numpy()
+    import oracle
+    op = pu.oracle_params(p)
+    for b in range(w.batch):
+        for h in range(w.H):
+            ref = oracle.head(None, synth.to_f64(host["k"][b, h], w.dtype), None, prm=op, want_out=False)
+            for beta in range(NB):
+                if ref["gap_p"][beta] < pu.NEAR_TIE:
+                    continue
+                n = ref["n_ret"][beta]
+                assert nret[b, h, beta] == n, (b, h, beta)
+                np.testing.assert_array_equal(ret[b, h, beta, :n], ref["retained"][beta, :n])
+                assert np.all(ret[b, h, beta, n:] == -1)
+
+
+# ------------------------------------------------------------ whole prefill ----
+
+def test_config_small_fs_equivalent():
+    """1024 tokens, 32 cells: pruning never binds, so FS-L equals FS (both checked)."""
+    w = synth.WORKLOADS["small_fs_equiv"]
+    _, sel_l = check(w, fsl.Params(prune=True))
+    _, sel_f = check(w, fsl.Params(prune=False))
+    np.testing.assert_array_equal(sel_l, sel_f)
+
+
+def test_config_4k_pruning_active():
+    check(synth.WORKLOADS["prefill_4k"], fsl.Params())
+
+
+@pytest.mark.parametrize("w,p,extra", [
+    (synth.Workload(batch=2, H=2, N=2000, d=128, dtype="bf16", seed=41, needle_frac=0.005), fsl.Params(), {}),
+    (synth.Workload(batch=1, H=3, N=1500, d=64, dtype="bf16", seed=42, needle_frac=0.01), fsl.Params(P=6, W=2), {}),
+    (synth.Workload(batch=1, H=2, N=2100, d=128, dtype="f32", seed=43, needle_frac=0.01), fsl.Params(P=10, W=4), {}),
+    (synth.Workload(batch=1, H=2, N=1300, d=64, dtype="f32", seed=44), fsl.Params(prune=False), {}),
+    (synth.Workload(batch=1, H=2, N=1300, d=128, dtype="bf16", seed=45, needle_frac=0.01), fsl.Params(prune=False), {}),
+    (synth.Workload(batch=1, H=2, N=1024, d=64, dtype="f32", seed=46), fsl.Params(K=1), {}),
+    (synth.Workload(batch=1, H=2, N=1024, d=128, dtype="bf16", seed=47), fsl.Params(K=3, P=5, W=1), {}),
+    (synth.Workload(batch=1, H=2, N=1024, d=64, dtype="bf16", seed=48), fsl.Params(K=8, P=9, W=3), {}),
+    (synth.Workload(batch=1, H=2, N=1024, d=64, dtype="f32", seed=49), fsl.Params(P=0, W=0), {}),
+    (synth.Workload(batch=1, H=2, N=1024, d=64, dtype="f32", seed=50), fsl.Params(P=0, W=2, K=4), {}),
+    (synth.Workload(batch=1, H=2, N=1200, d=64, dtype="f32", seed=51, needle_frac=0.01), fsl.Params(), {"lam": 0.0}),
+    (synth.Workload(batch=1, H=2, N=1200, d=128, dtype="bf16", seed=52, needle_frac=0.01), fsl.Params(),
+     {"lam": 0.0}),
+    (synth.Workload(batch=1, H=2, N=1200, d=64, dtype="f32", seed=53), fsl.Params(), {"sigma": 40.0, "lam": 0.3}),
+    (synth.Workload(batch=1, H=4, N=1100, d=128, dtype="bf16", seed=54, needle_frac=0.01), fsl.Params(P=12, W=3),
+     {"gain": True}),
+], ids=["bf16d128", "bf16d64P6", "f32d128P10", "FSf32", "FSbf16", "K1", "K3", "K8", "P0W0", "P0W2", "lam0f32",
+        "lam0bf16", "sigma40", "gain"])
+def test_prefill_variants(w, p, extra):
+    gain = synth.gains(99, w.H, w.d) if extra.get("gain") else None
+    check(w, p, sigma=extra.get("sigma", 4.0), lam=extra.get("lam", 1.0), gain=gain)
+
+
+@pytest.mark.parametrize("N", [1, 31, 32, 127, 128, 129, 160, 1023])
+def test_ragged_and_tiny_lengths(N):
+    w = synth.Workload(batch=1, H=2, N=N, d=64, dtype="bf16", seed=60 + N, needle_frac=0.02)
+    out, sel = check(w, fsl.Params(P=3, W=1))
+    assert np.all(sel[:, :, :min(N, 128)] == -1) and np.all(out[:, :, :min(N, 128)] == 0)
+
+
+def test_deterministic():
+    w = synth.Workload(batch=1, H=2, N=2048, d=128, dtype="bf16", seed=70, needle_frac=0.005)
+    host = pu.inputs(w)
+    o1, s1 = run_prefill(w, host, fsl.Params())
+    o2, s2 = run_prefill(w, host, fsl.Params())
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(o1, o2)
+
+
+# --------------------------------------------------- full-size, sampled heads ----
+
+def test_headline_16k_sampled_heads():
+    """b4 H16 d128 N16384 bf16: the whole batch on the GPU, every query of sampled
+    (sequence, head) pairs against the oracle."""
+    w = synth.WORKLOADS["prefill_16k"]
+    check(w, fsl.Params(), heads=[(0, 0), (1, 5), (2, 10), (3, 15)])
+
+
+def test_fs_32k_sampled():
+    """FS (no pruning), b1 H16 d128 N32768 bf16: up to 1020 cells scored per query."""
+    w = synth.WORKLOADS["fs_32k"]
+    check(w, fsl.Params(prune=False), heads=[(0, 3), (0, 12)])
