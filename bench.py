@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the FS-L long-range prefill on one MI355X.
+
+Workload (seeded, synthetic): FS-L long-range prefill, batch 4, H=16, d=128,
+N=16384 tokens, bf16 q/k/v ~ N(0,1) per feature, every key scaled by a
+lognormal(0, 0.5) factor and 0.5% of the keys by 4; s=32, B=128, P=64, W=8,
+K=4, sigma_h=4, lambda_h=1.
+
+A step is one pass of the whole path over the batch: cell summaries, retained
+sets, scores + top-K, gather-readout + RMSNorm, issued through the C ABI as
+four calls on one stream with HIP events between them, so that every kernel's
+average launch time is measured inside the timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "long-range FS-L query-tokens/s at 16k prefill; % HBM/MFMA roofline"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "readout_16k_counters.json")
+WORKLOADS = {
+    "prefill_16k": dict(prune=True),
+    "fs_32k": dict(prune=False),
+    "prefill_4k": dict(prune=True),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest(name: str) -> str:
+    path = os.path.join(ROOT, "cell_routed_long_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def distinct_cells_per_block(sel, B: int):
+    """U_beta: distinct selected cells of every (sequence, head, block)."""
+    import numpy as np
+    b, H, N, K = sel.shape
+    NB = (N + B - 1) // B
+    pad = NB * B - N
+    s = np.concatenate([sel, np.full((b, H, pad, K), -1, sel.dtype)], axis=2) if pad else sel
+    s = np.sort(s.reshape(b, H, NB, B * K), axis=-1)
+    valid = s >= 0
+    new = np.ones_like(valid)
+    new[..., 1:] = s[..., 1:] != s[..., :-1]
+    return (valid & new).sum(axis=-1)  # [b, H, NB]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_16k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run one 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the long-range branch shards by (sequence, head) with no "
+              f"exchange, so --gpus {args.gpus} is not run (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import cell_routed_long_amd as fsl
+    import synth
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 1
+    if not os.path.exists(fsl.LIB_PATH):
+        fsl.build()
+    fsl.lib()
+
+    w = synth.WORKLOADS[args.workload]
+    prm = fsl.Params(prune=WORKLOADS[args.workload]["prune"])
+    sigma, lam = 4.0, 1.0
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    host = {x: synth.tensor(w, x) for x in "qkv"}
+    log(f"[bench] generated inputs in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = (to_dev(host[x]) for x in "qkv")
+    b, H, N, d = q.shape
+    M, NB, cap = N // prm.s, (N + prm.B - 1) // prm.B, prm.P + prm.W
+    kbar = torch.empty(b, H, M, d, dtype=torch.float32, device=dev)
+    a = torch.empty(b, H, M, dtype=torch.float32, device=dev)
+    sh = fsl.shape_of(k)
+    ws = torch.empty(max(1, fsl.fs_prune_workspace_bytes(sh, prm)), dtype=torch.uint8, device=dev)
+    retained = torch.empty(b, H, NB, cap, dtype=torch.int32, device=dev)
+    n_ret = torch.empty(b, H, NB, dtype=torch.int32, device=dev)
+    sel = torch.empty(b, H, N, prm.K, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    names = ["cell_summaries", "prune", "score_topk", "readout"]
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        fsl.fs_cell_summaries(k, kbar, a, prm)
+        if evs is not None:
+            evs[1].record(stream)
+        if prm.prune:
+            fsl.fs_prune_retained(sh, a, retained, n_ret, ws, prm)
+        if evs is not None:
+            evs[2].record(stream)
+        fsl.fs_score_select(q, kbar, a, retained if prm.prune else None, n_ret if prm.prune else None,
+                            sigma, lam, sel, prm)
+        if evs is not None:
+            evs[3].record(stream)
+        fsl.fs_readout(q, k, v, sel, None, out, prm)
+        if evs is not None:
+            evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = sum(evs[s_][0].elapsed_time(evs[s_][4]) for s_ in range(args.steps))
+    per_kernel_ms = {names[i]: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
+                     for i in range(4)}
+    ms_per_step = wall * 1e3 / args.steps
+    value = b * N * args.steps / wall
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step wall, {gpu_ms / args.steps:.3f} ms/step events; "
+        f"kernels {per_kernel_ms}")
+
+    # the single-call path (fs_longrange_prefill), same work, for reference
+    single = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pws = torch.empty(fsl.fs_prefill_workspace_bytes(sh, prm), dtype=torch.uint8, device=dev)
+    out2 = torch.empty_like(q)
+    fsl.fs_longrange_prefill(q, k, v, sigma, lam, None, out2, None, None, pws, prm)
+    single[0].record(stream)
+    reps = max(1, min(args.steps, 10))
+    for _ in range(reps):
+        fsl.fs_longrange_prefill(q, k, v, sigma, lam, None, out2, None, None, pws, prm)
+    single[1].record(stream)
+    torch.cuda.synchronize()
+    single_ms = single[0].elapsed_time(single[1]) / reps
+    same = bool(torch.equal(out, out2))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- algorithmic work per launch ----
+    sel_h = sel.cpu().numpy()
+    U = distinct_cells_per_block(sel_h, prm.B)
+    n_ret_h = n_ret.cpu().numpy() if prm.prune else None
+    esz = 2 if w.dtype == "bf16" else 4
+    qkv_bytes = b * H * N * d * esz
+    cell_kv_bytes = prm.s * d * esz * 2
+    if prm.prune:
+        A_sizes = n_ret_h.astype(np.int64)
+    else:
+        A_sizes = np.broadcast_to(np.minimum(np.arange(NB) * (prm.B // prm.s), M), (b, H, NB)).astype(np.int64)
+    score_flop = float(2 * prm.B * d * A_sizes.sum())
+    read_flop = float(4 * prm.s * d * np.count_nonzero(sel_h >= 0))
+    alg = {
+        "cell_summaries": dict(bytes=qkv_bytes + b * H * M * (d + 1) * 4),
+        "prune": dict(bytes=b * H * M * 4 * 2 + b * H * NB * (cap + 1) * 4 if prm.prune else 0),
+        "score_topk": dict(bytes=qkv_bytes + b * H * M * (d + 1) * 4 + b * H * N * prm.K * 4, flop=score_flop),
+        "readout": dict(bytes=2 * qkv_bytes + b * H * N * prm.K * 4 + int(U.sum()) * cell_kv_bytes,
+                        flop=read_flop),
+    }
+    kernels = {}
+    for nm in names:
+        t = per_kernel_ms[nm] * 1e-3
+        e = {"ms": round(per_kernel_ms[nm], 4), "alg_bytes": int(alg[nm]["bytes"])}
+        if t > 0:
+            e["GBps"] = round(alg[nm]["bytes"] / t / 1e9, 1)
+            e["hbm_frac"] = round(alg[nm]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)
+            if "flop" in alg[nm]:
+                e["TFLOPs"] = round(alg[nm]["flop"] / t / 1e12, 2)
+                e["mfma_frac"] = round(alg[nm]["flop"] / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        kernels[nm] = e
+    dominant = max(names, key=lambda n: per_kernel_ms[n])
+    dom_t = per_kernel_ms[dominant] * 1e-3
+    achieved = alg[dominant]["bytes"] / dom_t / 1e9
+
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        if (cnt.get("kernel") == dominant and cnt.get("workload") == args.workload and
+                cnt.get("source_sha256_16") == kernel_source_digest(cnt["source"])):
+            traffic = int(cnt["hbm_bytes_per_launch"])
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dominant,
+                "alg_bytes_per_launch": int(alg[dominant]["bytes"])}
+
+    # ---- oracle on the host cores, bounded sample, plus a parity spot check ----
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        threads = min(16, len(os.sched_getaffinity(0)))
+        heads = [(bb, hh) for bb in range(min(b, 2)) for hh in range(H)]
+        if args.workload == "fs_32k":
+            heads = heads[:4]
+        op = oracle.Params(s=prm.s, B=prm.B, P=prm.P, W=prm.W, K=prm.K, prune=prm.prune, sigma=sigma, lam=lam,
+                           eps=prm.eps)
+        inputs64 = {bh: tuple(synth.to_f64(host[x][bh[0], bh[1]], w.dtype) for x in "qkv") for bh in heads}
+
+        def one(bh):
+            qq, kk, vv = inputs64[bh]
+            return bh, oracle.head(qq, kk, vv, None, op)
+
+        t1 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            refs = dict(ex.map(one, heads))
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(len(heads) * N / H / cpu_s, 1), "unit": "query-tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{len(heads)} of {b * H} (sequence, head) pairs, all {N} queries each "
+                         f"({len(heads) * N / H:.0f} query-tokens); {cpu_s:.1f}s wall"}
+        out_h = out.float().cpu().numpy()
+        worst, mism, ties, checked = 0.0, 0, 0, 0
+        for (bb, hh), ref in refs.items():
+            ok = (ref["gap_k"] >= 1e-6) & (np.nan_to_num(ref["gap_p"][np.arange(N) // prm.B], nan=np.inf) >= 1e-6)
+            ties += int((~ok).sum())
+            checked += int(ok.sum())
+            mism += int(np.any(sel_h[bb, hh][ok] != ref["sel"][ok], axis=1).sum())
+            worst = max(worst, float(np.abs(out_h[bb, hh][ok] - ref["out"][ok]).max()))
+        parity = {"heads": len(heads), "queries": checked, "near_ties": ties, "selection_mismatches": mism,
+                  "max_abs_err": worst}
+        log(f"[bench] oracle {cpu_s:.1f}s on {threads} threads; parity {parity}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": b, "heads": H, "seq_len": N, "head_dim": d, "s": prm.s, "B": prm.B,
+                   "P": prm.P, "W": prm.W, "K": prm.K, "prune": prm.prune, "sigma_h": sigma, "lambda_h": lam,
+                   "mean_distinct_cells_per_block": round(float(U[..., 1:].mean()), 3) if NB > 1 else 0.0},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "single_call_ms": round(single_ms, 4),
+        "single_call_matches_staged": same,
+        "parity_spot_check": parity,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

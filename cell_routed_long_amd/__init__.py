@@ -68,6 +68,8 @@ def lib():
         L.fs_prune_workspace_bytes.argtypes = [P_shape, P_prm]
         L.fs_prune_workspace_bytes.restype = sz
         L.fs_prune_retained.argtypes = [P_shape, P_prm, vp, vp, vp, vp, sz, vp]
+        L.fs_score_select.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.fs_readout.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp]
         L.fs_prefill_workspace_bytes.argtypes = [P_shape, P_prm]
         L.fs_prefill_workspace_bytes.restype = sz
         L.fs_longrange_prefill.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
@@ -75,7 +77,8 @@ def lib():
         L.fs_decode_state_bytes.restype = sz
         L.fs_longrange_decode.argtypes = [P_prm, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                           vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        for name in ("fs_cell_summaries", "fs_prune_retained", "fs_longrange_prefill", "fs_longrange_decode"):
+        for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout",
+                     "fs_longrange_prefill", "fs_longrange_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -149,6 +152,22 @@ def fs_prune_retained(sh: fs_shape, a, retained, n_retained, workspace, params: 
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().fs_prune_retained(ctypes.byref(sh), ctypes.byref(prm), _ptr(a), _ptr(retained), _ptr(n_retained),
                                    _ptr(workspace), nbytes, _stream(stream)), "fs_prune_retained")
+
+
+def fs_score_select(q, kbar, a, retained, n_retained, sigma_h, lambda_h, sel, params: Params = Params(),
+                    stream=None):
+    """Eq. 7 scores and per-query top-K: sel [b,H,N,K] int32."""
+    sh, prm = shape_of(q), params.c()
+    sig, lam = _floats(sigma_h, sh.H), _floats(lambda_h, sh.H)
+    _check(lib().fs_score_select(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(kbar), _ptr(a), _ptr(retained),
+                                 _ptr(n_retained), sig, lam, _ptr(sel), _stream(stream)), "fs_score_select")
+
+
+def fs_readout(q, k, v, sel, gain, out, params: Params = Params(), stream=None):
+    """Eq. 9 readout with Eq. 17 RMSNorm: out [b,H,N,d]."""
+    sh, prm = shape_of(q), params.c()
+    _check(lib().fs_readout(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(gain),
+                            _ptr(out), _stream(stream)), "fs_readout")
 
 
 def fs_prefill_workspace_bytes(sh: fs_shape, params: Params = Params()) -> int:

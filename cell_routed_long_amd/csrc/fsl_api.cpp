@@ -169,6 +169,36 @@ FSL_EXPORT fs_status fs_prune_retained(const fs_shape *shape, const fs_params *p
                                    static_cast<hipStream_t>(stream)));
 }
 
+FSL_EXPORT fs_status fs_score_select(const fs_shape *shape, const fs_params *prm, const void *q, const float *kbar,
+                                     const float *a, const int32_t *retained, const int32_t *n_retained,
+                                     const float *sigma_h, const float *lambda_h, int32_t *sel, void *stream)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(shape->H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    const Geometry g = geometry(shape, prm);
+    if (!q || !sel || ((!kbar || !a) && g.M > 0) || (g.prune && (!retained || !n_retained)))
+        return FS_ERR_INVALID;
+    return hip_status(launch_score_topk(g, hc, q, kbar, a, g.prune ? retained : nullptr,
+                                        g.prune ? n_retained : nullptr, sel, static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
+                                const void *v, const int32_t *sel, const float *gain, void *out, void *stream)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    if (!q || !k || !v || !sel || !out)
+        return FS_ERR_INVALID;
+    const Geometry g = geometry(shape, prm);
+    return hip_status(launch_readout(g, q, k, v, sel, gain, out, static_cast<hipStream_t>(stream)));
+}
+
 FSL_EXPORT size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm)
 {
     if (check_all(shape, prm) != FS_OK)

@@ -100,6 +100,33 @@ fs_status fs_prune_retained(const fs_shape *shape, const fs_params *prm, const f
                             int32_t *retained, int32_t *n_retained,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Routing scores and per-query selection, Eq. 7 and Sec. 3.3 "Per-query
+ * selection": r_ic = q_i . kbar_c / sqrt(d) + lambda_h a_c erf((i - p_c) /
+ * (2 sigma_h)) over A_i (the retained set of the query's block for FS-L, the
+ * whole prefix C_i for FS), and T_i = the min(K, |A_i|) best cells.
+ *   q           [batch, H, N, d]        shape dtype (input)
+ *   kbar, a     from fs_cell_summaries  (input)
+ *   retained, n_retained  from fs_prune_retained (input; NULL when prune == 0)
+ *   sigma_h, lambda_h     host [H] fp32 (sigma > 0, lambda >= 0)
+ *   sel         [batch, H, N, K] int32, (score desc, id asc), -1 padded (output)
+ */
+fs_status fs_score_select(const fs_shape *shape, const fs_params *prm, const void *q, const float *kbar,
+                          const float *a, const int32_t *retained, const int32_t *n_retained,
+                          const float *sigma_h, const float *lambda_h, int32_t *sel, void *stream);
+
+/*
+ * Token readout and RMSNorm, Eq. 9 (softmax over the tokens of the selected
+ * cells jointly, NoPE logits q_i . k_j / sqrt(d)) followed by Eq. 17's RMSNorm
+ * with gain; rows whose selection is empty are written as zeros.
+ *   q, k, v     [batch, H, N, d]  shape dtype (input)
+ *   sel         [batch, H, N, K]  int32 from fs_score_select (input)
+ *   gain        device [H, d] fp32, or NULL for unit gains
+ *   out         [batch, H, N, d]  shape dtype (output)
+ */
+fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k, const void *v,
+                     const int32_t *sel, const float *gain, void *out, void *stream);
+
 /* Bytes of workspace fs_longrange_prefill needs (0 on invalid arguments). */
 size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm);
 
