@@ -206,10 +206,21 @@ def fs_longrange_decode(state, q, k_new, v_new, sigma_h, lambda_h, gain, out, se
 
 # ------------------------------------------------------- allocation helpers --
 
+def new_state(batch: int, H: int, d: int, dtype, params: Params = Params(), device="cuda"):
+    """A decode-state buffer (uint8 tensor) of fs_decode_state_bytes for this shape."""
+    import torch
+    code = FS_BF16 if dtype == torch.bfloat16 else FS_F32
+    n = fs_decode_state_bytes(batch, H, d, code, params)
+    if n == 0:
+        raise FslError(FS_ERR_UNSUPPORTED, "fs_decode_state_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def prefill(q, k, v, params: Params = Params(), sigma=4.0, lam=1.0, gain=None, want_out=True, want_sel=True,
-            workspace=None, stream=None):
+            workspace=None, stream=None, state=None):
     """Allocate outputs and workspace with torch and run fs_longrange_prefill.
 
+    `state`, if given (see new_state), is filled for continuing at position N.
     Returns (out or None, sel or None, workspace)."""
     import torch
     sh = shape_of(k)
@@ -218,8 +229,20 @@ def prefill(q, k, v, params: Params = Params(), sigma=4.0, lam=1.0, gain=None, w
         raise FslError(FS_ERR_UNSUPPORTED, "fs_prefill_workspace_bytes")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
-    out = torch.empty_like(q) if want_out else None
+    out = torch.empty_like(k) if want_out else None
     sel = torch.empty(k.shape[0], k.shape[1], k.shape[2], params.K, dtype=torch.int32, device=k.device) \
         if want_sel else None
-    fs_longrange_prefill(q, k, v, sigma, lam, gain, out, sel, None, workspace, params, stream)
+    fs_longrange_prefill(q, k, v, sigma, lam, gain, out, sel, state, workspace, params, stream)
     return out, sel, workspace
+
+
+def decode(state, q, k_new, v_new, params: Params = Params(), sigma=4.0, lam=1.0, gain=None, want_sel=True,
+           out=None, sel=None, stream=None):
+    """One decode step (fs_longrange_decode) for [batch, H, d] inputs; returns (out, sel or None)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    if want_sel and sel is None:
+        sel = torch.empty(q.shape[0], q.shape[1], params.K, dtype=torch.int32, device=q.device)
+    fs_longrange_decode(state, q, k_new, v_new, sigma, lam, gain, out, sel if want_sel else None, params, stream)
+    return out, (sel if want_sel else None)

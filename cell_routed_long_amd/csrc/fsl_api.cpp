@@ -3,6 +3,7 @@
 // call, so a rejected call touches neither the device nor the runtime.
 #include "fsl.h"
 
+#include <climits>
 #include <cmath>
 #include <cstring>
 
@@ -109,11 +110,84 @@ fs_status check_heads(int H, const float *sigma_h, const float *lambda_h, HeadCo
             return FS_ERR_INVALID;
         hc->inv_two_sigma[h] = 1.0f / (2.0f * sigma_h[h]);
         hc->lambda[h] = lambda_h[h];
+        hc->sigma[h] = sigma_h[h];
     }
     return FS_OK;
 }
 
 inline fs_status hip_status(hipError_t e) { return e == hipSuccess ? FS_OK : FS_ERR_HIP; }
+
+// Streaming decode needs FS-L (a bounded retained set) and at most kMaxSlots
+// slots per (sequence, head): P + W retained cells plus B/s pending cells.
+fs_status check_decode_params(const fs_params *p)
+{
+    fs_status st = check_params(p);
+    if (st != FS_OK)
+        return st;
+    if (!p->prune || (int64_t)p->P + p->W + p->B / p->s > kMaxSlots)
+        return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
+fs_status check_decode_dims(int32_t batch, int32_t H, int32_t d, fs_dtype dtype)
+{
+    if (batch < 1 || H < 1 || d < 1 || (dtype != FS_F32 && dtype != FS_BF16))
+        return FS_ERR_INVALID;
+    if ((d != 64 && d != 128) || H > FS_MAX_HEADS)
+        return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
+// Record layout of the decode state (see StateLayout in fsl_device.h).
+StateLayout state_layout(int32_t d, fs_dtype dtype, const fs_params *p)
+{
+    StateLayout L;
+    std::memset(&L, 0, sizeof(L));
+    const size_t esz = dtype == FS_BF16 ? 2 : 4;
+    L.S = p->P + p->W + p->B / p->s;
+    size_t off = align_up(sizeof(StateMeta));
+    L.off_ret = (int64_t)off;
+    off += align_up((size_t)L.S * sizeof(int32_t));
+    L.off_cell = (int64_t)off;
+    off += align_up((size_t)L.S * sizeof(int32_t));
+    L.off_flags = (int64_t)off;
+    off += align_up((size_t)L.S * sizeof(int32_t));
+    L.off_a = (int64_t)off;
+    off += align_up((size_t)L.S * sizeof(float));
+    L.off_kbar = (int64_t)off;
+    off += align_up((size_t)L.S * d * sizeof(float));
+    L.off_k = (int64_t)off;
+    off += align_up((size_t)L.S * p->s * d * esz);
+    L.off_v = (int64_t)off;
+    off += align_up((size_t)L.S * p->s * d * esz);
+    L.rec_bytes = (int64_t)off;
+    return L;
+}
+
+StateHeader state_header(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, const fs_params *p,
+                         const StateLayout &L)
+{
+    StateHeader h;
+    std::memset(&h, 0, sizeof(h));
+    h.magic = kStateMagic;
+    h.version = kStateVersion;
+    h.batch = batch;
+    h.H = H;
+    h.d = d;
+    h.dtype = (int32_t)dtype;
+    h.s = p->s;
+    h.B = p->B;
+    h.P = p->P;
+    h.W = p->W;
+    h.n_slots = L.S;
+    h.rec_bytes = L.rec_bytes;
+    return h;
+}
+
+size_t state_bytes_of(int32_t batch, int32_t H, const StateLayout &L)
+{
+    return (size_t)kStateHeaderBytes + (size_t)batch * H * (size_t)L.rec_bytes;
+}
 
 } // namespace
 } // namespace fsl
@@ -165,7 +239,7 @@ FSL_EXPORT fs_status fs_prune_retained(const fs_shape *shape, const fs_params *p
     if (workspace_bytes < fs_prune_workspace_bytes(shape, prm))
         return FS_ERR_WORKSPACE;
     const Geometry g = geometry(shape, prm);
-    return hip_status(launch_prune(g, a, static_cast<int32_t *>(workspace), retained, n_retained,
+    return hip_status(launch_prune(g, a, static_cast<int32_t *>(workspace), retained, n_retained, 1,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -226,8 +300,13 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
     if (out && !v)
         return FS_ERR_INVALID;
     if (state) {
-        (void)state_bytes;
-        return FS_ERR_UNSUPPORTED; // decode state not built by this version
+        st = check_decode_params(prm);
+        if (st != FS_OK)
+            return st;
+        if (!v)
+            return FS_ERR_INVALID;
+        if (state_bytes != fs_decode_state_bytes(shape->batch, shape->H, shape->d, shape->dtype, prm))
+            return FS_ERR_STATE;
     }
     const Geometry g = geometry(shape, prm);
     const PrefillLayout L = prefill_layout(g);
@@ -243,25 +322,28 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
     int32_t *sel_buf = sel ? sel : reinterpret_cast<int32_t *>(ws + L.sel);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    const bool route = out || sel; // state-only calls skip scoring and readout
     hipError_t e = launch_cell_summaries(g, k, kbar, a, s);
     if (e == hipSuccess && g.prune)
-        e = launch_prune(g, a, death, retained, n_ret, s);
-    if (e == hipSuccess)
+        e = launch_prune(g, a, death, retained, n_ret, route ? 1 : 0, s);
+    if (e == hipSuccess && route)
         e = launch_score_topk(g, hc, q, kbar, a, g.prune ? retained : nullptr, g.prune ? n_ret : nullptr, sel_buf,
                               s);
     if (e == hipSuccess && out)
         e = launch_readout(g, q, k, v, sel_buf, gain, out, s);
+    if (e == hipSuccess && state) {
+        const StateLayout SL = state_layout(g.d, shape->dtype, prm);
+        const StateHeader hdr = state_header(shape->batch, shape->H, g.d, shape->dtype, prm, SL);
+        e = launch_state_build(g, SL, hdr, state, k, v, kbar, a, death, s);
+    }
     return hip_status(e);
 }
 
 FSL_EXPORT size_t fs_decode_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, const fs_params *prm)
 {
-    (void)batch;
-    (void)H;
-    (void)d;
-    (void)dtype;
-    (void)prm;
-    return 0; // streaming decode state not provided by this version
+    if (check_decode_dims(batch, H, d, dtype) != FS_OK || check_decode_params(prm) != FS_OK)
+        return 0;
+    return state_bytes_of(batch, H, state_layout(d, dtype, prm));
 }
 
 FSL_EXPORT fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
@@ -269,7 +351,25 @@ FSL_EXPORT fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, in
                                          const void *v_new, const float *sigma_h, const float *lambda_h,
                                          const float *gain, void *out, int32_t *sel, void *stream)
 {
-    (void)prm; (void)batch; (void)H; (void)d; (void)dtype; (void)state; (void)state_bytes; (void)q;
-    (void)k_new; (void)v_new; (void)sigma_h; (void)lambda_h; (void)gain; (void)out; (void)sel; (void)stream;
-    return FS_ERR_UNSUPPORTED;
+    fs_status st = check_decode_dims(batch, H, d, dtype);
+    if (st != FS_OK)
+        return st;
+    st = check_decode_params(prm);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    if (!state || !q || !k_new || !v_new || !out)
+        return FS_ERR_INVALID;
+    if ((int64_t)batch * H > INT32_MAX)
+        return FS_ERR_UNSUPPORTED;
+    const StateLayout L = state_layout(d, dtype, prm);
+    if (state_bytes != state_bytes_of(batch, H, L))
+        return FS_ERR_STATE;
+    const StateHeader expect = state_header(batch, H, d, dtype, prm, L);
+    return hip_status(launch_decode_step(batch * H, H, d, dtype == FS_BF16 ? 1 : 0, prm->K, prm->P, prm->W, prm->eps,
+                                         L, expect, hc, state, q, k_new, v_new, gain, out, sel,
+                                         static_cast<hipStream_t>(stream)));
 }

@@ -98,6 +98,43 @@ __device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xo
 struct HeadConsts {
     float inv_two_sigma[128]; // 1 / (2 sigma_h)
     float lambda[128];        // lambda_h
+    float sigma[128];         // sigma_h as given (the decode step scores in fp64)
+};
+
+} // namespace fsl
+
+namespace fsl {
+
+// ---- streaming decode state (one flat caller-owned buffer) ----------------
+// Layout: a StateHeader padded to kStateHeaderBytes, then one record per
+// (sequence, head), each rec_bytes long.  A record holds n_slots cell slots
+// (P + W retained + B/s cells of the block being filled); a slot carries the
+// cell's raw keys and values, its fp32 mean key and norm, its absolute cell id
+// (-1 = free) and whether the cell is in TopP.  The retained set is a list of
+// slots in ascending cell-id order.
+constexpr uint32_t kStateMagic = 0x31534C46u; // "FLS1"
+constexpr uint32_t kStateVersion = 1;
+constexpr int64_t kStateHeaderBytes = 256;
+constexpr int32_t kFlagTop = 1; // the slot's cell belongs to TopP of the current prefix
+constexpr int kMaxSlots = 128;  // P + W + B/s supported by the decode kernels
+
+struct StateHeader {
+    uint32_t magic, version;
+    int32_t batch, H, d, dtype, s, B, P, W, n_slots, pad;
+    int64_t rec_bytes;
+};
+
+struct StateMeta {
+    int64_t pos;      // next position to be processed
+    int32_t n_ret;    // |A| of the current block
+    int32_t cur_slot; // slot of the cell receiving tokens, -1 if none yet
+};
+
+struct StateLayout {
+    int32_t S;         // slots per record
+    int32_t pad;
+    int64_t rec_bytes; // bytes per (sequence, head) record
+    int64_t off_ret, off_cell, off_flags, off_a, off_kbar, off_k, off_v; // offsets inside a record
 };
 
 } // namespace fsl

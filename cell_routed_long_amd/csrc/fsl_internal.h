@@ -25,8 +25,9 @@ struct Geometry {
 hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, hipStream_t st);
 
 // death[c]: first query block whose TopP no longer holds cell c (INT32_MAX: never leaves).
+// emit = 0 computes only the exit blocks (enough to build a decode state).
 hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32_t *retained,
-                        int32_t *n_ret, hipStream_t st);
+                        int32_t *n_ret, int emit, hipStream_t st);
 
 hipError_t launch_score_topk(const Geometry &g, const HeadConsts &hc, const void *q, const float *kbar,
                              const float *a, const int32_t *retained, const int32_t *n_ret, int32_t *sel,
@@ -34,5 +35,17 @@ hipError_t launch_score_topk(const Geometry &g, const HeadConsts &hc, const void
 
 hipError_t launch_readout(const Geometry &g, const void *q, const void *k, const void *v,
                           const int32_t *sel, const float *gain, void *out, hipStream_t st);
+
+// Decode state of every (sequence, head) for continuing at position g.N, from
+// the prefill's summaries (kbar, a), exit blocks (death) and raw keys/values.
+hipError_t launch_state_build(const Geometry &g, const StateLayout &L, const StateHeader &hdr, void *state,
+                              const void *k, const void *v, const float *kbar, const float *a,
+                              const int32_t *death, hipStream_t st);
+
+// One decode step for bh = batch * H records.
+hipError_t launch_decode_step(int32_t bh, int32_t H, int32_t d, int32_t bf16, int32_t K, int32_t P, int32_t W,
+                              float eps, const StateLayout &L, const StateHeader &expect, const HeadConsts &hc,
+                              void *state, const void *q, const void *k_new, const void *v_new,
+                              const float *gain, void *out, int32_t *sel, hipStream_t st);
 
 } // namespace fsl

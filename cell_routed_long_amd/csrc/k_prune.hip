@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kWave) void prune_emit_kernel(const int32_t *__rest
 } // namespace
 
 hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32_t *retained, int32_t *n_ret,
-                        hipStream_t st)
+                        int emit, hipStream_t st)
 {
     const int cpb = g.B / g.s;
     if (g.M > 0) {
@@ -121,6 +121,8 @@ hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32
         if (err != hipSuccess)
             return err;
     }
+    if (!emit)
+        return hipSuccess;
     dim3 grid2((unsigned)g.NB, (unsigned)g.bh);
     hipLaunchKernelGGL(prune_emit_kernel, grid2, dim3(kWave), 0, st, death, retained, n_ret, g.M, g.NB, g.cap, g.W,
                        cpb);

@@ -144,7 +144,8 @@ size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm);
  *   sel         [batch, H, N, K]   int32 T_i by (score desc, id asc), -1 padded,
  *               or NULL (output)
  *   state       decode state to fill for continuing at position N (see
- *               fs_decode_state_bytes), or NULL
+ *               fs_decode_state_bytes; requires prune = 1 and v), or NULL;
+ *               state_bytes must equal fs_decode_state_bytes() (FS_ERR_STATE)
  *   workspace   fs_prefill_workspace_bytes() bytes of device memory (scratch)
  * At least one of out, sel, state must be non-NULL.  q and v may be NULL when
  * out and sel are both NULL (state-only prefill of a long prefix).
@@ -155,25 +156,52 @@ fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params *prm,
                                void *out, int32_t *sel, void *state, size_t state_bytes,
                                void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of one decode state for `batch` sequences x H heads (0 on invalid
- * arguments).  The state is one flat caller-owned device buffer; copying its
- * bytes checkpoints the stream exactly. */
+/*
+ * Streaming decode (Sec. 3.3 "Inference"; App. C "Bounded cache", Eq. 15).
+ *
+ * The decode state is one flat caller-owned device buffer: a 256-byte header
+ * (shape, P, W, slot count) followed by one record per (sequence, head).  A
+ * record holds P + W + B/s cell slots: the retained set A of the current query
+ * block (at most P + W cells, Eq. 8) plus the cells of the block being filled.
+ * Each slot keeps the cell's raw keys and values (dtype), its fp32 mean key and
+ * norm (Eq. 5), its absolute cell id and whether it is in TopP; the record also
+ * keeps the next position and the retained slots in ascending cell-id order.
+ * Memory per (sequence, head) is therefore constant in the context length.
+ * Copying the buffer's bytes checkpoints the stream exactly.
+ * Supported: FS-L (prune = 1) with P + W + B/s <= 128 slots.
+ */
+
+/* Bytes of one decode state for `batch` sequences x H heads (0 on invalid or
+ * unsupported arguments, including prune = 0: FS keeps the whole prefix). */
 size_t fs_decode_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
                              const fs_params *prm);
 
 /*
- * One decode step of the long-range branch for every sequence (Sec. 3.3
- * "Inference"; App. C "Bounded cache", Eq. 15): with i the stored position,
- *   (1) if i is a block start, the block's newly eligible cells are merged
- *       into TopP (Eq. 15), Recent_W advances and cells in neither are evicted;
+ * One decode step of the long-range branch for every (sequence, head), one
+ * token each.  With i the record's stored position:
+ *   (1) if i is a block start (i % B == 0, i > 0), the B/s cells that just
+ *       became eligible are merged into TopP (Eq. 15: TopP(C u D) =
+ *       TopP(TopP(C) u D), ties to the smaller id), A = Recent_W u TopP, and
+ *       slots whose cell is in neither are freed;
  *   (2) k_new, v_new are appended; when position i completes a cell its
- *       summary (Eq. 5) is formed;
- *   (3) q is scored against the retained cells (Eq. 7), its top-K selected and
- *       read out (Eq. 9) with RMSNorm; the position advances to i + 1.
- *   state        from fs_longrange_prefill (or a copy of one)   (in/out)
- *   q, k_new, v_new  [batch, H, d]  dtype                       (input)
- *   sigma_h, lambda_h, gain        as for fs_longrange_prefill
- *   out          [batch, H, d] dtype (output);  sel [batch, H, K] int32 or NULL
+ *       summary (Eq. 5) is formed (fp64 sums, rounded once to fp32);
+ *   (3) q is scored against A (Eq. 7, evaluated in fp64), its min(K, |A|) best
+ *       cells are selected and read out (Eq. 9) with RMSNorm (Eq. 17); the
+ *       position advances to i + 1.
+ * The output equals the prefill's at position i (same causal operator).
+ *   prm              as for the prefill that built the state (K may differ)
+ *   state            fs_decode_state_bytes() bytes, filled by
+ *                    fs_longrange_prefill (or a byte copy of such a state)   (in/out)
+ *   q, k_new, v_new  device [batch, H, d] dtype                             (input)
+ *   sigma_h, lambda_h, gain   as for fs_longrange_prefill
+ *   out              device [batch, H, d] dtype                             (output)
+ *   sel              device [batch, H, K] int32, (score desc, id asc), -1 padded, or NULL
+ * Errors: FS_ERR_STATE when state_bytes does not match this shape and prm.  A
+ * buffer of the right size whose header was not written by
+ * fs_longrange_prefill for this shape is detected on the device: out is set to
+ * NaN, sel to -1, and the buffer is left untouched.  One launch per step, no
+ * host synchronisation: steps can be captured in a HIP graph.  Steps on the
+ * same state must be ordered (same stream or explicit dependencies).
  */
 fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, int32_t d,
                               fs_dtype dtype, void *state, size_t state_bytes,

@@ -119,3 +119,66 @@ def test_prune_requires_fsl_mode(L):
     p = prm()
     assert L.fs_prune_retained(ctypes.byref(sh), ctypes.byref(p), vp(1), vp(1), vp(1), vp(1), 0,
                                None) == fsl.FS_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------ decode ----
+
+def test_decode_state_bytes(L):
+    p = fsl.Params()
+    b, H, d = 32, 8, 128
+    n = fsl.fs_decode_state_bytes(b, H, d, fsl.FS_BF16, p)
+    S = p.P + p.W + p.B // p.s  # retained + pending slots
+    per_rec = S * p.s * d * 2 * 2 + S * d * 4  # raw K/V + mean keys
+    assert 256 + b * H * per_rec <= n <= 256 + b * H * (per_rec + 8 * 1024)
+    assert fsl.fs_decode_state_bytes(b, H, d, fsl.FS_F32, p) > n
+    # FS (no pruning) has no bounded state; P + W + B/s above 128 slots is not supported
+    assert fsl.fs_decode_state_bytes(b, H, d, fsl.FS_BF16, fsl.Params(prune=False)) == 0
+    assert fsl.fs_decode_state_bytes(b, H, d, fsl.FS_BF16, fsl.Params(P=120, W=5)) == 0
+    assert fsl.fs_decode_state_bytes(b, H, d, fsl.FS_BF16, fsl.Params(P=120, W=4)) > 0
+    assert fsl.fs_decode_state_bytes(0, H, d, fsl.FS_BF16, p) == 0
+    assert fsl.fs_decode_state_bytes(b, H, 96, fsl.FS_BF16, p) == 0
+
+
+def test_decode_validation_before_launch(L):
+    p = fsl.Params()
+    prm_c = p.c()
+    b, H, d = 2, 3, 64
+    n = fsl.fs_decode_state_bytes(b, H, d, fsl.FS_F32, p)
+    vp = ctypes.c_void_p
+    sig = (ctypes.c_float * H)(*([4.0] * H))
+    lam = (ctypes.c_float * H)(*([1.0] * H))
+    bad = (ctypes.c_float * H)(*([-1.0] * H))
+
+    def call(prm=prm_c, st_bytes=n, sigma=sig, q=1, out=1, state=1, dd=d, dtype=fsl.FS_F32):
+        return L.fs_longrange_decode(ctypes.byref(prm), b, H, dd, dtype, vp(state) if state else None, st_bytes,
+                                     vp(q) if q else None, vp(1), vp(1), sigma, lam, None,
+                                     vp(out) if out else None, None, None)
+
+    assert call(st_bytes=n - 1) == fsl.FS_ERR_STATE
+    assert call(st_bytes=n + 256) == fsl.FS_ERR_STATE
+    assert call(q=0) == fsl.FS_ERR_INVALID
+    assert call(out=0) == fsl.FS_ERR_INVALID
+    assert call(state=0) == fsl.FS_ERR_INVALID
+    assert call(sigma=bad) == fsl.FS_ERR_INVALID
+    assert call(dd=96) == fsl.FS_ERR_UNSUPPORTED
+    assert call(dtype=5) == fsl.FS_ERR_INVALID
+    assert call(prm=fsl.Params(prune=False).c()) == fsl.FS_ERR_UNSUPPORTED
+    assert call(prm=fsl.Params(K=0).c()) == fsl.FS_ERR_INVALID
+
+
+def test_prefill_state_validation(L):
+    sh = shape(b=1, H=2, N=1000, d=64)
+    p = fsl.Params()
+    vp = ctypes.c_void_p
+    sig = (ctypes.c_float * 2)(4.0, 4.0)
+    lam = (ctypes.c_float * 2)(1.0, 1.0)
+    ws = fsl.fs_prefill_workspace_bytes(sh, p)
+    n = fsl.fs_decode_state_bytes(1, 2, 64, fsl.FS_F32, p)
+
+    def call(prm, st_bytes, v=1):
+        return L.fs_longrange_prefill(ctypes.byref(sh), ctypes.byref(prm), None, vp(1), vp(v) if v else None, sig,
+                                      lam, None, None, None, vp(1), st_bytes, vp(1), ws, None)
+
+    assert call(p.c(), n - 1) == fsl.FS_ERR_STATE
+    assert call(p.c(), n, v=0) == fsl.FS_ERR_INVALID            # the state keeps raw values
+    assert call(fsl.Params(prune=False).c(), n) == fsl.FS_ERR_UNSUPPORTED
