@@ -27,11 +27,15 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "long-range FS-L query-tokens/s at 16k prefill; % HBM/MFMA roofline"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "readout_16k_counters.json")
+DECODE_METRIC = "long-range FS-L decode query-tokens/s at a 262,144-token context; % HBM roofline"
 WORKLOADS = {
     "prefill_16k": dict(prune=True),
     "fs_32k": dict(prune=False),
     "prefill_4k": dict(prune=True),
+    "decode_256k": dict(prune=True, decode=True),
 }
+DECODE_PREFIX = 262144
+DECODE_LAYER_STATES = 12  # independent states in rotation: 12 x ~26 MB per step exceeds the 256 MB MALL
 
 
 def log(*a):
@@ -86,6 +90,9 @@ def main() -> int:
     if not os.path.exists(fsl.LIB_PATH):
         fsl.build()
     fsl.lib()
+
+    if WORKLOADS[args.workload].get("decode"):
+        return run_decode(args)
 
     w = synth.WORKLOADS[args.workload]
     prm = fsl.Params(prune=WORKLOADS[args.workload]["prune"])
@@ -279,6 +286,208 @@ def main() -> int:
         "kernels": kernels,
         "single_call_ms": round(single_ms, 4),
         "single_call_matches_staged": same,
+        "parity_spot_check": parity,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_decode(args) -> int:
+    """Streaming decode: b32 H8 d128 bf16 sequences with a 262,144-token prefix.
+
+    The state comes from a state-only prefill of the prefix; a step is one
+    fs_longrange_decode call (one token for every sequence).  The timed region
+    replays, as one HIP graph, `steps` token steps over DECODE_LAYER_STATES
+    independent copies of the state (as the layers of a model would), so the
+    per-step working set cannot stay in the last-level cache.  Throughput counts
+    one query-token per sequence, step and layer-state."""
+    import numpy as np
+    import torch
+
+    import cell_routed_long_amd as fsl
+    import synth
+
+    w = synth.WORKLOADS["decode_256k"]
+    prm = fsl.Params()
+    sigma, lam = 4.0, 1.0
+    dev = torch.device("cuda:0")
+    b, H, d, N0 = w.batch, w.H, w.d, DECODE_PREFIX
+    T = w.N - N0
+    steps = min(args.steps, T)
+    R = DECODE_LAYER_STATES
+    stream = torch.cuda.current_stream()
+
+    # ---- prefix K/V, generated per sequence on the host and uploaded ----
+    t0 = time.time()
+    dk = torch.empty(b, H, N0, d, dtype=torch.bfloat16, device=dev)
+    dv = torch.empty_like(dk)
+    for bb in range(b):
+        for x, dst in (("k", dk), ("v", dv)):
+            a = synth.tensor(w, x, 0, N0, heads=[(bb, h) for h in range(H)])
+            dst[bb].copy_(torch.from_numpy(a.view(np.int16)).view(torch.bfloat16))
+        if bb % 8 == 7:
+            log(f"[bench] prefix generated for {bb + 1}/{b} sequences ({time.time() - t0:.0f}s)")
+    steps_in = {x: torch.from_numpy(np.ascontiguousarray(np.moveaxis(synth.tensor(w, x, N0, w.N), 2, 0))
+                                    .view(np.int16)).view(torch.bfloat16).to(dev) for x in "qkv"}
+    log(f"[bench] inputs ready in {time.time() - t0:.0f}s")
+
+    # ---- state-only prefill of the prefix ----
+    snap = fsl.new_state(b, H, d, torch.bfloat16, prm)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ws = None
+    ev0.record(stream)
+    _, _, ws = fsl.prefill(None, dk, dv, prm, sigma=sigma, lam=lam, want_out=False, want_sel=False, state=snap)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = ev0.elapsed_time(ev1)
+    del ws, dk, dv
+    torch.cuda.empty_cache()
+    states = [torch.empty_like(snap) for _ in range(R)]
+    outs = torch.empty(R, steps, b, H, d, dtype=torch.bfloat16, device=dev)
+    sels = torch.empty(R, steps, b, H, prm.K, dtype=torch.int32, device=dev)
+
+    def restore():
+        for st in states:
+            st.copy_(snap)
+
+    def run(layer_states):
+        for t in range(steps):
+            for r in layer_states:
+                fsl.decode(states[r], steps_in["q"][t], steps_in["k"][t], steps_in["v"][t], prm, sigma=sigma,
+                           lam=lam, out=outs[r, t], sel=sels[r, t])
+
+    # warm-up (eager), then capture; states are restored before each timed replay
+    restore()
+    for _ in range(max(1, args.warmup)):
+        run(range(R))
+        restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            run(range(R))
+    stream.wait_stream(cap)
+    graph1 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph1, stream=cap):
+            run([0])
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+
+    restore()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    graph_ms = ev0.elapsed_time(ev1)
+    out_h = outs[0].float().cpu().numpy()  # [steps, b, H, d]
+    sel_h = sels[0].cpu().numpy()
+    same_states = bool(all(torch.equal(sels[r], sels[0]) for r in range(R)))
+    per_launch_ms = graph_ms / (steps * R)
+    log(f"[bench] decode graph: {graph_ms:.3f} ms for {steps} steps x {R} states = {per_launch_ms * 1e3:.2f} us "
+        f"per step and state (state build {build_ms:.2f} ms)")
+
+    # single state, warm cache, and eager launches, for reference
+    restore()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    graph1.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    single_us = ev0.elapsed_time(ev1) / steps * 1e3
+    restore()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    run(range(R))
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = ev0.elapsed_time(ev1) / (steps * R) * 1e3
+
+    # ---- algorithmic bytes per launch (one step of every (sequence, head)) ----
+    n_sel = np.count_nonzero(sel_h >= 0, axis=-1)  # [steps, b, H]
+    n_ret = min(prm.P + prm.W, N0 // prm.s)
+    per_pair = (n_ret * (d * 4 + 4 + 4)            # mean keys, norms, slot ids of A
+                + 3 * d * 2 + d * 2                # q, k_new, v_new in; out
+                + 2 * d * 2 + 16)                  # appended key/value row; position
+    alg_bytes = b * H * per_pair + float(n_sel.mean()) * b * H * prm.s * d * 2 * 2
+    achieved = alg_bytes / (per_launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_step_kernel",
+                "alg_bytes_per_launch": int(alg_bytes)}
+    value = b * steps * R / (graph_ms * 1e-3)
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        threads = min(16, len(os.sched_getaffinity(0)))
+        pairs = [(bb, h) for bb in (0, b - 1) for h in range(H)]
+        op = oracle.Params(s=prm.s, B=prm.B, P=prm.P, W=prm.W, K=prm.K, prune=True, sigma=sigma, lam=lam,
+                           eps=prm.eps)
+
+        def inputs(bh):
+            kk = synth.to_f64(synth.tensor(w, "k", heads=[bh], threads=1)[0], w.dtype)
+            vv = synth.to_f64(synth.tensor(w, "v", heads=[bh], threads=1)[0], w.dtype)
+            qq = np.zeros_like(kk)
+            qq[N0:] = synth.to_f64(synth.tensor(w, "q", N0, w.N, heads=[bh], threads=1)[0], w.dtype)
+            return bh, (qq, kk, vv)
+
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            data = dict(ex.map(inputs, pairs))
+
+        def one(bh):
+            qq, kk, vv = data[bh]
+            return bh, oracle.head(qq, kk, vv, None, op, i_lo=N0, i_hi=N0 + steps, want_summaries=False)
+
+        t1 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            refs = dict(ex.map(one, pairs))
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(len(pairs) / H * steps / cpu_s, 1), "unit": "query-tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{len(pairs)} of {b * H} (sequence, head) pairs (sequences 0 and {b - 1}), all {steps} "
+                         f"decode positions each, from the raw 262,144-token prefix; {cpu_s:.1f}s wall"}
+        worst, mism, ties, checked = 0.0, 0, 0, 0
+        for (bb, hh), ref in refs.items():
+            ok = (ref["gap_k"] >= 1e-6) & (np.nan_to_num(ref["gap_p"][np.arange(N0, N0 + steps) // prm.B],
+                                                         nan=np.inf) >= 1e-6)
+            ties += int((~ok).sum())
+            checked += int(ok.sum())
+            mism += int(np.any(sel_h[:, bb, hh][ok] != ref["sel"][ok], axis=1).sum())
+            worst = max(worst, float(np.abs(out_h[:, bb, hh][ok] - ref["out"][ok]).max()))
+        parity = {"heads": len(pairs), "steps": checked, "near_ties": ties, "selection_mismatches": mism,
+                  "max_abs_err": worst}
+        log(f"[bench] oracle {cpu_s:.1f}s on {threads} threads; parity {parity}")
+
+    result = {
+        "metric": DECODE_METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(graph_ms / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": b, "heads": H, "prefix": N0, "head_dim": d, "s": prm.s, "B": prm.B,
+                   "P": prm.P, "W": prm.W, "K": prm.K, "sigma_h": sigma, "lambda_h": lam, "layer_states": R,
+                   "timing": "one HIP graph replay of steps x layer_states decode launches"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "us_per_step_and_state": round(per_launch_ms * 1e3, 3),
+        "us_per_step_single_state_warm": round(single_us, 3),
+        "us_per_step_eager": round(eager_us, 3),
+        "state_build_ms": round(build_ms, 3),
+        "state_bytes": int(snap.numel()),
+        "layer_states_agree": same_states,
         "parity_spot_check": parity,
     }
     print(json.dumps(result), flush=True)

@@ -146,7 +146,7 @@ StateLayout state_layout(int32_t d, fs_dtype dtype, const fs_params *p)
     const size_t esz = dtype == FS_BF16 ? 2 : 4;
     L.S = p->P + p->W + p->B / p->s;
     size_t off = align_up(sizeof(StateMeta));
-    L.off_ret = (int64_t)off;
+    L.off_ridx = (int64_t)off;
     off += align_up((size_t)L.S * sizeof(int32_t));
     L.off_cell = (int64_t)off;
     off += align_up((size_t)L.S * sizeof(int32_t));

@@ -94,6 +94,45 @@ __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(
 __device__ __forceinline__ int shfl_xor_i(int x, int m) { return __shfl_xor(x, m, kWave); }
 __device__ __forceinline__ double shfl_xor_d(double x, int m) { return __shfl_xor(x, m, kWave); }
 
+// ---- wave-wide reductions on the DPP network (no LDS round trip) ----------
+// Call with all 64 lanes active.  Within each row of 16 lanes the butterfly
+// pairs lanes i^1, i^2 (quad permutes), then mirrors within 8 and 16 lanes;
+// the four row results are combined through v_readlane, so every lane gets the
+// same value in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float readlane_f(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ int readlane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ double readlane_d(double x, int l)
+{
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, l);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), l);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ float wave_sum_f(float x)
+{
+    x += dpp_f<0xB1>(x);  // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);  // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x); // row_half_mirror
+    x += dpp_f<0x140>(x); // row_mirror
+    return (readlane_f(x, 0) + readlane_f(x, 16)) + (readlane_f(x, 32) + readlane_f(x, 48));
+}
+__device__ __forceinline__ float wave_max_f(float x)
+{
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
+}
+
 // Per-head routing constants, passed by value with every launch.
 struct HeadConsts {
     float inv_two_sigma[128]; // 1 / (2 sigma_h)
@@ -110,8 +149,8 @@ namespace fsl {
 // (sequence, head), each rec_bytes long.  A record holds n_slots cell slots
 // (P + W retained + B/s cells of the block being filled); a slot carries the
 // cell's raw keys and values, its fp32 mean key and norm, its absolute cell id
-// (-1 = free) and whether the cell is in TopP.  The retained set is a list of
-// slots in ascending cell-id order.
+// (-1 = free), whether the cell is in TopP, and its position in the retained
+// set A listed in ascending cell-id order (-1 = not in A).
 constexpr uint32_t kStateMagic = 0x31534C46u; // "FLS1"
 constexpr uint32_t kStateVersion = 1;
 constexpr int64_t kStateHeaderBytes = 256;
@@ -134,7 +173,7 @@ struct StateLayout {
     int32_t S;         // slots per record
     int32_t pad;
     int64_t rec_bytes; // bytes per (sequence, head) record
-    int64_t off_ret, off_cell, off_flags, off_a, off_kbar, off_k, off_v; // offsets inside a record
+    int64_t off_ridx, off_cell, off_flags, off_a, off_kbar, off_k, off_v; // offsets inside a record
 };
 
 } // namespace fsl

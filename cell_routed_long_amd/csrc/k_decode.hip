@@ -16,7 +16,9 @@
 //       rounded once, exactly as the prefill summary kernel does;
 //   (3) q is scored against A in fp64 (Eq. 7), its top-K cells are chosen by
 //       rank (score desc, id asc), and the readout (Eq. 9) with RMSNorm
-//       (Eq. 17) runs over their tokens.
+//       (Eq. 17) runs over their tokens: each wave gathers one selected cell
+//       and keeps a running softmax (max, sum, weighted values) that the waves
+//       combine at the end, so the readout needs a single barrier.
 // All branching on the position happens on the device, so a step can be
 // captured in a HIP graph.  The prefill builds the state directly from its
 // exit blocks (state_build_kernel), so no merge chain is replayed.
@@ -64,9 +66,49 @@ __device__ __forceinline__ void load_row_f32(const T *__restrict__ p, float (&x)
     }
 }
 
+// Order-preserving integer images of the two rankings (a larger key ranks first):
+//   TopP by (norm desc, id asc): the fp32 norm's bits (made monotone) above the
+//   complemented id -- exact;
+//   top-K by (score desc, id asc): the fp64 score's bits made monotone, with the
+//   lowest 7 bits replaced by 127 - (position in A).  Positions in A follow cell
+//   ids, so scores within 2^-45 (relative) of each other count as tied and go to
+//   the smaller id; the numerical error of any score is far larger than that.
+__device__ __forceinline__ uint64_t norm_key(float a, int32_t cell)
+{
+    uint32_t u = __float_as_uint(a);
+    u = (u >> 31) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - cell);
+}
+__device__ __forceinline__ uint64_t score_key(double sc, int pos)
+{
+    uint64_t u = (uint64_t)__double_as_longlong(sc);
+    u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+    return (u & ~(uint64_t)0x7f) | (uint64_t)(127 - pos);
+}
+
+// Number of keys in k[0 .. n8) (n8 a multiple of 8, entries past the live ones
+// zero) that are larger than `mine`: the rank of `mine` among distinct keys.
+__device__ __forceinline__ int count_greater(const uint64_t *k, int n8, uint64_t mine)
+{
+    int r = 0;
+    for (int x = 0; x < n8; x += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(k + x + e);
+            v[e] = ((uint64_t)w[1] << 32) | w[0];
+            v[e + 1] = ((uint64_t)w[3] << 32) | w[2];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            r += v[e] > mine ? 1 : 0;
+    }
+    return r;
+}
+
 struct Record {
     StateMeta *meta;
-    int32_t *ret, *cell, *flags;
+    int32_t *ridx, *cell, *flags;
     float *a, *kbar;
     char *k, *v;
 };
@@ -76,7 +118,7 @@ __device__ __forceinline__ Record record_at(char *state, const StateLayout &L, i
     char *rec = state + kStateHeaderBytes + bh * L.rec_bytes;
     Record R;
     R.meta = reinterpret_cast<StateMeta *>(rec);
-    R.ret = reinterpret_cast<int32_t *>(rec + L.off_ret);
+    R.ridx = reinterpret_cast<int32_t *>(rec + L.off_ridx);
     R.cell = reinterpret_cast<int32_t *>(rec + L.off_cell);
     R.flags = reinterpret_cast<int32_t *>(rec + L.off_flags);
     R.a = reinterpret_cast<float *>(rec + L.off_a);
@@ -171,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void state_build_kernel(char *__restrict_
         R.cell[x] = c;
         R.flags[x] = s_flags[x];
         R.a[x] = (c >= 0 && c < M) ? a[bh * M + c] : 0.0f;
-        R.ret[x] = x < n_A ? x : -1;
+        R.ridx[x] = x < n_A ? x : -1;
     }
     if (t == 0) {
         R.meta->pos = N;
@@ -205,9 +247,13 @@ __global__ __launch_bounds__(kThreads) void state_build_kernel(char *__restrict_
 }
 
 // ------------------------------------------------------------------------
-// One decode step.  Thread t owns half (t & 1) of slot t >> 1 while scoring,
-// so its 64 (or 32) fp32 mean-key values are loaded at entry, before the
-// position is known.
+// One decode step.  Latency, not bandwidth, bounds a step (one workgroup per
+// (sequence, head) moves ~100 KB), so the kernel is laid out as two memory
+// round trips with no dependent loads in between: (a) the header, position,
+// slot tables, token and every slot's mean key, all issued at entry (while
+// scoring, thread t owns half t & 1 of slot t >> 1); (b) the selected cells'
+// keys and values.  Ranks (Eq. 15 merge, top-K) are counted by every thread
+// at once over 64-bit integer keys in LDS; reductions run on the DPP network.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict__ state, StateLayout L,
                                                                StateHeader expect, HeadConsts hc,
@@ -218,32 +264,68 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
                                                                T *__restrict__ out, int32_t *__restrict__ sel,
                                                                int H, int K, int P, int W, float eps)
 {
-    __shared__ int32_t s_cell[kMaxSlots], s_flags[kMaxSlots], s_ret[kMaxSlots], s_tmp[kMaxSlots];
+    constexpr int EPC = 16 / (int)sizeof(T); // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;             // chunks per row
+    constexpr int RG = kWave / CPR;          // value rows per load step
+    constexpr int VR = kS / RG;              // value loads per lane
+    constexpr int HALF = D / 2;              // key features per lane (two lanes per token)
+    constexpr int FPT = D / 2;               // mean-key features per thread while scoring
+
+    __shared__ int32_t s_cell[kMaxSlots], s_flags[kMaxSlots], s_ridx[kMaxSlots];
+    __shared__ __attribute__((aligned(16))) int32_t s_kc[kMaxSlots]; // kept cell ids (merge), read 4 at a time
     __shared__ float s_a[kMaxSlots];
-    __shared__ double s_score[kMaxSlots];
+    __shared__ __attribute__((aligned(16))) uint64_t s_key[kMaxSlots]; // ranking keys (merge, then top-K)
+    __shared__ int32_t s_rc[kMaxSlots];   // cell ids, by position in A
+    __shared__ int32_t s_rslot[kMaxSlots];
     __shared__ float s_q[D];
     __shared__ T s_knew[D];
     __shared__ T s_vnew[D];
     __shared__ int32_t s_sel_slot[kKmax], s_sel_cell[kKmax];
-    __shared__ float s_logit[kKmax * kS];
-    __shared__ float s_p[kKmax * kS];
-    __shared__ float s_upart[kWaves][D];
+    __shared__ float s_upart[kWaves][RG * D]; // per wave and value-row group: partial P.V
+    __shared__ float s_m[kWaves], s_z[kWaves];
     __shared__ double s_colsum[kWaves][D];
     __shared__ double s_rowmax[kWaves];
     __shared__ float s_red[kWaves];
     __shared__ int32_t s_int[2];
-    __shared__ float s_z;
 
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
-    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    const int t = threadIdx.x, lane = t & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave); // wave-uniform, kept in a scalar register
     T *o_row = out + bh * D;
+    const Record R = record_at(state, L, bh); // in bounds: the host checked the buffer size
+    T *sk = reinterpret_cast<T *>(R.k);
+    T *sv = reinterpret_cast<T *>(R.v);
 
-    const StateHeader *hdr = reinterpret_cast<const StateHeader *>(state);
-    const bool valid = hdr->magic == kStateMagic && hdr->version == kStateVersion && hdr->batch == expect.batch &&
-                       hdr->H == expect.H && hdr->d == D && hdr->dtype == expect.dtype && hdr->P == P &&
-                       hdr->W == W && hdr->n_slots == L.S && hdr->rec_bytes == L.rec_bytes;
-    if (!valid) { // not a state of this shape: flag the output, leave the state alone
+    // ---- (a) entry loads: header, position, slot tables, token, mean keys ----
+    const StateHeader hv = *reinterpret_cast<const StateHeader *>(state);
+    const StateMeta mv = *R.meta;
+    if (t < kMaxSlots) {
+        const bool in = t < L.S;
+        s_cell[t] = in ? R.cell[t] : -1;
+        s_flags[t] = in ? R.flags[t] : 0;
+        s_a[t] = in ? R.a[t] : 0.0f;
+        s_ridx[t] = in ? R.ridx[t] : -1;
+    }
+    if (t < D) {
+        s_q[t] = elem_to_f32<T>(q[bh * D + t]);
+        s_knew[t] = k_new[bh * D + t];
+        s_vnew[t] = v_new[bh * D + t];
+    }
+    const int my_slot = t >> 1, my_part = t & 1;
+    float kb[FPT];
+    if (my_slot < L.S) {
+        load_row_f32<float, FPT>(R.kbar + (int64_t)my_slot * D + my_part * FPT, kb);
+    } else {
+#pragma unroll
+        for (int e = 0; e < FPT; ++e)
+            kb[e] = 0.0f;
+    }
+    const int bad = (int)(hv.magic != kStateMagic) | (int)(hv.version != kStateVersion) |
+                    (int)(hv.batch != expect.batch) | (int)(hv.H != expect.H) | (int)(hv.d != D) |
+                    (int)(hv.dtype != expect.dtype) | (int)(hv.P != P) | (int)(hv.W != W) |
+                    (int)(hv.n_slots != L.S) | (int)(hv.rec_bytes != L.rec_bytes);
+    if (bad) { // not a state of this shape: flag the output, leave the state alone
         if (t < D) {
             if constexpr (sizeof(T) == 2)
                 o_row[t] = (T)0x7fc0u; // bf16 quiet NaN
@@ -254,45 +336,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
             sel[bh * K + t] = -1;
         return;
     }
-    const Record R = record_at(state, L, bh);
-    T *sk = reinterpret_cast<T *>(R.k);
-    T *sv = reinterpret_cast<T *>(R.v);
-
-    // ---- entry loads: position, slot tables, token, mean keys ----
-    const int64_t i = R.meta->pos;
-    int n_ret = R.meta->n_ret;
-    n_ret = n_ret < 0 ? 0 : (n_ret > L.S ? L.S : n_ret);
-    int cur = R.meta->cur_slot;
-    if (t < kMaxSlots) {
-        const bool in = t < L.S;
-        s_cell[t] = in ? R.cell[t] : -1;
-        s_flags[t] = in ? R.flags[t] : 0;
-        s_a[t] = in ? R.a[t] : 0.0f;
-        s_ret[t] = in ? R.ret[t] : -1;
-    }
-    if (t < D) {
-        s_q[t] = elem_to_f32<T>(q[bh * D + t]);
-        s_knew[t] = k_new[bh * D + t];
-        s_vnew[t] = v_new[bh * D + t];
-    }
-    constexpr int FPT = D / 2; // mean-key features per thread
-    const int my_slot = t >> 1, my_part = t & 1;
-    float kb[FPT];
-    if (my_slot < L.S) {
-        const float *src = R.kbar + (int64_t)my_slot * D + my_part * FPT;
-#pragma unroll
-        for (int e = 0; e < FPT; e += 4) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(src + e);
-            kb[e] = __uint_as_float(w[0]);
-            kb[e + 1] = __uint_as_float(w[1]);
-            kb[e + 2] = __uint_as_float(w[2]);
-            kb[e + 3] = __uint_as_float(w[3]);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < FPT; ++e)
-            kb[e] = 0.0f;
-    }
+    const int64_t i = mv.pos;
+    int n_ret = mv.n_ret < 0 ? 0 : (mv.n_ret > L.S ? L.S : mv.n_ret);
+    int cur = mv.cur_slot;
     __syncthreads();
 
     const int64_t beta = i / kB;
@@ -303,42 +349,43 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     if (i % kB == 0 && i > 0) {
         const int64_t d_lo = (beta - 1) * kCpb, d_hi = beta * kCpb;
         const int64_t rec_lo = d_hi > W ? d_hi - W : 0;
+        const int S8 = (L.S + 7) & ~7;
         int32_t c = -1;
-        float av = 0.0f;
         bool cand = false;
-        if (t < L.S) {
+        uint64_t my = 0;
+        if (t < kMaxSlots) {
             c = s_cell[t];
-            av = s_a[t];
             cand = c >= 0 && ((s_flags[t] & kFlagTop) || (c >= d_lo && c < d_hi));
+            my = cand ? norm_key(s_a[t], c) : 0;
+            s_key[t] = my;
         }
-        if (t < kMaxSlots)
-            s_tmp[t] = cand ? 1 : 0;
         __syncthreads();
-        int rank = 0;
-        if (cand)
-            for (int u = 0; u < L.S; ++u)
-                rank += (s_tmp[u] && ranks_before(s_a[u], s_cell[u], av, c)) ? 1 : 0;
-        const bool top = cand && rank < P;
+        // rank among TopP(C) u D by (a desc, id asc)
+        const bool top = cand && count_greater(s_key, S8, my) < P;
         const bool keep = c >= 0 && (top || (c >= rec_lo && c < d_hi));
-        __syncthreads();
         if (t < kMaxSlots) {
             s_flags[t] = top ? kFlagTop : 0;
             s_cell[t] = keep ? c : -1;
-            s_tmp[t] = keep ? 1 : 0;
-            s_ret[t] = -1;
+            s_kc[t] = keep ? c : INT_MAX;
         }
         __syncthreads();
-        if (keep) {
-            int pos = 0;
-            for (int u = 0; u < L.S; ++u)
-                pos += (s_tmp[u] && s_cell[u] < c) ? 1 : 0;
-            s_ret[pos] = t;
+        int pos = -1;
+        if (keep) { // position in A: kept cells with a smaller id
+            pos = 0;
+            for (int u = 0; u < S8; u += 4) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(&s_kc[u]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pos += (int32_t)w[e] < c ? 1 : 0;
+            }
         }
+        if (t < kMaxSlots)
+            s_ridx[t] = pos;
         n_ret = __syncthreads_count(keep);
         if (t < L.S) {
             R.cell[t] = s_cell[t];
             R.flags[t] = s_flags[t];
-            R.ret[t] = s_ret[t];
+            R.ridx[t] = pos;
         }
         if (t == 0)
             R.meta->n_ret = n_ret;
@@ -346,25 +393,13 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
 
     // ---- (2) append the token; a new cell takes the lowest free slot ----
     if (r == 0) {
-        if (wave == 0) {
-            int found = -1;
-            for (int base = 0; base < L.S; base += kWave) {
-                const int x = base + lane;
-                const uint64_t m = __ballot(x < L.S && s_cell[x] < 0);
-                if (m) {
-                    found = base + __ffsll((unsigned long long)m) - 1;
-                    break;
-                }
-            }
-            if (lane == 0)
-                s_int[0] = found;
-        }
-        __syncthreads();
-        cur = s_int[0];
+        const uint64_t f0 = __ballot(lane < L.S && s_cell[lane] < 0);
+        const uint64_t f1 = __ballot(lane + kWave < L.S && s_cell[lane + kWave] < 0);
+        cur = f0 ? __ffsll((unsigned long long)f0) - 1 : (f1 ? kWave + __ffsll((unsigned long long)f1) - 1 : -1);
         if (t == 0 && cur >= 0) {
-            s_cell[cur] = (int32_t)c_new;
             R.cell[cur] = (int32_t)c_new;
             R.flags[cur] = 0;
+            R.ridx[cur] = -1;
             R.meta->cur_slot = cur;
         }
     }
@@ -419,140 +454,126 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
         if (t == 0)
             R.a[cur] = (float)sqrt(fmax(fmax(s_rowmax[0], s_rowmax[1]), fmax(s_rowmax[2], s_rowmax[3])));
     }
-    __syncthreads();
 
-    // ---- (3) Eq. 7 over A in fp64, rank-based top-K ----
-    if (t < kMaxSlots)
-        s_tmp[t] = -1;
-    if (t < kKmax) { // every rank below min(K, |A|) is written below; slot 0 keeps reads in bounds regardless
-        s_sel_slot[t] = 0;
-        s_sel_cell[t] = -1;
-    }
-    __syncthreads();
-    if (t < n_ret && t < L.S) {
-        const int u = s_ret[t];
-        if (u >= 0 && u < L.S)
-            s_tmp[u] = t;
-    }
-    __syncthreads();
-    const bool scored = my_slot < L.S && s_tmp[my_slot] >= 0;
+    // ---- (3) Eq. 7 over A in fp64 ----
+    const int ri = my_slot < L.S ? s_ridx[my_slot] : -1;
+    const bool scored = ri >= 0 && ri < n_ret;
     double dot = 0.0;
     if (scored) {
+        double part4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int e = 0; e < FPT; ++e)
-            dot = fma((double)s_q[my_part * FPT + e], (double)kb[e], dot);
+            part4[e & 3] = fma((double)s_q[my_part * FPT + e], (double)kb[e], part4[e & 3]);
+        dot = (part4[0] + part4[1]) + (part4[2] + part4[3]);
     }
     dot += shfl_xor_d(dot, 1);
     if (scored && my_part == 0) {
         const int32_t c = s_cell[my_slot];
         const double delta = (double)i - ((double)c + 0.5) * kS;
         const double g = erf(delta / (2.0 * (double)hc.sigma[h]));
-        s_score[my_slot] = dot / sqrt((double)D) + (double)hc.lambda[h] * (double)s_a[my_slot] * g;
+        s_key[ri] = score_key(dot / sqrt((double)D) + (double)hc.lambda[h] * (double)s_a[my_slot] * g, ri);
+        s_rc[ri] = c;
+        s_rslot[ri] = my_slot;
+    }
+    const int n8 = (n_ret + 7) & ~7;
+    if (t >= n_ret && t < n8)
+        s_key[t] = 0; // padding ranks last
+    if (t < kKmax) { // every rank below min(K, |A|) is written below; slot 0 keeps reads in bounds regardless
+        s_sel_slot[t] = 0;
+        s_sel_cell[t] = -1;
     }
     __syncthreads();
-    if (scored && my_part == 0) {
-        const double sc = s_score[my_slot];
-        const int32_t c = s_cell[my_slot];
-        int rank = 0;
-        for (int x = 0; x < n_ret; ++x) {
-            const int u = s_ret[x];
-            if (u < 0 || u >= L.S)
-                continue;
-            const double su = s_score[u];
-            const int32_t cu = s_cell[u];
-            rank += (su > sc || (su == sc && cu < c)) ? 1 : 0;
-        }
+
+    // ---- top-K by rank (score desc, id asc) ----
+    if (t < n_ret) {
+        const int rank = count_greater(s_key, n8, s_key[t]);
         if (rank < K) {
-            s_sel_slot[rank] = my_slot;
-            s_sel_cell[rank] = c;
+            const int slot = s_rslot[t];
+            s_sel_slot[rank] = slot >= 0 && slot < L.S ? slot : 0;
+            s_sel_cell[rank] = s_rc[t];
         }
     }
     const int nT = n_ret < K ? n_ret : K;
     __syncthreads();
 
-    // ---- readout: wave w gathers selections w, w + 4 ----
-    constexpr int HALF = D / 2;  // key features per lane (two lanes per token)
-    constexpr int FV = D / 64;   // value features per lane
+    // ---- (b) readout: wave w gathers selections w, w + 4 with a running softmax ----
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    float vpre[kS][FV];
-    const int j0 = wave;
-    if (j0 < nT) {
-        const int slot = s_sel_slot[j0];
-        const T *vb = sv + (int64_t)slot * kS * D + lane * FV;
+    const int vrow0 = lane / CPR, vch = lane % CPR;
+    float m_w = -INFINITY, z_w = 0.0f;
+    float acc[EPC];
 #pragma unroll
-        for (int row = 0; row < kS; ++row)
-#pragma unroll
-            for (int e = 0; e < FV; ++e)
-                vpre[row][e] = elem_to_f32<T>(vb[(int64_t)row * D + e]);
-    }
+    for (int e = 0; e < EPC; ++e)
+        acc[e] = 0.0f;
     for (int j = wave; j < nT; j += kWaves) {
         const int slot = s_sel_slot[j];
+        const T *kc = sk + (int64_t)slot * kS * D;
+        const T *vc = sv + (int64_t)slot * kS * D;
+        u32x4 vraw[VR];
+#pragma unroll
+        for (int x = 0; x < VR; ++x)
+            vraw[x] = *reinterpret_cast<const u32x4 *>(vc + (int64_t)(vrow0 + RG * x) * D + vch * EPC);
         float kr[HALF];
-        load_row_f32<T, HALF>(sk + ((int64_t)slot * kS + (lane >> 1)) * D + (lane & 1) * HALF, kr);
-        float d0 = 0.0f;
+        load_row_f32<T, HALF>(kc + (int64_t)(lane >> 1) * D + (lane & 1) * HALF, kr);
+        float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int e = 0; e < HALF; ++e)
-            d0 = fmaf(s_q[(lane & 1) * HALF + e], kr[e], d0);
-        d0 += shfl_xor_f(d0, 1);
-        if ((lane & 1) == 0)
-            s_logit[j * kS + (lane >> 1)] = d0 * inv_sqrt_d;
-    }
-    __syncthreads();
-    float m = -INFINITY;
-    for (int x = lane; x < nT * kS; x += kWave)
-        m = fmaxf(m, s_logit[x]);
+            lp[e & 3] = fmaf(s_q[(lane & 1) * HALF + e], kr[e], lp[e & 3]);
+        float l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+        l = (l + dpp_f<0xB1>(l)) * inv_sqrt_d; // logit of token lane / 2, on both lanes of the pair
+        const float m_new = fmaxf(m_w, wave_max_f(l));
+        const float scale = expf(m_w - m_new); // 0 on the wave's first cell
+        const float p = expf(l - m_new);
+        z_w = z_w * scale + wave_sum_f((lane & 1) ? 0.0f : p);
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1)
-        m = fmaxf(m, shfl_xor_f(m, o));
-    for (int x = t; x < nT * kS; x += kThreads)
-        s_p[x] = expf(s_logit[x] - m);
-    __syncthreads();
-    if (wave == 0) {
-        float z = 0.0f;
-        for (int x = lane; x < nT * kS; x += kWave)
-            z += s_p[x];
+        for (int e = 0; e < EPC; ++e)
+            acc[e] *= scale;
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1)
-            z += shfl_xor_f(z, o);
-        if (lane == 0)
-            s_z = z;
-    }
-    float uacc[FV];
+        for (int x = 0; x < VR; ++x) {
+            const float pr = __shfl(p, 2 * (vrow0 + RG * x), kWave);
+            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int e = 0; e < FV; ++e)
-        uacc[e] = 0.0f;
-    if (j0 < nT) {
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] = fmaf(pr, bf16_bits_to_f32(vraw[x][e] & 0xffffu), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(pr, bf16_bits_to_f32(vraw[x][e] >> 16), acc[2 * e + 1]);
+                }
+            } else {
 #pragma unroll
-        for (int row = 0; row < kS; ++row) {
-            const float p = s_p[j0 * kS + row];
-#pragma unroll
-            for (int e = 0; e < FV; ++e)
-                uacc[e] = fmaf(p, vpre[row][e], uacc[e]);
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = fmaf(pr, __uint_as_float(vraw[x][e]), acc[e]);
+            }
         }
-    }
-    for (int j = wave + kWaves; j < nT; j += kWaves) {
-        const int slot = s_sel_slot[j];
-        const T *vb = sv + (int64_t)slot * kS * D + lane * FV;
-        for (int row = 0; row < kS; ++row) {
-            const float p = s_p[j * kS + row];
-#pragma unroll
-            for (int e = 0; e < FV; ++e)
-                uacc[e] = fmaf(p, elem_to_f32<T>(vb[(int64_t)row * D + e]), uacc[e]);
-        }
+        m_w = m_new;
     }
 #pragma unroll
-    for (int e = 0; e < FV; ++e)
-        s_upart[wave][lane * FV + e] = uacc[e];
+    for (int e = 0; e < EPC; ++e)
+        s_upart[wave][vrow0 * D + vch * EPC + e] = acc[e];
+    if (lane == 0) {
+        s_m[wave] = m_w;
+        s_z[wave] = z_w;
+    }
     __syncthreads();
 
-    // ---- normalise, RMSNorm over d (Eq. 17), write ----
+    // ---- combine the waves and row groups, normalise, RMSNorm over d (Eq. 17), write ----
     float u = 0.0f;
-    if (t < D && nT > 0)
-        u = ((s_upart[0][t] + s_upart[1][t]) + (s_upart[2][t] + s_upart[3][t])) / s_z;
-    float sq = t < D ? u * u : 0.0f;
+    if (t < D && nT > 0) {
+        float M = s_m[0];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1)
-        sq += shfl_xor_f(sq, o);
+        for (int w = 1; w < kWaves; ++w)
+            M = fmaxf(M, s_m[w]);
+        float Z = 0.0f, U = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = s_m[w] == -INFINITY ? 0.0f : expf(s_m[w] - M);
+            float uw = 0.0f;
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+                uw += s_upart[w][g * D + t];
+            Z = fmaf(s_z[w], f, Z);
+            U = fmaf(uw, f, U);
+        }
+        u = U / Z;
+    }
+    const float sq = wave_sum_f(t < D ? u * u : 0.0f);
     if (lane == 0)
         s_red[wave] = sq;
     __syncthreads();
