@@ -111,6 +111,7 @@ def main() -> int:
     b, H, N, d = q.shape
     M, NB, cap = N // prm.s, (N + prm.B - 1) // prm.B, prm.P + prm.W
     kbar = torch.empty(b, H, M, d, dtype=torch.float32, device=dev)
+    kbar_split = torch.empty(b, H, M, 3, d, dtype=torch.int16, device=dev) if w.dtype == "bf16" else None
     a = torch.empty(b, H, M, dtype=torch.float32, device=dev)
     sh = fsl.shape_of(k)
     ws = torch.empty(max(1, fsl.fs_prune_workspace_bytes(sh, prm)), dtype=torch.uint8, device=dev)
@@ -120,40 +121,38 @@ def main() -> int:
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    names = ["cell_summaries", "prune", "score_topk", "readout"]
+    names = ["cell_summaries", "prune", "route_readout"]
 
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        fsl.fs_cell_summaries(k, kbar, a, prm)
+        fsl.fs_cell_summaries(k, kbar, a, prm, kbar_split=kbar_split)
         if evs is not None:
             evs[1].record(stream)
         if prm.prune:
             fsl.fs_prune_retained(sh, a, retained, n_ret, ws, prm)
         if evs is not None:
             evs[2].record(stream)
-        fsl.fs_score_select(q, kbar, a, retained if prm.prune else None, n_ret if prm.prune else None,
-                            sigma, lam, sel, prm)
+        # scores, top-K and the gather-readout: one kernel for bf16 (fs_score_select + fs_readout otherwise)
+        fsl.fs_select_readout(q, k, v, kbar, a, retained if prm.prune else None, n_ret if prm.prune else None,
+                              sigma, lam, None, out, sel, prm, kbar_split=kbar_split)
         if evs is not None:
             evs[3].record(stream)
-        fsl.fs_readout(q, k, v, sel, None, out, prm)
-        if evs is not None:
-            evs[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for s_ in range(args.steps):
         step(evs[s_])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    gpu_ms = sum(evs[s_][0].elapsed_time(evs[s_][4]) for s_ in range(args.steps))
+    gpu_ms = sum(evs[s_][0].elapsed_time(evs[s_][len(names)]) for s_ in range(args.steps))
     per_kernel_ms = {names[i]: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]))
-                     for i in range(4)}
+                     for i in range(len(names))}
     ms_per_step = wall * 1e3 / args.steps
     value = b * N * args.steps / wall
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step wall, {gpu_ms / args.steps:.3f} ms/step events; "
@@ -193,12 +192,15 @@ def main() -> int:
         A_sizes = np.broadcast_to(np.minimum(np.arange(NB) * (prm.B // prm.s), M), (b, H, NB)).astype(np.int64)
     score_flop = float(2 * prm.B * d * A_sizes.sum())
     read_flop = float(4 * prm.s * d * np.count_nonzero(sel_h >= 0))
+    # algorithmic bytes: each input read once, each output written once, the summaries (and their bf16 parts)
+    # read once per head, and the keys/values of every block's distinct selected cells once per block
     alg = {
-        "cell_summaries": dict(bytes=qkv_bytes + b * H * M * (d + 1) * 4),
+        "cell_summaries": dict(bytes=qkv_bytes + b * H * M * (d + 1) * 4 + (b * H * M * 3 * d * 2 if esz == 2 else 0)),
         "prune": dict(bytes=b * H * M * 4 * 2 + b * H * NB * (cap + 1) * 4 if prm.prune else 0),
-        "score_topk": dict(bytes=qkv_bytes + b * H * M * (d + 1) * 4 + b * H * N * prm.K * 4, flop=score_flop),
-        "readout": dict(bytes=2 * qkv_bytes + b * H * N * prm.K * 4 + int(U.sum()) * cell_kv_bytes,
-                        flop=read_flop),
+        "route_readout": dict(bytes=2 * qkv_bytes + b * H * M * (d * (6 if esz == 2 else 4) + 4)
+                              + (b * H * NB * (cap + 1) * 4 if prm.prune else 0) + b * H * N * prm.K * 4
+                              + int(U.sum()) * cell_kv_bytes,
+                              flop=score_flop + read_flop),
     }
     kernels = {}
     for nm in names:

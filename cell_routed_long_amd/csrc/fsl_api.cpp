@@ -15,7 +15,7 @@ namespace fsl {
 namespace {
 
 constexpr int64_t kMaxTokens = int64_t(1) << 22; // LDS union bitmap of the readout: N/32 bits <= 16 KB
-constexpr int kMaxRetained = 1024;               // P + W
+constexpr int kMaxRetained = kMaxRetainedCap;    // P + W
 constexpr int kMaxK = 8;
 constexpr size_t kAlign = 256;
 
@@ -76,7 +76,7 @@ Geometry geometry(const fs_shape *sh, const fs_params *p)
 
 // Workspace of fs_longrange_prefill, carved in this order (256-byte aligned).
 struct PrefillLayout {
-    size_t kbar, a, death, retained, n_ret, sel, total;
+    size_t kbar, ksplit, a, death, retained, n_ret, sel, total;
 };
 
 PrefillLayout prefill_layout(const Geometry &g)
@@ -85,6 +85,8 @@ PrefillLayout prefill_layout(const Geometry &g)
     size_t off = 0;
     L.kbar = off;
     off += align_up((size_t)g.bh * g.M * g.d * sizeof(float));
+    L.ksplit = off; // bf16 parts of kbar for the scorer (bf16 shapes)
+    off += g.bf16 ? align_up((size_t)g.bh * g.M * 3 * g.d * sizeof(uint16_t)) : 0;
     L.a = off;
     off += align_up((size_t)g.bh * g.M * sizeof(float));
     L.death = off;
@@ -208,7 +210,7 @@ FSL_EXPORT const char *fs_status_string(fs_status status)
 }
 
 FSL_EXPORT fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *prm, const void *k, float *kbar,
-                                       float *a, void *stream)
+                                       float *a, uint16_t *kbar_split, void *stream)
 {
     fs_status st = check_all(shape, prm);
     if (st != FS_OK)
@@ -216,7 +218,8 @@ FSL_EXPORT fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *p
     const Geometry g = geometry(shape, prm);
     if (!k || ((!kbar || !a) && g.M > 0)) // no complete cell: nothing to write
         return FS_ERR_INVALID;
-    return hip_status(launch_cell_summaries(g, k, kbar, a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_cell_summaries(g, k, kbar, a, g.bf16 ? kbar_split : nullptr,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 FSL_EXPORT size_t fs_prune_workspace_bytes(const fs_shape *shape, const fs_params *prm)
@@ -244,8 +247,9 @@ FSL_EXPORT fs_status fs_prune_retained(const fs_shape *shape, const fs_params *p
 }
 
 FSL_EXPORT fs_status fs_score_select(const fs_shape *shape, const fs_params *prm, const void *q, const float *kbar,
-                                     const float *a, const int32_t *retained, const int32_t *n_retained,
-                                     const float *sigma_h, const float *lambda_h, int32_t *sel, void *stream)
+                                     const uint16_t *kbar_split, const float *a, const int32_t *retained,
+                                     const int32_t *n_retained, const float *sigma_h, const float *lambda_h,
+                                     int32_t *sel, void *stream)
 {
     fs_status st = check_all(shape, prm);
     if (st != FS_OK)
@@ -257,8 +261,9 @@ FSL_EXPORT fs_status fs_score_select(const fs_shape *shape, const fs_params *prm
     const Geometry g = geometry(shape, prm);
     if (!q || !sel || ((!kbar || !a) && g.M > 0) || (g.prune && (!retained || !n_retained)))
         return FS_ERR_INVALID;
-    return hip_status(launch_score_topk(g, hc, q, kbar, a, g.prune ? retained : nullptr,
-                                        g.prune ? n_retained : nullptr, sel, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_score_topk(g, hc, q, kbar, g.bf16 ? kbar_split : nullptr, a,
+                                        g.prune ? retained : nullptr, g.prune ? n_retained : nullptr, sel,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 FSL_EXPORT fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
@@ -271,6 +276,36 @@ FSL_EXPORT fs_status fs_readout(const fs_shape *shape, const fs_params *prm, con
         return FS_ERR_INVALID;
     const Geometry g = geometry(shape, prm);
     return hip_status(launch_readout(g, q, k, v, sel, gain, out, static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT fs_status fs_select_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
+                                       const void *v, const float *kbar, const uint16_t *kbar_split, const float *a,
+                                       const int32_t *retained, const int32_t *n_retained, const float *sigma_h,
+                                       const float *lambda_h, const float *gain, void *out, int32_t *sel,
+                                       void *stream)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(shape->H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    const Geometry g = geometry(shape, prm);
+    if (!q || !k || !v || !out || ((!kbar || !a) && g.M > 0) || (g.prune && (!retained || !n_retained)))
+        return FS_ERR_INVALID;
+    const bool fused = g.bf16 && kbar_split && (!g.prune || g.cap <= kFusedMaxCap);
+    if (!fused && !sel)
+        return FS_ERR_INVALID; // the two-kernel path passes the selections through `sel`
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t *ret = g.prune ? retained : nullptr;
+    const int32_t *nr = g.prune ? n_retained : nullptr;
+    if (fused)
+        return hip_status(launch_route_readout(g, hc, q, k, v, kbar_split, a, ret, nr, gain, out, sel, s));
+    hipError_t e = launch_score_topk(g, hc, q, kbar, g.bf16 ? kbar_split : nullptr, a, ret, nr, sel, s);
+    if (e == hipSuccess)
+        e = launch_readout(g, q, k, v, sel, gain, out, s);
+    return hip_status(e);
 }
 
 FSL_EXPORT size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm)
@@ -315,6 +350,7 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
 
     char *ws = static_cast<char *>(workspace);
     float *kbar = reinterpret_cast<float *>(ws + L.kbar);
+    uint16_t *ksplit = g.bf16 ? reinterpret_cast<uint16_t *>(ws + L.ksplit) : nullptr;
     float *a = reinterpret_cast<float *>(ws + L.a);
     int32_t *death = reinterpret_cast<int32_t *>(ws + L.death);
     int32_t *retained = reinterpret_cast<int32_t *>(ws + L.retained);
@@ -323,14 +359,20 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     const bool route = out || sel; // state-only calls skip scoring and readout
-    hipError_t e = launch_cell_summaries(g, k, kbar, a, s);
+    hipError_t e = launch_cell_summaries(g, k, kbar, a, route ? ksplit : nullptr, s);
     if (e == hipSuccess && g.prune)
         e = launch_prune(g, a, death, retained, n_ret, route ? 1 : 0, s);
-    if (e == hipSuccess && route)
-        e = launch_score_topk(g, hc, q, kbar, a, g.prune ? retained : nullptr, g.prune ? n_ret : nullptr, sel_buf,
-                              s);
-    if (e == hipSuccess && out)
-        e = launch_readout(g, q, k, v, sel_buf, gain, out, s);
+    const bool fused = out && g.bf16 && (!g.prune || g.cap <= kFusedMaxCap);
+    if (e == hipSuccess && fused) {
+        e = launch_route_readout(g, hc, q, k, v, ksplit, a, g.prune ? retained : nullptr, g.prune ? n_ret : nullptr,
+                                 gain, out, sel, s);
+    } else {
+        if (e == hipSuccess && route)
+            e = launch_score_topk(g, hc, q, kbar, ksplit, a, g.prune ? retained : nullptr,
+                                  g.prune ? n_ret : nullptr, sel_buf, s);
+        if (e == hipSuccess && out)
+            e = launch_readout(g, q, k, v, sel_buf, gain, out, s);
+    }
     if (e == hipSuccess && state) {
         const StateLayout SL = state_layout(g.d, shape->dtype, prm);
         const StateHeader hdr = state_header(shape->batch, shape->H, g.d, shape->dtype, prm, SL);

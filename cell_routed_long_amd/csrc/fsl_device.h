@@ -133,6 +133,55 @@ __device__ __forceinline__ float wave_max_f(float x)
     return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
+// ---- XCD-aware block order ---------------------------------------------------
+// The dispatcher deals workgroups round-robin over the 8 XCDs (each with its own
+// L2).  Renumbering the linear workgroup id so that XCD x receives the x-th
+// contiguous run of logical blocks keeps the blocks of one head (which share
+// its mean keys and its most-selected cells) on one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t w, int64_t total)
+{
+    const int64_t per = (total + kXcds - 1) / kXcds; // blocks on the fuller XCDs
+    const int64_t full = total - (per - 1) * kXcds;  // XCDs that receive `per` blocks
+    const int64_t xcd = w % kXcds, idx = w / kXcds;
+    return xcd < full ? xcd * per + idx : full * per + (xcd - full) * (per - 1) + idx;
+}
+
+// Round x0, x1 to bf16 (nearest even, hardware conversion) and pack them.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float x0, float x1)
+{
+    const bf16x2 v = {(__bf16)x0, (__bf16)x1};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- coalesced tile transfers through LDS (bf16, 128 rows) -------------------
+// A workgroup's 128 query rows are one contiguous span of global memory, while
+// the matrix-core layouts give each lane one row.  Moving a tile through LDS
+// with 16-byte accesses by consecutive threads makes every wave instruction
+// touch 4 whole rows instead of 32 partial ones.  Rows at or past `rows` are
+// zero-filled on load and skipped on store.  stride: LDS row pitch in elements.
+template <int D, int NT>
+__device__ __forceinline__ void tile_load_bf16(uint16_t *lds, int stride, const uint16_t *__restrict__ g, int rows)
+{
+    constexpr int CPR = D / 8; // 16-byte chunks per row
+    for (int c = threadIdx.x; c < 128 * CPR; c += NT) {
+        const int r = c / CPR, c8 = (c % CPR) * 8;
+        const u32x4 w = r < rows ? *reinterpret_cast<const u32x4 *>(g + (int64_t)r * D + c8) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(lds + r * stride + c8) = w;
+    }
+}
+template <int D, int NT>
+__device__ __forceinline__ void tile_store_bf16(uint16_t *__restrict__ g, const uint16_t *lds, int stride, int rows)
+{
+    constexpr int CPR = D / 8;
+    for (int c = threadIdx.x; c < 128 * CPR; c += NT) {
+        const int r = c / CPR, c8 = (c % CPR) * 8;
+        if (r < rows)
+            *reinterpret_cast<u32x4 *>(g + (int64_t)r * D + c8) = *reinterpret_cast<const u32x4 *>(lds + r * stride + c8);
+    }
+}
+
 // Per-head routing constants, passed by value with every launch.
 struct HeadConsts {
     float inv_two_sigma[128]; // 1 / (2 sigma_h)

@@ -8,6 +8,8 @@
 
 namespace fsl {
 
+constexpr int kMaxRetainedCap = 1024; // largest P + W accepted by the ABI
+
 // Geometry every kernel shares (derived and validated by the ABI layer).
 struct Geometry {
     int32_t bh;        // batch * H
@@ -22,19 +24,30 @@ struct Geometry {
     float eps;
 };
 
-hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, hipStream_t st);
+// kbar_split (optional): [bh, M, 3, d] bf16 hi/mid/lo parts of kbar.
+hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split,
+                                 hipStream_t st);
 
 // death[c]: first query block whose TopP no longer holds cell c (INT32_MAX: never leaves).
 // emit = 0 computes only the exit blocks (enough to build a decode state).
 hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32_t *retained,
                         int32_t *n_ret, int emit, hipStream_t st);
 
+// kbar_split (optional, bf16 only): the parts written by launch_cell_summaries.
 hipError_t launch_score_topk(const Geometry &g, const HeadConsts &hc, const void *q, const float *kbar,
-                             const float *a, const int32_t *retained, const int32_t *n_ret, int32_t *sel,
-                             hipStream_t st);
+                             const uint16_t *kbar_split, const float *a, const int32_t *retained,
+                             const int32_t *n_ret, int32_t *sel, hipStream_t st);
 
 hipError_t launch_readout(const Geometry &g, const void *q, const void *k, const void *v,
                           const int32_t *sel, const float *gain, void *out, hipStream_t st);
+
+// Routing and readout of every 128-query block in one launch (bf16 only; the
+// retained lists at most kFusedMaxCap long).  sel may be NULL.
+constexpr int kFusedMaxCap = 256;
+hipError_t launch_route_readout(const Geometry &g, const HeadConsts &hc, const void *q, const void *k,
+                                const void *v, const uint16_t *kbar_split, const float *a,
+                                const int32_t *retained, const int32_t *n_ret, const float *gain, void *out,
+                                int32_t *sel, hipStream_t st);
 
 // Decode state of every (sequence, head) for continuing at position g.N, from
 // the prefill's summaries (kbar, a), exit blocks (death) and raw keys/values.

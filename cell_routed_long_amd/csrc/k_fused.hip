@@ -1,0 +1,494 @@
+// Routing and readout of one 128-query block in a single launch (FreeSolo,
+// Sec. 3.3 "Cell scoring" Eq. 7, "Per-query selection", "Token readout" Eq. 9,
+// App. D.2 Eq. 17), for bf16 tensors.
+//
+// The separate scorer and readout kernels each wait on a chain of dependent
+// memory round trips per block (count -> retained list -> mean keys; stored
+// selections -> union -> cells) with little work in flight, and both read the
+// block's queries.  Here one workgroup does both steps for its block:
+//   entry     the query fragments (kept in registers for both matrix products),
+//             |A_beta| and the retained list are requested together;
+//   routing   the retained mean keys (bf16 hi/mid/lo parts from the summary
+//             pass) are staged 32 cells at a time, the next tile in flight
+//             while the matrix cores score the current one; each lane keeps its
+//             query's top-K in registers, exactly as fs_score_select does;
+//   union     the selections go to LDS (and, if asked, to global memory) and
+//             the block's distinct selected cells are listed in id order;
+//   readout   each listed cell's keys and values are gathered once and applied
+//             to every query of the block on the matrix cores with the running
+//             softmax, exactly as fs_readout does; the next cell is in flight
+//             while the current one is on the matrix cores;
+//   epilogue  RMSNorm, then the block's output tile goes out through LDS with
+//             coalesced 16-byte stores.
+// The arithmetic is the same as the two separate kernels, so the results are
+// bitwise those of fs_score_select followed by fs_readout.
+#include "fsl_internal.h"
+
+#include <climits>
+
+namespace fsl {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLazy = 8.0f; // the softmax running max moves only when it grows by more than 2^8
+
+template <int D>
+struct alignas(16) FusedSmem {
+    static constexpr int kStride = D + 8;   // bf16 elements per row (16-byte pad against bank conflicts)
+    static constexpr int kStrideV = 32 + 4; // bf16 elements per V^T row
+    union {
+        uint16_t kb[3][32][kStride]; // routing: one tile of mean-key parts
+        struct {                     // readout: one cell
+            uint16_t k[32][kStride];
+            uint16_t vt[D][kStrideV];
+        };
+        uint16_t tile[128][kStride]; // epilogue: the block's output tile
+    };
+    float prior[32];
+    float pc[32];
+    int32_t id[32];
+};
+
+// The ranking (score desc, id asc) as one order-preserving 64-bit key: the
+// score's bits made monotone above 0x7fffffff - id.  A larger key ranks
+// first; 0 marks an empty entry (every real key is larger).
+__device__ __forceinline__ uint64_t rank_key(float score, uint32_t low)
+{
+    uint32_t u = __float_as_uint(score + 0.0f); // -0 -> +0: equal scores must tie
+    u ^= (uint32_t)((int32_t)u >> 31) | 0x80000000u;
+    return ((uint64_t)u << 32) | low;
+}
+
+// Insert key into the descending list kl of KT keys (a select network: a key
+// below the last entry moves nothing).
+template <int KT>
+__device__ __forceinline__ void insert_key(uint64_t (&kl)[KT], uint64_t key)
+{
+#pragma unroll
+    for (int j = KT - 1; j > 0; --j)
+        kl[j] = key > kl[j - 1] ? kl[j - 1] : (key > kl[j] ? key : kl[j]);
+    kl[0] = key > kl[0] ? key : kl[0];
+}
+
+template <int D, int KT>
+__global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ kbar_split, const float *__restrict__ a, const int32_t *__restrict__ retained,
+    const int32_t *__restrict__ n_ret, const float *__restrict__ gain, uint16_t *__restrict__ out,
+    int32_t *__restrict__ sel, int64_t N, int64_t M, int NB, int cap, int prune, int H, int s,
+    int cells_per_block, float eps, HeadConsts hc)
+{
+    __shared__ FusedSmem<D> sm;
+    __shared__ int32_t s_A[kFusedMaxCap];
+    __shared__ int32_t sel_s[128][KT];
+    __shared__ int32_t ulist[128 * KT];
+    __shared__ int32_t n_u;
+    extern __shared__ uint32_t bitmap[]; // ceil(M / 32) words
+
+    constexpr int PER = D / 8;  // mean-key elements staged per thread and tile
+    constexpr int SCH = PER / 8; // 16-byte chunks per part and thread
+    constexpr int KC = D / 16;  // k-steps of the bf16 matrix products
+    const int64_t lb = xcd_logical_block(blockIdx.x, (int64_t)gridDim.x);
+    const int beta = (int)(lb % NB);
+    const int64_t head = lb / NB;
+    const int h = (int)(head % H);
+    const int t = threadIdx.x;
+    const int wave = t / kWave;
+    const int lane = t & (kWave - 1);
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    const int64_t q0 = (int64_t)beta * 128;
+    const int64_t qi = q0 + wave * 32 + col; // this lane's query position
+    const bool q_ok = qi < N;
+    const float qpos = (float)qi; // exact: N <= 2^22
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D); // readout logits in the exp2 domain
+    const float inv2s = hc.inv_two_sigma[h];
+    const float lam = hc.lambda[h];
+
+    int64_t n_avail = (int64_t)beta * cells_per_block;
+    if (n_avail > M)
+        n_avail = M;
+
+    // ---- entry: |A|, the retained list and the query fragments, all at once ----
+    const int nA = prune ? n_ret[head * NB + beta] : (int)n_avail;
+    if (prune && t < cap)
+        s_A[t] = retained[(head * NB + beta) * (int64_t)cap + t];
+    bf16x8 qf[KC];
+    {
+        const uint16_t *qrow = q + (head * N + (q_ok ? qi : 0)) * D;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+            qf[kc] = as_bf16x8(q_ok ? *reinterpret_cast<const u32x4 *>(qrow + kc * 16 + half * 8)
+                                    : u32x4{0, 0, 0, 0});
+    }
+    __syncthreads();
+
+    // ---- routing (Eq. 7) with the running top-K of this lane's query ----
+    const int srow = t >> 3, spart = t & 7; // staging role: row of the tile, feature part
+    u32x4 pre3[3 * SCH];
+    int pre_id;
+    float pre_a;
+    auto prefetch = [&](int t0) {
+        const int x = t0 + srow;
+        pre_id = x < nA ? (prune ? s_A[x] : x) : -1;
+        pre_a = 0.0f;
+        if (pre_id >= 0) {
+            const uint16_t *src = kbar_split + (head * M + pre_id) * 3 * D + spart * PER;
+#pragma unroll
+            for (int part = 0; part < 3; ++part)
+#pragma unroll
+                for (int u = 0; u < SCH; ++u)
+                    pre3[part * SCH + u] = *reinterpret_cast<const u32x4 *>(src + part * D + u * 8);
+            if (spart == 0)
+                pre_a = a[head * M + pre_id];
+        } else {
+#pragma unroll
+            for (int u = 0; u < 3 * SCH; ++u)
+                pre3[u] = u32x4{0, 0, 0, 0};
+        }
+    };
+    if (nA > 0)
+        prefetch(0);
+
+    uint64_t kl[KT]; // this lane's best keys so far
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+        kl[j] = 0;
+    for (int t0 = 0; t0 < nA; t0 += 32) {
+        __syncthreads();
+        if (spart == 0) {
+            sm.id[srow] = pre_id >= 0 ? 0x7fffffff - pre_id : -1;   // low half of the ranking key
+            sm.prior[srow] = pre_id >= 0 ? lam * pre_a : 0.0f;
+            sm.pc[srow] = pre_id >= 0 ? (float)pre_id * s + 0.5f * s : 0.0f;
+        }
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+            for (int u = 0; u < SCH; ++u)
+                *reinterpret_cast<u32x4 *>(&sm.kb[part][srow][spart * PER + u * 8]) = pre3[part * SCH + u];
+        __syncthreads();
+        if (t0 + 32 < nA)
+            prefetch(t0 + 32); // overlaps the matrix work below
+
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[r] = 0.0f;
+#pragma unroll
+        for (int sp = 2; sp >= 0; --sp) { // smallest parts first
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.kb[sp][col][kc * 16 + half * 8]);
+                acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
+            }
+        }
+        // erf only below 4 (above it rounds to 1 in fp32); see the scorer
+        // this lane's 16 rows come in 4 runs of 4 consecutive rows: 12 vector LDS reads
+        float prv[16], pcv[16];
+        int idv[16]; // low key halves; -1 on padding rows
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int r0 = 8 * g + 4 * half;
+            const u32x4 vp = *reinterpret_cast<const u32x4 *>(&sm.prior[r0]);
+            const u32x4 vc = *reinterpret_cast<const u32x4 *>(&sm.pc[r0]);
+            const u32x4 vi = *reinterpret_cast<const u32x4 *>(&sm.id[r0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                prv[4 * g + e] = __uint_as_float(vp[e]);
+                pcv[4 * g + e] = __uint_as_float(vc[e]);
+                idv[4 * g + e] = (int)vi[e];
+            }
+        }
+        // erf only below 4 (from there on it rounds to 1 in fp32, and fmaf(prior,
+        // 1, content) == prior + content); a wave takes the long path only if
+        // one of its queries is that close to one of its cells
+        float pcmax = pcv[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+            pcmax = fmaxf(pcmax, pcv[r]);
+        const bool need_erf = __ballot(q_ok && (qpos - pcmax) * inv2s < 4.0f) != 0ull;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float g = 1.0f;
+            if (need_erf) {
+                const float x = (qpos - pcv[r]) * inv2s; // (i - p_c) / (2 sigma_h), i - p_c exact
+                if (x < 4.0f)
+                    g = erff(x);
+            }
+            const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
+            const uint64_t key = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
+            if (__ballot(key > kl[KT - 1])) // wave-uniform: in priority order most cells fall below every K-th best
+                insert_key<KT>(kl, key);
+        }
+    }
+    // merge with the partner lane (same query, other 16 rows of every tile)
+    {
+        uint64_t pk[KT]; // the partner's list as it was, before either lane inserts
+#pragma unroll
+        for (int j = 0; j < KT; ++j)
+            pk[j] = ((uint64_t)(uint32_t)shfl_xor_i((int)(kl[j] >> 32), 32) << 32) |
+                    (uint32_t)shfl_xor_i((int)(uint32_t)kl[j], 32);
+#pragma unroll
+        for (int j = 0; j < KT; ++j)
+            insert_key<KT>(kl, pk[j]);
+    }
+
+    // ---- selections to LDS (and global), then their union in id order ----
+    const int n_words = (int)((n_avail + 31) / 32);
+    for (int w = t; w < n_words; w += kThreads)
+        bitmap[w] = 0u;
+    int my_sel[KT];
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+        my_sel[j] = (q_ok && kl[j]) ? 0x7fffffff - (int32_t)(uint32_t)kl[j] : -1;
+    if (half == 0) {
+#pragma unroll
+        for (int j = 0; j < KT; ++j)
+            sel_s[wave * 32 + col][j] = my_sel[j];
+        if (sel && q_ok) {
+            int32_t *dst = sel + (head * N + qi) * KT;
+#pragma unroll
+            for (int j = 0; j < KT; ++j)
+                dst[j] = my_sel[j];
+        }
+    }
+    __syncthreads();
+    for (int x = t; x < 128 * KT; x += kThreads) {
+        const int32_t c = sel_s[x / KT][x % KT];
+        if (c >= 0)
+            atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int total = 0;
+        for (int base = 0; base < n_words; base += kWave) {
+            const int w = base + lane;
+            const uint32_t bits = w < n_words ? bitmap[w] : 0u;
+            const int cnt = __popc(bits);
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int y = __shfl_up(incl, o, kWave);
+                if (lane >= o)
+                    incl += y;
+            }
+            int pos = total + incl - cnt;
+            uint32_t b = bits;
+            while (b) {
+                const int bit = __ffs(b) - 1;
+                b &= b - 1u;
+                if (pos < 128 * KT)
+                    ulist[pos] = w * 32 + bit;
+                ++pos;
+            }
+            total += __shfl(incl, kWave - 1, kWave);
+        }
+        if (lane == 0)
+            n_u = total < 128 * KT ? total : 128 * KT;
+    }
+    __syncthreads();
+    const int nU = n_u;
+
+    // ---- readout (Eq. 9): one gathered cell at a time, next one in flight ----
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int KCH = (32 * CPR) / kThreads; // K chunks per thread: 1 or 2
+    const int tp = t & 15;
+    const int fc = t >> 4; // V roles exist for fc < CPR
+    u32x4 pk[KCH], pv0, pv1;
+    auto fetch = [&](int cell) {
+        const uint16_t *kc_src = k + (head * N + (int64_t)cell * s) * D;
+        const uint16_t *vc_src = v + (head * N + (int64_t)cell * s) * D;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int ch = t + u * kThreads;
+            pk[u] = *reinterpret_cast<const u32x4 *>(kc_src + (int64_t)(ch / CPR) * D + (ch % CPR) * 8);
+        }
+        if (fc < CPR) {
+            pv0 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp) * D + fc * 8);
+            pv1 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp + 1) * D + fc * 8);
+        }
+    };
+    if (nU > 0)
+        fetch(ulist[0]);
+
+    constexpr int DT = D / 32; // feature tiles of the output
+    f32x16 o_acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            o_acc[dt][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f; // m_run in the exp2 domain
+
+    for (int x = 0; x < nU; ++x) {
+        const int cell = ulist[x];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int ch = t + u * kThreads;
+            *reinterpret_cast<u32x4 *>(&sm.k[ch / CPR][(ch % CPR) * 8]) = pk[u];
+        }
+        if (fc < CPR) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t a0 = (pv0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t a1 = (pv1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][2 * tp]) = a0 | (a1 << 16);
+            }
+        }
+        __syncthreads();
+        if (x + 1 < nU)
+            fetch(ulist[x + 1]);
+
+        bool mine = false;
+#pragma unroll
+        for (int j = 0; j < KT; ++j)
+            mine |= my_sel[j] == cell;
+        if (__ballot(mine) == 0ull)
+            continue; // no query of this wave reads the cell
+
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[r] = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
+            acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
+        }
+        float p[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = acc[r] * scale_log2;
+            tmax = fmaxf(tmax, p[r]);
+        }
+        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        float alpha = 1.0f, psum = 0.0f;
+        if (mine) {
+            if (tmax > m_run + kLazy) {
+                alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+                m_run = tmax;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(p[r] - m_run);
+                psum += p[r];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                p[r] = 0.0f;
+        }
+        psum += shfl_xor_f(psum, 32);
+        l_run = l_run * alpha + psum;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    o_acc[dt][r] *= alpha;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            u32x4 ph, pl;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float x0 = p[8 * kk + 2 * w], x1 = p[8 * kk + 2 * w + 1];
+                const uint32_t hp = cvt_pk_bf16(x0, x1);
+                ph[w] = hp;
+                pl[w] = cvt_pk_bf16(x0 - bf16_bits_to_f32(hp & 0xffffu), x1 - bf16_bits_to_f32(hp >> 16));
+            }
+            const bf16x8 bh = as_bf16x8(ph), bl = as_bf16x8(pl);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int m = dt * 32 + col;
+                const u32x2 lo4 = *reinterpret_cast<const u32x2 *>(&sm.vt[m][16 * kk + 4 * half]);
+                const u32x2 hi4 = *reinterpret_cast<const u32x2 *>(&sm.vt[m][16 * kk + 8 + 4 * half]);
+                const bf16x8 av = as_bf16x8(u32x4{lo4[0], lo4[1], hi4[0], hi4[1]});
+                o_acc[dt] = mfma_bf16(av, bl, o_acc[dt]);
+                o_acc[dt] = mfma_bf16(av, bh, o_acc[dt]);
+            }
+        }
+    }
+
+    // ---- normalise, RMSNorm over d (Eq. 17), write through LDS ----
+    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float ms = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float u = o_acc[dt][r] * inv_l;
+            o_acc[dt][r] = u;
+            ms += u * u;
+        }
+    ms += shfl_xor_f(ms, 32);
+    const float rs = 1.0f / sqrtf(ms / (float)D + eps);
+    const float *gh = gain ? gain + (int64_t)h * D : nullptr;
+    __syncthreads(); // the last cell's LDS reads are done: the tile area takes the output
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d0 = dt * 32 + 8 * rg + 4 * half;
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float gv = gh ? gh[d0 + e] : 1.0f;
+                y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+            }
+            *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
+                u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};
+        }
+    __syncthreads();
+    tile_store_bf16<D, kThreads>(out + (head * N + q0) * D, &sm.tile[0][0], sm.kStride,
+                                 (int)(N - q0 < 128 ? N - q0 : 128));
+}
+
+template <int D, int KT>
+hipError_t launch_k(const Geometry &g, const HeadConsts &hc, const void *q, const void *k, const void *v,
+                    const uint16_t *kbar_split, const float *a, const int32_t *retained, const int32_t *n_ret,
+                    const float *gain, void *out, int32_t *sel, hipStream_t st)
+{
+    dim3 grid((unsigned)((int64_t)g.NB * g.bh)); // one linear range, renumbered per XCD in the kernel
+    const size_t words = (size_t)((g.M + 31) / 32);
+    const size_t dyn = (words > 0 ? words : 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL((route_readout_kernel<D, KT>), grid, dim3(kThreads), dyn, st,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                       static_cast<const uint16_t *>(v), kbar_split, a, retained, n_ret, gain,
+                       static_cast<uint16_t *>(out), sel, g.N, g.M, g.NB, g.cap, g.prune, g.H, g.s, g.B / g.s, g.eps,
+                       hc);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Geometry &g, const HeadConsts &hc, const void *q, const void *k, const void *v,
+                    const uint16_t *ks, const float *a, const int32_t *retained, const int32_t *n_ret,
+                    const float *gain, void *out, int32_t *sel, hipStream_t st)
+{
+    switch (g.K) {
+    case 1: return launch_k<D, 1>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    case 2: return launch_k<D, 2>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    case 3: return launch_k<D, 3>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    case 4: return launch_k<D, 4>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    case 5: return launch_k<D, 5>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    case 6: return launch_k<D, 6>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    case 7: return launch_k<D, 7>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    default: return launch_k<D, 8>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    }
+}
+
+} // namespace
+
+hipError_t launch_route_readout(const Geometry &g, const HeadConsts &hc, const void *q, const void *k,
+                                const void *v, const uint16_t *kbar_split, const float *a,
+                                const int32_t *retained, const int32_t *n_ret, const float *gain, void *out,
+                                int32_t *sel, hipStream_t st)
+{
+    return g.d == 64 ? launch_d<64>(g, hc, q, k, v, kbar_split, a, retained, n_ret, gain, out, sel, st)
+                     : launch_d<128>(g, hc, q, k, v, kbar_split, a, retained, n_ret, gain, out, sel, st);
+}
+
+} // namespace fsl

@@ -11,10 +11,13 @@
 // beta < death(c) = e / (B/s) + 1 (the first block in which e is available).
 // This gives the same sets as the page's Eq. 15 merge (App. C "Bounded cache")
 // with every block independent:
-//   prune_death_kernel: one thread per cell scans the head's norms (staged
-//       through LDS) in id order and stops at its P-th outranking cell;
-//   prune_emit_kernel:  one wave per (head, block) compacts, in id order, the
-//       non-recent cells still alive plus the W most recent cells.
+//   prune_death_kernel: one wave per cell scans the head's norms 64 ids at a
+//       time; the ballot of "id x outranks c" counts outranking cells, and the
+//       P-th one is located inside the 64-id window where the count reaches P;
+//   prune_emit_kernel:  one wave per (head, block) collects the non-recent cells
+//       still alive plus the W most recent cells and writes them in priority
+//       order (a desc, id asc), so that the scorer meets the cells with the
+//       largest prior terms first.
 #include "fsl_internal.h"
 
 #include <climits>
@@ -23,43 +26,38 @@ namespace fsl {
 namespace {
 
 constexpr int kDeathThreads = 256;
-constexpr int kTile = 2048; // norms staged per LDS pass
+constexpr int kDeathCells = kDeathThreads / kWave; // cells per workgroup, one per wave
 
 __global__ __launch_bounds__(kDeathThreads) void prune_death_kernel(const float *__restrict__ a,
                                                                     int32_t *__restrict__ death, int64_t M,
                                                                     int P, int cells_per_block)
 {
-    __shared__ float tile[kTile];
+    const int lane = threadIdx.x & (kWave - 1);
     const int64_t head = blockIdx.y;
-    const int64_t c = (int64_t)blockIdx.x * kDeathThreads + threadIdx.x;
+    const int64_t c = (int64_t)blockIdx.x * kDeathCells + (threadIdx.x / kWave);
+    if (c >= M)
+        return; // whole wave
     const float *ah = a + head * M;
-    const float ac = c < M ? ah[c] : 0.0f;
-    int count = 0;
-    int64_t e = -1;
-    bool done = (c >= M) || (P == 0);
-    for (int64_t base = 0; base < M; base += kTile) {
-        const int len = (int)((M - base) < kTile ? (M - base) : kTile);
-        __syncthreads();
-        for (int x = threadIdx.x; x < len; x += kDeathThreads)
-            tile[x] = ah[base + x];
-        __syncthreads();
-        if (!done) {
-            for (int x = 0; x < len; ++x) {
-                const float ax = tile[x];
-                const int64_t cx = base + x;
-                if (ax > ac || (ax == ac && cx < c)) {
-                    if (++count == P) {
-                        e = cx;
-                        done = true;
-                        break;
-                    }
-                }
+    const float ac = ah[c];
+    int64_t e = -1; // id of the P-th cell outranking c, in id order
+    if (P > 0) {
+        int count = 0;
+        for (int64_t base = 0; base < M; base += kWave) {
+            const int64_t x = base + lane;
+            const float ax = x < M ? ah[x] : 0.0f;
+            const bool o = x < M && (ax > ac || (ax == ac && x < c)); // x ranks before c
+            const uint64_t m = __ballot(o);
+            const int n = __popcll(m);
+            if (count + n >= P) {
+                const int before = __popcll(m & ((1ull << lane) - 1ull));
+                const uint64_t hit = __ballot(o && before == P - count - 1);
+                e = base + __ffsll((unsigned long long)hit) - 1;
+                break;
             }
+            count += n;
         }
-        if (__syncthreads_count(done ? 1 : 0) == (int)blockDim.x)
-            break;
     }
-    if (c < M) {
+    if (lane == 0) {
         int32_t dth;
         if (P == 0)
             dth = 0; // never in TopP
@@ -72,10 +70,13 @@ __global__ __launch_bounds__(kDeathThreads) void prune_death_kernel(const float 
 }
 
 __global__ __launch_bounds__(kWave) void prune_emit_kernel(const int32_t *__restrict__ death,
+                                                           const float *__restrict__ a,
                                                            int32_t *__restrict__ retained,
                                                            int32_t *__restrict__ n_ret, int64_t M, int NB,
                                                            int cap, int W, int cells_per_block)
 {
+    __shared__ __attribute__((aligned(16))) int32_t s_id[kMaxRetainedCap + 4];
+    __shared__ __attribute__((aligned(16))) float s_a[kMaxRetainedCap + 4];
     const int beta = blockIdx.x;
     const int64_t head = blockIdx.y;
     const int lane = threadIdx.x;
@@ -84,24 +85,47 @@ __global__ __launch_bounds__(kWave) void prune_emit_kernel(const int32_t *__rest
         n_avail = M;
     const int64_t recent0 = n_avail > W ? n_avail - W : 0;
     const int32_t *dh = death + head * M;
+    const float *ah = a + head * M;
     int32_t *dst = retained + (head * NB + beta) * (int64_t)cap;
     int count = 0;
-    // non-recent cells still in TopP, ascending
+    // non-recent cells still in TopP
     for (int64_t base = 0; base < recent0; base += kWave) {
         const int64_t c = base + lane;
         const bool keep = c < recent0 && dh[c] > beta;
         const uint64_t mask = __ballot(keep);
         const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
         if (keep && pos < cap)
-            dst[pos] = (int32_t)c;
+            s_id[pos] = (int32_t)c;
         count += __popcll(mask);
     }
     if (count > cap - (int)(n_avail - recent0)) // only reachable with non-finite norms
         count = cap - (int)(n_avail - recent0);
     // the W most recent cells
     for (int64_t c = recent0 + lane; c < n_avail; c += kWave)
-        dst[count + (c - recent0)] = (int32_t)c;
+        s_id[count + (c - recent0)] = (int32_t)c;
     count += (int)(n_avail - recent0);
+    const int n4 = (count + 3) & ~3;
+    for (int x = lane; x < n4; x += kWave) {
+        const bool live = x < count;
+        const int32_t c = live ? s_id[x] : INT32_MAX;
+        s_a[x] = live ? ah[c] : -INFINITY; // padding ranks last
+        s_id[x] = c;
+    }
+    __syncthreads();
+    // priority order (a desc, id asc): each cell's rank is the number of cells before it
+    for (int x = lane; x < count; x += kWave) {
+        const float ax = s_a[x];
+        const int32_t cx = s_id[x];
+        int rank = 0;
+        for (int y = 0; y < n4; y += 4) {
+            const u32x4 va = *reinterpret_cast<const u32x4 *>(&s_a[y]);
+            const u32x4 vi = *reinterpret_cast<const u32x4 *>(&s_id[y]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rank += ranks_before(__uint_as_float(va[e]), (int)vi[e], ax, cx) ? 1 : 0;
+        }
+        dst[rank] = cx;
+    }
     for (int x = count + lane; x < cap; x += kWave)
         dst[x] = -1;
     if (lane == 0)
@@ -115,7 +139,7 @@ hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32
 {
     const int cpb = g.B / g.s;
     if (g.M > 0) {
-        dim3 grid((unsigned)((g.M + kDeathThreads - 1) / kDeathThreads), (unsigned)g.bh);
+        dim3 grid((unsigned)((g.M + kDeathCells - 1) / kDeathCells), (unsigned)g.bh);
         hipLaunchKernelGGL(prune_death_kernel, grid, dim3(kDeathThreads), 0, st, a, death, g.M, g.P, cpb);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
@@ -124,7 +148,7 @@ hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32
     if (!emit)
         return hipSuccess;
     dim3 grid2((unsigned)g.NB, (unsigned)g.bh);
-    hipLaunchKernelGGL(prune_emit_kernel, grid2, dim3(kWave), 0, st, death, retained, n_ret, g.M, g.NB, g.cap, g.W,
+    hipLaunchKernelGGL(prune_emit_kernel, grid2, dim3(kWave), 0, st, death, a, retained, n_ret, g.M, g.NB, g.cap, g.W,
                        cpb);
     return hipGetLastError();
 }

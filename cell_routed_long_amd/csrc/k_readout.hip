@@ -20,7 +20,11 @@
 // Precision: q and k are exact in bf16 (fp32 products, fp32 accumulation);
 // the probabilities are split into bf16 hi + lo parts for the P.V product so
 // that the readout keeps ~16 mantissa bits before the final rounding.  fp32
-// tensors use the fp32 MFMA.
+// tensors use the fp32 MFMA.  The softmax runs in the exp2 domain with a lazy
+// running max: it is raised only when a logit exceeds it by more than 8 (so
+// every weight stays below 2^8 and the accumulators are rescaled rarely); the
+// result is the same softmax up to rounding.  The next cell's keys and values
+// are fetched into registers while the current cell is on the matrix cores.
 #include "fsl_internal.h"
 
 #include <type_traits>
@@ -29,7 +33,7 @@ namespace fsl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKmax = 8;
+constexpr float kLazy = 8.0f; // the running max moves only when it grows by more than 2^8
 
 template <typename T, int D>
 struct ReadoutSmem;
@@ -38,8 +42,14 @@ template <int D>
 struct alignas(16) ReadoutSmem<uint16_t, D> {
     static constexpr int kStrideK = D + 8; // bf16 elements per K row
     static constexpr int kStrideV = 32 + 4; // bf16 elements per V^T row (72 bytes)
-    uint16_t k[32][kStrideK];
-    uint16_t vt[D][kStrideV];
+    static constexpr int kStrideT = D + 8; // bf16 elements per row of a 128-row query/output tile
+    union {
+        struct {
+            uint16_t k[32][kStrideK];
+            uint16_t vt[D][kStrideV];
+        };
+        uint16_t tile[128][kStrideT]; // the block's q tile at entry, its output tile at exit
+    };
 };
 
 template <int D>
@@ -49,22 +59,24 @@ struct alignas(16) ReadoutSmem<float, D> {
     float v[32][kStride];
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__ q, const T *__restrict__ k,
+template <typename T, int D, int KT>
+__global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                            const T *__restrict__ v,
                                                            const int32_t *__restrict__ sel,
                                                            const float *__restrict__ gain, T *__restrict__ out,
-                                                           int64_t N, int64_t M, int H, int K, int s,
+                                                           int64_t N, int64_t M, int NB, int H, int s,
                                                            int cells_per_block, float eps)
 {
     __shared__ ReadoutSmem<T, D> sm;
-    __shared__ int32_t sel_s[128][kKmax];
-    __shared__ int32_t ulist[128 * kKmax];
+    __shared__ int32_t sel_s[128][KT];
+    __shared__ int32_t ulist[128 * KT];
     __shared__ int32_t n_u;
     extern __shared__ uint32_t bitmap[]; // ceil(M / 32) words
 
-    const int beta = blockIdx.x;
-    const int64_t head = blockIdx.y;
+    constexpr bool kBf16 = sizeof(T) == 2;
+    const int64_t lb = xcd_logical_block(blockIdx.x, (int64_t)gridDim.x);
+    const int beta = (int)(lb % NB);
+    const int64_t head = lb / NB;
     const int h = (int)(head % H);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -73,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
     const int64_t q0 = (int64_t)beta * 128;
     const int64_t qi = q0 + wave * 32 + col;
     const bool q_ok = qi < N;
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    // logits in the exp2 domain: log2(e) / sqrt(d)
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
 
     int64_t n_avail = (int64_t)beta * cells_per_block;
     if (n_avail > M)
@@ -83,18 +96,18 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
     // ---- selections of the block's queries, and their union ----
     for (int w = threadIdx.x; w < n_words; w += kThreads)
         bitmap[w] = 0u;
-    for (int x = threadIdx.x; x < 128 * kKmax; x += kThreads) {
-        const int r = x / kKmax, j = x % kKmax;
+    for (int x = threadIdx.x; x < 128 * KT; x += kThreads) {
+        const int r = x / KT, j = x % KT;
         int32_t c = -1;
-        if (j < K && q0 + r < N)
-            c = sel[(head * N + q0 + r) * K + j];
+        if (q0 + r < N)
+            c = sel[(head * N + q0 + r) * KT + j];
         if (c >= n_avail)
             c = -1; // not a cell of this block's prefix: ignore
         sel_s[r][j] = c;
     }
     __syncthreads();
-    for (int x = threadIdx.x; x < 128 * kKmax; x += kThreads) {
-        const int32_t c = sel_s[x / kKmax][x % kKmax];
+    for (int x = threadIdx.x; x < 128 * KT; x += kThreads) {
+        const int32_t c = sel_s[x / KT][x % KT];
         if (c >= 0)
             atomicOr(&bitmap[c >> 5], 1u << (c & 31));
     }
@@ -117,39 +130,63 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
             while (b) {
                 const int bit = __ffs(b) - 1;
                 b &= b - 1u;
-                if (pos < 128 * kKmax)
+                if (pos < 128 * KT)
                     ulist[pos] = w * 32 + bit;
                 ++pos;
             }
             total += __shfl(incl, kWave - 1, kWave);
         }
         if (lane == 0)
-            n_u = total < 128 * kKmax ? total : 128 * kKmax;
+            n_u = total < 128 * KT ? total : 128 * KT;
     }
     __syncthreads();
     const int nU = n_u;
 
-    int my_sel[kKmax];
+    int my_sel[KT];
 #pragma unroll
-    for (int j = 0; j < kKmax; ++j)
+    for (int j = 0; j < KT; ++j)
         my_sel[j] = sel_s[wave * 32 + col][j];
 
-    // ---- query fragments ----
-    constexpr bool kBf16 = sizeof(T) == 2;
+    // ---- query fragments (bf16: the tile comes in through LDS, coalesced) ----
     constexpr int KC = kBf16 ? D / 16 : D / 2;
     using QFrag = typename std::conditional<kBf16, bf16x8, float>::type;
     QFrag qf[KC];
-    {
+    const int rows = (int)(N - q0 < 128 ? N - q0 : 128);
+    if constexpr (kBf16) {
+        tile_load_bf16<D, kThreads>(&sm.tile[0][0], sm.kStrideT, q + (head * N + q0) * D, rows);
+        __syncthreads();
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+            qf[kc] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.tile[wave * 32 + col][kc * 16 + half * 8]));
+    } else {
         const T *qrow = q + (head * N + (q_ok ? qi : 0)) * D;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            if constexpr (kBf16) {
-                u32x4 w = q_ok ? *reinterpret_cast<const u32x4 *>(qrow + kc * 16 + half * 8) : u32x4{0, 0, 0, 0};
-                qf[kc] = as_bf16x8(w);
-            } else {
-                qf[kc] = q_ok ? qrow[kc * 2 + half] : 0.0f;
-            }
+        for (int kc = 0; kc < KC; ++kc)
+            qf[kc] = q_ok ? qrow[kc * 2 + half] : 0.0f;
+    }
+
+    // ---- gather roles (bf16): K in 16-byte chunks, V^T by (token pair, 8-feature chunk) ----
+    constexpr int CPR = D / 8;                   // 16-byte chunks per row
+    constexpr int KCH = (32 * CPR) / kThreads;   // K chunks per thread: 1 or 2
+    const int tp = threadIdx.x & 15;
+    const int fc = threadIdx.x >> 4;             // V roles exist for fc < CPR
+    u32x4 pk[KCH > 0 ? KCH : 1], pv0, pv1;
+    auto fetch = [&](int cell) {
+        const T *kc_src = k + (head * N + (int64_t)cell * s) * D;
+        const T *vc_src = v + (head * N + (int64_t)cell * s) * D;
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int ch = threadIdx.x + u * kThreads;
+            pk[u] = *reinterpret_cast<const u32x4 *>(kc_src + (int64_t)(ch / CPR) * D + (ch % CPR) * 8);
         }
+        if (fc < CPR) {
+            pv0 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp) * D + fc * 8);
+            pv1 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp + 1) * D + fc * 8);
+        }
+    };
+    if constexpr (kBf16) {
+        if (nU > 0)
+            fetch(ulist[0]);
     }
 
     constexpr int DT = D / 32; // feature tiles of the output
@@ -159,35 +196,29 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             o_acc[dt][r] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f; // m_run in the exp2 domain
 
     for (int x = 0; x < nU; ++x) {
         const int cell = ulist[x];
-        const T *kc_src = k + (head * N + (int64_t)cell * s) * D;
-        const T *vc_src = v + (head * N + (int64_t)cell * s) * D;
         __syncthreads();
-        // ---- gather the cell's 32 keys and values into LDS ----
+        // ---- the cell's 32 keys and values into LDS ----
         if constexpr (kBf16) {
-            constexpr int CPR = D / 8; // 16-byte chunks per row
 #pragma unroll
-            for (int ch = threadIdx.x; ch < 32 * CPR; ch += kThreads) {
-                const int row = ch / CPR, c8 = (ch % CPR) * 8;
-                *reinterpret_cast<u32x4 *>(&sm.k[row][c8]) =
-                    *reinterpret_cast<const u32x4 *>(kc_src + (int64_t)row * D + c8);
+            for (int u = 0; u < KCH; ++u) {
+                const int ch = threadIdx.x + u * kThreads;
+                *reinterpret_cast<u32x4 *>(&sm.k[ch / CPR][(ch % CPR) * 8]) = pk[u];
             }
-            // V^T: thread -> (token pair, 8-feature chunk)
-            const int tp = threadIdx.x & 15;
-            for (int fc = threadIdx.x >> 4; fc < CPR; fc += kThreads / 16) {
-                const u32x4 r0 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp) * D + fc * 8);
-                const u32x4 r1 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp + 1) * D + fc * 8);
+            if (fc < CPR) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t a0 = (r0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    const uint32_t a1 = (r1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    const uint32_t a0 = (pv0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    const uint32_t a1 = (pv1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
                     *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][2 * tp]) = a0 | (a1 << 16);
                 }
             }
         } else {
+            const T *kc_src = k + (head * N + (int64_t)cell * s) * D;
+            const T *vc_src = v + (head * N + (int64_t)cell * s) * D;
             for (int e = threadIdx.x; e < 32 * D; e += kThreads) {
                 const int row = e / D, f = e % D;
                 sm.k[row][f] = kc_src[(int64_t)row * D + f];
@@ -195,11 +226,15 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
             }
         }
         __syncthreads();
+        if constexpr (kBf16) {
+            if (x + 1 < nU)
+                fetch(ulist[x + 1]); // overlaps the matrix work below
+        }
 
         bool mine = false;
 #pragma unroll
-        for (int j = 0; j < kKmax; ++j)
-            mine |= (j < K) && (my_sel[j] == cell);
+        for (int j = 0; j < KT; ++j)
+            mine |= my_sel[j] == cell;
         if (__ballot(mine) == 0ull)
             continue; // no query of this wave reads the cell
 
@@ -220,25 +255,26 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
                 acc = mfma_f32(sm.k[col][kc * 2 + half], qf[kc], acc);
         }
 
-        // ---- online softmax over the query's own tokens ----
+        // ---- online softmax over the query's own tokens (exp2 domain) ----
         float p[16];
         float tmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p[r] = acc[r] * inv_sqrt_d;
+            p[r] = acc[r] * scale_log2;
             tmax = fmaxf(tmax, p[r]);
         }
         tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
         float alpha = 1.0f, psum = 0.0f;
         if (mine) {
-            const float m_new = fmaxf(m_run, tmax);
-            alpha = expf(m_run - m_new); // 0 on the first cell (m_run = -inf)
+            if (tmax > m_run + kLazy) { // first cell (m_run = -inf) or a much larger logit
+                alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+                m_run = tmax;
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[r] = expf(p[r] - m_new);
+                p[r] = __builtin_amdgcn_exp2f(p[r] - m_run); // <= 2^8
                 psum += p[r];
             }
-            m_run = m_new;
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -246,11 +282,13 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
         }
         psum += shfl_xor_f(psum, 32);
         l_run = l_run * alpha + psum;
+        if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                o_acc[dt][r] *= alpha;
+                for (int r = 0; r < 16; ++r)
+                    o_acc[dt][r] *= alpha;
+        }
 
         // ---- O^T[d x 32 queries] += V^T . P^T ----
         if constexpr (kBf16) {
@@ -260,9 +298,9 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const float x0 = p[8 * kk + 2 * w], x1 = p[8 * kk + 2 * w + 1];
-                    const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-                    ph[w] = h0 | (h1 << 16);
-                    pl[w] = pack_bf16x2(x0 - bf16_bits_to_f32(h0), x1 - bf16_bits_to_f32(h1));
+                    const uint32_t hp = cvt_pk_bf16(x0, x1);
+                    ph[w] = hp;
+                    pl[w] = cvt_pk_bf16(x0 - bf16_bits_to_f32(hp & 0xffffu), x1 - bf16_bits_to_f32(hp >> 16));
                 }
                 const bf16x8 bh = as_bf16x8(ph), bl = as_bf16x8(pl);
 #pragma unroll
@@ -297,9 +335,9 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
         }
     ms += shfl_xor_f(ms, 32);
     const float rs = 1.0f / sqrtf(ms / (float)D + eps);
-    if (q_ok) {
-        T *dst = out + (head * N + qi) * D;
-        const float *gh = gain ? gain + (int64_t)h * D : nullptr;
+    const float *gh = gain ? gain + (int64_t)h * D : nullptr;
+    if constexpr (kBf16) {
+        __syncthreads(); // the last cell's LDS reads are done: the tile area takes the output
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -311,27 +349,58 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T *__restrict__
                     const float gv = gh ? gh[d0 + e] : 1.0f;
                     y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
                 }
-                if constexpr (kBf16) {
-                    *reinterpret_cast<u32x2 *>(dst + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-                } else {
-                    *reinterpret_cast<u32x4 *>(dst + d0) = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]),
-                                                                 __float_as_uint(y[2]), __float_as_uint(y[3])};
+                *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
+                    u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};
+            }
+        __syncthreads();
+        tile_store_bf16<D, kThreads>(reinterpret_cast<uint16_t *>(out) + (head * N + q0) * D, &sm.tile[0][0],
+                                     sm.kStrideT, rows);
+    } else if (q_ok) {
+        T *dst = out + (head * N + qi) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d0 = dt * 32 + 8 * rg + 4 * half;
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gv = gh ? gh[d0 + e] : 1.0f;
+                    y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
                 }
+                *reinterpret_cast<u32x4 *>(dst + d0) = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]),
+                                                             __float_as_uint(y[2]), __float_as_uint(y[3])};
             }
     }
+}
+
+template <typename T, int D, int KT>
+hipError_t launch_k(const Geometry &g, const void *q, const void *k, const void *v, const int32_t *sel,
+                    const float *gain, void *out, hipStream_t st)
+{
+    dim3 grid((unsigned)((int64_t)g.NB * g.bh)); // one linear range, renumbered per XCD in the kernel
+    const size_t words = (size_t)((g.M + 31) / 32);
+    const size_t dyn = (words > 0 ? words : 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL((readout_kernel<T, D, KT>), grid, dim3(kThreads), dyn, st, static_cast<const T *>(q),
+                       static_cast<const T *>(k), static_cast<const T *>(v), sel, gain, static_cast<T *>(out), g.N,
+                       g.M, g.NB, g.H, g.s, g.B / g.s, g.eps);
+    return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_t(const Geometry &g, const void *q, const void *k, const void *v, const int32_t *sel,
                     const float *gain, void *out, hipStream_t st)
 {
-    dim3 grid((unsigned)g.NB, (unsigned)g.bh);
-    const size_t words = (size_t)((g.M + 31) / 32);
-    const size_t dyn = (words > 0 ? words : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL((readout_kernel<T, D>), grid, dim3(kThreads), dyn, st, static_cast<const T *>(q),
-                       static_cast<const T *>(k), static_cast<const T *>(v), sel, gain, static_cast<T *>(out), g.N,
-                       g.M, g.H, g.K, g.s, g.B / g.s, g.eps);
-    return hipGetLastError();
+    switch (g.K) {
+    case 1: return launch_k<T, D, 1>(g, q, k, v, sel, gain, out, st);
+    case 2: return launch_k<T, D, 2>(g, q, k, v, sel, gain, out, st);
+    case 3: return launch_k<T, D, 3>(g, q, k, v, sel, gain, out, st);
+    case 4: return launch_k<T, D, 4>(g, q, k, v, sel, gain, out, st);
+    case 5: return launch_k<T, D, 5>(g, q, k, v, sel, gain, out, st);
+    case 6: return launch_k<T, D, 6>(g, q, k, v, sel, gain, out, st);
+    case 7: return launch_k<T, D, 7>(g, q, k, v, sel, gain, out, st);
+    default: return launch_k<T, D, 8>(g, q, k, v, sel, gain, out, st);
+    }
 }
 
 } // namespace

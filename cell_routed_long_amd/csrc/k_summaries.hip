@@ -7,7 +7,10 @@
 // row it touches, so the column sums need only a final cross-lane reduction,
 // and each row's squared norm is reduced across the lanes that share the row.
 // Sums and squared norms accumulate in fp64 (exact for bf16 keys) and are
-// rounded once to fp32.  HBM-bound: the kernel reads each key exactly once.
+// rounded once to fp32.  Optionally the fp32 mean is also written as three
+// bf16 parts (hi, mid, lo), the operands the block scorer feeds to the bf16
+// matrix cores, so that the split is done once per cell instead of once per
+// query block.  HBM-bound: the kernel reads each key exactly once.
 #include "fsl_internal.h"
 
 namespace fsl {
@@ -15,8 +18,9 @@ namespace {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void cell_summaries_kernel(const T *__restrict__ k, float *__restrict__ kbar,
-                                                             float *__restrict__ a, int64_t N, int64_t M,
-                                                             int64_t total_cells)
+                                                             float *__restrict__ a,
+                                                             uint16_t *__restrict__ kbar_split, int64_t N,
+                                                             int64_t M, int64_t total_cells)
 {
     constexpr int EPC = 16 / (int)sizeof(T); // elements per 16-byte chunk
     constexpr int R = D / EPC;               // chunks per key row: 8, 16 or 32
@@ -86,33 +90,59 @@ __global__ __launch_bounds__(256) void cell_summaries_kernel(const T *__restrict
 
     if (lane < R) {
         float *dst = kbar + cell * D + group * EPC;
+        float m[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e)
-            dst[e] = (float)(colsum[e] * (1.0 / 32.0));
+        for (int e = 0; e < EPC; ++e) {
+            m[e] = (float)(colsum[e] * (1.0 / 32.0));
+            dst[e] = m[e];
+        }
+        if (kbar_split) { // bf16 hi, mid, lo parts of the fp32 mean (24 mantissa bits in all)
+            uint32_t pk[3][EPC / 2];
+#pragma unroll
+            for (int e = 0; e < EPC; e += 2) {
+                const uint32_t hi = cvt_pk_bf16(m[e], m[e + 1]);
+                const float r0 = m[e] - bf16_bits_to_f32(hi & 0xffffu), r1 = m[e + 1] - bf16_bits_to_f32(hi >> 16);
+                const uint32_t mid = cvt_pk_bf16(r0, r1);
+                const float s0 = r0 - bf16_bits_to_f32(mid & 0xffffu), s1 = r1 - bf16_bits_to_f32(mid >> 16);
+                pk[0][e / 2] = hi;
+                pk[1][e / 2] = mid;
+                pk[2][e / 2] = cvt_pk_bf16(s0, s1);
+            }
+#pragma unroll
+            for (int part = 0; part < 3; ++part) {
+                uint32_t *o = reinterpret_cast<uint32_t *>(kbar_split + (cell * 3 + part) * D + group * EPC);
+#pragma unroll
+                for (int e = 0; e < EPC / 2; ++e)
+                    o[e] = pk[part][e];
+            }
+        }
     }
     if (lane == 0)
         a[cell] = (float)sqrt(best);
 }
 
 template <typename T, int D>
-hipError_t launch_t(const Geometry &g, const void *k, float *kbar, float *a, hipStream_t st)
+hipError_t launch_t(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split, hipStream_t st)
 {
     const int64_t total = (int64_t)g.bh * g.M;
     if (total == 0)
         return hipSuccess;
     const int64_t blocks = (total + 3) / 4;
     hipLaunchKernelGGL((cell_summaries_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const T *>(k), kbar, a, g.N, g.M, total);
+                       static_cast<const T *>(k), kbar, a, kbar_split, g.N, g.M, total);
     return hipGetLastError();
 }
 
 } // namespace
 
-hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, hipStream_t st)
+hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split,
+                                 hipStream_t st)
 {
     if (g.bf16)
-        return g.d == 64 ? launch_t<uint16_t, 64>(g, k, kbar, a, st) : launch_t<uint16_t, 128>(g, k, kbar, a, st);
-    return g.d == 64 ? launch_t<float, 64>(g, k, kbar, a, st) : launch_t<float, 128>(g, k, kbar, a, st);
+        return g.d == 64 ? launch_t<uint16_t, 64>(g, k, kbar, a, kbar_split, st)
+                         : launch_t<uint16_t, 128>(g, k, kbar, a, kbar_split, st);
+    return g.d == 64 ? launch_t<float, 64>(g, k, kbar, a, kbar_split, st)
+                     : launch_t<float, 128>(g, k, kbar, a, kbar_split, st);
 }
 
 } // namespace fsl

@@ -75,13 +75,18 @@ const char *fs_status_string(fs_status status);
  * Cell summaries, Eq. 5: for every complete cell c < M = floor(N/s) of every
  * (sequence, head), kbar[c] = (1/s) sum_{j in I_c} k_j and a[c] = max_{j in I_c}
  * ||k_j||_2 (p_c = (c + 1/2) s is implicit).
- *   k     [batch, H, N, d]  shape dtype            (input)
- *   kbar  [batch, H, M, d]  fp32                   (output)
- *   a     [batch, H, M]     fp32                   (output)
+ *   k           [batch, H, N, d]     shape dtype                    (input)
+ *   kbar        [batch, H, M, d]     fp32                           (output)
+ *   a           [batch, H, M]        fp32                           (output)
+ *   kbar_split  [batch, H, M, 3, d]  bf16 bit patterns, or NULL     (output)
+ *               kbar[c] as three bf16 parts hi, mid, lo (hi = bf16(kbar),
+ *               mid = bf16(kbar - hi), lo = bf16(kbar - hi - mid)): the operands
+ *               fs_score_select feeds to the bf16 matrix cores.  bf16 shapes
+ *               only; not written for fp32 shapes.
  * Sums and norms accumulate in fp64 and are rounded once to fp32.
  */
 fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *prm, const void *k,
-                            float *kbar, float *a, void *stream);
+                            float *kbar, float *a, uint16_t *kbar_split, void *stream);
 
 /* Bytes of workspace fs_prune_retained needs (0 on invalid arguments). */
 size_t fs_prune_workspace_bytes(const fs_shape *shape, const fs_params *prm);
@@ -91,7 +96,8 @@ size_t fs_prune_workspace_bytes(const fs_shape *shape, const fs_params *prm);
  * (sequence, head), A_beta = Recent_W(C_beta) u TopP_{c in C_beta}(a_c) with
  * C_beta = {c : (c+1) s <= beta B}.  Requires prm->prune == 1.
  *   a           [batch, H, M]            fp32, from fs_cell_summaries (input)
- *   retained    [batch, H, NB, P + W]    int32 cell ids ascending, -1 padded (output)
+ *   retained    [batch, H, NB, P + W]    int32 cell ids in priority order (a desc, id
+ *                                        asc), -1 padded (output)
  *   n_retained  [batch, H, NB]           int32 |A_beta| (output)
  *   workspace   fs_prune_workspace_bytes() bytes of device memory (scratch)
  * NB = ceil(N / B).  Block 0 is always empty.
@@ -107,13 +113,16 @@ fs_status fs_prune_retained(const fs_shape *shape, const fs_params *prm, const f
  * whole prefix C_i for FS), and T_i = the min(K, |A_i|) best cells.
  *   q           [batch, H, N, d]        shape dtype (input)
  *   kbar, a     from fs_cell_summaries  (input)
+ *   kbar_split  from fs_cell_summaries, or NULL: the scorer then splits kbar
+ *               itself (bf16 shapes; ignored for fp32 shapes)
  *   retained, n_retained  from fs_prune_retained (input; NULL when prune == 0)
  *   sigma_h, lambda_h     host [H] fp32 (sigma > 0, lambda >= 0)
  *   sel         [batch, H, N, K] int32, (score desc, id asc), -1 padded (output)
  */
 fs_status fs_score_select(const fs_shape *shape, const fs_params *prm, const void *q, const float *kbar,
-                          const float *a, const int32_t *retained, const int32_t *n_retained,
-                          const float *sigma_h, const float *lambda_h, int32_t *sel, void *stream);
+                          const uint16_t *kbar_split, const float *a, const int32_t *retained,
+                          const int32_t *n_retained, const float *sigma_h, const float *lambda_h,
+                          int32_t *sel, void *stream);
 
 /*
  * Token readout and RMSNorm, Eq. 9 (softmax over the tokens of the selected
@@ -126,6 +135,27 @@ fs_status fs_score_select(const fs_shape *shape, const fs_params *prm, const voi
  */
 fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k, const void *v,
                      const int32_t *sel, const float *gain, void *out, void *stream);
+
+/*
+ * Routing and readout in one call: fs_score_select followed by fs_readout
+ * (Eq. 7, per-query top-K, Eq. 9 with Eq. 17's RMSNorm), same arguments and
+ * results.  For bf16 shapes given kbar_split (and FS, or FS-L with P + W <=
+ * 256) it runs as a single kernel in which each 128-query block scores its
+ * retained cells, selects, and reads out its selected cells without the
+ * selections going through global memory; the outputs are bitwise those of
+ * the two separate calls.
+ *   q, k, v                [batch, H, N, d]  shape dtype (input)
+ *   kbar, kbar_split, a    from fs_cell_summaries (kbar_split may be NULL)
+ *   retained, n_retained   from fs_prune_retained (FS-L; NULL for FS)
+ *   sigma_h, lambda_h      host [H] fp32;  gain  device [H, d] fp32 or NULL
+ *   out                    [batch, H, N, d] shape dtype (output)
+ *   sel                    [batch, H, N, K] int32 (output); may be NULL only
+ *                          when the single-kernel form applies
+ */
+fs_status fs_select_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
+                            const void *v, const float *kbar, const uint16_t *kbar_split, const float *a,
+                            const int32_t *retained, const int32_t *n_retained, const float *sigma_h,
+                            const float *lambda_h, const float *gain, void *out, int32_t *sel, void *stream);
 
 /* Bytes of workspace fs_longrange_prefill needs (0 on invalid arguments). */
 size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm);

@@ -62,10 +62,11 @@ def test_cell_summaries(w):
     M = w.N // 32
     kbar = torch.empty(w.batch, w.H, M, w.d, dtype=torch.float32, device="cuda")
     a = torch.empty(w.batch, w.H, M, dtype=torch.float32, device="cuda")
+    ks = torch.full((w.batch, w.H, M, 3, w.d), -1, dtype=torch.int16, device="cuda")
     print(f"[gpu] summaries {w}", flush=True)
-    fsl.fs_cell_summaries(k, kbar, a)
+    fsl.fs_cell_summaries(k, kbar, a, kbar_split=ks)
     torch.cuda.synchronize()
-    kbar, a = kbar.cpu().numpy(), a.cpu().numpy()
+    kbar, a, ks = kbar.cpu().numpy(), a.cpu().numpy(), ks.cpu().numpy().view(np.uint16)
     import oracle
     for b in range(w.batch):
         for h in range(w.H):
@@ -73,6 +74,24 @@ def test_cell_summaries(w):
             # fp64 sums rounded once: the mean is the correctly rounded fp32 of the exact mean
             np.testing.assert_array_equal(kbar[b, h], rk.astype(np.float32))
             np.testing.assert_allclose(a[b, h], ra, rtol=1.2e-7, atol=0)
+    if w.dtype == "bf16":
+        # the three bf16 parts: hi = bf16(kbar), mid = bf16(kbar - hi), lo = bf16(kbar - hi - mid), nearest-even
+        def rne(x):
+            u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+            return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+        def widen(hb):
+            return (hb.astype(np.uint32) << 16).view(np.float32)
+
+        hi = rne(kbar)
+        r1 = (kbar - widen(hi)).astype(np.float32)
+        mid = rne(r1)
+        lo = rne((r1 - widen(mid)).astype(np.float32))
+        np.testing.assert_array_equal(ks[..., 0, :], hi)
+        np.testing.assert_array_equal(ks[..., 1, :], mid)
+        np.testing.assert_array_equal(ks[..., 2, :], lo)
+    else:
+        assert np.all(ks == 0xFFFF)  # not written for fp32 shapes
 
 
 # ------------------------------------------------------------------ pruning ----
@@ -98,19 +117,23 @@ def test_prune_retained(w, P, W):
     print(f"[gpu] prune {w} P={P} W={W}", flush=True)
     fsl.fs_prune_retained(sh, a, ret, nret, ws, p)
     torch.cuda.synchronize()
-    ret, nret = ret.cpu().numpy(), nret.cpu().numpy()
+    ret, nret, a_gpu = ret.cpu().numpy(), nret.cpu().numpy(), a.cpu().numpy()
     import oracle
     op = pu.oracle_params(p)
     for b in range(w.batch):
         for h in range(w.H):
             ref = oracle.head(None, synth.to_f64(host["k"][b, h], w.dtype), None, prm=op, want_out=False)
             for beta in range(NB):
+                n = nret[b, h, beta]
+                row = ret[b, h, beta, :n]
+                # listed in priority order (a desc, id asc) of the norms the GPU computed
+                key = [(-a_gpu[b, h, c], c) for c in row]
+                assert key == sorted(key), (b, h, beta)
+                assert np.all(ret[b, h, beta, n:] == -1)
                 if ref["gap_p"][beta] < pu.NEAR_TIE:
                     continue
-                n = ref["n_ret"][beta]
-                assert nret[b, h, beta] == n, (b, h, beta)
-                np.testing.assert_array_equal(ret[b, h, beta, :n], ref["retained"][beta, :n])
-                assert np.all(ret[b, h, beta, n:] == -1)
+                assert n == ref["n_ret"][beta], (b, h, beta)
+                np.testing.assert_array_equal(np.sort(row), ref["retained"][beta, :n])
 
 
 # ------------------------------------------------------------ whole prefill ----
@@ -180,3 +203,73 @@ def test_fs_32k_sampled():
     """FS (no pruning), b1 H16 d128 N32768 bf16: up to 1020 cells scored per query."""
     w = synth.WORKLOADS["fs_32k"]
     check(w, fsl.Params(prune=False), heads=[(0, 3), (0, 12)])
+
+
+def test_score_with_precomputed_split_matches():
+    """fs_score_select with the bf16 parts from fs_cell_summaries selects exactly what it
+    selects when it splits the fp32 means itself (same operands on the matrix cores)."""
+    w = synth.Workload(batch=2, H=2, N=3000, d=128, dtype="bf16", seed=71, needle_frac=0.01)
+    p = fsl.Params()
+    host = pu.inputs(w)
+    q, k = (pu.to_device(host[x], w.dtype) for x in "qk")
+    M, NB = w.N // 32, (w.N + 127) // 128
+    kbar = torch.empty(w.batch, w.H, M, w.d, dtype=torch.float32, device="cuda")
+    a = torch.empty(w.batch, w.H, M, dtype=torch.float32, device="cuda")
+    ks = torch.empty(w.batch, w.H, M, 3, w.d, dtype=torch.int16, device="cuda")
+    fsl.fs_cell_summaries(k, kbar, a, p, kbar_split=ks)
+    sh = fsl.shape_of(k)
+    ws = torch.empty(fsl.fs_prune_workspace_bytes(sh, p), dtype=torch.uint8, device="cuda")
+    ret = torch.empty(w.batch, w.H, NB, p.P + p.W, dtype=torch.int32, device="cuda")
+    nret = torch.empty(w.batch, w.H, NB, dtype=torch.int32, device="cuda")
+    fsl.fs_prune_retained(sh, a, ret, nret, ws, p)
+    s1 = torch.empty(w.batch, w.H, w.N, p.K, dtype=torch.int32, device="cuda")
+    s2 = torch.empty_like(s1)
+    print("[gpu] score with and without split operands", flush=True)
+    fsl.fs_score_select(q, kbar, a, ret, nret, 4.0, 1.0, s1, p)
+    fsl.fs_score_select(q, kbar, a, ret, nret, 4.0, 1.0, s2, p, kbar_split=ks)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("w,p,extra", [
+    (synth.Workload(batch=2, H=2, N=2000, d=128, dtype="bf16", seed=72, needle_frac=0.005), fsl.Params(), {}),
+    (synth.Workload(batch=1, H=3, N=1500, d=64, dtype="bf16", seed=73, needle_frac=0.01), fsl.Params(P=6, W=2, K=3),
+     {"gain": True}),
+    (synth.Workload(batch=1, H=2, N=1300, d=128, dtype="bf16", seed=74, needle_frac=0.01), fsl.Params(prune=False),
+     {}),
+    (synth.Workload(batch=1, H=2, N=1111, d=128, dtype="bf16", seed=75), fsl.Params(P=9, W=3, K=8), {"lam": 0.0}),
+    (synth.Workload(batch=1, H=2, N=100, d=64, dtype="bf16", seed=76), fsl.Params(P=2, W=1), {}),
+], ids=["d128", "d64-K3-gain", "FS", "K8-lam0", "one-block"])
+def test_fused_route_readout_matches_two_kernels(w, p, extra):
+    """fs_select_readout in its single-kernel form gives bitwise the selections and outputs
+    of fs_score_select followed by fs_readout."""
+    host = pu.inputs(w)
+    q, k, v = (pu.to_device(host[x], w.dtype) for x in "qkv")
+    gain = torch.from_numpy(synth.gains(97, w.H, w.d)).cuda() if extra.get("gain") else None
+    lam = extra.get("lam", 1.0)
+    M, NB = w.N // 32, (w.N + 127) // 128
+    kbar = torch.empty(w.batch, w.H, max(M, 1), w.d, dtype=torch.float32, device="cuda")
+    a = torch.empty(w.batch, w.H, max(M, 1), dtype=torch.float32, device="cuda")
+    ks = torch.empty(w.batch, w.H, max(M, 1), 3, w.d, dtype=torch.int16, device="cuda")
+    fsl.fs_cell_summaries(k, kbar, a, p, kbar_split=ks)
+    ret = nret = None
+    if p.prune:
+        sh = fsl.shape_of(k)
+        ws = torch.empty(fsl.fs_prune_workspace_bytes(sh, p), dtype=torch.uint8, device="cuda")
+        ret = torch.empty(w.batch, w.H, NB, p.P + p.W, dtype=torch.int32, device="cuda")
+        nret = torch.empty(w.batch, w.H, NB, dtype=torch.int32, device="cuda")
+        fsl.fs_prune_retained(sh, a, ret, nret, ws, p)
+    s1 = torch.empty(w.batch, w.H, w.N, p.K, dtype=torch.int32, device="cuda")
+    s2 = torch.full_like(s1, -7)
+    o1 = torch.empty_like(q)
+    o2 = torch.empty_like(q)
+    print(f"[gpu] fused vs two kernels {w} {p}", flush=True)
+    fsl.fs_score_select(q, kbar, a, ret, nret, 4.0, lam, s1, p, kbar_split=ks)
+    fsl.fs_readout(q, k, v, s1, gain, o1, p)
+    fsl.fs_select_readout(q, k, v, kbar, a, ret, nret, 4.0, lam, gain, o2, s2, p, kbar_split=ks)
+    o3 = torch.empty_like(q)
+    fsl.fs_select_readout(q, k, v, kbar, a, ret, nret, 4.0, lam, gain, o3, None, p, kbar_split=ks)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
