@@ -155,6 +155,58 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float x0, float x1)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// The ranking (score desc, id asc) as one order-preserving 64-bit key: the
+// score's bits made monotone above 0x7fffffff - id.  A larger key ranks
+// first; 0 marks an empty entry (every real key is larger).
+__device__ __forceinline__ uint64_t rank_key(float score, uint32_t low)
+{
+    uint32_t u = __float_as_uint(score + 0.0f); // -0 -> +0: equal scores must tie
+    u ^= (uint32_t)((int32_t)u >> 31) | 0x80000000u;
+    return ((uint64_t)u << 32) | low;
+}
+
+// Insert key into the descending list kl of KT keys (a select network: a key
+// below the last entry moves nothing).
+template <int KT>
+__device__ __forceinline__ void insert_key(uint64_t (&kl)[KT], uint64_t key)
+{
+#pragma unroll
+    for (int j = KT - 1; j > 0; --j)
+        kl[j] = key > kl[j - 1] ? kl[j - 1] : (key > kl[j] ? key : kl[j]);
+    kl[0] = key > kl[0] ? key : kl[0];
+}
+
+
+// Enter one scored tile's 16 keys of this lane into its descending top-KT list.
+// On the first tile the list is empty and its first KT keys go in without a
+// test.  The rest are first tested as a group against the K-th best (on the
+// high words, which can only let too many through): the retained cells come
+// in priority order, so after the first tile a key seldom enters, and a wave
+// skips the select network unless one of its lanes keeps one of these keys.
+// The keys are consumed.
+template <int KT>
+__device__ __forceinline__ void take_tile_keys(uint64_t (&kl)[KT], uint64_t (&key)[16], bool first)
+{
+    if (first) {
+#pragma unroll
+        for (int r = 0; r < KT && r < 16; ++r) {
+            insert_key<KT>(kl, key[r]);
+            key[r] = 0; // now in the list: must not enter twice
+        }
+    }
+    const uint32_t kth = (uint32_t)(kl[KT - 1] >> 32);
+    bool any = false;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        any |= (uint32_t)(key[r] >> 32) >= kth;
+    if (__ballot(any) == 0ull)
+        return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (__ballot(key[r] > kl[KT - 1]))
+            insert_key<KT>(kl, key[r]);
+}
+
 // ---- coalesced tile transfers through LDS (bf16, 128 rows) -------------------
 // A workgroup's 128 query rows are one contiguous span of global memory, while
 // the matrix-core layouts give each lane one row.  Moving a tile through LDS

@@ -25,17 +25,24 @@
 #include "fsl_internal.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace fsl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kLazy = 8.0f; // the softmax running max moves only when it grows by more than 2^8
+constexpr float kLazy = 16.0f; // the softmax running max moves only when it grows by more than 2^16
+
+// V^T rows keep a cell's 32 tokens in the order 0-3, 8-11, 4-7, 12-15, 16-19,
+// 24-27, 20-23, 28-31: then the 8 tokens a lane feeds to one P.V product
+// (16 kk + 4 half + 0..3 and 16 kk + 8 + 4 half + 0..3, the order of its
+// probabilities in the logits accumulator) are 16 contiguous bytes.
+__device__ __forceinline__ int vt_pos(int tok) { return tok ^ (((tok >> 2) ^ (tok >> 3)) & 1) * 12; }
 
 template <int D>
 struct alignas(16) FusedSmem {
     static constexpr int kStride = D + 8;   // bf16 elements per row (16-byte pad against bank conflicts)
-    static constexpr int kStrideV = 32 + 4; // bf16 elements per V^T row
+    static constexpr int kStrideV = 32 + 8; // bf16 elements per V^T row (80 bytes: 16-byte aligned, conflict-free)
     union {
         uint16_t kb[3][32][kStride]; // routing: one tile of mean-key parts
         struct {                     // readout: one cell
@@ -48,27 +55,6 @@ struct alignas(16) FusedSmem {
     float pc[32];
     int32_t id[32];
 };
-
-// The ranking (score desc, id asc) as one order-preserving 64-bit key: the
-// score's bits made monotone above 0x7fffffff - id.  A larger key ranks
-// first; 0 marks an empty entry (every real key is larger).
-__device__ __forceinline__ uint64_t rank_key(float score, uint32_t low)
-{
-    uint32_t u = __float_as_uint(score + 0.0f); // -0 -> +0: equal scores must tie
-    u ^= (uint32_t)((int32_t)u >> 31) | 0x80000000u;
-    return ((uint64_t)u << 32) | low;
-}
-
-// Insert key into the descending list kl of KT keys (a select network: a key
-// below the last entry moves nothing).
-template <int KT>
-__device__ __forceinline__ void insert_key(uint64_t (&kl)[KT], uint64_t key)
-{
-#pragma unroll
-    for (int j = KT - 1; j > 0; --j)
-        kl[j] = key > kl[j - 1] ? kl[j - 1] : (key > kl[j] ? key : kl[j]);
-    kl[0] = key > kl[0] ? key : kl[0];
-}
 
 template <int D, int KT>
 __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
@@ -172,17 +158,25 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             prefetch(t0 + 32); // overlaps the matrix work below
 
         f32x16 acc;
+        // three independent accumulators (lo, mid, hi parts) keep the matrix cores busy;
+        // the parts are added smallest first
+        f32x16 acc3[3];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            acc[r] = 0.0f;
+        for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-        for (int sp = 2; sp >= 0; --sp) { // smallest parts first
+            for (int r = 0; r < 16; ++r)
+                acc3[sp][r] = 0.0f;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
+        for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+            for (int sp = 2; sp >= 0; --sp) {
                 const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.kb[sp][col][kc * 16 + half * 8]);
-                acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
+                acc3[sp] = mfma_bf16(as_bf16x8(w), qf[kc], acc3[sp]);
             }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[r] = (acc3[2][r] + acc3[1][r]) + acc3[0][r];
         // erf only below 4 (above it rounds to 1 in fp32); see the scorer
         // this lane's 16 rows come in 4 runs of 4 consecutive rows: 12 vector LDS reads
         float prv[16], pcv[16];
@@ -208,19 +202,25 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         for (int r = 1; r < 16; ++r)
             pcmax = fmaxf(pcmax, pcv[r]);
         const bool need_erf = __ballot(q_ok && (qpos - pcmax) * inv2s < 4.0f) != 0ull;
+        uint64_t key[16];
+        if (need_erf) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float g = 1.0f;
-            if (need_erf) {
+            for (int r = 0; r < 16; ++r) {
+                float g = 1.0f;
                 const float x = (qpos - pcv[r]) * inv2s; // (i - p_c) / (2 sigma_h), i - p_c exact
                 if (x < 4.0f)
                     g = erff(x);
+                const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
             }
-            const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
-            const uint64_t key = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-            if (__ballot(key > kl[KT - 1])) // wave-uniform: in priority order most cells fall below every K-th best
-                insert_key<KT>(kl, key);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float score = fmaf(prv[r], 1.0f, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
+            }
         }
+        take_tile_keys<KT>(kl, key, t0 == 0);
     }
     // merge with the partner lane (same query, other 16 rows of every tile)
     {
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             for (int e = 0; e < 8; ++e) {
                 const uint32_t a0 = (pv0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
                 const uint32_t a1 = (pv1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][2 * tp]) = a0 | (a1 << 16);
+                *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][vt_pos(2 * tp)]) = a0 | (a1 << 16);
             }
         }
         __syncthreads();
@@ -348,32 +348,37 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         if (__ballot(mine) == 0ull)
             continue; // no query of this wave reads the cell
 
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            acc[r] = 0.0f;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
-            acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
-        }
-        float p[16];
-        float tmax = -INFINITY;
+        f32x16 acc, acc2; // even and odd k-steps: two independent chains
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p[r] = acc[r] * scale_log2;
-            tmax = fmaxf(tmax, p[r]);
+            acc[r] = 0.0f;
+            acc2[r] = 0.0f;
         }
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+#pragma unroll
+        for (int kc = 0; kc < KC; kc += 2) {
+            const u32x4 w0 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
+            const u32x4 w1 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + 16 + half * 8]);
+            acc = mfma_bf16(as_bf16x8(w0), qf[kc], acc);
+            acc2 = mfma_bf16(as_bf16x8(w1), qf[kc + 1], acc2);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[r] += acc2[r];
+        float p[16];
+        float amax = acc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+            amax = fmaxf(amax, acc[r]);
+        const float tmax = fmaxf(amax, shfl_xor_f(amax, 32)) * scale_log2; // scale > 0: max commutes
         float alpha = 1.0f, psum = 0.0f;
         if (mine) {
-            if (tmax > m_run + kLazy) {
-                alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+            if (tmax > m_run + kLazy) { // a much larger logit; on the first cell o and l are still 0
+                alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - tmax);
                 m_run = tmax;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(p[r] - m_run);
+                p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -m_run)); // <= 2^16
                 psum += p[r];
             }
         } else {
@@ -401,15 +406,16 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
                 pl[w] = cvt_pk_bf16(x0 - bf16_bits_to_f32(hp & 0xffffu), x1 - bf16_bits_to_f32(hp >> 16));
             }
             const bf16x8 bh = as_bf16x8(ph), bl = as_bf16x8(pl);
+            bf16x8 av[DT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int m = dt * 32 + col;
-                const u32x2 lo4 = *reinterpret_cast<const u32x2 *>(&sm.vt[m][16 * kk + 4 * half]);
-                const u32x2 hi4 = *reinterpret_cast<const u32x2 *>(&sm.vt[m][16 * kk + 8 + 4 * half]);
-                const bf16x8 av = as_bf16x8(u32x4{lo4[0], lo4[1], hi4[0], hi4[1]});
-                o_acc[dt] = mfma_bf16(av, bl, o_acc[dt]);
-                o_acc[dt] = mfma_bf16(av, bh, o_acc[dt]);
-            }
+            for (int dt = 0; dt < DT; ++dt)
+                av[dt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.vt[dt * 32 + col][16 * kk + 8 * half]));
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) // lo parts of every tile, then hi parts: no back-to-back chain
+                o_acc[dt] = mfma_bf16(av[dt], bl, o_acc[dt]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o_acc[dt] = mfma_bf16(av[dt], bh, o_acc[dt]);
         }
     }
 
@@ -426,22 +432,31 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         }
     ms += shfl_xor_f(ms, 32);
     const float rs = 1.0f / sqrtf(ms / (float)D + eps);
-    const float *gh = gain ? gain + (int64_t)h * D : nullptr;
     __syncthreads(); // the last cell's LDS reads are done: the tile area takes the output
+    // one straight-line copy with the gain vector and one without (the test is uniform)
+    auto emit = [&](auto with_gain) {
+        const float *gh = gain + (int64_t)h * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const int d0 = dt * 32 + 8 * rg + 4 * half;
-            float y[4];
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d0 = dt * 32 + 8 * rg + 4 * half;
+                float y[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float gv = gh ? gh[d0 + e] : 1.0f;
-                y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+                for (int e = 0; e < 4; ++e) {
+                    float gv = 1.0f;
+                    if constexpr (decltype(with_gain)::value)
+                        gv = gh[d0 + e];
+                    y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+                }
+                *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
+                    u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};
             }
-            *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
-                u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};
-        }
+    };
+    if (gain)
+        emit(std::true_type{});
+    else
+        emit(std::false_type{});
     __syncthreads();
     tile_store_bf16<D, kThreads>(out + (head * N + q0) * D, &sm.tile[0][0], sm.kStride,
                                  (int)(N - q0 < 128 ? N - q0 : 128));

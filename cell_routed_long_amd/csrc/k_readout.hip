@@ -21,8 +21,8 @@
 // the probabilities are split into bf16 hi + lo parts for the P.V product so
 // that the readout keeps ~16 mantissa bits before the final rounding.  fp32
 // tensors use the fp32 MFMA.  The softmax runs in the exp2 domain with a lazy
-// running max: it is raised only when a logit exceeds it by more than 8 (so
-// every weight stays below 2^8 and the accumulators are rescaled rarely); the
+// running max: it is raised only when a logit exceeds it by more than 16 (so
+// every weight stays below 2^16 and the accumulators are rescaled rarely); the
 // result is the same softmax up to rounding.  The next cell's keys and values
 // are fetched into registers while the current cell is on the matrix cores.
 #include "fsl_internal.h"
@@ -33,7 +33,13 @@ namespace fsl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kLazy = 8.0f; // the running max moves only when it grows by more than 2^8
+constexpr float kLazy = 16.0f; // the running max moves only when it grows by more than 2^16
+
+// V^T rows keep a cell's 32 tokens in the order 0-3, 8-11, 4-7, 12-15, 16-19,
+// 24-27, 20-23, 28-31: then the 8 tokens a lane feeds to one P.V product
+// (16 kk + 4 half + 0..3 and 16 kk + 8 + 4 half + 0..3, the order of its
+// probabilities in the logits accumulator) are 16 contiguous bytes.
+__device__ __forceinline__ int vt_pos(int tok) { return tok ^ (((tok >> 2) ^ (tok >> 3)) & 1) * 12; }
 
 template <typename T, int D>
 struct ReadoutSmem;
@@ -41,7 +47,7 @@ struct ReadoutSmem;
 template <int D>
 struct alignas(16) ReadoutSmem<uint16_t, D> {
     static constexpr int kStrideK = D + 8; // bf16 elements per K row
-    static constexpr int kStrideV = 32 + 4; // bf16 elements per V^T row (72 bytes)
+    static constexpr int kStrideV = 32 + 8; // bf16 elements per V^T row (80 bytes: 16-byte aligned, conflict-free)
     static constexpr int kStrideT = D + 8; // bf16 elements per row of a 128-row query/output tile
     union {
         struct {
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t a0 = (pv0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
                     const uint32_t a1 = (pv1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][2 * tp]) = a0 | (a1 << 16);
+                    *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][vt_pos(2 * tp)]) = a0 | (a1 << 16);
                 }
             }
         } else {
@@ -244,11 +250,20 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
         for (int r = 0; r < 16; ++r)
             acc[r] = 0.0f;
         if constexpr (kBf16) {
+            f32x16 acc2; // even and odd k-steps: two independent chains
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
-                acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
+            for (int r = 0; r < 16; ++r)
+                acc2[r] = 0.0f;
+#pragma unroll
+            for (int kc = 0; kc < KC; kc += 2) {
+                const u32x4 w0 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
+                const u32x4 w1 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + 16 + half * 8]);
+                acc = mfma_bf16(as_bf16x8(w0), qf[kc], acc);
+                acc2 = mfma_bf16(as_bf16x8(w1), qf[kc + 1], acc2);
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[r] += acc2[r];
         } else {
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
@@ -257,22 +272,20 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
 
         // ---- online softmax over the query's own tokens (exp2 domain) ----
         float p[16];
-        float tmax = -INFINITY;
+        float amax = acc[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = acc[r] * scale_log2;
-            tmax = fmaxf(tmax, p[r]);
-        }
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        for (int r = 1; r < 16; ++r)
+            amax = fmaxf(amax, acc[r]);
+        const float tmax = fmaxf(amax, shfl_xor_f(amax, 32)) * scale_log2; // scale > 0: max commutes
         float alpha = 1.0f, psum = 0.0f;
         if (mine) {
-            if (tmax > m_run + kLazy) { // first cell (m_run = -inf) or a much larger logit
-                alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+            if (tmax > m_run + kLazy) { // a much larger logit; on the first cell o and l are still 0
+                alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - tmax);
                 m_run = tmax;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(p[r] - m_run); // <= 2^8
+                p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -m_run)); // <= 2^16
                 psum += p[r];
             }
         } else {
@@ -303,15 +316,16 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
                     pl[w] = cvt_pk_bf16(x0 - bf16_bits_to_f32(hp & 0xffffu), x1 - bf16_bits_to_f32(hp >> 16));
                 }
                 const bf16x8 bh = as_bf16x8(ph), bl = as_bf16x8(pl);
+                bf16x8 av[DT];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int m = dt * 32 + col;
-                    const u32x2 lo4 = *reinterpret_cast<const u32x2 *>(&sm.vt[m][16 * kk + 4 * half]);
-                    const u32x2 hi4 = *reinterpret_cast<const u32x2 *>(&sm.vt[m][16 * kk + 8 + 4 * half]);
-                    const bf16x8 av = as_bf16x8(u32x4{lo4[0], lo4[1], hi4[0], hi4[1]});
-                    o_acc[dt] = mfma_bf16(av, bl, o_acc[dt]);
-                    o_acc[dt] = mfma_bf16(av, bh, o_acc[dt]);
-                }
+                for (int dt = 0; dt < DT; ++dt)
+                    av[dt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.vt[dt * 32 + col][16 * kk + 8 * half]));
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) // lo parts of every tile, then hi parts: no back-to-back chain
+                    o_acc[dt] = mfma_bf16(av[dt], bl, o_acc[dt]);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    o_acc[dt] = mfma_bf16(av[dt], bh, o_acc[dt]);
             }
         } else {
 #pragma unroll
@@ -335,42 +349,57 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
         }
     ms += shfl_xor_f(ms, 32);
     const float rs = 1.0f / sqrtf(ms / (float)D + eps);
-    const float *gh = gain ? gain + (int64_t)h * D : nullptr;
+    const float *gh = gain + (int64_t)h * D;
+    // y = g * u * rs for the four features d0..d0+3 (g = 1 without a gain vector;
+    // the test is uniform, so each copy below is straight-line code)
+    auto rms4 = [&](float (&y)[4], int dt, int rg, int d0, auto with_gain) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float gv = 1.0f;
+            if constexpr (decltype(with_gain)::value)
+                gv = gh[d0 + e];
+            y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+        }
+    };
     if constexpr (kBf16) {
         __syncthreads(); // the last cell's LDS reads are done: the tile area takes the output
+        auto emit = [&](auto with_gain) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = dt * 32 + 8 * rg + 4 * half;
-                float y[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float gv = gh ? gh[d0 + e] : 1.0f;
-                    y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int d0 = dt * 32 + 8 * rg + 4 * half;
+                    float y[4];
+                    rms4(y, dt, rg, d0, with_gain);
+                    *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
+                        u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};
                 }
-                *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
-                    u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};
-            }
+        };
+        if (gain)
+            emit(std::true_type{});
+        else
+            emit(std::false_type{});
         __syncthreads();
         tile_store_bf16<D, kThreads>(reinterpret_cast<uint16_t *>(out) + (head * N + q0) * D, &sm.tile[0][0],
                                      sm.kStrideT, rows);
     } else if (q_ok) {
         T *dst = out + (head * N + qi) * D;
+        auto emit = [&](auto with_gain) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d0 = dt * 32 + 8 * rg + 4 * half;
-                float y[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float gv = gh ? gh[d0 + e] : 1.0f;
-                    y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int d0 = dt * 32 + 8 * rg + 4 * half;
+                    float y[4];
+                    rms4(y, dt, rg, d0, with_gain);
+                    *reinterpret_cast<u32x4 *>(dst + d0) = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]),
+                                                                 __float_as_uint(y[2]), __float_as_uint(y[3])};
                 }
-                *reinterpret_cast<u32x4 *>(dst + d0) = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]),
-                                                             __float_as_uint(y[2]), __float_as_uint(y[3])};
-            }
+        };
+        if (gain)
+            emit(std::true_type{});
+        else
+            emit(std::false_type{});
     }
 }
 

@@ -48,27 +48,6 @@ struct alignas(16) ScoreSmem<float, D> {
     int32_t id[32];
 };
 
-// The ranking (score desc, id asc) as one order-preserving 64-bit key: the
-// score's bits made monotone above 0x7fffffff - id.  A larger key ranks
-// first; 0 marks an empty entry (every real key is larger).
-__device__ __forceinline__ uint64_t rank_key(float score, uint32_t low)
-{
-    uint32_t u = __float_as_uint(score + 0.0f); // -0 -> +0: equal scores must tie
-    u ^= (uint32_t)((int32_t)u >> 31) | 0x80000000u;
-    return ((uint64_t)u << 32) | low;
-}
-
-// Insert key into the descending list kl of KT keys (a select network: a key
-// below the last entry moves nothing).
-template <int KT>
-__device__ __forceinline__ void insert_key(uint64_t (&kl)[KT], uint64_t key)
-{
-#pragma unroll
-    for (int j = KT - 1; j > 0; --j)
-        kl[j] = key > kl[j - 1] ? kl[j - 1] : (key > kl[j] ? key : kl[j]);
-    kl[0] = key > kl[0] ? key : kl[0];
-}
-
 template <typename T, int D, int KT, bool kPre>
 __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     const T *__restrict__ q, const float *__restrict__ kbar, const uint16_t *__restrict__ kbar_split,
@@ -212,19 +191,30 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
 
         // ---- S^T[32 cells x 32 queries] on the matrix cores ----
         f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            acc[r] = 0.0f;
         if constexpr (kBf16) {
+            // three independent accumulators (lo, mid, hi parts) keep the matrix cores busy;
+            // the parts are added smallest first
+            f32x16 acc3[3];
 #pragma unroll
-            for (int sp = 2; sp >= 0; --sp) { // smallest parts first
+            for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
+                for (int r = 0; r < 16; ++r)
+                    acc3[sp][r] = 0.0f;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+                for (int sp = 2; sp >= 0; --sp) {
                     const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.kb[sp][col][kc * 16 + half * 8]);
-                    acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
+                    acc3[sp] = mfma_bf16(as_bf16x8(w), qf[kc], acc3[sp]);
                 }
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[r] = (acc3[2][r] + acc3[1][r]) + acc3[0][r];
         } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[r] = 0.0f;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
                 acc = mfma_f32(sm.kb[col][kc * 2 + half], qf[kc], acc);
@@ -259,19 +249,25 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
         for (int r = 1; r < 16; ++r)
             pcmax = fmaxf(pcmax, pcv[r]);
         const bool need_erf = __ballot(q_ok && (qpos - pcmax) * inv2s < 4.0f) != 0ull;
+        uint64_t key[16];
+        if (need_erf) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float g = 1.0f;
-            if (need_erf) {
+            for (int r = 0; r < 16; ++r) {
+                float g = 1.0f;
                 const float x = (qpos - pcv[r]) * inv2s; // (i - p_c) / (2 sigma_h), i - p_c exact
                 if (x < 4.0f)
                     g = erff(x);
+                const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
             }
-            const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
-            const uint64_t key = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-            if (__ballot(key > kl[KT - 1])) // wave-uniform: in priority order most cells fall below every K-th best
-                insert_key<KT>(kl, key);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float score = fmaf(prv[r], 1.0f, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
+            }
         }
+        take_tile_keys<KT>(kl, key, t0 == 0);
     }
 
     // ---- merge with the partner lane (same query, other 16 rows) ----
