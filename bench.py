@@ -26,7 +26,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "long-range FS-L query-tokens/s at 16k prefill; % HBM/MFMA roofline"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "readout_16k_counters.json")
 DECODE_METRIC = "long-range FS-L decode query-tokens/s at a 262,144-token context; % HBM roofline"
 WORKLOADS = {
     "prefill_16k": dict(prune=True),
@@ -42,10 +41,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest(name: str) -> str:
-    path = os.path.join(ROOT, "cell_routed_long_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_digest(names) -> str:
+    """First 16 hex digits of the SHA-256 of the named csrc files, concatenated."""
+    h = hashlib.sha256()
+    for name in ([names] if isinstance(names, str) else names):
+        with open(os.path.join(ROOT, "cell_routed_long_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
+    summary for this workload, or None when there is none or the kernel's source
+    changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        cnt = json.load(f)
+    if (cnt.get("kernel") != kernel or cnt.get("workload") != workload or
+            cnt.get("source_sha256_16") != kernel_source_digest(cnt["sources"])):
+        return None
+    return int(cnt["hbm_bytes_per_launch"])
 
 
 def distinct_cells_per_block(sel, B: int):
@@ -217,13 +234,7 @@ def main() -> int:
     dom_t = per_kernel_ms[dominant] * 1e-3
     achieved = alg[dominant]["bytes"] / dom_t / 1e9
 
-    traffic = None
-    if os.path.exists(COUNTERS_FILE):
-        with open(COUNTERS_FILE) as f:
-            cnt = json.load(f)
-        if (cnt.get("kernel") == dominant and cnt.get("workload") == args.workload and
-                cnt.get("source_sha256_16") == kernel_source_digest(cnt["source"])):
-            traffic = int(cnt["hbm_bytes_per_launch"])
+    traffic = measured_traffic(dominant, args.workload)
 
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dominant,
@@ -410,6 +421,13 @@ def run_decode(args) -> int:
     torch.cuda.synchronize()
     eager_us = ev0.elapsed_time(ev1) / (steps * R) * 1e3
 
+    if args.copy_calibration:  # a 1 GiB copy whose bytes are known, for HBM counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- algorithmic bytes per launch (one step of every (sequence, head)) ----
     n_sel = np.count_nonzero(sel_h >= 0, axis=-1)  # [steps, b, H]
     n_ret = min(prm.P + prm.W, N0 // prm.s)
@@ -419,8 +437,8 @@ def run_decode(args) -> int:
     alg_bytes = b * H * per_pair + float(n_sel.mean()) * b * H * prm.s * d * 2 * 2
     achieved = alg_bytes / (per_launch_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_step_kernel",
-                "alg_bytes_per_launch": int(alg_bytes)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_step", "decode_256k"),
+                "kernel": "decode_step", "alg_bytes_per_launch": int(alg_bytes)}
     value = b * steps * R / (graph_ms * 1e-3)
 
     cpu = parity = None
