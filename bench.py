@@ -129,6 +129,7 @@ def main() -> int:
     M, NB, cap = N // prm.s, (N + prm.B - 1) // prm.B, prm.P + prm.W
     kbar = torch.empty(b, H, M, d, dtype=torch.float32, device=dev)
     kbar_split = torch.empty(b, H, M, 3, d, dtype=torch.int16, device=dev) if w.dtype == "bf16" else None
+    kbar_norm = torch.empty(b, H, M, dtype=torch.float32, device=dev) if w.dtype == "bf16" else None
     a = torch.empty(b, H, M, dtype=torch.float32, device=dev)
     sh = fsl.shape_of(k)
     ws = torch.empty(max(1, fsl.fs_prune_workspace_bytes(sh, prm)), dtype=torch.uint8, device=dev)
@@ -143,7 +144,7 @@ def main() -> int:
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        fsl.fs_cell_summaries(k, kbar, a, prm, kbar_split=kbar_split)
+        fsl.fs_cell_summaries(k, kbar, a, prm, kbar_split=kbar_split, kbar_norm=kbar_norm)
         if evs is not None:
             evs[1].record(stream)
         if prm.prune:
@@ -152,7 +153,7 @@ def main() -> int:
             evs[2].record(stream)
         # scores, top-K and the gather-readout: one kernel for bf16 (fs_score_select + fs_readout otherwise)
         fsl.fs_select_readout(q, k, v, kbar, a, retained if prm.prune else None, n_ret if prm.prune else None,
-                              sigma, lam, None, out, sel, prm, kbar_split=kbar_split)
+                              sigma, lam, None, out, sel, prm, kbar_split=kbar_split, kbar_norm=kbar_norm)
         if evs is not None:
             evs[3].record(stream)
 
@@ -212,7 +213,8 @@ def main() -> int:
     # algorithmic bytes: each input read once, each output written once, the summaries (and their bf16 parts)
     # read once per head, and the keys/values of every block's distinct selected cells once per block
     alg = {
-        "cell_summaries": dict(bytes=qkv_bytes + b * H * M * (d + 1) * 4 + (b * H * M * 3 * d * 2 if esz == 2 else 0)),
+        "cell_summaries": dict(bytes=qkv_bytes + b * H * M * (d + 1) * 4
+                               + (b * H * M * (3 * d * 2 + 4) if esz == 2 else 0)),
         "prune": dict(bytes=b * H * M * 4 * 2 + b * H * NB * (cap + 1) * 4 if prm.prune else 0),
         "route_readout": dict(bytes=2 * qkv_bytes + b * H * M * (d * (6 if esz == 2 else 4) + 4)
                               + (b * H * NB * (cap + 1) * 4 if prm.prune else 0) + b * H * N * prm.K * 4

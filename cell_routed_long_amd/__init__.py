@@ -64,13 +64,13 @@ def lib():
         P_shape, P_prm = ctypes.POINTER(fs_shape), ctypes.POINTER(fs_params)
         L.fs_status_string.argtypes = [ctypes.c_int]
         L.fs_status_string.restype = ctypes.c_char_p
-        L.fs_cell_summaries.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp]
+        L.fs_cell_summaries.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp]
         L.fs_prune_workspace_bytes.argtypes = [P_shape, P_prm]
         L.fs_prune_workspace_bytes.restype = sz
         L.fs_prune_retained.argtypes = [P_shape, P_prm, vp, vp, vp, vp, sz, vp]
         L.fs_score_select.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.fs_readout.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp]
-        L.fs_select_readout.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.fs_select_readout.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.fs_prefill_workspace_bytes.argtypes = [P_shape, P_prm]
         L.fs_prefill_workspace_bytes.restype = sz
         L.fs_longrange_prefill.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
@@ -135,12 +135,13 @@ def _floats(vals, H):
 
 # ------------------------------------------------------------- C ABI calls --
 
-def fs_cell_summaries(k, kbar, a, params: Params = Params(), stream=None, kbar_split=None):
+def fs_cell_summaries(k, kbar, a, params: Params = Params(), stream=None, kbar_split=None, kbar_norm=None):
     """Eq. 5: kbar [b,H,N/s,d] fp32 and a [b,H,N/s] fp32 from k [b,H,N,d]; optionally
-    kbar_split [b,H,N/s,3,d] (int16/bf16 storage): the bf16 hi/mid/lo parts of kbar."""
+    kbar_split [b,H,N/s,3,d] (int16/bf16 storage): the bf16 hi/mid/lo parts of kbar, and
+    kbar_norm [b,H,N/s] fp32: the norms of kbar."""
     sh, prm = shape_of(k), params.c()
     _check(lib().fs_cell_summaries(ctypes.byref(sh), ctypes.byref(prm), _ptr(k), _ptr(kbar), _ptr(a),
-                                   _ptr(kbar_split), _stream(stream)), "fs_cell_summaries")
+                                   _ptr(kbar_split), _ptr(kbar_norm), _stream(stream)), "fs_cell_summaries")
 
 
 def fs_prune_workspace_bytes(sh: fs_shape, params: Params = Params()) -> int:
@@ -174,12 +175,14 @@ def fs_readout(q, k, v, sel, gain, out, params: Params = Params(), stream=None):
 
 
 def fs_select_readout(q, k, v, kbar, a, retained, n_retained, sigma_h, lambda_h, gain, out, sel=None,
-                      params: Params = Params(), stream=None, kbar_split=None):
-    """fs_score_select + fs_readout in one call (one kernel for bf16 with kbar_split)."""
+                      params: Params = Params(), stream=None, kbar_split=None, kbar_norm=None):
+    """fs_score_select + fs_readout in one call (one kernel for bf16 with kbar_split; with
+    kbar_norm too, tiles of cells that no query can select are passed over)."""
     sh, prm = shape_of(q), params.c()
     sig, lam = _floats(sigma_h, sh.H), _floats(lambda_h, sh.H)
     _check(lib().fs_select_readout(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar),
-                                   _ptr(kbar_split), _ptr(a), _ptr(retained), _ptr(n_retained), sig, lam,
+                                   _ptr(kbar_split), _ptr(kbar_norm), _ptr(a), _ptr(retained), _ptr(n_retained),
+                                   sig, lam,
                                    _ptr(gain), _ptr(out), _ptr(sel), _stream(stream)), "fs_select_readout")
 
 

@@ -76,7 +76,7 @@ Geometry geometry(const fs_shape *sh, const fs_params *p)
 
 // Workspace of fs_longrange_prefill, carved in this order (256-byte aligned).
 struct PrefillLayout {
-    size_t kbar, ksplit, a, death, retained, n_ret, sel, total;
+    size_t kbar, ksplit, knorm, a, death, retained, n_ret, sel, total;
 };
 
 PrefillLayout prefill_layout(const Geometry &g)
@@ -87,6 +87,8 @@ PrefillLayout prefill_layout(const Geometry &g)
     off += align_up((size_t)g.bh * g.M * g.d * sizeof(float));
     L.ksplit = off; // bf16 parts of kbar for the scorer (bf16 shapes)
     off += g.bf16 ? align_up((size_t)g.bh * g.M * 3 * g.d * sizeof(uint16_t)) : 0;
+    L.knorm = off; // norms of kbar for the fused kernel's tile bound (bf16 shapes)
+    off += g.bf16 ? align_up((size_t)g.bh * g.M * sizeof(float)) : 0;
     L.a = off;
     off += align_up((size_t)g.bh * g.M * sizeof(float));
     L.death = off;
@@ -210,7 +212,7 @@ FSL_EXPORT const char *fs_status_string(fs_status status)
 }
 
 FSL_EXPORT fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *prm, const void *k, float *kbar,
-                                       float *a, uint16_t *kbar_split, void *stream)
+                                       float *a, uint16_t *kbar_split, float *kbar_norm, void *stream)
 {
     fs_status st = check_all(shape, prm);
     if (st != FS_OK)
@@ -218,7 +220,7 @@ FSL_EXPORT fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *p
     const Geometry g = geometry(shape, prm);
     if (!k || ((!kbar || !a) && g.M > 0)) // no complete cell: nothing to write
         return FS_ERR_INVALID;
-    return hip_status(launch_cell_summaries(g, k, kbar, a, g.bf16 ? kbar_split : nullptr,
+    return hip_status(launch_cell_summaries(g, k, kbar, a, g.bf16 ? kbar_split : nullptr, kbar_norm,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -279,8 +281,9 @@ FSL_EXPORT fs_status fs_readout(const fs_shape *shape, const fs_params *prm, con
 }
 
 FSL_EXPORT fs_status fs_select_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
-                                       const void *v, const float *kbar, const uint16_t *kbar_split, const float *a,
-                                       const int32_t *retained, const int32_t *n_retained, const float *sigma_h,
+                                       const void *v, const float *kbar, const uint16_t *kbar_split,
+                                       const float *kbar_norm, const float *a, const int32_t *retained,
+                                       const int32_t *n_retained, const float *sigma_h,
                                        const float *lambda_h, const float *gain, void *out, int32_t *sel,
                                        void *stream)
 {
@@ -301,7 +304,7 @@ FSL_EXPORT fs_status fs_select_readout(const fs_shape *shape, const fs_params *p
     const int32_t *ret = g.prune ? retained : nullptr;
     const int32_t *nr = g.prune ? n_retained : nullptr;
     if (fused)
-        return hip_status(launch_route_readout(g, hc, q, k, v, kbar_split, a, ret, nr, gain, out, sel, s));
+        return hip_status(launch_route_readout(g, hc, q, k, v, kbar_split, kbar_norm, a, ret, nr, gain, out, sel, s));
     hipError_t e = launch_score_topk(g, hc, q, kbar, g.bf16 ? kbar_split : nullptr, a, ret, nr, sel, s);
     if (e == hipSuccess)
         e = launch_readout(g, q, k, v, sel, gain, out, s);
@@ -351,6 +354,7 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
     char *ws = static_cast<char *>(workspace);
     float *kbar = reinterpret_cast<float *>(ws + L.kbar);
     uint16_t *ksplit = g.bf16 ? reinterpret_cast<uint16_t *>(ws + L.ksplit) : nullptr;
+    float *knorm = g.bf16 ? reinterpret_cast<float *>(ws + L.knorm) : nullptr;
     float *a = reinterpret_cast<float *>(ws + L.a);
     int32_t *death = reinterpret_cast<int32_t *>(ws + L.death);
     int32_t *retained = reinterpret_cast<int32_t *>(ws + L.retained);
@@ -359,13 +363,13 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     const bool route = out || sel; // state-only calls skip scoring and readout
-    hipError_t e = launch_cell_summaries(g, k, kbar, a, route ? ksplit : nullptr, s);
+    const bool fused = out && g.bf16 && (!g.prune || g.cap <= kFusedMaxCap);
+    hipError_t e = launch_cell_summaries(g, k, kbar, a, route ? ksplit : nullptr, fused ? knorm : nullptr, s);
     if (e == hipSuccess && g.prune)
         e = launch_prune(g, a, death, retained, n_ret, route ? 1 : 0, s);
-    const bool fused = out && g.bf16 && (!g.prune || g.cap <= kFusedMaxCap);
     if (e == hipSuccess && fused) {
-        e = launch_route_readout(g, hc, q, k, v, ksplit, a, g.prune ? retained : nullptr, g.prune ? n_ret : nullptr,
-                                 gain, out, sel, s);
+        e = launch_route_readout(g, hc, q, k, v, ksplit, knorm, a, g.prune ? retained : nullptr,
+                                 g.prune ? n_ret : nullptr, gain, out, sel, s);
     } else {
         if (e == hipSuccess && route)
             e = launch_score_topk(g, hc, q, kbar, ksplit, a, g.prune ? retained : nullptr,

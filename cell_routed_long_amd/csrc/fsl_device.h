@@ -133,6 +133,17 @@ __device__ __forceinline__ float wave_max_f(float x)
     return fmaxf(fmaxf(readlane_f(x, 0), readlane_f(x, 16)), fmaxf(readlane_f(x, 32), readlane_f(x, 48)));
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
+{
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, true));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, true));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, true));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xf, 0xf, true));
+    const uint32_t a0 = (uint32_t)readlane_i((int)x, 0), a1 = (uint32_t)readlane_i((int)x, 16);
+    const uint32_t a2 = (uint32_t)readlane_i((int)x, 32), a3 = (uint32_t)readlane_i((int)x, 48);
+    return min(min(a0, a1), min(a2, a3));
+}
+
 // ---- XCD-aware block order ---------------------------------------------------
 // The dispatcher deals workgroups round-robin over the 8 XCDs (each with its own
 // L2).  Renumbering the linear workgroup id so that XCD x receives the x-th

@@ -25,8 +25,9 @@ struct Geometry {
 };
 
 // kbar_split (optional): [bh, M, 3, d] bf16 hi/mid/lo parts of kbar.
+// kbar_norm (optional): [bh, M] fp32 Euclidean norms of kbar.
 hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split,
-                                 hipStream_t st);
+                                 float *kbar_norm, hipStream_t st);
 
 // death[c]: first query block whose TopP no longer holds cell c (INT32_MAX: never leaves).
 // emit = 0 computes only the exit blocks (enough to build a decode state).
@@ -42,10 +43,12 @@ hipError_t launch_readout(const Geometry &g, const void *q, const void *k, const
                           const int32_t *sel, const float *gain, void *out, hipStream_t st);
 
 // Routing and readout of every 128-query block in one launch (bf16 only; the
-// retained lists at most kFusedMaxCap long).  sel may be NULL.
+// retained lists at most kFusedMaxCap long).  sel may be NULL.  With kbar_norm
+// (optional) a tile of retained cells is passed over when no cell of it can
+// reach any query's top-K (the results do not change).
 constexpr int kFusedMaxCap = 256;
 hipError_t launch_route_readout(const Geometry &g, const HeadConsts &hc, const void *q, const void *k,
-                                const void *v, const uint16_t *kbar_split, const float *a,
+                                const void *v, const uint16_t *kbar_split, const float *kbar_norm, const float *a,
                                 const int32_t *retained, const int32_t *n_ret, const float *gain, void *out,
                                 int32_t *sel, hipStream_t st);
 

@@ -23,7 +23,9 @@
 // The arithmetic is the same as the two separate kernels, so the results are
 // bitwise those of fs_score_select followed by fs_readout.
 #include "fsl_internal.h"
+#include "readout_math.h"
 
+#include <cfloat>
 #include <climits>
 #include <type_traits>
 
@@ -31,7 +33,6 @@ namespace fsl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kLazy = 16.0f; // the softmax running max moves only when it grows by more than 2^16
 
 // V^T rows keep a cell's 32 tokens in the order 0-3, 8-11, 4-7, 12-15, 16-19,
 // 24-27, 20-23, 28-31: then the 8 tokens a lane feeds to one P.V product
@@ -59,7 +60,8 @@ struct alignas(16) FusedSmem {
 template <int D, int KT>
 __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const uint16_t *__restrict__ kbar_split, const float *__restrict__ a, const int32_t *__restrict__ retained,
+    const uint16_t *__restrict__ kbar_split, const float *__restrict__ kbar_norm, const float *__restrict__ a,
+    const int32_t *__restrict__ retained,
     const int32_t *__restrict__ n_ret, const float *__restrict__ gain, uint16_t *__restrict__ out,
     int32_t *__restrict__ sel, int64_t N, int64_t M, int NB, int cap, int prune, int H, int s,
     int cells_per_block, float eps, HeadConsts hc)
@@ -115,6 +117,15 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     u32x4 pre3[3 * SCH];
     int pre_id;
     float pre_a;
+    // the tile bound needs every retained cell's prior and mean-key norm: one
+    // load each per block, kept in registers until the first tile is scored
+    const bool bound = kbar_norm != nullptr && nA > 32 && nA <= kThreads;
+    float b_pr = 0.0f, b_kn = 0.0f;
+    if (bound && t < nA) {
+        const int64_t id = head * M + (prune ? s_A[t] : t);
+        b_pr = lam * a[id];
+        b_kn = kbar_norm[id];
+    }
     auto prefetch = [&](int t0) {
         const int x = t0 + srow;
         pre_id = x < nA ? (prune ? s_A[x] : x) : -1;
@@ -141,8 +152,51 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
 #pragma unroll
     for (int j = 0; j < KT; ++j)
         kl[j] = 0;
+    // Tile bound (with kbar_norm): every score in a tile is at most
+    //   max_c (lambda a_c) + max_i |q_i| max_c |kbar_c| / sqrt(d)
+    // (Cauchy-Schwarz on the content term; 0 < g <= 1 for every available cell,
+    // whose centre lies at least s/2 before the block), widened for rounding.
+    // When it falls below every query's K-th best key so far, no cell of the
+    // tile can enter any top-K, and the tile is passed over: the selections are
+    // those of scoring every cell.  The first tile is always scored.
+    __shared__ float s_bpr[kThreads], s_bkn[kThreads], s_qn[kThreads / kWave];
+    __shared__ uint32_t s_tau[2][kThreads / kWave];
     for (int t0 = 0; t0 < nA; t0 += 32) {
+        const int par = (t0 >> 5) & 1; // tau slots alternate, so no wave overwrites one still being read
+        if (bound && t0 > 0) {
+            const uint32_t tau = wave_min_u32(q_ok ? (uint32_t)(kl[KT - 1] >> 32) : 0xffffffffu);
+            if (lane == 0)
+                s_tau[par][wave] = tau;
+        }
         __syncthreads();
+        // bound of a tile against the block's smallest K-th best key (tau);
+        // tau only grows, so a tile found below it now stays below it later
+        uint32_t tau = 0;
+        float qn = 0.0f;
+        auto tile_below = [&](int tb) {
+            const int x = tb + lane;
+            const float pr = lane < 32 && x < nA ? s_bpr[x] : 0.0f; // >= 0 unless NaN
+            const float kn = lane < 32 && x < nA ? s_bkn[x] : 0.0f;
+            const bool bad = __ballot(!(pr <= FLT_MAX) || !(kn <= FLT_MAX)) != 0ull; // NaN or infinite
+            const float pm = bad ? INFINITY : wave_max_f(pr), km = wave_max_f(kn);
+            const float ub = (pm + qn * km * inv_sqrt_d * (1.0f + 0x1p-10f)) * (1.0f + 0x1p-10f);
+            // ub >= 0: its ranking key's high word is its bits with the sign bit set
+            return ub <= FLT_MAX && (__float_as_uint(ub) | 0x80000000u) < tau;
+        };
+        if (bound && t0 > 0) {
+            qn = s_qn[0];
+            tau = s_tau[par][0];
+#pragma unroll
+            for (int w = 1; w < kThreads / kWave; ++w) {
+                qn = fmaxf(qn, s_qn[w]);
+                tau = min(tau, s_tau[par][w]);
+            }
+            if (tile_below(t0)) {
+                if (t0 + 32 < nA && !tile_below(t0 + 32))
+                    prefetch(t0 + 32); // the next tile is fetched only if it may be scored
+                continue;
+            }
+        }
         if (spart == 0) {
             sm.id[srow] = pre_id >= 0 ? 0x7fffffff - pre_id : -1;   // low half of the ranking key
             sm.prior[srow] = pre_id >= 0 ? lam * pre_a : 0.0f;
@@ -154,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             for (int u = 0; u < SCH; ++u)
                 *reinterpret_cast<u32x4 *>(&sm.kb[part][srow][spart * PER + u * 8]) = pre3[part * SCH + u];
         __syncthreads();
-        if (t0 + 32 < nA)
+        if (t0 + 32 < nA && !(bound && t0 > 0 && tile_below(t0 + 32)))
             prefetch(t0 + 32); // overlaps the matrix work below
 
         f32x16 acc;
@@ -177,6 +231,29 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             acc[r] = (acc3[2][r] + acc3[1][r]) + acc3[0][r];
+        if (bound && t0 == 0) { // the largest |q_i| of this wave, for the tile bound
+            float ss = 0.0f;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const u32x4 w = __builtin_bit_cast(u32x4, qf[kc]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16x2 x = __builtin_bit_cast(bf16x2, w[e]);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+                }
+            }
+            ss += shfl_xor_f(ss, 32); // the partner lane holds the other half of the features
+            // + 2^-100: covers subnormal elements, should the dot product flush them
+            const float qn = q_ok ? sqrtf(ss) * (1.0f + 0x1p-10f) + 0x1p-100f : 0.0f;
+            const bool badq = __ballot(!(qn <= FLT_MAX)) != 0ull;
+            const float qm = wave_max_f(qn);
+            if (lane == 0)
+                s_qn[wave] = badq ? INFINITY : qm;
+            if (t < nA) { // read after the next barrier, like s_qn
+                s_bpr[t] = b_pr;
+                s_bkn[t] = b_kn;
+            }
+        }
         // erf only below 4 (above it rounds to 1 in fp32); see the scorer
         // this lane's 16 rows come in 4 runs of 4 consecutive rows: 12 vector LDS reads
         float prv[16], pcv[16];
@@ -348,46 +425,17 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         if (__ballot(mine) == 0ull)
             continue; // no query of this wave reads the cell
 
-        f32x16 acc, acc2; // even and odd k-steps: two independent chains
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            acc[r] = 0.0f;
-            acc2[r] = 0.0f;
-        }
-#pragma unroll
-        for (int kc = 0; kc < KC; kc += 2) {
-            const u32x4 w0 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
-            const u32x4 w1 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + 16 + half * 8]);
-            acc = mfma_bf16(as_bf16x8(w0), qf[kc], acc);
-            acc2 = mfma_bf16(as_bf16x8(w1), qf[kc + 1], acc2);
-        }
+        f32x16 acc;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            acc[r] += acc2[r];
-        float p[16];
-        float amax = acc[0];
+            acc[r] = 0.0f;
 #pragma unroll
-        for (int r = 1; r < 16; ++r)
-            amax = fmaxf(amax, acc[r]);
-        const float tmax = fmaxf(amax, shfl_xor_f(amax, 32)) * scale_log2; // scale > 0: max commutes
-        float alpha = 1.0f, psum = 0.0f;
-        if (mine) {
-            if (tmax > m_run + kLazy) { // a much larger logit; on the first cell o and l are still 0
-                alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - tmax);
-                m_run = tmax;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -m_run)); // <= 2^16
-                psum += p[r];
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                p[r] = 0.0f;
+        for (int kc = 0; kc < KC; ++kc) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
+            acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
         }
-        psum += shfl_xor_f(psum, 32);
-        l_run = l_run * alpha + psum;
+        float p[16];
+        const float alpha = softmax_cell(acc, mine, scale_log2, m_run, l_run, p);
         if (__ballot(alpha != 1.0f)) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -397,15 +445,8 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            u32x4 ph, pl;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float x0 = p[8 * kk + 2 * w], x1 = p[8 * kk + 2 * w + 1];
-                const uint32_t hp = cvt_pk_bf16(x0, x1);
-                ph[w] = hp;
-                pl[w] = cvt_pk_bf16(x0 - bf16_bits_to_f32(hp & 0xffffu), x1 - bf16_bits_to_f32(hp >> 16));
-            }
-            const bf16x8 bh = as_bf16x8(ph), bl = as_bf16x8(pl);
+            bf16x8 bh, bl;
+            split_bf16x8(&p[8 * kk], bh, bl);
             bf16x8 av[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -420,18 +461,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     }
 
     // ---- normalise, RMSNorm over d (Eq. 17), write through LDS ----
-    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float ms = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float u = o_acc[dt][r] * inv_l;
-            o_acc[dt][r] = u;
-            ms += u * u;
-        }
-    ms += shfl_xor_f(ms, 32);
-    const float rs = 1.0f / sqrtf(ms / (float)D + eps);
+    const float c = rms_factor<DT>(o_acc, l_run, eps); // y = c * o, times the gain
     __syncthreads(); // the last cell's LDS reads are done: the tile area takes the output
     // one straight-line copy with the gain vector and one without (the test is uniform)
     auto emit = [&](auto with_gain) {
@@ -444,10 +474,9 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
                 float y[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float gv = 1.0f;
+                    y[e] = o_acc[dt][4 * rg + e] * c;
                     if constexpr (decltype(with_gain)::value)
-                        gv = gh[d0 + e];
-                    y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+                        y[e] = l_run > 0.0f ? y[e] * gh[d0 + e] : 0.0f;
                 }
                 *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
                     u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};
@@ -464,15 +493,15 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
 
 template <int D, int KT>
 hipError_t launch_k(const Geometry &g, const HeadConsts &hc, const void *q, const void *k, const void *v,
-                    const uint16_t *kbar_split, const float *a, const int32_t *retained, const int32_t *n_ret,
-                    const float *gain, void *out, int32_t *sel, hipStream_t st)
+                    const uint16_t *kbar_split, const float *kbar_norm, const float *a, const int32_t *retained,
+                    const int32_t *n_ret, const float *gain, void *out, int32_t *sel, hipStream_t st)
 {
     dim3 grid((unsigned)((int64_t)g.NB * g.bh)); // one linear range, renumbered per XCD in the kernel
     const size_t words = (size_t)((g.M + 31) / 32);
     const size_t dyn = (words > 0 ? words : 1) * sizeof(uint32_t);
     hipLaunchKernelGGL((route_readout_kernel<D, KT>), grid, dim3(kThreads), dyn, st,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                       static_cast<const uint16_t *>(v), kbar_split, a, retained, n_ret, gain,
+                       static_cast<const uint16_t *>(v), kbar_split, kbar_norm, a, retained, n_ret, gain,
                        static_cast<uint16_t *>(out), sel, g.N, g.M, g.NB, g.cap, g.prune, g.H, g.s, g.B / g.s, g.eps,
                        hc);
     return hipGetLastError();
@@ -480,30 +509,30 @@ hipError_t launch_k(const Geometry &g, const HeadConsts &hc, const void *q, cons
 
 template <int D>
 hipError_t launch_d(const Geometry &g, const HeadConsts &hc, const void *q, const void *k, const void *v,
-                    const uint16_t *ks, const float *a, const int32_t *retained, const int32_t *n_ret,
-                    const float *gain, void *out, int32_t *sel, hipStream_t st)
+                    const uint16_t *ks, const float *kn, const float *a, const int32_t *retained,
+                    const int32_t *n_ret, const float *gain, void *out, int32_t *sel, hipStream_t st)
 {
     switch (g.K) {
-    case 1: return launch_k<D, 1>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
-    case 2: return launch_k<D, 2>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
-    case 3: return launch_k<D, 3>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
-    case 4: return launch_k<D, 4>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
-    case 5: return launch_k<D, 5>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
-    case 6: return launch_k<D, 6>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
-    case 7: return launch_k<D, 7>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
-    default: return launch_k<D, 8>(g, hc, q, k, v, ks, a, retained, n_ret, gain, out, sel, st);
+    case 1: return launch_k<D, 1>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
+    case 2: return launch_k<D, 2>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
+    case 3: return launch_k<D, 3>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
+    case 4: return launch_k<D, 4>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
+    case 5: return launch_k<D, 5>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
+    case 6: return launch_k<D, 6>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
+    case 7: return launch_k<D, 7>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
+    default: return launch_k<D, 8>(g, hc, q, k, v, ks, kn, a, retained, n_ret, gain, out, sel, st);
     }
 }
 
 } // namespace
 
 hipError_t launch_route_readout(const Geometry &g, const HeadConsts &hc, const void *q, const void *k,
-                                const void *v, const uint16_t *kbar_split, const float *a,
+                                const void *v, const uint16_t *kbar_split, const float *kbar_norm, const float *a,
                                 const int32_t *retained, const int32_t *n_ret, const float *gain, void *out,
                                 int32_t *sel, hipStream_t st)
 {
-    return g.d == 64 ? launch_d<64>(g, hc, q, k, v, kbar_split, a, retained, n_ret, gain, out, sel, st)
-                     : launch_d<128>(g, hc, q, k, v, kbar_split, a, retained, n_ret, gain, out, sel, st);
+    return g.d == 64 ? launch_d<64>(g, hc, q, k, v, kbar_split, kbar_norm, a, retained, n_ret, gain, out, sel, st)
+                     : launch_d<128>(g, hc, q, k, v, kbar_split, kbar_norm, a, retained, n_ret, gain, out, sel, st);
 }
 
 } // namespace fsl

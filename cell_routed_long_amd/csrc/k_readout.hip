@@ -26,6 +26,7 @@
 // result is the same softmax up to rounding.  The next cell's keys and values
 // are fetched into registers while the current cell is on the matrix cores.
 #include "fsl_internal.h"
+#include "readout_math.h"
 
 #include <type_traits>
 
@@ -33,7 +34,6 @@ namespace fsl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kLazy = 16.0f; // the running max moves only when it grows by more than 2^16
 
 // V^T rows keep a cell's 32 tokens in the order 0-3, 8-11, 4-7, 12-15, 16-19,
 // 24-27, 20-23, 28-31: then the 8 tokens a lane feeds to one P.V product
@@ -250,20 +250,11 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
         for (int r = 0; r < 16; ++r)
             acc[r] = 0.0f;
         if constexpr (kBf16) {
-            f32x16 acc2; // even and odd k-steps: two independent chains
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc2[r] = 0.0f;
-#pragma unroll
-            for (int kc = 0; kc < KC; kc += 2) {
-                const u32x4 w0 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
-                const u32x4 w1 = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + 16 + half * 8]);
-                acc = mfma_bf16(as_bf16x8(w0), qf[kc], acc);
-                acc2 = mfma_bf16(as_bf16x8(w1), qf[kc + 1], acc2);
+            for (int kc = 0; kc < KC; ++kc) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
+                acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[r] += acc2[r];
         } else {
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
@@ -272,29 +263,7 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
 
         // ---- online softmax over the query's own tokens (exp2 domain) ----
         float p[16];
-        float amax = acc[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-            amax = fmaxf(amax, acc[r]);
-        const float tmax = fmaxf(amax, shfl_xor_f(amax, 32)) * scale_log2; // scale > 0: max commutes
-        float alpha = 1.0f, psum = 0.0f;
-        if (mine) {
-            if (tmax > m_run + kLazy) { // a much larger logit; on the first cell o and l are still 0
-                alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - tmax);
-                m_run = tmax;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -m_run)); // <= 2^16
-                psum += p[r];
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                p[r] = 0.0f;
-        }
-        psum += shfl_xor_f(psum, 32);
-        l_run = l_run * alpha + psum;
+        const float alpha = softmax_cell(acc, mine, scale_log2, m_run, l_run, p);
         if (__ballot(alpha != 1.0f)) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -307,15 +276,8 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
         if constexpr (kBf16) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                u32x4 ph, pl;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float x0 = p[8 * kk + 2 * w], x1 = p[8 * kk + 2 * w + 1];
-                    const uint32_t hp = cvt_pk_bf16(x0, x1);
-                    ph[w] = hp;
-                    pl[w] = cvt_pk_bf16(x0 - bf16_bits_to_f32(hp & 0xffffu), x1 - bf16_bits_to_f32(hp >> 16));
-                }
-                const bf16x8 bh = as_bf16x8(ph), bl = as_bf16x8(pl);
+                bf16x8 bh, bl;
+                split_bf16x8(&p[8 * kk], bh, bl);
                 bf16x8 av[DT];
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
@@ -337,28 +299,16 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
     }
 
     // ---- normalise, RMSNorm over d, write ----
-    const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float ms = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float u = o_acc[dt][r] * inv_l;
-            o_acc[dt][r] = u;
-            ms += u * u;
-        }
-    ms += shfl_xor_f(ms, 32);
-    const float rs = 1.0f / sqrtf(ms / (float)D + eps);
+    const float c = rms_factor<DT>(o_acc, l_run, eps); // y = c * o, times the gain
     const float *gh = gain + (int64_t)h * D;
     // y = g * u * rs for the four features d0..d0+3 (g = 1 without a gain vector;
     // the test is uniform, so each copy below is straight-line code)
     auto rms4 = [&](float (&y)[4], int dt, int rg, int d0, auto with_gain) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float gv = 1.0f;
+            y[e] = o_acc[dt][4 * rg + e] * c;
             if constexpr (decltype(with_gain)::value)
-                gv = gh[d0 + e];
-            y[e] = l_run > 0.0f ? gv * o_acc[dt][4 * rg + e] * rs : 0.0f;
+                y[e] = l_run > 0.0f ? y[e] * gh[d0 + e] : 0.0f;
         }
     };
     if constexpr (kBf16) {

@@ -10,7 +10,9 @@
 // rounded once to fp32.  Optionally the fp32 mean is also written as three
 // bf16 parts (hi, mid, lo), the operands the block scorer feeds to the bf16
 // matrix cores, so that the split is done once per cell instead of once per
-// query block.  HBM-bound: the kernel reads each key exactly once.
+// query block, and its Euclidean norm (fp64, rounded once), which bounds the
+// content term of every score of the cell (|q . kbar| <= |q| |kbar|).
+// HBM-bound: the kernel reads each key exactly once.
 #include "fsl_internal.h"
 
 namespace fsl {
@@ -19,8 +21,9 @@ namespace {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void cell_summaries_kernel(const T *__restrict__ k, float *__restrict__ kbar,
                                                              float *__restrict__ a,
-                                                             uint16_t *__restrict__ kbar_split, int64_t N,
-                                                             int64_t M, int64_t total_cells)
+                                                             uint16_t *__restrict__ kbar_split,
+                                                             float *__restrict__ kbar_norm, int64_t N, int64_t M,
+                                                             int64_t total_cells)
 {
     constexpr int EPC = 16 / (int)sizeof(T); // elements per 16-byte chunk
     constexpr int R = D / EPC;               // chunks per key row: 8, 16 or 32
@@ -88,14 +91,26 @@ __global__ __launch_bounds__(256) void cell_summaries_kernel(const T *__restrict
     for (int m = R; m < kWave; m <<= 1)
         best = fmax(best, shfl_xor_d(best, m));
 
+    float m[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e)
+        m[e] = (float)(colsum[e] * (1.0 / 32.0));
+    if (kbar_norm) { // |kbar|, from the fp32 mean as stored; lanes < R hold all d features
+        double nsq = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+            nsq += (double)m[e] * (double)m[e];
+#pragma unroll
+        for (int mm = 1; mm < R; mm <<= 1)
+            nsq += shfl_xor_d(nsq, mm);
+        if (lane == 0)
+            kbar_norm[cell] = (float)sqrt(nsq);
+    }
     if (lane < R) {
         float *dst = kbar + cell * D + group * EPC;
-        float m[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-            m[e] = (float)(colsum[e] * (1.0 / 32.0));
+        for (int e = 0; e < EPC; ++e)
             dst[e] = m[e];
-        }
         if (kbar_split) { // bf16 hi, mid, lo parts of the fp32 mean (24 mantissa bits in all)
             uint32_t pk[3][EPC / 2];
 #pragma unroll
@@ -122,27 +137,28 @@ __global__ __launch_bounds__(256) void cell_summaries_kernel(const T *__restrict
 }
 
 template <typename T, int D>
-hipError_t launch_t(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split, hipStream_t st)
+hipError_t launch_t(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split, float *kbar_norm,
+                    hipStream_t st)
 {
     const int64_t total = (int64_t)g.bh * g.M;
     if (total == 0)
         return hipSuccess;
     const int64_t blocks = (total + 3) / 4;
     hipLaunchKernelGGL((cell_summaries_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const T *>(k), kbar, a, kbar_split, g.N, g.M, total);
+                       static_cast<const T *>(k), kbar, a, kbar_split, kbar_norm, g.N, g.M, total);
     return hipGetLastError();
 }
 
 } // namespace
 
 hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split,
-                                 hipStream_t st)
+                                 float *kbar_norm, hipStream_t st)
 {
     if (g.bf16)
-        return g.d == 64 ? launch_t<uint16_t, 64>(g, k, kbar, a, kbar_split, st)
-                         : launch_t<uint16_t, 128>(g, k, kbar, a, kbar_split, st);
-    return g.d == 64 ? launch_t<float, 64>(g, k, kbar, a, kbar_split, st)
-                     : launch_t<float, 128>(g, k, kbar, a, kbar_split, st);
+        return g.d == 64 ? launch_t<uint16_t, 64>(g, k, kbar, a, kbar_split, kbar_norm, st)
+                         : launch_t<uint16_t, 128>(g, k, kbar, a, kbar_split, kbar_norm, st);
+    return g.d == 64 ? launch_t<float, 64>(g, k, kbar, a, kbar_split, kbar_norm, st)
+                     : launch_t<float, 128>(g, k, kbar, a, kbar_split, kbar_norm, st);
 }
 
 } // namespace fsl

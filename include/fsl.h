@@ -83,10 +83,14 @@ const char *fs_status_string(fs_status status);
  *               mid = bf16(kbar - hi), lo = bf16(kbar - hi - mid)): the operands
  *               fs_score_select feeds to the bf16 matrix cores.  bf16 shapes
  *               only; not written for fp32 shapes.
+ *   kbar_norm   [batch, H, M]        fp32, or NULL                  (output)
+ *               ||kbar[c]||_2 of the fp32 mean; fs_select_readout uses it to
+ *               bound the content term of Eq. 7 (|q . kbar| <= |q| |kbar|).
  * Sums and norms accumulate in fp64 and are rounded once to fp32.
  */
 fs_status fs_cell_summaries(const fs_shape *shape, const fs_params *prm, const void *k,
-                            float *kbar, float *a, uint16_t *kbar_split, void *stream);
+                            float *kbar, float *a, uint16_t *kbar_split, float *kbar_norm,
+                            void *stream);
 
 /* Bytes of workspace fs_prune_retained needs (0 on invalid arguments). */
 size_t fs_prune_workspace_bytes(const fs_shape *shape, const fs_params *prm);
@@ -143,9 +147,14 @@ fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q,
  * 256) it runs as a single kernel in which each 128-query block scores its
  * retained cells, selects, and reads out its selected cells without the
  * selections going through global memory; the outputs are bitwise those of
- * the two separate calls.
+ * the two separate calls.  Given kbar_norm as well, that kernel passes over a
+ * tile of 32 retained cells when an upper bound of every score in it
+ * (max lambda_h a_c + max |q_i| max |kbar_c| / sqrt(d), widened for rounding)
+ * lies below every query's K-th best score so far: no such cell can be
+ * selected, so the results are unchanged.
  *   q, k, v                [batch, H, N, d]  shape dtype (input)
- *   kbar, kbar_split, a    from fs_cell_summaries (kbar_split may be NULL)
+ *   kbar, kbar_split, kbar_norm, a   from fs_cell_summaries (kbar_split and
+ *                          kbar_norm may be NULL)
  *   retained, n_retained   from fs_prune_retained (FS-L; NULL for FS)
  *   sigma_h, lambda_h      host [H] fp32;  gain  device [H, d] fp32 or NULL
  *   out                    [batch, H, N, d] shape dtype (output)
@@ -153,9 +162,10 @@ fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q,
  *                          when the single-kernel form applies
  */
 fs_status fs_select_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
-                            const void *v, const float *kbar, const uint16_t *kbar_split, const float *a,
-                            const int32_t *retained, const int32_t *n_retained, const float *sigma_h,
-                            const float *lambda_h, const float *gain, void *out, int32_t *sel, void *stream);
+                            const void *v, const float *kbar, const uint16_t *kbar_split,
+                            const float *kbar_norm, const float *a, const int32_t *retained,
+                            const int32_t *n_retained, const float *sigma_h, const float *lambda_h,
+                            const float *gain, void *out, int32_t *sel, void *stream);
 
 /* Bytes of workspace fs_longrange_prefill needs (0 on invalid arguments). */
 size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_params *prm);

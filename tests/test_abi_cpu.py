@@ -52,7 +52,7 @@ def prm(**kw):
 def call_summaries(L, sh, p, k=1, kbar=1, a=1):
     vp = ctypes.c_void_p
     return L.fs_cell_summaries(ctypes.byref(sh), ctypes.byref(p), vp(k) if k else None,
-                               vp(kbar) if kbar else None, vp(a) if a else None, None, None)
+                               vp(kbar) if kbar else None, vp(a) if a else None, None, None, None)
 
 
 @pytest.mark.parametrize("sh,p,expect", [
@@ -79,16 +79,17 @@ def test_summaries_rejects_bad_arguments(L, sh, p, expect):
 def test_null_pointers_rejected(L):
     assert call_summaries(L, shape(), prm(), k=0) == fsl.FS_ERR_INVALID
     assert call_summaries(L, shape(), prm(), a=0) == fsl.FS_ERR_INVALID
-    assert L.fs_cell_summaries(None, ctypes.byref(prm()), None, None, None, None, None) == fsl.FS_ERR_INVALID
+    assert L.fs_cell_summaries(None, ctypes.byref(prm()), None, None, None, None, None, None) == fsl.FS_ERR_INVALID
 
 
 def test_workspace_sizes(L):
     sh, p = shape(b=4, H=16, N=16384, d=128, dtype=fsl.FS_BF16), prm()
     ws = fsl.fs_prefill_workspace_bytes(sh, fsl.Params())
     M, NB = 16384 // 32, 16384 // 128
-    # summaries (fp32 and bf16 parts) + norms + per-cell exit blocks + retained lists + counts + selections
-    at_least = 64 * (M * 128 * 4 + M * 3 * 128 * 2 + M * 4 + M * 4 + NB * 72 * 4 + NB * 4 + 16384 * 4 * 4)
-    assert at_least <= ws <= at_least + 7 * 256
+    # summaries (fp32, bf16 parts and their norms) + key norms + per-cell exit blocks + retained lists + counts
+    # + selections
+    at_least = 64 * (M * 128 * 4 + M * 3 * 128 * 2 + M * 4 + M * 4 + M * 4 + NB * 72 * 4 + NB * 4 + 16384 * 4 * 4)
+    assert at_least <= ws <= at_least + 8 * 256
     assert fsl.fs_prefill_workspace_bytes(shape(d=96), fsl.Params()) == 0
     assert fsl.fs_prune_workspace_bytes(sh, fsl.Params()) >= 64 * M * 4
 

@@ -63,10 +63,13 @@ def test_cell_summaries(w):
     kbar = torch.empty(w.batch, w.H, M, w.d, dtype=torch.float32, device="cuda")
     a = torch.empty(w.batch, w.H, M, dtype=torch.float32, device="cuda")
     ks = torch.full((w.batch, w.H, M, 3, w.d), -1, dtype=torch.int16, device="cuda")
+    kn = torch.full((w.batch, w.H, M), -1.0, dtype=torch.float32, device="cuda")
     print(f"[gpu] summaries {w}", flush=True)
-    fsl.fs_cell_summaries(k, kbar, a, kbar_split=ks)
+    fsl.fs_cell_summaries(k, kbar, a, kbar_split=ks, kbar_norm=kn)
     torch.cuda.synchronize()
-    kbar, a, ks = kbar.cpu().numpy(), a.cpu().numpy(), ks.cpu().numpy().view(np.uint16)
+    kbar, a, ks, kn = kbar.cpu().numpy(), a.cpu().numpy(), ks.cpu().numpy().view(np.uint16), kn.cpu().numpy()
+    # the norm of the stored fp32 mean, summed in fp64 and rounded once
+    np.testing.assert_allclose(kn, np.sqrt((kbar.astype(np.float64) ** 2).sum(-1)), rtol=1.2e-7, atol=0)
     import oracle
     for b in range(w.batch):
         for h in range(w.H):
@@ -239,10 +242,13 @@ def test_score_with_precomputed_split_matches():
      {}),
     (synth.Workload(batch=1, H=2, N=1111, d=128, dtype="bf16", seed=75), fsl.Params(P=9, W=3, K=8), {"lam": 0.0}),
     (synth.Workload(batch=1, H=2, N=100, d=64, dtype="bf16", seed=76), fsl.Params(P=2, W=1), {}),
-], ids=["d128", "d64-K3-gain", "FS", "K8-lam0", "one-block"])
+    # content matters: priors close together, so the tile bound holds for some tiles and not others
+    (synth.Workload(batch=1, H=4, N=4000, d=128, dtype="bf16", seed=77), fsl.Params(), {"lam": 0.02}),
+    (synth.Workload(batch=2, H=2, N=4096, d=128, dtype="bf16", seed=78, needle_frac=0.005), fsl.Params(), {}),
+], ids=["d128", "d64-K3-gain", "FS", "K8-lam0", "one-block", "lam0.02", "needles-4k"])
 def test_fused_route_readout_matches_two_kernels(w, p, extra):
     """fs_select_readout in its single-kernel form gives bitwise the selections and outputs
-    of fs_score_select followed by fs_readout."""
+    of fs_score_select followed by fs_readout, with and without the tile bound (kbar_norm)."""
     host = pu.inputs(w)
     q, k, v = (pu.to_device(host[x], w.dtype) for x in "qkv")
     gain = torch.from_numpy(synth.gains(97, w.H, w.d)).cuda() if extra.get("gain") else None
@@ -251,7 +257,8 @@ def test_fused_route_readout_matches_two_kernels(w, p, extra):
     kbar = torch.empty(w.batch, w.H, max(M, 1), w.d, dtype=torch.float32, device="cuda")
     a = torch.empty(w.batch, w.H, max(M, 1), dtype=torch.float32, device="cuda")
     ks = torch.empty(w.batch, w.H, max(M, 1), 3, w.d, dtype=torch.int16, device="cuda")
-    fsl.fs_cell_summaries(k, kbar, a, p, kbar_split=ks)
+    kn = torch.empty(w.batch, w.H, max(M, 1), dtype=torch.float32, device="cuda")
+    fsl.fs_cell_summaries(k, kbar, a, p, kbar_split=ks, kbar_norm=kn)
     ret = nret = None
     if p.prune:
         sh = fsl.shape_of(k)
@@ -269,7 +276,12 @@ def test_fused_route_readout_matches_two_kernels(w, p, extra):
     fsl.fs_select_readout(q, k, v, kbar, a, ret, nret, 4.0, lam, gain, o2, s2, p, kbar_split=ks)
     o3 = torch.empty_like(q)
     fsl.fs_select_readout(q, k, v, kbar, a, ret, nret, 4.0, lam, gain, o3, None, p, kbar_split=ks)
+    s4 = torch.full_like(s1, -7)
+    o4 = torch.empty_like(q)
+    fsl.fs_select_readout(q, k, v, kbar, a, ret, nret, 4.0, lam, gain, o4, s4, p, kbar_split=ks, kbar_norm=kn)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2)
+    assert torch.equal(s1, s4)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o4.view(torch.int16))
