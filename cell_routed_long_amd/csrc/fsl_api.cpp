@@ -42,6 +42,10 @@ fs_status check_shape(const fs_shape *sh)
     if ((sh->d != 64 && sh->d != 128) || sh->H > FS_MAX_HEADS || sh->N > kMaxTokens ||
         (int64_t)sh->batch * sh->H > 65535)
         return FS_ERR_UNSUPPORTED;
+    // grids: one wave per cell (summaries), one workgroup per 128-query block;
+    // at most 2^26 cells keeps every launch below 2^32 work-items
+    if ((int64_t)sh->batch * sh->H * ((sh->N + 31) / 32) > ((int64_t)1 << 26))
+        return FS_ERR_UNSUPPORTED;
     return FS_OK;
 }
 

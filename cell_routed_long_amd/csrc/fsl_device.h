@@ -150,11 +150,12 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x)
 // contiguous run of logical blocks keeps the blocks of one head (which share
 // its mean keys and its most-selected cells) on one L2.
 constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_logical_block(int64_t w, int64_t total)
+// 32-bit arithmetic: the host keeps every grid below 2^24 workgroups.
+__device__ __forceinline__ uint32_t xcd_logical_block(uint32_t w, uint32_t total)
 {
-    const int64_t per = (total + kXcds - 1) / kXcds; // blocks on the fuller XCDs
-    const int64_t full = total - (per - 1) * kXcds;  // XCDs that receive `per` blocks
-    const int64_t xcd = w % kXcds, idx = w / kXcds;
+    const uint32_t per = (total + kXcds - 1) / kXcds; // blocks on the fuller XCDs
+    const uint32_t full = total - (per - 1) * kXcds;  // XCDs that receive `per` blocks
+    const uint32_t xcd = w % kXcds, idx = w / kXcds;
     return xcd < full ? xcd * per + idx : full * per + (xcd - full) * (per - 1) + idx;
 }
 
@@ -188,19 +189,19 @@ __device__ __forceinline__ void insert_key(uint64_t (&kl)[KT], uint64_t key)
 }
 
 
-// Enter one scored tile's 16 keys of this lane into its descending top-KT list.
+// Enter one scored tile's NK keys of this lane into its descending top-KT list.
 // On the first tile the list is empty and its first KT keys go in without a
 // test.  The rest are first tested as a group against the K-th best (on the
 // high words, which can only let too many through): the retained cells come
 // in priority order, so after the first tile a key seldom enters, and a wave
 // skips the select network unless one of its lanes keeps one of these keys.
 // The keys are consumed.
-template <int KT>
-__device__ __forceinline__ void take_tile_keys(uint64_t (&kl)[KT], uint64_t (&key)[16], bool first)
+template <int KT, int NK = 16>
+__device__ __forceinline__ void take_tile_keys(uint64_t (&kl)[KT], uint64_t (&key)[NK], bool first)
 {
     if (first) {
 #pragma unroll
-        for (int r = 0; r < KT && r < 16; ++r) {
+        for (int r = 0; r < KT && r < NK; ++r) {
             insert_key<KT>(kl, key[r]);
             key[r] = 0; // now in the list: must not enter twice
         }
@@ -208,12 +209,12 @@ __device__ __forceinline__ void take_tile_keys(uint64_t (&kl)[KT], uint64_t (&ke
     const uint32_t kth = (uint32_t)(kl[KT - 1] >> 32);
     bool any = false;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < NK; ++r)
         any |= (uint32_t)(key[r] >> 32) >= kth;
     if (__ballot(any) == 0ull)
         return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < NK; ++r)
         if (__ballot(key[r] > kl[KT - 1]))
             insert_key<KT>(kl, key[r]);
 }
@@ -224,21 +225,21 @@ __device__ __forceinline__ void take_tile_keys(uint64_t (&kl)[KT], uint64_t (&ke
 // with 16-byte accesses by consecutive threads makes every wave instruction
 // touch 4 whole rows instead of 32 partial ones.  Rows at or past `rows` are
 // zero-filled on load and skipped on store.  stride: LDS row pitch in elements.
-template <int D, int NT>
+template <int D, int NT, int ROWS = 128>
 __device__ __forceinline__ void tile_load_bf16(uint16_t *lds, int stride, const uint16_t *__restrict__ g, int rows)
 {
     constexpr int CPR = D / 8; // 16-byte chunks per row
-    for (int c = threadIdx.x; c < 128 * CPR; c += NT) {
+    for (int c = threadIdx.x; c < ROWS * CPR; c += NT) {
         const int r = c / CPR, c8 = (c % CPR) * 8;
         const u32x4 w = r < rows ? *reinterpret_cast<const u32x4 *>(g + (int64_t)r * D + c8) : u32x4{0, 0, 0, 0};
         *reinterpret_cast<u32x4 *>(lds + r * stride + c8) = w;
     }
 }
-template <int D, int NT>
+template <int D, int NT, int ROWS = 128>
 __device__ __forceinline__ void tile_store_bf16(uint16_t *__restrict__ g, const uint16_t *lds, int stride, int rows)
 {
     constexpr int CPR = D / 8;
-    for (int c = threadIdx.x; c < 128 * CPR; c += NT) {
+    for (int c = threadIdx.x; c < ROWS * CPR; c += NT) {
         const int r = c / CPR, c8 = (c % CPR) * 8;
         if (r < rows)
             *reinterpret_cast<u32x4 *>(g + (int64_t)r * D + c8) = *reinterpret_cast<const u32x4 *>(lds + r * stride + c8);

@@ -76,9 +76,9 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     constexpr int PER = D / 8;  // mean-key elements staged per thread and tile
     constexpr int SCH = PER / 8; // 16-byte chunks per part and thread
     constexpr int KC = D / 16;  // k-steps of the bf16 matrix products
-    const int64_t lb = xcd_logical_block(blockIdx.x, (int64_t)gridDim.x);
-    const int beta = (int)(lb % NB);
-    const int64_t head = lb / NB;
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int beta = (int)(lb % (uint32_t)NB);
+    const int64_t head = (int64_t)(lb / (uint32_t)NB);
     const int h = (int)(head % H);
     const int t = threadIdx.x;
     const int wave = t / kWave;

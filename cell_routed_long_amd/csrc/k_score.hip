@@ -59,9 +59,9 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
     __shared__ ScoreSmem<T, D> sm;
     constexpr bool kBf16 = sizeof(T) == 2;
     constexpr int PER = D / 8; // mean-key floats staged per thread and tile
-    const int64_t lb = xcd_logical_block(blockIdx.x, (int64_t)gridDim.x);
-    const int beta = (int)(lb % NB);
-    const int64_t head = lb / NB;
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int beta = (int)(lb % (uint32_t)NB);
+    const int64_t head = (int64_t)(lb / (uint32_t)NB);
     const int h = (int)(head % H);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);

@@ -58,7 +58,9 @@ typedef struct {
     float eps;
 } fs_params;
 
-/* batch sequences x H heads x N positions x d features (d in {64, 128}). */
+/* batch sequences x H heads x N positions x d features (d in {64, 128}).
+ * Kernels support N <= 2^22, batch * H <= 65535 and batch * H * ceil(N / 32)
+ * <= 2^26 cells; larger shapes give FS_ERR_UNSUPPORTED. */
 typedef struct {
     int32_t batch, H;
     int64_t N;
@@ -151,7 +153,7 @@ fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q,
  * tile of 32 retained cells when an upper bound of every score in it
  * (max lambda_h a_c + max |q_i| max |kbar_c| / sqrt(d), widened for rounding)
  * lies below every query's K-th best score so far: no such cell can be
- * selected, so the results are unchanged.
+ * selected, so the results are bitwise unchanged.
  *   q, k, v                [batch, H, N, d]  shape dtype (input)
  *   kbar, kbar_split, kbar_norm, a   from fs_cell_summaries (kbar_split and
  *                          kbar_norm may be NULL)

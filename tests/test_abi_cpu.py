@@ -71,6 +71,8 @@ def call_summaries(L, sh, p, k=1, kbar=1, a=1):
     (shape(), prm(B=256), fsl.FS_ERR_UNSUPPORTED),
     (shape(), prm(P=1000, W=100), fsl.FS_ERR_UNSUPPORTED),
     (shape(N=(1 << 22) + 1), prm(), fsl.FS_ERR_UNSUPPORTED),
+    (shape(b=8, H=128, N=1 << 22), prm(), fsl.FS_ERR_UNSUPPORTED),  # more than 2^26 cells
+    (shape(b=512, H=128), prm(), fsl.FS_ERR_UNSUPPORTED),          # batch * H > 65535
 ])
 def test_summaries_rejects_bad_arguments(L, sh, p, expect):
     assert call_summaries(L, sh, p) == expect
