@@ -91,6 +91,7 @@ __device__ __forceinline__ uint64_t score_key(double sc, int pos)
 __device__ __forceinline__ int count_greater(const uint64_t *k, int n8, uint64_t mine)
 {
     int r = 0;
+#pragma unroll 4
     for (int x = 0; x < n8; x += 8) {
         uint64_t v[8];
 #pragma unroll
@@ -470,7 +471,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     if (scored && my_part == 0) {
         const int32_t c = s_cell[my_slot];
         const double delta = (double)i - ((double)c + 0.5) * kS;
-        const double g = erf(delta / (2.0 * (double)hc.sigma[h]));
+        // erf rounds to exactly 1 in fp64 from 6 on (erfc(6) < 2^-54): skip the series there
+        const double x = delta / (2.0 * (double)hc.sigma[h]);
+        const double g = x >= 6.0 ? 1.0 : erf(x);
         s_key[ri] = score_key(dot / sqrt((double)D) + (double)hc.lambda[h] * (double)s_a[my_slot] * g, ri);
         s_rc[ri] = c;
         s_rslot[ri] = my_slot;

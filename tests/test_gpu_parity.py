@@ -208,6 +208,14 @@ def test_fs_32k_sampled():
     check(w, fsl.Params(prune=False), heads=[(0, 3), (0, 12)])
 
 
+@pytest.mark.parametrize("P,W", [(240, 16), (300, 20)], ids=["cap256-single-kernel", "cap320-two-kernels"])
+def test_large_retained_sets(P, W):
+    """Retained sets at the single-kernel limit (P + W = 256) and past it (the
+    prefill then scores and reads out in two kernels), bf16 d128 N8192."""
+    w = synth.Workload(batch=1, H=2, N=8192, d=128, dtype="bf16", seed=79, needle_frac=0.01)
+    check(w, fsl.Params(P=P, W=W))
+
+
 def test_score_with_precomputed_split_matches():
     """fs_score_select with the bf16 parts from fs_cell_summaries selects exactly what it
     selects when it splits the fp32 means itself (same operands on the matrix cores)."""
