@@ -8,8 +8,10 @@ K=4, sigma_h=4, lambda_h=1.
 
 A step is one pass of the whole path over the batch: cell summaries, retained
 sets, scores + top-K, gather-readout + RMSNorm, issued through the C ABI as
-four calls on one stream with HIP events between them, so that every kernel's
-average launch time is measured inside the timed region.  Prints one JSON line.
+three calls on one stream with HIP events between them, so that every kernel's
+average launch time is measured inside the timed region.  Before the W warm-up
+steps, steps run untimed for SETTLE_S seconds so that the GPU clocks have left
+their ramp.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -23,6 +25,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+SETTLE_S = 0.3  # seconds of untimed load before the warm-up steps
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "long-range FS-L query-tokens/s at 16k prefill; % HBM/MFMA roofline"
@@ -39,6 +42,23 @@ DECODE_LAYER_STATES = 12  # independent states in rotation: 12 x ~26 MB per step
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def settle_clocks(work, seconds: float = SETTLE_S) -> int:
+    """Run `work` back to back, untimed, for `seconds` of wall time before the
+    warm-up steps: the GPU raises its clocks only after some tens of
+    milliseconds of sustained load, and a timed region right after a short
+    warm-up would measure the ramp.  Returns the number of calls made."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        work()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def kernel_source_digest(names) -> str:
@@ -82,8 +102,8 @@ def distinct_cells_per_block(sel, B: int):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_16k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -157,6 +177,7 @@ def main() -> int:
         if evs is not None:
             evs[3].record(stream)
 
+    settle = settle_clocks(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -299,6 +320,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "settle_steps": settle,
         "single_call_ms": round(single_ms, 4),
         "single_call_matches_staged": same,
         "parity_spot_check": parity,
@@ -391,6 +413,11 @@ def run_decode(args) -> int:
     stream.wait_stream(cap)
     torch.cuda.synchronize()
 
+    def replay_all():
+        restore()
+        graph.replay()
+
+    settle = settle_clocks(replay_all)
     restore()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -507,6 +534,7 @@ def run_decode(args) -> int:
         "us_per_step_and_state": round(per_launch_ms * 1e3, 3),
         "us_per_step_single_state_warm": round(single_us, 3),
         "us_per_step_eager": round(eager_us, 3),
+        "settle_replays": settle,
         "state_build_ms": round(build_ms, 3),
         "state_bytes": int(snap.numel()),
         "layer_states_agree": same_states,

@@ -16,10 +16,8 @@
 //             the block's distinct selected cells are listed in id order;
 //   readout   each listed cell's keys and values are gathered once and applied
 //             to every query of the block on the matrix cores with the running
-//             softmax, exactly as fs_readout does; two LDS buffers alternate, so
-//             the next cell is staged while the current one is on the matrix
-//             cores and one barrier per cell suffices, with the cell after it
-//             already requested from memory;
+//             softmax, exactly as fs_readout does; the next cell is in flight
+//             while the current one is on the matrix cores;
 //   epilogue  RMSNorm, then the block's output tile goes out through LDS with
 //             coalesced 16-byte stores.
 // The arithmetic is the same as the two separate kernels, so the results are
@@ -48,10 +46,10 @@ struct alignas(16) FusedSmem {
     static constexpr int kStrideV = 32 + 8; // bf16 elements per V^T row (80 bytes: 16-byte aligned, conflict-free)
     union {
         uint16_t kb[3][32][kStride]; // routing: one tile of mean-key parts
-        struct {                     // readout: two cells (double buffer)
+        struct {                     // readout: one cell
             uint16_t k[32][kStride];
             uint16_t vt[D][kStrideV];
-        } rb[2];
+        };
         uint16_t tile[128][kStride]; // epilogue: the block's output tile
     };
     float prior[32];
@@ -282,20 +280,21 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             pcmax = fmaxf(pcmax, pcv[r]);
         const bool need_erf = __ballot(q_ok && (qpos - pcmax) * inv2s < 4.0f) != 0ull;
         uint64_t key[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float score = fmaf(prv[r], 1.0f, acc[r] * inv_sqrt_d);
-            key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-        }
-        if (need_erf) { // redo the rows where a query of the wave is close enough for erf < 1
+        if (need_erf) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                float g = 1.0f;
                 const float x = (qpos - pcv[r]) * inv2s; // (i - p_c) / (2 sigma_h), i - p_c exact
-                if (__ballot(q_ok && x < 4.0f)) {
-                    const float g = x < 4.0f ? erff(x) : 1.0f;
-                    const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
-                    key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-                }
+                if (x < 4.0f)
+                    g = erff(x);
+                const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float score = fmaf(prv[r], 1.0f, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
             }
         }
         take_tile_keys<KT>(kl, key, t0 == 0);
@@ -368,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     __syncthreads();
     const int nU = n_u;
 
-    // ---- readout (Eq. 9): one gathered cell at a time, double-buffered ----
+    // ---- readout (Eq. 9): one gathered cell at a time, next one in flight ----
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int KCH = (32 * CPR) / kThreads; // K chunks per thread: 1 or 2
     const int tp = t & 15;
@@ -387,28 +386,8 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             pv1 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp + 1) * D + fc * 8);
         }
     };
-    auto stage = [&](int bi) {
-#pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int ch = t + u * kThreads;
-            *reinterpret_cast<u32x4 *>(&sm.rb[bi].k[ch / CPR][(ch % CPR) * 8]) = pk[u];
-        }
-        if (fc < CPR) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t a0 = (pv0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                const uint32_t a1 = (pv1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *reinterpret_cast<uint32_t *>(&sm.rb[bi].vt[fc * 8 + e][vt_pos(2 * tp)]) = a0 | (a1 << 16);
-            }
-        }
-    };
-    if (nU > 0) {
+    if (nU > 0)
         fetch(ulist[0]);
-        stage(0);
-        if (nU > 1)
-            fetch(ulist[1]);
-    }
-    __syncthreads();
 
     constexpr int DT = D / 32; // feature tiles of the output
     f32x16 o_acc[DT];
@@ -421,20 +400,30 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
 
     for (int x = 0; x < nU; ++x) {
         const int cell = ulist[x];
-        const int bi = x & 1;
-        if (x + 1 < nU) { // cell x+1 into the other buffer (free since the last barrier)
-            stage(bi ^ 1);
-            if (x + 2 < nU)
-                fetch(ulist[x + 2]);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < KCH; ++u) {
+            const int ch = t + u * kThreads;
+            *reinterpret_cast<u32x4 *>(&sm.k[ch / CPR][(ch % CPR) * 8]) = pk[u];
         }
+        if (fc < CPR) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t a0 = (pv0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                const uint32_t a1 = (pv1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][vt_pos(2 * tp)]) = a0 | (a1 << 16);
+            }
+        }
+        __syncthreads();
+        if (x + 1 < nU)
+            fetch(ulist[x + 1]);
+
         bool mine = false;
 #pragma unroll
         for (int j = 0; j < KT; ++j)
             mine |= my_sel[j] == cell;
-        if (__ballot(mine) == 0ull) {
-            __syncthreads();
+        if (__ballot(mine) == 0ull)
             continue; // no query of this wave reads the cell
-        }
 
         f32x16 acc;
 #pragma unroll
@@ -442,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             acc[r] = 0.0f;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.rb[bi].k[col][kc * 16 + half * 8]);
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.k[col][kc * 16 + half * 8]);
             acc = mfma_bf16(as_bf16x8(w), qf[kc], acc);
         }
         float p[16];
@@ -461,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             bf16x8 av[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                av[dt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.rb[bi].vt[dt * 32 + col][16 * kk + 8 * half]));
+                av[dt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.vt[dt * 32 + col][16 * kk + 8 * half]));
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) // lo parts of every tile, then hi parts: no back-to-back chain
                 o_acc[dt] = mfma_bf16(av[dt], bl, o_acc[dt]);
@@ -469,7 +458,6 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             for (int dt = 0; dt < DT; ++dt)
                 o_acc[dt] = mfma_bf16(av[dt], bh, o_acc[dt]);
         }
-        __syncthreads();
     }
 
     // ---- normalise, RMSNorm over d (Eq. 17), write through LDS ----

@@ -250,20 +250,21 @@ __global__ __launch_bounds__(kThreads) void score_topk_kernel(
             pcmax = fmaxf(pcmax, pcv[r]);
         const bool need_erf = __ballot(q_ok && (qpos - pcmax) * inv2s < 4.0f) != 0ull;
         uint64_t key[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float score = fmaf(prv[r], 1.0f, acc[r] * inv_sqrt_d);
-            key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-        }
-        if (need_erf) { // redo the rows where a query of the wave is close enough for erf < 1
+        if (need_erf) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                float g = 1.0f;
                 const float x = (qpos - pcv[r]) * inv2s; // (i - p_c) / (2 sigma_h), i - p_c exact
-                if (__ballot(q_ok && x < 4.0f)) {
-                    const float g = x < 4.0f ? erff(x) : 1.0f;
-                    const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
-                    key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-                }
+                if (x < 4.0f)
+                    g = erff(x);
+                const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float score = fmaf(prv[r], 1.0f, acc[r] * inv_sqrt_d);
+                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
             }
         }
         take_tile_keys<KT>(kl, key, t0 == 0);
