@@ -14,10 +14,12 @@
 //             query's top-K in registers, exactly as fs_score_select does;
 //   union     the selections go to LDS (and, if asked, to global memory) and
 //             the block's distinct selected cells are listed in id order;
-//   readout   each listed cell's keys and values are gathered once and applied
-//             to every query of the block on the matrix cores with the running
-//             softmax, exactly as fs_readout does; the next cell is in flight
-//             while the current one is on the matrix cores;
+//   readout   each listed cell's keys and values are gathered once into LDS
+//             (both row-major; the P.V operand comes from transposing LDS
+//             reads) and applied to every query of the block on the matrix
+//             cores with the running softmax, exactly as fs_readout does; the
+//             next cell is in flight while the current one is on the matrix
+//             cores;
 //   epilogue  RMSNorm, then the block's output tile goes out through LDS with
 //             coalesced 16-byte stores.
 // The arithmetic is the same as the two separate kernels, so the results are
@@ -32,23 +34,20 @@
 namespace fsl {
 namespace {
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 
-// V^T rows keep a cell's 32 tokens in the order 0-3, 8-11, 4-7, 12-15, 16-19,
-// 24-27, 20-23, 28-31: then the 8 tokens a lane feeds to one P.V product
-// (16 kk + 4 half + 0..3 and 16 kk + 8 + 4 half + 0..3, the order of its
-// probabilities in the logits accumulator) are 16 contiguous bytes.
-__device__ __forceinline__ int vt_pos(int tok) { return tok ^ (((tok >> 2) ^ (tok >> 3)) & 1) * 12; }
 
 template <int D>
 struct alignas(16) FusedSmem {
     static constexpr int kStride = D + 8;   // bf16 elements per row (16-byte pad against bank conflicts)
-    static constexpr int kStrideV = 32 + 8; // bf16 elements per V^T row (80 bytes: 16-byte aligned, conflict-free)
+    static constexpr int kStrideVR = D + 16; // bf16 elements per V row (transposed reads of 4 rows hit distinct banks)
     union {
         uint16_t kb[3][32][kStride]; // routing: one tile of mean-key parts
         struct {                     // readout: one cell
             uint16_t k[32][kStride];
-            uint16_t vt[D][kStrideV];
+            uint16_t v[32][kStrideVR];
         };
         uint16_t tile[128][kStride]; // epilogue: the block's output tile
     };
@@ -370,9 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     // ---- readout (Eq. 9): one gathered cell at a time, next one in flight ----
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int KCH = (32 * CPR) / kThreads; // K chunks per thread: 1 or 2
-    const int tp = t & 15;
-    const int fc = t >> 4; // V roles exist for fc < CPR
-    u32x4 pk[KCH], pv0, pv1;
+    u32x4 pk[KCH], pv[KCH];
     auto fetch = [&](int cell) {
         const uint16_t *kc_src = k + (head * N + (int64_t)cell * s) * D;
         const uint16_t *vc_src = v + (head * N + (int64_t)cell * s) * D;
@@ -380,10 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         for (int u = 0; u < KCH; ++u) {
             const int ch = t + u * kThreads;
             pk[u] = *reinterpret_cast<const u32x4 *>(kc_src + (int64_t)(ch / CPR) * D + (ch % CPR) * 8);
-        }
-        if (fc < CPR) {
-            pv0 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp) * D + fc * 8);
-            pv1 = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(2 * tp + 1) * D + fc * 8);
+            pv[u] = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(ch / CPR) * D + (ch % CPR) * 8);
         }
     };
     if (nU > 0)
@@ -405,14 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         for (int u = 0; u < KCH; ++u) {
             const int ch = t + u * kThreads;
             *reinterpret_cast<u32x4 *>(&sm.k[ch / CPR][(ch % CPR) * 8]) = pk[u];
-        }
-        if (fc < CPR) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t a0 = (pv0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                const uint32_t a1 = (pv1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                *reinterpret_cast<uint32_t *>(&sm.vt[fc * 8 + e][vt_pos(2 * tp)]) = a0 | (a1 << 16);
-            }
+            *reinterpret_cast<u32x4 *>(&sm.v[ch / CPR][(ch % CPR) * 8]) = pv[u];
         }
         __syncthreads();
         if (x + 1 < nU)
@@ -447,10 +434,22 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 bh, bl;
             split_bf16x8(&p[8 * kk], bh, bl);
+            // A = V^T rows: lane (col, half) needs V[t][dt * 32 + col] for the tokens t of its
+            // probabilities (16 kk + 4 half + 0..3, then + 8); two transposed 4-row reads
+            // from row-major V give them (lane j of a 16-lane group names row j / 4, and
+            // features 4 (j % 4) .. +3 of the group's 16)
             bf16x8 av[DT];
+            const int r0 = 16 * kk + 4 * half + ((lane & 15) >> 2);
+            const int c0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                av[dt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.vt[dt * 32 + col][16 * kk + 8 * half]));
+            for (int dt = 0; dt < DT; ++dt) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)&sm.v[r0][dt * 32 + c0]);
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)&sm.v[r0 + 8][dt * 32 + c0]);
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                av[dt] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+            }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) // lo parts of every tile, then hi parts: no back-to-back chain
                 o_acc[dt] = mfma_bf16(av[dt], bl, o_acc[dt]);

@@ -88,28 +88,42 @@ __global__ __launch_bounds__(kWave) void prune_emit_kernel(const int32_t *__rest
     const float *ah = a + head * M;
     int32_t *dst = retained + (head * NB + beta) * (int64_t)cap;
     int count = 0;
-    // non-recent cells still in TopP
-    for (int64_t base = 0; base < recent0; base += kWave) {
-        const int64_t c = base + lane;
-        const bool keep = c < recent0 && dh[c] > beta;
-        const uint64_t mask = __ballot(keep);
-        const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
-        if (keep && pos < cap)
-            s_id[pos] = (int32_t)c;
-        count += __popcll(mask);
+    // non-recent cells still in TopP: exit blocks and norms, 8 windows of 64 per round trip
+    constexpr int kWin = 8;
+    for (int64_t base = 0; base < recent0; base += kWin * kWave) {
+        int32_t dv[kWin];
+        float av[kWin];
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+            const int64_t c = base + u * kWave + lane;
+            dv[u] = c < recent0 ? dh[c] : 0;
+            av[u] = c < recent0 ? ah[c] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+            const int64_t c = base + u * kWave + lane;
+            const bool keep = c < recent0 && dv[u] > beta;
+            const uint64_t mask = __ballot(keep);
+            const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+            if (keep && pos < cap) {
+                s_id[pos] = (int32_t)c;
+                s_a[pos] = av[u];
+            }
+            count += __popcll(mask);
+        }
     }
     if (count > cap - (int)(n_avail - recent0)) // only reachable with non-finite norms
         count = cap - (int)(n_avail - recent0);
     // the W most recent cells
-    for (int64_t c = recent0 + lane; c < n_avail; c += kWave)
+    for (int64_t c = recent0 + lane; c < n_avail; c += kWave) {
         s_id[count + (c - recent0)] = (int32_t)c;
+        s_a[count + (c - recent0)] = ah[c];
+    }
     count += (int)(n_avail - recent0);
     const int n4 = (count + 3) & ~3;
-    for (int x = lane; x < n4; x += kWave) {
-        const bool live = x < count;
-        const int32_t c = live ? s_id[x] : INT32_MAX;
-        s_a[x] = live ? ah[c] : -INFINITY; // padding ranks last
-        s_id[x] = c;
+    for (int x = count + lane; x < n4; x += kWave) { // padding ranks last
+        s_a[x] = -INFINITY;
+        s_id[x] = INT32_MAX;
     }
     __syncthreads();
     // priority order (a desc, id asc): each cell's rank is the number of cells before it

@@ -19,7 +19,7 @@ namespace fsl {
 namespace {
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void cell_summaries_kernel(const T *__restrict__ k, float *__restrict__ kbar,
+__global__ __launch_bounds__(256, 5) void cell_summaries_kernel(const T *__restrict__ k, float *__restrict__ kbar,
                                                              float *__restrict__ a,
                                                              uint16_t *__restrict__ kbar_split,
                                                              float *__restrict__ kbar_norm, int64_t N, int64_t M,
