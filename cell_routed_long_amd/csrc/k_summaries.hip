@@ -12,7 +12,9 @@
 // matrix cores, so that the split is done once per cell instead of once per
 // query block, and its Euclidean norm (fp64, rounded once), which bounds the
 // content term of every score of the cell (|q . kbar| <= |q| |kbar|).
-// HBM-bound: the kernel reads each key exactly once.
+// HBM-bound: the kernel reads each key exactly once, with streaming
+// (non-temporal) loads, so the keys do not displace from the caches the cells
+// and mean keys the routing and readout kernel gathers next.
 #include "fsl_internal.h"
 
 namespace fsl {
@@ -46,7 +48,8 @@ __global__ __launch_bounds__(256, 5) void cell_summaries_kernel(const T *__restr
     u32x4 buf[PER_LANE];
 #pragma unroll
     for (int t = 0; t < PER_LANE; ++t)
-        buf[t] = *reinterpret_cast<const u32x4 *>(base + (int64_t)(row0 + t * ROWS_STEP) * D + group * EPC);
+        buf[t] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(base + (int64_t)(row0 + t * ROWS_STEP) * D + group * EPC));
 
     double colsum[EPC];
 #pragma unroll
