@@ -99,16 +99,19 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
 
     // ---- entry: |A|, the retained list and the query fragments, all at once ----
     const int nA = prune ? n_ret[head * NB + beta] : (int)n_avail;
-    if (prune && t < cap)
-        s_A[t] = retained[(head * NB + beta) * (int64_t)cap + t];
+    const int32_t my_ret = prune && t < cap ? retained[(head * NB + beta) * (int64_t)cap + t] : 0;
     bf16x8 qf[KC];
     {
-        const uint16_t *qrow = q + (head * N + (q_ok ? qi : 0)) * D;
+        // lanes past N load row N-1 and are masked where their results would count
+        // (routing keys, the tile bound, selections); nothing here waits for the
+        // loads, so the retained list and first mean-key tile are requested with them
+        const uint16_t *qrow = q + (head * N + (q_ok ? qi : N - 1)) * D;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
-            qf[kc] = as_bf16x8(q_ok ? *reinterpret_cast<const u32x4 *>(qrow + kc * 16 + half * 8)
-                                    : u32x4{0, 0, 0, 0});
+            qf[kc] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + kc * 16 + half * 8));
     }
+    if (prune && t < cap)
+        s_A[t] = my_ret;
     __syncthreads();
 
     // ---- routing (Eq. 7) with the running top-K of this lane's query ----
@@ -120,17 +123,21 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     // load each per block, kept in registers until the first tile is scored
     const bool bound = kbar_norm != nullptr && nA > 32 && nA <= kThreads;
     float b_pr = 0.0f, b_kn = 0.0f;
-    if (bound && t < nA) {
+    if (bound && t < nA) { // lambda is applied where the values are first used, so nothing waits here
         const int64_t id = head * M + (prune ? s_A[t] : t);
-        b_pr = lam * a[id];
+        b_pr = a[id];
         b_kn = kbar_norm[id];
     }
+    const uint16_t *kbs_h = kbar_split + head * M * 3 * D; // this head's mean-key parts
+    int pre_t0 = -1;                                       // the tile whose parts pre3 holds
     auto prefetch = [&](int t0) {
+        pre_t0 = t0;
         const int x = t0 + srow;
         pre_id = x < nA ? (prune ? s_A[x] : x) : -1;
         pre_a = 0.0f;
         if (pre_id >= 0) {
-            const uint16_t *src = kbar_split + (head * M + pre_id) * 3 * D + spart * PER;
+            // < 3 d M elements: the offset fits 32 bits
+            const uint16_t *src = kbs_h + (uint32_t)(pre_id * 3 * D + spart * PER);
 #pragma unroll
             for (int part = 0; part < 3; ++part)
 #pragma unroll
@@ -160,8 +167,9 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     // those of scoring every cell.  The first tile is always scored.
     __shared__ float s_bpr[kThreads], s_bkn[kThreads], s_qn[kThreads / kWave];
     __shared__ uint32_t s_tau[2][kThreads / kWave];
-    for (int t0 = 0; t0 < nA; t0 += 32) {
-        const int par = (t0 >> 5) & 1; // tau slots alternate, so no wave overwrites one still being read
+    int iter = 0;
+    for (int t0 = 0; t0 < nA; t0 += 32, ++iter) {
+        const int par = iter & 1; // tau slots alternate, so no wave overwrites one still being read
         if (bound && t0 > 0) {
             const uint32_t tau = wave_min_u32(q_ok ? (uint32_t)(kl[KT - 1] >> 32) : 0xffffffffu);
             if (lane == 0)
@@ -190,11 +198,14 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
                 qn = fmaxf(qn, s_qn[w]);
                 tau = min(tau, s_tau[par][w]);
             }
-            if (tile_below(t0)) {
-                if (t0 + 32 < nA && !tile_below(t0 + 32))
-                    prefetch(t0 + 32); // the next tile is fetched only if it may be scored
-                continue;
-            }
+            // tau stays fixed until a tile is scored: pass over every tile below it at once
+            // (the test is uniform over the block, so every wave leaves or stays together)
+            while (t0 < nA && tile_below(t0))
+                t0 += 32;
+            if (t0 >= nA)
+                break;
+            if (pre_t0 != t0)
+                prefetch(t0); // the tile held in registers was passed over
         }
         if (spart == 0) {
             sm.id[srow] = pre_id >= 0 ? 0x7fffffff - pre_id : -1;   // low half of the ranking key
@@ -237,7 +248,10 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
                 const u32x4 w = __builtin_bit_cast(u32x4, qf[kc]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bf16x2 x = __builtin_bit_cast(bf16x2, w[e]);
+                    // the element goes through a named copy: hipcc miscompiles a bit cast
+                    // of a vector element taken in place (it reads element 0)
+                    const uint32_t we = w[e];
+                    const bf16x2 x = __builtin_bit_cast(bf16x2, we);
                     ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
                 }
             }
@@ -249,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             if (lane == 0)
                 s_qn[wave] = badq ? INFINITY : qm;
             if (t < nA) { // read after the next barrier, like s_qn
-                s_bpr[t] = b_pr;
+                s_bpr[t] = lam * b_pr;
                 s_bkn[t] = b_kn;
             }
         }
@@ -370,14 +384,16 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int KCH = (32 * CPR) / kThreads; // K chunks per thread: 1 or 2
     u32x4 pk[KCH], pv[KCH];
+    const uint16_t *k_h = k + head * N * D, *v_h = v + head * N * D; // this head's keys and values
     auto fetch = [&](int cell) {
-        const uint16_t *kc_src = k + (head * N + (int64_t)cell * s) * D;
-        const uint16_t *vc_src = v + (head * N + (int64_t)cell * s) * D;
+        // element offsets within the head: N d <= 2^29, so 32 bits hold them
+        const uint32_t base = (uint32_t)cell * (uint32_t)(s * D);
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
             const int ch = t + u * kThreads;
-            pk[u] = *reinterpret_cast<const u32x4 *>(kc_src + (int64_t)(ch / CPR) * D + (ch % CPR) * 8);
-            pv[u] = *reinterpret_cast<const u32x4 *>(vc_src + (int64_t)(ch / CPR) * D + (ch % CPR) * 8);
+            const uint32_t off = base + (uint32_t)((ch / CPR) * D + (ch % CPR) * 8);
+            pk[u] = *reinterpret_cast<const u32x4 *>(k_h + off);
+            pv[u] = *reinterpret_cast<const u32x4 *>(v_h + off);
         }
     };
     if (nU > 0)
@@ -465,6 +481,14 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
     // one straight-line copy with the gain vector and one without (the test is uniform)
     auto emit = [&](auto with_gain) {
         const float *gh = gain + (int64_t)h * D;
+        u32x4 gv[DT][4]; // this lane's 4-feature runs of the gain vector, loaded together
+        if constexpr (decltype(with_gain)::value) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg)
+                    gv[dt][rg] = *reinterpret_cast<const u32x4 *>(gh + dt * 32 + 8 * rg + 4 * half);
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -475,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
                 for (int e = 0; e < 4; ++e) {
                     y[e] = o_acc[dt][4 * rg + e] * c;
                     if constexpr (decltype(with_gain)::value)
-                        y[e] = l_run > 0.0f ? y[e] * gh[d0 + e] : 0.0f;
+                        y[e] = l_run > 0.0f ? y[e] * __uint_as_float(gv[dt][rg][e]) : 0.0f;
                 }
                 *reinterpret_cast<u32x2 *>(&sm.tile[wave * 32 + col][d0]) =
                     u32x2{cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3])};

@@ -253,12 +253,20 @@ def test_score_with_precomputed_split_matches():
     # content matters: priors close together, so the tile bound holds for some tiles and not others
     (synth.Workload(batch=1, H=4, N=4000, d=128, dtype="bf16", seed=77), fsl.Params(), {"lam": 0.02}),
     (synth.Workload(batch=2, H=2, N=4096, d=128, dtype="bf16", seed=78, needle_frac=0.005), fsl.Params(), {}),
-], ids=["d128", "d64-K3-gain", "FS", "K8-lam0", "one-block", "lam0.02", "needles-4k"])
+    # content only, and every query feature at index 0 or 1 mod 8 is zero: the tile bound's
+    # |q| must come from all features (a norm from one element pair per 16-byte run is
+    # 0 here, and then every tile after the first would be passed over)
+    (synth.Workload(batch=1, H=2, N=3000, d=128, dtype="bf16", seed=79), fsl.Params(), {"lam": 0.0, "q_gaps": True}),
+], ids=["d128", "d64-K3-gain", "FS", "K8-lam0", "one-block", "lam0.02", "needles-4k", "lam0-qgaps"])
 def test_fused_route_readout(w, p, extra):
     """fs_select_readout in its single-kernel form gives bitwise the selections and
     outputs of fs_score_select followed by fs_readout, with and without the tile bound
     (kbar_norm) and without the selections output; both meet the oracle."""
     host = pu.inputs(w)
+    if extra.get("q_gaps"):
+        f = np.arange(w.d) % 8
+        host["q"] = host["q"].copy()
+        host["q"][..., (f == 0) | (f == 1)] = 0
     q, k, v = (pu.to_device(host[x], w.dtype) for x in "qkv")
     gain_h = synth.gains(97, w.H, w.d) if extra.get("gain") else None
     gain = torch.from_numpy(gain_h).cuda() if gain_h is not None else None
