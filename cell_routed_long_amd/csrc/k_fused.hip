@@ -56,8 +56,14 @@ struct alignas(16) FusedSmem {
     int32_t id[32];
 };
 
+// Three workgroups per CU (168 VGPRs) hide more of each block's memory latency; at
+// d = 128 the compiler then spills a few lane constants, and more of them for K > 4,
+// where two workgroups per CU are kept.
 template <int D, int KT>
-__global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
+constexpr int kFusedBlocksPerCU = (D <= 64 || KT <= 4) ? 3 : 2;
+
+template <int D, int KT>
+__global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_readout_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ kbar_split, const float *__restrict__ kbar_norm, const float *__restrict__ a,
     const int32_t *__restrict__ retained,
@@ -217,6 +223,10 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
 #pragma unroll
             for (int u = 0; u < SCH; ++u)
                 *reinterpret_cast<u32x4 *>(&sm.kb[part][srow][spart * PER + u * 8]) = pre3[part * SCH + u];
+        if (bound && t0 == 0 && t < nA) { // loaded before the tile, so here already; read after a later barrier
+            s_bpr[t] = lam * b_pr;
+            s_bkn[t] = b_kn;
+        }
         __syncthreads();
         if (t0 + 32 < nA && !(bound && t0 > 0 && tile_below(t0 + 32)))
             prefetch(t0 + 32); // overlaps the matrix work below
@@ -262,10 +272,6 @@ __global__ __launch_bounds__(kThreads, 2) void route_readout_kernel(
             const float qm = wave_max_f(qn);
             if (lane == 0)
                 s_qn[wave] = badq ? INFINITY : qm;
-            if (t < nA) { // read after the next barrier, like s_qn
-                s_bpr[t] = lam * b_pr;
-                s_bkn[t] = b_kn;
-            }
         }
         // erf only below 4 (above it rounds to 1 in fp32); see the scorer
         // this lane's 16 rows come in 4 runs of 4 consecutive rows: 12 vector LDS reads
