@@ -265,7 +265,7 @@ namespace fsl {
 // (-1 = free), whether the cell is in TopP, and its position in the retained
 // set A listed in ascending cell-id order (-1 = not in A).
 constexpr uint32_t kStateMagic = 0x31534C46u; // "FLS1"
-constexpr uint32_t kStateVersion = 1;
+constexpr uint32_t kStateVersion = 2;
 constexpr int64_t kStateHeaderBytes = 256;
 constexpr int32_t kFlagTop = 1; // the slot's cell belongs to TopP of the current prefix
 constexpr int kMaxSlots = 128;  // P + W + B/s supported by the decode kernels
@@ -276,10 +276,14 @@ struct StateHeader {
     int64_t rec_bytes;
 };
 
+constexpr int kStateHints = 4; // one per wave of the decode step kernel
+
 struct StateMeta {
-    int64_t pos;      // next position to be processed
-    int32_t n_ret;    // |A| of the current block
-    int32_t cur_slot; // slot of the cell receiving tokens, -1 if none yet
+    int64_t pos;               // next position to be processed
+    int32_t n_ret;             // |A| of the current block
+    int32_t cur_slot;          // slot of the cell receiving tokens, -1 if none yet
+    int32_t hint[kStateHints]; // per wave of the step kernel: the slot it read first at the previous step
+                               // (-1: none); only a prefetch hint, results never depend on it
 };
 
 struct StateLayout {

@@ -221,6 +221,8 @@ __global__ __launch_bounds__(kThreads) void state_build_kernel(char *__restrict_
         R.meta->n_ret = n_A;
         R.meta->cur_slot = (N % kS) != 0 ? n_A + n_pend - 1 : -1;
     }
+    if (t < kStateHints)
+        R.meta->hint[t] = -1;
     for (int e = t; e < L.S * D; e += kThreads) {
         const int x = e / D, f = e % D;
         const int32_t c = s_cell[x];
@@ -248,13 +250,21 @@ __global__ __launch_bounds__(kThreads) void state_build_kernel(char *__restrict_
 }
 
 // ------------------------------------------------------------------------
-// One decode step.  Latency, not bandwidth, bounds a step (one workgroup per
-// (sequence, head) moves ~100 KB), so the kernel is laid out as two memory
-// round trips with no dependent loads in between: (a) the header, position,
-// slot tables, token and every slot's mean key, all issued at entry (while
-// scoring, thread t owns half t & 1 of slot t >> 1); (b) the selected cells'
-// keys and values.  Ranks (Eq. 15 merge, top-K) are counted by every thread
-// at once over 64-bit integer keys in LDS; reductions run on the DPP network.
+// One decode step.  Latency, not bandwidth, bounds a step: one workgroup per
+// (sequence, head) moves ~100 KB through a chain of dependent phases.  So every
+// load the step can know of at entry is issued at once, with no branch between
+// the loads and their first use (a divergent branch makes the compiler wait for
+// a load inside it): the slot tables, the token, every slot's mean key, the gain
+// and the keys and values of the cell this wave read at the previous step.  The
+// record keeps that slot per wave as a hint.  Queries of one head keep choosing
+// the same high-norm cells, so the hint is usually right and the gather needs no
+// second round trip.  The prefetched rows are used only if the hinted slot is
+// selected again, and the rows of a selected cell never change (only the cell
+// being filled is written, and it is not in A), so no result depends on the hint.
+// Ranks (Eq. 15 merge, top-K) are counted over 64-bit integer keys in LDS; the
+// top-K is taken per wave first and then over the waves' candidates.  Each
+// selected cell's softmax partials are kept apart by rank and combined in rank
+// order, so outputs are bitwise the same whichever wave read which cell.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict__ state, StateLayout L,
                                                                StateHeader expect, HeadConsts hc,
@@ -268,26 +278,34 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     constexpr int EPC = 16 / (int)sizeof(T); // elements per 16-byte chunk
     constexpr int CPR = D / EPC;             // chunks per row
     constexpr int RG = kWave / CPR;          // value rows per load step
-    constexpr int VR = kS / RG;              // value loads per lane
+    constexpr int VR = kS / RG;              // value chunks per lane
     constexpr int HALF = D / 2;              // key features per lane (two lanes per token)
+    constexpr int KC = HALF / EPC;           // key chunks per lane
     constexpr int FPT = D / 2;               // mean-key features per thread while scoring
+    constexpr int NCAND = kWaves * kKmax;    // the waves' top-K candidates
+    constexpr int SPW = kWave / 2;           // slots scored per wave (two threads per slot)
+    // a cell is prefetched when a lane's share of it fits in 64 registers
+    constexpr bool kPrefetch = KC + VR <= 16;
+    static_assert(kWaves == kStateHints, "one prefetch hint per wave");
+    static_assert(SPW * kWaves == kMaxSlots, "every slot has two scoring threads");
+    static_assert(kThreads % kMaxSlots == 0 && kThreads % D == 0, "threads cover the slots and features evenly");
 
     __shared__ int32_t s_cell[kMaxSlots], s_flags[kMaxSlots], s_ridx[kMaxSlots];
     __shared__ __attribute__((aligned(16))) int32_t s_kc[kMaxSlots]; // kept cell ids (merge), read 4 at a time
     __shared__ float s_a[kMaxSlots];
-    __shared__ __attribute__((aligned(16))) uint64_t s_key[kMaxSlots]; // ranking keys (merge, then top-K)
-    __shared__ int32_t s_rc[kMaxSlots];   // cell ids, by position in A
-    __shared__ int32_t s_rslot[kMaxSlots];
+    __shared__ __attribute__((aligned(16))) uint64_t s_key[kMaxSlots]; // merge keys, then score keys, by slot
+    __shared__ __attribute__((aligned(16))) uint64_t s_cand[NCAND];   // per wave: its K best score keys
+    __shared__ int32_t s_pos_slot[kMaxSlots];                         // slot of each position in A
+    __shared__ int32_t s_selw[kWaves][kKmax];                         // per wave: the selected slots by rank
     __shared__ float s_q[D];
+    __shared__ double s_qd[D];
     __shared__ T s_knew[D];
     __shared__ T s_vnew[D];
-    __shared__ int32_t s_sel_slot[kKmax], s_sel_cell[kKmax];
-    __shared__ float s_upart[kWaves][RG * D]; // per wave and value-row group: partial P.V
-    __shared__ float s_m[kWaves], s_z[kWaves];
+    __shared__ float s_upart[kKmax][RG * D]; // per selected cell (by rank) and value-row group: partial P.V
+    __shared__ float s_m[kKmax], s_z[kKmax];
     __shared__ double s_colsum[kWaves][D];
     __shared__ double s_rowmax[kWaves];
     __shared__ float s_red[kWaves];
-    __shared__ int32_t s_int[2];
 
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
@@ -297,31 +315,49 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     const Record R = record_at(state, L, bh); // in bounds: the host checked the buffer size
     T *sk = reinterpret_cast<T *>(R.k);
     T *sv = reinterpret_cast<T *>(R.v);
+    const int vrow0 = lane / CPR, vch = lane % CPR;
 
-    // ---- (a) entry loads: header, position, slot tables, token, mean keys ----
+    // ---- (a) entry: all loads first (clamped indices, no branches), then their uses ----
+    // Threads t and t + 128 (t + D) load and store the same slot (feature), so the
+    // LDS stores need no branch for the compiler to sink the loads into.
+    const int td = t & (D - 1);
+    const float g_in = gain ? gain[(int64_t)h * D + td] : 1.0f; // first: its branch must precede the others
     const StateHeader hv = *reinterpret_cast<const StateHeader *>(state);
     const StateMeta mv = *R.meta;
-    if (t < kMaxSlots) {
-        const bool in = t < L.S;
-        s_cell[t] = in ? R.cell[t] : -1;
-        s_flags[t] = in ? R.flags[t] : 0;
-        s_a[t] = in ? R.a[t] : 0.0f;
-        s_ridx[t] = in ? R.ridx[t] : -1;
-    }
-    if (t < D) {
-        s_q[t] = elem_to_f32<T>(q[bh * D + t]);
-        s_knew[t] = k_new[bh * D + t];
-        s_vnew[t] = v_new[bh * D + t];
-    }
+    const int tt = t & (kMaxSlots - 1);
+    const bool t_in = tt < L.S;
+    const int ts = t_in ? tt : 0; // L.S >= 1
+    const int32_t cell_in = R.cell[ts], flags_in = R.flags[ts], ridx_in = R.ridx[ts];
+    const float a_in = R.a[ts];
+    const T q_in = q[bh * D + td], k_in = k_new[bh * D + td], v_in = v_new[bh * D + td];
+    // Every wave's small loads go out before any wave's bulk loads: the whole
+    // step's traffic is requested at once and would otherwise queue ahead of them.
+    asm volatile("" ::: "memory"); // keeps the small loads above the barrier
+    __builtin_amdgcn_s_barrier();
     const int my_slot = t >> 1, my_part = t & 1;
-    float kb[FPT];
-    if (my_slot < L.S) {
-        load_row_f32<float, FPT>(R.kbar + (int64_t)my_slot * D + my_part * FPT, kb);
-    } else {
+    const int ks = my_slot < L.S ? my_slot : 0;
+    u32x4 kbraw[FPT / 4];
 #pragma unroll
-        for (int e = 0; e < FPT; ++e)
-            kb[e] = 0.0f;
+    for (int c = 0; c < FPT / 4; ++c)
+        kbraw[c] = *reinterpret_cast<const u32x4 *>(R.kbar + (int64_t)ks * D + my_part * FPT + 4 * c);
+    int my_hint = mv.hint[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        my_hint = wave == w ? mv.hint[w] : my_hint;
+    my_hint = kPrefetch && my_hint >= 0 && my_hint < L.S ? my_hint : -1;
+    u32x4 kraw[KC], vraw[VR];
+    if constexpr (kPrefetch) { // slot 0 stands in for a missing hint: the read is wasted, never used
+        const int ps = my_hint >= 0 ? my_hint : 0;
+        const T *kc = sk + (int64_t)ps * kS * D + (int64_t)(lane >> 1) * D + (lane & 1) * HALF;
+        const T *vc = sv + (int64_t)ps * kS * D + (int64_t)vrow0 * D + vch * EPC;
+#pragma unroll
+        for (int x = 0; x < KC; ++x)
+            kraw[x] = *reinterpret_cast<const u32x4 *>(kc + x * EPC);
+#pragma unroll
+        for (int x = 0; x < VR; ++x)
+            vraw[x] = *reinterpret_cast<const u32x4 *>(vc + (int64_t)RG * x * D);
     }
+
     const int bad = (int)(hv.magic != kStateMagic) | (int)(hv.version != kStateVersion) |
                     (int)(hv.batch != expect.batch) | (int)(hv.H != expect.H) | (int)(hv.d != D) |
                     (int)(hv.dtype != expect.dtype) | (int)(hv.P != P) | (int)(hv.W != W) |
@@ -336,6 +372,22 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
         if (sel && t < K)
             sel[bh * K + t] = -1;
         return;
+    }
+    s_cell[tt] = t_in ? cell_in : -1;
+    s_flags[tt] = t_in ? flags_in : 0;
+    s_a[tt] = t_in ? a_in : 0.0f;
+    s_ridx[tt] = t_in ? ridx_in : -1;
+    s_pos_slot[tt] = 0;
+    if (t < NCAND) {
+        s_cand[t] = 0;                 // empty candidates rank last
+        s_selw[t / kKmax][t % kKmax] = 0; // slot 0 for any rank a corrupted state leaves unlisted
+    }
+    {
+        const float qf = elem_to_f32<T>(q_in);
+        s_q[td] = qf;
+        s_qd[td] = (double)qf;
+        s_knew[td] = k_in;
+        s_vnew[td] = v_in;
     }
     const int64_t i = mv.pos;
     int n_ret = mv.n_ret < 0 ? 0 : (mv.n_ret > L.S ? L.S : mv.n_ret);
@@ -456,80 +508,98 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
             R.a[cur] = (float)sqrt(fmax(fmax(s_rowmax[0], s_rowmax[1]), fmax(s_rowmax[2], s_rowmax[3])));
     }
 
-    // ---- (3) Eq. 7 over A in fp64 ----
-    const int ri = my_slot < L.S ? s_ridx[my_slot] : -1;
+    // ---- (3) Eq. 7 over A in fp64; each wave keeps the K best of its slots ----
+    const int ri = s_ridx[my_slot]; // my_slot < kMaxSlots; -1 past L.S
     const bool scored = ri >= 0 && ri < n_ret;
-    double dot = 0.0;
-    if (scored) {
-        double part4[4] = {0.0, 0.0, 0.0, 0.0};
+    double part4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int e = 0; e < FPT; ++e)
-            part4[e & 3] = fma((double)s_q[my_part * FPT + e], (double)kb[e], part4[e & 3]);
-        dot = (part4[0] + part4[1]) + (part4[2] + part4[3]);
+    for (int c = 0; c < FPT / 4; ++c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            part4[e] = fma(s_qd[my_part * FPT + 4 * c + e], (double)__uint_as_float(kbraw[c][e]), part4[e]);
     }
+    double dot = (part4[0] + part4[1]) + (part4[2] + part4[3]);
     dot += shfl_xor_d(dot, 1);
+    uint64_t key = 0;
     if (scored && my_part == 0) {
         const int32_t c = s_cell[my_slot];
         const double delta = (double)i - ((double)c + 0.5) * kS;
         // erf rounds to exactly 1 in fp64 from 6 on (erfc(6) < 2^-54): skip the series there
         const double x = delta / (2.0 * (double)hc.sigma[h]);
         const double g = x >= 6.0 ? 1.0 : erf(x);
-        s_key[ri] = score_key(dot / sqrt((double)D) + (double)hc.lambda[h] * (double)s_a[my_slot] * g, ri);
-        s_rc[ri] = c;
-        s_rslot[ri] = my_slot;
+        key = score_key(dot / sqrt((double)D) + (double)hc.lambda[h] * (double)s_a[my_slot] * g, ri);
+        s_pos_slot[ri] = my_slot;
     }
-    const int n8 = (n_ret + 7) & ~7;
-    if (t >= n_ret && t < n8)
-        s_key[t] = 0; // padding ranks last
-    if (t < kKmax) { // every rank below min(K, |A|) is written below; slot 0 keeps reads in bounds regardless
-        s_sel_slot[t] = 0;
-        s_sel_cell[t] = -1;
+    if (my_part == 0)
+        s_key[my_slot] = key;
+    // the wave reads back only what its own lanes wrote: a wave-level barrier orders it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (key != 0) {
+        const int rk = count_greater(s_key + wave * SPW, SPW, key);
+        if (rk < K)
+            s_cand[wave * kKmax + rk] = key;
     }
     __syncthreads();
 
-    // ---- top-K by rank (score desc, id asc) ----
-    if (t < n_ret) {
-        const int rank = count_greater(s_key, n8, s_key[t]);
-        if (rank < K) {
-            const int slot = s_rslot[t];
-            s_sel_slot[rank] = slot >= 0 && slot < L.S ? slot : 0;
-            s_sel_cell[rank] = s_rc[t];
+    // ---- top-K over the candidates (score desc, id asc), taken by every wave ----
+    // Each wave lists the selected slots by rank in its own LDS row, then reads it back.
+    {
+        const uint64_t ck = lane < NCAND ? s_cand[lane] : 0;
+        const int grank = ck != 0 ? count_greater(s_cand, NCAND, ck) : NCAND;
+        if (grank < K) {
+            const int sl = s_pos_slot[127 - (int)((uint32_t)ck & 0x7fu)];
+            s_selw[wave][grank] = sl >= 0 && sl < L.S ? sl : 0;
         }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int nT = n_ret < K ? n_ret : K;
-    __syncthreads();
+    // wave w reads out ranks w and w + 4; the slot at rank w is its next hint
+    const int rk0 = wave, rk1 = wave + kWaves;
+    const int slot0 = __builtin_amdgcn_readfirstlane(rk0 < nT ? s_selw[wave][rk0] : -1);
+    const int slot1 = __builtin_amdgcn_readfirstlane(rk1 < nT ? s_selw[wave][rk1] : -1);
 
-    // ---- (b) readout: wave w gathers selections w, w + 4 with a running softmax ----
+    // ---- (b) readout (Eq. 9): one cell per pass, its softmax partials stored by rank ----
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const int vrow0 = lane / CPR, vch = lane % CPR;
-    float m_w = -INFINITY, z_w = 0.0f;
-    float acc[EPC];
+    auto read_cell = [&](int rk, int slot, bool have) {
+        if (!have) {
+            const T *kc = sk + (int64_t)slot * kS * D + (int64_t)(lane >> 1) * D + (lane & 1) * HALF;
+            const T *vc = sv + (int64_t)slot * kS * D + (int64_t)vrow0 * D + vch * EPC;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e)
-        acc[e] = 0.0f;
-    for (int j = wave; j < nT; j += kWaves) {
-        const int slot = s_sel_slot[j];
-        const T *kc = sk + (int64_t)slot * kS * D;
-        const T *vc = sv + (int64_t)slot * kS * D;
-        u32x4 vraw[VR];
+            for (int x = 0; x < KC; ++x)
+                kraw[x] = *reinterpret_cast<const u32x4 *>(kc + x * EPC);
 #pragma unroll
-        for (int x = 0; x < VR; ++x)
-            vraw[x] = *reinterpret_cast<const u32x4 *>(vc + (int64_t)(vrow0 + RG * x) * D + vch * EPC);
-        float kr[HALF];
-        load_row_f32<T, HALF>(kc + (int64_t)(lane >> 1) * D + (lane & 1) * HALF, kr);
+            for (int x = 0; x < VR; ++x)
+                vraw[x] = *reinterpret_cast<const u32x4 *>(vc + (int64_t)RG * x * D);
+        }
         float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int e = 0; e < HALF; ++e)
-            lp[e & 3] = fmaf(s_q[(lane & 1) * HALF + e], kr[e], lp[e & 3]);
+        for (int x = 0; x < KC; ++x) {
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int f = (lane & 1) * HALF + x * EPC + 2 * e;
+                    lp[e] = fmaf(s_q[f], bf16_bits_to_f32(kraw[x][e] & 0xffffu), lp[e]);
+                    lp[e] = fmaf(s_q[f + 1], bf16_bits_to_f32(kraw[x][e] >> 16), lp[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    lp[e] = fmaf(s_q[(lane & 1) * HALF + x * EPC + e], __uint_as_float(kraw[x][e]), lp[e]);
+            }
+        }
         float l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
         l = (l + dpp_f<0xB1>(l)) * inv_sqrt_d; // logit of token lane / 2, on both lanes of the pair
-        const float m_new = fmaxf(m_w, wave_max_f(l));
-        const float scale = expf(m_w - m_new); // 0 on the wave's first cell
-        const float p = expf(l - m_new);
-        z_w = z_w * scale + wave_sum_f((lane & 1) ? 0.0f : p);
+        const float mx = wave_max_f(l);
+        const float p = expf(l - mx);
+        const float z = wave_sum_f((lane & 1) ? 0.0f : p);
+        float acc[EPC];
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
-            acc[e] *= scale;
+            acc[e] = 0.0f;
 #pragma unroll
         for (int x = 0; x < VR; ++x) {
             const float pr = __shfl(p, 2 * (vrow0 + RG * x), kWave);
@@ -545,34 +615,41 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
                     acc[e] = fmaf(pr, __uint_as_float(vraw[x][e]), acc[e]);
             }
         }
-        m_w = m_new;
-    }
 #pragma unroll
-    for (int e = 0; e < EPC; ++e)
-        s_upart[wave][vrow0 * D + vch * EPC + e] = acc[e];
-    if (lane == 0) {
-        s_m[wave] = m_w;
-        s_z[wave] = z_w;
-    }
+        for (int e = 0; e < EPC; ++e)
+            s_upart[rk][vrow0 * D + vch * EPC + e] = acc[e];
+        if (lane == 0) {
+            s_m[rk] = mx;
+            s_z[rk] = z;
+        }
+    };
+    if (slot0 >= 0)
+        read_cell(rk0, slot0, slot0 == my_hint);
+    if (slot1 >= 0)
+        read_cell(rk1, slot1, false);
+    if (kPrefetch && lane == 0)
+        R.meta->hint[wave] = slot0;
     __syncthreads();
 
-    // ---- combine the waves and row groups, normalise, RMSNorm over d (Eq. 17), write ----
+    // ---- combine the cells in rank order, normalise, RMSNorm over d (Eq. 17), write ----
     float u = 0.0f;
     if (t < D && nT > 0) {
         float M = s_m[0];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-            M = fmaxf(M, s_m[w]);
+        for (int q8 = 1; q8 < kKmax; ++q8)
+            M = q8 < nT ? fmaxf(M, s_m[q8]) : M;
         float Z = 0.0f, U = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = s_m[w] == -INFINITY ? 0.0f : expf(s_m[w] - M);
-            float uw = 0.0f;
+        for (int q8 = 0; q8 < kKmax; ++q8) {
+            if (q8 < nT) {
+                const float f = expf(s_m[q8] - M);
+                float uw = 0.0f;
 #pragma unroll
-            for (int g = 0; g < RG; ++g)
-                uw += s_upart[w][g * D + t];
-            Z = fmaf(s_z[w], f, Z);
-            U = fmaf(uw, f, U);
+                for (int g = 0; g < RG; ++g)
+                    uw += s_upart[q8][g * D + t];
+                Z = fmaf(s_z[q8], f, Z);
+                U = fmaf(uw, f, U);
+            }
         }
         u = U / Z;
     }
@@ -586,15 +663,14 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
         ms += s_red[w];
     const float rs = 1.0f / sqrtf(ms / (float)D + eps);
     if (t < D) {
-        const float gv = gain ? gain[(int64_t)h * D + t] : 1.0f;
-        const float y = nT > 0 ? gv * u * rs : 0.0f;
+        const float y = nT > 0 ? g_in * u * rs : 0.0f;
         if constexpr (sizeof(T) == 2)
             o_row[t] = (T)f32_to_bf16_bits(y);
         else
             o_row[t] = y;
     }
-    if (sel && t < K)
-        sel[bh * K + t] = t < nT ? s_sel_cell[t] : -1;
+    if (sel && t < K) // wave 0 reads its own list
+        sel[bh * K + t] = t < nT ? s_cell[s_selw[0][t]] : -1;
     if (t == 0)
         R.meta->pos = i + 1;
 }
@@ -651,3 +727,4 @@ hipError_t launch_decode_step(int32_t bh, int32_t H, int32_t d, int32_t bf16, in
 }
 
 } // namespace fsl
+

@@ -207,7 +207,8 @@ fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params *prm,
  * block (at most P + W cells, Eq. 8) plus the cells of the block being filled.
  * Each slot keeps the cell's raw keys and values (dtype), its fp32 mean key and
  * norm (Eq. 5), its absolute cell id and whether it is in TopP; the record also
- * keeps the next position and the retained slots in ascending cell-id order.
+ * keeps the next position, the retained slots in ascending cell-id order and,
+ * as a prefetch hint only, the slots the last step read.
  * Memory per (sequence, head) is therefore constant in the context length.
  * Copying the buffer's bytes checkpoints the stream exactly.
  * Supported: FS-L (prune = 1) with P + W + B/s <= 128 slots.
