@@ -14,11 +14,11 @@
 //       slot is taken when a cell starts); when the token completes the cell,
 //       its mean key and largest key norm (Eq. 5) are formed in fp64 and
 //       rounded once, exactly as the prefill summary kernel does;
-//   (3) q is scored against A in fp64 (Eq. 7), its top-K cells are chosen by
-//       rank (score desc, id asc), and the readout (Eq. 9) with RMSNorm
-//       (Eq. 17) runs over their tokens: each wave gathers one selected cell
-//       and keeps a running softmax (max, sum, weighted values) that the waves
-//       combine at the end, so the readout needs a single barrier.
+//   (3) q is scored against A (Eq. 7, in fp32 with the prefill's arithmetic),
+//       its top-K cells are chosen by rank (score desc, id asc), and the
+//       readout (Eq. 9) with RMSNorm (Eq. 17) runs over their tokens: each
+//       wave gathers one selected cell, keeps its softmax partials (max, sum,
+//       weighted values) apart, and the cells are combined in rank order.
 // All branching on the position happens on the device, so a step can be
 // captured in a HIP graph.  The prefill builds the state directly from its
 // exit blocks (state_build_kernel), so no merge chain is replayed.
@@ -69,21 +69,13 @@ __device__ __forceinline__ void load_row_f32(const T *__restrict__ p, float (&x)
 // Order-preserving integer images of the two rankings (a larger key ranks first):
 //   TopP by (norm desc, id asc): the fp32 norm's bits (made monotone) above the
 //   complemented id -- exact;
-//   top-K by (score desc, id asc): the fp64 score's bits made monotone, with the
-//   lowest 7 bits replaced by 127 - (position in A).  Positions in A follow cell
-//   ids, so scores within 2^-45 (relative) of each other count as tied and go to
-//   the smaller id; the numerical error of any score is far larger than that.
+//   top-K by (score desc, id asc): rank_key of the fp32 score above
+//   127 - (position in A) -- exact, since positions in A follow cell ids.
 __device__ __forceinline__ uint64_t norm_key(float a, int32_t cell)
 {
     uint32_t u = __float_as_uint(a);
     u = (u >> 31) ? ~u : (u | 0x80000000u);
     return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - cell);
-}
-__device__ __forceinline__ uint64_t score_key(double sc, int pos)
-{
-    uint64_t u = (uint64_t)__double_as_longlong(sc);
-    u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-    return (u & ~(uint64_t)0x7f) | (uint64_t)(127 - pos);
 }
 
 // Number of keys in k[0 .. n8) (n8 a multiple of 8, entries past the live ones
@@ -298,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     __shared__ int32_t s_pos_slot[kMaxSlots];                         // slot of each position in A
     __shared__ int32_t s_selw[kWaves][kKmax];                         // per wave: the selected slots by rank
     __shared__ float s_q[D];
-    __shared__ double s_qd[D];
+    __shared__ __attribute__((aligned(16))) T s_qt[D]; // q as given (bf16 pairs feed dot2)
     __shared__ T s_knew[D];
     __shared__ T s_vnew[D];
     __shared__ float s_upart[kKmax][RG * D]; // per selected cell (by rank) and value-row group: partial P.V
@@ -336,6 +328,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     __builtin_amdgcn_s_barrier();
     const int my_slot = t >> 1, my_part = t & 1;
     const int ks = my_slot < L.S ? my_slot : 0;
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
     u32x4 kbraw[FPT / 4];
 #pragma unroll
     for (int c = 0; c < FPT / 4; ++c)
@@ -385,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     {
         const float qf = elem_to_f32<T>(q_in);
         s_q[td] = qf;
-        s_qd[td] = (double)qf;
+        s_qt[td] = q_in;
         s_knew[td] = k_in;
         s_vnew[td] = v_in;
     }
@@ -508,26 +501,26 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
             R.a[cur] = (float)sqrt(fmax(fmax(s_rowmax[0], s_rowmax[1]), fmax(s_rowmax[2], s_rowmax[3])));
     }
 
-    // ---- (3) Eq. 7 over A in fp64; each wave keeps the K best of its slots ----
+    // ---- (3) Eq. 7 over A, in fp32 as the prefill scores; each wave keeps the K best of its slots ----
     const int ri = s_ridx[my_slot]; // my_slot < kMaxSlots; -1 past L.S
     const bool scored = ri >= 0 && ri < n_ret;
-    double part4[4] = {0.0, 0.0, 0.0, 0.0};
+    float part4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < FPT / 4; ++c) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            part4[e] = fma(s_qd[my_part * FPT + 4 * c + e], (double)__uint_as_float(kbraw[c][e]), part4[e]);
+            part4[e] = fmaf(s_q[my_part * FPT + 4 * c + e], __uint_as_float(kbraw[c][e]), part4[e]);
     }
-    double dot = (part4[0] + part4[1]) + (part4[2] + part4[3]);
-    dot += shfl_xor_d(dot, 1);
+    float dot = (part4[0] + part4[1]) + (part4[2] + part4[3]);
+    dot += dpp_f<0xB1>(dot); // the slot's other half (lanes 2j, 2j + 1)
     uint64_t key = 0;
     if (scored && my_part == 0) {
         const int32_t c = s_cell[my_slot];
-        const double delta = (double)i - ((double)c + 0.5) * kS;
-        // erf rounds to exactly 1 in fp64 from 6 on (erfc(6) < 2^-54): skip the series there
-        const double x = delta / (2.0 * (double)hc.sigma[h]);
-        const double g = x >= 6.0 ? 1.0 : erf(x);
-        key = score_key(dot / sqrt((double)D) + (double)hc.lambda[h] * (double)s_a[my_slot] * g, ri);
+        // (i - p_c) / (2 sigma_h) with i - p_c exact below 2^24; erf rounds to 1 in fp32 from 4 on
+        const float x = (float)(i - ((int64_t)c * kS + kS / 2)) * hc.inv_two_sigma[h];
+        const float g = x < 4.0f ? erff(x) : 1.0f;
+        const float score = fmaf(hc.lambda[h] * s_a[my_slot], g, dot * inv_sqrt_d);
+        key = rank_key(score, 127u - (uint32_t)ri); // ties: the smaller position in A (the smaller id) first
         s_pos_slot[ri] = my_slot;
     }
     if (my_part == 0)
@@ -561,9 +554,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     const int rk0 = wave, rk1 = wave + kWaves;
     const int slot0 = __builtin_amdgcn_readfirstlane(rk0 < nT ? s_selw[wave][rk0] : -1);
     const int slot1 = __builtin_amdgcn_readfirstlane(rk1 < nT ? s_selw[wave][rk1] : -1);
+    const int32_t sel_cell = t < nT ? s_cell[s_selw[0][t < kKmax ? t : 0]] : -1; // for lanes t < K of wave 0
 
     // ---- (b) readout (Eq. 9): one cell per pass, its softmax partials stored by rank ----
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
     auto read_cell = [&](int rk, int slot, bool have) {
         if (!have) {
             const T *kc = sk + (int64_t)slot * kS * D + (int64_t)(lane >> 1) * D + (lane & 1) * HALF;
@@ -579,11 +572,12 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
 #pragma unroll
         for (int x = 0; x < KC; ++x) {
             if constexpr (sizeof(T) == 2) {
+                const u32x4 qw = *reinterpret_cast<const u32x4 *>(&s_qt[(lane & 1) * HALF + x * EPC]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int f = (lane & 1) * HALF + x * EPC + 2 * e;
-                    lp[e] = fmaf(s_q[f], bf16_bits_to_f32(kraw[x][e] & 0xffffu), lp[e]);
-                    lp[e] = fmaf(s_q[f + 1], bf16_bits_to_f32(kraw[x][e] >> 16), lp[e]);
+                    const uint32_t qe = qw[e], ke = kraw[x][e]; // named copies: a bit_cast of an element in place reads element 0
+                    lp[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qe),
+                                                            __builtin_bit_cast(bf16x2, ke), lp[e], false);
                 }
             } else {
 #pragma unroll
@@ -669,8 +663,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
         else
             o_row[t] = y;
     }
-    if (sel && t < K) // wave 0 reads its own list
-        sel[bh * K + t] = t < nT ? s_cell[s_selw[0][t]] : -1;
+    if (sel && t < K)
+        sel[bh * K + t] = sel_cell;
     if (t == 0)
         R.meta->pos = i + 1;
 }

@@ -228,7 +228,7 @@ size_t fs_decode_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype
  *       slots whose cell is in neither are freed;
  *   (2) k_new, v_new are appended; when position i completes a cell its
  *       summary (Eq. 5) is formed (fp64 sums, rounded once to fp32);
- *   (3) q is scored against A (Eq. 7, evaluated in fp64), its min(K, |A|) best
+ *   (3) q is scored against A (Eq. 7, in fp32 as the prefill), its min(K, |A|) best
  *       cells are selected and read out (Eq. 9) with RMSNorm (Eq. 17); the
  *       position advances to i + 1.
  * The output equals the prefill's at position i (same causal operator).
