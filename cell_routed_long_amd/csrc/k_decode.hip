@@ -297,7 +297,6 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     __shared__ float s_m[kKmax], s_z[kKmax];
     __shared__ double s_colsum[kWaves][D];
     __shared__ double s_rowmax[kWaves];
-    __shared__ float s_red[kWaves];
 
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
@@ -312,8 +311,12 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     // ---- (a) entry: all loads first (clamped indices, no branches), then their uses ----
     // Threads t and t + 128 (t + D) load and store the same slot (feature), so the
     // LDS stores need no branch for the compiler to sink the loads into.
+    constexpr int FPL = D / kWave; // output features per lane of wave 0
     const int td = t & (D - 1);
-    const float g_in = gain ? gain[(int64_t)h * D + td] : 1.0f; // first: its branch must precede the others
+    float g_in[FPL]; // gain of the output features of lane (t % 64); first: its branch must precede the others
+#pragma unroll
+    for (int j = 0; j < FPL; ++j)
+        g_in[j] = gain ? gain[(int64_t)h * D + FPL * lane + j] : 1.0f;
     const StateHeader hv = *reinterpret_cast<const StateHeader *>(state);
     const StateMeta mv = *R.meta;
     const int tt = t & (kMaxSlots - 1);
@@ -625,43 +628,53 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
         R.meta->hint[wave] = slot0;
     __syncthreads();
 
-    // ---- combine the cells in rank order, normalise, RMSNorm over d (Eq. 17), write ----
-    float u = 0.0f;
-    if (t < D && nT > 0) {
+    // ---- wave 0: combine the cells in rank order, normalise, RMSNorm over d (Eq. 17), write ----
+    if (wave != 0)
+        return;
+    float u[FPL];
+#pragma unroll
+    for (int j = 0; j < FPL; ++j)
+        u[j] = 0.0f;
+    if (nT > 0) {
         float M = s_m[0];
 #pragma unroll
         for (int q8 = 1; q8 < kKmax; ++q8)
             M = q8 < nT ? fmaxf(M, s_m[q8]) : M;
-        float Z = 0.0f, U = 0.0f;
+        float Z = 0.0f, U[FPL];
+#pragma unroll
+        for (int j = 0; j < FPL; ++j)
+            U[j] = 0.0f;
 #pragma unroll
         for (int q8 = 0; q8 < kKmax; ++q8) {
             if (q8 < nT) {
                 const float f = expf(s_m[q8] - M);
-                float uw = 0.0f;
-#pragma unroll
-                for (int g = 0; g < RG; ++g)
-                    uw += s_upart[q8][g * D + t];
                 Z = fmaf(s_z[q8], f, Z);
-                U = fmaf(uw, f, U);
+#pragma unroll
+                for (int j = 0; j < FPL; ++j) {
+                    float uw = 0.0f;
+#pragma unroll
+                    for (int g = 0; g < RG; ++g)
+                        uw += s_upart[q8][g * D + FPL * lane + j];
+                    U[j] = fmaf(uw, f, U[j]);
+                }
             }
         }
-        u = U / Z;
-    }
-    const float sq = wave_sum_f(t < D ? u * u : 0.0f);
-    if (lane == 0)
-        s_red[wave] = sq;
-    __syncthreads();
-    float ms = 0.0f;
 #pragma unroll
-    for (int w = 0; w < (D + kWave - 1) / kWave; ++w)
-        ms += s_red[w];
-    const float rs = 1.0f / sqrtf(ms / (float)D + eps);
-    if (t < D) {
-        const float y = nT > 0 ? g_in * u * rs : 0.0f;
+        for (int j = 0; j < FPL; ++j)
+            u[j] = U[j] / Z;
+    }
+    float sq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < FPL; ++j)
+        sq = fmaf(u[j], u[j], sq);
+    const float rs = 1.0f / sqrtf(wave_sum_f(sq) / (float)D + eps);
+#pragma unroll
+    for (int j = 0; j < FPL; ++j) {
+        const float y = nT > 0 ? g_in[j] * u[j] * rs : 0.0f;
         if constexpr (sizeof(T) == 2)
-            o_row[t] = (T)f32_to_bf16_bits(y);
+            o_row[FPL * lane + j] = (T)f32_to_bf16_bits(y);
         else
-            o_row[t] = y;
+            o_row[FPL * lane + j] = y;
     }
     if (sel && t < K)
         sel[bh * K + t] = sel_cell;
