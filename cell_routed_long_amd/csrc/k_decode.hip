@@ -243,19 +243,21 @@ __global__ __launch_bounds__(kThreads) void state_build_kernel(char *__restrict_
 
 // ------------------------------------------------------------------------
 // One decode step.  Latency, not bandwidth, bounds a step: one workgroup per
-// (sequence, head) moves ~100 KB through a chain of dependent phases.  So every
-// load the step can know of at entry is issued at once, with no branch between
-// the loads and their first use (a divergent branch makes the compiler wait for
-// a load inside it): the slot tables, the token, every slot's mean key, the gain
-// and the keys and values of the cell this wave read at the previous step.  The
-// record keeps that slot per wave as a hint.  Queries of one head keep choosing
-// the same high-norm cells, so the hint is usually right and the gather needs no
-// second round trip.  The prefetched rows are used only if the hinted slot is
-// selected again, and the rows of a selected cell never change (only the cell
-// being filled is written, and it is not in A), so no result depends on the hint.
-// Ranks (Eq. 15 merge, top-K) are counted over 64-bit integer keys in LDS; the
-// top-K is taken per wave first and then over the waves' candidates.  Each
-// selected cell's softmax partials are kept apart by rank and combined in rank
+// (sequence, head) moves ~100 KB through a chain of dependent phases.  So the
+// loads the step can know of at entry -- the slot tables, the token, the gain
+// and every slot's mean key -- are issued at once, with no branch between the
+// loads and their first use (a divergent branch makes the compiler wait for a
+// load inside it).  Right after the first barrier each wave requests the keys
+// and values of the cell it read at the previous step: the record keeps that
+// slot per wave as a hint.  Queries of one head keep choosing the same
+// high-norm cells in the same order, so the hint is usually right and the
+// gather overlaps the scoring instead of following it.  The prefetched rows
+// are used only if the hinted slot is selected again at the same rank, and the
+// rows of a selected cell never change (only the cell being filled is written,
+// and it is not in A), so no result depends on the hint.  Ranks (Eq. 15 merge,
+// top-K) are counted over 64-bit integer keys in LDS; the top-K is taken per
+// wave first and then over the waves' candidates.  Each selected cell's
+// softmax partials are kept apart by rank, and wave 0 combines them in rank
 // order, so outputs are bitwise the same whichever wave read which cell.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict__ state, StateLayout L,
@@ -325,10 +327,6 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     const int32_t cell_in = R.cell[ts], flags_in = R.flags[ts], ridx_in = R.ridx[ts];
     const float a_in = R.a[ts];
     const T q_in = q[bh * D + td], k_in = k_new[bh * D + td], v_in = v_new[bh * D + td];
-    // Every wave's small loads go out before any wave's bulk loads: the whole
-    // step's traffic is requested at once and would otherwise queue ahead of them.
-    asm volatile("" ::: "memory"); // keeps the small loads above the barrier
-    __builtin_amdgcn_s_barrier();
     const int my_slot = t >> 1, my_part = t & 1;
     const int ks = my_slot < L.S ? my_slot : 0;
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
@@ -342,18 +340,6 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
         my_hint = wave == w ? mv.hint[w] : my_hint;
     my_hint = kPrefetch && my_hint >= 0 && my_hint < L.S ? my_hint : -1;
     u32x4 kraw[KC], vraw[VR];
-    if constexpr (kPrefetch) { // slot 0 stands in for a missing hint: the read is wasted, never used
-        const int ps = my_hint >= 0 ? my_hint : 0;
-        const T *kc = sk + (int64_t)ps * kS * D + (int64_t)(lane >> 1) * D + (lane & 1) * HALF;
-        const T *vc = sv + (int64_t)ps * kS * D + (int64_t)vrow0 * D + vch * EPC;
-#pragma unroll
-        for (int x = 0; x < KC; ++x)
-            kraw[x] = *reinterpret_cast<const u32x4 *>(kc + x * EPC);
-#pragma unroll
-        for (int x = 0; x < VR; ++x)
-            vraw[x] = *reinterpret_cast<const u32x4 *>(vc + (int64_t)RG * x * D);
-    }
-
     const int bad = (int)(hv.magic != kStateMagic) | (int)(hv.version != kStateVersion) |
                     (int)(hv.batch != expect.batch) | (int)(hv.H != expect.H) | (int)(hv.d != D) |
                     (int)(hv.dtype != expect.dtype) | (int)(hv.P != P) | (int)(hv.W != W) |
@@ -389,6 +375,20 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     int n_ret = mv.n_ret < 0 ? 0 : (mv.n_ret > L.S ? L.S : mv.n_ret);
     int cur = mv.cur_slot;
     __syncthreads();
+    // The cell prefetch goes out only now: issued with the loads above, it delayed
+    // them (and the barrier) by the whole step's traffic; from here it overlaps
+    // the scoring and top-K.
+    if constexpr (kPrefetch) { // slot 0 stands in for a missing hint: the read is wasted, never used
+        const int ps = my_hint >= 0 ? my_hint : 0;
+        const T *kc = sk + (int64_t)ps * kS * D + (int64_t)(lane >> 1) * D + (lane & 1) * HALF;
+        const T *vc = sv + (int64_t)ps * kS * D + (int64_t)vrow0 * D + vch * EPC;
+#pragma unroll
+        for (int x = 0; x < KC; ++x)
+            kraw[x] = *reinterpret_cast<const u32x4 *>(kc + x * EPC);
+#pragma unroll
+        for (int x = 0; x < VR; ++x)
+            vraw[x] = *reinterpret_cast<const u32x4 *>(vc + (int64_t)RG * x * D);
+    }
 
     const int64_t beta = i / kB;
     const int r = (int)(i % kS);
