@@ -80,7 +80,7 @@ Geometry geometry(const fs_shape *sh, const fs_params *p)
 
 // Workspace of fs_longrange_prefill, carved in this order (256-byte aligned).
 struct PrefillLayout {
-    size_t kbar, ksplit, knorm, a, death, retained, n_ret, sel, total;
+    size_t kbar, ksplit, knorm, a, death, ord, retained, n_ret, sel, total;
 };
 
 PrefillLayout prefill_layout(const Geometry &g)
@@ -97,6 +97,8 @@ PrefillLayout prefill_layout(const Geometry &g)
     off += align_up((size_t)g.bh * g.M * sizeof(float));
     L.death = off;
     off += g.prune ? align_up((size_t)g.bh * g.M * sizeof(int32_t)) : 0;
+    L.ord = off; // cells in priority order with their exit blocks (list building)
+    off += g.prune ? align_up((size_t)g.bh * g.M * sizeof(int64_t)) : 0;
     L.retained = off;
     off += g.prune ? align_up((size_t)g.bh * g.NB * g.cap * sizeof(int32_t)) : 0;
     L.n_ret = off;
@@ -233,7 +235,8 @@ FSL_EXPORT size_t fs_prune_workspace_bytes(const fs_shape *shape, const fs_param
     if (check_all(shape, prm) != FS_OK)
         return 0;
     const Geometry g = geometry(shape, prm);
-    return align_up((size_t)g.bh * (g.M > 0 ? g.M : 1) * sizeof(int32_t));
+    const size_t cells = (size_t)g.bh * (g.M > 0 ? g.M : 1);
+    return align_up(cells * sizeof(int32_t)) + align_up(cells * sizeof(int64_t)); // exit blocks, priority order
 }
 
 FSL_EXPORT fs_status fs_prune_retained(const fs_shape *shape, const fs_params *prm, const float *a,
@@ -248,8 +251,10 @@ FSL_EXPORT fs_status fs_prune_retained(const fs_shape *shape, const fs_params *p
     if (workspace_bytes < fs_prune_workspace_bytes(shape, prm))
         return FS_ERR_WORKSPACE;
     const Geometry g = geometry(shape, prm);
-    return hip_status(launch_prune(g, a, static_cast<int32_t *>(workspace), retained, n_retained, 1,
-                                   static_cast<hipStream_t>(stream)));
+    const size_t cells = (size_t)g.bh * (g.M > 0 ? g.M : 1);
+    int32_t *death = static_cast<int32_t *>(workspace);
+    int64_t *ord = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + align_up(cells * sizeof(int32_t)));
+    return hip_status(launch_prune(g, a, death, ord, retained, n_retained, 1, static_cast<hipStream_t>(stream)));
 }
 
 FSL_EXPORT fs_status fs_score_select(const fs_shape *shape, const fs_params *prm, const void *q, const float *kbar,
@@ -361,6 +366,7 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
     float *knorm = g.bf16 ? reinterpret_cast<float *>(ws + L.knorm) : nullptr;
     float *a = reinterpret_cast<float *>(ws + L.a);
     int32_t *death = reinterpret_cast<int32_t *>(ws + L.death);
+    int64_t *ord = reinterpret_cast<int64_t *>(ws + L.ord);
     int32_t *retained = reinterpret_cast<int32_t *>(ws + L.retained);
     int32_t *n_ret = reinterpret_cast<int32_t *>(ws + L.n_ret);
     int32_t *sel_buf = sel ? sel : reinterpret_cast<int32_t *>(ws + L.sel);
@@ -370,7 +376,7 @@ FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params
     const bool fused = out && g.bf16 && (!g.prune || g.cap <= kFusedMaxCap);
     hipError_t e = launch_cell_summaries(g, k, kbar, a, route ? ksplit : nullptr, fused ? knorm : nullptr, s);
     if (e == hipSuccess && g.prune)
-        e = launch_prune(g, a, death, retained, n_ret, route ? 1 : 0, s);
+        e = launch_prune(g, a, death, ord, retained, n_ret, route ? 1 : 0, s);
     if (e == hipSuccess && fused) {
         e = launch_route_readout(g, hc, q, k, v, ksplit, knorm, a, g.prune ? retained : nullptr,
                                  g.prune ? n_ret : nullptr, gain, out, sel, s);

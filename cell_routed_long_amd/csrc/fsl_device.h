@@ -177,6 +177,16 @@ __device__ __forceinline__ uint64_t rank_key(float score, uint32_t low)
     return ((uint64_t)u << 32) | low;
 }
 
+// TopP's order (norm desc, id asc) as one 64-bit key: the fp32 norm's bits made
+// monotone above 0x7fffffff - cell.  For norms (never -0 or NaN) it is exactly
+// that order; a larger key ranks first and every key is nonzero.
+__device__ __forceinline__ uint64_t norm_key(float a, int32_t cell)
+{
+    uint32_t u = __float_as_uint(a);
+    u = (u >> 31) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - cell);
+}
+
 // Insert key into the descending list kl of KT keys (a select network: a key
 // below the last entry moves nothing).
 template <int KT>

@@ -30,8 +30,9 @@ hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, 
                                  float *kbar_norm, hipStream_t st);
 
 // death[c]: first query block whose TopP no longer holds cell c (INT32_MAX: never leaves).
+// ord: [bh, M] scratch (the head's cells in priority order, with their exit blocks).
 // emit = 0 computes only the exit blocks (enough to build a decode state).
-hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32_t *retained,
+hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int64_t *ord, int32_t *retained,
                         int32_t *n_ret, int emit, hipStream_t st);
 
 // kbar_split (optional, bf16 only): the parts written by launch_cell_summaries.

@@ -67,16 +67,9 @@ __device__ __forceinline__ void load_row_f32(const T *__restrict__ p, float (&x)
 }
 
 // Order-preserving integer images of the two rankings (a larger key ranks first):
-//   TopP by (norm desc, id asc): the fp32 norm's bits (made monotone) above the
-//   complemented id -- exact;
+//   TopP by (norm desc, id asc): norm_key;
 //   top-K by (score desc, id asc): rank_key of the fp32 score above
 //   127 - (position in A) -- exact, since positions in A follow cell ids.
-__device__ __forceinline__ uint64_t norm_key(float a, int32_t cell)
-{
-    uint32_t u = __float_as_uint(a);
-    u = (u >> 31) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0x7fffffff - cell);
-}
 
 // Number of keys in k[0 .. n8) (n8 a multiple of 8, entries past the live ones
 // zero) that are larger than `mine`: the rank of `mine` among distinct keys.

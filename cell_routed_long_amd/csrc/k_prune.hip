@@ -146,12 +146,137 @@ __global__ __launch_bounds__(kWave) void prune_emit_kernel(const int32_t *__rest
         n_ret[head * NB + beta] = count;
 }
 
+// For list building, two passes that need no per-block sort:
+//   prune_rank_kernel: four lanes per cell compare its key (norm_key) with
+//       every key of the head, staged in LDS, 64 keys per round (16 per lane):
+//       the number of larger keys is the cell's rank in priority order (a
+//       desc, id asc), and the P-th larger key in id order is its exit
+//       block's cell e (a prefix sum over the four lanes' counts tells which
+//       lane's 16 keys hold it).  The cell is written as (exit block, id) at
+//       its rank, so `ord` lists the head's cells in priority order;
+//   prune_list_kernel: one wave per (head, block) keeps, in that order, the
+//       cells of C_beta still in TopP (exit block > beta) or among the W most
+//       recent, which is A_beta already in priority order.
+constexpr int kRankMaxCells = 4096; // keys of one head in LDS (32 KB)
+constexpr int kRankThreads = 256;   // 64 cells per workgroup, four lanes each
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x)
+{
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, true);
+}
+
+__global__ __launch_bounds__(kRankThreads) void prune_rank_kernel(const float *__restrict__ a,
+                                                                  int32_t *__restrict__ death,
+                                                                  int64_t *__restrict__ ord, int64_t M, int P,
+                                                                  int cells_per_block)
+{
+    __shared__ __attribute__((aligned(16))) uint64_t s_key[kRankMaxCells];
+    const int64_t head = blockIdx.y;
+    const int t = threadIdx.x;
+    const int m = (int)M; // <= kRankMaxCells (host check)
+    const int m64 = (m + 63) & ~63;
+    const float *ah = a + head * M;
+    for (int x = t; x < m64; x += kRankThreads)
+        s_key[x] = x < m ? norm_key(ah[x], x) : 0; // 0 is below every key
+    __syncthreads();
+    const int c = blockIdx.x * (kRankThreads / 4) + t / 4;
+    const int sub = t & 3; // this lane's 16 keys of every 64
+    const uint64_t kc = s_key[c < m ? c : 0];
+    int count = 0, e = -1; // larger keys in the rounds so far; the P-th of them in id order
+    for (int base = 0; base < m64; base += 64) {
+        uint64_t k[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(&s_key[base + 16 * sub + 2 * j]);
+            k[2 * j] = ((uint64_t)w[1] << 32) | w[0];
+            k[2 * j + 1] = ((uint64_t)w[3] << 32) | w[2];
+        }
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            n += k[j] > kc ? 1 : 0;
+        // counts of the quad's four lanes (quad_perm broadcasts of lanes 0..3)
+        const int n0 = dpp_i<0x00>(n), n1 = dpp_i<0x55>(n), n2 = dpp_i<0xAA>(n), n3 = dpp_i<0xFF>(n);
+        const int before = count + (sub > 0 ? n0 : 0) + (sub > 1 ? n1 : 0) + (sub > 2 ? n2 : 0);
+        int e_here = -1;
+        if (before < P && before + n >= P) { // the P-th larger key is one of these 16
+            int need = P - before;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (k[j] > kc && need > 0 && --need == 0)
+                    e_here = base + 16 * sub + j;
+        }
+        e_here = max(e_here, dpp_i<0xB1>(e_here)); // quad_perm [1,0,3,2]
+        e_here = max(e_here, dpp_i<0x4E>(e_here)); // quad_perm [2,3,0,1]
+        e = max(e, e_here);
+        count += (n0 + n1) + (n2 + n3);
+    }
+    if (c >= m || sub != 0)
+        return;
+    const int32_t dth = P == 0 ? 0 : (e < 0 ? INT32_MAX : (int32_t)(e / cells_per_block + 1));
+    death[head * M + c] = dth;
+    ord[head * M + count] = ((int64_t)dth << 32) | (uint32_t)c; // keys are distinct: ranks are a permutation
+}
+
+__global__ __launch_bounds__(kWave) void prune_list_kernel(const int64_t *__restrict__ ord,
+                                                           int32_t *__restrict__ retained,
+                                                           int32_t *__restrict__ n_ret, int64_t M, int NB, int cap,
+                                                           int W, int cells_per_block)
+{
+    const int beta = blockIdx.x;
+    const int64_t head = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int64_t n_avail = (int64_t)beta * cells_per_block < M ? (int64_t)beta * cells_per_block : M; // Eq. 6
+    const int64_t recent0 = n_avail > W ? n_avail - W : 0;
+    const int64_t *oh = ord + head * M;
+    int32_t *dst = retained + (head * NB + beta) * (int64_t)cap;
+    int count = 0;
+    constexpr int kWin = 8; // 8 windows of 64 cells per round trip
+    for (int64_t base = 0; base < M; base += kWin * kWave) {
+        int64_t ov[kWin];
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+            const int64_t j = base + u * kWave + lane;
+            ov[u] = j < M ? oh[j] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+            const int32_t c = (int32_t)(uint32_t)ov[u];
+            const int32_t d = (int32_t)(ov[u] >> 32);
+            const bool keep = c >= 0 && (c < recent0 ? d > beta : c < n_avail);
+            const uint64_t mask = __ballot(keep);
+            const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+            if (keep && pos < cap) // at most P non-recent cells stay in TopP(C_beta): pos < P + W
+                dst[pos] = c;
+            count += __popcll(mask);
+        }
+    }
+    if (count > cap)
+        count = cap;
+    for (int x = count + lane; x < cap; x += kWave)
+        dst[x] = -1;
+    if (lane == 0)
+        n_ret[head * NB + beta] = count;
+}
+
 } // namespace
 
-hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int32_t *retained, int32_t *n_ret,
-                        int emit, hipStream_t st)
+hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int64_t *ord, int32_t *retained,
+                        int32_t *n_ret, int emit, hipStream_t st)
 {
     const int cpb = g.B / g.s;
+    if (emit && g.M > 0 && g.M <= kRankMaxCells) {
+        dim3 grid((unsigned)((g.M + kRankThreads / 4 - 1) / (kRankThreads / 4)), (unsigned)g.bh);
+        hipLaunchKernelGGL(prune_rank_kernel, grid, dim3(kRankThreads), 0, st, a, death, ord, g.M, g.P, cpb);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+        dim3 grid2((unsigned)g.NB, (unsigned)g.bh);
+        hipLaunchKernelGGL(prune_list_kernel, grid2, dim3(kWave), 0, st, ord, retained, n_ret, g.M, g.NB, g.cap, g.W,
+                           cpb);
+        return hipGetLastError();
+    }
     if (g.M > 0) {
         dim3 grid((unsigned)((g.M + kDeathCells - 1) / kDeathCells), (unsigned)g.bh);
         hipLaunchKernelGGL(prune_death_kernel, grid, dim3(kDeathThreads), 0, st, a, death, g.M, g.P, cpb);

@@ -88,12 +88,13 @@ def test_workspace_sizes(L):
     sh, p = shape(b=4, H=16, N=16384, d=128, dtype=fsl.FS_BF16), prm()
     ws = fsl.fs_prefill_workspace_bytes(sh, fsl.Params())
     M, NB = 16384 // 32, 16384 // 128
-    # summaries (fp32, bf16 parts and their norms) + key norms + per-cell exit blocks + retained lists + counts
-    # + selections
-    at_least = 64 * (M * 128 * 4 + M * 3 * 128 * 2 + M * 4 + M * 4 + M * 4 + NB * 72 * 4 + NB * 4 + 16384 * 4 * 4)
-    assert at_least <= ws <= at_least + 8 * 256
+    # summaries (fp32, bf16 parts and their norms) + key norms + per-cell exit blocks + the cells of every head in
+    # priority order (8 bytes each) + retained lists + counts + selections
+    at_least = 64 * (M * 128 * 4 + M * 3 * 128 * 2 + M * 4 + M * 4 + M * 4 + M * 8 + NB * 72 * 4 + NB * 4
+                     + 16384 * 4 * 4)
+    assert at_least <= ws <= at_least + 9 * 256
     assert fsl.fs_prefill_workspace_bytes(shape(d=96), fsl.Params()) == 0
-    assert fsl.fs_prune_workspace_bytes(sh, fsl.Params()) >= 64 * M * 4
+    assert fsl.fs_prune_workspace_bytes(sh, fsl.Params()) >= 64 * M * (4 + 8)
 
 
 def test_prefill_validation_before_launch(L):
