@@ -104,7 +104,10 @@ def test_cell_summaries(w):
     (synth.Workload(batch=2, H=2, N=5000, d=64, dtype="f32", seed=31, needle_frac=0.01), 5, 3),
     (synth.Workload(batch=1, H=2, N=3000, d=128, dtype="bf16", seed=32), 0, 4),
     (synth.Workload(batch=1, H=2, N=3000, d=128, dtype="bf16", seed=33), 7, 0),
-], ids=["cfg4k", "P5W3", "P0W4", "P7W0"])
+    # heads of up to 4096 cells are ranked once and filtered per block; longer ones take the other kernels
+    (synth.Workload(batch=1, H=1, N=4096 * 32 + 31, d=64, dtype="bf16", seed=34, needle_frac=0.005), 64, 8),
+    (synth.Workload(batch=1, H=1, N=4100 * 32, d=64, dtype="bf16", seed=35, needle_frac=0.005), 64, 8),
+], ids=["cfg4k", "P5W3", "P0W4", "P7W0", "M4096-ranked", "M4100-per-block"])
 def test_prune_retained(w, P, W):
     p = fsl.Params(P=P, W=W)
     host = pu.inputs(w)
