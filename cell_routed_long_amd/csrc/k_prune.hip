@@ -154,9 +154,10 @@ __global__ __launch_bounds__(kWave) void prune_emit_kernel(const int32_t *__rest
 //       block's cell e (a prefix sum over the four lanes' counts tells which
 //       lane's 16 keys hold it).  The cell is written as (exit block, id) at
 //       its rank, so `ord` lists the head's cells in priority order;
-//   prune_list_kernel: one wave per (head, block) keeps, in that order, the
-//       cells of C_beta still in TopP (exit block > beta) or among the W most
-//       recent, which is A_beta already in priority order.
+//   prune_list_kernel: the order is staged in LDS once per 16 blocks of a head,
+//       and one wave per block keeps, in that order, the cells of C_beta still
+//       in TopP (exit block > beta) or among the W most recent, which is A_beta
+//       already in priority order.
 constexpr int kRankMaxCells = 4096; // keys of one head in LDS (32 KB)
 constexpr int kRankThreads = 256;   // 64 cells per workgroup, four lanes each
 
@@ -219,38 +220,40 @@ __global__ __launch_bounds__(kRankThreads) void prune_rank_kernel(const float *_
     ord[head * M + count] = ((int64_t)dth << 32) | (uint32_t)c; // keys are distinct: ranks are a permutation
 }
 
-__global__ __launch_bounds__(kWave) void prune_list_kernel(const int64_t *__restrict__ ord,
-                                                           int32_t *__restrict__ retained,
-                                                           int32_t *__restrict__ n_ret, int64_t M, int NB, int cap,
-                                                           int W, int cells_per_block)
+constexpr int kListThreads = 1024; // 16 blocks of one head per workgroup, one wave each
+constexpr int kListBlocks = kListThreads / kWave;
+
+__global__ __launch_bounds__(kListThreads) void prune_list_kernel(const int64_t *__restrict__ ord,
+                                                                  int32_t *__restrict__ retained,
+                                                                  int32_t *__restrict__ n_ret, int64_t M, int NB,
+                                                                  int cap, int W, int cells_per_block)
 {
-    const int beta = blockIdx.x;
+    __shared__ int64_t s_ord[kRankMaxCells]; // the head's cells in priority order, read once
     const int64_t head = blockIdx.y;
-    const int lane = threadIdx.x;
-    const int64_t n_avail = (int64_t)beta * cells_per_block < M ? (int64_t)beta * cells_per_block : M; // Eq. 6
-    const int64_t recent0 = n_avail > W ? n_avail - W : 0;
+    const int t = threadIdx.x, lane = t & (kWave - 1);
+    const int m = (int)M; // <= kRankMaxCells (host check)
     const int64_t *oh = ord + head * M;
+    for (int x = t; x < m; x += kListThreads)
+        s_ord[x] = oh[x];
+    __syncthreads();
+    const int beta = blockIdx.x * kListBlocks + t / kWave;
+    if (beta >= NB)
+        return; // whole wave
+    const int n_avail = (int64_t)beta * cells_per_block < M ? beta * cells_per_block : m; // |C_beta|, Eq. 6
+    const int recent0 = n_avail > W ? n_avail - W : 0;
     int32_t *dst = retained + (head * NB + beta) * (int64_t)cap;
     int count = 0;
-    constexpr int kWin = 8; // 8 windows of 64 cells per round trip
-    for (int64_t base = 0; base < M; base += kWin * kWave) {
-        int64_t ov[kWin];
-#pragma unroll
-        for (int u = 0; u < kWin; ++u) {
-            const int64_t j = base + u * kWave + lane;
-            ov[u] = j < M ? oh[j] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kWin; ++u) {
-            const int32_t c = (int32_t)(uint32_t)ov[u];
-            const int32_t d = (int32_t)(ov[u] >> 32);
-            const bool keep = c >= 0 && (c < recent0 ? d > beta : c < n_avail);
-            const uint64_t mask = __ballot(keep);
-            const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
-            if (keep && pos < cap) // at most P non-recent cells stay in TopP(C_beta): pos < P + W
-                dst[pos] = c;
-            count += __popcll(mask);
-        }
+    for (int base = 0; base < m; base += kWave) {
+        const int j = base + lane;
+        const int64_t ov = j < m ? s_ord[j] : -1;
+        const int32_t c = (int32_t)(uint32_t)ov;
+        const int32_t d = (int32_t)(ov >> 32);
+        const bool keep = c >= 0 && (c < recent0 ? d > beta : c < n_avail);
+        const uint64_t mask = __ballot(keep);
+        const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+        if (keep && pos < cap) // at most P non-recent cells stay in TopP(C_beta): pos < P + W
+            dst[pos] = c;
+        count += __popcll(mask);
     }
     if (count > cap)
         count = cap;
@@ -272,9 +275,9 @@ hipError_t launch_prune(const Geometry &g, const float *a, int32_t *death, int64
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
-        dim3 grid2((unsigned)g.NB, (unsigned)g.bh);
-        hipLaunchKernelGGL(prune_list_kernel, grid2, dim3(kWave), 0, st, ord, retained, n_ret, g.M, g.NB, g.cap, g.W,
-                           cpb);
+        dim3 grid2((unsigned)((g.NB + kListBlocks - 1) / kListBlocks), (unsigned)g.bh);
+        hipLaunchKernelGGL(prune_list_kernel, grid2, dim3(kListThreads), 0, st, ord, retained, n_ret, g.M, g.NB,
+                           g.cap, g.W, cpb);
         return hipGetLastError();
     }
     if (g.M > 0) {
