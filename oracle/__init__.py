@@ -8,7 +8,8 @@ arrays into it and runs independent (sequence, head) pairs on a thread pool
 (ctypes releases the GIL while the C code runs).
 
 Page: "FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
-Extrapolation" (arXiv 2610.17191), Sec. 3.3 Eqs. 5-9 and App. D.2 Eq. 17.
+Extrapolation" (arXiv 2610.17191), Sec. 3.3 Eqs. 5-9 and App. D.2 Eq. 17; the
+local branch of Sec. 3.2 (Eqs. 3-4) and the combination of Eq. 2.
 """
 from __future__ import annotations
 
@@ -58,6 +59,9 @@ def _bind(path: str):
     lib.oracle_retained.restype = i64
     lib.oracle_cell_score.argtypes = [ctypes.POINTER(_Cfg), vp, vp, ctypes.c_double, i64, i64]
     lib.oracle_cell_score.restype = ctypes.c_double
+    lib.oracle_local.argtypes = [i64, ctypes.c_int32, i64, ctypes.c_double, vp, vp, vp, ctypes.c_double, vp, i64, i64,
+                                 vp]
+    lib.oracle_local.restype = ctypes.c_int
     return lib
 
 
@@ -207,3 +211,17 @@ def batch(q, k, v, g=None, prm: Params = Params(), heads=None, i_lo: int = 0, i_
     n = threads or min(16, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=n) as ex:
         return dict(ex.map(one, pairs))
+
+
+def local(q, k, v, w: int = 512, rope_base: float = 10000.0, alpha: float = 0.0, o_lr=None, i_lo: int = 0,
+          i_hi: int | None = None):
+    """Local branch (Sec. 3.2, Eqs. 3-4) for one head, plus alpha * o_lr (Eq. 2) when o_lr
+    [(i_hi - i_lo), d] is given: q, k, v [N, d] -> out [(i_hi - i_lo), d]."""
+    q, k, v, o_lr = _f64(q), _f64(k), _f64(v), _f64(o_lr)
+    N, d = k.shape
+    i_hi = N if i_hi is None else i_hi
+    out = np.zeros((i_hi - i_lo, d))
+    rc = _load().oracle_local(N, d, w, rope_base, _p(q), _p(k), _p(v), alpha, _p(o_lr), i_lo, i_hi, _p(out))
+    if rc != 0:
+        raise ValueError("oracle_local rejected its arguments")
+    return out

@@ -278,3 +278,65 @@ int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const d
     free(kb);
     return status;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Local branch, Sec. 3.2 Eqs. 3-4, and Eq. 2.                              */
+
+/* x turned by R(p): pair (2m, 2m+1) by the angle p * theta_m (Su et al., RoFormer). */
+static void rope_rotate(const double *x, int32_t d, double p, double rope_base, double *y)
+{
+    for (int32_t m = 0; m < d / 2; ++m) {
+        const double theta = pow(rope_base, -2.0 * m / d);
+        const double c = cos(p * theta), sn = sin(p * theta);
+        y[2 * m] = x[2 * m] * c - x[2 * m + 1] * sn;
+        y[2 * m + 1] = x[2 * m] * sn + x[2 * m + 1] * c;
+    }
+}
+
+int oracle_local(int64_t N, int32_t d, int64_t w, double rope_base, const double *q, const double *k,
+                 const double *v, double alpha, const double *o_lr, int64_t i_lo, int64_t i_hi, double *out)
+{
+    if (d <= 0 || (d & 1) || w < 0 || !(rope_base > 0.0) || i_lo < 0 || i_hi > N || i_lo > i_hi)
+        return -1;
+    /* R(j) k_j for every key the queries can reach, once */
+    const int64_t j0 = i_lo - w > 0 ? i_lo - w : 0;
+    const int64_t nk = i_hi - j0;
+    double *kr = malloc((size_t)(nk > 0 ? nk : 1) * d * sizeof(double));
+    double *qr = malloc((size_t)d * sizeof(double));
+    double *logit = malloc((size_t)(w + 1) * sizeof(double));
+    if (!kr || !qr || !logit) {
+        free(kr); free(qr); free(logit);
+        return -1;
+    }
+    for (int64_t j = j0; j < i_hi; ++j)
+        rope_rotate(k + j * d, d, (double)j, rope_base, kr + (j - j0) * d);
+    for (int64_t i = i_lo; i < i_hi; ++i) {
+        rope_rotate(q + i * d, d, (double)i, rope_base, qr);
+        const int64_t lo = i - w > 0 ? i - w : 0; /* L_i = [lo, i] */
+        double mx = -INFINITY;
+        for (int64_t j = lo; j <= i; ++j) {
+            double dot = 0.0;
+            for (int32_t f = 0; f < d; ++f)
+                dot += qr[f] * kr[(j - j0) * d + f];
+            logit[j - lo] = dot / sqrt((double)d);
+            if (logit[j - lo] > mx)
+                mx = logit[j - lo];
+        }
+        double z = 0.0;
+        for (int64_t j = lo; j <= i; ++j) {
+            logit[j - lo] = exp(logit[j - lo] - mx);
+            z += logit[j - lo];
+        }
+        double *o = out + (i - i_lo) * d;
+        for (int32_t f = 0; f < d; ++f) {
+            double u = 0.0;
+            for (int64_t j = lo; j <= i; ++j)
+                u += logit[j - lo] * v[j * d + f];
+            o[f] = u / z + (o_lr ? alpha * o_lr[(i - i_lo) * d + f] : 0.0);
+        }
+    }
+    free(logit);
+    free(qr);
+    free(kr);
+    return 0;
+}

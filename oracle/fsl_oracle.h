@@ -7,7 +7,8 @@
  *
  * Source: "FreeSolo: Linear-time Sparse Attention with Zero-Shot Length
  * Extrapolation" (arXiv 2610.17191), Sec. 3.3 (Eqs. 5-9), Sec. 2 (Eq. 1) and
- * App. D.2 (Eq. 17).  Every array is fp64 and row-major; one call handles one
+ * App. D.2 (Eq. 17); the local branch of Sec. 3.2 (Eqs. 3-4) and the branch
+ * combination of Sec. 3.1 (Eq. 2).  Every array is fp64 and row-major; one call handles one
  * (sequence, head) pair.
  */
 #ifndef FSL_ORACLE_H
@@ -67,6 +68,21 @@ int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const d
                 const double *g, int64_t i_lo, int64_t i_hi, int64_t cap,
                 double *kbar, double *a, int32_t *retained, int32_t *n_ret, double *gap_p,
                 int32_t *sel, double *gap_k, double *out, double *scores);
+
+/*
+ * Local branch (Sec. 3.2, Eqs. 3-4) and the branch combination (Sec. 3.1,
+ * Eq. 2) for one (sequence, head), queries i in [i_lo, i_hi):
+ *   L_i   = {j : 0 <= j <= i, i - j <= w}   (a full window holds w + 1 tokens)
+ *   l_ij  = (R(i) q_i) . (R(j) k_j) / sqrt(d), R(p) the RoPE rotation at
+ *           position p (Su et al.): feature pair (2m, 2m+1) turned by the angle
+ *           p * theta_m, theta_m = rope_base^(-2m/d)
+ *   o_sr  = softmax_{j in L_i}(l_ij) V_{L_i}
+ *   out_i = o_sr_i + alpha * o_lr_i, or o_sr_i when o_lr is NULL.
+ *   q, k, v [N, d];  o_lr, out [(i_hi - i_lo), d].
+ * Returns 0, or -1 for invalid arguments (odd d, w < 0, rope_base <= 0).
+ */
+int oracle_local(int64_t N, int32_t d, int64_t w, double rope_base, const double *q, const double *k,
+                 const double *v, double alpha, const double *o_lr, int64_t i_lo, int64_t i_hi, double *out);
 
 #ifdef __cplusplus
 }

@@ -42,6 +42,15 @@ MUTATIONS = [
      "const int64_t b_i = (int64_t)cfg->B * (blk + 1);"),
     ("gain ignored", "o[f] = (g ? g[f] : 1.0) * o[f] * inv;", "o[f] = o[f] * inv;"),
     ("query and key swapped in score", "dot += q_i[f] * kbar_c[f];", "dot += q_i[f] * q_i[f];"),
+    ("rope rotation reversed", "y[2 * m] = x[2 * m] * c - x[2 * m + 1] * sn;", "y[2 * m] = x[2 * m] * c + x[2 * m + 1] * sn;"),
+    ("rope frequency base^(-m/d)", "pow(rope_base, -2.0 * m / d)", "pow(rope_base, -1.0 * m / d)"),
+    ("local window one short", "const int64_t lo = i - w > 0 ? i - w : 0;",
+     "const int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;"),
+    ("local logits without 1/sqrt(d)", "logit[j - lo] = dot / sqrt((double)d);", "logit[j - lo] = dot;"),
+    ("alpha on the local branch", "o[f] = u / z + (o_lr ? alpha * o_lr[(i - i_lo) * d + f] : 0.0);",
+     "o[f] = alpha * u / z + (o_lr ? o_lr[(i - i_lo) * d + f] : 0.0);"),
+    ("keys rotated at the query position", "rope_rotate(k + j * d, d, (double)j, rope_base",
+     "rope_rotate(k + j * d, d, (double)i_lo, rope_base"),
 ]
 
 

@@ -395,3 +395,100 @@ def test_partial_range_matches_full_run():
     part = oracle.head(q, k, v, i_lo=300, i_hi=777)
     np.testing.assert_array_equal(part["sel"], full["sel"][300:777])
     np.testing.assert_array_equal(part["out"], full["out"][300:777])
+
+
+# ------------------------------------------- local branch (Eqs. 3-4) and Eq. 2 ----
+
+def test_local_window_zero_reads_own_value():
+    """Sec. 3.2 with w = 0: L_i = {i}, so the local output is v_i whatever q and k are."""
+    r = rng(40)
+    q, k, v = (r.normal(size=(50, 8)) for _ in range(3))
+    np.testing.assert_allclose(oracle.local(q, k, v, w=0), v, rtol=0, atol=1e-15)
+
+
+def test_local_zero_query_reads_window_mean():
+    """q = 0 makes every logit equal, so o_i is the mean of v over [max(0, i - w), i]:
+    a full window holds w + 1 tokens (Sec. 3.2)."""
+    r = rng(41)
+    N, d, w = 60, 6, 7
+    k, v = r.normal(size=(N, d)), r.normal(size=(N, d))
+    o = oracle.local(np.zeros((N, d)), k, v, w=w)
+    for i in range(N):
+        np.testing.assert_allclose(o[i], v[max(0, i - w): i + 1].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def _softmax_read(logits, vals):
+    p = np.exp(logits - logits.max())
+    return (p / p.sum()) @ vals
+
+
+def test_local_rope_angle_difference_closed_form():
+    """d = 2 has one pair with theta_0 = 1.  For q = (1, 0) and k = (0, 1) the rotated
+    product is cos(i)(-sin j) + sin(i)cos(j) = sin(i - j) (angle difference), so the
+    logits are sin(i - j) / sqrt(2) (Eq. 3)."""
+    N, w = 40, 9
+    q = np.tile([1.0, 0.0], (N, 1))
+    k = np.tile([0.0, 1.0], (N, 1))
+    v = rng(42).normal(size=(N, 2))
+    o = oracle.local(q, k, v, w=w)
+    for i in range(N):
+        js = np.arange(max(0, i - w), i + 1)
+        np.testing.assert_allclose(o[i], _softmax_read(np.sin(i - js) / np.sqrt(2.0), v[js]), rtol=0, atol=1e-13)
+
+
+def test_local_rope_frequency_closed_form():
+    """theta_m = base^(-2m/d): with d = 4 and base 100, pair 1 turns by 100^(-1/2) = 0.1
+    rad per position, so q = (0, 0, 1, 0), k = (0, 0, 0, 1) give sin(0.1 (i - j)) / 2."""
+    N, w = 30, 12
+    q = np.tile([0.0, 0.0, 1.0, 0.0], (N, 1))
+    k = np.tile([0.0, 0.0, 0.0, 1.0], (N, 1))
+    v = rng(43).normal(size=(N, 4))
+    o = oracle.local(q, k, v, w=w, rope_base=100.0)
+    for i in range(N):
+        js = np.arange(max(0, i - w), i + 1)
+        np.testing.assert_allclose(o[i], _softmax_read(np.sin(0.1 * (i - js)) / 2.0, v[js]), rtol=0, atol=1e-13)
+
+
+def test_local_relative_position_invariance():
+    """Eq. 3: the logits depend on j - i only, so prepending m tokens leaves the output
+    of every query whose window holds none of them unchanged."""
+    r = rng(44)
+    N, d, w, m = 80, 8, 10, 13
+    q, k, v = (r.normal(size=(N, d)) for _ in range(3))
+    pre = [r.normal(size=(m, d)) for _ in range(3)]
+    o = oracle.local(q, k, v, w=w)
+    o2 = oracle.local(np.vstack([pre[0], q]), np.vstack([pre[1], k]), np.vstack([pre[2], v]), w=w)
+    np.testing.assert_allclose(o2[m + w:], o[w:], rtol=0, atol=1e-12)
+
+
+def test_local_relative_form_brute_force():
+    """Tiny brute force through Eq. 3's second form, q_i^T R(j - i) k_j, with R built as an
+    explicit block-diagonal rotation matrix (the oracle rotates q and k separately)."""
+    r = rng(45)
+    N, d, w, base = 25, 8, 6, 10000.0
+    q, k, v = (r.normal(size=(N, d)) for _ in range(3))
+
+    def rot(p):
+        R = np.zeros((d, d))
+        for mm in range(d // 2):
+            a = p * base ** (-2.0 * mm / d)
+            R[2 * mm:2 * mm + 2, 2 * mm:2 * mm + 2] = [[np.cos(a), -np.sin(a)], [np.sin(a), np.cos(a)]]
+        return R
+
+    o = oracle.local(q, k, v, w=w, rope_base=base)
+    for i in range(N):
+        js = np.arange(max(0, i - w), i + 1)
+        logits = np.array([q[i] @ rot(j - i) @ k[j] for j in js]) / np.sqrt(d)
+        np.testing.assert_allclose(o[i], _softmax_read(logits, v[js]), rtol=0, atol=1e-12)
+
+
+def test_local_branch_combination_eq2():
+    """Eq. 2: o = o_sr + alpha_h o_lr.  With alpha = 0 the local branch alone; the
+    difference between two alphas is their difference times the long-range output."""
+    r = rng(46)
+    N, d, w = 30, 4, 5
+    q, k, v, olr = (r.normal(size=(N, d)) for _ in range(4))
+    o0 = oracle.local(q, k, v, w=w)
+    np.testing.assert_array_equal(oracle.local(q, k, v, w=w, alpha=0.0, o_lr=olr), o0)
+    o1 = oracle.local(q, k, v, w=w, alpha=1.25, o_lr=olr)
+    np.testing.assert_allclose(o1 - o0, 1.25 * olr, rtol=0, atol=1e-14)
