@@ -78,8 +78,9 @@ def lib():
         L.fs_decode_state_bytes.restype = sz
         L.fs_longrange_decode.argtypes = [P_prm, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                           vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.fs_local_window.argtypes = [P_shape, ctypes.c_int64, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp]
         for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout",
-                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_decode"):
+                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_decode", "fs_local_window"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -262,3 +263,21 @@ def decode(state, q, k_new, v_new, params: Params = Params(), sigma=4.0, lam=1.0
         sel = torch.empty(q.shape[0], q.shape[1], params.K, dtype=torch.int32, device=q.device)
     fs_longrange_decode(state, q, k_new, v_new, sigma, lam, gain, out, sel if want_sel else None, params, stream)
     return out, (sel if want_sel else None)
+
+
+def fs_local_window(q, k, v, out, w: int = 512, rope_base: float = 10000.0, alpha=None, o_lr=None, stream=None):
+    """Local branch (Sec. 3.2, Eqs. 3-4) into out [b,H,N,d]; with o_lr and alpha [H],
+    out = o_sr + alpha_h * o_lr (Eq. 2).  out may be o_lr."""
+    sh = shape_of(q)
+    al = None if alpha is None else _floats(alpha, sh.H)
+    _check(lib().fs_local_window(ctypes.byref(sh), int(w), float(rope_base), _ptr(q), _ptr(k), _ptr(v), al,
+                                 _ptr(o_lr), _ptr(out), _stream(stream)), "fs_local_window")
+
+
+def local(q, k, v, w: int = 512, rope_base: float = 10000.0, alpha=None, o_lr=None):
+    """Allocate the output with torch and run fs_local_window; returns it."""
+    import torch
+    out = torch.empty_like(q)
+    fs_local_window(q, k, v, out, w, rope_base, alpha, o_lr)
+    return out
+

@@ -429,3 +429,30 @@ FSL_EXPORT fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, in
                                          L, expect, hc, state, q, k_new, v_new, gain, out, sel,
                                          static_cast<hipStream_t>(stream)));
 }
+
+FSL_EXPORT fs_status fs_local_window(const fs_shape *shape, int64_t w, float rope_base, const void *q, const void *k,
+                                     const void *v, const float *alpha_h, const void *o_lr, void *out,
+                                     void *stream)
+{
+    fs_status st = check_shape(shape);
+    if (st != FS_OK)
+        return st;
+    if (!q || !k || !v || !out || w < 0 || !(rope_base > 1.0f) || !std::isfinite(rope_base))
+        return FS_ERR_INVALID;
+    LocalConsts lc;
+    std::memset(&lc, 0, sizeof(lc));
+    lc.rope_base = rope_base;
+    if (o_lr) {
+        if (!alpha_h)
+            return FS_ERR_INVALID;
+        for (int h = 0; h < shape->H; ++h) {
+            if (!std::isfinite(alpha_h[h]))
+                return FS_ERR_INVALID;
+            lc.alpha[h] = alpha_h[h];
+        }
+    }
+    fs_params p{32, 128, 0, 0, 1, 0, 0.0f}; // only the block size matters here
+    const Geometry g = geometry(shape, &p);
+    return hip_status(launch_local(g, lc, w, q, k, v, o_lr, out, static_cast<hipStream_t>(stream)));
+}
+

@@ -65,4 +65,12 @@ hipError_t launch_decode_step(int32_t bh, int32_t H, int32_t d, int32_t bf16, in
                               void *state, const void *q, const void *k_new, const void *v_new,
                               const float *gain, void *out, int32_t *sel, hipStream_t st);
 
+// Local branch (Sec. 3.2, Eqs. 3-4) plus alpha_h * o_lr (Eq. 2) when o_lr is not NULL.
+struct LocalConsts {
+    float alpha[128]; // alpha_h
+    float rope_base;  // RoPE frequencies theta_m = rope_base^(-2m/d)
+};
+hipError_t launch_local(const Geometry &g, const LocalConsts &lc, int64_t w, const void *q, const void *k,
+                        const void *v, const void *o_lr, void *out, hipStream_t st);
+
 } // namespace fsl

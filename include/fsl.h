@@ -252,6 +252,33 @@ fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, in
                               const float *sigma_h, const float *lambda_h, const float *gain,
                               void *out, int32_t *sel, void *stream);
 
+/*
+ * Local branch (Sec. 3.2, Eqs. 3-4) and the branch combination (Sec. 3.1,
+ * Eq. 2) for every query i of every (sequence, head):
+ *   o_sr_i = softmax_{j in L_i}((R(i) q_i) . (R(j) k_j) / sqrt(d)) V_{L_i},
+ *   L_i = {j : 0 <= j <= i, i - j <= w} (a full window holds w + 1 tokens),
+ *   R(p) turning feature pair (2m, 2m+1) by p * rope_base^(-2m/d) (the RoPE
+ *   rotation of Su et al., which the page cites),
+ *   out_i = o_sr_i + alpha_h * o_lr_i when o_lr is given, else out_i = o_sr_i.
+ *   shape       batch, H, N, d, dtype as for the other calls
+ *   w           look-back radius, >= 0 (the page's w is 512)
+ *   rope_base   > 1 and finite (RoFormer's 10000 unless the model says otherwise)
+ *   q, k, v     device [batch, H, N, d] dtype, unrotated (the same q, k, v as the
+ *               long-range branch, which reads them unrotated)          (input)
+ *   alpha_h     host [H] fp32, finite; required when o_lr is given, else ignored
+ *   o_lr        device [batch, H, N, d] dtype: the long-range output (out of
+ *               fs_longrange_prefill), or NULL                          (input)
+ *   out         device [batch, H, N, d] dtype; may be the o_lr buffer (each row
+ *               is read before it is written)                           (output)
+ * Arithmetic: bf16 inputs are rotated in fp32 and kept as bf16 hi + lo parts
+ * (logits from three bf16 products with fp32 accumulation); fp32 inputs use
+ * fp32 products.  The softmax is exact up to rounding.
+ * Errors: FS_ERR_INVALID for a NULL q/k/v/out, w < 0, a bad rope_base, o_lr
+ * without alpha_h or a non-finite alpha; FS_ERR_UNSUPPORTED as for the shape.
+ */
+fs_status fs_local_window(const fs_shape *shape, int64_t w, float rope_base, const void *q, const void *k,
+                          const void *v, const float *alpha_h, const void *o_lr, void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
