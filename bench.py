@@ -30,11 +30,14 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "long-range FS-L query-tokens/s at 16k prefill; % HBM/MFMA roofline"
 DECODE_METRIC = "long-range FS-L decode query-tokens/s at a 262,144-token context; % HBM roofline"
+LOCAL_METRIC = "local RoPE window branch + branch combination query-tokens/s at 16k prefill (w=512); % HBM roofline"
+LOCAL_W = 512
 WORKLOADS = {
     "prefill_16k": dict(prune=True),
     "fs_32k": dict(prune=False),
     "prefill_4k": dict(prune=True),
     "decode_256k": dict(prune=True, decode=True),
+    "local_16k": dict(prune=True, local=True),
 }
 DECODE_PREFIX = 262144
 DECODE_LAYER_STATES = 12  # independent states in rotation: 12 x ~26 MB per step exceeds the 256 MB MALL
@@ -130,6 +133,8 @@ def main() -> int:
 
     if WORKLOADS[args.workload].get("decode"):
         return run_decode(args)
+    if WORKLOADS[args.workload].get("local"):
+        return run_local(args)
 
     w = synth.WORKLOADS[args.workload]
     prm = fsl.Params(prune=WORKLOADS[args.workload]["prune"])
@@ -323,6 +328,102 @@ def main() -> int:
         "settle_steps": settle,
         "single_call_ms": round(single_ms, 4),
         "single_call_matches_staged": same,
+        "parity_spot_check": parity,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_local(args) -> int:
+    """Local RoPE window branch with the branch combination (Eqs. 2-4) on the
+    headline prefill's inputs (b4 H16 d128 N16384 bf16), w = 512: one step is one
+    fs_local_window call that reads q, k, v and the long-range output (computed
+    once, untimed, by fs_longrange_prefill) and writes o_sr + alpha_h o_lr."""
+    import numpy as np
+    import torch
+
+    import cell_routed_long_amd as fsl
+    import synth
+
+    w = synth.WORKLOADS["prefill_16k"]
+    prm = fsl.Params()
+    dev = torch.device("cuda:0")
+    host = {x: synth.tensor(w, x) for x in "qkv"}
+    dq, dk, dv = (torch.from_numpy(host[x].view(np.int16)).view(torch.bfloat16).to(dev) for x in "qkv")
+    b, H, N, d = w.batch, w.H, w.N, w.d
+    o_lr, _, _ = fsl.prefill(dq, dk, dv, prm, want_sel=False)
+    alpha = [0.25 + 0.05 * h for h in range(H)]  # alpha_h is learned; the page gives no values
+    out = torch.empty_like(dq)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fsl.fs_local_window(dq, dk, dv, out, w=LOCAL_W, alpha=alpha, o_lr=o_lr)
+
+    settle_clocks(step)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = b * N / (ms * 1e-3)
+
+    # algorithmic work: q, k, v and o_lr read once, out written once; 4 d FLOP per (query, window token)
+    alg_bytes = 5 * b * H * N * d * 2
+    win = np.minimum(np.arange(N), LOCAL_W) + 1
+    alg_flop = float(b * H * 4 * d * win.sum())
+    t_hbm, t_mfma = alg_bytes / (HBM_PEAK_GBS * 1e9), alg_flop / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("local_window", "local_16k"), "kernel": "local_window",
+                "alg_bytes_per_launch": int(alg_bytes), "alg_tflop_per_launch": round(alg_flop / 1e12, 4),
+                "mfma_frac_algorithmic": round(alg_flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        threads = min(16, len(os.sched_getaffinity(0)))
+        heads = [(bb, h) for bb in range(b) for h in range(0, H, 4)]
+        rows = (N - 2048, N)  # full windows: every query reads w + 1 tokens
+        olr_h = o_lr.float().cpu().numpy()
+        al = np.asarray(alpha)
+
+        def one(bh):
+            bb, h = bh
+            return bh, oracle.local(synth.to_f64(host["q"][bb, h], "bf16"), synth.to_f64(host["k"][bb, h], "bf16"),
+                                    synth.to_f64(host["v"][bb, h], "bf16"), w=LOCAL_W, alpha=float(al[h]),
+                                    o_lr=olr_h[bb, h, rows[0]:rows[1]], i_lo=rows[0], i_hi=rows[1])
+
+        t1 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            refs = dict(ex.map(one, heads))
+        cpu_s = time.perf_counter() - t1
+        n_q = len(heads) * (rows[1] - rows[0]) / H
+        cpu = {"value": round(n_q / cpu_s, 1), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(heads)} of {b * H} (sequence, head) pairs, the last {rows[1] - rows[0]} queries each "
+                         f"({n_q:.0f} query-tokens); {cpu_s:.1f}s wall"}
+        got = out.float().cpu().numpy()
+        err = max(float(np.abs(got[bb, h, rows[0]:rows[1]] - r).max()) for (bb, h), r in refs.items())
+        rel = max(float((np.abs(got[bb, h, rows[0]:rows[1]] - r) / np.maximum(1.0, np.abs(r))).max())
+                  for (bb, h), r in refs.items())
+        parity = {"heads": len(heads), "rows": rows[1] - rows[0], "max_abs_err": err, "max_err_rel_to_max1": rel}
+        log(f"[bench] oracle {cpu_s:.1f}s on {threads} threads; parity {parity}")
+
+    result = {
+        "metric": LOCAL_METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "local RoPE window (w=512) + branch combination, b4 H16 d128 N16384 bf16",
+                   "batch": b, "heads": H, "seq_len": N, "head_dim": d, "w": LOCAL_W, "rope_base": 10000.0},
+        "roofline": roofline, "cpu_baseline": cpu, "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "parity_spot_check": parity,
     }
     print(json.dumps(result), flush=True)

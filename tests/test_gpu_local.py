@@ -25,6 +25,12 @@ def need_gpu():
     fsl.lib()
 
 
+# bf16 outputs of this branch are not RMS-normalised and, with alpha_h o_lr added,
+# can exceed 8, where one bf16 half-ulp alone is 2^-5: the bound is 2e-2 absolute
+# or 0.5% of the reference (about one bf16 ulp), whichever is larger.
+TOL_BF16_REL = 5e-3
+
+
 def check_rows(got, ref, dtype, what):
     got = got.astype(np.float64)
     if dtype == "f32":
@@ -33,8 +39,10 @@ def check_rows(got, ref, dtype, what):
         worst = int(np.argmax(err / tol))
         assert np.all(err <= tol), f"{what}: fp32 error {err[worst]:.3g} > {tol[worst]:.3g} at row {worst}"
     else:
+        tol = np.maximum(pu.TOL_BF16, TOL_BF16_REL * np.abs(ref))
         err = np.abs(got - ref)
-        assert err.max() <= pu.TOL_BF16, f"{what}: bf16 error {err.max():.3g}"
+        worst = np.unravel_index(int(np.argmax(err / tol)), err.shape)
+        assert np.all(err <= tol), f"{what}: bf16 error {err[worst]:.3g} > {tol[worst]:.3g} at {worst}"
 
 
 def run_case(w, win, base=10000.0, combine=False, in_place=False, heads=None, rows=None, seed=5):
