@@ -373,6 +373,12 @@ def run_local(args) -> int:
     wall = time.perf_counter() - wall0
     ms = ev0.elapsed_time(ev1) / args.steps
     value = b * N / (ms * 1e-3)
+    if args.copy_calibration:  # a 1 GiB copy whose bytes are known, for HBM counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # algorithmic work: q, k, v and o_lr read once, out written once; 4 d FLOP per (query, window token)
     alg_bytes = 5 * b * H * N * d * 2
@@ -391,8 +397,8 @@ def run_local(args) -> int:
         import oracle
         from concurrent.futures import ThreadPoolExecutor
         threads = min(16, len(os.sched_getaffinity(0)))
-        heads = [(bb, h) for bb in range(b) for h in range(0, H, 4)]
-        rows = (N - 2048, N)  # full windows: every query reads w + 1 tokens
+        heads = [(bb, h) for bb in range(b) for h in range(0, H, 2)]
+        rows = (N - 4096, N)  # full windows: every query reads w + 1 tokens
         olr_h = o_lr.float().cpu().numpy()
         al = np.asarray(alpha)
 
