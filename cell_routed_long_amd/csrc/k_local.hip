@@ -33,10 +33,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// V^T rows keep a tile's 32 tokens in the order 0-3, 8-11, 4-7, 12-15, 16-19,
-// 24-27, 20-23, 28-31, so the 8 tokens a lane feeds to one P.V product are 16
-// contiguous bytes (the order of its probabilities in the logits accumulator).
-__device__ __forceinline__ int vt_pos(int tok) { return tok ^ (((tok >> 2) ^ (tok >> 3)) & 1) * 12; }
 
 template <typename T, int D>
 struct LocalSmem;

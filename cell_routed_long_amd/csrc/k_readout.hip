@@ -35,11 +35,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// V^T rows keep a cell's 32 tokens in the order 0-3, 8-11, 4-7, 12-15, 16-19,
-// 24-27, 20-23, 28-31: then the 8 tokens a lane feeds to one P.V product
-// (16 kk + 4 half + 0..3 and 16 kk + 8 + 4 half + 0..3, the order of its
-// probabilities in the logits accumulator) are 16 contiguous bytes.
-__device__ __forceinline__ int vt_pos(int tok) { return tok ^ (((tok >> 2) ^ (tok >> 3)) & 1) * 12; }
 
 template <typename T, int D>
 struct ReadoutSmem;
