@@ -13,12 +13,13 @@
 // with an online softmax in which tokens outside a query's window get p = 0.
 // Only offsets matter (Eq. 3: R(i)^T R(j) = R(j - i)), so positions are taken
 // relative to the block start: every angle is below (w + 160) * theta_0, and
-// cos/sin of (32 a + b) theta_m come from two small tables (per tile: 32 a;
-// per workgroup: b < 32), built in fp64, by the angle-addition formulas.
+// cos/sin of (32 a + b) theta_m come from two small tables (per tile: 32 a,
+// stepped from the first tile by 32 theta_m; per workgroup: b < 32), built in
+// fp64, by the angle-addition formulas.
 //
 // Precision (bf16): the rotated q and k are split into bf16 hi + lo parts and
-// the logits take three products (lo.hi and hi.lo first, then hi.hi, in one
-// accumulator), so they keep ~16 mantissa bits; the probabilities are split
+// the logits take three products (lo.hi and hi.lo in one accumulator, hi.hi in
+// another, added at the end), so they keep ~16 mantissa bits; the probabilities are split
 // likewise for P.V.  With q and k rounded to bf16 after the rotation the
 // outputs of high-norm keys drift by up to 0.08 from the exact ones, and with
 // bf16 probabilities by up to 0.02.  fp32 tensors use the fp32 matrix cores
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
     __shared__ double s_theta[NP];
     __shared__ float2 s_row[32][NP];  // (cos, sin) of b theta_m, b < 32
     __shared__ float2 s_base[2][NP];  // (cos, sin) of a tile's offset times theta_m (double-buffered)
+    __shared__ float2 s_step[NP];     // (cos, sin) of 32 theta_m: one tile further
     __shared__ float2 s_qbase[4][NP]; // (cos, sin) of 32 a theta_m for the block's 128 query rows
 
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -120,11 +122,16 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
         s_row[e / NP][e % NP] = sincos_pair((double)(e / NP) * s_theta[e % NP]);
     for (int e = t; e < 4 * NP; e += kThreads)
         s_qbase[e / NP][e % NP] = sincos_pair((double)(32 * (e / NP)) * s_theta[e % NP]);
-    auto tile_base = [&](int x, int buf) { // offset of tile x from the block start, a multiple of 32
+    // tile x starts 32 x tokens after tile 0: its angles are tile 0's turned by 32 theta_m
+    // x times (fp32 angle additions; about 1e-6 relative after the ~20 tiles of a window)
+    if (t < NP) {
+        s_base[0][t] = sincos_pair((double)(t_lo - q0) * s_theta[t]);
+        s_step[t] = sincos_pair(32.0 * s_theta[t]);
+    }
+    auto tile_base = [&](int x, int buf) { // tile x from tile x - 1, whose angles are in buf ^ 1
         if (t < NP)
-            s_base[buf][t] = sincos_pair((double)(t_lo + 32 * (int64_t)x - q0) * s_theta[t]);
+            s_base[buf][t] = cs_add(s_base[buf ^ 1][t], s_step[t]);
     };
-    tile_base(0, 0);
     __syncthreads();
 
     // ---- rotated query fragments ----
@@ -277,22 +284,23 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
         // ---- logits S^T[32 tokens x 32 queries], tokens outside the window masked ----
         f32x16 acc;
         if constexpr (kBf16) {
+            f32x16 acc_s; // the small products (lo.hi, hi.lo); acc takes hi.hi: two interleaved chains
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < 16; ++r) {
                 acc[r] = 0.0f;
-            // the small products first, then the large one, in one accumulator
+                acc_s[r] = 0.0f;
+            }
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const bf16x8 kl = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.k[1][col][kc * 16 + half * 8]));
                 const bf16x8 kh = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.k[0][col][kc * 16 + half * 8]));
-                acc = mfma_bf16(kl, qf[kc], acc);
-                acc = mfma_bf16(kh, qf_lo[kc], acc);
+                acc_s = mfma_bf16(kl, qf[kc], acc_s);
+                acc = mfma_bf16(kh, qf[kc], acc);
+                acc_s = mfma_bf16(kh, qf_lo[kc], acc_s);
             }
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const bf16x8 kh = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.k[0][col][kc * 16 + half * 8]));
-                acc = mfma_bf16(kh, qf[kc], acc);
-            }
+            for (int r = 0; r < 16; ++r)
+                acc[r] += acc_s[r];
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r)

@@ -31,15 +31,17 @@ def need_gpu():
 TOL_BF16_REL = 5e-3
 
 
-def check_rows(got, ref, dtype, what):
+def check_rows(got, ref, dtype, what, lr_scale=0.0):
+    """lr_scale: alpha_h when the long-range output that was added came from the GPU
+    (within its own tolerance): Eq. 2 is linear, so its error adds, scaled by alpha_h."""
     got = got.astype(np.float64)
     if dtype == "f32":
-        tol = pu.TOL_F32 * np.maximum(1.0, np.abs(ref).max(axis=1))
+        tol = (1.0 + lr_scale) * pu.TOL_F32 * np.maximum(1.0, np.abs(ref).max(axis=1))
         err = np.abs(got - ref).max(axis=1)
         worst = int(np.argmax(err / tol))
         assert np.all(err <= tol), f"{what}: fp32 error {err[worst]:.3g} > {tol[worst]:.3g} at row {worst}"
     else:
-        tol = np.maximum(pu.TOL_BF16, TOL_BF16_REL * np.abs(ref))
+        tol = np.maximum(pu.TOL_BF16, TOL_BF16_REL * np.abs(ref)) + lr_scale * pu.TOL_BF16
         err = np.abs(got - ref)
         worst = np.unravel_index(int(np.argmax(err / tol)), err.shape)
         assert np.all(err <= tol), f"{what}: bf16 error {err[worst]:.3g} > {tol[worst]:.3g} at {worst}"
@@ -116,3 +118,29 @@ def test_local_rejects_bad_arguments():
         fsl.fs_local_window(q, q, q, q.clone(), rope_base=1.0)
     with pytest.raises(fsl.FslError):  # o_lr without alpha
         fsl.fs_local_window(q, q, q, q.clone(), o_lr=q)
+
+
+@pytest.mark.parametrize("w", [synth.WORKLOADS["prefill_4k"],
+                               synth.Workload(batch=1, H=2, N=2500, d=128, dtype="bf16", seed=111,
+                                              needle_frac=0.005)],
+                         ids=["cfg4k-f32", "bf16d128"])
+def test_full_attention_output_end_to_end(w):
+    """The whole FreeSolo attention output of Eq. 2: the long-range prefill's output
+    (Eqs. 5-9, 17) fed into the local branch with per-head alpha, against the oracle's
+    long-range output combined by the oracle's local branch (near-tie queries skipped)."""
+    p = fsl.Params()
+    host = pu.inputs(w)
+    dq, dk, dv = (pu.to_device(host[x], w.dtype) for x in "qkv")
+    alpha = np.linspace(0.5, 1.5, w.H).astype(np.float32)
+    print(f"[gpu] full attention output {w}", flush=True)
+    o_lr, _, _ = fsl.prefill(dq, dk, dv, p, want_sel=False)
+    fsl.fs_local_window(dq, dk, dv, o_lr, w=512, alpha=alpha, o_lr=o_lr)  # in place: o_lr becomes o
+    torch.cuda.synchronize()
+    got = o_lr.float().cpu().numpy()
+    heads = [(b, h) for b in range(w.batch) for h in range(w.H)]
+    refs = pu.run_oracle(w, host, p, heads)
+    for (b, h), ref in refs.items():
+        skip = pu.excluded_queries(ref, p, 0, w.N)
+        full = oracle.local(*(synth.to_f64(host[x][b, h], w.dtype) for x in "qkv"), w=512, alpha=float(alpha[h]),
+                            o_lr=ref["out"])
+        check_rows(got[b, h][~skip], full[~skip], w.dtype, f"full output b{b} h{h}", lr_scale=float(alpha[h]))
