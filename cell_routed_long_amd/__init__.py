@@ -79,8 +79,15 @@ def lib():
         L.fs_longrange_decode.argtypes = [P_prm, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                           vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.fs_local_window.argtypes = [P_shape, ctypes.c_int64, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp]
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        L.fs_local_state_bytes.argtypes = [i32, i32, i32, ctypes.c_int, i64]
+        L.fs_local_state_bytes.restype = sz
+        L.fs_local_state_build.argtypes = [i32, i32, i32, ctypes.c_int, i64, ctypes.c_float, vp, sz, vp, vp, i64,
+                                           i64, vp]
+        L.fs_local_decode.argtypes = [i32, i32, i32, ctypes.c_int, i64, vp, sz, vp, vp, vp, vp, vp, vp, vp]
         for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout",
-                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_decode", "fs_local_window"):
+                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_decode", "fs_local_window",
+                     "fs_local_state_build", "fs_local_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -281,3 +288,37 @@ def local(q, k, v, w: int = 512, rope_base: float = 10000.0, alpha=None, o_lr=No
     fs_local_window(q, k, v, out, w, rope_base, alpha, o_lr)
     return out
 
+
+
+def fs_local_state_bytes(batch: int, H: int, d: int, dtype_code: int, w: int = 512) -> int:
+    return int(lib().fs_local_state_bytes(batch, H, d, dtype_code, int(w)))
+
+
+def fs_local_state_build(state, k, v, pos: int, w: int = 512, rope_base: float = 10000.0, stream=None):
+    """Fill a local decode state (uint8 tensor of fs_local_state_bytes) from k, v [b,H,n,d]:
+    the raw keys and values at positions pos - n .. pos - 1 (n = 0 for an empty prefix)."""
+    b, Hh, n, d = k.shape
+    code = _dtype_code(k)
+    _check(lib().fs_local_state_build(b, Hh, d, code, int(w), float(rope_base), _ptr(state),
+                                      state.numel() * state.element_size(), _ptr(k), _ptr(v), n, int(pos),
+                                      _stream(stream)), "fs_local_state_build")
+
+
+def fs_local_decode(state, q, k_new, v_new, out, w: int = 512, alpha=None, o_lr=None, stream=None):
+    """One local-branch decode step for [batch, H, d] inputs into out; with o_lr and
+    alpha [H], out = o_sr + alpha_h * o_lr (Eq. 2).  out may be o_lr."""
+    b, H, d = q.shape
+    al = None if alpha is None else _floats(alpha, H)
+    _check(lib().fs_local_decode(b, H, d, _dtype_code(q), int(w), _ptr(state), state.numel() * state.element_size(),
+                                 _ptr(q), _ptr(k_new), _ptr(v_new), al, _ptr(o_lr), _ptr(out), _stream(stream)),
+           "fs_local_decode")
+
+
+def new_local_state(batch: int, H: int, d: int, dtype, w: int = 512, device="cuda"):
+    """A local decode-state buffer (uint8 tensor of fs_local_state_bytes)."""
+    import torch
+    code = FS_BF16 if dtype == torch.bfloat16 else FS_F32
+    n = fs_local_state_bytes(batch, H, d, code, w)
+    if n == 0:
+        raise FslError(FS_ERR_UNSUPPORTED, "fs_local_state_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)

@@ -199,6 +199,72 @@ size_t state_bytes_of(int32_t batch, int32_t H, const StateLayout &L)
     return (size_t)kStateHeaderBytes + (size_t)batch * H * (size_t)L.rec_bytes;
 }
 
+// ---- local-branch decode state ----
+constexpr int64_t kMaxLocalWindow = 65535; // ring of w + 1 <= 65536 tokens
+
+LocalStateLayout local_layout(int32_t d, fs_dtype dtype, int64_t w)
+{
+    LocalStateLayout L;
+    std::memset(&L, 0, sizeof(L));
+    const size_t esz = dtype == FS_BF16 ? 2 : 4;
+    L.R = w + 1;
+    L.off_table = kLocalStateHeaderBytes;
+    L.off_rec = (int64_t)align_up((size_t)L.off_table + (size_t)L.R * (size_t)(d / 2) * sizeof(float) * 2);
+    L.off_k = (int64_t)align_up(sizeof(int64_t));
+    L.off_v = (int64_t)align_up((size_t)L.off_k + (size_t)L.R * d * esz);
+    L.rec_bytes = (int64_t)align_up((size_t)L.off_v + (size_t)L.R * d * esz);
+    return L;
+}
+
+LocalStateHeader local_header(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w, float rope_base,
+                              const LocalStateLayout &L)
+{
+    LocalStateHeader h;
+    std::memset(&h, 0, sizeof(h));
+    h.magic = kLocalStateMagic;
+    h.version = kLocalStateVersion;
+    h.batch = batch;
+    h.H = H;
+    h.d = d;
+    h.dtype = (int32_t)dtype;
+    h.w = w;
+    h.rec_bytes = L.rec_bytes;
+    h.rope_base = rope_base;
+    return h;
+}
+
+fs_status check_local_dims(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w)
+{
+    fs_status st = check_decode_dims(batch, H, d, dtype);
+    if (st != FS_OK)
+        return st;
+    if (w < 0)
+        return FS_ERR_INVALID;
+    if (w > kMaxLocalWindow || (int64_t)batch * H > 65535)
+        return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
+size_t local_state_bytes_of(int32_t batch, int32_t H, const LocalStateLayout &L)
+{
+    return (size_t)L.off_rec + (size_t)batch * H * (size_t)L.rec_bytes;
+}
+
+// alpha_h of Eq. 2: required and finite when o_lr is given, else unused.
+fs_status local_alpha(int32_t H, const float *alpha_h, const void *o_lr, LocalConsts *lc)
+{
+    if (!o_lr)
+        return FS_OK;
+    if (!alpha_h)
+        return FS_ERR_INVALID;
+    for (int h = 0; h < H; ++h) {
+        if (!std::isfinite(alpha_h[h]))
+            return FS_ERR_INVALID;
+        lc->alpha[h] = alpha_h[h];
+    }
+    return FS_OK;
+}
+
 } // namespace
 } // namespace fsl
 
@@ -442,17 +508,58 @@ FSL_EXPORT fs_status fs_local_window(const fs_shape *shape, int64_t w, float rop
     LocalConsts lc;
     std::memset(&lc, 0, sizeof(lc));
     lc.rope_base = rope_base;
-    if (o_lr) {
-        if (!alpha_h)
-            return FS_ERR_INVALID;
-        for (int h = 0; h < shape->H; ++h) {
-            if (!std::isfinite(alpha_h[h]))
-                return FS_ERR_INVALID;
-            lc.alpha[h] = alpha_h[h];
-        }
-    }
+    st = local_alpha(shape->H, alpha_h, o_lr, &lc);
+    if (st != FS_OK)
+        return st;
     fs_params p{32, 128, 0, 0, 1, 0, 0.0f}; // only the block size matters here
     const Geometry g = geometry(shape, &p);
     return hip_status(launch_local(g, lc, w, q, k, v, o_lr, out, static_cast<hipStream_t>(stream)));
 }
 
+
+FSL_EXPORT size_t fs_local_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w)
+{
+    if (check_local_dims(batch, H, d, dtype, w) != FS_OK)
+        return 0;
+    return local_state_bytes_of(batch, H, local_layout(d, dtype, w));
+}
+
+FSL_EXPORT fs_status fs_local_state_build(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w,
+                                          float rope_base, void *state, size_t state_bytes, const void *k,
+                                          const void *v, int64_t n, int64_t pos, void *stream)
+{
+    fs_status st = check_local_dims(batch, H, d, dtype, w);
+    if (st != FS_OK)
+        return st;
+    if (!state || !(rope_base > 1.0f) || !std::isfinite(rope_base) || n < 0 || pos < n ||
+        n < (pos < w ? pos : w) || (n > 0 && (!k || !v)))
+        return FS_ERR_INVALID;
+    const LocalStateLayout L = local_layout(d, dtype, w);
+    if (state_bytes != local_state_bytes_of(batch, H, L))
+        return FS_ERR_STATE;
+    const LocalStateHeader hdr = local_header(batch, H, d, dtype, w, rope_base, L);
+    return hip_status(launch_local_state_build(batch * H, d, dtype == FS_BF16 ? 1 : 0, L, hdr, state, k, v, n, pos,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT fs_status fs_local_decode(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w, void *state,
+                                     size_t state_bytes, const void *q, const void *k_new, const void *v_new,
+                                     const float *alpha_h, const void *o_lr, void *out, void *stream)
+{
+    fs_status st = check_local_dims(batch, H, d, dtype, w);
+    if (st != FS_OK)
+        return st;
+    if (!state || !q || !k_new || !v_new || !out)
+        return FS_ERR_INVALID;
+    LocalConsts lc;
+    std::memset(&lc, 0, sizeof(lc));
+    st = local_alpha(H, alpha_h, o_lr, &lc);
+    if (st != FS_OK)
+        return st;
+    const LocalStateLayout L = local_layout(d, dtype, w);
+    if (state_bytes != local_state_bytes_of(batch, H, L))
+        return FS_ERR_STATE;
+    const LocalStateHeader expect = local_header(batch, H, d, dtype, w, 0.0f, L);
+    return hip_status(launch_local_decode(batch * H, H, d, dtype == FS_BF16 ? 1 : 0, L, expect, lc, state, q, k_new,
+                                          v_new, o_lr, out, static_cast<hipStream_t>(stream)));
+}

@@ -303,4 +303,32 @@ struct StateLayout {
     int64_t off_ridx, off_cell, off_flags, off_a, off_kbar, off_k, off_v; // offsets inside a record
 };
 
+
+// ---- streaming state of the local branch (one flat caller-owned buffer) ---
+// Layout: a LocalStateHeader padded to kLocalStateHeaderBytes; the rotation
+// table, R x d/2 float2 (cos, sin) of o * theta_m for offsets o = 0 .. R - 1,
+// shared by every record; then one record per (sequence, head), rec_bytes long:
+// the next position (int64, padded to 256 bytes), then a ring of R = w + 1 raw
+// keys and one of R raw values (token p in slot p mod R), each R x d of the
+// input dtype.
+constexpr uint32_t kLocalStateMagic = 0x314C4C46u; // "FLL1"
+constexpr uint32_t kLocalStateVersion = 1;
+constexpr int64_t kLocalStateHeaderBytes = 256;
+
+struct LocalStateHeader {
+    uint32_t magic, version;
+    int32_t batch, H, d, dtype;
+    int64_t w, rec_bytes;
+    float rope_base;
+    int32_t pad;
+};
+
+struct LocalStateLayout {
+    int64_t R;         // ring slots, w + 1
+    int64_t off_table; // from the start of the buffer
+    int64_t off_rec;   // first record, from the start of the buffer
+    int64_t rec_bytes; // bytes per (sequence, head) record
+    int64_t off_k, off_v; // inside a record
+};
+
 } // namespace fsl

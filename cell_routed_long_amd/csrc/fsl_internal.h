@@ -73,4 +73,15 @@ struct LocalConsts {
 hipError_t launch_local(const Geometry &g, const LocalConsts &lc, int64_t w, const void *q, const void *k,
                         const void *v, const void *o_lr, void *out, hipStream_t st);
 
+// Local-branch decode state: the rotation table and, for every (sequence, head),
+// the last min(n, w) of the n tokens given (positions pos - n .. pos - 1).
+hipError_t launch_local_state_build(int32_t bh, int32_t d, int32_t bf16, const LocalStateLayout &L,
+                                    const LocalStateHeader &hdr, void *state, const void *k, const void *v,
+                                    int64_t n, int64_t pos, hipStream_t st);
+
+// One local-branch decode step (plus alpha_h * o_lr when o_lr is not NULL) for bh records.
+hipError_t launch_local_decode(int32_t bh, int32_t H, int32_t d, int32_t bf16, const LocalStateLayout &L,
+                               const LocalStateHeader &expect, const LocalConsts &lc, void *state, const void *q,
+                               const void *k_new, const void *v_new, const void *o_lr, void *out, hipStream_t st);
+
 } // namespace fsl

@@ -279,6 +279,55 @@ fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, in
 fs_status fs_local_window(const fs_shape *shape, int64_t w, float rope_base, const void *q, const void *k,
                           const void *v, const float *alpha_h, const void *o_lr, void *out, void *stream);
 
+/*
+ * Size in bytes of the local branch's decode state for batch x H heads and
+ * look-back radius w (Sec. 3.2; the bounded decode cache of App. C keeps a
+ * local ring of the last w tokens).  Layout: a 256-byte header; a table of
+ * (cos, sin) of o * theta_m for o = 0 .. w and m < d/2 (fp32 pairs, shared by
+ * every head); then per (sequence, head) the next position (int64) and rings of
+ * w + 1 raw keys and w + 1 raw values of the dtype (token p in slot p mod
+ * (w + 1)).  0 for an unsupported or invalid combination (d not 64/128,
+ * H > FS_MAX_HEADS, w < 0 or w > 65535, batch * H > 65535).
+ */
+size_t fs_local_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w);
+
+/*
+ * Builds the local decode state for continuing at position pos.
+ *   w, rope_base  as for fs_local_window
+ *   state         device buffer of exactly fs_local_state_bytes() bytes (FS_ERR_STATE otherwise)
+ *   k, v          device [batch, H, n, d] dtype: the n raw (unrotated) keys and
+ *                 values at positions pos - n .. pos - 1 (a whole prompt: n = pos;
+ *                 its tail is enough: n >= min(pos, w)).  May be NULL when n = 0.
+ *   n, pos        0 <= min(pos, w) <= n <= pos
+ * Keeps the last min(n, w) tokens.  Errors: FS_ERR_INVALID for a NULL state, a
+ * bad rope_base or n, pos out of range.
+ */
+fs_status fs_local_state_build(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w, float rope_base,
+                               void *state, size_t state_bytes, const void *k, const void *v, int64_t n,
+                               int64_t pos, void *stream);
+
+/*
+ * One decode step of the local branch for the token at each record's next
+ * position i (Sec. 3.2, Eqs. 3-4, for the one query i; Sec. 3.1, Eq. 2):
+ *   o_sr = softmax_{j in [max(0, i - w), i]}(q_i . R(j - i) k_j / sqrt(d)) V,
+ *   out = o_sr + alpha_h * o_lr when o_lr is given, else out = o_sr;
+ * then k_new, v_new enter the ring and the position advances.  The result
+ * equals row i of fs_local_window over the whole sequence.
+ *   q, k_new, v_new  device [batch, H, d] dtype, unrotated              (input)
+ *   alpha_h          host [H] fp32, finite; required when o_lr is given
+ *   o_lr             device [batch, H, d] dtype (fs_longrange_decode's out), or NULL
+ *   out              device [batch, H, d] dtype; may be the o_lr buffer  (output)
+ * Arithmetic: fp32 (keys turned by the fp32 table, exact up to rounding).
+ * Errors: FS_ERR_STATE when state_bytes does not match; a buffer of the right
+ * size not built by fs_local_state_build for this shape and w is detected on
+ * the device: out is set to NaN and the buffer is left untouched.  One launch
+ * per step, no host synchronisation (steps can be captured in a HIP graph);
+ * steps on one state must be ordered.
+ */
+fs_status fs_local_decode(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w, void *state,
+                          size_t state_bytes, const void *q, const void *k_new, const void *v_new,
+                          const float *alpha_h, const void *o_lr, void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

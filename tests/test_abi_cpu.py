@@ -186,3 +186,57 @@ def test_prefill_state_validation(L):
     assert call(p.c(), n - 1) == fsl.FS_ERR_STATE
     assert call(p.c(), n, v=0) == fsl.FS_ERR_INVALID            # the state keeps raw values
     assert call(fsl.Params(prune=False).c(), n) == fsl.FS_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ local branch ----
+
+def test_local_state_bytes(L):
+    b, H, d, w = 32, 8, 128, 512
+    R = w + 1
+    align = lambda x: (x + 255) // 256 * 256
+    rec = 256 + align(R * d * 2) + align(R * d * 2)  # position, key ring, value ring
+    assert fsl.fs_local_state_bytes(b, H, d, fsl.FS_BF16, w) == 256 + align(R * (d // 2) * 8) + b * H * rec
+    assert fsl.fs_local_state_bytes(b, H, d, fsl.FS_F32, w) > fsl.fs_local_state_bytes(b, H, d, fsl.FS_BF16, w)
+    assert fsl.fs_local_state_bytes(b, H, d, fsl.FS_BF16, 0) > 0
+    for bad in [(b, H, d, fsl.FS_BF16, -1), (b, H, d, fsl.FS_BF16, 65536), (b, H, 96, fsl.FS_BF16, w),
+                (0, H, d, fsl.FS_BF16, w), (b, 129, d, fsl.FS_BF16, w), (b, H, d, 3, w)]:
+        assert fsl.fs_local_state_bytes(*bad) == 0
+
+
+def test_local_state_build_validation(L):
+    b, H, d, w = 1, 2, 64, 16
+    n_bytes = fsl.fs_local_state_bytes(b, H, d, fsl.FS_F32, w)
+    vp = ctypes.c_void_p
+
+    def call(n, pos, st_bytes=n_bytes, base=10000.0, state=1, k=1):
+        return L.fs_local_state_build(b, H, d, fsl.FS_F32, w, base, vp(state) if state else None, st_bytes,
+                                      vp(k) if k else None, vp(1), n, pos, None)
+
+    assert call(5, 4) == fsl.FS_ERR_INVALID            # more tokens than positions before pos
+    assert call(10, 100) == fsl.FS_ERR_INVALID         # fewer than the w tokens the window needs
+    assert call(3, 5) == fsl.FS_ERR_INVALID            # pos < w: all pos tokens are needed
+    assert call(-1, 0) == fsl.FS_ERR_INVALID
+    assert call(16, 100, base=1.0) == fsl.FS_ERR_INVALID
+    assert call(16, 100, state=0) == fsl.FS_ERR_INVALID
+    assert call(16, 100, k=0) == fsl.FS_ERR_INVALID
+    assert call(16, 100, st_bytes=n_bytes - 1) == fsl.FS_ERR_STATE
+
+
+def test_local_decode_validation(L):
+    b, H, d, w = 1, 2, 64, 16
+    n_bytes = fsl.fs_local_state_bytes(b, H, d, fsl.FS_F32, w)
+    vp = ctypes.c_void_p
+    alpha = (ctypes.c_float * H)(1.0, 1.0)
+    nan_alpha = (ctypes.c_float * H)(1.0, float("nan"))
+
+    def call(st_bytes=n_bytes, q=1, out=1, al=None, o_lr=None, ww=w):
+        return L.fs_local_decode(b, H, d, fsl.FS_F32, ww, vp(1), st_bytes, vp(q) if q else None, vp(1), vp(1), al,
+                                 vp(o_lr) if o_lr else None, vp(out) if out else None, None)
+
+    assert call(q=0) == fsl.FS_ERR_INVALID
+    assert call(out=0) == fsl.FS_ERR_INVALID
+    assert call(o_lr=1) == fsl.FS_ERR_INVALID           # o_lr without alpha_h
+    assert call(o_lr=1, al=nan_alpha) == fsl.FS_ERR_INVALID
+    assert call(st_bytes=n_bytes + 256) == fsl.FS_ERR_STATE
+    assert call(ww=-1) == fsl.FS_ERR_INVALID
+    assert call(ww=w + 1) == fsl.FS_ERR_STATE          # a state for another w has another size

@@ -25,28 +25,6 @@ def need_gpu():
     fsl.lib()
 
 
-# bf16 outputs of this branch are not RMS-normalised and, with alpha_h o_lr added,
-# can exceed 8, where one bf16 half-ulp alone is 2^-5: the bound is 2e-2 absolute
-# or 0.5% of the reference (about one bf16 ulp), whichever is larger.
-TOL_BF16_REL = 5e-3
-
-
-def check_rows(got, ref, dtype, what, lr_scale=0.0):
-    """lr_scale: alpha_h when the long-range output that was added came from the GPU
-    (within its own tolerance): Eq. 2 is linear, so its error adds, scaled by alpha_h."""
-    got = got.astype(np.float64)
-    if dtype == "f32":
-        tol = (1.0 + lr_scale) * pu.TOL_F32 * np.maximum(1.0, np.abs(ref).max(axis=1))
-        err = np.abs(got - ref).max(axis=1)
-        worst = int(np.argmax(err / tol))
-        assert np.all(err <= tol), f"{what}: fp32 error {err[worst]:.3g} > {tol[worst]:.3g} at row {worst}"
-    else:
-        tol = np.maximum(pu.TOL_BF16, TOL_BF16_REL * np.abs(ref)) + lr_scale * pu.TOL_BF16
-        err = np.abs(got - ref)
-        worst = np.unravel_index(int(np.argmax(err / tol)), err.shape)
-        assert np.all(err <= tol), f"{what}: bf16 error {err[worst]:.3g} > {tol[worst]:.3g} at {worst}"
-
-
 def run_case(w, win, base=10000.0, combine=False, in_place=False, heads=None, rows=None, seed=5):
     host = pu.inputs(w)
     dq, dk, dv = (pu.to_device(host[x], w.dtype) for x in "qkv")
@@ -72,7 +50,7 @@ def run_case(w, win, base=10000.0, combine=False, in_place=False, heads=None, ro
                            synth.to_f64(host["v"][b, h], w.dtype), w=win, rope_base=base,
                            alpha=0.0 if alpha is None else float(alpha[h]),
                            o_lr=None if olr_ref is None else olr_ref[b, h, lo:hi], i_lo=lo, i_hi=hi)
-        check_rows(got[b, h, lo:hi], ref, w.dtype, f"local b{b} h{h}")
+        pu.check_rows(got[b, h, lo:hi], ref, w.dtype, f"local b{b} h{h}")
 
 
 @pytest.mark.parametrize("w,win", [
@@ -143,4 +121,4 @@ def test_full_attention_output_end_to_end(w):
         skip = pu.excluded_queries(ref, p, 0, w.N)
         full = oracle.local(*(synth.to_f64(host[x][b, h], w.dtype) for x in "qkv"), w=512, alpha=float(alpha[h]),
                             o_lr=ref["out"])
-        check_rows(got[b, h][~skip], full[~skip], w.dtype, f"full output b{b} h{h}", lr_scale=float(alpha[h]))
+        pu.check_rows(got[b, h][~skip], full[~skip], w.dtype, f"full output b{b} h{h}", lr_scale=float(alpha[h]))
