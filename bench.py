@@ -31,6 +31,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "long-range FS-L query-tokens/s at 16k prefill; % HBM/MFMA roofline"
 DECODE_METRIC = "long-range FS-L decode query-tokens/s at a 262,144-token context; % HBM roofline"
 LOCAL_METRIC = "local RoPE window branch + branch combination query-tokens/s at 16k prefill (w=512); % HBM roofline"
+LOCAL_DECODE_METRIC = ("local RoPE window branch + branch combination decode query-tokens/s at a 262,144-token "
+                       "context (w=512); % HBM roofline")
 LOCAL_W = 512
 WORKLOADS = {
     "prefill_16k": dict(prune=True),
@@ -38,6 +40,7 @@ WORKLOADS = {
     "prefill_4k": dict(prune=True),
     "decode_256k": dict(prune=True, decode=True),
     "local_16k": dict(prune=True, local=True),
+    "local_decode_256k": dict(prune=True, local_decode=True),
 }
 DECODE_PREFIX = 262144
 DECODE_LAYER_STATES = 12  # independent states in rotation: 12 x ~26 MB per step exceeds the 256 MB MALL
@@ -133,6 +136,8 @@ def main() -> int:
 
     if WORKLOADS[args.workload].get("decode"):
         return run_decode(args)
+    if WORKLOADS[args.workload].get("local_decode"):
+        return run_local_decode(args)
     if WORKLOADS[args.workload].get("local"):
         return run_local(args)
 
@@ -646,6 +651,155 @@ def run_decode(args) -> int:
         "state_bytes": int(snap.numel()),
         "layer_states_agree": same_states,
         "parity_spot_check": parity,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_local_decode(args) -> int:
+    """Streaming decode of the local branch with the branch combination: b32 H8
+    d128 bf16 sequences at positions 262,144 onward, w = 512.  Each state is built
+    from the last 512 tokens before position 262,144 (all a step can read); a step
+    is one fs_local_decode call (one token for every sequence, out = o_sr +
+    alpha_h o_lr).  The timed region replays, as one HIP graph, `steps` token
+    steps over DECODE_LAYER_STATES independent states (as the layers of a model
+    would), so the per-step working set cannot stay in the last-level cache."""
+    import numpy as np
+    import torch
+
+    import cell_routed_long_amd as fsl
+    import synth
+
+    w = synth.WORKLOADS["decode_256k"]
+    dev = torch.device("cuda:0")
+    b, H, d, N0 = w.batch, w.H, w.d, DECODE_PREFIX
+    steps = min(args.steps, w.N - N0)
+    R = DECODE_LAYER_STATES
+    lo = N0 - LOCAL_W
+    stream = torch.cuda.current_stream()
+    host = {x: synth.tensor(w, x, lo, N0 + steps) for x in "qkv"}  # positions [lo, N0 + steps)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    dk, dv = to_dev(host["k"][:, :, :LOCAL_W]), to_dev(host["v"][:, :, :LOCAL_W])
+    steps_in = {x: to_dev(np.moveaxis(host[x][:, :, LOCAL_W:], 2, 0)) for x in "qkv"}  # [steps, b, H, d]
+    alpha = [0.25 + 0.05 * h for h in range(H)]  # alpha_h is learned; the page gives no values
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    o_lr = torch.randn(steps, b, H, d, generator=gen).to(torch.bfloat16).to(dev)  # stands in for the long-range out
+
+    snap = fsl.new_local_state(b, H, d, torch.bfloat16, w=LOCAL_W)
+    snap.zero_()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    fsl.fs_local_state_build(snap, dk, dv, pos=N0, w=LOCAL_W)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = ev0.elapsed_time(ev1)
+    states = [torch.empty_like(snap) for _ in range(R)]
+    outs = torch.empty(R, steps, b, H, d, dtype=torch.bfloat16, device=dev)
+
+    def restore():
+        for st in states:
+            st.copy_(snap)
+
+    def run(layer_states):
+        for t in range(steps):
+            for r in layer_states:
+                fsl.fs_local_decode(states[r], steps_in["q"][t], steps_in["k"][t], steps_in["v"][t], outs[r, t],
+                                    w=LOCAL_W, alpha=alpha, o_lr=o_lr[t])
+
+    restore()
+    for _ in range(max(1, args.warmup)):
+        run(range(R))
+        restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            run(range(R))
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+
+    def replay_all():
+        restore()
+        graph.replay()
+
+    settle = settle_clocks(replay_all)
+    restore()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    graph_ms = ev0.elapsed_time(ev1)
+    per_launch_ms = graph_ms / (steps * R)
+    out_h = outs[0].float().cpu().numpy()  # [steps, b, H, d]
+    same_states = bool(all(torch.equal(outs[r], outs[0]) for r in range(R)))
+    log(f"[bench] local decode graph: {graph_ms:.3f} ms for {steps} steps x {R} states = "
+        f"{per_launch_ms * 1e3:.2f} us per step and state (state build {build_ms:.3f} ms)")
+    if args.copy_calibration:  # a 1 GiB copy whose bytes are known, for HBM counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # algorithmic bytes per launch: the w ring keys and values of every (sequence, head);
+    # q, k_new, v_new, o_lr in, out written, the new row appended, the position; the
+    # rotation table (shared by every head) once
+    per_pair = LOCAL_W * d * 2 * 2 + 4 * d * 2 + d * 2 + 2 * d * 2 + 16
+    alg_bytes = b * H * per_pair + (LOCAL_W + 1) * (d // 2) * 8
+    achieved = alg_bytes / (per_launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("local_decode", "local_decode_256k"), "kernel": "local_decode",
+                "alg_bytes_per_launch": int(alg_bytes)}
+    value = b * steps * R / (graph_ms * 1e-3)
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        threads = min(16, len(os.sched_getaffinity(0)))
+        pairs = [(bb, h) for bb in range(b) for h in range(H)]
+        olr_h = np.moveaxis(o_lr.float().cpu().numpy(), 0, 2)  # [b, H, steps, d]
+
+        def one(bh):
+            bb, h = bh
+            # rows LOCAL_W .. LOCAL_W + steps of the window's frame are positions N0 .. N0 + steps
+            # (RoPE's relative form makes the result independent of the frame)
+            return bh, oracle.local(*(synth.to_f64(host[x][bb, h], "bf16") for x in "qkv"), w=LOCAL_W,
+                                    alpha=alpha[h], o_lr=olr_h[bb, h], i_lo=LOCAL_W, i_hi=LOCAL_W + steps)
+
+        # the whole step sample takes well under a second: repeat it for about 10 s of CPU work
+        t1 = time.perf_counter()
+        passes = 0
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            while passes == 0 or time.perf_counter() - t1 < 10.0:
+                refs = dict(ex.map(one, pairs))
+                passes += 1
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(passes * len(pairs) / H * steps / cpu_s, 1), "unit": "query-tokens/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"all {len(pairs)} (sequence, head) pairs, all {steps} decode positions each, from the "
+                         f"{LOCAL_W} tokens before position {N0}, {passes} passes; {cpu_s:.1f}s wall"}
+        err = max(float(np.abs(out_h[:, bb, hh] - r).max()) for (bb, hh), r in refs.items())
+        parity = {"heads": len(pairs), "steps": steps, "max_abs_err": err}
+        log(f"[bench] oracle {cpu_s:.1f}s on {threads} threads; parity {parity}")
+
+    result = {
+        "metric": LOCAL_DECODE_METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(graph_ms / steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": "local RoPE window (w=512) + branch combination decode, b32 H8 d128 bf16 at "
+                               "positions 262,144 onward", "batch": b, "heads": H, "prefix": N0, "head_dim": d,
+                   "w": LOCAL_W, "rope_base": 10000.0, "layer_states": R,
+                   "timing": "one HIP graph replay of steps x layer_states decode launches"},
+        "roofline": roofline, "cpu_baseline": cpu, "us_per_step_and_state": round(per_launch_ms * 1e3, 3),
+        "wall_ms": round(wall * 1e3, 3), "settle_replays": settle, "state_build_ms": round(build_ms, 3),
+        "state_bytes": int(snap.numel()), "layer_states_agree": same_states, "parity_spot_check": parity,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -200,19 +200,20 @@ size_t state_bytes_of(int32_t batch, int32_t H, const StateLayout &L)
 }
 
 // ---- local-branch decode state ----
-constexpr int64_t kMaxLocalWindow = 65535; // ring of w + 1 <= 65536 tokens
+constexpr int64_t kMaxLocalWindow = 65535; // ring of w tokens, table of w + 1 rows
 
 LocalStateLayout local_layout(int32_t d, fs_dtype dtype, int64_t w)
 {
     LocalStateLayout L;
     std::memset(&L, 0, sizeof(L));
     const size_t esz = dtype == FS_BF16 ? 2 : 4;
-    L.R = w + 1;
+    L.w = w;
+    L.slots = w > 0 ? w : 1;
     L.off_table = kLocalStateHeaderBytes;
-    L.off_rec = (int64_t)align_up((size_t)L.off_table + (size_t)L.R * (size_t)(d / 2) * sizeof(float) * 2);
+    L.off_rec = (int64_t)align_up((size_t)L.off_table + (size_t)(w + 1) * (size_t)(d / 2) * sizeof(float) * 2);
     L.off_k = (int64_t)align_up(sizeof(int64_t));
-    L.off_v = (int64_t)align_up((size_t)L.off_k + (size_t)L.R * d * esz);
-    L.rec_bytes = (int64_t)align_up((size_t)L.off_v + (size_t)L.R * d * esz);
+    L.off_v = (int64_t)align_up((size_t)L.off_k + (size_t)L.slots * d * esz);
+    L.rec_bytes = (int64_t)align_up((size_t)L.off_v + (size_t)L.slots * d * esz);
     return L;
 }
 

@@ -306,13 +306,13 @@ struct StateLayout {
 
 // ---- streaming state of the local branch (one flat caller-owned buffer) ---
 // Layout: a LocalStateHeader padded to kLocalStateHeaderBytes; the rotation
-// table, R x d/2 float2 (cos, sin) of o * theta_m for offsets o = 0 .. R - 1,
+// table, (w + 1) x d/2 float2 (cos, sin) of o * theta_m for offsets o = 0 .. w,
 // shared by every record; then one record per (sequence, head), rec_bytes long:
-// the next position (int64, padded to 256 bytes), then a ring of R = w + 1 raw
-// keys and one of R raw values (token p in slot p mod R), each R x d of the
-// input dtype.
+// the next position (int64, padded to 256 bytes), then a ring of the last w raw
+// keys and one of the last w raw values (token p in slot p mod w; one unused
+// slot when w = 0), each slots x d of the input dtype.
 constexpr uint32_t kLocalStateMagic = 0x314C4C46u; // "FLL1"
-constexpr uint32_t kLocalStateVersion = 1;
+constexpr uint32_t kLocalStateVersion = 2;
 constexpr int64_t kLocalStateHeaderBytes = 256;
 
 struct LocalStateHeader {
@@ -324,7 +324,8 @@ struct LocalStateHeader {
 };
 
 struct LocalStateLayout {
-    int64_t R;         // ring slots, w + 1
+    int64_t w;         // look-back radius: the table has w + 1 rows
+    int64_t slots;     // ring slots, max(w, 1)
     int64_t off_table; // from the start of the buffer
     int64_t off_rec;   // first record, from the start of the buffer
     int64_t rec_bytes; // bytes per (sequence, head) record

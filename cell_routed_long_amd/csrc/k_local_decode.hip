@@ -2,28 +2,33 @@
 // window moves one token per step) with the branch combination of Eq. 2.
 //
 // A step for the token at position i reads the window [max(0, i - w), i]: the
-// step's own k_new, v_new (offset o = 0) and the ring's tokens i - o for
-// 0 < o < min(i + 1, w + 1).  Logits take the relative form of Eq. 3,
-// q_i . R(-o) k_{i-o}, with R(-o) turning feature pair m by -o theta_m; the
-// cos/sin of o theta_m come from a table built once per state in fp64, so the
-// ring holds raw keys and no angle grows with the position.
+// step's own k_new, v_new (offset o = 0) and the ring's w slots, which hold
+// the tokens i - w .. i - 1 (offsets w .. 1; those before position 0 are
+// masked).  Logits take the relative form of Eq. 3, q_i . R(-o) k_{i-o} =
+// (R(o) q_i) . k_{i-o}, with R(o) turning feature pair m by o theta_m; the ring
+// holds raw keys, so no angle grows with the position.
 //
-// One workgroup per (sequence, head).  Sixteen lanes share a row (a token):
-// each holds d/16 features of its key, value and table entries, so a row is
-// one coalesced read per array.  Every group of 16 lanes runs its own online
-// softmax over its rows; the groups meet in LDS at the end.  Row loads of
-// kUnroll passes are issued before any of them is used.  Finally the new token
-// goes into slot i mod (w + 1), whose old token i - w - 1 is outside this and
-// every later window.
+// One workgroup of 512 threads per (sequence, head).  Sixteen lanes share a
+// row (a ring slot) and hold d/16 of its features, so a row is one coalesced
+// read per array; a group of 16 lanes owns kRows consecutive slots per pass,
+// and a pass of the 32 groups covers 32 kRows slots (the whole w = 512 ring for
+// bf16, every load of it in flight together).  The loads go by slot, so they do not wait for the position; the
+// offsets follow once it arrives.  Along a group's slots the offset falls by
+// one per slot, with one jump from 1 to w where the ring wraps: the group turns
+// the query once with the (cos, sin) table entry of its first offset (built in
+// fp64 with the state), then by -theta_m per slot, and takes R(w) q at the
+// wrap.  Every group runs an online softmax over its rows; the groups meet by
+// shuffles inside a wave and in LDS across waves.  The new token then replaces
+// the oldest one, in slot i mod w, after every read of the ring.
 #include "fsl_internal.h"
 
 namespace fsl {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kLanesPerRow = 16;
-constexpr int kGroups = kThreads / kLanesPerRow; // rows per pass of the workgroup
-constexpr int kUnroll = 4;                        // passes whose loads are in flight together
+constexpr int kGroups = kThreads / kLanesPerRow; // 32 groups of 16 lanes
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T x);
@@ -97,16 +102,26 @@ __global__ __launch_bounds__(256) void local_state_build_kernel(char *__restrict
     if (t == 0)
         *reinterpret_cast<int64_t *>(rec) = pos;
     constexpr int CPR = D * (int)sizeof(T) / 16; // 16-byte chunks per row
-    const int64_t keep = n < L.R - 1 ? n : L.R - 1;
+    const int64_t keep = n < L.w ? n : L.w;
     for (int64_t e = t; e < keep * CPR; e += 256) {
         const int64_t r = n - keep + e / CPR; // row of the given tokens; its position is pos - n + r
         const int ch = (int)(e % CPR);
-        const int64_t slot = (pos - n + r) % L.R;
+        const int64_t slot = (pos - n + r) % L.slots;
         reinterpret_cast<u32x4 *>(rec + L.off_k + slot * D * (int64_t)sizeof(T))[ch] =
             reinterpret_cast<const u32x4 *>(k + (bh * n + r) * D)[ch];
         reinterpret_cast<u32x4 *>(rec + L.off_v + slot * D * (int64_t)sizeof(T))[ch] =
             reinterpret_cast<const u32x4 *>(v + (bh * n + r) * D)[ch];
     }
+}
+
+// Sum over the 16 lanes of a DPP row, in every lane of the row.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_f<0xB1>(x);  // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);  // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x); // row_half_mirror
+    x += dpp_f<0x140>(x); // row_mirror
+    return x;
 }
 
 // ---- one step ----
@@ -119,142 +134,230 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
                                                                 const T *__restrict__ o_lr, T *__restrict__ out,
                                                                 int H)
 {
-    constexpr int FPL = D / kLanesPerRow;        // features per lane
+    constexpr int FPL = D / kLanesPerRow;         // features per lane
+    constexpr int NPL = FPL / 2;                  // feature pairs per lane
     constexpr int NDW = FPL * (int)sizeof(T) / 4; // dwords of a lane's key (or value) features
     constexpr int NP = D / 2;
+    constexpr int kRows = 32 / (int)sizeof(T);    // slots per group and pass (16 bf16, 8 fp32)
+    constexpr int kPass = kGroups * kRows;        // slots per pass
     static_assert(FPL % 2 == 0, "whole feature pairs per lane");
 
-    __shared__ float s_knew[D], s_vnew[D];
-    __shared__ float s_m[kGroups], s_l[kGroups];
-    __shared__ float s_acc[kGroups][D + 1];
+    __shared__ float s_m[kWaves], s_l[kWaves];
+    __shared__ float s_acc[kWaves][D + 1];
 
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
     const int grp = t / kLanesPerRow, part = t % kLanesPerRow;
+    const int64_t w = L.w;
     char *rec = state + L.off_rec + bh * L.rec_bytes; // in bounds: the host checked the buffer size
+    const int64_t lane_off = part * FPL * (int64_t)sizeof(T);
+    const char *kring = rec + L.off_k + lane_off;
+    const char *vring = rec + L.off_v + lane_off;
+    const char *tab = state + L.off_table + part * NPL * (int64_t)sizeof(float2);
+    const float scale = 1.4426950408889634f / sqrtf((float)D); // log2(e) / sqrt(d): exp2 domain
+
+    // Nothing waits for memory before a pass's ring rows are requested, and
+    // nothing branches on the header: every address here lies inside the buffer
+    // whatever the header holds, and a foreign header only changes what is
+    // written at the end.
     const LocalStateHeader hv = *reinterpret_cast<const LocalStateHeader *>(state);
     const int64_t i = *reinterpret_cast<const int64_t *>(rec);
-    const int bad = (int)(hv.magic != kLocalStateMagic) | (int)(hv.version != kLocalStateVersion) |
-                    (int)(hv.batch != expect.batch) | (int)(hv.H != expect.H) | (int)(hv.d != D) |
-                    (int)(hv.dtype != expect.dtype) | (int)(hv.w != expect.w) |
-                    (int)(hv.rec_bytes != expect.rec_bytes) | (int)(i < 0);
-    T *o_row = out + bh * D;
-    if (bad) { // not a state of this shape: flag the output, leave the state alone
-        if (t < D) {
-            if constexpr (sizeof(T) == 2)
-                o_row[t] = (T)0x7fc0u; // bf16 quiet NaN
-            else
-                o_row[t] = __uint_as_float(0x7fc00000u);
-        }
-        return;
-    }
-    const int64_t R = L.R;
-    const int64_t nwin = i + 1 < R ? i + 1 : R; // offsets 0 .. nwin - 1
-    const int64_t slot0 = i % R;
-    if (t < D) {
-        s_knew[t] = to_f32<T>(k_new[bh * D + t]);
-        s_vnew[t] = to_f32<T>(v_new[bh * D + t]);
-    }
-    float qf[FPL];
-#pragma unroll
-    for (int e = 0; e < FPL; ++e)
-        qf[e] = to_f32<T>(q[bh * D + part * FPL + e]);
-    __syncthreads();
+    uint32_t qr[NDW], kr0[NDW], vr0[NDW], stp[FPL], cw[FPL];
+    load_dwords<NDW>(reinterpret_cast<const char *>(q + bh * D) + lane_off, qr);
+    load_dwords<NDW>(reinterpret_cast<const char *>(k_new + bh * D) + lane_off, kr0);
+    load_dwords<NDW>(reinterpret_cast<const char *>(v_new + bh * D) + lane_off, vr0);
+    load_dwords<FPL>(tab + (w > 0 ? 1 : 0) * NP * (int64_t)sizeof(float2), stp); // (cos, sin) of theta_m
+    load_dwords<FPL>(tab + w * NP * (int64_t)sizeof(float2), cw);                // of w theta_m
+    // what the epilogue writes or adds, element t: requested now, not after the softmax
+    const int te = t < D ? t : 0;
+    const T olr_t = o_lr ? o_lr[bh * D + te] : T(0);
+    const T kn_t = k_new[bh * D + te], vn_t = v_new[bh * D + te];
 
-    const char *kring = rec + L.off_k + part * FPL * (int64_t)sizeof(T);
-    const char *vring = rec + L.off_v + part * FPL * (int64_t)sizeof(T);
-    const char *tab = state + L.off_table + part * (FPL / 2) * (int64_t)sizeof(float2);
-    const float scale = 1.4426950408889634f / sqrtf((float)D); // log2(e) / sqrt(d): exp2 domain
+    // slot of token i - 1 (offset 1); slots of offsets above min(i, w) hold no token yet.
+    // Slots and offsets fit in 32 bits: w <= 65535.
+    const int wi = (int)w;
+    const int64_t i_nn = i > 0 ? i : 0;
+    const int last = (int)((i_nn + w - 1) % L.slots);
+    const int n_valid = (int)(i_nn < w ? i_nn : w);
+    // offset of slot s: last - s + 1, or that plus w past the wrap (always in 1 .. w)
+    auto offset_of = [&](int sl) { return sl <= last ? last - sl + 1 : last - sl + 1 + wi; };
+    constexpr int kHalf = kRows / 2; // rows per softmax update
+
     float m = -INFINITY, l = 0.0f, acc[FPL];
 #pragma unroll
     for (int e = 0; e < FPL; ++e)
         acc[e] = 0.0f;
 
-    for (int64_t base = 0; base < nwin; base += kGroups * kUnroll) {
-        uint32_t kr[kUnroll][NDW], vr[kUnroll][NDW], cr[kUnroll][FPL];
-        int64_t orow[kUnroll];
+    for (int base = 0; base < wi; base += kPass) {
+        // the pass's rows and the angle of the group's first offset are requested
+        // before anything waits for memory
+        const int s0 = base + grp * kRows; // the group's first slot in this pass
+        uint32_t kr[kRows][NDW], vr[kRows][NDW], c0[FPL];
+        // (loads complete in issue order: the angle goes between the two halves, so
+        // the first half's rows can be used while the second half arrives)
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t o = base + u * kGroups + grp;
-            orow[u] = o;
-            const int64_t oc = o < nwin ? o : 0; // rows past the window read offset 0 (in bounds, unused)
-            int64_t slot = slot0 - oc;
-            slot += slot < 0 ? R : 0;
-            load_dwords<NDW>(kring + slot * D * (int64_t)sizeof(T), kr[u]);
-            load_dwords<NDW>(vring + slot * D * (int64_t)sizeof(T), vr[u]);
-            load_dwords<FPL>(tab + oc * NP * (int64_t)sizeof(float2), cr[u]);
+        for (int u = 0; u < kRows; ++u) {
+            if (u == kRows / 2)
+                load_dwords<FPL>(tab + (int64_t)offset_of(s0 < wi ? s0 : 0) * NP * (int64_t)sizeof(float2), c0);
+            const int sc = s0 + u < wi ? s0 + u : 0; // slots past the ring read slot 0 (in bounds, unused)
+            load_dwords<NDW>(kring + (int64_t)sc * D * (int64_t)sizeof(T), kr[u]);
+            load_dwords<NDW>(vring + (int64_t)sc * D * (int64_t)sizeof(T), vr[u]);
         }
-        float x[kUnroll];
-        float mx = m;
+        __builtin_amdgcn_sched_barrier(0);
+        // q and the angle w theta_m are loop-invariant; these empty asm statements
+        // keep their use (and the wait for them) here, behind the pass's loads,
+        // instead of hoisted in front of the loop
+        uint32_t qv[NDW], cwv[FPL];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bool fresh = orow[u] == 0; // the step's own token, not yet in the ring
-            float dot = 0.0f;
+        for (int e = 0; e < NDW; ++e) {
+            qv[e] = qr[e];
+            asm volatile("" : "+v"(qv[e]));
+        }
 #pragma unroll
-            for (int p = 0; p < FPL / 2; ++p) {
-                const float c = __uint_as_float(cr[u][2 * p]), sn = __uint_as_float(cr[u][2 * p + 1]);
-                const float k0 = fresh ? s_knew[part * FPL + 2 * p] : feature<T, NDW>(kr[u], 2 * p);
-                const float k1 = fresh ? s_knew[part * FPL + 2 * p + 1] : feature<T, NDW>(kr[u], 2 * p + 1);
-                // q . R(-o) k with R(-o)(k0, k1) = (k0 c + k1 s, -k0 s + k1 c)
-                dot = fmaf(qf[2 * p], fmaf(k0, c, k1 * sn), dot);
-                dot = fmaf(qf[2 * p + 1], fmaf(-k0, sn, k1 * c), dot);
+        for (int e = 0; e < FPL; ++e) {
+            cwv[e] = cw[e];
+            asm volatile("" : "+v"(cwv[e]));
+        }
+
+        // R(o0) q for the first offset; R(w) q, taken where the slots wrap from offset 1 to w
+        float qx[NPL], qy[NPL], wx[NPL], wy[NPL];
+#pragma unroll
+        for (int p = 0; p < NPL; ++p) {
+            const float q0 = feature<T, NDW>(qv, 2 * p), q1 = feature<T, NDW>(qv, 2 * p + 1);
+            const float c = __uint_as_float(c0[2 * p]), sn = __uint_as_float(c0[2 * p + 1]);
+            qx[p] = fmaf(q0, c, -q1 * sn);
+            qy[p] = fmaf(q0, sn, q1 * c);
+            const float cwc = __uint_as_float(cwv[2 * p]), cws = __uint_as_float(cwv[2 * p + 1]);
+            wx[p] = fmaf(q0, cwc, -q1 * cws);
+            wy[p] = fmaf(q0, cws, q1 * cwc);
+        }
+#pragma unroll
+        for (int hh = 0; hh < kRows; hh += kHalf) {
+            float x[kHalf];
+            float mx = m;
+#pragma unroll
+            for (int uu = 0; uu < kHalf; ++uu) {
+                const int u = hh + uu;
+                const int s = s0 + u;
+                if (u > 0) { // offset of slot s: one less than slot s - 1's, or w at the wrap
+                    const bool wrap = s == last + 1;
+#pragma unroll
+                    for (int p = 0; p < NPL; ++p) {
+                        const float c = __uint_as_float(stp[2 * p]), sn = __uint_as_float(stp[2 * p + 1]);
+                        const float nx = fmaf(qx[p], c, qy[p] * sn); // R(-1)
+                        const float ny = fmaf(-qx[p], sn, qy[p] * c);
+                        qx[p] = wrap ? wx[p] : nx;
+                        qy[p] = wrap ? wy[p] : ny;
+                    }
+                }
+                float dot = 0.0f;
+#pragma unroll
+                for (int p = 0; p < NPL; ++p) {
+                    dot = fmaf(qx[p], feature<T, NDW>(kr[u], 2 * p), dot);
+                    dot = fmaf(qy[p], feature<T, NDW>(kr[u], 2 * p + 1), dot);
+                }
+                dot = row16_sum(dot);
+                x[uu] = (s < wi && offset_of(s) <= n_valid) ? dot * scale : -INFINITY;
+                mx = fmaxf(mx, x[uu]);
+            }
+            if (mx > m) { // the group's running maximum grows: rescale what it holds
+                const float f = exp2f(m - mx);
+                l *= f;
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    acc[e] *= f;
+                m = mx;
             }
 #pragma unroll
-            for (int msk = 1; msk < kLanesPerRow; msk <<= 1)
-                dot += __shfl_xor(dot, msk, kWave);
-            x[u] = orow[u] < nwin ? dot * scale : -INFINITY;
-            mx = fmaxf(mx, x[u]);
-        }
-        if (mx > m) { // the group's running maximum grows: rescale what it holds
-            const float f = exp2f(m - mx);
-            l *= f;
+            for (int uu = 0; uu < kHalf; ++uu) {
+                const float p = x[uu] == -INFINITY ? 0.0f : exp2f(x[uu] - m);
+                l += p;
 #pragma unroll
-            for (int e = 0; e < FPL; ++e)
-                acc[e] *= f;
-            m = mx;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bool fresh = orow[u] == 0;
-            const float p = orow[u] < nwin ? exp2f(x[u] - m) : 0.0f;
-            l += p;
-#pragma unroll
-            for (int e = 0; e < FPL; ++e) {
-                const float vv = fresh ? s_vnew[part * FPL + e] : feature<T, NDW>(vr[u], e);
-                acc[e] = fmaf(p, vv, acc[e]);
+                for (int e = 0; e < FPL; ++e)
+                    acc[e] = fmaf(p, feature<T, NDW>(vr[hh + uu], e), acc[e]);
             }
         }
     }
 
-    // the groups' partial softmaxes meet (a group without rows has m = -inf and weight 0)
+    // offset 0, the step's own token, joins group 0's softmax
+    {
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < FPL; ++e)
+            dot = fmaf(feature<T, NDW>(qr, e), feature<T, NDW>(kr0, e), dot);
+        dot = row16_sum(dot);
+        if (grp == 0) {
+            const float x0 = dot * scale;
+            const float mx = fmaxf(m, x0);
+            const float f = m == -INFINITY ? 0.0f : exp2f(m - mx), p0 = exp2f(x0 - mx);
+            l = fmaf(l, f, p0);
+#pragma unroll
+            for (int e = 0; e < FPL; ++e)
+                acc[e] = fmaf(acc[e], f, p0 * feature<T, NDW>(vr0, e));
+            m = mx;
+        }
+    }
+
+    // the four groups of a wave meet (a group without rows has m = -inf and weight 0)
+    float M = fmaxf(m, __shfl_xor(m, 16, kWave));
+    M = fmaxf(M, __shfl_xor(M, 32, kWave));
+    const float f = m == -INFINITY ? 0.0f : exp2f(m - M);
+    l *= f;
 #pragma unroll
     for (int e = 0; e < FPL; ++e)
-        s_acc[grp][part * FPL + e] = acc[e];
-    if (part == 0) {
-        s_m[grp] = m;
-        s_l[grp] = l;
+        acc[e] *= f;
+#pragma unroll
+    for (int msk = 16; msk < kWave; msk <<= 1) {
+        l += __shfl_xor(l, msk, kWave);
+#pragma unroll
+        for (int e = 0; e < FPL; ++e)
+            acc[e] += __shfl_xor(acc[e], msk, kWave);
+    }
+    if (lane < kLanesPerRow) {
+#pragma unroll
+        for (int e = 0; e < FPL; ++e)
+            s_acc[wave][part * FPL + e] = acc[e];
+        if (lane == 0) {
+            s_m[wave] = M;
+            s_l[wave] = l;
+        }
     }
     __syncthreads();
+
+    const bool bad = hv.magic != kLocalStateMagic || hv.version != kLocalStateVersion || hv.batch != expect.batch ||
+                     hv.H != expect.H || hv.d != D || hv.dtype != expect.dtype || hv.w != expect.w ||
+                     hv.rec_bytes != expect.rec_bytes || i < 0;
+    T *o_row = out + bh * D;
     if (t < D) {
-        float M = s_m[0]; // group 0 holds offset 0, so M is finite
+        float Mw = s_m[0]; // wave 0 holds offset 0, so Mw is finite
 #pragma unroll
-        for (int g = 1; g < kGroups; ++g)
-            M = fmaxf(M, s_m[g]);
+        for (int g = 1; g < kWaves; ++g)
+            Mw = fmaxf(Mw, s_m[g]);
         float z = 0.0f, u = 0.0f;
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-            const float f = exp2f(s_m[g] - M);
-            z = fmaf(s_l[g], f, z);
-            u = fmaf(s_acc[g][t], f, u);
+        for (int g = 0; g < kWaves; ++g) {
+            const float fw = exp2f(s_m[g] - Mw);
+            z = fmaf(s_l[g], fw, z);
+            u = fmaf(s_acc[g][t], fw, u);
         }
         u /= z;
-        const float y = o_lr ? fmaf(lc.alpha[h], to_f32<T>(o_lr[bh * D + t]), u) : u;
-        o_row[t] = from_f32<T>(y);
-        reinterpret_cast<T *>(rec + L.off_k)[slot0 * D + t] = k_new[bh * D + t];
-        reinterpret_cast<T *>(rec + L.off_v)[slot0 * D + t] = v_new[bh * D + t];
+        const float y = o_lr ? fmaf(lc.alpha[h], to_f32<T>(olr_t), u) : u;
+        if (bad) { // not a state of this shape: flag the output, leave the state alone
+            if constexpr (sizeof(T) == 2)
+                o_row[t] = (T)0x7fc0u; // bf16 quiet NaN
+            else
+                o_row[t] = __uint_as_float(0x7fc00000u);
+        } else {
+            o_row[t] = from_f32<T>(y);
+            if (w > 0) { // the new token replaces token i - w, read above for the last time
+                const int64_t slot = i % w;
+                reinterpret_cast<T *>(rec + L.off_k)[slot * D + t] = kn_t;
+                reinterpret_cast<T *>(rec + L.off_v)[slot * D + t] = vn_t;
+            }
+        }
     }
-    if (t == 0)
+    if (t == 0 && !bad)
         *reinterpret_cast<int64_t *>(rec) = i + 1;
 }
 
@@ -287,9 +390,9 @@ hipError_t launch_local_state_build(int32_t bh, int32_t d, int32_t bf16, const L
                                     int64_t n, int64_t pos, hipStream_t st)
 {
     const int NP = d / 2;
-    const int64_t entries = L.R * NP;
+    const int64_t entries = (L.w + 1) * NP;
     hipLaunchKernelGGL(local_table_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, st,
-                       reinterpret_cast<float2 *>(static_cast<char *>(state) + L.off_table), L.R, NP, d,
+                       reinterpret_cast<float2 *>(static_cast<char *>(state) + L.off_table), L.w + 1, NP, d,
                        hdr.rope_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -285,8 +285,8 @@ fs_status fs_local_window(const fs_shape *shape, int64_t w, float rope_base, con
  * local ring of the last w tokens).  Layout: a 256-byte header; a table of
  * (cos, sin) of o * theta_m for o = 0 .. w and m < d/2 (fp32 pairs, shared by
  * every head); then per (sequence, head) the next position (int64) and rings of
- * w + 1 raw keys and w + 1 raw values of the dtype (token p in slot p mod
- * (w + 1)).  0 for an unsupported or invalid combination (d not 64/128,
+ * the last w raw keys and the last w raw values of the dtype (token p in slot
+ * p mod w; one unused slot when w = 0).  0 for an unsupported or invalid combination (d not 64/128,
  * H > FS_MAX_HEADS, w < 0 or w > 65535, batch * H > 65535).
  */
 size_t fs_local_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w);

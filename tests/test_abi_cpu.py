@@ -192,10 +192,10 @@ def test_prefill_state_validation(L):
 
 def test_local_state_bytes(L):
     b, H, d, w = 32, 8, 128, 512
-    R = w + 1
     align = lambda x: (x + 255) // 256 * 256
-    rec = 256 + align(R * d * 2) + align(R * d * 2)  # position, key ring, value ring
-    assert fsl.fs_local_state_bytes(b, H, d, fsl.FS_BF16, w) == 256 + align(R * (d // 2) * 8) + b * H * rec
+    rec = 256 + align(w * d * 2) + align(w * d * 2)  # position, rings of the last w keys and values
+    # header, (cos, sin) table of offsets 0 .. w, records
+    assert fsl.fs_local_state_bytes(b, H, d, fsl.FS_BF16, w) == 256 + align((w + 1) * (d // 2) * 8) + b * H * rec
     assert fsl.fs_local_state_bytes(b, H, d, fsl.FS_F32, w) > fsl.fs_local_state_bytes(b, H, d, fsl.FS_BF16, w)
     assert fsl.fs_local_state_bytes(b, H, d, fsl.FS_BF16, 0) > 0
     for bad in [(b, H, d, fsl.FS_BF16, -1), (b, H, d, fsl.FS_BF16, 65536), (b, H, 96, fsl.FS_BF16, w),
