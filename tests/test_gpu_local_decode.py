@@ -80,7 +80,11 @@ def check_steps(w, host, win, N0, T, got, olr, alpha, lo=0, base=10000.0, heads=
     (synth.Workload(batch=1, H=2, N=150, d=128, dtype="f32", seed=204), 512, 20, 130),   # window never full
     (synth.Workload(batch=1, H=2, N=40, d=128, dtype="bf16", seed=205), 7, 0, 40),       # empty prefix, many wraps
     (synth.Workload(batch=1, H=2, N=30, d=64, dtype="f32", seed=206), 0, 10, 20),        # w = 0: o_i = v_i
-], ids=["bf16d128-w512", "bf16d64-w100-wrap", "f32d64-w64", "f32d128-short", "empty-prefix-w7", "w0"])
+    (synth.Workload(batch=1, H=2, N=1600, d=128, dtype="bf16", seed=211), 1100, 1500, 100),  # three passes
+    (synth.Workload(batch=1, H=2, N=900, d=128, dtype="f32", seed=212), 300, 820, 80),   # two passes, full
+    (synth.Workload(batch=1, H=2, N=700, d=64, dtype="bf16", seed=213), 515, 300, 300),  # fills past one pass
+], ids=["bf16d128-w512", "bf16d64-w100-wrap", "f32d64-w64", "f32d128-short", "empty-prefix-w7", "w0",
+        "bf16d128-w1100", "f32d128-w300", "bf16d64-w515-fill"])
 def test_local_decode_stream(w, win, N0, T):
     host = pu.inputs(w)
     got, olr, alpha, _, _ = run_steps(w, host, win, N0, T)
@@ -173,3 +177,11 @@ def test_local_decode_rejects_foreign_state():
     # a state for another w has another size: rejected on the host
     with pytest.raises(fsl.FslError):
         fsl.fs_local_decode(state, q, q, q, out, w=win + 1)
+
+
+def test_local_decode_largest_window():
+    """w = 65535, the largest window the ABI accepts (a 65,536-row table and rings)."""
+    w = synth.Workload(batch=1, H=1, N=65540, d=64, dtype="f32", seed=214)
+    host = pu.inputs(w)
+    got, olr, alpha, _, _ = run_steps(w, host, 65535, 65537, 3)
+    check_steps(w, host, 65535, 65537, 3, got, olr, alpha)
