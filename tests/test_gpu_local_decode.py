@@ -185,3 +185,40 @@ def test_local_decode_largest_window():
     host = pu.inputs(w)
     got, olr, alpha, _, _ = run_steps(w, host, 65535, 65537, 3)
     check_steps(w, host, 65535, 65537, 3, got, olr, alpha)
+
+
+def test_full_attention_decode_output():
+    """The whole FreeSolo attention output at decode (Eq. 2): every step's long-range
+    output (fs_longrange_decode: Eqs. 5-9, 15, 17) is fed into the local decode with a
+    per-head alpha, against the oracle's long-range rows combined by the oracle's local
+    branch.  Steps whose long-range selection is decided by a near-tie are skipped;
+    the long-range output's own tolerance is added, scaled by alpha_h (Eq. 2 is linear)."""
+    w = synth.Workload(batch=2, H=2, N=1400, d=128, dtype="bf16", seed=215, needle_frac=0.01)
+    p = fsl.Params(P=6, W=2)
+    N0, T, win = 1000, 120, 512
+    host = pu.inputs(w)
+    dk, dv = (pu.to_device(np.ascontiguousarray(host[x][:, :, :N0]), w.dtype) for x in "kv")
+    print(f"[gpu] full attention decode {w} {p} N0={N0} T={T} w={win}", flush=True)
+    lr_state = fsl.new_state(w.batch, w.H, w.d, torch.bfloat16, p)
+    fsl.prefill(None, dk, dv, p, want_out=False, want_sel=False, state=lr_state)
+    loc_state = fsl.new_local_state(w.batch, w.H, w.d, torch.bfloat16, w=win)
+    fsl.fs_local_state_build(loc_state, dk, dv, pos=N0, w=win)
+    st = {x: steps_of(host[x][:, :, N0:N0 + T], w.dtype) for x in "qkv"}
+    alpha = np.linspace(0.5, 1.5, w.H).astype(np.float32)
+    outs = torch.empty(T, w.batch, w.H, w.d, dtype=torch.bfloat16, device="cuda")
+    for t in range(T):
+        o_lr, _ = fsl.decode(lr_state, st["q"][t], st["k"][t], st["v"][t], p, want_sel=False)
+        fsl.fs_local_decode(loc_state, st["q"][t], st["k"][t], st["v"][t], outs[t], w=win, alpha=alpha, o_lr=o_lr)
+    torch.cuda.synchronize()
+    got = np.moveaxis(outs.float().cpu().numpy(), 0, 2)
+    heads = [(b, h) for b in range(w.batch) for h in range(w.H)]
+    refs = pu.run_oracle(w, host, p, heads, i_lo=N0, i_hi=N0 + T)
+    skipped = 0
+    for (b, h), ref in refs.items():
+        skip = pu.excluded_queries(ref, p, N0, T)
+        skipped += int(skip.sum())
+        full = oracle.local(*(synth.to_f64(host[x][b, h], w.dtype) for x in "qkv"), w=win, alpha=float(alpha[h]),
+                            o_lr=ref["out"], i_lo=N0, i_hi=N0 + T)
+        pu.check_rows(got[b, h][~skip], full[~skip], w.dtype, f"full decode output b{b} h{h}",
+                      lr_scale=float(alpha[h]))
+    assert skipped <= 0.01 * len(heads) * T
