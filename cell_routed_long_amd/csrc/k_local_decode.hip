@@ -11,15 +11,16 @@
 // One workgroup of 512 threads per (sequence, head).  Sixteen lanes share a
 // row (a ring slot) and hold d/16 of its features, so a row is one coalesced
 // read per array; a group of 16 lanes owns kRows consecutive slots per pass,
-// and a pass of the 32 groups covers 32 kRows slots (the whole w = 512 ring for
-// bf16, every load of it in flight together).  The loads go by slot, so they do not wait for the position; the
-// offsets follow once it arrives.  Along a group's slots the offset falls by
-// one per slot, with one jump from 1 to w where the ring wraps: the group turns
-// the query once with the (cos, sin) table entry of its first offset (built in
-// fp64 with the state), then by -theta_m per slot, and takes R(w) q at the
-// wrap.  Every group runs an online softmax over its rows; the groups meet by
-// shuffles inside a wave and in LDS across waves.  The new token then replaces
-// the oldest one, in slot i mod w, after every read of the ring.
+// and a pass of the 32 groups covers 32 kRows slots (the whole w = 512 ring
+// for bf16, every load of it in flight together).  The loads go by slot, so
+// they do not wait for the position; the offsets follow once it arrives.
+// Along a group's slots the offset falls by one per slot, with one jump from 1
+// to w where the ring wraps: the group turns the query once with the (cos,
+// sin) table entry of its first offset (built in fp64 with the state), then by
+// -theta_m per slot, and takes R(w) q at the wrap.  Every group runs an online
+// softmax over its rows; the groups meet in LDS, where 512 / d adjacent lanes
+// finish each feature.  The new token then replaces the oldest one, in slot
+// i mod w, after every read of the ring.
 #include "fsl_internal.h"
 
 namespace fsl {
@@ -142,8 +143,10 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
     constexpr int kPass = kGroups * kRows;        // slots per pass
     static_assert(FPL % 2 == 0, "whole feature pairs per lane");
 
-    __shared__ float s_m[kWaves], s_l[kWaves];
-    __shared__ float s_acc[kWaves][D + 1];
+    constexpr int TPF = kThreads / D;  // lanes per feature in the final combination: 4 (d = 128) or 8
+    constexpr int GPT = kGroups / TPF; // groups each of them combines
+    __shared__ float s_m[kGroups], s_l[kGroups];
+    __shared__ float s_acc[kGroups][D + 1];
 
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
@@ -169,9 +172,11 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
     load_dwords<NDW>(reinterpret_cast<const char *>(v_new + bh * D) + lane_off, vr0);
     load_dwords<FPL>(tab + (w > 0 ? 1 : 0) * NP * (int64_t)sizeof(float2), stp); // (cos, sin) of theta_m
     load_dwords<FPL>(tab + w * NP * (int64_t)sizeof(float2), cw);                // of w theta_m
-    // what the epilogue writes or adds, element t: requested now, not after the softmax
-    const int te = t < D ? t : 0;
-    const T olr_t = o_lr ? o_lr[bh * D + te] : T(0);
+    // what the epilogue writes or adds, element t: requested now, not after the softmax,
+    // and without a branch (a load under a branch would be waited for at its end)
+    const int te = t / TPF; // the feature this thread finishes
+    const T *olr_src = o_lr ? o_lr : q; // q stands in when there is no o_lr (then unused)
+    const T olr_t = olr_src[bh * D + te];
     const T kn_t = k_new[bh * D + te], vn_t = v_new[bh * D + te];
 
     // slot of token i - 1 (offset 1); slots of offsets above min(i, w) hold no token yet.
@@ -299,61 +304,57 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
         }
     }
 
-    // the four groups of a wave meet (a group without rows has m = -inf and weight 0)
-    float M = fmaxf(m, __shfl_xor(m, 16, kWave));
-    M = fmaxf(M, __shfl_xor(M, 32, kWave));
-    const float f = m == -INFINITY ? 0.0f : exp2f(m - M);
-    l *= f;
+    // every group's partial softmax goes to LDS (a group without rows has m = -inf and weight 0)
 #pragma unroll
     for (int e = 0; e < FPL; ++e)
-        acc[e] *= f;
-#pragma unroll
-    for (int msk = 16; msk < kWave; msk <<= 1) {
-        l += __shfl_xor(l, msk, kWave);
-#pragma unroll
-        for (int e = 0; e < FPL; ++e)
-            acc[e] += __shfl_xor(acc[e], msk, kWave);
-    }
-    if (lane < kLanesPerRow) {
-#pragma unroll
-        for (int e = 0; e < FPL; ++e)
-            s_acc[wave][part * FPL + e] = acc[e];
-        if (lane == 0) {
-            s_m[wave] = M;
-            s_l[wave] = l;
-        }
+        s_acc[grp][part * FPL + e] = acc[e];
+    if (part == 0) {
+        s_m[grp] = m;
+        s_l[grp] = l;
     }
     __syncthreads();
+
+    // TPF adjacent lanes finish feature te, each combining GPT groups, then add up by DPP
+    const int sub = t % TPF;
+    float M = s_m[0]; // group 0 holds offset 0, so M is finite
+#pragma unroll
+    for (int g = 1; g < kGroups; ++g)
+        M = fmaxf(M, s_m[g]);
+    float z = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < GPT; ++gg) {
+        const int g = sub * GPT + gg;
+        const float fw = exp2f(s_m[g] - M);
+        z = fmaf(s_l[g], fw, z);
+        u = fmaf(s_acc[g][te], fw, u);
+    }
+    z += dpp_f<0xB1>(z); // quad_perm [1,0,3,2]
+    u += dpp_f<0xB1>(u);
+    z += dpp_f<0x4E>(z); // quad_perm [2,3,0,1]
+    u += dpp_f<0x4E>(u);
+    if constexpr (TPF == 8) {
+        z += dpp_f<0x141>(z); // row_half_mirror: the two quads of each 8-lane half
+        u += dpp_f<0x141>(u);
+    }
 
     const bool bad = hv.magic != kLocalStateMagic || hv.version != kLocalStateVersion || hv.batch != expect.batch ||
                      hv.H != expect.H || hv.d != D || hv.dtype != expect.dtype || hv.w != expect.w ||
                      hv.rec_bytes != expect.rec_bytes || i < 0;
     T *o_row = out + bh * D;
-    if (t < D) {
-        float Mw = s_m[0]; // wave 0 holds offset 0, so Mw is finite
-#pragma unroll
-        for (int g = 1; g < kWaves; ++g)
-            Mw = fmaxf(Mw, s_m[g]);
-        float z = 0.0f, u = 0.0f;
-#pragma unroll
-        for (int g = 0; g < kWaves; ++g) {
-            const float fw = exp2f(s_m[g] - Mw);
-            z = fmaf(s_l[g], fw, z);
-            u = fmaf(s_acc[g][t], fw, u);
-        }
+    if (sub == 0) {
         u /= z;
         const float y = o_lr ? fmaf(lc.alpha[h], to_f32<T>(olr_t), u) : u;
         if (bad) { // not a state of this shape: flag the output, leave the state alone
             if constexpr (sizeof(T) == 2)
-                o_row[t] = (T)0x7fc0u; // bf16 quiet NaN
+                o_row[te] = (T)0x7fc0u; // bf16 quiet NaN
             else
-                o_row[t] = __uint_as_float(0x7fc00000u);
+                o_row[te] = __uint_as_float(0x7fc00000u);
         } else {
-            o_row[t] = from_f32<T>(y);
+            o_row[te] = from_f32<T>(y);
             if (w > 0) { // the new token replaces token i - w, read above for the last time
                 const int64_t slot = i % w;
-                reinterpret_cast<T *>(rec + L.off_k)[slot * D + t] = kn_t;
-                reinterpret_cast<T *>(rec + L.off_v)[slot * D + t] = vn_t;
+                reinterpret_cast<T *>(rec + L.off_k)[slot * D + te] = kn_t;
+                reinterpret_cast<T *>(rec + L.off_v)[slot * D + te] = vn_t;
             }
         }
     }
