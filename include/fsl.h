@@ -286,8 +286,9 @@ fs_status fs_local_window(const fs_shape *shape, int64_t w, float rope_base, con
  * (cos, sin) of o * theta_m for o = 0 .. w and m < d/2 (fp32 pairs, shared by
  * every head); then per (sequence, head) the next position (int64) and rings of
  * the last w raw keys and the last w raw values of the dtype (token p in slot
- * p mod w; one unused slot when w = 0).  0 for an unsupported or invalid combination (d not 64/128,
- * H > FS_MAX_HEADS, w < 0 or w > 65535, batch * H > 65535).
+ * p mod w; one unused slot when w = 0).  0 for an unsupported or invalid
+ * combination (d not 64/128, H > FS_MAX_HEADS, w < 0 or w > 65535,
+ * batch * H > 65535).
  */
 size_t fs_local_state_bytes(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w);
 
@@ -317,7 +318,9 @@ fs_status fs_local_state_build(int32_t batch, int32_t H, int32_t d, fs_dtype dty
  *   alpha_h          host [H] fp32, finite; required when o_lr is given
  *   o_lr             device [batch, H, d] dtype (fs_longrange_decode's out), or NULL
  *   out              device [batch, H, d] dtype; may be the o_lr buffer  (output)
- * Arithmetic: fp32 (keys turned by the fp32 table, exact up to rounding).
+ * Arithmetic: fp32.  The query is turned by R(o) for each key's offset o, from
+ * the state's fp64-built table and fp32 steps of theta_m (relative error below
+ * 1e-6); products, softmax and sums in fp32.
  * Errors: FS_ERR_STATE when state_bytes does not match; a buffer of the right
  * size not built by fs_local_state_build for this shape and w is detected on
  * the device: out is set to NaN and the buffer is left untouched.  One launch
