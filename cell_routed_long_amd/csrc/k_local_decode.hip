@@ -27,7 +27,6 @@ namespace fsl {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kLanesPerRow = 16;
 constexpr int kGroups = kThreads / kLanesPerRow; // 32 groups of 16 lanes
 
@@ -150,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
 
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
-    const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+    const int t = threadIdx.x;
     const int grp = t / kLanesPerRow, part = t % kLanesPerRow;
     const int64_t w = L.w;
     char *rec = state + L.off_rec + bh * L.rec_bytes; // in bounds: the host checked the buffer size
@@ -172,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
     load_dwords<NDW>(reinterpret_cast<const char *>(v_new + bh * D) + lane_off, vr0);
     load_dwords<FPL>(tab + (w > 0 ? 1 : 0) * NP * (int64_t)sizeof(float2), stp); // (cos, sin) of theta_m
     load_dwords<FPL>(tab + w * NP * (int64_t)sizeof(float2), cw);                // of w theta_m
-    // what the epilogue writes or adds, element t: requested now, not after the softmax,
-    // and without a branch (a load under a branch would be waited for at its end)
+    // what the epilogue writes or adds for feature te: requested now, not after the
+    // softmax, and without a branch (a load under a branch is waited for at its end)
     const int te = t / TPF; // the feature this thread finishes
     const T *olr_src = o_lr ? o_lr : q; // q stands in when there is no o_lr (then unused)
     const T olr_t = olr_src[bh * D + te];
