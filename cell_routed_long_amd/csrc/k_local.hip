@@ -309,11 +309,18 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
             for (int kc = 0; kc < KC; ++kc)
                 acc = mfma_f32(sm.k[col][kc * 2 + half], qf[kc], acc);
         }
+        // the tile's rows inside this query's window, tile-relative: lo_r <= row <= hi_r
+        // (j >= qi - w, j <= qi, j < N); most tiles lie wholly inside every window
+        const int64_t lo64 = my_lo - ts, hi64 = (qi < N - 1 ? qi : N - 1) - ts;
+        const int lo_r = lo64 < 0 ? 0 : (lo64 > 32 ? 32 : (int)lo64);
+        const int hi_r = hi64 > 31 ? 31 : (hi64 < -1 ? -1 : (int)hi64);
+        if (__ballot(lo_r > 0 || hi_r < 31) != 0ull) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t j = ts + acc_row(r, half);
-            if (!(j <= qi && j >= my_lo && j < N))
-                acc[r] = -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+                const int row = acc_row(r, half);
+                if (row < lo_r || row > hi_r)
+                    acc[r] = -INFINITY;
+            }
         }
 
         // ---- online softmax (exp2 domain) ----
