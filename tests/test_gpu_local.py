@@ -88,6 +88,12 @@ def test_local_headline_shape_sampled():
     run_case(w, 512, heads=[(1, 7)], rows=(0, 400))
 
 
+def test_local_maximum_length_sampled():
+    """N = 2^22, the longest sequence the ABI accepts: the last 300 rows against the oracle."""
+    w = synth.Workload(batch=1, H=1, N=1 << 22, d=64, dtype="bf16", seed=112)
+    run_case(w, 512, rows=(w.N - 300, w.N))
+
+
 def test_local_rejects_bad_arguments():
     q = torch.zeros(1, 1, 64, 64, device="cuda")
     with pytest.raises(fsl.FslError):

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import cell_routed_long_amd as fsl
+import oracle
 import synth
 from tests import parity_utils as pu
 
@@ -209,6 +210,27 @@ def test_fs_32k_sampled():
     """FS (no pruning), b1 H16 d128 N32768 bf16: up to 1020 cells scored per query."""
     w = synth.WORKLOADS["fs_32k"]
     check(w, fsl.Params(prune=False), heads=[(0, 3), (0, 12)])
+
+
+def test_maximum_length_sampled_blocks():
+    """N = 2^22, the longest sequence the ABI accepts: 131,072 cells per head, so the
+    retained sets take the per-block pruning path.  The whole sequence runs on the GPU;
+    the queries of an early, a middle and the last block are compared with the oracle."""
+    w = synth.Workload(batch=1, H=1, N=1 << 22, d=64, dtype="bf16", seed=80, needle_frac=0.001)
+    p = fsl.Params()
+    host = pu.inputs(w)
+    out, sel = run_prefill(w, host, p)
+    qf, kf, vf = (synth.to_f64(host[x][0, 0], w.dtype) for x in "qkv")
+    del host
+    checked = skipped = 0
+    for lo in (128 * 40, (w.N // 2) // 128 * 128, w.N - 128):
+        ref = oracle.head(qf, kf, vf, None, pu.oracle_params(p), lo, lo + 128, want_summaries=False)
+        c, s = pu.compare_head(sel[0, 0, lo:lo + 128], out[0, 0, lo:lo + 128], ref, p, w.dtype, i_lo=lo,
+                               what=f"N=2^22 block {lo // 128}")
+        checked += c
+        skipped += s
+    print(f"checked {checked} queries, {skipped} near-ties excluded")
+    assert skipped <= 0.01 * (checked + skipped)
 
 
 @pytest.mark.parametrize("P,W", [(240, 16), (300, 20)], ids=["cap256-single-kernel", "cap320-two-kernels"])
