@@ -222,3 +222,12 @@ def test_full_attention_decode_output():
         pu.check_rows(got[b, h][~skip], full[~skip], w.dtype, f"full decode output b{b} h{h}",
                       lr_scale=float(alpha[h]))
     assert skipped <= 0.01 * len(heads) * T
+
+
+def test_local_decode_largest_grid():
+    """batch * H = 65,408 (b511 H128) records, w = 64: one step, sampled records
+    against the oracle."""
+    w = synth.Workload(batch=511, H=128, N=161, d=64, dtype="bf16", seed=216)
+    host = pu.inputs(w)
+    got, olr, alpha, _, _ = run_steps(w, host, 64, 160, 1)
+    check_steps(w, host, 64, 160, 1, got, olr, alpha, heads=[(0, 0), (255, 64), (510, 127)])

@@ -233,6 +233,42 @@ def test_maximum_length_sampled_blocks():
     assert skipped <= 0.01 * (checked + skipped)
 
 
+def test_per_head_constants_at_max_heads():
+    """H = 128, the most heads accepted, each with its own sigma_h and lambda_h (Eq. 7):
+    sampled heads against the oracle with that head's constants."""
+    w = synth.Workload(batch=1, H=128, N=700, d=64, dtype="f32", seed=81, needle_frac=0.01)
+    p = fsl.Params(P=6, W=2)
+    sig = [2.0 + h / 16.0 for h in range(w.H)]
+    lam = [0.25 + h / 64.0 for h in range(w.H)]
+    host = pu.inputs(w)
+    dq, dk, dv = (pu.to_device(host[x], w.dtype) for x in "qkv")
+    print(f"[gpu] per-head constants {w}", flush=True)
+    out, sel, _ = fsl.prefill(dq, dk, dv, p, sigma=sig, lam=lam)
+    torch.cuda.synchronize()
+    out, sel = out.float().cpu().numpy(), sel.cpu().numpy()
+    for h in (0, 1, 63, 127):
+        op = oracle.Params(s=p.s, B=p.B, P=p.P, W=p.W, K=p.K, prune=p.prune, sigma=sig[h], lam=lam[h], eps=p.eps)
+        ref = oracle.head(*(synth.to_f64(host[x][0, h], w.dtype) for x in "qkv"), None, op)
+        pu.compare_head(sel[0, h], out[0, h], ref, p, w.dtype, what=f"H=128 head {h}")
+
+
+def test_largest_grid_sampled_heads():
+    """batch * H = 65,408 (b511 H128), close to the 65,535 the ABI accepts, N = 160 (one
+    routed block per head): the long-range prefill and the local branch over every head,
+    sampled heads against the oracle."""
+    w = synth.Workload(batch=511, H=128, N=160, d=64, dtype="bf16", seed=82, needle_frac=0.02)
+    p = fsl.Params()
+    host = pu.inputs(w)
+    out, sel = run_prefill(w, host, p)
+    dq, dk, dv = (pu.to_device(host[x], w.dtype) for x in "qkv")
+    loc = fsl.local(dq, dk, dv, w=64).float().cpu().numpy()
+    heads = [(0, 0), (255, 64), (510, 127)]
+    for (b, h), ref in pu.run_oracle(w, host, p, heads).items():
+        pu.compare_head(sel[b, h], out[b, h], ref, p, w.dtype, what=f"b{b} h{h}")
+        lref = oracle.local(*(synth.to_f64(host[x][b, h], w.dtype) for x in "qkv"), w=64)
+        pu.check_rows(loc[b, h], lref, w.dtype, f"local b{b} h{h}")
+
+
 @pytest.mark.parametrize("P,W", [(240, 16), (300, 20)], ids=["cap256-single-kernel", "cap320-two-kernels"])
 def test_large_retained_sets(P, W):
     """Retained sets at the single-kernel limit (P + W = 256) and past it (the
