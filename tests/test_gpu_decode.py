@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import cell_routed_long_amd as fsl
+import oracle
 import synth
 from tests import parity_utils as pu
 
@@ -229,3 +230,25 @@ def test_decode_full_length_sampled():
                        needle_frac=w0.needle_frac)
     N0 = 262144
     check_stream(w, fsl.Params(), N0, 130, heads=[(0, 1), (1, 6)])
+
+
+def test_decode_per_head_constants():
+    """Every head with its own sigma_h and lambda_h (Eq. 7) through the prefill that
+    builds the state and the decode steps: each head against the oracle with its own."""
+    w = synth.Workload(batch=2, H=6, N=1400, d=64, dtype="f32", seed=93, needle_frac=0.01)
+    p = fsl.Params(P=6, W=2)
+    sig = [1.5 + 2.0 * h for h in range(w.H)]
+    lam = [0.2 + 0.3 * h for h in range(w.H)]
+    N0, T = 1000, 400
+    host = pu.inputs(w)
+    out, sel, _ = run_stream(w, host, p, N0, T, sigma=sig, lam=lam)
+    skipped = checked = 0
+    for b in range(w.batch):
+        for h in range(w.H):
+            op = oracle.Params(s=p.s, B=p.B, P=p.P, W=p.W, K=p.K, prune=p.prune, sigma=sig[h], lam=lam[h],
+                               eps=p.eps)
+            ref = oracle.head(*(synth.to_f64(host[x][b, h], w.dtype) for x in "qkv"), None, op, N0, N0 + T)
+            c, s_ = pu.compare_head(sel[b, h], out[b, h], ref, p, w.dtype, i_lo=N0, what=f"decode b{b} h{h}")
+            checked += c
+            skipped += s_
+    assert skipped <= 0.01 * (checked + skipped)
