@@ -157,7 +157,10 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
     const char *kring = rec + L.off_k + lane_off;
     const char *vring = rec + L.off_v + lane_off;
     const char *tab = state + L.off_table + part * NPL * (int64_t)sizeof(float2);
-    const float scale = 1.4426950408889634f / sqrtf((float)D); // log2(e) / sqrt(d): exp2 domain
+    // log2(e) / sqrt(d): the softmax works in the exp2 domain with the hardware exp2 (one
+    // instruction; results below 2^-126 flush to 0, far below any weight that counts next
+    // to the largest, which is 1)
+    const float scale = 1.4426950408889634f / sqrtf((float)D);
 
     // Nothing waits for memory before a pass's ring rows are requested, and
     // nothing branches on the header: every address here lies inside the buffer
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
                 mx = fmaxf(mx, x[uu]);
             }
             if (mx > m) { // the group's running maximum grows: rescale what it holds
-                const float f = exp2f(m - mx);
+                const float f = __builtin_amdgcn_exp2f(m - mx);
                 l *= f;
 #pragma unroll
                 for (int e = 0; e < FPL; ++e)
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
             }
 #pragma unroll
             for (int uu = 0; uu < kHalf; ++uu) {
-                const float p = x[uu] == -INFINITY ? 0.0f : exp2f(x[uu] - m);
+                const float p = x[uu] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[uu] - m);
                 l += p;
 #pragma unroll
                 for (int e = 0; e < FPL; ++e)
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
         if (grp == 0) {
             const float x0 = dot * scale;
             const float mx = fmaxf(m, x0);
-            const float f = m == -INFINITY ? 0.0f : exp2f(m - mx), p0 = exp2f(x0 - mx);
+            const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mx), p0 = __builtin_amdgcn_exp2f(x0 - mx);
             l = fmaf(l, f, p0);
 #pragma unroll
             for (int e = 0; e < FPL; ++e)
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
 #pragma unroll
     for (int gg = 0; gg < GPT; ++gg) {
         const int g = sub * GPT + gg;
-        const float fw = exp2f(s_m[g] - M);
+        const float fw = __builtin_amdgcn_exp2f(s_m[g] - M);
         z = fmaf(s_l[g], fw, z);
         u = fmaf(s_acc[g][te], fw, u);
     }
