@@ -12,6 +12,12 @@ three calls on one stream with HIP events between them, so that every kernel's
 average launch time is measured inside the timed region.  Before the W warm-up
 steps, steps run untimed for SETTLE_S seconds so that the GPU clocks have left
 their ramp.  Prints one JSON line.
+
+Other workloads (--workload): decode_256k (the long-range streaming decode,
+b32 H8 d128 after a 262,144-token prefix), local_16k (the local RoPE window
+branch with the branch combination on the prefill's inputs, w = 512) and
+local_decode_256k (its streaming decode at the decode workload's positions).
+Each prints the same kind of line with its own metric, roofline and oracle rate.
 """
 from __future__ import annotations
 
