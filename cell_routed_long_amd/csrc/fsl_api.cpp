@@ -120,7 +120,6 @@ fs_status check_heads(int H, const float *sigma_h, const float *lambda_h, HeadCo
             return FS_ERR_INVALID;
         hc->inv_two_sigma[h] = 1.0f / (2.0f * sigma_h[h]);
         hc->lambda[h] = lambda_h[h];
-        hc->sigma[h] = sigma_h[h];
     }
     return FS_OK;
 }
@@ -506,6 +505,8 @@ FSL_EXPORT fs_status fs_local_window(const fs_shape *shape, int64_t w, float rop
         return st;
     if (!q || !k || !v || !out || w < 0 || !(rope_base > 1.0f) || !std::isfinite(rope_base))
         return FS_ERR_INVALID;
+    if (w > kMaxLocalWindow)
+        return FS_ERR_UNSUPPORTED;
     LocalConsts lc;
     std::memset(&lc, 0, sizeof(lc));
     lc.rope_base = rope_base;

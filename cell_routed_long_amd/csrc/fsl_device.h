@@ -260,7 +260,6 @@ __device__ __forceinline__ void tile_store_bf16(uint16_t *__restrict__ g, const 
 struct HeadConsts {
     float inv_two_sigma[128]; // 1 / (2 sigma_h)
     float lambda[128];        // lambda_h
-    float sigma[128];         // sigma_h as given (the decode step scores in fp64)
 };
 
 } // namespace fsl

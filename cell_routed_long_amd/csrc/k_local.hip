@@ -78,8 +78,18 @@ __device__ __forceinline__ float2 rotate(float x, float y, float2 cs)
     return make_float2(fmaf(x, cs.x, -y * cs.y), fmaf(x, cs.y, y * cs.x));
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__restrict__ q, const T *__restrict__ k,
+// LONG: windows of many tiles.  A running fp32 sum over n tiles can lose about
+// n * 2^-24 of its value (every tile's contribution is rounded into a total that
+// may already hold the window's largest terms); over the ~2,050 tiles of the
+// largest window that is 1e-4.  The long form therefore sums each run of kRun
+// tiles separately and adds the run into a second total, which bounds the loss by
+// about (kRun + n / kRun) * 2^-24.  The second set of accumulators costs registers,
+// so that form runs one workgroup per CU.
+constexpr int kRun = 16;
+constexpr int64_t kLongWindow = 1024; // windows at least this long take the long form
+
+template <typename T, int D, bool LONG>
+__global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                                 const T *__restrict__ v,
                                                                 const T *__restrict__ o_lr, T *__restrict__ out,
                                                                 LocalConsts lc, int64_t N, int NB, int H,
@@ -122,15 +132,21 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
         s_row[e / NP][e % NP] = sincos_pair((double)(e / NP) * s_theta[e % NP]);
     for (int e = t; e < 4 * NP; e += kThreads)
         s_qbase[e / NP][e % NP] = sincos_pair((double)(32 * (e / NP)) * s_theta[e % NP]);
-    // tile x starts 32 x tokens after tile 0: its angles are tile 0's turned by 32 theta_m
-    // x times (fp32 angle additions; about 1e-6 relative after the ~20 tiles of a window)
+    // tile x starts 32 x tokens after tile 0: its angles are the previous tile's turned by
+    // 32 theta_m (one fp32 angle addition, about 6e-8 relative each).  A short window has
+    // at most 37 tiles; the long form takes the angles afresh from fp64 every kRun tiles,
+    // so the stepped angles never carry more than kRun additions however long the window.
     if (t < NP) {
         s_base[0][t] = sincos_pair((double)(t_lo - q0) * s_theta[t]);
         s_step[t] = sincos_pair(32.0 * s_theta[t]);
     }
-    auto tile_base = [&](int x, int buf) { // tile x from tile x - 1, whose angles are in buf ^ 1
-        if (t < NP)
-            s_base[buf][t] = cs_add(s_base[buf ^ 1][t], s_step[t]);
+    auto tile_base = [&](int x, int buf) { // tile x, from tile x - 1 whose angles are in buf ^ 1
+        if (t < NP) {
+            if (LONG && x % kRun == 0)
+                s_base[buf][t] = sincos_pair((double)(t_lo - q0 + 32 * (int64_t)x) * s_theta[t]);
+            else
+                s_base[buf][t] = cs_add(s_base[buf ^ 1][t], s_step[t]);
+        }
     };
     __syncthreads();
 
@@ -221,6 +237,15 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
         for (int r = 0; r < 16; ++r)
             o_acc[dt][r] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f; // m_run in the exp2 domain
+    f32x16 o_tot[LONG ? DT : 1];            // LONG: the completed runs of kRun tiles
+    float l_tot = 0.0f;
+    if constexpr (LONG) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o_tot[dt][r] = 0.0f;
+    }
     const int64_t my_lo = qi - w; // the query's window is [my_lo, qi]
 
     for (int x = 0; x < n_tiles; ++x) {
@@ -274,6 +299,20 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
         if constexpr (kBf16) {
             if (x + 1 < n_tiles)
                 fetch(x + 1); // overlaps the matrix work below
+        }
+
+        if constexpr (LONG) {
+            if (x % kRun == 0 && x > 0) { // close the run of tiles x - kRun .. x - 1
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        o_tot[dt][r] += o_acc[dt][r];
+                        o_acc[dt][r] = 0.0f;
+                    }
+                l_tot += l_run;
+                l_run = 0.0f;
+            }
         }
 
         // does the tile meet the query's window?
@@ -332,6 +371,14 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     o_acc[dt][r] *= alpha;
+            if constexpr (LONG) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        o_tot[dt][r] *= alpha;
+                l_tot *= alpha;
+            }
         }
 
         // ---- O^T[d x 32 queries] += V^T . P^T ----
@@ -358,6 +405,15 @@ __global__ __launch_bounds__(kThreads, 2) void local_window_kernel(const T *__re
                 for (int r = 0; r < 16; ++r)
                     o_acc[dt] = mfma_f32(sm.v[acc_row(r, half)][dt * 32 + col], p[r], o_acc[dt]);
         }
+    }
+
+    if constexpr (LONG) { // the last, partial run
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o_acc[dt][r] += o_tot[dt][r];
+        l_run += l_tot;
     }
 
     // ---- o_sr = O / l, plus alpha_h o_lr (Eq. 2), written out ----
@@ -421,9 +477,14 @@ hipError_t launch_t(const Geometry &g, const LocalConsts &lc, int64_t w, const v
                     const void *o_lr, void *out, hipStream_t st)
 {
     dim3 grid((unsigned)((int64_t)g.NB * g.bh)); // one linear range, renumbered per XCD in the kernel
-    hipLaunchKernelGGL((local_window_kernel<T, D>), grid, dim3(kThreads), 0, st, static_cast<const T *>(q),
-                       static_cast<const T *>(k), static_cast<const T *>(v), static_cast<const T *>(o_lr),
-                       static_cast<T *>(out), lc, g.N, g.NB, g.H, w);
+    if (w >= kLongWindow)
+        hipLaunchKernelGGL((local_window_kernel<T, D, true>), grid, dim3(kThreads), 0, st, static_cast<const T *>(q),
+                           static_cast<const T *>(k), static_cast<const T *>(v), static_cast<const T *>(o_lr),
+                           static_cast<T *>(out), lc, g.N, g.NB, g.H, w);
+    else
+        hipLaunchKernelGGL((local_window_kernel<T, D, false>), grid, dim3(kThreads), 0, st,
+                           static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v),
+                           static_cast<const T *>(o_lr), static_cast<T *>(out), lc, g.N, g.NB, g.H, w);
     return hipGetLastError();
 }
 

@@ -191,10 +191,18 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
     auto offset_of = [&](int sl) { return sl <= last ? last - sl + 1 : last - sl + 1 + wi; };
     constexpr int kHalf = kRows / 2; // rows per softmax update
 
-    float m = -INFINITY, l = 0.0f, acc[FPL];
+    // A group adds up to w / 32 rows one after another; a running fp32 sum of n terms
+    // can lose about n * 2^-24 of its value, 1e-4 at the largest window.  Each run of
+    // kRunPasses passes is therefore summed on its own and then added into a second
+    // total (acc_t, l_t): the loss stays near (rows per run + runs) * 2^-24.  Windows
+    // of up to kRunPasses passes never close a run.
+    constexpr int kRunPasses = 8;
+    float m = -INFINITY, l = 0.0f, acc[FPL], l_t = 0.0f, acc_t[FPL];
 #pragma unroll
-    for (int e = 0; e < FPL; ++e)
+    for (int e = 0; e < FPL; ++e) {
         acc[e] = 0.0f;
+        acc_t[e] = 0.0f;
+    }
 
     for (int base = 0; base < wi; base += kPass) {
         // the pass's rows and the angle of the group's first offset are requested
@@ -271,9 +279,12 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
             if (mx > m) { // the group's running maximum grows: rescale what it holds
                 const float f = __builtin_amdgcn_exp2f(m - mx);
                 l *= f;
+                l_t *= f;
 #pragma unroll
-                for (int e = 0; e < FPL; ++e)
+                for (int e = 0; e < FPL; ++e) {
                     acc[e] *= f;
+                    acc_t[e] *= f;
+                }
                 m = mx;
             }
 #pragma unroll
@@ -285,7 +296,20 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
                     acc[e] = fmaf(p, feature<T, NDW>(vr[hh + uu], e), acc[e]);
             }
         }
+        if ((base / kPass) % kRunPasses == kRunPasses - 1) { // close the run
+#pragma unroll
+            for (int e = 0; e < FPL; ++e) {
+                acc_t[e] += acc[e];
+                acc[e] = 0.0f;
+            }
+            l_t += l;
+            l = 0.0f;
+        }
     }
+#pragma unroll
+    for (int e = 0; e < FPL; ++e)
+        acc[e] += acc_t[e];
+    l += l_t;
 
     // offset 0, the step's own token, joins group 0's softmax
     {

@@ -261,7 +261,8 @@ fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, in
  *   rotation of Su et al., which the page cites),
  *   out_i = o_sr_i + alpha_h * o_lr_i when o_lr is given, else out_i = o_sr_i.
  *   shape       batch, H, N, d, dtype as for the other calls
- *   w           look-back radius, >= 0 (the page's w is 512)
+ *   w           look-back radius, 0 <= w <= 65535 (the page's w is 512; larger
+ *               windows give FS_ERR_UNSUPPORTED)
  *   rope_base   > 1 and finite (RoFormer's 10000 unless the model says otherwise)
  *   q, k, v     device [batch, H, N, d] dtype, unrotated (the same q, k, v as the
  *               long-range branch, which reads them unrotated)          (input)

@@ -59,6 +59,10 @@ def _bind(path: str):
     lib.oracle_retained.restype = i64
     lib.oracle_cell_score.argtypes = [ctypes.POINTER(_Cfg), vp, vp, ctypes.c_double, i64, i64]
     lib.oracle_cell_score.restype = ctypes.c_double
+    lib.oracle_cell_score_mag.argtypes = [ctypes.POINTER(_Cfg), vp, vp, ctypes.c_double, i64, i64]
+    lib.oracle_cell_score_mag.restype = ctypes.c_double
+    lib.oracle_readout.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, i64, vp]
+    lib.oracle_readout.restype = None
     lib.oracle_local.argtypes = [i64, ctypes.c_int32, i64, ctypes.c_double, vp, vp, vp, ctypes.c_double, vp, i64, i64,
                                  vp]
     lib.oracle_local.restype = ctypes.c_int
@@ -148,6 +152,27 @@ def cell_score(q_i, kbar_c, a_c: float, i: int, c: int, prm: Params = Params()) 
     q_i = _f64(q_i); kbar_c = _f64(kbar_c)
     cfg = prm.cfg(0, len(q_i))
     return float(_load().oracle_cell_score(ctypes.byref(cfg), _p(q_i), _p(kbar_c), float(a_c), i, c))
+
+
+def cell_score_mag(q_i, kbar_c, a_c: float, i: int, c: int, prm: Params = Params()) -> float:
+    """The size of the terms Eq. 7 sums for (query i, cell c); see fsl_oracle.h."""
+    q_i = _f64(q_i); kbar_c = _f64(kbar_c)
+    cfg = prm.cfg(0, len(q_i))
+    return float(_load().oracle_cell_score_mag(ctypes.byref(cfg), _p(q_i), _p(kbar_c), float(a_c), i, c))
+
+
+def readout(q_i, k, v, cells, g=None, prm: Params = Params()):
+    """Eq. 9 + Eq. 17 for one query over a given selection `cells` (ids; -1 entries
+    are ignored): q_i [d], k, v [N, d] -> o [d] (zero for an empty selection)."""
+    q_i, k, v, g = _f64(q_i), _f64(k), _f64(v), _f64(g)
+    T = np.ascontiguousarray([c for c in cells if c >= 0], dtype=np.int64)
+    M = k.shape[0] // prm.s
+    if np.any(T >= M):
+        raise ValueError("selection names a cell past the last complete one")
+    o = np.zeros(k.shape[1])
+    cfg = prm.cfg(k.shape[0], k.shape[1])
+    _load().oracle_readout(ctypes.byref(cfg), _p(q_i), _p(k), _p(v), _p(g), _p(T) if len(T) else None, len(T), _p(o))
+    return o
 
 
 def cap_for(N: int, prm: Params) -> int:

@@ -134,20 +134,39 @@ int64_t oracle_retained(const oracle_cfg *cfg, int64_t n_avail, const double *a,
 
 /* ---- Eq. 7: cell score ------------------------------------------------------ */
 
+/* g_h(i - p_c) of the prior */
+static double prior_gate(const oracle_cfg *cfg, int64_t i, int64_t c)
+{
+    const double p_c = ((double)c + 0.5) * cfg->s;        /* cell centre, Eq. 5 */
+    return erf(((double)i - p_c) / (2.0 * cfg->sigma));
+}
+
 double oracle_cell_score(const oracle_cfg *cfg, const double *q_i, const double *kbar_c,
                          double a_c, int64_t i, int64_t c)
 {
     double dot = 0.0;
     for (int32_t f = 0; f < cfg->d; ++f)
         dot += q_i[f] * kbar_c[f];
-    const double p_c = ((double)c + 0.5) * cfg->s;        /* cell centre, Eq. 5 */
-    const double g = erf(((double)i - p_c) / (2.0 * cfg->sigma)); /* g_h(i - p_c) */
+    const double g = prior_gate(cfg, i, c);
     return dot / sqrt((double)cfg->d) + cfg->lambda * a_c * g;
+}
+
+/* The size of the terms r_ic is summed from: sum_f |q_if kbar_cf| / sqrt(d) +
+ * lambda a_c |g|.  A floating-point evaluation of Eq. 7 is exact to a few roundings
+ * of this size, not of |r_ic| (the content term can cancel), so the near-tie gap of
+ * two scores is measured against it. */
+double oracle_cell_score_mag(const oracle_cfg *cfg, const double *q_i, const double *kbar_c,
+                             double a_c, int64_t i, int64_t c)
+{
+    double sum = 0.0;
+    for (int32_t f = 0; f < cfg->d; ++f)
+        sum += fabs(q_i[f] * kbar_c[f]);
+    return sum / sqrt((double)cfg->d) + cfg->lambda * a_c * fabs(prior_gate(cfg, i, c));
 }
 
 /* ---- Eq. 9 / Eq. 1 / Eq. 17: token readout and RMSNorm --------------------- */
 
-static void readout(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
+void oracle_readout(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
                     const double *g, const int64_t *T, int64_t nT, double *o)
 {
     const int32_t d = cfg->d, s = cfg->s;
@@ -266,10 +285,19 @@ int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const d
         if (sel)
             for (int32_t t = 0; t < K; ++t)
                 sel[row * K + t] = t < nT ? (int32_t)T[t] : -1;
-        if (gap_k)
-            gap_k[row] = nA > K ? relative_gap(rank[K - 1].val, rank[K].val) : INFINITY;
+        if (gap_k) {
+            gap_k[row] = INFINITY;
+            if (nA > K) { /* |r_K - r_K+1| against the larger of the two scores' term sizes */
+                const double m1 = oracle_cell_score_mag(cfg, q_i, kb + rank[K - 1].id * d, an[rank[K - 1].id], i,
+                                                        rank[K - 1].id);
+                const double m2 = oracle_cell_score_mag(cfg, q_i, kb + rank[K].id * d, an[rank[K].id], i,
+                                                        rank[K].id);
+                const double m = fmax(m1, m2);
+                gap_k[row] = m > 0.0 ? fabs(rank[K - 1].val - rank[K].val) / m : 0.0;
+            }
+        }
         if (out)
-            readout(cfg, q_i, k, v, g, T, nT, out + row * d);
+            oracle_readout(cfg, q_i, k, v, g, T, nT, out + row * d);
     }
     free(T);
     free(rank);

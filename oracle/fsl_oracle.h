@@ -50,6 +50,20 @@ int64_t oracle_retained(const oracle_cfg *cfg, int64_t n_avail, const double *a,
 double oracle_cell_score(const oracle_cfg *cfg, const double *q_i, const double *kbar_c,
                          double a_c, int64_t i, int64_t c);
 
+/* The size of the terms Eq. 7 sums for (query i, cell c):
+ * sum_f |q_if kbar_cf| / sqrt(d) + lambda a_c |erf((i - p_c) / (2 sigma))|.
+ * Floating-point scores are exact to a few roundings of this size; near-tie
+ * gaps of scores are measured against it. */
+double oracle_cell_score_mag(const oracle_cfg *cfg, const double *q_i, const double *kbar_c,
+                             double a_c, int64_t i, int64_t c);
+
+/* Eq. 9 with Eq. 17 for one query and a given selection T[0..nT) of cell ids:
+ * the joint softmax over the tokens of those cells (NoPE logits q_i . k_j /
+ * sqrt(d)), then RMSNorm with gain g (unit gains when g is NULL); o = 0 when
+ * nT = 0.  k, v [N, d] hold every token the cells cover; o [d]. */
+void oracle_readout(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
+                    const double *g, const int64_t *T, int64_t nT, double *o);
+
 /*
  * The whole branch for one (sequence, head), for queries i in [i_lo, i_hi).
  *   q, k, v  [N, d];  g [d] or NULL (unit gains)
@@ -57,7 +71,8 @@ double oracle_cell_score(const oracle_cfg *cfg, const double *q_i, const double 
  *   retained [NB, cap] (-1 padded), n_ret [NB], gap_p [NB]   per query block
  *       touched by [i_lo, i_hi), indexed by absolute block (optional)
  *   sel [(i_hi-i_lo), K] selected cells (-1 padded), in (score desc, id asc)
- *   gap_k [(i_hi-i_lo)] relative gap of the K-th and (K+1)-th scores, or +inf
+ *   gap_k [(i_hi-i_lo)] gap of the K-th and (K+1)-th scores relative to the
+ *       larger of their term sizes (oracle_cell_score_mag), or +inf
  *   out [(i_hi-i_lo), d] long-range output after RMSNorm
  *   scores [(i_hi-i_lo), cap] scores of the retained cells in ascending id
  *       order (optional; NaN padded)

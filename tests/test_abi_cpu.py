@@ -240,3 +240,20 @@ def test_local_decode_validation(L):
     assert call(st_bytes=n_bytes + 256) == fsl.FS_ERR_STATE
     assert call(ww=-1) == fsl.FS_ERR_INVALID
     assert call(ww=w + 1) == fsl.FS_ERR_STATE          # a state for another w has another size
+
+
+def test_local_window_validation(L):
+    sh = shape(b=1, H=2, N=256, d=64)
+    vp = ctypes.c_void_p
+    alpha = (ctypes.c_float * 2)(1.0, 1.0)
+
+    def call(w=512, base=10000.0, q=1, o_lr=None, al=None):
+        return L.fs_local_window(ctypes.byref(sh), w, base, vp(q) if q else None, vp(1), vp(1), al,
+                                 vp(o_lr) if o_lr else None, vp(1), None)
+
+    assert call(q=0) == fsl.FS_ERR_INVALID
+    assert call(w=-1) == fsl.FS_ERR_INVALID
+    assert call(base=1.0) == fsl.FS_ERR_INVALID
+    assert call(o_lr=1) == fsl.FS_ERR_INVALID            # o_lr without alpha_h
+    assert call(w=65536) == fsl.FS_ERR_UNSUPPORTED       # past the largest window
+    assert call(w=65536, o_lr=1, al=alpha) == fsl.FS_ERR_UNSUPPORTED

@@ -4,7 +4,7 @@ The page defines decoding as the same causal operator as prompt prefill (FreeSol
 Sec. 3.3 "Inference"), so the reference for a decode step at position i is the
 oracle's prefill output at i over the whole sequence.  Each case builds a state
 with a prefill of N0 tokens, feeds T more tokens one step at a time, and compares
-every step's selection (exact, near-ties excepted) and output (tolerance) with the
+every step's selection (exact; near-ties validated) and output (tolerance) with the
 oracle at positions N0 .. N0+T-1; see tests/parity_utils.py for the rules.
 """
 import numpy as np
@@ -67,7 +67,7 @@ def check_stream(w, p, N0, T, heads=None, sigma=4.0, lam=1.0, gain=None, state_o
                                what=f"decode {w.name or w} b{b} h{h}")
         checked += c
         skipped += s
-    print(f"checked {checked} decode steps, {skipped} near-ties excluded")
+    print(f"checked {checked} decode steps exactly, {skipped} near-ties validated")
     assert skipped <= max_skip_frac * (checked + skipped)
     return out, sel, state
 
@@ -245,9 +245,9 @@ def test_decode_per_head_constants():
     skipped = checked = 0
     for b in range(w.batch):
         for h in range(w.H):
-            op = oracle.Params(s=p.s, B=p.B, P=p.P, W=p.W, K=p.K, prune=p.prune, sigma=sig[h], lam=lam[h],
-                               eps=p.eps)
-            ref = oracle.head(*(synth.to_f64(host[x][b, h], w.dtype) for x in "qkv"), None, op, N0, N0 + T)
+            op = pu.oracle_params(p, sig[h], lam[h])
+            x = tuple(synth.to_f64(host[t][b, h], w.dtype) for t in "qkv")
+            ref = pu.attach(oracle.head(*x, None, op, N0, N0 + T), x + (None,), op)
             c, s_ = pu.compare_head(sel[b, h], out[b, h], ref, p, w.dtype, i_lo=N0, what=f"decode b{b} h{h}")
             checked += c
             skipped += s_

@@ -88,6 +88,23 @@ def test_local_headline_shape_sampled():
     run_case(w, 512, heads=[(1, 7)], rows=(0, 400))
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_local_largest_window_sampled(dtype, d):
+    """w = 65535, the largest window accepted: each block walks about 2,050 key tiles,
+    so the tiles' stepped rotation angles must not drift (they are taken afresh from
+    fp64 every 16 tiles).  N = 70,000; the last 96 rows, whose windows are full, and
+    rows near the first block boundaries against the oracle."""
+    w = synth.Workload(batch=1, H=1, N=70000, d=d, dtype=dtype, seed=113, needle_frac=0.005)
+    run_case(w, 65535, rows=(w.N - 96, w.N))
+    run_case(w, 65535, rows=(65000, 65200))
+
+
+def test_local_rejects_window_past_limit():
+    q = torch.zeros(1, 1, 64, 64, device="cuda")
+    with pytest.raises(fsl.FslError):
+        fsl.fs_local_window(q, q, q, q.clone(), w=65536)
+
+
 def test_local_maximum_length_sampled():
     """N = 2^22, the longest sequence the ABI accepts: the last 300 rows against the oracle."""
     w = synth.Workload(batch=1, H=1, N=1 << 22, d=64, dtype="bf16", seed=112)
@@ -111,20 +128,22 @@ def test_local_rejects_bad_arguments():
 def test_full_attention_output_end_to_end(w):
     """The whole FreeSolo attention output of Eq. 2: the long-range prefill's output
     (Eqs. 5-9, 17) fed into the local branch with per-head alpha, against the oracle's
-    long-range output combined by the oracle's local branch (near-tie queries skipped)."""
+    long-range output combined by the oracle's local branch.  At near-tie queries the
+    long-range reference is the oracle's readout of the GPU's validated selection."""
     p = fsl.Params()
     host = pu.inputs(w)
     dq, dk, dv = (pu.to_device(host[x], w.dtype) for x in "qkv")
     alpha = np.linspace(0.5, 1.5, w.H).astype(np.float32)
     print(f"[gpu] full attention output {w}", flush=True)
-    o_lr, _, _ = fsl.prefill(dq, dk, dv, p, want_sel=False)
+    o_lr, sel, _ = fsl.prefill(dq, dk, dv, p)
     fsl.fs_local_window(dq, dk, dv, o_lr, w=512, alpha=alpha, o_lr=o_lr)  # in place: o_lr becomes o
     torch.cuda.synchronize()
     got = o_lr.float().cpu().numpy()
+    sel = sel.cpu().numpy()
     heads = [(b, h) for b in range(w.batch) for h in range(w.H)]
     refs = pu.run_oracle(w, host, p, heads)
     for (b, h), ref in refs.items():
-        skip = pu.excluded_queries(ref, p, 0, w.N)
+        lr_ref, _ = pu.lr_reference(sel[b, h], ref, p, 0, f"b{b} h{h}")
         full = oracle.local(*(synth.to_f64(host[x][b, h], w.dtype) for x in "qkv"), w=512, alpha=float(alpha[h]),
-                            o_lr=ref["out"])
-        pu.check_rows(got[b, h][~skip], full[~skip], w.dtype, f"full output b{b} h{h}", lr_scale=float(alpha[h]))
+                            o_lr=lr_ref)
+        pu.check_rows(got[b, h], full, w.dtype, f"full output b{b} h{h}", lr_scale=float(alpha[h]))

@@ -49,6 +49,16 @@ MUTATIONS = [
     ("local logits without 1/sqrt(d)", "logit[j - lo] = dot / sqrt((double)d);", "logit[j - lo] = dot;"),
     ("alpha on the local branch", "o[f] = u / z + (o_lr ? alpha * o_lr[(i - i_lo) * d + f] : 0.0);",
      "o[f] = alpha * u / z + (o_lr ? o_lr[(i - i_lo) * d + f] : 0.0);"),
+    ("gap_p one rank low", "*gap_p = relative_gap(order[cfg->P - 1].val, order[cfg->P].val);",
+     "*gap_p = relative_gap(order[cfg->P].val, order[cfg->P + 1 < n_avail ? cfg->P + 1 : cfg->P].val);"),
+    ("gap_p against the largest norm", "*gap_p = relative_gap(order[cfg->P - 1].val, order[cfg->P].val);",
+     "*gap_p = relative_gap(order[0].val, order[cfg->P].val);"),
+    ("readout reads the first selected cell for every cell", "for (int64_t j = T[t] * s; j < (T[t] + 1) * s; ++j)",
+     "for (int64_t j = T[0] * s; j < (T[0] + 1) * s; ++j)"),
+    ("gap_k term size without abs", "sum += fabs(q_i[f] * kbar_c[f]);", "sum += q_i[f] * kbar_c[f];"),
+    ("gap_k term size without the prior",
+     "return sum / sqrt((double)cfg->d) + cfg->lambda * a_c * fabs(prior_gate(cfg, i, c));",
+     "return sum / sqrt((double)cfg->d);"),
     ("keys rotated at the query position", "rope_rotate(k + j * d, d, (double)j, rope_base",
      "rope_rotate(k + j * d, d, (double)i_lo, rope_base"),
 ]

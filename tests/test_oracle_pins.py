@@ -193,6 +193,37 @@ def test_incremental_topp_eq15():
         assert list(got) == expect, blk
 
 
+def test_gap_p_known_boundary():
+    """gap_P is the relative gap |a_(P) - a_(P+1)| / max(|a_(P)|, |a_(P+1)|) between the P-th
+    and (P+1)-th largest key norms of the prefix (near-ties there decide which cell Eq. 8
+    keeps).  Hand-built norms with known gaps at every rank; +inf when there is no boundary."""
+    a = np.array([3.0, 10.0, 7.5, 9.0, 1.0, 8.0, 6.0])  # sorted: 10, 9, 8, 7.5, 6, 3, 1
+    srt = sorted(a, reverse=True)
+    for P in range(1, len(a)):
+        _, gap = oracle.retained(a, len(a), Params(P=P, W=0))
+        expect = (srt[P - 1] - srt[P]) / srt[P - 1]
+        assert gap == pytest.approx(expect, rel=1e-15), P
+    assert oracle.retained(a, len(a), Params(P=len(a), W=0))[1] == np.inf  # the whole prefix fits
+    assert oracle.retained(a, 4, Params(P=5, W=0))[1] == np.inf             # only the first 4 cells available
+    assert oracle.retained(a, len(a), Params(P=0, W=2))[1] == np.inf        # no TopP at all
+    # only the available prefix counts: cells 0..3 are 3, 10, 7.5, 9 -> P=2 boundary is 9 vs 7.5
+    assert oracle.retained(a, 4, Params(P=2, W=0))[1] == pytest.approx(1.5 / 9.0, rel=1e-15)
+    # an exact tie at the boundary has gap 0 (and the smaller id wins, App. C)
+    ids, gap = oracle.retained(np.array([5.0, 2.0, 5.0, 1.0]), 4, Params(P=1, W=0))
+    assert gap == 0.0 and list(ids) == [0]
+    # the per-block gap reported by the whole-head run is the same quantity
+    g = rng(18)
+    N, d = 2048, 4
+    k = g.normal(size=(N, d)) * g.lognormal(size=(N, 1))
+    prm = Params(P=5, W=2)
+    res = oracle.head(np.zeros((N, d)), k, np.zeros((N, d)), prm=prm, want_out=False)
+    for blk in range(1, N // 128):
+        n = blk * 4
+        srt = np.sort(res["a"][:n])[::-1]
+        expect = (srt[4] - srt[5]) / srt[4] if n > 5 else np.inf
+        assert res["gap_p"][blk] == pytest.approx(expect, rel=1e-14)
+
+
 # ---------------------------------------------------------- selection ------
 
 def test_topk_rank_count_and_gap():
@@ -213,9 +244,35 @@ def test_topk_rank_count_and_gap():
                 chosen.append((outrank, c))
         expect = [c for _, c in sorted(chosen)] + [-1] * (prm.K - len(chosen))
         assert list(res["sel"][i]) == expect
-        if len(A) > prm.K:
+        if len(A) > prm.K:  # measured against the term sizes, which are at least the scores
             rs = np.sort(r)[::-1]
-            assert res["gap_k"][i] == pytest.approx(abs(rs[prm.K - 1] - rs[prm.K]) / max(abs(rs[prm.K - 1]), abs(rs[prm.K])))
+            plain = abs(rs[prm.K - 1] - rs[prm.K]) / max(abs(rs[prm.K - 1]), abs(rs[prm.K]))
+            assert 0 <= res["gap_k"][i] <= plain * (1 + 1e-12)
+
+
+def test_gap_k_against_term_sizes_closed_form():
+    """The K/K+1 gap is taken relative to the size of the terms Eq. 7 sums,
+    sum_f |q_f kbar_f| / sqrt(d) + lambda a_c |g|, not to the scores themselves (content
+    terms can cancel; fp32 scores are exact only to roundings of that size).  s = 1 makes
+    kbar_c = k_c and a_c = |k_c|; a vanishing sigma makes g = 1 for every earlier cell."""
+    d, s, B = 2, 1, 4
+    k = np.array([[3.0, -2.0], [0.5, 0.4], [-1.0, -1.0], [0.1, 0.0], [0.0, 0.0], [0.0, 0.0], [0.0, 0.0],
+                  [0.0, 0.0]])
+    q = np.tile([1.0, 1.0], (len(k), 1))
+    # query 4 (block 1) sees cells 0..3 with content scores 1, 0.9, -2, 0.1 (times 1/sqrt 2)
+    res = oracle.head(q, k, np.zeros_like(k), prm=Params(s=s, B=B, K=1, prune=False, lam=0.0), want_out=False)
+    assert res["sel"][4][0] == 0
+    assert res["gap_k"][4] == pytest.approx(0.1 / 5.0, rel=1e-14)   # |1 - 0.9| / max(5, 0.9)
+    prm = Params(s=s, B=B, K=1, prune=False, lam=0.5, sigma=1e-9)
+    res = oracle.head(q, k, np.zeros_like(k), prm=prm, want_out=False)
+    r = [(1.0 + 0.5 * np.sqrt(13.0) * np.sqrt(2)) / np.sqrt(2), (0.9 + 0.5 * np.sqrt(0.41) * np.sqrt(2)) / np.sqrt(2)]
+    m = [(5.0 + 0.5 * np.sqrt(13.0) * np.sqrt(2)) / np.sqrt(2), (0.9 + 0.5 * np.sqrt(0.41) * np.sqrt(2)) / np.sqrt(2)]
+    assert oracle.cell_score(q[4], k[0], np.sqrt(13.0), 4, 0, prm) == pytest.approx(r[0], rel=1e-14)
+    assert oracle.cell_score_mag(q[4], k[0], np.sqrt(13.0), 4, 0, prm) == pytest.approx(m[0], rel=1e-14)
+    assert oracle.cell_score_mag(q[4], k[2], np.sqrt(2.0), 4, 2, prm) == pytest.approx(
+        (2.0 + 0.5 * np.sqrt(2.0) * np.sqrt(2)) / np.sqrt(2), rel=1e-14)          # |-1| + |-1|, no cancellation
+    # cell 2 scores (-2 + 1) / sqrt 2 < cell 1's; the boundary pair is cells 0 and 1
+    assert res["gap_k"][4] == pytest.approx((r[0] - r[1]) / max(m), rel=1e-13)
 
 
 # ------------------------------------------------------------ readout ------
@@ -281,6 +338,27 @@ def test_zero_query_reads_mean_value():
     for i in range(128, N, 37):
         toks = np.concatenate([np.arange(c * 32, (c + 1) * 32) for c in res["sel"][i] if c >= 0])
         np.testing.assert_allclose(res["out"][i], _rmsnorm(v[toks].mean(0), gain, 1e-8), rtol=1e-12, atol=1e-13)
+
+
+def test_readout_of_given_selection():
+    """Eq. 9 + Eq. 17 for a caller-given selection (the check of near-tie queries reads out
+    the GPU's own choice with it): brute-force softmax over exactly the listed cells' tokens,
+    -1 entries ignored, an empty selection gives 0, q = 0 gives the mean of the values."""
+    g = rng(19)
+    s, N, d = 32, 512, 8
+    q, k, v = (g.normal(size=(N, d)) for _ in range(3))
+    gain = g.uniform(0.5, 1.5, size=d)
+    prm = Params()
+    for cells in ([3], [0, 7, 2], [9, -1, 4, -1], [5, 1, 14, 6]):
+        toks = np.concatenate([np.arange(c * s, (c + 1) * s) for c in cells if c >= 0])
+        logits = k[toks] @ q[300] / np.sqrt(d)
+        w = np.exp(logits - logits.max()); w /= w.sum()
+        np.testing.assert_allclose(oracle.readout(q[300], k, v, cells, gain, prm),
+                                   _rmsnorm(w @ v[toks], gain, prm.eps), rtol=1e-12, atol=1e-13)
+    assert np.all(oracle.readout(q[300], k, v, [-1, -1], gain, prm) == 0)
+    toks = np.concatenate([np.arange(c * s, (c + 1) * s) for c in (2, 11)])
+    np.testing.assert_allclose(oracle.readout(np.zeros(d), k, v, [11, 2], None, prm),
+                               _rmsnorm(v[toks].mean(0), 1.0, prm.eps), rtol=1e-12, atol=1e-13)
 
 
 def test_rmsnorm_epsilon_placement(golden):
