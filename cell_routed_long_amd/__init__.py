@@ -74,6 +74,9 @@ def lib():
         L.fs_prefill_workspace_bytes.argtypes = [P_shape, P_prm]
         L.fs_prefill_workspace_bytes.restype = sz
         L.fs_longrange_prefill.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+        L.fs_noalloc_scratch_bytes.argtypes = []
+        L.fs_noalloc_scratch_bytes.restype = sz
+        L.fs_longrange_prefill_noalloc.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fs_decode_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, P_prm]
         L.fs_decode_state_bytes.restype = sz
         L.fs_longrange_decode.argtypes = [P_prm, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
@@ -86,7 +89,8 @@ def lib():
                                            i64, vp]
         L.fs_local_decode.argtypes = [i32, i32, i32, ctypes.c_int, i64, vp, sz, vp, vp, vp, vp, vp, vp, vp]
         for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout",
-                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_decode", "fs_local_window",
+                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_prefill_noalloc",
+                     "fs_longrange_decode", "fs_local_window",
                      "fs_local_state_build", "fs_local_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -210,6 +214,23 @@ def fs_longrange_prefill(q, k, v, sigma_h, lambda_h, gain, out, sel, state, work
     _check(lib().fs_longrange_prefill(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), sig, lam,
                                       _ptr(gain), _ptr(out), _ptr(sel), _ptr(state), st_bytes, _ptr(workspace),
                                       ws_bytes, _stream(stream)), "fs_longrange_prefill")
+
+
+def fs_noalloc_scratch_bytes() -> int:
+    return int(lib().fs_noalloc_scratch_bytes())
+
+
+def fs_longrange_prefill_noalloc(q, k, v, sigma_h, lambda_h, gain, out, sel, state=None,
+                                 params: Params = Params(), stream=None):
+    """fs_longrange_prefill with the library's fixed device scratch as workspace (no
+    allocation anywhere); see include/fsl.h."""
+    sh, prm = shape_of(k), params.c()
+    H = sh.H
+    sig, lam = _floats(sigma_h, H), _floats(lambda_h, H)
+    st_bytes = 0 if state is None else state.numel() * state.element_size()
+    _check(lib().fs_longrange_prefill_noalloc(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), sig,
+                                              lam, _ptr(gain), _ptr(out), _ptr(sel), _ptr(state), st_bytes,
+                                              _stream(stream)), "fs_longrange_prefill_noalloc")
 
 
 def fs_decode_state_bytes(batch: int, H: int, d: int, dtype_code: int, params: Params = Params()) -> int:

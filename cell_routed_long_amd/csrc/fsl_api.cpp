@@ -393,6 +393,40 @@ FSL_EXPORT size_t fs_prefill_workspace_bytes(const fs_shape *shape, const fs_par
     return prefill_layout(geometry(shape, prm)).total;
 }
 
+namespace fsl {
+
+fs_status prefill_check(const fs_shape *shape, const fs_params *prm, const void *q, const void *k, const void *v,
+                        const float *sigma_h, const float *lambda_h, void *out, int32_t *sel, void *state,
+                        size_t state_bytes, size_t *workspace_needed)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(shape->H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    if (!k || (!out && !sel && !state))
+        return FS_ERR_INVALID;
+    if ((out || sel) && !q)
+        return FS_ERR_INVALID;
+    if (out && !v)
+        return FS_ERR_INVALID;
+    if (state) {
+        st = check_decode_params(prm);
+        if (st != FS_OK)
+            return st;
+        if (!v)
+            return FS_ERR_INVALID;
+        if (state_bytes != fs_decode_state_bytes(shape->batch, shape->H, shape->d, shape->dtype, prm))
+            return FS_ERR_STATE;
+    }
+    *workspace_needed = prefill_layout(geometry(shape, prm)).total;
+    return FS_OK;
+}
+
+} // namespace fsl
+
 FSL_EXPORT fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
                                           const void *v, const float *sigma_h, const float *lambda_h,
                                           const float *gain, void *out, int32_t *sel, void *state,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fsl.h"
 #include "fsl_device.h"
 
 namespace fsl {
@@ -83,5 +84,11 @@ hipError_t launch_local_state_build(int32_t bh, int32_t d, int32_t bf16, const L
 hipError_t launch_local_decode(int32_t bh, int32_t H, int32_t d, int32_t bf16, const LocalStateLayout &L,
                                const LocalStateHeader &expect, const LocalConsts &lc, void *state, const void *q,
                                const void *k_new, const void *v_new, const void *o_lr, void *out, hipStream_t st);
+
+// Host-side checks of fs_longrange_prefill's arguments (everything but the
+// workspace); on FS_OK, *workspace_needed holds the workspace it needs.
+fs_status prefill_check(const fs_shape *shape, const fs_params *prm, const void *q, const void *k, const void *v,
+                        const float *sigma_h, const float *lambda_h, void *out, int32_t *sel, void *state,
+                        size_t state_bytes, size_t *workspace_needed);
 
 } // namespace fsl

@@ -199,6 +199,28 @@ fs_status fs_longrange_prefill(const fs_shape *shape, const fs_params *prm,
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fs_longrange_prefill without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid allocation).  Same arguments (less the workspace),
+ * results and errors as fs_longrange_prefill; the workspace is a fixed
+ * device array of fs_noalloc_scratch_bytes() (32 MiB) inside the library,
+ * one per GPU, held until the process ends.  Shapes whose
+ * fs_prefill_workspace_bytes() exceed it give FS_ERR_WORKSPACE before
+ * anything is enqueued (32 MiB covers, e.g., 2 sequences x 16 heads x 16384
+ * tokens at d = 128 in bf16; split larger batches into several calls).  The
+ * first call on a device looks up that device's copy of the array (no
+ * allocation; FS_ERR_HIP if the runtime refuses).  Every call on one GPU uses
+ * the same array: calls that overlap on one GPU (different streams, or
+ * unordered host threads) race; calls ordered on one stream do not.
+ */
+size_t fs_noalloc_scratch_bytes(void);
+fs_status fs_longrange_prefill_noalloc(const fs_shape *shape, const fs_params *prm,
+                                       const void *q, const void *k, const void *v,
+                                       const float *sigma_h, const float *lambda_h, const float *gain,
+                                       void *out, int32_t *sel, void *state, size_t state_bytes,
+                                       void *stream);
+
+/*
  * Streaming decode (Sec. 3.3 "Inference"; App. C "Bounded cache", Eq. 15).
  *
  * The decode state is one flat caller-owned device buffer: a 256-byte header

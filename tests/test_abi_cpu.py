@@ -257,3 +257,26 @@ def test_local_window_validation(L):
     assert call(o_lr=1) == fsl.FS_ERR_INVALID            # o_lr without alpha_h
     assert call(w=65536) == fsl.FS_ERR_UNSUPPORTED       # past the largest window
     assert call(w=65536, o_lr=1, al=alpha) == fsl.FS_ERR_UNSUPPORTED
+
+
+def test_noalloc_prefill_rejects_before_launch(L):
+    """fs_longrange_prefill_noalloc checks its arguments and the workspace the shape needs
+    against its fixed scratch on the host, before any HIP call."""
+    cap = fsl.fs_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    vp = ctypes.c_void_p
+    H = 16
+    sig = (ctypes.c_float * H)(*[4.0] * H)
+    lam = (ctypes.c_float * H)(*[1.0] * H)
+    p = prm()
+    big = shape(b=4, H=H, N=16384, d=128, dtype=fsl.FS_BF16)
+    assert fsl.fs_prefill_workspace_bytes(big) > cap
+    assert L.fs_longrange_prefill_noalloc(ctypes.byref(big), ctypes.byref(p), vp(1), vp(1), vp(1), sig, lam, None,
+                                          vp(1), None, None, 0, None) == fsl.FS_ERR_WORKSPACE
+    fits = shape(b=2, H=H, N=16384, d=128, dtype=fsl.FS_BF16)
+    assert fsl.fs_prefill_workspace_bytes(fits) <= cap
+    # invalid arguments are reported as for fs_longrange_prefill, also where the shape would not fit
+    assert L.fs_longrange_prefill_noalloc(ctypes.byref(big), ctypes.byref(p), vp(1), None, vp(1), sig, lam, None,
+                                          vp(1), None, None, 0, None) == fsl.FS_ERR_INVALID
+    assert L.fs_longrange_prefill_noalloc(ctypes.byref(fits), ctypes.byref(p), vp(1), vp(1), vp(1), sig, lam, None,
+                                          None, None, None, 0, None) == fsl.FS_ERR_INVALID
