@@ -23,14 +23,14 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfsl_oracle.so")
-_SRC = os.path.join(_HERE, "fsl_oracle.c")
+SOURCES = [os.path.join(_HERE, "fsl_oracle.c"), os.path.join(_HERE, "fsb_oracle.c")]
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (host only)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp, *SOURCES, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -40,6 +40,10 @@ class _Cfg(ctypes.Structure):
                 ("B", ctypes.c_int32), ("P", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("prune", ctypes.c_int32), ("sigma", ctypes.c_double),
                 ("lambda_", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+class _FsbCfg(ctypes.Structure):
+    _fields_ = [("tau", ctypes.c_double), ("Wb", ctypes.c_int32), ("c", ctypes.c_double)]
 
 
 _lib = None
@@ -63,6 +67,17 @@ def _bind(path: str):
     lib.oracle_cell_score_mag.restype = ctypes.c_double
     lib.oracle_readout.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, i64, vp]
     lib.oracle_readout.restype = None
+    lib.oracle_fsb_chunks.argtypes = [i64, vp]
+    lib.oracle_fsb_chunks.restype = ctypes.c_int32
+    lib.oracle_fsb_forest.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp, i64, i64] + [vp] * 11
+    lib.oracle_fsb_forest.restype = i64
+    lib.oracle_fsb_node_priority.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_FsbCfg), vp, i64, vp,
+                                             ctypes.c_double, ctypes.c_double, ctypes.c_double]
+    lib.oracle_fsb_node_priority.restype = ctypes.c_double
+    lib.oracle_fsb_rerank_score.argtypes = [ctypes.POINTER(_Cfg), vp, vp, ctypes.c_double, i64, i64, vp]
+    lib.oracle_fsb_rerank_score.restype = ctypes.c_double
+    lib.oracle_fsb_head.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_FsbCfg), vp, vp, vp, vp, i64, i64] + [vp] * 7
+    lib.oracle_fsb_head.restype = ctypes.c_int
     lib.oracle_local.argtypes = [i64, ctypes.c_int32, i64, ctypes.c_double, vp, vp, vp, ctypes.c_double, vp, i64, i64,
                                  vp]
     lib.oracle_local.restype = ctypes.c_int
@@ -250,3 +265,88 @@ def local(q, k, v, w: int = 512, rope_base: float = 10000.0, alpha: float = 0.0,
     if rc != 0:
         raise ValueError("oracle_local rejected its arguments")
     return out
+
+
+# ------------------------------------------------------------------ FS-B (Sec. 3.4; App. E.1) ----
+
+@dataclass(frozen=True)
+class FsbParams:
+    """FS-B parameters: the second forest's norm threshold tau (Eq. 10), the beam width W^b and
+    the radius weight c of Eq. 11 (the page uses W^b = 16, c = 8)."""
+    tau: float = 0.0
+    Wb: int = 16
+    c: float = 8.0
+
+    def cfg(self) -> _FsbCfg:
+        return _FsbCfg(self.tau, self.Wb, self.c)
+
+
+def fsb_chunks(M: int) -> list:
+    """Eq. 18: the chunk sizes of M admitted cells, largest first."""
+    sizes = np.zeros(64, dtype=np.int64)
+    r = _load().oracle_fsb_chunks(M, _p(sizes))
+    return [int(x) for x in sizes[:r]]
+
+
+def fsb_forest(kbar, a, cells, prm: Params = Params()):
+    """One forest (App. E.1) over the admitted `cells` (arrival order); returns a dict of node
+    arrays (count, cell, left, right, minid, mu, rho, A, pmin), the root and the smallest
+    median-split gap."""
+    kbar, a = _f64(kbar), _f64(a)
+    cells = np.ascontiguousarray(cells, dtype=np.int64)
+    M, d = len(cells), kbar.shape[1]
+    cap = max(1, 2 * M + 1)
+    out = {x: np.zeros(cap, dtype=np.int64) for x in ("count", "cell", "left", "right", "minid")}
+    out.update({x: np.zeros(cap) for x in ("rho", "A", "pmin")})
+    out["mu"] = np.zeros((cap, d))
+    n_nodes = np.zeros(1, dtype=np.int64)
+    gap = np.full(1, np.inf)
+    cfg = prm.cfg(kbar.shape[0] * prm.s, d)
+    root = _load().oracle_fsb_forest(ctypes.byref(cfg), _p(kbar), _p(a), _p(cells) if M else None, M, cap,
+                                     _p(out["count"]), _p(out["cell"]), _p(out["left"]), _p(out["right"]),
+                                     _p(out["minid"]), _p(out["mu"]), _p(out["rho"]), _p(out["A"]), _p(out["pmin"]),
+                                     _p(n_nodes), _p(gap))
+    n = int(n_nodes[0]) if root >= 0 else 0
+    res = {x: y[:n].copy() for x, y in out.items()}
+    res["root"] = int(root)
+    res["min_split_gap"] = float(gap[0])
+    return res
+
+
+def fsb_node_priority(q_i, i: int, mu, rho: float, A: float, pmin: float, prm: Params = Params(),
+                      fb: FsbParams = FsbParams()) -> float:
+    """Eq. 11 for one node summary."""
+    q_i, mu = _f64(q_i), _f64(mu)
+    cfg, fc = prm.cfg(0, len(q_i)), fb.cfg()
+    return float(_load().oracle_fsb_node_priority(ctypes.byref(cfg), ctypes.byref(fc), _p(q_i), i, _p(mu),
+                                                  float(rho), float(A), float(pmin)))
+
+
+def fsb_rerank_score(q_i, k, a_c: float, i: int, c: int, prm: Params = Params()):
+    """Eq. 12 for query i and cell c -> (score, size of its terms)."""
+    q_i, k = _f64(q_i), _f64(k)
+    mag = np.zeros(1)
+    cfg = prm.cfg(k.shape[0], k.shape[1])
+    r = _load().oracle_fsb_rerank_score(ctypes.byref(cfg), _p(q_i), _p(k), float(a_c), i, c, _p(mag))
+    return float(r), float(mag[0])
+
+
+def fsb_head(q, k, v, g=None, prm: Params = Params(), fb: FsbParams = FsbParams(), i_lo: int = 0,
+             i_hi: int | None = None, want_out: bool = True):
+    """FS-B for one (sequence, head): dict with sel [n, K], cand [n, 2 W^b], n_cand [n],
+    gap_beam, gap_rerank, gap_split [n], out [n, d], and the cell summaries kbar, a."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    N, d = k.shape
+    i_hi = N if i_hi is None else i_hi
+    n = i_hi - i_lo
+    res = {"sel": np.full((n, prm.K), -1, dtype=np.int32), "cand": np.full((n, 2 * fb.Wb), -1, dtype=np.int32),
+           "n_cand": np.zeros(n, dtype=np.int32), "gap_beam": np.zeros(n), "gap_rerank": np.zeros(n),
+           "gap_split": np.zeros(n), "out": np.zeros((n, d)) if want_out else None}
+    cfg, fc = prm.cfg(N, d), fb.cfg()
+    rc = _load().oracle_fsb_head(ctypes.byref(cfg), ctypes.byref(fc), _p(q), _p(k), _p(v), _p(g), i_lo, i_hi,
+                                 _p(res["sel"]), _p(res["cand"]), _p(res["n_cand"]), _p(res["gap_beam"]),
+                                 _p(res["gap_rerank"]), _p(res["gap_split"]), _p(res["out"]))
+    if rc != 0:
+        raise ValueError("oracle_fsb_head rejected its arguments")
+    res["kbar"], res["a"] = cell_summaries(k, prm)
+    return res

@@ -99,6 +99,55 @@ int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const d
 int oracle_local(int64_t N, int32_t d, int64_t w, double rope_base, const double *q, const double *k,
                  const double *v, double alpha, const double *o_lr, int64_t i_lo, int64_t i_hi, double *out);
 
+/* ---- FS-B (Sec. 3.4; App. E.1), in fsb_oracle.c ------------------------- */
+
+typedef struct {
+    double tau;  /* the second forest admits cells with a_c >= tau (Eq. 10) */
+    int32_t Wb;  /* beam width per forest (the page's W^b = 16) */
+    double c;    /* radius weight of Eq. 11 (the page's c = 8) */
+} oracle_fsb_cfg;
+
+/* Eq. 18: the binary decomposition of M, largest chunk first; returns r. */
+int32_t oracle_fsb_chunks(int64_t M, int64_t *sizes);
+
+/* One forest (App. E.1) over M admitted cells `cells` (ids, arrival order) with
+ * mean keys kbar [*, d] and norms a: node arrays of at most cap entries
+ * (count = cells below, cell = the cell of a leaf or -1, left/right children
+ * or -1, minid = smallest cell id below, mu [n, d], rho, A, pmin = p_v^min).
+ * Returns the root (-1 when M = 0, -2 when cap is too small); *n_nodes gets
+ * the node count and *min_split_gap the smallest relative gap of the two
+ * projections straddling any median split. */
+int64_t oracle_fsb_forest(const oracle_cfg *cfg, const double *kbar, const double *a, const int64_t *cells,
+                          int64_t M, int64_t cap, int64_t *count, int64_t *cell, int64_t *left, int64_t *right,
+                          int64_t *minid, double *mu, double *rho, double *A, double *pmin, int64_t *n_nodes,
+                          double *min_split_gap);
+
+/* Eq. 11 for one node summary (mu [d], rho, A, pmin) and query i. */
+double oracle_fsb_node_priority(const oracle_cfg *cfg, const oracle_fsb_cfg *fb, const double *q_i, int64_t i,
+                                const double *mu, double rho, double A, double pmin);
+
+/* Eq. 12 for query i and cell c (k [N, d] holds the cell's tokens); *mag (may be
+ * NULL) gets the size of its terms. */
+double oracle_fsb_rerank_score(const oracle_cfg *cfg, const double *q_i, const double *k, double a_c, int64_t i,
+                               int64_t c, double *mag);
+
+/*
+ * FS-B for one (sequence, head), queries i in [i_lo, i_hi): both forests over
+ * the block's available cells, a beam of W^b per forest, the union of the
+ * leaves reached reranked by Eq. 12, the min(K, |B_i|) best read out (Eq. 9,
+ * Eq. 17).  Outputs per query row (each may be NULL):
+ *   sel [n, K] (reranked score desc, id asc; -1 padded), cand [n, 2 W^b] the
+ *   candidate cells B_i ascending (-1 padded), n_cand [n] = |B_i|,
+ *   gap_beam [n] smallest beam-cut gap (relative to the larger term size),
+ *   gap_rerank [n] K/K+1 gap of the reranked scores (relative to term size),
+ *   gap_split [n] smallest median-split gap of the query's block's forests,
+ *   out [n, d].
+ * Returns 0, or -1 for invalid arguments.
+ */
+int oracle_fsb_head(const oracle_cfg *cfg, const oracle_fsb_cfg *fb, const double *q, const double *k,
+                    const double *v, const double *g, int64_t i_lo, int64_t i_hi, int32_t *sel, int32_t *cand,
+                    int32_t *n_cand, double *gap_beam, double *gap_rerank, double *gap_split, double *out);
+
 #ifdef __cplusplus
 }
 #endif

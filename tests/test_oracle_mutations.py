@@ -1,6 +1,7 @@
 """The oracle's pins must be able to fail.
 
-Each case plants one plausible mistake in a private copy of the oracle's C source
+Each case plants one plausible mistake in a private copy of one of the oracle's C
+sources (fsl_oracle.c: FS / FS-L and the local branch; fsb_oracle.c: FS-B)
 (a wrong sign, a dropped term, an off-by-one index, a swapped operand, a reversed
 tie rule), builds it with gcc on the CPU, and runs the pin suite against it: at
 least one pin must fail for every planted mistake.  The shipped oracle is never
@@ -12,9 +13,12 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_fsb_oracle_pins as fsb_pins
 from tests import test_oracle_pins as pins
 
-ORACLE_SRC = os.path.join(os.path.dirname(oracle.__file__), "fsl_oracle.c")
+ORACLE_DIR = os.path.dirname(oracle.__file__)
+ORACLE_SRC = os.path.join(ORACLE_DIR, "fsl_oracle.c")
+FSB_SRC = os.path.join(ORACLE_DIR, "fsb_oracle.c")
 
 # (name, original text, planted text)
 MUTATIONS = [
@@ -64,32 +68,70 @@ MUTATIONS = [
 ]
 
 
+# planted in fsb_oracle.c (FS-B: Sec. 3.4; App. E.1)
+FSB_MUTATIONS = [
+    ("chunks smallest first", "for (int k = 62; k >= 0; --k) /* powers of two of M, largest first */",
+     "for (int k = 0; k <= 62; ++k) /* powers of two of M, largest first */"),
+    ("split sorted descending", "    if (p->val < q->val) return -1;\n    if (p->val > q->val) return 1;\n    return (p->id",
+     "    if (p->val > q->val) return -1;\n    if (p->val < q->val) return 1;\n    return (p->id"),
+    ("node mean not divided by n", "mu[f] = s / (double)n;", "mu[f] = s;"),
+    ("chunk radius from the first cell only", "        if (r > rho)\n            rho = r;",
+     "        if (x == 0)\n            rho = r;"),
+    ("join radius without the centre shift", "const double ra = F->rho[a_] + dist(F->mu + a_ * d, mu, d);",
+     "const double ra = F->rho[a_];"),
+    ("join centre unweighted", "mu[f] = (na * F->mu[a_ * d + f] + nb * F->mu[b_ * d + f]) / (na + nb);",
+     "mu[f] = (F->mu[a_ * d + f] + F->mu[b_ * d + f]) / 2.0;"),
+    ("node norm is the smallest", "        if (a[cells[x]] > A)\n            A = a[cells[x]];",
+     "        if (A == -INFINITY || a[cells[x]] < A)\n            A = a[cells[x]];"),
+    ("p_min from the latest cell", "        if (cells[x] < mn)\n            mn = cells[x];",
+     "        if (cells[x] > mn)\n            mn = cells[x];"),
+    ("priority without the radius term", "const double spread = fb->c * q_norm(q, d) * F->rho[v];",
+     "const double spread = 0.0;"),
+    ("priority prior at the node's end", "const double g = erf(((double)i - F->pmin[v]) / (2.0 * cfg->sigma)); /* g_h(i - p_v^min) */",
+     "const double g = erf(((double)i - F->pmin[v] - 64.0 * F->count[v]) / (2.0 * cfg->sigma)); /* g_h(i - p_v^min) */"),
+    ("leaves compete for their slots", "                leaves[n_leaf++] = beam[x]; /* a leaf keeps its slot */",
+     "                kids[n_kid++] = beam[x];"),
+    ("second forest admits above the threshold only", "if (a[c] >= fb->tau)", "if (a[c] > fb->tau)"),
+    ("rerank without the log", "return mx + log(z) + cfg->lambda * a_c * g;", "return mx + z + cfg->lambda * a_c * g;"),
+    ("rerank without the prior", "return mx + log(z) + cfg->lambda * a_c * g;", "return mx + log(z);"),
+    ("rerank logits without 1/sqrt(d)", "        l[t] = dot / sqrt((double)d);", "        l[t] = dot;"),
+    ("selection by the worst candidates", "while (y >= 0 && (rank[y].val < kv.val ||", "while (y >= 0 && (rank[y].val > kv.val ||"),
+    ("power iteration started at the nearest cell", "if (nrm > best || (nrm == best && cells[c] < bestid)) {",
+     "if (best < 0 || nrm < best || (nrm == best && cells[c] < bestid)) {"),
+]
+
+
 def _pin_functions(golden):
-    """Every pin as a zero-argument callable."""
+    """Every pin of both suites as a zero-argument callable."""
     calls = []
-    for name in dir(pins):
-        fn = getattr(pins, name)
-        if not name.startswith("test_") or not callable(fn):
-            continue
-        if name == "test_retention_brute_force":
-            for P, W in [(0, 3), (3, 0), (4, 2), (7, 5)]:
-                calls.append((f"{name}[{P},{W}]", lambda fn=fn, P=P, W=W: fn(P, W)))
-        elif fn.__code__.co_argcount == 1:
-            calls.append((name, lambda fn=fn: fn(golden)))
-        else:
-            calls.append((name, fn))
+    for mod in (pins, fsb_pins):
+        for name in dir(mod):
+            fn = getattr(mod, name)
+            if not name.startswith("test_") or not callable(fn):
+                continue
+            marks = getattr(fn, "pytestmark", [])
+            params = [m for m in marks if m.name == "parametrize"]
+            if params:
+                argnames = [x.strip() for x in params[0].args[0].split(",")]
+                for vals in params[0].args[1]:
+                    vals = vals if isinstance(vals, tuple) else (vals,)
+                    calls.append((f"{name}{vals}", lambda fn=fn, a=dict(zip(argnames, vals)): fn(**a)))
+            elif fn.__code__.co_argcount == 1:
+                calls.append((name, lambda fn=fn: fn(golden)))
+            else:
+                calls.append((name, fn))
     return calls
 
 
-@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_planted_mistake(name, old, new, tmp_path, golden):
-    src = open(ORACLE_SRC).read()
+def _check_caught(src_path, name, old, new, tmp_path, golden):
+    src = open(src_path).read()
     assert src.count(old) == 1, f"mutation site for '{name}' not found exactly once"
-    mutated = tmp_path / "fsl_oracle_mut.c"
+    mutated = tmp_path / os.path.basename(src_path)
     mutated.write_text(src.replace(old, new))
+    others = [s for s in oracle.SOURCES if os.path.basename(s) != os.path.basename(src_path)]
     lib = tmp_path / "libmut.so"
-    inc = os.path.dirname(ORACLE_SRC)
-    subprocess.check_call(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-I", inc, "-o", str(lib), str(mutated), "-lm"])
+    subprocess.check_call(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-I", ORACLE_DIR, "-o", str(lib),
+                           str(mutated), *others, "-lm"])
     failed = []
     with oracle.use_library(str(lib)):
         for pin_name, call in _pin_functions(golden):
@@ -98,3 +140,13 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path, golden):
             except (AssertionError, ValueError, FloatingPointError):
                 failed.append(pin_name)
     assert failed, f"no pin caught the planted mistake '{name}'"
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, old, new, tmp_path, golden):
+    _check_caught(ORACLE_SRC, name, old, new, tmp_path, golden)
+
+
+@pytest.mark.parametrize("name,old,new", FSB_MUTATIONS, ids=[m[0] for m in FSB_MUTATIONS])
+def test_fsb_pins_catch_planted_mistake(name, old, new, tmp_path, golden):
+    _check_caught(FSB_SRC, name, old, new, tmp_path, golden)
