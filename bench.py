@@ -50,6 +50,7 @@ WORKLOADS = {
     "decode_256k": dict(prune=True, decode=True),
     "local_16k": dict(prune=True, local=True),
     "local_decode_256k": dict(prune=True, local_decode=True),
+    "fsb_16k": dict(fsb=True),
 }
 DECODE_PREFIX = 262144
 DECODE_LAYER_STATES = 12  # independent states in rotation: 12 x ~26 MB per step exceeds the 256 MB MALL
@@ -197,6 +198,8 @@ def main() -> int:
         return run_local_decode(args)
     if WORKLOADS[args.workload].get("local"):
         return run_local(args)
+    if WORKLOADS[args.workload].get("fsb"):
+        return run_fsb(args)
 
     wl = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wl.get("inputs", args.workload)]
@@ -419,6 +422,137 @@ def main() -> int:
         "single_call_ms": round(single_ms, 4),
         "single_call_matches_staged": same,
         "parity_spot_check": parity,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+FSB_METRIC = "long-range FS-B query-tokens/s at 16k prefill (W^b=16, c=8); % roofline"
+
+
+def run_fsb(args) -> int:
+    """FS-B (Sec. 3.4; App. E.1) on the headline prefill's inputs, b4 H16 d128 N16384
+    bf16, W^b = 16, c = 8, K = 4: one step is one fs_fsb_prefill call (fp64 summaries,
+    the second forest's admission, both forests' chunk trees, the beam search with the
+    rerank, and the readout).  tau_h is the median cell norm of a separate 4096-token
+    calibration window per head, computed once with fs_cell_summaries."""
+    import numpy as np
+    import torch
+
+    import cell_routed_long_amd as fsl
+    import synth
+
+    w = synth.WORKLOADS["prefill_16k"]
+    prm, fb = fsl.Params(), fsl.FsbParams()
+    sigma, lam = 4.0, 1.0
+    dev = torch.device("cuda:0")
+    host = {x: synth.tensor(w, x) for x in "qkv"}
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = (to_dev(host[x]) for x in "qkv")
+    b, H, N, d = q.shape
+    # tau_h: median cell norm of a calibration window drawn like the keys with another seed
+    cal = synth.Workload(batch=1, H=H, N=4096, d=d, dtype="bf16", seed=w.seed + 1000, needle_frac=w.needle_frac)
+    kc = to_dev(synth.tensor(cal, "k"))
+    kbc = torch.empty(1, H, 128, d, dtype=torch.float32, device=dev)
+    ac = torch.empty(1, H, 128, dtype=torch.float32, device=dev)
+    fsl.fs_cell_summaries(kc, kbc, ac)
+    tau = [float(x) for x in torch.median(ac[0], dim=1).values.cpu()]
+    sh = fsl.shape_of(k)
+    ws = torch.empty(fsl.fs_fsb_workspace_bytes(sh, prm, fb), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    sel = torch.empty(b, H, N, prm.K, dtype=torch.int32, device=dev)
+    cand = torch.empty(b, H, N, 2 * fb.Wb, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fsl.fs_fsb_prefill(q, k, v, sigma, lam, tau, None, out, sel, cand, ws, prm, fb)
+
+    settle = settle_clocks(step, 1.0)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = b * N / (ms * 1e-3)
+    cand_h = cand.cpu().numpy()
+    n_cand = (cand_h >= 0).sum(-1)
+    sel_h = sel.cpu().numpy()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # algorithmic work of the call (the page's cost, App. E.2): per query and forest, W^b
+    # children of 2 d FLOP on each of ceil(log2 M) levels; the rerank, 2 s d FLOP per
+    # candidate cell; the readout, 4 s d FLOP per selected cell.  Bytes: q, k, v, out once,
+    # plus the fp64 summaries and the node tables written and read once.
+    NB = (N + prm.B - 1) // prm.B
+    Mb = np.minimum(np.arange(NB) * (prm.B // prm.s), N // prm.s)
+    lev = np.where(Mb > 1, np.ceil(np.log2(np.maximum(Mb, 1))), 0.0)
+    search_flop = float(b * H * prm.B * 2 * (2 * fb.Wb * lev).sum() * 2 * d)
+    rerank_flop = float(n_cand.sum()) * prm.s * 2 * d
+    read_flop = float((sel_h >= 0).sum()) * prm.s * 4 * d
+    flop = search_flop + rerank_flop + read_flop
+    M = N // prm.s
+    alg_bytes = 4 * b * H * N * d * 2 + b * H * M * d * (4 + 8) * 2 + b * H * 2 * (2 * M) * (d * 4 + 16) * 2
+    roofline = {"bound": "mfma", "achieved": round(flop / (ms * 1e-3) / 1e12, 2), "peak": 157.3, "unit": "TFLOP/s",
+                "frac": round(flop / (ms * 1e-3) / 1e12 / 157.3, 4), "traffic": None, "kernel": "fs_fsb_prefill",
+                "alg_flop_per_launch": flop, "alg_bytes_per_launch": int(alg_bytes),
+                "hbm_frac_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "fp32 matrix-core peak (node priorities); all kernels of the call"}
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle_threads()
+        heads = [(bb, hh) for bb in range(b) for hh in range(0, H, 4)]
+        op = oracle.Params(s=prm.s, B=prm.B, K=prm.K, sigma=sigma, lam=lam, eps=prm.eps)
+        x64 = {bh: tuple(synth.to_f64(host[t][bh[0], bh[1]], "bf16") for t in "qkv") for bh in heads}
+
+        def one(bh):
+            return bh, oracle.fsb_head(*x64[bh], None, op, oracle.FsbParams(tau=tau[bh[1]], Wb=fb.Wb, c=fb.c))
+
+        t1 = single_thread_seconds(one, heads[0])
+        refs, passes, cpu_s = time_oracle(one, heads, threads)
+        model, visible = host_cpu()
+        cpu = {"value": round(passes * len(heads) * N / H / cpu_s, 1), "unit": "query-tokens/s", "cores": threads,
+               "kind": "oracle", "cpu_model": model, "host_cpus_visible": visible,
+               "single_thread_s_per_pair": round(t1, 3),
+               "sample": f"{len(heads)} of {b * H} (sequence, head) pairs, all {N} queries each, {passes} passes; "
+                         f"{cpu_s:.1f}s wall"}
+        out_h = out.float().cpu().numpy()
+        mism = ties = 0
+        worst = 0.0
+        for (bb, hh), ref in refs.items():
+            tie = (ref["gap_beam"] < 1e-6) | (ref["gap_rerank"] < 1e-6) | (ref["gap_split"] < 1e-9)
+            ok = ~tie
+            ties += int(tie.sum())
+            mism += int(np.any(sel_h[bb, hh][ok] != ref["sel"][ok], axis=1).sum())
+            mism += int(np.any(cand_h[bb, hh][ok] != ref["cand"][ok], axis=1).sum())
+            worst = max(worst, float(np.abs(out_h[bb, hh][ok] - ref["out"][ok]).max()))
+        parity = {"heads": len(heads), "queries_exact": len(heads) * N - ties, "near_ties": ties,
+                  "selection_or_candidate_mismatches": mism, "max_abs_err": worst}
+        log(f"[bench] oracle {cpu_s:.1f}s on {threads} threads; parity {parity}")
+
+    result = {
+        "metric": FSB_METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "FS-B prefill b4 H16 d128 N16384 bf16, 0.5% needles", "batch": b, "heads": H,
+                   "seq_len": N, "head_dim": d, "s": prm.s, "B": prm.B, "K": prm.K, "Wb": fb.Wb, "c": fb.c,
+                   "sigma_h": sigma, "lambda_h": lam, "tau_h": [round(t_, 4) for t_ in tau],
+                   "mean_candidates_per_query": round(float(n_cand[:, :, prm.B:].mean()), 3)},
+        "roofline": roofline, "cpu_baseline": cpu, "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "settle_steps": settle, "parity_spot_check": parity,
     }
     print(json.dumps(result), flush=True)
     return 0

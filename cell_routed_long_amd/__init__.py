@@ -35,6 +35,20 @@ class fs_shape(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class fs_fsb_params(ctypes.Structure):
+    _fields_ = [("Wb", ctypes.c_int32), ("c", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class FsbParams:
+    """FS-B search parameters (Sec. 3.4): beam width W^b and the radius weight c of Eq. 11."""
+    Wb: int = 16
+    c: float = 8.0
+
+    def c_struct(self) -> fs_fsb_params:
+        return fs_fsb_params(self.Wb, self.c)
+
+
 @dataclass(frozen=True)
 class Params:
     """Method parameters; defaults are the page's (App. A)."""
@@ -77,6 +91,10 @@ def lib():
         L.fs_noalloc_scratch_bytes.argtypes = []
         L.fs_noalloc_scratch_bytes.restype = sz
         L.fs_longrange_prefill_noalloc.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        P_fsb = ctypes.POINTER(fs_fsb_params)
+        L.fs_fsb_workspace_bytes.argtypes = [P_shape, P_prm, P_fsb]
+        L.fs_fsb_workspace_bytes.restype = sz
+        L.fs_fsb_prefill.argtypes = [P_shape, P_prm, P_fsb, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fs_decode_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, P_prm]
         L.fs_decode_state_bytes.restype = sz
         L.fs_longrange_decode.argtypes = [P_prm, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
@@ -89,7 +107,7 @@ def lib():
                                            i64, vp]
         L.fs_local_decode.argtypes = [i32, i32, i32, ctypes.c_int, i64, vp, sz, vp, vp, vp, vp, vp, vp, vp]
         for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout",
-                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_prefill_noalloc",
+                     "fs_select_readout", "fs_longrange_prefill", "fs_longrange_prefill_noalloc", "fs_fsb_prefill",
                      "fs_longrange_decode", "fs_local_window",
                      "fs_local_state_build", "fs_local_decode"):
             getattr(L, name).restype = ctypes.c_int
@@ -249,6 +267,22 @@ def fs_longrange_decode(state, q, k_new, v_new, sigma_h, lambda_h, gain, out, se
                                      lam, _ptr(gain), _ptr(out), _ptr(sel), _stream(stream)), "fs_longrange_decode")
 
 
+def fs_fsb_workspace_bytes(sh: fs_shape, params: Params = Params(), fsb: FsbParams = FsbParams()) -> int:
+    prm, fb = params.c(), fsb.c_struct()
+    return int(lib().fs_fsb_workspace_bytes(ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(fb)))
+
+
+def fs_fsb_prefill(q, k, v, sigma_h, lambda_h, tau_h, gain, out, sel, cand, workspace, params: Params = Params(),
+                   fsb: FsbParams = FsbParams(), stream=None):
+    """FS-B over a whole prompt (Sec. 3.4; App. E.1); see include/fsl.h."""
+    sh, prm, fb = shape_of(k), params.c(), fsb.c_struct()
+    H = sh.H
+    sig, lam, tau = _floats(sigma_h, H), _floats(lambda_h, H), _floats(tau_h, H)
+    _check(lib().fs_fsb_prefill(ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(fb), _ptr(q), _ptr(k), _ptr(v), sig,
+                                lam, tau, _ptr(gain), _ptr(out), _ptr(sel), _ptr(cand), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)), "fs_fsb_prefill")
+
+
 # ------------------------------------------------------- allocation helpers --
 
 def new_state(batch: int, H: int, d: int, dtype, params: Params = Params(), device="cuda"):
@@ -343,3 +377,22 @@ def new_local_state(batch: int, H: int, d: int, dtype, w: int = 512, device="cud
     if n == 0:
         raise FslError(FS_ERR_UNSUPPORTED, "fs_local_state_bytes")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fsb_prefill(q, k, v, tau, params: Params = Params(), fsb: FsbParams = FsbParams(), sigma=4.0, lam=1.0,
+                gain=None, want_out=True, want_sel=True, want_cand=False, workspace=None, stream=None):
+    """Allocate outputs and workspace with torch and run fs_fsb_prefill; tau is a float or
+    [H] floats.  Returns (out or None, sel or None, cand or None, workspace)."""
+    import torch
+    sh = shape_of(k)
+    ws_bytes = fs_fsb_workspace_bytes(sh, params, fsb)
+    if ws_bytes == 0:
+        raise FslError(FS_ERR_UNSUPPORTED, "fs_fsb_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
+    b, H, N, _ = k.shape
+    out = torch.empty_like(k) if want_out else None
+    sel = torch.empty(b, H, N, params.K, dtype=torch.int32, device=k.device) if want_sel else None
+    cand = torch.empty(b, H, N, 2 * fsb.Wb, dtype=torch.int32, device=k.device) if want_cand else None
+    fs_fsb_prefill(q, k, v, sigma, lam, tau, gain, out, sel, cand, workspace, params, fsb, stream)
+    return out, sel, cand, workspace

@@ -265,6 +265,75 @@ fs_status local_alpha(int32_t H, const float *alpha_h, const void *o_lr, LocalCo
     return FS_OK;
 }
 
+// ---- FS-B ----
+FsbLayout fsb_layout(const Geometry &g)
+{
+    FsbLayout L;
+    std::memset(&L, 0, sizeof(L));
+    const int64_t last = (int64_t)(g.NB - 1) * (g.B / g.s); // cells available to the last block
+    L.Mu = g.M < last ? g.M : last;
+    int levels = 0;
+    while (levels < kFsbMaxLevels && ((int64_t)1 << levels) <= L.Mu)
+        ++levels;
+    L.levels = levels;
+    for (int k = 0; k < levels; ++k) {
+        const int64_t chunks = ((L.Mu >> k) + 1) / 2; // chunks of 2^k cells at even multiples of 2^k
+        L.chunk_base[k + 1] = L.chunk_base[k] + chunks;
+        L.node_base[k + 1] = L.node_base[k] + chunks * ((int64_t(2) << k) - 1);
+    }
+    L.chunks = L.chunk_base[levels];
+    L.nodes = L.node_base[levels];
+    return L;
+}
+
+struct FsbWorkspace {
+    size_t kbar, kbar64, a, a64, adm, cnt, node_mu, node_meta, sel, total;
+};
+
+FsbWorkspace fsb_workspace(const Geometry &g, const FsbLayout &L)
+{
+    FsbWorkspace W;
+    size_t off = 0;
+    const size_t cells = (size_t)g.bh * (g.M > 0 ? g.M : 1);
+    W.kbar = off;
+    off += align_up(cells * g.d * sizeof(float));
+    W.kbar64 = off;
+    off += align_up(cells * g.d * sizeof(double));
+    W.a = off;
+    off += align_up(cells * sizeof(float));
+    W.a64 = off;
+    off += align_up(cells * sizeof(double));
+    W.adm = off;
+    off += align_up(cells * sizeof(int32_t));
+    W.cnt = off;
+    off += align_up((size_t)g.bh * (g.M + 1) * sizeof(int32_t));
+    W.node_mu = off;
+    off += align_up((size_t)g.bh * 2 * (L.nodes > 0 ? L.nodes : 1) * g.d * sizeof(float));
+    W.node_meta = off;
+    off += align_up((size_t)g.bh * 2 * (L.nodes > 0 ? L.nodes : 1) * sizeof(FsbNodeMeta));
+    W.sel = off;
+    off += align_up((size_t)g.bh * g.N * g.K * sizeof(int32_t));
+    W.total = off;
+    return W;
+}
+
+fs_status check_fsb(const fs_shape *shape, const fs_params *prm, const fs_fsb_params *fb)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    if (!fb)
+        return FS_ERR_INVALID;
+    if (fb->Wb < 1 || !(fb->c >= 0.0f) || !std::isfinite(fb->c))
+        return FS_ERR_INVALID;
+    if (fb->Wb > kFsbMaxBeam)
+        return FS_ERR_UNSUPPORTED;
+    const Geometry g = geometry(shape, prm);
+    if (fsb_layout(g).Mu > kFsbMaxCells)
+        return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
 } // namespace
 } // namespace fsl
 
@@ -598,4 +667,60 @@ FSL_EXPORT fs_status fs_local_decode(int32_t batch, int32_t H, int32_t d, fs_dty
     const LocalStateHeader expect = local_header(batch, H, d, dtype, w, 0.0f, L);
     return hip_status(launch_local_decode(batch * H, H, d, dtype == FS_BF16 ? 1 : 0, L, expect, lc, state, q, k_new,
                                           v_new, o_lr, out, static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT size_t fs_fsb_workspace_bytes(const fs_shape *shape, const fs_params *prm, const fs_fsb_params *fb)
+{
+    if (check_fsb(shape, prm, fb) != FS_OK)
+        return 0;
+    const Geometry g = geometry(shape, prm);
+    return fsb_workspace(g, fsb_layout(g)).total;
+}
+
+FSL_EXPORT fs_status fs_fsb_prefill(const fs_shape *shape, const fs_params *prm, const fs_fsb_params *fb,
+                                    const void *q, const void *k, const void *v, const float *sigma_h,
+                                    const float *lambda_h, const float *tau_h, const float *gain, void *out,
+                                    int32_t *sel, int32_t *cand, void *workspace, size_t workspace_bytes,
+                                    void *stream)
+{
+    fs_status st = check_fsb(shape, prm, fb);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(shape->H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    if (!q || !k || !tau_h || !workspace || (!out && !sel && !cand) || (out && !v))
+        return FS_ERR_INVALID;
+    FsbConsts fc;
+    std::memset(&fc, 0, sizeof(fc));
+    for (int h = 0; h < shape->H; ++h) {
+        if (!std::isfinite(tau_h[h]))
+            return FS_ERR_INVALID;
+        fc.tau[h] = (double)tau_h[h];
+    }
+    fc.Wb = fb->Wb;
+    fc.c = fb->c;
+    const Geometry g = geometry(shape, prm);
+    const FsbLayout L = fsb_layout(g);
+    const FsbWorkspace W = fsb_workspace(g, L);
+    if (workspace_bytes < W.total)
+        return FS_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *kbar = reinterpret_cast<float *>(ws + W.kbar);
+    double *kbar64 = reinterpret_cast<double *>(ws + W.kbar64);
+    float *a = reinterpret_cast<float *>(ws + W.a);
+    double *a64 = reinterpret_cast<double *>(ws + W.a64);
+    int32_t *adm = reinterpret_cast<int32_t *>(ws + W.adm);
+    int32_t *cnt = reinterpret_cast<int32_t *>(ws + W.cnt);
+    float *node_mu = reinterpret_cast<float *>(ws + W.node_mu);
+    FsbNodeMeta *node_meta = reinterpret_cast<FsbNodeMeta *>(ws + W.node_meta);
+    int32_t *sel_buf = sel ? sel : reinterpret_cast<int32_t *>(ws + W.sel);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_cell_summaries(g, k, kbar, a, nullptr, nullptr, s, kbar64, a64);
+    if (e == hipSuccess)
+        e = launch_fsb(g, L, hc, fc, q, k, kbar64, a, a64, adm, cnt, node_mu, node_meta, sel_buf, cand, s);
+    if (e == hipSuccess && out)
+        e = launch_readout(g, q, k, v, sel_buf, gain, out, s);
+    return hip_status(e);
 }

@@ -27,8 +27,9 @@ struct Geometry {
 
 // kbar_split (optional): [bh, M, 3, d] bf16 hi/mid/lo parts of kbar.
 // kbar_norm (optional): [bh, M] fp32 Euclidean norms of kbar.
+// kbar64 [bh, M, d], a64 [bh, M] (optional): the same summaries before the rounding to fp32.
 hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split,
-                                 float *kbar_norm, hipStream_t st);
+                                 float *kbar_norm, hipStream_t st, double *kbar64 = nullptr, double *a64 = nullptr);
 
 // death[c]: first query block whose TopP no longer holds cell c (INT32_MAX: never leaves).
 // ord: [bh, M] scratch (the head's cells in priority order, with their exit blocks).
@@ -84,6 +85,42 @@ hipError_t launch_local_state_build(int32_t bh, int32_t d, int32_t bf16, const L
 hipError_t launch_local_decode(int32_t bh, int32_t H, int32_t d, int32_t bf16, const LocalStateLayout &L,
                                const LocalStateHeader &expect, const LocalConsts &lc, void *state, const void *q,
                                const void *k_new, const void *v_new, const void *o_lr, void *out, hipStream_t st);
+
+// ---- FS-B (Sec. 3.4; App. E.1): two causal forests, beam search, token rerank ----
+constexpr int kFsbMaxBeam = 16;          // W^b
+constexpr int64_t kFsbMaxCells = 4096;   // admitted cells per forest (N <= 131,072 at s = 32)
+constexpr int kFsbMaxLevels = 13;        // chunk sizes 2^0 .. 2^12
+
+// Per-node summary (Eq. 20/21) beside the fp32 mean key: radius, largest norm,
+// smallest cell id below (p_min = (minid + 1/2) s) and, for a leaf, its cell (-1 otherwise).
+struct FsbNodeMeta {
+    float rho, A;
+    int32_t minid, cell;
+};
+
+// Storage of one forest's chunk trees for one head: every aligned chunk of 2^k
+// admitted cells that starts at an even multiple of 2^k (the only ones a binary
+// decomposition uses), heap-ordered (node h of a chunk, 1 <= h < 2^(k+1), at h - 1).
+struct FsbLayout {
+    int64_t Mu;                           // cells the forests can hold: the last block's available cells
+    int32_t levels;                       // chunk levels k = 0 .. levels - 1
+    int64_t chunk_base[kFsbMaxLevels + 1]; // first chunk of level k, per forest
+    int64_t node_base[kFsbMaxLevels + 1];  // first node of level k, per forest
+    int64_t chunks, nodes;                 // per forest
+};
+
+struct FsbConsts {
+    double tau[128]; // the second forest admits cells with a_c >= tau_h (Eq. 10)
+    int32_t Wb;      // beam width
+    float c;         // radius weight of Eq. 11
+};
+
+// Admission of the second forest, chunk trees of both forests, then the search,
+// rerank and top-K of every query (sel [bh, N, K]; cand [bh, N, 2 Wb] optional).
+hipError_t launch_fsb(const Geometry &g, const FsbLayout &L, const HeadConsts &hc, const FsbConsts &fc,
+                      const void *q, const void *k, const double *kbar64, const float *a, const double *a64,
+                      int32_t *adm, int32_t *adm_count, float *node_mu, FsbNodeMeta *node_meta, int32_t *sel,
+                      int32_t *cand, hipStream_t st);
 
 // Host-side checks of fs_longrange_prefill's arguments (everything but the
 // workspace); on FS_OK, *workspace_needed holds the workspace it needs.

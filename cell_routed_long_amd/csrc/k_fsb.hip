@@ -1,0 +1,762 @@
+// FS-B, FreeSolo's balanced tree search (Sec. 3.4 "Balanced tree search
+// (FS-B)"; App. E.1 "Streaming forests"): for every query block, two causal
+// forests over the available cells (all of them, Eq. 10's A^0, and those with
+// a_c >= tau_h, A^tau), a beam of W^b nodes per forest ranked by Eq. 11 down to
+// the leaves, and the union of the leaves reranked with the token keys (Eq. 12);
+// the K best cells are the selection, read out by the readout kernel.
+//
+// Three kernels:
+//   * fsb_admit_kernel: per head, the second forest's admitted cells in arrival
+//     order and their running count (a_c in fp64, so the admission equals an
+//     fp64 evaluation exactly).
+//   * fsb_build_kernel: one workgroup per aligned chunk of 2^k admitted cells
+//     that starts at an even multiple of 2^k (the only chunks a binary
+//     decomposition of the admitted count uses, App. E.1 "Chunks"), for both
+//     forests of every head.  A chunk never changes once complete, so its tree
+//     is built once and serves every block whose forest holds it.  One wave per
+//     node: fp64 mean, farthest cell, two power iterations (Eq. 19), then the
+//     node's cells are sorted by their projection in LDS (bitonic) and halved;
+//     node summaries (Eq. 20) are written heap-ordered, mean keys as fp32.
+//   * fsb_search_kernel: one workgroup per (sequence, head, 128-query block).
+//     It forms the block's join nodes (Eq. 21) from its chunks' roots and runs
+//     the 128 beams level-synchronously: each level the children of every
+//     query's internal beam nodes are collected into one list (an LDS bitmap
+//     over the block's forest nodes dedupes them), scored for all 128 queries
+//     32 nodes at a time on the fp32 matrix cores (the q . mu term of Eq. 11),
+//     and each query keeps its leaves plus its best W^b - #leaves children.
+//     The union of the leaves reached is then reranked cell by cell: a cell's
+//     32 token keys are staged once and the logits of all 128 queries come
+//     from the matrix cores; each query that has the cell as a candidate takes
+//     the log-sum-exp (Eq. 12) and keeps its top K.
+//
+// Ties follow the oracle's readings: the smaller cell id (nodes: the smaller
+// smallest cell id below, which names one node among disjoint subtrees).
+#include "fsl_internal.h"
+
+#include <climits>
+
+namespace fsl {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ double wave_sum_d(double x)
+{
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1)
+        x += shfl_xor_d(x, m); // x + y == y + x: every lane ends with the same sum
+    return x;
+}
+
+// ---------------------------------------------------------------- admission
+
+__global__ __launch_bounds__(kThreads) void fsb_admit_kernel(const double *__restrict__ a64, int32_t *__restrict__ adm,
+                                                          int32_t *__restrict__ cnt, int64_t M, int H, FsbConsts fc)
+{
+    const int64_t bh = blockIdx.x;
+    const double tau = fc.tau[bh % H];
+    const double *ah = a64 + bh * M;
+    int32_t *admh = adm + bh * M;
+    int32_t *cnth = cnt + bh * (M + 1);
+    __shared__ int32_t s_wave[kWaves];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (threadIdx.x == 0)
+        cnth[0] = 0;
+    int32_t base = 0;
+    for (int64_t c0 = 0; c0 < M; c0 += kThreads) {
+        const int64_t c = c0 + threadIdx.x;
+        const bool in = c < M && ah[c] >= tau; // Eq. 10: a_c >= tau_h, in fp64
+        const uint64_t bal = __ballot(in);
+        const int before = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            s_wave[wave] = __popcll(bal);
+        __syncthreads();
+        int32_t off = base, tot = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            off += w < wave ? s_wave[w] : 0;
+            tot += s_wave[w];
+        }
+        if (in)
+            admh[off + before] = (int32_t)c;
+        if (c < M)
+            cnth[c + 1] = off + before + (in ? 1 : 0);
+        base += tot;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- construction
+
+constexpr int kBuildThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kBuildThreads) void fsb_build_kernel(const double *__restrict__ kbar64,
+                                                               const float *__restrict__ a,
+                                                               const int32_t *__restrict__ adm,
+                                                               const int32_t *__restrict__ cnt,
+                                                               float *__restrict__ node_mu,
+                                                               FsbNodeMeta *__restrict__ node_meta, int64_t M,
+                                                               FsbLayout L)
+{
+    constexpr int FPL = D / kWave; // features per lane
+    constexpr int NW = kBuildThreads / kWave;
+    __shared__ int32_t perm[kFsbMaxCells];
+    __shared__ double key[kFsbMaxCells];
+
+    int64_t w = blockIdx.x;
+    const int64_t per = 2 * L.chunks;
+    const int64_t bh = w / per;
+    w -= bh * per;
+    const int f = (int)(w / L.chunks);
+    w -= (int64_t)f * L.chunks;
+    int k = 0;
+    while (k + 1 < L.levels && w >= L.chunk_base[k + 1])
+        ++k;
+    const int64_t jj = w - L.chunk_base[k];
+    const int64_t n = (int64_t)1 << k, start = 2 * jj * n;
+    const int64_t Mf = f == 0 ? L.Mu : cnt[bh * (M + 1) + L.Mu];
+    if (start + n > Mf)
+        return; // not a complete chunk of this forest: never read
+    const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
+    for (int64_t p = t; p < n; p += kBuildThreads)
+        perm[p] = f == 0 ? (int32_t)(start + p) : adm[bh * M + start + p];
+    __syncthreads();
+    const int64_t out0 = (bh * 2 + f) * L.nodes + L.node_base[k] + jj * (2 * n - 1);
+    const double *kb = kbar64 + bh * M * D;
+    const float *ah = a + bh * M;
+
+    for (int l = 0; l <= k; ++l) {
+        const int64_t nv = n >> l, nodes = (int64_t)1 << l;
+        for (int64_t s = wave; s < nodes; s += NW) {
+            int32_t *cells = perm + s * nv;
+            double *keys = key + s * nv;
+            const int64_t node = out0 + nodes + s - 1; // heap index nodes + s
+            float *mu_out = node_mu + node * D;
+            if (nv == 1) { // a leaf: the cell itself
+                const int32_t c = cells[0];
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    mu_out[lane + kWave * e] = (float)kb[(int64_t)c * D + lane + kWave * e];
+                if (lane == 0)
+                    node_meta[node] = FsbNodeMeta{0.0f, ah[c], c, c};
+                continue;
+            }
+            // mean of the cells' mean keys, summed in the node's cell order
+            double mu[FPL];
+#pragma unroll
+            for (int e = 0; e < FPL; ++e) {
+                double sum = 0.0;
+                for (int64_t x = 0; x < nv; ++x)
+                    sum += kb[(int64_t)cells[x] * D + lane + kWave * e];
+                mu[e] = sum / (double)nv;
+            }
+            // distances from the mean: the farthest cell (smaller id on ties) starts the
+            // power iteration and gives the radius; the largest norm and the earliest cell
+            double best = -1.0;
+            int32_t bestc = INT_MAX, mn = INT_MAX;
+            float A = -INFINITY;
+            for (int64_t x = 0; x < nv; ++x) {
+                const int32_t c = cells[x];
+                double sq = 0.0;
+#pragma unroll
+                for (int e = 0; e < FPL; ++e) {
+                    const double xv = kb[(int64_t)c * D + lane + kWave * e] - mu[e];
+                    sq += xv * xv;
+                }
+                const double nrm = sqrt(wave_sum_d(sq));
+                if (nrm > best || (nrm == best && c < bestc)) {
+                    best = nrm;
+                    bestc = c;
+                }
+                A = fmaxf(A, ah[c]);
+                mn = min(mn, c);
+            }
+            double u[FPL];
+            auto normalise = [&]() {
+                double sq = 0.0;
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    sq += u[e] * u[e];
+                sq = wave_sum_d(sq);
+                if (sq > 0.0) {
+                    const double inv = 1.0 / sqrt(sq);
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        u[e] *= inv;
+                }
+            };
+#pragma unroll
+            for (int e = 0; e < FPL; ++e)
+                u[e] = kb[(int64_t)bestc * D + lane + kWave * e] - mu[e];
+            normalise();
+            for (int it = 0; it < 2; ++it) { // u <- sum_c (x_c . u) x_c, normalised (Eq. 19)
+                double wv[FPL];
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    wv[e] = 0.0;
+                for (int64_t x = 0; x < nv; ++x) {
+                    const int32_t c = cells[x];
+                    double xv[FPL], p = 0.0;
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e) {
+                        xv[e] = kb[(int64_t)c * D + lane + kWave * e] - mu[e];
+                        p += xv[e] * u[e];
+                    }
+                    p = wave_sum_d(p);
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        wv[e] += p * xv[e];
+                }
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    u[e] = wv[e];
+                normalise();
+            }
+            for (int64_t x = 0; x < nv; ++x) { // projections on u^(2)
+                const int32_t c = cells[x];
+                double p = 0.0;
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    p += (kb[(int64_t)c * D + lane + kWave * e] - mu[e]) * u[e];
+                p = wave_sum_d(p);
+                if (lane == 0)
+                    keys[x] = p;
+            }
+#pragma unroll
+            for (int e = 0; e < FPL; ++e)
+                mu_out[lane + kWave * e] = (float)mu[e];
+            if (lane == 0)
+                node_meta[node] = FsbNodeMeta{(float)best, A, mn, -1};
+            wave_lds_sync();
+            // sort the node's cells by (projection asc, id asc); the first half goes left
+            for (int64_t size = 2; size <= nv; size <<= 1) {
+                for (int64_t stride = size >> 1; stride > 0; stride >>= 1) {
+                    for (int64_t p = lane; p < nv / 2; p += kWave) {
+                        const int64_t i1 = 2 * p - (p & (stride - 1)), i2 = i1 + stride;
+                        const bool asc = (i1 & size) == 0;
+                        const double k1 = keys[i1], k2 = keys[i2];
+                        const int32_t c1 = cells[i1], c2 = cells[i2];
+                        const bool gt = k1 > k2 || (k1 == k2 && c1 > c2);
+                        if (gt == asc) {
+                            keys[i1] = k2;
+                            keys[i2] = k1;
+                            cells[i1] = c2;
+                            cells[i2] = c1;
+                        }
+                    }
+                    wave_lds_sync();
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- search
+
+constexpr int kMaxChunksPerForest = kFsbMaxLevels; // popcount of an admitted count below 2^13
+constexpr int kMaxForestNodes = 2 * (int)kFsbMaxCells; // 2M - 1 nodes
+constexpr int kBmWords = kMaxForestNodes / 32;
+constexpr int kMaxKids = 2 * kFsbMaxBeam;
+constexpr uint32_t kJoinRef = 0x40000000u;
+
+template <typename T, int D>
+struct SearchSmem {
+    int32_t beam[128][kFsbMaxBeam]; // node refs of each query's beam
+    int32_t nb[128];
+    int32_t nk[128], nleaf[128];
+    int32_t kref[128][kMaxKids];   // children being ranked
+    uint16_t kidx[128][kMaxKids];  // their position in the level's node list
+    float ku[128][kMaxKids];       // their priority (Eq. 11)
+    uint16_t kmin[128][kMaxKids];  // their smallest cell id
+    int32_t cand[128][kMaxKids];   // candidate cells (forest 0, then the second forest)
+    int32_t ncand[128];
+    uint32_t bm[kBmWords];         // the level's node set (forest-local index), or the candidates' cells
+    int32_t wb[kBmWords];          // prefix counts of bm
+    uint16_t list[kMaxForestNodes]; // the level's nodes (forest-local index), or the candidates' cells
+    int32_t nlist;
+    union {
+        float mu[32][D + 1]; // a tile of node means
+        uint16_t kt16[32][D + 8];
+        float kt32[32][D + 1];
+    };
+    float trho[32], tA[32];
+    int32_t tmin[32];
+    float ut[kWaves][32][33]; // priorities of the tile: [wave][node row][query column]
+    float jmu[kMaxChunksPerForest][D];
+    FsbNodeMeta jmeta[kMaxChunksPerForest];
+    int32_t jcount[kMaxChunksPerForest];
+    double red[2][kThreads / kWave];
+    // the block's forest: chunk t has 2^ck[t] cells, its nodes from node index cbase[t],
+    // forest-local index lbase[t] .. lbase[t+1] - 1; join node t at lbase[r] + t
+    int32_t ck[kMaxChunksPerForest];
+    int64_t cbase[kMaxChunksPerForest];
+    int32_t lbase[kMaxChunksPerForest + 1];
+    int32_t r;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__restrict__ q, const T *__restrict__ k,
+                                                              const float *__restrict__ a,
+                                                              const int32_t *__restrict__ cnt,
+                                                              const float *__restrict__ node_mu,
+                                                              const FsbNodeMeta *__restrict__ node_meta,
+                                                              int32_t *__restrict__ sel, int32_t *__restrict__ cand,
+                                                              HeadConsts hc, FsbConsts fc, FsbLayout L, int64_t N,
+                                                              int64_t M, int NB, int H, int K)
+{
+    constexpr bool kBf16 = sizeof(T) == 2;
+    __shared__ SearchSmem<T, D> sm;
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int beta = (int)(lb % (uint32_t)NB);
+    const int64_t bh = (int64_t)(lb / (uint32_t)NB);
+    const int h = (int)(bh % H);
+    const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
+    const int qs = wave * 32 + col; // this lane's query slot in the block
+    const int64_t i = (int64_t)beta * 128 + qs;
+    const bool q_ok = i < N;
+    const float lam = hc.lambda[h], its = hc.inv_two_sigma[h];
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    const int Wb = fc.Wb;
+    const int64_t n_avail = ((int64_t)beta * 128 / 32) < L.Mu ? ((int64_t)beta * 128 / 32) : L.Mu;
+
+    // ---- the query in the layouts of the two products ----
+    const T *qrow = q + (bh * N + (q_ok ? i : 0)) * D;
+    float qf[D / 2]; // fp32 32x32x2 B operand: feature 2 kc + half
+#pragma unroll
+    for (int kc = 0; kc < D / 2; ++kc) {
+        if constexpr (kBf16)
+            qf[kc] = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(qrow)[2 * kc + half]);
+        else
+            qf[kc] = qrow[2 * kc + half];
+    }
+    float qsq = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < D / 2; ++kc)
+        qsq = fmaf(qf[kc], qf[kc], qsq);
+    qsq += shfl_xor_f(qsq, 32);
+    const float qnorm = sqrtf(qsq);
+
+    if (t < 128)
+        sm.ncand[t] = 0;
+
+    for (int f = 0; f < 2; ++f) {
+        const int64_t Mf = f == 0 ? n_avail : cnt[bh * (M + 1) + n_avail];
+        if (Mf == 0)
+            continue; // an empty forest adds no candidates (a block-uniform branch)
+        // ---- the forest's chunks (Eq. 18) and join nodes (Eq. 21) ----
+        if (t == 0) {
+            int r = 0, lbase = 0;
+            int64_t off = 0;
+            for (int kk = kFsbMaxLevels - 1; kk >= 0; --kk) {
+                if (!((Mf >> kk) & 1))
+                    continue;
+                const int64_t jj = (off >> kk) / 2; // the chunk starts at an even multiple of 2^kk
+                sm.ck[r] = kk;
+                sm.cbase[r] = (bh * 2 + f) * L.nodes + L.node_base[kk] + jj * ((2 << kk) - 1);
+                sm.lbase[r] = lbase;
+                lbase += (2 << kk) - 1;
+                off += (int64_t)1 << kk;
+                ++r;
+            }
+            sm.lbase[r] = lbase;
+            sm.r = r;
+        }
+        __syncthreads();
+        const int r = sm.r;
+        // join nodes from the smallest chunk up: J_t over root(G_t) and J_(t+1) (or root(G_(r-1)))
+        for (int jt = r - 2; jt >= 0; --jt) {
+            const int64_t ra = sm.cbase[jt];
+            const FsbNodeMeta ma = node_meta[ra];
+            const double na = (double)((int64_t)1 << sm.ck[jt]);
+            const float *mb_mu;
+            FsbNodeMeta mb;
+            double nbn;
+            if (jt == r - 2) {
+                mb_mu = node_mu + sm.cbase[r - 1] * D;
+                mb = node_meta[sm.cbase[r - 1]];
+                nbn = (double)((int64_t)1 << sm.ck[r - 1]);
+            } else {
+                mb_mu = sm.jmu[jt + 1];
+                mb = sm.jmeta[jt + 1];
+                nbn = (double)sm.jcount[jt + 1];
+            }
+            double da = 0.0, db = 0.0;
+            if (t < D) {
+                const double xa = node_mu[ra * D + t], xb = mb_mu[t];
+                const double m = (na * xa + nbn * xb) / (na + nbn);
+                sm.jmu[jt][t] = (float)m;
+                da = (xa - m) * (xa - m);
+                db = (xb - m) * (xb - m);
+            }
+            da = wave_sum_d(da);
+            db = wave_sum_d(db);
+            if (lane == 0) {
+                sm.red[0][wave] = da;
+                sm.red[1][wave] = db;
+            }
+            __syncthreads();
+            if (t == 0) {
+                double sa = 0.0, sb = 0.0;
+                for (int w = 0; w < kWaves; ++w) {
+                    sa += sm.red[0][w];
+                    sb += sm.red[1][w];
+                }
+                const float rho = fmaxf(ma.rho + (float)sqrt(sa), mb.rho + (float)sqrt(sb));
+                sm.jmeta[jt] = FsbNodeMeta{rho, fmaxf(ma.A, mb.A), min(ma.minid, mb.minid), -1};
+                sm.jcount[jt] = (int32_t)(na + nbn);
+            }
+            __syncthreads();
+        }
+        const int lj = sm.lbase[r];
+        // node refs: chunk node (t, heap h) = t << 16 | h; join node t = kJoinRef | t
+        auto is_leaf = [&](int32_t ref) {
+            return !(ref & kJoinRef) && (ref & 0xffff) >= (1 << sm.ck[ref >> 16]);
+        };
+        auto local_of = [&](int32_t ref) {
+            return (ref & kJoinRef) ? lj + (ref & 0xffff) : sm.lbase[ref >> 16] + (ref & 0xffff) - 1;
+        };
+        const int32_t root = r == 1 ? (int32_t)((0 << 16) | 1) : (int32_t)(kJoinRef | 0);
+        if (t < 128) {
+            sm.beam[t][0] = root;
+            sm.nb[t] = (int64_t)beta * 128 + t < N ? 1 : 0;
+        }
+        const int nwords = (sm.lbase[r] + r - 1 + 31) / 32;
+
+        // ---- beam search, level by level ----
+        for (;;) {
+            for (int x = t; x < nwords; x += kThreads)
+                sm.bm[x] = 0u;
+            __syncthreads();
+            int nk = 0;
+            if (half == 0) { // expand this query's internal nodes; leaves keep their slots
+                int nleaf = 0;
+                for (int e = 0; e < sm.nb[qs]; ++e) {
+                    const int32_t ref = sm.beam[qs][e];
+                    if (is_leaf(ref)) {
+                        ++nleaf;
+                        continue;
+                    }
+                    int32_t c0, c1;
+                    if (ref & kJoinRef) {
+                        const int jt = ref & 0xffff;
+                        c0 = (jt << 16) | 1;
+                        c1 = jt + 1 <= r - 2 ? (int32_t)(kJoinRef | (jt + 1)) : (int32_t)(((r - 1) << 16) | 1);
+                    } else {
+                        c0 = ref + (ref & 0xffff);     // heap 2h
+                        c1 = ref + (ref & 0xffff) + 1; // heap 2h + 1
+                    }
+                    sm.kref[qs][nk++] = c0;
+                    sm.kref[qs][nk++] = c1;
+                    const int l0 = local_of(c0), l1 = local_of(c1);
+                    atomicOr(&sm.bm[l0 >> 5], 1u << (l0 & 31));
+                    atomicOr(&sm.bm[l1 >> 5], 1u << (l1 & 31));
+                }
+                sm.nk[qs] = nk;
+                sm.nleaf[qs] = nleaf;
+            }
+            if (!__syncthreads_or(nk > 0))
+                break; // every beam holds only leaves
+            // the level's node list: prefix counts over the bitmap words
+            if (t == 0) {
+                int32_t run = 0;
+                for (int x = 0; x < nwords; ++x) {
+                    sm.wb[x] = run;
+                    run += __popc(sm.bm[x]);
+                }
+                sm.nlist = run;
+            }
+            __syncthreads();
+            for (int x = t; x < nwords; x += kThreads) {
+                uint32_t bits = sm.bm[x];
+                int32_t pos = sm.wb[x];
+                while (bits) {
+                    const int b = __ffs(bits) - 1;
+                    bits &= bits - 1;
+                    sm.list[pos++] = (uint16_t)(x * 32 + b);
+                }
+            }
+            if (half == 0) {
+                for (int e = 0; e < sm.nk[qs]; ++e) {
+                    const int l = local_of(sm.kref[qs][e]);
+                    sm.kidx[qs][e] = (uint16_t)(sm.wb[l >> 5] + __popc(sm.bm[l >> 5] & ((1u << (l & 31)) - 1u)));
+                }
+            }
+            __syncthreads();
+            const int Z = sm.nlist;
+            // ---- priorities (Eq. 11) of the level's nodes, 32 at a time, for all 128 queries ----
+            for (int t0 = 0; t0 < Z; t0 += 32) {
+                { // stage the tile's means and summaries
+                    const int row = t / 8, part = t % 8;
+                    constexpr int FP = D / 8; // features per thread
+                    const int u = t0 + row;
+                    const float *src = nullptr;
+                    FsbNodeMeta meta{0.0f, 0.0f, 0, -1};
+                    if (u < Z) {
+                        const int l = sm.list[u];
+                        if (l >= lj) {
+                            src = sm.jmu[l - lj];
+                            meta = sm.jmeta[l - lj];
+                        } else {
+                            int ct = 0;
+                            while (ct + 1 < r && l >= sm.lbase[ct + 1])
+                                ++ct;
+                            const int64_t gi = sm.cbase[ct] + (l - sm.lbase[ct]);
+                            src = node_mu + gi * D;
+                            meta = node_meta[gi];
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < FP; ++e)
+                        sm.mu[row][part * FP + e] = src ? src[part * FP + e] : 0.0f;
+                    if (part == 0) {
+                        sm.trho[row] = meta.rho;
+                        sm.tA[row] = meta.A;
+                        sm.tmin[row] = meta.minid;
+                    }
+                }
+                __syncthreads();
+                f32x16 acc;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+                    acc[rr] = 0.0f;
+#pragma unroll
+                for (int kc = 0; kc < D / 2; ++kc)
+                    acc = mfma_f32(sm.mu[col][2 * kc + half], qf[kc], acc); // node row col, query column col
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int row = acc_row(rr, half);
+                    const float pmin = ((float)sm.tmin[row] + 0.5f) * 32.0f;
+                    const float g = erff(((float)i - pmin) * its);
+                    sm.ut[wave][row][col] =
+                        fmaf(fmaf(fc.c * qnorm, sm.trho[row], acc[rr]), inv_sqrt_d, lam * sm.tA[row] * g);
+                }
+                wave_lds_sync();
+                for (int e = half; e < sm.nk[qs]; e += 2) {
+                    const int u = sm.kidx[qs][e] - t0;
+                    if (u >= 0 && u < 32) {
+                        sm.ku[qs][e] = sm.ut[wave][u][col];
+                        sm.kmin[qs][e] = (uint16_t)sm.tmin[u];
+                    }
+                }
+                __syncthreads();
+            }
+            // ---- each query keeps its leaves and its best Wb - #leaves children ----
+            {
+                uint64_t top[kFsbMaxBeam];
+#pragma unroll
+                for (int e = 0; e < kFsbMaxBeam; ++e)
+                    top[e] = 0ull;
+                const int nkq = sm.nk[qs];
+                for (int e = half; e < nkq; e += 2)
+                    insert_key<kFsbMaxBeam>(top, rank_key(sm.ku[qs][e], ((0xffffu - sm.kmin[qs][e]) << 16) | (uint32_t)e));
+                uint64_t mine[kFsbMaxBeam]; // sent as ranked before the partner's keys enter the list
+#pragma unroll
+                for (int e = 0; e < kFsbMaxBeam; ++e)
+                    mine[e] = top[e];
+#pragma unroll
+                for (int e = 0; e < kFsbMaxBeam; ++e) { // the partner lane ranked the other children
+                    const uint64_t o = mine[e];
+                    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)o, 32, kWave);
+                    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(o >> 32), 32, kWave);
+                    const uint64_t other = ((uint64_t)hi << 32) | lo;
+                    if (other)
+                        insert_key<kFsbMaxBeam>(top, other);
+                }
+                if (half == 0 && nkq > 0) {
+                    int nb2 = 0;
+                    for (int e = 0; e < sm.nb[qs]; ++e)
+                        if (is_leaf(sm.beam[qs][e]))
+                            sm.beam[qs][nb2++] = sm.beam[qs][e];
+                    const int keep = Wb - sm.nleaf[qs];
+#pragma unroll
+                    for (int e = 0; e < kFsbMaxBeam; ++e)
+                        if (e < keep && top[e] != 0ull)
+                            sm.beam[qs][nb2++] = sm.kref[qs][(int)(top[e] & 0xffffu)];
+                    sm.nb[qs] = nb2;
+                }
+            }
+            __syncthreads();
+        }
+        // ---- the leaves reached join the query's candidates (deduplicated) ----
+        if (half == 0) {
+            int nc = sm.ncand[qs];
+            for (int e = 0; e < sm.nb[qs]; ++e) {
+                const int32_t ref = sm.beam[qs][e];
+                const int ct = ref >> 16;
+                const int32_t cell = node_meta[sm.cbase[ct] + (ref & 0xffff) - 1].cell;
+                bool dup = false;
+                for (int x = 0; x < nc; ++x)
+                    dup |= sm.cand[qs][x] == cell;
+                if (!dup)
+                    sm.cand[qs][nc++] = cell;
+            }
+            sm.ncand[qs] = nc;
+        }
+        __syncthreads();
+    }
+
+    // ---- candidates in ascending id order; their union over the block ----
+    const int mwords = (int)((n_avail + 31) / 32);
+    for (int x = t; x < mwords; x += kThreads)
+        sm.bm[x] = 0u;
+    __syncthreads();
+    if (half == 0) {
+        const int nc = sm.ncand[qs];
+        for (int x = 1; x < nc; ++x) {
+            const int32_t v = sm.cand[qs][x];
+            int y = x - 1;
+            while (y >= 0 && sm.cand[qs][y] > v) {
+                sm.cand[qs][y + 1] = sm.cand[qs][y];
+                --y;
+            }
+            sm.cand[qs][y + 1] = v;
+        }
+        for (int x = 0; x < nc; ++x)
+            atomicOr(&sm.bm[sm.cand[qs][x] >> 5], 1u << (sm.cand[qs][x] & 31));
+    }
+    __syncthreads();
+    if (t == 0) {
+        int32_t run = 0;
+        for (int x = 0; x < mwords; ++x) {
+            sm.wb[x] = run;
+            run += __popc(sm.bm[x]);
+        }
+        sm.nlist = run;
+    }
+    __syncthreads();
+    for (int x = t; x < mwords; x += kThreads) {
+        uint32_t bits = sm.bm[x];
+        int32_t pos = sm.wb[x];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            sm.list[pos++] = (uint16_t)(x * 32 + b);
+        }
+    }
+    __syncthreads();
+
+    // ---- rerank (Eq. 12): one candidate cell at a time, all queries on the matrix cores ----
+    constexpr int KB = kBf16 ? D / 16 : 1;
+    bf16x8 qb[KB];
+    if constexpr (kBf16) {
+#pragma unroll
+        for (int kc = 0; kc < KB; ++kc)
+            qb[kc] = as_bf16x8(*reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qrow) + kc * 16 +
+                                                                half * 8));
+    }
+    uint64_t topk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        topk[e] = 0ull;
+    const int nc = sm.ncand[qs];
+    const int Zc = sm.nlist;
+    const T *kh = k + bh * N * D;
+    for (int u = 0; u < Zc; ++u) {
+        const int32_t c = sm.list[u];
+        if constexpr (kBf16) { // the cell's 32 token keys, 16 bytes per thread
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(kh) + (int64_t)c * 32 * D;
+            for (int x = t; x < 32 * D / 8; x += kThreads) {
+                const int row = x / (D / 8), c8 = (x % (D / 8)) * 8;
+                *reinterpret_cast<u32x4 *>(&sm.kt16[row][c8]) =
+                    *reinterpret_cast<const u32x4 *>(src + (int64_t)row * D + c8);
+            }
+        } else {
+            const float *src = reinterpret_cast<const float *>(kh) + (int64_t)c * 32 * D;
+            for (int x = t; x < 32 * D; x += kThreads)
+                sm.kt32[x / D][x % D] = src[x];
+        }
+        __syncthreads();
+        f32x16 acc;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            acc[rr] = 0.0f;
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int kc = 0; kc < KB; ++kc)
+                acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.kt16[col][kc * 16 + half * 8])), qb[kc],
+                                acc);
+        } else {
+#pragma unroll
+            for (int kc = 0; kc < D / 2; ++kc)
+                acc = mfma_f32(sm.kt32[col][2 * kc + half], qf[kc], acc);
+        }
+        // is c one of this query's candidates? (sorted list, at most 2 Wb)
+        bool mine = false;
+        for (int x = 0; x < nc; ++x)
+            mine |= sm.cand[qs][x] == c;
+        float m = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            m = fmaxf(m, acc[rr] * inv_sqrt_d);
+        m = fmaxf(m, shfl_xor_f(m, 32));
+        float z = 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            z += expf(acc[rr] * inv_sqrt_d - m);
+        z += shfl_xor_f(z, 32);
+        if (mine) {
+            const float g = erff(((float)i - ((float)c + 0.5f) * 32.0f) * its);
+            const float score = m + logf(z) + lam * a[bh * M + c] * g;
+            insert_key<8>(topk, rank_key(score, 0x7fffffffu - (uint32_t)c));
+        }
+        __syncthreads();
+    }
+    if (half == 0 && q_ok) {
+        int32_t *dst = sel + (bh * N + i) * K;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < K)
+                dst[e] = topk[e] ? (int32_t)(0x7fffffffu - (uint32_t)topk[e]) : -1;
+        if (cand) {
+            int32_t *cd = cand + (bh * N + i) * 2 * Wb;
+            for (int x = 0; x < 2 * Wb; ++x)
+                cd[x] = x < nc ? sm.cand[qs][x] : -1;
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_t(const Geometry &g, const FsbLayout &L, const HeadConsts &hc, const FsbConsts &fc, const void *q,
+                    const void *k, const double *kbar64, const float *a, const double *a64, int32_t *adm,
+                    int32_t *adm_count, float *node_mu, FsbNodeMeta *node_meta, int32_t *sel, int32_t *cand,
+                    hipStream_t st)
+{
+    hipLaunchKernelGGL(fsb_admit_kernel, dim3((unsigned)g.bh), dim3(kThreads), 0, st, a64, adm, adm_count, g.M, g.H,
+                       fc);
+    if (L.Mu > 0)
+        hipLaunchKernelGGL((fsb_build_kernel<D>), dim3((unsigned)((int64_t)g.bh * 2 * L.chunks)),
+                           dim3(kBuildThreads), 0, st, kbar64, a, adm, adm_count, node_mu, node_meta, g.M, L);
+    hipLaunchKernelGGL((fsb_search_kernel<T, D>), dim3((unsigned)((int64_t)g.bh * g.NB)), dim3(kThreads), 0, st,
+                       static_cast<const T *>(q), static_cast<const T *>(k), a, adm_count, node_mu, node_meta, sel,
+                       cand, hc, fc, L, g.N, g.M, g.NB, g.H, g.K);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_fsb(const Geometry &g, const FsbLayout &L, const HeadConsts &hc, const FsbConsts &fc,
+                      const void *q, const void *k, const double *kbar64, const float *a, const double *a64,
+                      int32_t *adm, int32_t *adm_count, float *node_mu, FsbNodeMeta *node_meta, int32_t *sel,
+                      int32_t *cand, hipStream_t st)
+{
+    if (g.bf16)
+        return g.d == 64 ? launch_t<uint16_t, 64>(g, L, hc, fc, q, k, kbar64, a, a64, adm, adm_count, node_mu,
+                                                  node_meta, sel, cand, st)
+                         : launch_t<uint16_t, 128>(g, L, hc, fc, q, k, kbar64, a, a64, adm, adm_count, node_mu,
+                                                   node_meta, sel, cand, st);
+    return g.d == 64 ? launch_t<float, 64>(g, L, hc, fc, q, k, kbar64, a, a64, adm, adm_count, node_mu, node_meta,
+                                           sel, cand, st)
+                     : launch_t<float, 128>(g, L, hc, fc, q, k, kbar64, a, a64, adm, adm_count, node_mu, node_meta,
+                                            sel, cand, st);
+}
+
+} // namespace fsl

@@ -24,8 +24,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, 5) void cell_summaries_kernel(const T *__restrict__ k, float *__restrict__ kbar,
                                                              float *__restrict__ a,
                                                              uint16_t *__restrict__ kbar_split,
-                                                             float *__restrict__ kbar_norm, int64_t N, int64_t M,
-                                                             int64_t total_cells)
+                                                             float *__restrict__ kbar_norm,
+                                                             double *__restrict__ kbar64, double *__restrict__ a64,
+                                                             int64_t N, int64_t M, int64_t total_cells)
 {
     constexpr int EPC = 16 / (int)sizeof(T); // elements per 16-byte chunk
     constexpr int R = D / EPC;               // chunks per key row: 8, 16 or 32
@@ -109,6 +110,11 @@ __global__ __launch_bounds__(256, 5) void cell_summaries_kernel(const T *__restr
         if (lane == 0)
             kbar_norm[cell] = (float)sqrt(nsq);
     }
+    if (kbar64 && lane < R) { // the fp64 mean (exact for bf16 keys: the sums are)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+            kbar64[cell * D + group * EPC + e] = colsum[e] * (1.0 / 32.0);
+    }
     if (lane < R) {
         float *dst = kbar + cell * D + group * EPC;
 #pragma unroll
@@ -135,33 +141,36 @@ __global__ __launch_bounds__(256, 5) void cell_summaries_kernel(const T *__restr
             }
         }
     }
-    if (lane == 0)
+    if (lane == 0) {
         a[cell] = (float)sqrt(best);
+        if (a64)
+            a64[cell] = sqrt(best);
+    }
 }
 
 template <typename T, int D>
 hipError_t launch_t(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split, float *kbar_norm,
-                    hipStream_t st)
+                    double *kbar64, double *a64, hipStream_t st)
 {
     const int64_t total = (int64_t)g.bh * g.M;
     if (total == 0)
         return hipSuccess;
     const int64_t blocks = (total + 3) / 4;
     hipLaunchKernelGGL((cell_summaries_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const T *>(k), kbar, a, kbar_split, kbar_norm, g.N, g.M, total);
+                       static_cast<const T *>(k), kbar, a, kbar_split, kbar_norm, kbar64, a64, g.N, g.M, total);
     return hipGetLastError();
 }
 
 } // namespace
 
 hipError_t launch_cell_summaries(const Geometry &g, const void *k, float *kbar, float *a, uint16_t *kbar_split,
-                                 float *kbar_norm, hipStream_t st)
+                                 float *kbar_norm, hipStream_t st, double *kbar64, double *a64)
 {
     if (g.bf16)
-        return g.d == 64 ? launch_t<uint16_t, 64>(g, k, kbar, a, kbar_split, kbar_norm, st)
-                         : launch_t<uint16_t, 128>(g, k, kbar, a, kbar_split, kbar_norm, st);
-    return g.d == 64 ? launch_t<float, 64>(g, k, kbar, a, kbar_split, kbar_norm, st)
-                     : launch_t<float, 128>(g, k, kbar, a, kbar_split, kbar_norm, st);
+        return g.d == 64 ? launch_t<uint16_t, 64>(g, k, kbar, a, kbar_split, kbar_norm, kbar64, a64, st)
+                         : launch_t<uint16_t, 128>(g, k, kbar, a, kbar_split, kbar_norm, kbar64, a64, st);
+    return g.d == 64 ? launch_t<float, 64>(g, k, kbar, a, kbar_split, kbar_norm, kbar64, a64, st)
+                     : launch_t<float, 128>(g, k, kbar, a, kbar_split, kbar_norm, kbar64, a64, st);
 }
 
 } // namespace fsl

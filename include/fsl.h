@@ -221,6 +221,59 @@ fs_status fs_longrange_prefill_noalloc(const fs_shape *shape, const fs_params *p
                                        void *stream);
 
 /*
+ * FS-B, balanced tree search (Sec. 3.4 "Balanced tree search (FS-B)"; App. E.1
+ * "Streaming forests").  Wb: beam width per forest (the page's W^b = 16);
+ * c: radius weight of the node priority, Eq. 11 (the page's c = 8).
+ * Supported: 1 <= Wb <= 16, c >= 0 finite.
+ */
+typedef struct {
+    int32_t Wb;
+    float c;
+} fs_fsb_params;
+
+/* Bytes of workspace fs_fsb_prefill needs (0 on invalid or unsupported arguments). */
+size_t fs_fsb_workspace_bytes(const fs_shape *shape, const fs_params *prm, const fs_fsb_params *fb);
+
+/*
+ * FS-B over a whole prompt, for every query position i.  For the query block
+ * of i, two causal forests over its available cells C_i (Eq. 6): one over all
+ * of them and one over those with a_c >= tau_h (Eq. 10), each a chain of
+ * balanced trees over the binary decomposition of its admitted count into
+ * aligned chunks (App. E.1, Eqs. 18-21: a chunk is split recursively at the
+ * median of its mean keys' projections on the principal direction from two
+ * power iterations started at the farthest cell; node summaries mu, rho, A,
+ * p_min; join nodes chain the chunk roots, smallest first).  Each forest keeps
+ * the Wb highest-priority nodes per level by U_v of Eq. 11 down to the leaves
+ * (a leaf in the beam keeps its slot; the other slots take the best children);
+ * the leaves of both beams are reranked by Eq. 12 (log-sum-exp of the cell's
+ * token logits plus the prior) and the min(K, |B_i|) best form the selection,
+ * read out with Eq. 9 and RMSNorm (Eq. 17) as in fs_readout.  Ties go to the
+ * smaller cell id (nodes: the smaller smallest cell id below them).
+ *   prm          s, B, K, eps as for the other calls (P, W, prune are not used)
+ *   q, k, v      [batch, H, N, d] shape dtype (input); v may be NULL when out is
+ *   sigma_h, lambda_h   host [H] fp32 as for fs_longrange_prefill
+ *   tau_h        host [H] fp32, finite: the second forest's norm threshold (the
+ *                page calibrates it as a median cell norm once per checkpoint)
+ *   gain         device [H, d] fp32 RMSNorm gains, or NULL for unit gains
+ *   out          [batch, H, N, d] shape dtype, or NULL (output)
+ *   sel          [batch, H, N, K] int32 (reranked score desc, id asc), -1
+ *                padded, or NULL (output)
+ *   cand         [batch, H, N, 2 Wb] int32 the candidate cells B_i in ascending
+ *                order, -1 padded, or NULL (output)
+ *   workspace    fs_fsb_workspace_bytes() bytes of device memory (scratch)
+ * Arithmetic: mean keys and norms in fp64 (the trees are built from them in
+ * fp64, the second forest admits by the fp64 norm); node priorities and
+ * rerank scores in fp32 with exact products on the matrix cores.
+ * Supported: at most 4096 cells available to the last block (N <= 131,200 at
+ * s = 32, B = 128); larger shapes give FS_ERR_UNSUPPORTED.
+ */
+fs_status fs_fsb_prefill(const fs_shape *shape, const fs_params *prm, const fs_fsb_params *fb,
+                         const void *q, const void *k, const void *v,
+                         const float *sigma_h, const float *lambda_h, const float *tau_h, const float *gain,
+                         void *out, int32_t *sel, int32_t *cand,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Streaming decode (Sec. 3.3 "Inference"; App. C "Bounded cache", Eq. 15).
  *
  * The decode state is one flat caller-owned device buffer: a 256-byte header

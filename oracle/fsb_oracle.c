@@ -552,11 +552,13 @@ int oracle_fsb_head(const oracle_cfg *cfg, const oracle_fsb_cfg *fb, const doubl
                 sel[row * K + t] = t < nT ? (int32_t)T[t] : -1;
         if (gap_beam)
             gap_beam[row] = gb;
-        if (gap_rerank) {
+        if (gap_rerank) { /* adjacent scores among the K + 1 best decide the ordered selection */
             gap_rerank[row] = INFINITY;
-            if (nc > K) {
-                const double m = fmax(rmag[K - 1], rmag[K]);
-                gap_rerank[row] = m > 0.0 ? fabs(rank[K - 1].val - rank[K].val) / m : 0.0;
+            for (int64_t t = 0; t < K && t + 1 < nc; ++t) {
+                const double m = fmax(rmag[t], rmag[t + 1]);
+                const double gp = m > 0.0 ? fabs(rank[t].val - rank[t + 1].val) / m : 0.0;
+                if (gp < gap_rerank[row])
+                    gap_rerank[row] = gp;
             }
         }
         if (gap_split)

@@ -285,15 +285,17 @@ int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const d
         if (sel)
             for (int32_t t = 0; t < K; ++t)
                 sel[row * K + t] = t < nT ? (int32_t)T[t] : -1;
-        if (gap_k) {
+        if (gap_k) { /* adjacent scores among the K + 1 best decide the ordered selection */
             gap_k[row] = INFINITY;
-            if (nA > K) { /* |r_K - r_K+1| against the larger of the two scores' term sizes */
-                const double m1 = oracle_cell_score_mag(cfg, q_i, kb + rank[K - 1].id * d, an[rank[K - 1].id], i,
-                                                        rank[K - 1].id);
-                const double m2 = oracle_cell_score_mag(cfg, q_i, kb + rank[K].id * d, an[rank[K].id], i,
-                                                        rank[K].id);
+            for (int64_t t = 0; t < K && t + 1 < nA; ++t) { /* |r_t - r_t+1| against their term sizes */
+                const double m1 = oracle_cell_score_mag(cfg, q_i, kb + rank[t].id * d, an[rank[t].id], i,
+                                                        rank[t].id);
+                const double m2 = oracle_cell_score_mag(cfg, q_i, kb + rank[t + 1].id * d, an[rank[t + 1].id], i,
+                                                        rank[t + 1].id);
                 const double m = fmax(m1, m2);
-                gap_k[row] = m > 0.0 ? fabs(rank[K - 1].val - rank[K].val) / m : 0.0;
+                const double gp = m > 0.0 ? fabs(rank[t].val - rank[t + 1].val) / m : 0.0;
+                if (gp < gap_k[row])
+                    gap_k[row] = gp;
             }
         }
         if (out)

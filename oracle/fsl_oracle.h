@@ -71,8 +71,9 @@ void oracle_readout(const oracle_cfg *cfg, const double *q_i, const double *k, c
  *   retained [NB, cap] (-1 padded), n_ret [NB], gap_p [NB]   per query block
  *       touched by [i_lo, i_hi), indexed by absolute block (optional)
  *   sel [(i_hi-i_lo), K] selected cells (-1 padded), in (score desc, id asc)
- *   gap_k [(i_hi-i_lo)] gap of the K-th and (K+1)-th scores relative to the
- *       larger of their term sizes (oracle_cell_score_mag), or +inf
+ *   gap_k [(i_hi-i_lo)] smallest gap of adjacent scores among the K + 1 best
+ *       (the order of the selection and its boundary), each relative to the
+ *       larger of the two scores' term sizes (oracle_cell_score_mag), or +inf
  *   out [(i_hi-i_lo), d] long-range output after RMSNorm
  *   scores [(i_hi-i_lo), cap] scores of the retained cells in ascending id
  *       order (optional; NaN padded)
@@ -139,7 +140,8 @@ double oracle_fsb_rerank_score(const oracle_cfg *cfg, const double *q_i, const d
  *   sel [n, K] (reranked score desc, id asc; -1 padded), cand [n, 2 W^b] the
  *   candidate cells B_i ascending (-1 padded), n_cand [n] = |B_i|,
  *   gap_beam [n] smallest beam-cut gap (relative to the larger term size),
- *   gap_rerank [n] K/K+1 gap of the reranked scores (relative to term size),
+ *   gap_rerank [n] smallest gap of adjacent reranked scores among the K + 1
+ *   best (relative to the larger term size),
  *   gap_split [n] smallest median-split gap of the query's block's forests,
  *   out [n, d].
  * Returns 0, or -1 for invalid arguments.

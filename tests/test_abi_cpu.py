@@ -280,3 +280,40 @@ def test_noalloc_prefill_rejects_before_launch(L):
                                           vp(1), None, None, 0, None) == fsl.FS_ERR_INVALID
     assert L.fs_longrange_prefill_noalloc(ctypes.byref(fits), ctypes.byref(p), vp(1), vp(1), vp(1), sig, lam, None,
                                           None, None, None, 0, None) == fsl.FS_ERR_INVALID
+
+
+def test_fsb_validation_before_launch(L):
+    """fs_fsb_prefill rejects bad arguments on the host (FS-B: Sec. 3.4)."""
+    vp = ctypes.c_void_p
+    H = 2
+    sig = (ctypes.c_float * H)(4.0, 4.0)
+    lam = (ctypes.c_float * H)(1.0, 1.0)
+    tau = (ctypes.c_float * H)(1.0, 1.0)
+    tau_nan = (ctypes.c_float * H)(1.0, float("nan"))
+    sh = shape(b=1, H=H, N=4096, d=128, dtype=fsl.FS_BF16)
+    p = prm()
+    fb = fsl.FsbParams().c_struct()
+    need = L.fs_fsb_workspace_bytes(ctypes.byref(sh), ctypes.byref(p), ctypes.byref(fb))
+    assert need > 0
+
+    def call(sh=sh, fb=fb, q=1, k=1, v=1, out=1, sel=None, cand=None, t=tau, ws=need):
+        return L.fs_fsb_prefill(ctypes.byref(sh), ctypes.byref(p), ctypes.byref(fb), vp(q) if q else None,
+                                vp(k) if k else None, vp(v) if v else None, sig, lam, t, None,
+                                vp(out) if out else None, vp(sel) if sel else None, vp(cand) if cand else None,
+                                vp(1), ws, None)
+
+    assert call(q=0) == fsl.FS_ERR_INVALID
+    assert call(k=0) == fsl.FS_ERR_INVALID
+    assert call(v=0) == fsl.FS_ERR_INVALID                  # out needs v
+    assert call(out=0) == fsl.FS_ERR_INVALID                # nothing to write
+    assert call(t=None) == fsl.FS_ERR_INVALID
+    assert call(t=tau_nan) == fsl.FS_ERR_INVALID
+    assert call(ws=need - 1) == fsl.FS_ERR_WORKSPACE
+    assert call(fb=fsl.FsbParams(Wb=0).c_struct()) == fsl.FS_ERR_INVALID
+    assert call(fb=fsl.FsbParams(c=-1.0).c_struct()) == fsl.FS_ERR_INVALID
+    assert call(fb=fsl.FsbParams(Wb=17).c_struct()) == fsl.FS_ERR_UNSUPPORTED
+    big = shape(b=1, H=H, N=131200 + 128, d=128, dtype=fsl.FS_BF16)  # 4100 cells available to the last block
+    assert L.fs_fsb_workspace_bytes(ctypes.byref(big), ctypes.byref(p), ctypes.byref(fb)) == 0
+    assert call(sh=big) == fsl.FS_ERR_UNSUPPORTED
+    edge = shape(b=1, H=H, N=131200, d=128, dtype=fsl.FS_BF16)  # exactly 4096
+    assert L.fs_fsb_workspace_bytes(ctypes.byref(edge), ctypes.byref(p), ctypes.byref(fb)) > 0

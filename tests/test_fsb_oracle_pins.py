@@ -256,6 +256,32 @@ def test_rerank_one_token_cells_is_eq7():
         assert r == pytest.approx(oracle.cell_score(q[i], kbar[c], a[c], i, c, prm), rel=1e-13, abs=1e-13)
 
 
+def test_rerank_gap_closed_form():
+    """The near-tie gap of the rerank: the smallest gap of adjacent scores among the K + 1
+    best, each against the larger of the two scores' term sizes.  One-token cells (s = 1),
+    content-only scores of cells (3, -2), (0.5, 0.4), (-1, -1), (0.1, 0) for q = (1, 1):
+    1, 0.9, -2, 0.1 (times 1/sqrt 2) with sizes 5, 0.9, 2, 0.1.  K = 2: the pairs (1, 0.9)
+    and (0.9, 0.1) give min(0.1 / 5, 0.8 / 0.9) = 0.02; K = 3 adds (0.1, -2): 2.1 / 2."""
+    d = 2
+    k = np.array([[3.0, -2.0], [0.5, 0.4], [-1.0, -1.0], [0.1, 0.0], [0.0, 0.0], [0.0, 0.0], [0.0, 0.0],
+                  [0.0, 0.0]])
+    q = np.tile([1.0, 1.0], (len(k), 1))
+    for K, expect in ((2, 0.1 / 5.0), (1, 0.1 / 5.0), (3, 0.1 / 5.0)):
+        res = oracle.fsb_head(q, k, np.zeros_like(k), prm=Params(s=1, B=4, K=K, lam=0.0),
+                              fb=FsbParams(tau=1e300, Wb=8), i_lo=4, i_hi=5, want_out=False)
+        assert list(res["sel"][0][:K]) == [0, 1, 3][:K]
+        assert res["gap_rerank"][0] == pytest.approx(expect, rel=1e-13)
+    # a second query with the order decided by the lower pair only: cells 1 and 3 selected
+    # (K = 2 from the candidates {1, 2, 3} of a forest without cell 0): pairs (0.9, 0.1) and
+    # (0.1, -2) -> min(0.8 / 0.9, 2.1 / 2)
+    k2 = k.copy()
+    k2[0] = [-30.0, -30.0]
+    res = oracle.fsb_head(q, k2, np.zeros_like(k2), prm=Params(s=1, B=4, K=2, lam=0.0),
+                          fb=FsbParams(tau=1e300, Wb=8), i_lo=4, i_hi=5, want_out=False)
+    assert list(res["sel"][0]) == [1, 3]
+    assert res["gap_rerank"][0] == pytest.approx(0.8 / 0.9, rel=1e-13)
+
+
 def test_rerank_log_sum_exp_closed_forms():
     """Identical tokens in a cell: LSE = l + log(s).  Two distinct logits: log(e^x + e^y) in
     closed form, finite even for logits near 1000 (a stable log-sum-exp)."""

@@ -63,6 +63,8 @@ MUTATIONS = [
     ("gap_k term size without the prior",
      "return sum / sqrt((double)cfg->d) + cfg->lambda * a_c * fabs(prior_gate(cfg, i, c));",
      "return sum / sqrt((double)cfg->d);"),
+    ("gap_k at the boundary only", "for (int64_t t = 0; t < K && t + 1 < nA; ++t) { /* |r_t - r_t+1|",
+     "for (int64_t t = K - 1; t < K && t + 1 < nA; ++t) { /* |r_t - r_t+1|"),
     ("keys rotated at the query position", "rope_rotate(k + j * d, d, (double)j, rope_base",
      "rope_rotate(k + j * d, d, (double)i_lo, rope_base"),
 ]
@@ -96,6 +98,8 @@ FSB_MUTATIONS = [
     ("rerank without the prior", "return mx + log(z) + cfg->lambda * a_c * g;", "return mx + log(z);"),
     ("rerank logits without 1/sqrt(d)", "        l[t] = dot / sqrt((double)d);", "        l[t] = dot;"),
     ("selection by the worst candidates", "while (y >= 0 && (rank[y].val < kv.val ||", "while (y >= 0 && (rank[y].val > kv.val ||"),
+    ("rerank gap at the boundary only", "for (int64_t t = 0; t < K && t + 1 < nc; ++t) {",
+     "for (int64_t t = K - 1; t < K && t + 1 < nc; ++t) {"),
     ("power iteration started at the nearest cell", "if (nrm > best || (nrm == best && cells[c] < bestid)) {",
      "if (best < 0 || nrm < best || (nrm == best && cells[c] < bestid)) {"),
 ]

@@ -273,6 +273,12 @@ def test_gap_k_against_term_sizes_closed_form():
         (2.0 + 0.5 * np.sqrt(2.0) * np.sqrt(2)) / np.sqrt(2), rel=1e-14)          # |-1| + |-1|, no cancellation
     # cell 2 scores (-2 + 1) / sqrt 2 < cell 1's; the boundary pair is cells 0 and 1
     assert res["gap_k"][4] == pytest.approx((r[0] - r[1]) / max(m), rel=1e-13)
+    # with K = 2 the pair that decides the order of the two selected cells counts too:
+    # content scores 1, 0.9, 0.1 (sizes 5, 0.9, 0.1): min(0.1 / 5, 0.8 / 0.9) = 0.02, not the
+    # boundary's 0.889
+    res2 = oracle.head(q, k, np.zeros_like(k), prm=Params(s=s, B=B, K=2, prune=False, lam=0.0), want_out=False)
+    assert list(res2["sel"][4]) == [0, 1]
+    assert res2["gap_k"][4] == pytest.approx(0.1 / 5.0, rel=1e-14)
 
 
 # ------------------------------------------------------------ readout ------
