@@ -95,6 +95,10 @@ def lib():
         L.fs_fsb_workspace_bytes.argtypes = [P_shape, P_prm, P_fsb]
         L.fs_fsb_workspace_bytes.restype = sz
         L.fs_fsb_prefill.argtypes = [P_shape, P_prm, P_fsb, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        i32_, i64_ = ctypes.c_int32, ctypes.c_int64
+        L.fs_decode_state_init.argtypes = [P_prm, i32_, i32_, i32_, ctypes.c_int, vp, sz, vp]
+        L.fs_longrange_prefill_chunk.argtypes = [P_prm, i32_, i32_, i32_, ctypes.c_int, vp, sz, i64_, vp, vp, vp, vp,
+                                                 vp, vp, vp, vp, vp]
         L.fs_decode_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, P_prm]
         L.fs_decode_state_bytes.restype = sz
         L.fs_longrange_decode.argtypes = [P_prm, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
@@ -108,7 +112,8 @@ def lib():
         L.fs_local_decode.argtypes = [i32, i32, i32, ctypes.c_int, i64, vp, sz, vp, vp, vp, vp, vp, vp, vp]
         for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout",
                      "fs_select_readout", "fs_longrange_prefill", "fs_longrange_prefill_noalloc", "fs_fsb_prefill",
-                     "fs_longrange_decode", "fs_local_window",
+                     "fs_longrange_decode", "fs_decode_state_init", "fs_longrange_prefill_chunk",
+                     "fs_local_window",
                      "fs_local_state_build", "fs_local_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -281,6 +286,39 @@ def fs_fsb_prefill(q, k, v, sigma_h, lambda_h, tau_h, gain, out, sel, cand, work
     _check(lib().fs_fsb_prefill(ctypes.byref(sh), ctypes.byref(prm), ctypes.byref(fb), _ptr(q), _ptr(k), _ptr(v), sig,
                                 lam, tau, _ptr(gain), _ptr(out), _ptr(sel), _ptr(cand), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)), "fs_fsb_prefill")
+
+
+def fs_decode_state_init(state, batch: int, H: int, d: int, dtype, params: Params = Params(), stream=None):
+    """An empty decode state at position 0 (dtype: a torch dtype)."""
+    import torch
+    code = FS_BF16 if dtype == torch.bfloat16 else FS_F32
+    prm = params.c()
+    _check(lib().fs_decode_state_init(ctypes.byref(prm), batch, H, d, code, _ptr(state),
+                                      state.numel() * state.element_size(), _stream(stream)), "fs_decode_state_init")
+
+
+def fs_longrange_prefill_chunk(state, q, k, v, sigma_h, lambda_h, gain, out, sel=None, params: Params = Params(),
+                               stream=None):
+    """Chunked prefill into a decode state: q, k, v, out [b, H, n, d], sel [b, H, n, K] or None."""
+    prm = params.c()
+    b, H, n, d = q.shape
+    sig, lam = _floats(sigma_h, H), _floats(lambda_h, H)
+    _check(lib().fs_longrange_prefill_chunk(ctypes.byref(prm), b, H, d, _dtype_code(q), _ptr(state),
+                                            state.numel() * state.element_size(), n, _ptr(q), _ptr(k), _ptr(v), sig,
+                                            lam, _ptr(gain), _ptr(out), _ptr(sel), _stream(stream)),
+           "fs_longrange_prefill_chunk")
+
+
+def prefill_chunk(state, q, k, v, params: Params = Params(), sigma=4.0, lam=1.0, gain=None, want_sel=True,
+                  out=None, sel=None, stream=None):
+    """Allocate the outputs with torch and run fs_longrange_prefill_chunk; returns (out, sel or None)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    if want_sel and sel is None:
+        sel = torch.empty(*q.shape[:3], params.K, dtype=torch.int32, device=q.device)
+    fs_longrange_prefill_chunk(state, q, k, v, sigma, lam, gain, out, sel if want_sel else None, params, stream)
+    return out, (sel if want_sel else None)
 
 
 # ------------------------------------------------------- allocation helpers --

@@ -198,6 +198,9 @@ size_t state_bytes_of(int32_t batch, int32_t H, const StateLayout &L)
     return (size_t)kStateHeaderBytes + (size_t)batch * H * (size_t)L.rec_bytes;
 }
 
+// Longest chunk fs_longrange_prefill_chunk takes in one call (the page prefills in chunks of 2048).
+constexpr int64_t kMaxChunk = 65536;
+
 // ---- local-branch decode state ----
 constexpr int64_t kMaxLocalWindow = 65535; // ring of w tokens, table of w + 1 rows
 
@@ -597,6 +600,55 @@ FSL_EXPORT fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, in
     return hip_status(launch_decode_step(batch * H, H, d, dtype == FS_BF16 ? 1 : 0, prm->K, prm->P, prm->W, prm->eps,
                                          L, expect, hc, state, q, k_new, v_new, gain, out, sel,
                                          static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT fs_status fs_decode_state_init(const fs_params *prm, int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
+                                          void *state, size_t state_bytes, void *stream)
+{
+    fs_status st = check_decode_dims(batch, H, d, dtype);
+    if (st != FS_OK)
+        return st;
+    st = check_decode_params(prm);
+    if (st != FS_OK)
+        return st;
+    if (!state)
+        return FS_ERR_INVALID;
+    if ((int64_t)batch * H > 65535)
+        return FS_ERR_UNSUPPORTED;
+    const StateLayout L = state_layout(d, dtype, prm);
+    if (state_bytes != state_bytes_of(batch, H, L))
+        return FS_ERR_STATE;
+    const StateHeader hdr = state_header(batch, H, d, dtype, prm, L);
+    return hip_status(launch_state_init(batch * H, L, hdr, state, static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT fs_status fs_longrange_prefill_chunk(const fs_params *prm, int32_t batch, int32_t H, int32_t d,
+                                                fs_dtype dtype, void *state, size_t state_bytes, int64_t n,
+                                                const void *q, const void *k, const void *v, const float *sigma_h,
+                                                const float *lambda_h, const float *gain, void *out, int32_t *sel,
+                                                void *stream)
+{
+    fs_status st = check_decode_dims(batch, H, d, dtype);
+    if (st != FS_OK)
+        return st;
+    st = check_decode_params(prm);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    if (!state || !q || !k || !v || !out || n < 1)
+        return FS_ERR_INVALID;
+    if (n > kMaxChunk || (int64_t)batch * H > 65535)
+        return FS_ERR_UNSUPPORTED;
+    const StateLayout L = state_layout(d, dtype, prm);
+    if (state_bytes != state_bytes_of(batch, H, L))
+        return FS_ERR_STATE;
+    const StateHeader expect = state_header(batch, H, d, dtype, prm, L);
+    return hip_status(launch_decode_step(batch * H, H, d, dtype == FS_BF16 ? 1 : 0, prm->K, prm->P, prm->W, prm->eps,
+                                         L, expect, hc, state, q, k, v, gain, out, sel,
+                                         static_cast<hipStream_t>(stream), (int)n));
 }
 
 FSL_EXPORT fs_status fs_local_window(const fs_shape *shape, int64_t w, float rope_base, const void *q, const void *k,

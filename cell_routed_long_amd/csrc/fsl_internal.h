@@ -61,11 +61,15 @@ hipError_t launch_state_build(const Geometry &g, const StateLayout &L, const Sta
                               const void *k, const void *v, const float *kbar, const float *a,
                               const int32_t *death, hipStream_t st);
 
-// One decode step for bh = batch * H records.
+// One decode step for bh = batch * H records (n_tok = 0: q, k_new, v_new, out [bh, d],
+// sel [bh, K]), or n_tok >= 1 consecutive steps in one launch (rows [bh, n_tok, ...]).
 hipError_t launch_decode_step(int32_t bh, int32_t H, int32_t d, int32_t bf16, int32_t K, int32_t P, int32_t W,
                               float eps, const StateLayout &L, const StateHeader &expect, const HeadConsts &hc,
                               void *state, const void *q, const void *k_new, const void *v_new,
-                              const float *gain, void *out, int32_t *sel, hipStream_t st);
+                              const float *gain, void *out, int32_t *sel, hipStream_t st, int n_tok = 0);
+
+// An empty decode state (position 0) for bh records.
+hipError_t launch_state_init(int32_t bh, const StateLayout &L, const StateHeader &hdr, void *state, hipStream_t st);
 
 // Local branch (Sec. 3.2, Eqs. 3-4) plus alpha_h * o_lr (Eq. 2) when o_lr is not NULL.
 struct LocalConsts {

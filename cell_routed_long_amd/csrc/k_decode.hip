@@ -252,7 +252,14 @@ __global__ __launch_bounds__(kThreads) void state_build_kernel(char *__restrict_
 // wave first and then over the waves' candidates.  Each selected cell's
 // softmax partials are kept apart by rank, and wave 0 combines them in rank
 // order, so outputs are bitwise the same whichever wave read which cell.
-template <typename T, int D>
+//
+// CHUNK: the same steps for n_tok consecutive tokens of every record in one
+// launch (a chunk of a prompt prefilled into the state, App. C "Bounded cache":
+// the bounded cache is prefilled in fixed-size chunks with the retention update
+// at every block boundary).  Token tau of record bh is row bh * n_tok + tau of
+// q, k_new, v_new, out and sel; the steps run in order, so the results are
+// those of n_tok single steps.
+template <typename T, int D, bool CHUNK>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict__ state, StateLayout L,
                                                                StateHeader expect, HeadConsts hc,
                                                                const T *__restrict__ q,
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
                                                                const T *__restrict__ v_new,
                                                                const float *__restrict__ gain,
                                                                T *__restrict__ out, int32_t *__restrict__ sel,
-                                                               int H, int K, int P, int W, float eps)
+                                                               int H, int K, int P, int W, float eps, int n_tok)
 {
     constexpr int EPC = 16 / (int)sizeof(T); // elements per 16-byte chunk
     constexpr int CPR = D / EPC;             // chunks per row
@@ -297,11 +304,14 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     const int h = (int)(bh % H);
     const int t = threadIdx.x, lane = t & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(t / kWave); // wave-uniform, kept in a scalar register
-    T *o_row = out + bh * D;
     const Record R = record_at(state, L, bh); // in bounds: the host checked the buffer size
     T *sk = reinterpret_cast<T *>(R.k);
     T *sv = reinterpret_cast<T *>(R.v);
     const int vrow0 = lane / CPR, vch = lane % CPR;
+    const int steps = CHUNK ? n_tok : 1;
+  for (int step = 0; step < steps; ++step) {
+    const int64_t tok = CHUNK ? bh * (int64_t)n_tok + step : bh; // this step's row of q, k_new, v_new, out, sel
+    T *o_row = out + tok * D;
 
     // ---- (a) entry: all loads first (clamped indices, no branches), then their uses ----
     // Threads t and t + 128 (t + D) load and store the same slot (feature), so the
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     const int ts = t_in ? tt : 0; // L.S >= 1
     const int32_t cell_in = R.cell[ts], flags_in = R.flags[ts], ridx_in = R.ridx[ts];
     const float a_in = R.a[ts];
-    const T q_in = q[bh * D + td], k_in = k_new[bh * D + td], v_in = v_new[bh * D + td];
+    const T q_in = q[tok * D + td], k_in = k_new[tok * D + td], v_in = v_new[tok * D + td];
     const int my_slot = t >> 1, my_part = t & 1;
     const int ks = my_slot < L.S ? my_slot : 0;
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
@@ -337,16 +347,19 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
                     (int)(hv.batch != expect.batch) | (int)(hv.H != expect.H) | (int)(hv.d != D) |
                     (int)(hv.dtype != expect.dtype) | (int)(hv.P != P) | (int)(hv.W != W) |
                     (int)(hv.n_slots != L.S) | (int)(hv.rec_bytes != L.rec_bytes);
-    if (bad) { // not a state of this shape: flag the output, leave the state alone
-        if (t < D) {
-            if constexpr (sizeof(T) == 2)
-                o_row[t] = (T)0x7fc0u; // bf16 quiet NaN
-            else
-                o_row[t] = __uint_as_float(0x7fc00000u);
+    if (bad) { // not a state of this shape: flag the outputs, leave the state alone
+        for (int s2 = step; s2 < steps; ++s2) {
+            const int64_t tk = CHUNK ? bh * (int64_t)n_tok + s2 : bh;
+            if (t < D) {
+                if constexpr (sizeof(T) == 2)
+                    out[tk * D + t] = (T)0x7fc0u; // bf16 quiet NaN
+                else
+                    out[tk * D + t] = __uint_as_float(0x7fc00000u);
+            }
+            if (sel && t < K)
+                sel[tk * K + t] = -1;
         }
-        if (sel && t < K)
-            sel[bh * K + t] = -1;
-        return;
+        return; // the header is the same for every thread: the whole workgroup leaves
     }
     s_cell[tt] = t_in ? cell_in : -1;
     s_flags[tt] = t_in ? flags_in : 0;
@@ -622,8 +635,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
     __syncthreads();
 
     // ---- wave 0: combine the cells in rank order, normalise, RMSNorm over d (Eq. 17), write ----
-    if (wave != 0)
+    if (!CHUNK && wave != 0)
         return;
+    if (wave == 0) {
     float u[FPL];
 #pragma unroll
     for (int j = 0; j < FPL; ++j)
@@ -670,9 +684,13 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(char *__restrict_
             o_row[FPL * lane + j] = y;
     }
     if (sel && t < K)
-        sel[bh * K + t] = sel_cell;
+        sel[tok * K + t] = sel_cell;
     if (t == 0)
         R.meta->pos = i + 1;
+    }
+    if constexpr (CHUNK)
+        __syncthreads(); // the next step reads what this one wrote to the record
+  }
 }
 
 template <typename T, int D>
@@ -688,13 +706,41 @@ hipError_t build_t(const Geometry &g, const StateLayout &L, const StateHeader &h
 template <typename T, int D>
 hipError_t step_t(int32_t bh, int32_t H, int32_t K, int32_t P, int32_t W, float eps, const StateLayout &L,
                   const StateHeader &expect, const HeadConsts &hc, void *state, const void *q, const void *k_new,
-                  const void *v_new, const float *gain, void *out, int32_t *sel, hipStream_t st)
+                  const void *v_new, const float *gain, void *out, int32_t *sel, int n_tok, hipStream_t st)
 {
-    hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3((unsigned)bh), dim3(kThreads), 0, st,
-                       static_cast<char *>(state), L, expect, hc, static_cast<const T *>(q),
-                       static_cast<const T *>(k_new), static_cast<const T *>(v_new), gain, static_cast<T *>(out),
-                       sel, H, K, P, W, eps);
+    if (n_tok == 0) // a single decode step
+        hipLaunchKernelGGL((decode_step_kernel<T, D, false>), dim3((unsigned)bh), dim3(kThreads), 0, st,
+                           static_cast<char *>(state), L, expect, hc, static_cast<const T *>(q),
+                           static_cast<const T *>(k_new), static_cast<const T *>(v_new), gain,
+                           static_cast<T *>(out), sel, H, K, P, W, eps, 1);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<T, D, true>), dim3((unsigned)bh), dim3(kThreads), 0, st,
+                           static_cast<char *>(state), L, expect, hc, static_cast<const T *>(q),
+                           static_cast<const T *>(k_new), static_cast<const T *>(v_new), gain,
+                           static_cast<T *>(out), sel, H, K, P, W, eps, n_tok);
     return hipGetLastError();
+}
+
+// An empty state at position 0: every slot free, nothing retained.
+__global__ void state_init_kernel(char *__restrict__ state, StateLayout L, StateHeader hdr)
+{
+    const int64_t bh = blockIdx.x;
+    if (bh == 0 && threadIdx.x == 0)
+        *reinterpret_cast<StateHeader *>(state) = hdr;
+    const Record R = record_at(state, L, bh);
+    for (int x = threadIdx.x; x < L.S; x += blockDim.x) {
+        R.cell[x] = -1;
+        R.flags[x] = 0;
+        R.ridx[x] = -1;
+        R.a[x] = 0.0f;
+    }
+    if (threadIdx.x == 0) {
+        R.meta->pos = 0;
+        R.meta->n_ret = 0;
+        R.meta->cur_slot = -1;
+    }
+    if (threadIdx.x < kStateHints)
+        R.meta->hint[threadIdx.x] = -1;
 }
 
 } // namespace
@@ -713,17 +759,24 @@ hipError_t launch_state_build(const Geometry &g, const StateLayout &L, const Sta
 hipError_t launch_decode_step(int32_t bh, int32_t H, int32_t d, int32_t bf16, int32_t K, int32_t P, int32_t W,
                               float eps, const StateLayout &L, const StateHeader &expect, const HeadConsts &hc,
                               void *state, const void *q, const void *k_new, const void *v_new,
-                              const float *gain, void *out, int32_t *sel, hipStream_t st)
+                              const float *gain, void *out, int32_t *sel, hipStream_t st, int n_tok)
 {
     if (bf16)
         return d == 64 ? step_t<uint16_t, 64>(bh, H, K, P, W, eps, L, expect, hc, state, q, k_new, v_new, gain, out,
-                                              sel, st)
+                                              sel, n_tok, st)
                        : step_t<uint16_t, 128>(bh, H, K, P, W, eps, L, expect, hc, state, q, k_new, v_new, gain,
-                                               out, sel, st);
+                                               out, sel, n_tok, st);
     return d == 64 ? step_t<float, 64>(bh, H, K, P, W, eps, L, expect, hc, state, q, k_new, v_new, gain, out, sel,
-                                       st)
+                                       n_tok, st)
                    : step_t<float, 128>(bh, H, K, P, W, eps, L, expect, hc, state, q, k_new, v_new, gain, out, sel,
-                                        st);
+                                        n_tok, st);
+}
+
+hipError_t launch_state_init(int32_t bh, const StateLayout &L, const StateHeader &hdr, void *state, hipStream_t st)
+{
+    hipLaunchKernelGGL(state_init_kernel, dim3((unsigned)bh), dim3(kThreads), 0, st, static_cast<char *>(state), L,
+                       hdr);
+    return hipGetLastError();
 }
 
 } // namespace fsl

@@ -328,6 +328,40 @@ fs_status fs_longrange_decode(const fs_params *prm, int32_t batch, int32_t H, in
                               void *out, int32_t *sel, void *stream);
 
 /*
+ * An empty decode state, at position 0 (nothing retained, every slot free), for
+ * prefilling a prompt entirely through fs_longrange_prefill_chunk.
+ *   state   fs_decode_state_bytes() bytes of device memory (FS_ERR_STATE otherwise)
+ */
+fs_status fs_decode_state_init(const fs_params *prm, int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
+                               void *state, size_t state_bytes, void *stream);
+
+/*
+ * Chunked prefill into a decode state (App. C "Bounded cache": the bounded
+ * cache is prefilled in fixed-size chunks -- the page uses 2048 tokens -- with
+ * the retention update at every block boundary; Sec. 3.3 "Inference").  The n
+ * tokens at the state's positions i .. i + n - 1 of every (sequence, head) are
+ * processed in order, each exactly as one fs_longrange_decode step (merge at
+ * block starts, append and cell summary, Eq. 7 scores over A, top-K, readout
+ * with Eq. 17), in one launch: the outputs and the final state are bitwise
+ * those of n single steps, and equal the whole-prompt prefill's at the same
+ * positions (the same causal operator).
+ *   state            as for fs_longrange_decode (built by fs_longrange_prefill,
+ *                    fs_decode_state_init, or an earlier chunk)            (in/out)
+ *   n                tokens per (sequence, head), 1 <= n <= 65536
+ *   q, k, v          device [batch, H, n, d] dtype: the chunk's rows          (input)
+ *   sigma_h, lambda_h, gain   as for fs_longrange_decode
+ *   out              device [batch, H, n, d] dtype                             (output)
+ *   sel              device [batch, H, n, K] int32, or NULL                    (output)
+ * Errors and the foreign-state check as for fs_longrange_decode (a foreign
+ * state gets NaN outputs for every row).
+ */
+fs_status fs_longrange_prefill_chunk(const fs_params *prm, int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
+                                     void *state, size_t state_bytes, int64_t n,
+                                     const void *q, const void *k, const void *v,
+                                     const float *sigma_h, const float *lambda_h, const float *gain,
+                                     void *out, int32_t *sel, void *stream);
+
+/*
  * Local branch (Sec. 3.2, Eqs. 3-4) and the branch combination (Sec. 3.1,
  * Eq. 2) for every query i of every (sequence, head):
  *   o_sr_i = softmax_{j in L_i}((R(i) q_i) . (R(j) k_j) / sqrt(d)) V_{L_i},

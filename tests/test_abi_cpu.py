@@ -317,3 +317,28 @@ def test_fsb_validation_before_launch(L):
     assert call(sh=big) == fsl.FS_ERR_UNSUPPORTED
     edge = shape(b=1, H=H, N=131200, d=128, dtype=fsl.FS_BF16)  # exactly 4096
     assert L.fs_fsb_workspace_bytes(ctypes.byref(edge), ctypes.byref(p), ctypes.byref(fb)) > 0
+
+
+def test_chunk_and_state_init_validation(L):
+    """fs_decode_state_init and fs_longrange_prefill_chunk reject bad arguments on the host."""
+    vp = ctypes.c_void_p
+    b, H, d = 1, 2, 64
+    p = prm()
+    n_bytes = fsl.fs_decode_state_bytes(b, H, d, fsl.FS_BF16)
+    sig = (ctypes.c_float * H)(4.0, 4.0)
+    lam = (ctypes.c_float * H)(1.0, 1.0)
+    assert L.fs_decode_state_init(ctypes.byref(p), b, H, d, fsl.FS_BF16, None, n_bytes, None) == fsl.FS_ERR_INVALID
+    assert L.fs_decode_state_init(ctypes.byref(p), b, H, d, fsl.FS_BF16, vp(1), n_bytes + 1, None) == fsl.FS_ERR_STATE
+    fs_p = prm(prune=False)
+    assert L.fs_decode_state_init(ctypes.byref(fs_p), b, H, d, fsl.FS_BF16, vp(1), n_bytes, None) == \
+        fsl.FS_ERR_UNSUPPORTED
+
+    def chunk(n=16, st=n_bytes, q=1, out=1):
+        return L.fs_longrange_prefill_chunk(ctypes.byref(p), b, H, d, fsl.FS_BF16, vp(1), st, n, vp(q) if q else None,
+                                            vp(1), vp(1), sig, lam, None, vp(out) if out else None, None, None)
+
+    assert chunk(n=0) == fsl.FS_ERR_INVALID
+    assert chunk(q=0) == fsl.FS_ERR_INVALID
+    assert chunk(out=0) == fsl.FS_ERR_INVALID
+    assert chunk(st=n_bytes - 256) == fsl.FS_ERR_STATE
+    assert chunk(n=65537) == fsl.FS_ERR_UNSUPPORTED
