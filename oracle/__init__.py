@@ -67,6 +67,8 @@ def _bind(path: str):
     lib.oracle_cell_score_mag.restype = ctypes.c_double
     lib.oracle_readout.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, i64, vp]
     lib.oracle_readout.restype = None
+    lib.oracle_backward_head.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp, vp, vp, vp, i64, i64] + [vp] * 8
+    lib.oracle_backward_head.restype = ctypes.c_int
     lib.oracle_fsb_chunks.argtypes = [i64, vp]
     lib.oracle_fsb_chunks.restype = ctypes.c_int32
     lib.oracle_fsb_forest.argtypes = [ctypes.POINTER(_Cfg), vp, vp, vp, i64, i64] + [vp] * 11
@@ -188,6 +190,30 @@ def readout(q_i, k, v, cells, g=None, prm: Params = Params()):
     cfg = prm.cfg(k.shape[0], k.shape[1])
     _load().oracle_readout(ctypes.byref(cfg), _p(q_i), _p(k), _p(v), _p(g), _p(T) if len(T) else None, len(T), _p(o))
     return o
+
+
+def backward(q, k, v, sel, dout, g=None, prm: Params = Params(), i_lo: int = 0, i_hi: int | None = None,
+             want_abs: bool = False):
+    """Readout backward (Sec. 3.3 "Training") for one (sequence, head): the gradients of
+    sum_i dout_i . o_i through the readout of the fixed selections sel [n, K] (queries i in
+    [i_lo, i_hi)).  Returns dict dq [n, d], dk, dv [N, d], dg [d] (and the *_abs sizes)."""
+    q, k, v, g, dout = _f64(q), _f64(k), _f64(v), _f64(g), _f64(dout)
+    N, d = k.shape
+    i_hi = N if i_hi is None else i_hi
+    n = i_hi - i_lo
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    res = {"dq": np.zeros((n, d)), "dk": np.zeros((N, d)), "dv": np.zeros((N, d)), "dg": np.zeros(d)}
+    if want_abs:
+        res.update({"dq_abs": np.zeros((n, d)), "dk_abs": np.zeros((N, d)), "dv_abs": np.zeros((N, d)),
+                    "dg_abs": np.zeros(d)})
+    cfg = prm.cfg(N, d)
+    rc = _load().oracle_backward_head(ctypes.byref(cfg), _p(q), _p(k), _p(v), _p(g), _p(sel), _p(dout), i_lo, i_hi,
+                                      _p(res["dq"]), _p(res["dk"]), _p(res["dv"]), _p(res["dg"]),
+                                      _p(res.get("dq_abs")), _p(res.get("dk_abs")), _p(res.get("dv_abs")),
+                                      _p(res.get("dg_abs")))
+    if rc != 0:
+        raise ValueError("oracle_backward_head rejected its arguments")
+    return res
 
 
 def cap_for(N: int, prm: Params) -> int:

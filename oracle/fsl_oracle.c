@@ -217,6 +217,151 @@ void oracle_readout(const oracle_cfg *cfg, const double *q_i, const double *k, c
     free(logit);
 }
 
+/* ---- readout backward (Sec. 3.3 "Training"; App. D.4) ----------------------- */
+/*
+ * Gradients of the loss through o_i = g (.) u r, r = 1 / sqrt(|u|^2 / d + eps),
+ * u = sum_j p_j v_j, p = softmax_j(l_j), l_j = q_i . k_j / sqrt(d) over the tokens
+ * j of a fixed selection T (no gradient through the selection), given
+ * dout = dL/do_i:
+ *   dL/du     = r (g (.) dout) - (r^3 / d) (sum_f g_f dout_f u_f) u
+ *   dL/dg    += r dout (.) u
+ *   dL/dv_j  += p_j dL/du
+ *   dL/dl_j   = p_j (dL/du . v_j - sum_j' p_j' dL/du . v_j')
+ *   dL/dq     = sum_j dL/dl_j k_j / sqrt(d),   dL/dk_j += dL/dl_j q_i / sqrt(d).
+ * The *_abs outputs (each may be NULL) receive the sums of the absolute values of
+ * the same terms (|r g dout| + |r^3/d s u| for du, and so on): the size the
+ * floating-point sums are exact to a few roundings of.
+ */
+void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
+                             const double *g, const int64_t *T, int64_t nT, const double *dout, double *dq,
+                             double *dk, double *dv, double *dg, double *dq_abs, double *dk_abs, double *dv_abs,
+                             double *dg_abs)
+{
+    const int32_t d = cfg->d, s = cfg->s;
+    for (int32_t f = 0; f < d; ++f) {
+        dq[f] = 0.0;
+        if (dq_abs)
+            dq_abs[f] = 0.0;
+    }
+    if (nT == 0) /* o is identically zero: no gradient */
+        return;
+    const int64_t nS = nT * s;
+    const double sd = sqrt((double)d);
+    int64_t *tok = malloc(sizeof(int64_t) * nS);
+    double *p = malloc(sizeof(double) * nS), *dl = malloc(sizeof(double) * nS), *dlabs = malloc(sizeof(double) * nS);
+    double *u = malloc(sizeof(double) * d), *du = malloc(sizeof(double) * d), *duabs = malloc(sizeof(double) * d);
+    int64_t n = 0;
+    for (int64_t t = 0; t < nT; ++t)
+        for (int32_t x = 0; x < s; ++x)
+            tok[n++] = T[t] * s + x;
+    /* forward: logits, softmax, u, r */
+    double mx = -INFINITY;
+    for (int64_t x = 0; x < nS; ++x) {
+        double dot = 0.0;
+        for (int32_t f = 0; f < d; ++f)
+            dot += q_i[f] * k[tok[x] * d + f];
+        p[x] = dot / sd;
+        if (p[x] > mx)
+            mx = p[x];
+    }
+    double z = 0.0;
+    for (int64_t x = 0; x < nS; ++x) {
+        p[x] = exp(p[x] - mx);
+        z += p[x];
+    }
+    for (int64_t x = 0; x < nS; ++x)
+        p[x] /= z;
+    double ms = 0.0;
+    for (int32_t f = 0; f < d; ++f) {
+        u[f] = 0.0;
+        for (int64_t x = 0; x < nS; ++x)
+            u[f] += p[x] * v[tok[x] * d + f];
+        ms += u[f] * u[f];
+    }
+    const double r = 1.0 / sqrt(ms / d + cfg->eps);
+    /* RMSNorm backward */
+    double sgu = 0.0, sguabs = 0.0;
+    for (int32_t f = 0; f < d; ++f) {
+        const double gf = g ? g[f] : 1.0;
+        sgu += gf * dout[f] * u[f];
+        sguabs += fabs(gf * dout[f] * u[f]);
+    }
+    for (int32_t f = 0; f < d; ++f) {
+        const double gf = g ? g[f] : 1.0;
+        du[f] = r * gf * dout[f] - r * r * r / d * sgu * u[f];
+        duabs[f] = fabs(r * gf * dout[f]) + r * r * r / d * sguabs * fabs(u[f]);
+        if (dg)
+            dg[f] += r * dout[f] * u[f];
+        if (dg_abs)
+            dg_abs[f] += fabs(r * dout[f] * u[f]);
+    }
+    /* softmax and value backward */
+    double delta = 0.0, deltaabs = 0.0;
+    for (int64_t x = 0; x < nS; ++x) {
+        double dp = 0.0, dpabs = 0.0;
+        for (int32_t f = 0; f < d; ++f) {
+            dp += du[f] * v[tok[x] * d + f];
+            dpabs += duabs[f] * fabs(v[tok[x] * d + f]);
+        }
+        dl[x] = dp;     /* dL/dp_j for now */
+        dlabs[x] = dpabs;
+        delta += p[x] * dp;
+        deltaabs += p[x] * dpabs;
+        for (int32_t f = 0; f < d; ++f) {
+            if (dv)
+                dv[tok[x] * d + f] += p[x] * du[f];
+            if (dv_abs)
+                dv_abs[tok[x] * d + f] += p[x] * duabs[f];
+        }
+    }
+    for (int64_t x = 0; x < nS; ++x) {
+        dlabs[x] = p[x] * (dlabs[x] + deltaabs);
+        dl[x] = p[x] * (dl[x] - delta);
+    }
+    /* logits backward */
+    for (int64_t x = 0; x < nS; ++x) {
+        for (int32_t f = 0; f < d; ++f) {
+            dq[f] += dl[x] * k[tok[x] * d + f] / sd;
+            if (dq_abs)
+                dq_abs[f] += dlabs[x] * fabs(k[tok[x] * d + f]) / sd;
+            if (dk)
+                dk[tok[x] * d + f] += dl[x] * q_i[f] / sd;
+            if (dk_abs)
+                dk_abs[tok[x] * d + f] += dlabs[x] * fabs(q_i[f]) / sd;
+        }
+    }
+    free(duabs); free(du); free(u); free(dlabs); free(dl); free(p); free(tok);
+}
+
+int oracle_backward_head(const oracle_cfg *cfg, const double *q, const double *k, const double *v, const double *g,
+                         const int32_t *sel, const double *dout, int64_t i_lo, int64_t i_hi, double *dq, double *dk,
+                         double *dv, double *dg, double *dq_abs, double *dk_abs, double *dv_abs, double *dg_abs)
+{
+    if (cfg->d <= 0 || cfg->s <= 0 || cfg->K < 1 || i_lo < 0 || i_hi > cfg->N || i_lo > i_hi || cfg->eps < 0.0)
+        return -1;
+    const int32_t d = cfg->d, K = cfg->K;
+    const int64_t M = cfg->N / cfg->s;
+    int64_t *T = malloc(sizeof(int64_t) * K);
+    for (int64_t i = i_lo; i < i_hi; ++i) {
+        const int64_t row = i - i_lo;
+        int64_t nT = 0;
+        for (int32_t t = 0; t < K; ++t) {
+            const int32_t c = sel[row * K + t];
+            if (c >= 0) {
+                if (c >= M) {
+                    free(T);
+                    return -1;
+                }
+                T[nT++] = c;
+            }
+        }
+        oracle_readout_backward(cfg, q + i * d, k, v, g, T, nT, dout + row * d, dq + row * d, dk, dv, dg,
+                                dq_abs ? dq_abs + row * d : NULL, dk_abs, dv_abs, dg_abs);
+    }
+    free(T);
+    return 0;
+}
+
 /* ---- the whole branch for one (sequence, head) ------------------------------ */
 
 int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const double *v,

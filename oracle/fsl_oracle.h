@@ -100,6 +100,27 @@ int oracle_head(const oracle_cfg *cfg, const double *q, const double *k, const d
 int oracle_local(int64_t N, int32_t d, int64_t w, double rope_base, const double *q, const double *k,
                  const double *v, double alpha, const double *o_lr, int64_t i_lo, int64_t i_hi, double *out);
 
+/*
+ * Readout backward (Sec. 3.3 "Training": gradients flow through the selected
+ * tokens only, none through the indices; App. D.4) for one query and a fixed
+ * selection T[0..nT): given dout = dL/do_i, writes dq [d] and adds into dk, dv
+ * [N, d] (rows of the selected tokens) and dg [d] (may be NULL).  The *_abs
+ * arrays (may be NULL) get the sums of the absolute values of the same terms.
+ * nT = 0 gives dq = 0 and adds nothing.
+ */
+void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
+                             const double *g, const int64_t *T, int64_t nT, const double *dout, double *dq,
+                             double *dk, double *dv, double *dg, double *dq_abs, double *dk_abs, double *dv_abs,
+                             double *dg_abs);
+
+/* The readout backward of queries i in [i_lo, i_hi) of one (sequence, head) with their
+ * selections sel [n, K] (-1 padded) and dout [n, d]: dq [n, d] written; dk, dv [N, d]
+ * and dg [d] accumulated (zero them first); *_abs likewise (may be NULL).  Returns 0,
+ * or -1 for invalid arguments (a selected cell past the last complete one). */
+int oracle_backward_head(const oracle_cfg *cfg, const double *q, const double *k, const double *v, const double *g,
+                         const int32_t *sel, const double *dout, int64_t i_lo, int64_t i_hi, double *dq, double *dk,
+                         double *dv, double *dg, double *dq_abs, double *dk_abs, double *dv_abs, double *dg_abs);
+
 /* ---- FS-B (Sec. 3.4; App. E.1), in fsb_oracle.c ------------------------- */
 
 typedef struct {

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_fsb_oracle_pins as fsb_pins
+from tests import test_oracle_backward_pins as bwd_pins
 from tests import test_oracle_pins as pins
 
 ORACLE_DIR = os.path.dirname(oracle.__file__)
@@ -67,6 +68,23 @@ MUTATIONS = [
      "for (int64_t t = K - 1; t < K && t + 1 < nA; ++t) { /* |r_t - r_t+1|"),
     ("keys rotated at the query position", "rope_rotate(k + j * d, d, (double)j, rope_base",
      "rope_rotate(k + j * d, d, (double)i_lo, rope_base"),
+    # readout backward (Sec. 3.3 "Training"; App. D.4)
+    ("backward: RMSNorm without the norm's own gradient", "du[f] = r * gf * dout[f] - r * r * r / d * sgu * u[f];",
+     "du[f] = r * gf * dout[f];"),
+    ("backward: RMSNorm correction r^2", "du[f] = r * gf * dout[f] - r * r * r / d * sgu * u[f];",
+     "du[f] = r * gf * dout[f] - r * r / d * sgu * u[f];"),
+    ("backward: gain dropped from du", "du[f] = r * gf * dout[f] -", "du[f] = r * dout[f] -"),
+    ("backward: gain dropped from the correction", "sgu += gf * dout[f] * u[f];", "sgu += dout[f] * u[f];"),
+    ("backward: eps dropped", "const double r = 1.0 / sqrt(ms / d + cfg->eps);", "const double r = 1.0 / sqrt(ms / d);"),
+    ("backward: softmax without the mean term", "dl[x] = p[x] * (dl[x] - delta);", "dl[x] = p[x] * dl[x];"),
+    ("backward: dq without 1/sqrt(d)", "dq[f] += dl[x] * k[tok[x] * d + f] / sd;", "dq[f] += dl[x] * k[tok[x] * d + f];"),
+    ("backward: dq overwritten per token", "dq[f] += dl[x] * k[tok[x] * d + f] / sd;",
+     "dq[f] = dl[x] * k[tok[x] * d + f] / sd;"),
+    ("backward: dk from the key not the query", "dk[tok[x] * d + f] += dl[x] * q_i[f] / sd;",
+     "dk[tok[x] * d + f] += dl[x] * k[tok[x] * d + f] / sd;"),
+    ("backward: dv without the softmax weight", "dv[tok[x] * d + f] += p[x] * du[f];", "dv[tok[x] * d + f] += du[f];"),
+    ("backward: dg without u", "dg[f] += r * dout[f] * u[f];", "dg[f] += r * dout[f];"),
+    ("backward: softmax gradient from keys", "dp += du[f] * v[tok[x] * d + f];", "dp += du[f] * k[tok[x] * d + f];"),
 ]
 
 
@@ -108,7 +126,7 @@ FSB_MUTATIONS = [
 def _pin_functions(golden):
     """Every pin of both suites as a zero-argument callable."""
     calls = []
-    for mod in (pins, fsb_pins):
+    for mod in (pins, fsb_pins, bwd_pins):
         for name in dir(mod):
             fn = getattr(mod, name)
             if not name.startswith("test_") or not callable(fn):
