@@ -228,9 +228,15 @@ void oracle_readout(const oracle_cfg *cfg, const double *q_i, const double *k, c
  *   dL/dv_j  += p_j dL/du
  *   dL/dl_j   = p_j (dL/du . v_j - sum_j' p_j' dL/du . v_j')
  *   dL/dq     = sum_j dL/dl_j k_j / sqrt(d),   dL/dk_j += dL/dl_j q_i / sqrt(d).
- * The *_abs outputs (each may be NULL) receive the sums of the absolute values of
- * the same terms (|r g dout| + |r^3/d s u| for du, and so on): the size the
- * floating-point sums are exact to a few roundings of.
+ *
+ * The *_abs outputs (each may be NULL) receive a first-order error scale of the
+ * same results: every quantity x carries a size xa, the sum of the absolute
+ * values of its own terms where each factor's error is scaled by the size of
+ * that factor (for a product a b: aa |b| + |a| ba; for a sum: the sum of the
+ * sizes).  The logits start with their term sums; p_j gets p_j (1 + la_j + the
+ * softmax mean of la); the inputs are exact.  A computation whose every step
+ * rounds to a relative e then differs from these results by a small multiple of
+ * e times the size, also where u, r or the softmax mean cancel.
  */
 void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
                              const double *g, const int64_t *T, int64_t nT, const double *dout, double *dq,
@@ -248,19 +254,24 @@ void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const dou
     const int64_t nS = nT * s;
     const double sd = sqrt((double)d);
     int64_t *tok = malloc(sizeof(int64_t) * nS);
-    double *p = malloc(sizeof(double) * nS), *dl = malloc(sizeof(double) * nS), *dlabs = malloc(sizeof(double) * nS);
-    double *u = malloc(sizeof(double) * d), *du = malloc(sizeof(double) * d), *duabs = malloc(sizeof(double) * d);
+    double *p = malloc(sizeof(double) * nS), *pa = malloc(sizeof(double) * nS);
+    double *dl = malloc(sizeof(double) * nS), *dla = malloc(sizeof(double) * nS);
+    double *u = malloc(sizeof(double) * d), *ua = malloc(sizeof(double) * d);
+    double *du = malloc(sizeof(double) * d), *dua = malloc(sizeof(double) * d);
     int64_t n = 0;
     for (int64_t t = 0; t < nT; ++t)
         for (int32_t x = 0; x < s; ++x)
             tok[n++] = T[t] * s + x;
-    /* forward: logits, softmax, u, r */
+    /* forward: logits (sizes la in pa for now), softmax, u, r */
     double mx = -INFINITY;
     for (int64_t x = 0; x < nS; ++x) {
-        double dot = 0.0;
-        for (int32_t f = 0; f < d; ++f)
+        double dot = 0.0, dota = 0.0;
+        for (int32_t f = 0; f < d; ++f) {
             dot += q_i[f] * k[tok[x] * d + f];
+            dota += fabs(q_i[f] * k[tok[x] * d + f]);
+        }
         p[x] = dot / sd;
+        pa[x] = dota / sd;
         if (p[x] > mx)
             mx = p[x];
     }
@@ -269,53 +280,64 @@ void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const dou
         p[x] = exp(p[x] - mx);
         z += p[x];
     }
-    for (int64_t x = 0; x < nS; ++x)
+    double mean_la = 0.0;
+    for (int64_t x = 0; x < nS; ++x) {
         p[x] /= z;
-    double ms = 0.0;
+        mean_la += p[x] * pa[x];
+    }
+    for (int64_t x = 0; x < nS; ++x)
+        pa[x] = p[x] * (1.0 + pa[x] + mean_la);
+    double ms = 0.0, msa = 0.0;
     for (int32_t f = 0; f < d; ++f) {
         u[f] = 0.0;
-        for (int64_t x = 0; x < nS; ++x)
+        ua[f] = 0.0;
+        for (int64_t x = 0; x < nS; ++x) {
             u[f] += p[x] * v[tok[x] * d + f];
+            ua[f] += pa[x] * fabs(v[tok[x] * d + f]);
+        }
         ms += u[f] * u[f];
+        msa += 2.0 * fabs(u[f]) * ua[f];
     }
     const double r = 1.0 / sqrt(ms / d + cfg->eps);
+    const double ra = r + r * r * r * (msa / d) / 2.0;
+    const double c3 = r * r * r / d, c3a = 3.0 * r * r * ra / d;
     /* RMSNorm backward */
-    double sgu = 0.0, sguabs = 0.0;
+    double sgu = 0.0, sgua = 0.0;
     for (int32_t f = 0; f < d; ++f) {
         const double gf = g ? g[f] : 1.0;
         sgu += gf * dout[f] * u[f];
-        sguabs += fabs(gf * dout[f] * u[f]);
+        sgua += fabs(gf * dout[f]) * ua[f];
     }
     for (int32_t f = 0; f < d; ++f) {
         const double gf = g ? g[f] : 1.0;
         du[f] = r * gf * dout[f] - r * r * r / d * sgu * u[f];
-        duabs[f] = fabs(r * gf * dout[f]) + r * r * r / d * sguabs * fabs(u[f]);
+        dua[f] = ra * fabs(gf * dout[f]) + c3a * fabs(sgu * u[f]) + c3 * (sgua * fabs(u[f]) + fabs(sgu) * ua[f]);
         if (dg)
             dg[f] += r * dout[f] * u[f];
         if (dg_abs)
-            dg_abs[f] += fabs(r * dout[f] * u[f]);
+            dg_abs[f] += ra * fabs(dout[f] * u[f]) + r * fabs(dout[f]) * ua[f];
     }
     /* softmax and value backward */
-    double delta = 0.0, deltaabs = 0.0;
+    double delta = 0.0, deltaa = 0.0;
     for (int64_t x = 0; x < nS; ++x) {
-        double dp = 0.0, dpabs = 0.0;
+        double dp = 0.0, dpa = 0.0;
         for (int32_t f = 0; f < d; ++f) {
             dp += du[f] * v[tok[x] * d + f];
-            dpabs += duabs[f] * fabs(v[tok[x] * d + f]);
+            dpa += dua[f] * fabs(v[tok[x] * d + f]);
         }
-        dl[x] = dp;     /* dL/dp_j for now */
-        dlabs[x] = dpabs;
+        dl[x] = dp; /* dL/dp_j and its size for now */
+        dla[x] = dpa;
         delta += p[x] * dp;
-        deltaabs += p[x] * dpabs;
+        deltaa += pa[x] * fabs(dp) + p[x] * dpa;
         for (int32_t f = 0; f < d; ++f) {
             if (dv)
                 dv[tok[x] * d + f] += p[x] * du[f];
             if (dv_abs)
-                dv_abs[tok[x] * d + f] += p[x] * duabs[f];
+                dv_abs[tok[x] * d + f] += pa[x] * fabs(du[f]) + p[x] * dua[f];
         }
     }
     for (int64_t x = 0; x < nS; ++x) {
-        dlabs[x] = p[x] * (dlabs[x] + deltaabs);
+        dla[x] = pa[x] * fabs(dl[x] - delta) + p[x] * (dla[x] + deltaa);
         dl[x] = p[x] * (dl[x] - delta);
     }
     /* logits backward */
@@ -323,14 +345,14 @@ void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const dou
         for (int32_t f = 0; f < d; ++f) {
             dq[f] += dl[x] * k[tok[x] * d + f] / sd;
             if (dq_abs)
-                dq_abs[f] += dlabs[x] * fabs(k[tok[x] * d + f]) / sd;
+                dq_abs[f] += dla[x] * fabs(k[tok[x] * d + f]) / sd;
             if (dk)
                 dk[tok[x] * d + f] += dl[x] * q_i[f] / sd;
             if (dk_abs)
-                dk_abs[tok[x] * d + f] += dlabs[x] * fabs(q_i[f]) / sd;
+                dk_abs[tok[x] * d + f] += dla[x] * fabs(q_i[f]) / sd;
         }
     }
-    free(duabs); free(du); free(u); free(dlabs); free(dl); free(p); free(tok);
+    free(dua); free(du); free(ua); free(u); free(dla); free(dl); free(pa); free(p); free(tok);
 }
 
 int oracle_backward_head(const oracle_cfg *cfg, const double *q, const double *k, const double *v, const double *g,

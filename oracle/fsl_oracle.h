@@ -105,7 +105,9 @@ int oracle_local(int64_t N, int32_t d, int64_t w, double rope_base, const double
  * tokens only, none through the indices; App. D.4) for one query and a fixed
  * selection T[0..nT): given dout = dL/do_i, writes dq [d] and adds into dk, dv
  * [N, d] (rows of the selected tokens) and dg [d] (may be NULL).  The *_abs
- * arrays (may be NULL) get the sums of the absolute values of the same terms.
+ * arrays (may be NULL) get a first-order error scale of the same results (the
+ * sizes of their terms, with every upstream factor's size carried along), the
+ * yardstick for comparing a rounded computation with these values.
  * nT = 0 gives dq = 0 and adds nothing.
  */
 void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,

@@ -182,3 +182,30 @@ def test_backward_rejects_a_cell_past_the_end():
     q, k, v = _head(64, 8, seed=21)
     with pytest.raises(ValueError):
         oracle.backward(q, k, v, np.array([[16, -1]], np.int32), np.ones((1, 8)), None, prm, 60, 61)
+
+
+def test_sizes_widen_where_u_cancels():
+    """With q = 0 the softmax is uniform (p = 1/4 over a 4-token cell); values v, -v, w,
+    -w + c give u = c / 4, far smaller than its terms.  Rounding p_j v_j and their sum
+    leaves u off by about e sum_j p_j |v_j| rather than e |u|, so dg = r dout u is off by
+    about e r |dout| sum_j p_j |v_j|: the error scale of dg must be at least that (here
+    ~1000 |dg|).  Without cancellation it stays comparable to |dg|."""
+    d, s = 4, 4
+    prm = oracle.Params(s=s, B=8, K=1, eps=1.0)
+    q = np.zeros((16, d))
+    k = RNG(20).standard_normal((16, d))
+    a = np.array([1.0, -2.0, 0.5, 3.0]) * 100.0
+    b = np.array([-1.5, 1.0, 2.0, -0.5]) * 100.0
+    c = np.array([0.3, 0.2, -0.1, 0.4])
+    v = np.zeros((16, d))
+    v[8:12] = [a, -a, b, -b + c]
+    dout = np.array([[1.0, -2.0, 0.5, 1.5]])
+    res = oracle.backward(q, k, v, np.array([[2]], np.int32), dout, None, prm, 12, 13, want_abs=True)
+    u = c / 4
+    r = 1.0 / np.sqrt(np.mean(u * u) + 1.0)
+    spread = np.abs(v[8:12]).sum(axis=0) / 4
+    assert np.all(res["dg_abs"] >= r * np.abs(dout[0]) * spread * (1 - 1e-12))
+    assert np.all(res["dg_abs"] > 100.0 * np.abs(res["dg"]))
+    v[8:12] = [a, a, b, b]  # no cancellation
+    res = oracle.backward(q, k, v, np.array([[2]], np.int32), dout, None, prm, 12, 13, want_abs=True)
+    assert np.all(res["dg_abs"] < 10.0 * np.abs(res["dg"]))

@@ -85,6 +85,8 @@ MUTATIONS = [
     ("backward: dv without the softmax weight", "dv[tok[x] * d + f] += p[x] * du[f];", "dv[tok[x] * d + f] += du[f];"),
     ("backward: dg without u", "dg[f] += r * dout[f] * u[f];", "dg[f] += r * dout[f];"),
     ("backward: softmax gradient from keys", "dp += du[f] * v[tok[x] * d + f];", "dp += du[f] * k[tok[x] * d + f];"),
+    ("backward: dg size without the size of u", "dg_abs[f] += ra * fabs(dout[f] * u[f]) + r * fabs(dout[f]) * ua[f];",
+     "dg_abs[f] += ra * fabs(dout[f] * u[f]);"),
 ]
 
 
