@@ -52,6 +52,7 @@ WORKLOADS = {
     "local_decode_256k": dict(prune=True, local_decode=True),
     "fsb_16k": dict(fsb=True),
     "chunk_256k": dict(prune=True, chunk=True),
+    "train_4k_bwd": dict(prune=True, backward=True),
 }
 DECODE_PREFIX = 262144
 DECODE_LAYER_STATES = 12  # independent states in rotation: 12 x ~26 MB per step exceeds the 256 MB MALL
@@ -203,6 +204,8 @@ def main() -> int:
         return run_fsb(args)
     if WORKLOADS[args.workload].get("chunk"):
         return run_chunk(args)
+    if WORKLOADS[args.workload].get("backward"):
+        return run_backward(args)
 
     wl = WORKLOADS[args.workload]
     w = synth.WORKLOADS[wl.get("inputs", args.workload)]
@@ -556,6 +559,142 @@ def run_fsb(args) -> int:
                    "mean_candidates_per_query": round(float(n_cand[:, :, prm.B:].mean()), 3)},
         "roofline": roofline, "cpu_baseline": cpu, "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "settle_steps": settle, "parity_spot_check": parity,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+BWD_METRIC = ("long-range readout backward query-tokens/s at the training shape (b16 H16 d64 N4096 bf16, "
+              "FS-L selections); % HBM roofline")
+
+
+def run_backward(args) -> int:
+    """The readout backward (Sec. 3.3 "Training"; App. D.4) on one GPU's share of the
+    pages' training step: 524,288 tokens per step over 8 GPUs at 4096 tokens is 16
+    sequences; 16 heads of width 64 (the 341M model).  The selections are the FS-L
+    prefill's on the same inputs (made once, outside the timed region: they are an
+    input of the backward); dout ~ N(0, 1); unit-range gains.  One step is one
+    fs_readout_backward call: the forward recomputation, du and the cell masks, dQ,
+    then dK/dV per cell and the gain reduction."""
+    import numpy as np
+    import torch
+
+    import cell_routed_long_amd as fsl
+    import synth
+
+    w = synth.WORKLOADS["train_4k"]
+    prm = fsl.Params()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    host = {x: synth.tensor(w, x) for x in ("q", "k", "v", "dout")}
+    gain_h = synth.gains(96, w.H, w.d)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, dout = (to_dev(host[x]) for x in ("q", "k", "v", "dout"))
+    gain = torch.from_numpy(gain_h).to(dev)
+    b, H, N, d = q.shape
+    _, sel, _ = fsl.prefill(q, k, v, prm, want_out=False)
+    sh = fsl.shape_of(q)
+    ws = torch.empty(fsl.fs_readout_backward_workspace_bytes(sh, prm), dtype=torch.uint8, device=dev)
+    dq, dk, dv = (torch.empty(b, H, N, d, dtype=torch.float32, device=dev) for _ in range(3))
+    dgain = torch.empty(H, d, dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fsl.fs_readout_backward(q, k, v, sel, gain, dout, dq, dk, dv, dgain, ws, prm)
+
+    settle = settle_clocks(step, 0.5)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = b * N / (ms * 1e-3)
+    # the forward readout over the same selections, for the backward / forward ratio
+    fw = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fsl.fs_readout(q, k, v, sel, gain, out, prm)
+    fw[0].record(stream)
+    for _ in range(10):
+        fsl.fs_readout(q, k, v, sel, gain, out, prm)
+    fw[1].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = fw[0].elapsed_time(fw[1]) / 10
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # algorithmic work of the call: q, k, v, dout (bf16) and the selections read once, dq, dk, dv
+    # (fp32) written once, the gains and their gradient; per (query, selected cell) the s tokens
+    # take 12 d FLOP: logits and u again (2 d each), dP, dq, dk, dv (2 d each)
+    sel_h = sel.cpu().numpy()
+    pairs = int((sel_h >= 0).sum())
+    alg_bytes = 4 * b * H * N * d * 2 + b * H * N * prm.K * 4 + 3 * b * H * N * d * 4 + 2 * H * d * 4
+    flop = float(pairs) * prm.s * 12 * d
+    t = ms * 1e-3
+    roofline = {"bound": "hbm", "achieved": round(alg_bytes / t / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(alg_bytes / t / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "fs_readout_backward (query side, key side, gain reduction)",
+                "alg_bytes_per_launch": int(alg_bytes), "alg_flop_per_launch": flop,
+                "mfma_frac_algorithmic": round(flop / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "note": "whole call; the per-kernel split is in the kernel-trace summary"}
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle_threads()
+        heads = [(bb, hh) for bb in range(0, b, 2) for hh in range(0, H, 2)]
+        op = oracle.Params(s=prm.s, B=prm.B, P=prm.P, W=prm.W, K=prm.K, eps=prm.eps)
+        x64 = {bh: tuple(synth.to_f64(host[t_][bh[0], bh[1]], "bf16") for t_ in ("q", "k", "v", "dout"))
+               for bh in heads}
+
+        def one(bh):
+            qq, kk, vv, gg = x64[bh]
+            return bh, oracle.backward(qq, kk, vv, sel_h[bh[0], bh[1]], gg, gain_h[bh[1]].astype(np.float64), op)
+
+        t1 = single_thread_seconds(one, heads[0])
+        _, passes, cpu_s = time_oracle(one, heads, threads)
+        model, visible = host_cpu()
+        cpu = {"value": round(passes * len(heads) * N / H / cpu_s, 1), "unit": "query-tokens/s", "cores": threads,
+               "kind": "oracle", "cpu_model": model, "host_cpus_visible": visible,
+               "single_thread_s_per_pair": round(t1, 3),
+               "sample": f"{len(heads)} of {b * H} (sequence, head) pairs, all {N} queries each, {passes} passes; "
+                         f"{cpu_s:.1f}s wall"}
+        # parity on two pairs, against the oracle's error scales (the bf16 bar of the parity tests)
+        from tests import parity_utils as pu
+        got = {nm: x.cpu().numpy() for nm, x in (("dq", dq), ("dk", dk), ("dv", dv))}
+        worst, bad = 0.0, 0
+        for bb, hh in [(0, 0), (b - 1, H - 1)]:
+            qq, kk, vv, gg = (synth.to_f64(host[t_][bb, hh], "bf16") for t_ in ("q", "k", "v", "dout"))
+            ref = oracle.backward(qq, kk, vv, sel_h[bb, hh], gg, gain_h[hh].astype(np.float64), op, want_abs=True)
+            for nm in ("dq", "dk", "dv"):
+                err = np.abs(got[nm][bb, hh] - ref[nm])
+                scale = ref[nm + "_abs"]
+                bad += int(pu.bwd_beyond_bar(got[nm][bb, hh], ref[nm], scale, "bf16").sum())
+                nz = scale > 0
+                worst = max(worst, float((err[nz] / scale[nz]).max()))
+        parity = {"heads": 2, "elements_beyond_bound": bad, "worst_error_over_scale": worst}
+        log(f"[bench] oracle {cpu_s:.1f}s on {threads} threads; parity {parity}")
+
+    result = {
+        "metric": BWD_METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": b, "heads": H, "seq_len": N, "head_dim": d, "s": prm.s, "B": prm.B,
+                   "P": prm.P, "W": prm.W, "K": prm.K, "selected_pairs": pairs,
+                   "gradient_dtype": "fp32"},
+        "roofline": roofline, "cpu_baseline": cpu, "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "forward_readout_ms": round(fwd_ms, 4), "settle_steps": settle, "parity_spot_check": parity,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -85,6 +85,9 @@ def lib():
         L.fs_score_select.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.fs_readout.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp]
         L.fs_select_readout.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.fs_readout_backward_workspace_bytes.argtypes = [P_shape, P_prm]
+        L.fs_readout_backward_workspace_bytes.restype = sz
+        L.fs_readout_backward.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fs_prefill_workspace_bytes.argtypes = [P_shape, P_prm]
         L.fs_prefill_workspace_bytes.restype = sz
         L.fs_longrange_prefill.argtypes = [P_shape, P_prm, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
@@ -110,7 +113,7 @@ def lib():
         L.fs_local_state_build.argtypes = [i32, i32, i32, ctypes.c_int, i64, ctypes.c_float, vp, sz, vp, vp, i64,
                                            i64, vp]
         L.fs_local_decode.argtypes = [i32, i32, i32, ctypes.c_int, i64, vp, sz, vp, vp, vp, vp, vp, vp, vp]
-        for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout",
+        for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout", "fs_readout_backward",
                      "fs_select_readout", "fs_longrange_prefill", "fs_longrange_prefill_noalloc", "fs_fsb_prefill",
                      "fs_longrange_decode", "fs_decode_state_init", "fs_longrange_prefill_chunk",
                      "fs_local_window",
@@ -207,6 +210,38 @@ def fs_readout(q, k, v, sel, gain, out, params: Params = Params(), stream=None):
     sh, prm = shape_of(q), params.c()
     _check(lib().fs_readout(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(gain),
                             _ptr(out), _stream(stream)), "fs_readout")
+
+
+def fs_readout_backward_workspace_bytes(sh: fs_shape, params: Params = Params()) -> int:
+    prm = params.c()
+    return int(lib().fs_readout_backward_workspace_bytes(ctypes.byref(sh), ctypes.byref(prm)))
+
+
+def fs_readout_backward(q, k, v, sel, gain, dout, dq, dk, dv, dgain, workspace, params: Params = Params(),
+                        stream=None):
+    """Backward of fs_readout through the fixed selection sel: dq, dk, dv [b,H,N,d] fp32 and
+    dgain [H,d] fp32 (when gain is given); see include/fsl.h."""
+    sh, prm = shape_of(q), params.c()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().fs_readout_backward(ctypes.byref(sh), ctypes.byref(prm), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
+                                     _ptr(gain), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgain),
+                                     _ptr(workspace), ws_bytes, _stream(stream)), "fs_readout_backward")
+
+
+def readout_backward(q, k, v, sel, dout, gain=None, params: Params = Params(), workspace=None, stream=None):
+    """Allocate the gradients and workspace with torch and run fs_readout_backward.
+    Returns (dq, dk, dv, dgain or None, workspace)."""
+    import torch
+    sh = shape_of(q)
+    ws_bytes = fs_readout_backward_workspace_bytes(sh, params)
+    if ws_bytes == 0:
+        raise FslError(FS_ERR_UNSUPPORTED, "fs_readout_backward_workspace_bytes")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    dgain = torch.empty(sh.H, sh.d, dtype=torch.float32, device=q.device) if gain is not None else None
+    fs_readout_backward(q, k, v, sel, gain, dout, dq, dk, dv, dgain, workspace, params, stream)
+    return dq, dk, dv, dgain, workspace
 
 
 def fs_select_readout(q, k, v, kbar, a, retained, n_retained, sigma_h, lambda_h, gain, out, sel=None,

@@ -320,6 +320,52 @@ FsbWorkspace fsb_workspace(const Geometry &g, const FsbLayout &L)
     return W;
 }
 
+// Workspace of fs_readout_backward, carved in this order (256-byte aligned).
+struct BwdLayout {
+    size_t du, lse, delta, masks, item_start, pstart, item_cell, partial, dg_part, dg2, total;
+};
+
+BwdLayout bwd_layout(const Geometry &g)
+{
+    const BwdSizes z = bwd_sizes(g);
+    BwdLayout L;
+    size_t off = 0;
+    L.du = off;
+    off += align_up((size_t)g.bh * g.N * g.d * sizeof(float)); // fp32, or two bf16 planes
+    L.lse = off;
+    off += align_up((size_t)g.bh * g.N * sizeof(float));
+    L.delta = off;
+    off += align_up((size_t)g.bh * g.N * sizeof(float));
+    L.masks = off;
+    off += align_up((size_t)g.bh * (g.M > 0 ? g.M : 1) * g.NB * 16);
+    L.item_start = off;
+    off += align_up((size_t)g.bh * (g.M + 1) * sizeof(int32_t));
+    L.pstart = off;
+    off += align_up((size_t)g.bh * (g.M + 1) * sizeof(int32_t));
+    L.item_cell = off;
+    off += align_up((size_t)g.bh * z.items_max * sizeof(int32_t));
+    L.partial = off;
+    off += align_up((size_t)g.bh * z.p_max * 2 * 32 * g.d * sizeof(float));
+    L.dg_part = off;
+    off += align_up((size_t)g.bh * g.NB * g.d * sizeof(float));
+    L.dg2 = off;
+    off += align_up((size_t)g.H * 32 * g.d * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+fs_status check_backward(const fs_shape *shape, const fs_params *prm)
+{
+    fs_status st = check_all(shape, prm);
+    if (st != FS_OK)
+        return st;
+    const Geometry g = geometry(shape, prm);
+    // one workgroup per cell on the key side: keep the grid below 2^24 workgroups
+    if (g.N > kBwdMaxTokens || (int64_t)g.bh * ((g.N + g.s - 1) / g.s) >= ((int64_t)1 << 24))
+        return FS_ERR_UNSUPPORTED;
+    return FS_OK;
+}
+
 fs_status check_fsb(const fs_shape *shape, const fs_params *prm, const fs_fsb_params *fb)
 {
     fs_status st = check_all(shape, prm);
@@ -425,6 +471,43 @@ FSL_EXPORT fs_status fs_readout(const fs_shape *shape, const fs_params *prm, con
         return FS_ERR_INVALID;
     const Geometry g = geometry(shape, prm);
     return hip_status(launch_readout(g, q, k, v, sel, gain, out, static_cast<hipStream_t>(stream)));
+}
+
+FSL_EXPORT size_t fs_readout_backward_workspace_bytes(const fs_shape *shape, const fs_params *prm)
+{
+    if (check_backward(shape, prm) != FS_OK)
+        return 0;
+    return bwd_layout(geometry(shape, prm)).total;
+}
+
+FSL_EXPORT fs_status fs_readout_backward(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
+                                         const void *v, const int32_t *sel, const float *gain, const void *dout,
+                                         float *dq, float *dk, float *dv, float *dgain, void *workspace,
+                                         size_t workspace_bytes, void *stream)
+{
+    fs_status st = check_backward(shape, prm);
+    if (st != FS_OK)
+        return st;
+    if (!q || !k || !v || !sel || !dout || !dq || !dk || !dv || !workspace)
+        return FS_ERR_INVALID;
+    const Geometry g = geometry(shape, prm);
+    const BwdLayout L = bwd_layout(g);
+    if (workspace_bytes < L.total)
+        return FS_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    BwdBuffers w;
+    w.du = ws + L.du;
+    w.lse = reinterpret_cast<float *>(ws + L.lse);
+    w.delta = reinterpret_cast<float *>(ws + L.delta);
+    w.masks = ws + L.masks;
+    w.item_start = reinterpret_cast<int32_t *>(ws + L.item_start);
+    w.pstart = reinterpret_cast<int32_t *>(ws + L.pstart);
+    w.item_cell = reinterpret_cast<int32_t *>(ws + L.item_cell);
+    w.partial = reinterpret_cast<float *>(ws + L.partial);
+    w.dg_part = reinterpret_cast<float *>(ws + L.dg_part);
+    w.dg2 = reinterpret_cast<float *>(ws + L.dg2);
+    return hip_status(launch_readout_backward(g, w, q, k, v, sel, gain, dout, dq, dk, dv, gain ? dgain : nullptr,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 FSL_EXPORT fs_status fs_select_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,

@@ -45,6 +45,40 @@ hipError_t launch_score_topk(const Geometry &g, const HeadConsts &hc, const void
 hipError_t launch_readout(const Geometry &g, const void *q, const void *k, const void *v,
                           const int32_t *sel, const float *gain, void *out, hipStream_t st);
 
+// Readout backward (Sec. 3.3 "Training"): device workspace of one call.
+//   du       per query dL/du: [bh, N, d] fp32 (fp32 tensors), or bf16 hi then lo
+//            planes of [bh, N, d] each (bf16 tensors)
+//   lse, delta [bh, N] fp32: the logits' log2-sum-exp2 (exp2 domain) and du . u
+//   masks    [bh, M, NB] 128-bit masks of the rows of each query block that
+//            selected each cell (for the cells available to the block)
+//   item_start, pstart [bh, M + 1] int32, item_cell [bh, items_max] int32: each
+//            cell's query list cut into chunks of at most kChunk queries
+//   partial  [bh, p_max, 2, 32, d] fp32 chunk sums of cells with several chunks
+//   dg_part  [bh, NB, d], dg2 [H, 32, d] fp32 partial gain gradients
+constexpr int64_t kBwdMaxTokens = 65536;            // the masks take N^2 / (s B) x 16 bytes per (sequence, head)
+constexpr int kBwdMaxCells = (int)(kBwdMaxTokens / 32);
+constexpr int kChunk = 512;                         // queries per chunk of a cell's list
+struct BwdBuffers {
+    void *du;
+    float *lse, *delta;
+    void *masks;
+    int32_t *item_start, *pstart, *item_cell;
+    float *partial, *dg_part, *dg2;
+};
+struct BwdSizes {
+    int64_t items_max; // chunks per head: M + ceil(N K / kChunk) bounds one per cell plus one per kChunk pairs
+    int64_t p_max;     // partial slots per head: a cell of n >= 2 chunks has more than (n - 1) kChunk
+                       // pairs and n <= 2 (n - 1), so 2 ceil(N K / kChunk) slots suffice
+};
+inline BwdSizes bwd_sizes(const Geometry &g)
+{
+    const int64_t extra = ((int64_t)g.N * g.K + kChunk - 1) / kChunk;
+    return BwdSizes{g.M + extra, 2 * extra > 0 ? 2 * extra : 1};
+}
+hipError_t launch_readout_backward(const Geometry &g, const BwdBuffers &w, const void *q, const void *k,
+                                   const void *v, const int32_t *sel, const float *gain, const void *dout, float *dq,
+                                   float *dk, float *dv, float *dgain, hipStream_t st);
+
 // Routing and readout of every 128-query block in one launch (bf16 only; the
 // retained lists at most kFusedMaxCap long).  sel may be NULL.  With kbar_norm
 // (optional) a tile of retained cells is passed over when no cell of it can

@@ -142,6 +142,39 @@ fs_status fs_score_select(const fs_shape *shape, const fs_params *prm, const voi
 fs_status fs_readout(const fs_shape *shape, const fs_params *prm, const void *q, const void *k, const void *v,
                      const int32_t *sel, const float *gain, void *out, void *stream);
 
+/* Bytes of workspace fs_readout_backward needs (0 on invalid or unsupported arguments). */
+size_t fs_readout_backward_workspace_bytes(const fs_shape *shape, const fs_params *prm);
+
+/*
+ * Backward of fs_readout (Sec. 3.3 "Training": gradients reach the shared
+ * projections through the selected-token readout; the top-P and top-K indices
+ * receive none; App. D.4).  With o_i = g * u_i r_i, u_i = softmax(q_i k_S / sqrt(d)) V_S
+ * over the tokens S_i of the cells sel[i] (Eq. 9) and r_i = 1/sqrt(|u_i|^2/d + eps)
+ * (Eq. 17), and dout_i = dL/do_i, the selection held fixed:
+ *   dq_i = sum_j dS_ij k_j / sqrt(d),  dk_j = sum_i dS_ij q_i / sqrt(d),
+ *   dv_j = sum_i p_ij du_i,  dgain = sum_i r_i dout_i * u_i,
+ * du_i = r_i g*dout_i - (r_i^3/d)(sum_f g_f dout_if u_if) u_i,
+ * dS_ij = p_ij (du_i . v_j - du_i . u_i).  The forward is recomputed from the
+ * inputs exactly as fs_readout reads them: a row's cells must be distinct, and
+ * entries < 0 or not available to the query's block (Eq. 6) are ignored.
+ *   q, k, v     [batch, H, N, d]  shape dtype (input)
+ *   sel         [batch, H, N, K]  int32 (input), as written by the selection calls
+ *   gain        device [H, d] fp32 RMSNorm gains, or NULL for unit gains
+ *   dout        [batch, H, N, d]  shape dtype (input)
+ *   dq, dk, dv  [batch, H, N, d]  fp32 (output; every element is written, 0 for a
+ *               query with no selected cell and for a token no query selected)
+ *   dgain       device [H, d] fp32 (output, summed over the batch), or NULL; not
+ *               written when gain is NULL
+ *   workspace   fs_readout_backward_workspace_bytes() bytes of device memory
+ * Deterministic: no floating-point atomics; repeated calls give identical bits.
+ * Supported: N <= 65,536 (the per-cell row masks take N^2/(s B) x 16 bytes per
+ * (sequence, head)) and batch * H * ceil(N / s) < 2^24.
+ */
+fs_status fs_readout_backward(const fs_shape *shape, const fs_params *prm, const void *q, const void *k,
+                              const void *v, const int32_t *sel, const float *gain, const void *dout, float *dq,
+                              float *dk, float *dv, float *dgain, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /*
  * Routing and readout in one call: fs_score_select followed by fs_readout
  * (Eq. 7, per-query top-K, Eq. 9 with Eq. 17's RMSNorm), same arguments and

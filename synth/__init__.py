@@ -17,6 +17,8 @@ so any (batch, head, position) slice can be regenerated on its own):
 * values are computed in fp64, rounded to fp32, and for bf16 workloads rounded
   again (nearest-even) to bf16.
 * optional gains: uniform on [0.5, 1.5) per (head, feature), stream 6.
+* upstream gradients dout (the loss gradient of a branch output, for the readout
+  backward): standard normal per feature, stream 7, flat index as for q.
 """
 from __future__ import annotations
 
@@ -32,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _SRC_PATH = os.path.join(_HERE, "gen.c")
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_KSCALE, STREAM_NEEDLE, STREAM_GAIN = 1, 2, 3, 4, 5, 6
+STREAM_Q, STREAM_K, STREAM_V, STREAM_KSCALE, STREAM_NEEDLE, STREAM_GAIN, STREAM_DOUT = 1, 2, 3, 4, 5, 6, 7
 
 
 def build(force: bool = False) -> str:
@@ -131,13 +133,13 @@ def _storage_dtype(dtype: str):
 
 def tensor(w: Workload, which: str, n0: int = 0, n1: int | None = None,
            heads: list[tuple[int, int]] | None = None, threads: int | None = None) -> np.ndarray:
-    """One of 'q', 'k', 'v' for positions [n0, n1).
+    """One of 'q', 'k', 'v', 'dout' for positions [n0, n1).
 
     Returns a C-contiguous array [batch, H, n1-n0, d] (or [len(heads), n1-n0, d]
     when `heads` lists (b, h) pairs) of float32, or of uint16 bf16 bit patterns.
     """
     n1 = w.N if n1 is None else n1
-    stream = {"q": STREAM_Q, "k": STREAM_K, "v": STREAM_V}[which]
+    stream = {"q": STREAM_Q, "k": STREAM_K, "v": STREAM_V, "dout": STREAM_DOUT}[which]
     pairs = heads if heads is not None else [(b, h) for b in range(w.batch) for h in range(w.H)]
     rows = n1 - n0
     st = _storage_dtype(w.dtype)
@@ -194,6 +196,9 @@ WORKLOADS = {
                             name="FS-L prefill b4 H16 d128 N16384 bf16, 0.5% needles"),
     "fs_32k": Workload(batch=1, H=16, N=32768, d=128, dtype="bf16", seed=4, needle_frac=0.005,
                        name="FS prefill b1 H16 d128 N32768 bf16, 0.5% needles"),
+    "train_4k": Workload(batch=16, H=16, N=4096, d=64, dtype="bf16", seed=6, needle_frac=0.005,
+                         name="FS-L readout backward b16 H16 d64 N4096 bf16 (one GPU's share of a 524,288-token "
+                              "training step of the 16-head, 64-wide attention), 0.5% needles"),
     "decode_256k": Workload(batch=32, H=8, N=262144 + 128, d=128, dtype="bf16", seed=5, needle_frac=0.005,
                             name="FS-L decode b32 H8 d128, 262144-token prefix + 128 steps, bf16"),
 }

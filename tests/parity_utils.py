@@ -40,6 +40,23 @@ def to_device(a: np.ndarray, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+# Readout backward bar: |gpu - oracle| <= BWD_REL[dtype] x the oracle's first-order error
+# scale + BWD_FLOOR x the tensor's largest scale.  The scale is a worst-case first-order
+# bound, so the bar is the relative rounding e of the path's arithmetic itself: for bf16
+# tensors the split products (p du, du v, dS k, ...) keep each factor to 2^-17, two factors
+# per product: e = 2^-16; for fp32 tensors the products are fp32 and the largest error is in
+# the softmax exponent, about 2^-23 |lse| with |lse| < 2^5: e = 2^-19 (relative, in p).
+BWD_REL = {"bf16": 2.0 ** -16, "f32": 2.0 ** -19}
+BWD_FLOOR = 1e-7
+
+
+def bwd_beyond_bar(got, ref, scale, dtype):
+    """Elements of a backward result beyond the bar (see BWD_REL)."""
+    import numpy as np
+    bound = BWD_REL[dtype] * scale + BWD_FLOOR * (scale.max() if scale.size else 0.0)
+    return np.abs(np.asarray(got, dtype=np.float64) - ref) > bound
+
+
 def inputs(w: synth.Workload):
     return {x: synth.tensor(w, x) for x in "qkv"}
 

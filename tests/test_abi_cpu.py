@@ -342,3 +342,36 @@ def test_chunk_and_state_init_validation(L):
     assert chunk(out=0) == fsl.FS_ERR_INVALID
     assert chunk(st=n_bytes - 256) == fsl.FS_ERR_STATE
     assert chunk(n=65537) == fsl.FS_ERR_UNSUPPORTED
+
+
+def test_readout_backward_validation_before_launch(L):
+    """fs_readout_backward rejects bad arguments on the host (readout backward: Sec. 3.3
+    "Training"), and its workspace covers du, lse, Delta, the cell masks and the gain partials."""
+    vp = ctypes.c_void_p
+    b, H, N, d = 2, 3, 4096, 64
+    sh = shape(b=b, H=H, N=N, d=d, dtype=fsl.FS_BF16)
+    p = prm()
+    need = L.fs_readout_backward_workspace_bytes(ctypes.byref(sh), ctypes.byref(p))
+    M, NB, K = N // 32, N // 128, 4
+    extra = -(-N * K // 512)  # chunks of 512 queries beyond one per cell
+    core = b * H * (N * d * 4 + 2 * N * 4 + M * NB * 16 + NB * d * 4)
+    tables = b * H * (2 * (M + 1) * 4 + (M + extra) * 4 + 2 * extra * 2 * 32 * d * 4) + H * 32 * d * 4
+    assert core + tables <= need < core + tables + 10 * 256
+
+    def call(sh=sh, q=1, k=1, v=1, sel=1, dout=1, dq=1, dk=1, dv=1, ws=need, wsp=1):
+        f = lambda x: vp(x) if x else None
+        return L.fs_readout_backward(ctypes.byref(sh), ctypes.byref(p), f(q), f(k), f(v), f(sel), None, f(dout),
+                                     f(dq), f(dk), f(dv), None, f(wsp), ws, None)
+
+    for name in ("q", "k", "v", "sel", "dout", "dq", "dk", "dv", "wsp"):
+        assert call(**{name: 0}) == fsl.FS_ERR_INVALID, name
+    assert call(ws=need - 1) == fsl.FS_ERR_WORKSPACE
+    big = shape(b=1, H=1, N=65536 + 1, d=d, dtype=fsl.FS_BF16)
+    assert L.fs_readout_backward_workspace_bytes(ctypes.byref(big), ctypes.byref(p)) == 0
+    assert call(sh=big) == fsl.FS_ERR_UNSUPPORTED
+    edge = shape(b=1, H=1, N=65536, d=d, dtype=fsl.FS_BF16)
+    assert L.fs_readout_backward_workspace_bytes(ctypes.byref(edge), ctypes.byref(p)) > 0
+    wide = shape(b=4096, H=128, N=1024, d=d, dtype=fsl.FS_BF16)  # 2^24 cells: the key side's grid is too large
+    assert call(sh=wide) == fsl.FS_ERR_UNSUPPORTED
+    assert call(sh=shape(b=1, H=1, N=4096, d=96, dtype=fsl.FS_BF16)) == fsl.FS_ERR_UNSUPPORTED
+    assert L.fs_readout_backward_workspace_bytes(ctypes.byref(sh), ctypes.byref(prm(K=9))) == 0

@@ -82,3 +82,78 @@ def test_topp_boundary_tie_validated():
         pu.check_retained_valid([1, 0, 6, 7], a, n, P, W)  # cell 0 (norm 5) is below the boundary
     with pytest.raises(AssertionError):
         pu.check_retained_valid([1, 3, 6], a, n, P, W)     # Recent_W incomplete
+
+
+# ---- the readout backward's bar (tests/test_gpu_backward.py) ---------------------------
+
+def _bf16(x):
+    """Round fp32 values to bf16 (nearest even), returned as fp32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _split(x, with_lo):
+    hi = _bf16(x)
+    return (hi, _bf16(x - hi)) if with_lo else (hi, np.zeros_like(hi))
+
+
+def _emulated_backward(q, k, v, sel, dout, s, with_lo):
+    """fp32 emulation of one head's readout backward with the matrix-product operands
+    that are not exact bf16 values (p, du, dS) split into bf16 hi + lo parts (or, with
+    with_lo False, rounded to bf16 alone); q, k, v, dout are exact bf16 values."""
+    f32 = np.float32
+    N, d = k.shape
+    dq = np.zeros((len(sel), d), f32)
+    dk = np.zeros((N, d), f32)
+    dv = np.zeros((N, d), f32)
+    sd = f32(np.sqrt(d))
+    for r, cells in enumerate(sel):
+        toks = np.array([c * s + x for c in cells if c >= 0 for x in range(s)], np.int64)
+        if len(toks) == 0:
+            continue
+        qi = q[r].astype(f32)
+        K, V = k[toks].astype(f32), v[toks].astype(f32)
+        lg = (K @ qi) / sd
+        p = np.exp(lg - lg.max()).astype(f32)
+        p = (p / p.sum()).astype(f32)
+        ph, pl = _split(p, with_lo)
+        u = (ph @ V + pl @ V).astype(f32)
+        rn = f32(1.0) / np.sqrt(f32(np.mean(u * u)) + f32(1e-8))
+        du = (rn * dout[r] - rn ** 3 / d * f32(np.sum(dout[r] * u)) * u).astype(f32)
+        uh, ul = _split(du, with_lo)
+        dp = (V @ uh + V @ ul).astype(f32)
+        ds = (p * (dp - f32(du @ u))).astype(f32)
+        sh, sl = _split(ds, with_lo)
+        dq[r] = (sh @ K + sl @ K) / sd
+        dk[toks] += (np.outer(sh, qi) + np.outer(sl, qi)) / sd
+        dv[toks] += np.outer(ph, uh) + np.outer(ph, ul) + np.outer(pl, uh)
+    return dq, dk, dv
+
+
+def _beyond_bar(got, ref, scale):
+    return int(pu.bwd_beyond_bar(got, ref, scale, "bf16").sum())
+
+
+def test_backward_bar_admits_split_products_and_rejects_bf16_only():
+    """The bf16 bar of the readout backward (2^-16 of the oracle's error scale) is met by
+    fp32 arithmetic whose non-bf16 product operands keep a lo part, and is missed when
+    the lo parts are dropped (operands rounded to bf16 alone, ~2^-9 of their size)."""
+    import synth
+    w = synth.Workload(batch=1, H=1, N=768, d=64, dtype="bf16", seed=77, needle_frac=0.01)
+    f64 = {x: synth.to_f64(synth.tensor(w, x)[0, 0], "bf16") for x in ("q", "k", "v", "dout")}
+    rng = np.random.default_rng(5)
+    i_lo = 384
+    sel = np.full((w.N - i_lo, 4), -1, np.int32)
+    for r in range(len(sel)):
+        n = ((i_lo + r) // 128) * 4
+        sel[r] = rng.choice(n, size=4, replace=False)
+    ref = oracle.backward(f64["q"], f64["k"], f64["v"], sel, f64["dout"][i_lo:], None, oracle.Params(), i_lo, w.N,
+                          want_abs=True)
+    args = (f64["q"][i_lo:].astype(np.float32), f64["k"].astype(np.float32), f64["v"].astype(np.float32), sel,
+            f64["dout"][i_lo:].astype(np.float32), 32)
+    good = _emulated_backward(*args, with_lo=True)
+    bad = _emulated_backward(*args, with_lo=False)
+    for name, g, b_ in zip(("dq", "dk", "dv"), good, bad):
+        assert _beyond_bar(g, ref[name], ref[name + "_abs"]) == 0, name
+        assert _beyond_bar(b_, ref[name], ref[name + "_abs"]) > 0, name
