@@ -233,10 +233,10 @@ void oracle_readout(const oracle_cfg *cfg, const double *q_i, const double *k, c
  * same results: every quantity x carries a size xa, the sum of the absolute
  * values of its own terms where each factor's error is scaled by the size of
  * that factor (for a product a b: aa |b| + |a| ba; for a sum: the sum of the
- * sizes).  The logits start with their term sums; p_j gets p_j (1 + la_j + the
- * softmax mean of la); the inputs are exact.  A computation whose every step
- * rounds to a relative e then differs from these results by a small multiple of
- * e times the size, also where u, r or the softmax mean cancel.
+ * sizes).  The inputs are exact and the softmax weights p_j are taken as known to
+ * a relative e (size p_j).  A computation whose products and sums after the
+ * softmax round to a relative e then differs from these results by a small
+ * multiple of e times the size, also where u, r or the softmax mean cancel.
  */
 void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const double *k, const double *v,
                              const double *g, const int64_t *T, int64_t nT, const double *dout, double *dq,
@@ -262,16 +262,13 @@ void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const dou
     for (int64_t t = 0; t < nT; ++t)
         for (int32_t x = 0; x < s; ++x)
             tok[n++] = T[t] * s + x;
-    /* forward: logits (sizes la in pa for now), softmax, u, r */
+    /* forward: logits, softmax, u, r */
     double mx = -INFINITY;
     for (int64_t x = 0; x < nS; ++x) {
-        double dot = 0.0, dota = 0.0;
-        for (int32_t f = 0; f < d; ++f) {
+        double dot = 0.0;
+        for (int32_t f = 0; f < d; ++f)
             dot += q_i[f] * k[tok[x] * d + f];
-            dota += fabs(q_i[f] * k[tok[x] * d + f]);
-        }
         p[x] = dot / sd;
-        pa[x] = dota / sd;
         if (p[x] > mx)
             mx = p[x];
     }
@@ -280,13 +277,10 @@ void oracle_readout_backward(const oracle_cfg *cfg, const double *q_i, const dou
         p[x] = exp(p[x] - mx);
         z += p[x];
     }
-    double mean_la = 0.0;
     for (int64_t x = 0; x < nS; ++x) {
         p[x] /= z;
-        mean_la += p[x] * pa[x];
+        pa[x] = p[x];
     }
-    for (int64_t x = 0; x < nS; ++x)
-        pa[x] = p[x] * (1.0 + pa[x] + mean_la);
     double ms = 0.0, msa = 0.0;
     for (int32_t f = 0; f < d; ++f) {
         u[f] = 0.0;
