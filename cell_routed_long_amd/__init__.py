@@ -71,9 +71,11 @@ def lib():
     """The loaded libfsl.so; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with cell_routed_long_amd.build()")
-        L = ctypes.CDLL(LIB_PATH)
+        # FSL_LIBRARY: an instrumented build of the same sources (the sanitizer test)
+        path = os.environ.get("FSL_LIBRARY") or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with cell_routed_long_amd.build()")
+        L = ctypes.CDLL(path)
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         P_shape, P_prm = ctypes.POINTER(fs_shape), ctypes.POINTER(fs_params)
         L.fs_status_string.argtypes = [ctypes.c_int]

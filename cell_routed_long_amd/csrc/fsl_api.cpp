@@ -33,11 +33,22 @@ fs_status check_params(const fs_params *p)
     return FS_OK;
 }
 
+// A C caller may store any int in an fs_dtype; reading a value outside the
+// enumerators through the C++ enum type is undefined, so validation reads the
+// field's bits as an int32 (later reads see a validated value).
+static_assert(sizeof(fs_dtype) == sizeof(int32_t), "fs_dtype is int-sized");
+bool dtype_valid(const fs_dtype &t)
+{
+    int32_t v;
+    std::memcpy(&v, &t, sizeof v);
+    return v == FS_F32 || v == FS_BF16;
+}
+
 fs_status check_shape(const fs_shape *sh)
 {
     if (!sh)
         return FS_ERR_INVALID;
-    if (sh->batch < 1 || sh->H < 1 || sh->N < 1 || sh->d < 1 || (sh->dtype != FS_F32 && sh->dtype != FS_BF16))
+    if (sh->batch < 1 || sh->H < 1 || sh->N < 1 || sh->d < 1 || !dtype_valid(sh->dtype))
         return FS_ERR_INVALID;
     if ((sh->d != 64 && sh->d != 128) || sh->H > FS_MAX_HEADS || sh->N > kMaxTokens ||
         (int64_t)sh->batch * sh->H > 65535)
@@ -138,9 +149,9 @@ fs_status check_decode_params(const fs_params *p)
     return FS_OK;
 }
 
-fs_status check_decode_dims(int32_t batch, int32_t H, int32_t d, fs_dtype dtype)
+fs_status check_decode_dims(int32_t batch, int32_t H, int32_t d, const fs_dtype &dtype)
 {
-    if (batch < 1 || H < 1 || d < 1 || (dtype != FS_F32 && dtype != FS_BF16))
+    if (batch < 1 || H < 1 || d < 1 || !dtype_valid(dtype))
         return FS_ERR_INVALID;
     if ((d != 64 && d != 128) || H > FS_MAX_HEADS)
         return FS_ERR_UNSUPPORTED;
@@ -236,7 +247,7 @@ LocalStateHeader local_header(int32_t batch, int32_t H, int32_t d, fs_dtype dtyp
     return h;
 }
 
-fs_status check_local_dims(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, int64_t w)
+fs_status check_local_dims(int32_t batch, int32_t H, int32_t d, const fs_dtype &dtype, int64_t w)
 {
     fs_status st = check_decode_dims(batch, H, d, dtype);
     if (st != FS_OK)
@@ -322,7 +333,7 @@ FsbWorkspace fsb_workspace(const Geometry &g, const FsbLayout &L)
 
 // Workspace of fs_readout_backward, carved in this order (256-byte aligned).
 struct BwdLayout {
-    size_t du, lse, delta, masks, item_start, pstart, item_cell, partial, dg_part, dg2, total;
+    size_t du, lse, delta, masks, item_start, pstart, item_cell, multi_cell, partial, dg_part, dg2, total;
 };
 
 BwdLayout bwd_layout(const Geometry &g)
@@ -344,6 +355,8 @@ BwdLayout bwd_layout(const Geometry &g)
     off += align_up((size_t)g.bh * (g.M + 1) * sizeof(int32_t));
     L.item_cell = off;
     off += align_up((size_t)g.bh * z.items_max * sizeof(int32_t));
+    L.multi_cell = off;
+    off += align_up((size_t)g.bh * (z.multi_max + 1) * sizeof(int32_t));
     L.partial = off;
     off += align_up((size_t)g.bh * z.p_max * 2 * 32 * g.d * sizeof(float));
     L.dg_part = off;
@@ -503,6 +516,7 @@ FSL_EXPORT fs_status fs_readout_backward(const fs_shape *shape, const fs_params 
     w.item_start = reinterpret_cast<int32_t *>(ws + L.item_start);
     w.pstart = reinterpret_cast<int32_t *>(ws + L.pstart);
     w.item_cell = reinterpret_cast<int32_t *>(ws + L.item_cell);
+    w.multi_cell = reinterpret_cast<int32_t *>(ws + L.multi_cell);
     w.partial = reinterpret_cast<float *>(ws + L.partial);
     w.dg_part = reinterpret_cast<float *>(ws + L.dg_part);
     w.dg2 = reinterpret_cast<float *>(ws + L.dg2);

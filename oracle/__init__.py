@@ -89,7 +89,8 @@ def _bind(path: str):
 def _load():
     global _lib
     if _lib is None:
-        _lib = _bind(build())
+        # FSL_ORACLE_LIBRARY: an instrumented build of the same sources (the sanitizer test)
+        _lib = _bind(os.environ.get("FSL_ORACLE_LIBRARY") or build())
     return _lib
 
 
