@@ -52,7 +52,9 @@ hipError_t launch_readout(const Geometry &g, const void *q, const void *k, const
 //   masks    [bh, M, NB] 128-bit masks of the rows of each query block that
 //            selected each cell (for the cells available to the block)
 //   item_start, pstart [bh, M + 1] int32, item_cell [bh, items_max] int32: each
-//            cell's query list cut into chunks of at most kChunk queries
+//            cell's query list cut into chunks of at most kChunk queries;
+//            multi_cell [bh, multi_max + 1] int32: the count, then the cells of
+//            several chunks
 //   partial  [bh, p_max, 2, 32, d] fp32 chunk sums of cells with several chunks
 //   dg_part  [bh, NB, d], dg2 [H, 32, d] fp32 partial gain gradients
 constexpr int64_t kBwdMaxTokens = 65536;            // the masks take N^2 / (s B) x 16 bytes per (sequence, head)
@@ -62,18 +64,19 @@ struct BwdBuffers {
     void *du;
     float *lse, *delta;
     void *masks;
-    int32_t *item_start, *pstart, *item_cell;
+    int32_t *item_start, *pstart, *item_cell, *multi_cell;
     float *partial, *dg_part, *dg2;
 };
 struct BwdSizes {
     int64_t items_max; // chunks per head: M + ceil(N K / kChunk) bounds one per cell plus one per kChunk pairs
     int64_t p_max;     // partial slots per head: a cell of n >= 2 chunks has more than (n - 1) kChunk
                        // pairs and n <= 2 (n - 1), so 2 ceil(N K / kChunk) slots suffice
+    int64_t multi_max; // cells of several chunks per head: each has more than kChunk pairs
 };
 inline BwdSizes bwd_sizes(const Geometry &g)
 {
     const int64_t extra = ((int64_t)g.N * g.K + kChunk - 1) / kChunk;
-    return BwdSizes{g.M + extra, 2 * extra > 0 ? 2 * extra : 1};
+    return BwdSizes{g.M + extra, 2 * extra > 0 ? 2 * extra : 1, extra};
 }
 hipError_t launch_readout_backward(const Geometry &g, const BwdBuffers &w, const void *q, const void *k,
                                    const void *v, const int32_t *sel, const float *gain, const void *dout, float *dq,

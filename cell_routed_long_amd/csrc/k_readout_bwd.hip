@@ -605,10 +605,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 4 && D == 128 ? 1 : 2) void 
 // sums over the cells; item_start[M] = the head's chunks.
 __global__ __launch_bounds__(256) void bwd_plan_kernel(const u32x4 *__restrict__ masks, int32_t *__restrict__ item_start,
                                                        int32_t *__restrict__ pstart, int32_t *__restrict__ item_cell,
-                                                       int64_t M, int NB, int cells_per_block, int64_t items_max)
+                                                       int32_t *__restrict__ multi_cell, int64_t M, int NB,
+                                                       int cells_per_block, int64_t items_max, int64_t multi_max)
 {
     __shared__ int32_t n_it[kBwdMaxCells], n_p[kBwdMaxCells];
-    __shared__ int32_t wsum[2][4];
+    __shared__ int32_t wsum[3][4];
     const int64_t head = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     for (int64_t c = threadIdx.x; c < M; c += blockDim.x) {
@@ -626,33 +627,37 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const u32x4 *__restrict__
     // exclusive scans over the cells: thread t takes cells [t*per, (t+1)*per)
     const int per = (int)((M + 255) / 256);
     const int c0 = threadIdx.x * per;
-    int si = 0, sp = 0;
+    int si = 0, sp = 0, sm_ = 0;
     for (int x = 0; x < per; ++x)
         if (c0 + x < M) {
             si += n_it[c0 + x];
             sp += n_p[c0 + x];
+            sm_ += n_p[c0 + x] > 0;
         }
-    int ii = si, ip = sp;
+    int ii = si, ip = sp, im = sm_;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        const int yi = __shfl_up(ii, o, kWave), yp = __shfl_up(ip, o, kWave);
+        const int yi = __shfl_up(ii, o, kWave), yp = __shfl_up(ip, o, kWave), ym = __shfl_up(im, o, kWave);
         if (lane >= o) {
             ii += yi;
             ip += yp;
+            im += ym;
         }
     }
     if (lane == kWave - 1) {
         wsum[0][wave] = ii;
         wsum[1][wave] = ip;
+        wsum[2][wave] = im;
     }
     __syncthreads();
-    int oi = ii - si, op = ip - sp;
+    int oi = ii - si, op = ip - sp, om = im - sm_;
     for (int w = 0; w < wave; ++w) {
         oi += wsum[0][w];
         op += wsum[1][w];
+        om += wsum[2][w];
     }
     int32_t *is = item_start + head * (M + 1), *ps = pstart + head * (M + 1);
-    int32_t *ic = item_cell + head * items_max;
+    int32_t *ic = item_cell + head * items_max, *mcl = multi_cell + head * (multi_max + 1);
     for (int x = 0; x < per; ++x) {
         const int64_t c = c0 + x;
         if (c >= M)
@@ -661,12 +666,15 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const u32x4 *__restrict__
         ps[c] = op;
         for (int t = 0; t < n_it[c]; ++t)
             ic[oi + t] = (int32_t)c;
+        if (n_p[c] > 0)
+            mcl[1 + om++] = (int32_t)c;
         oi += n_it[c];
         op += n_p[c];
     }
     if (threadIdx.x == 255) {
         is[M] = oi;
         ps[M] = op;
+        mcl[0] = om; // cells of several chunks
     }
 }
 
@@ -701,7 +709,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
     int cells_per_block, int64_t items_max, int64_t p_max, int64_t plane)
 {
     __shared__ KeySmem<T, D> sm;
-    __shared__ uint16_t qlist[4][kWin * 128]; // query offsets from the window's first query
+    __shared__ uint16_t qlist[4][kChunk]; // the chunk's query positions (N <= 65,536)
     __shared__ float lse_s[4][32], delta_s[4][32];
 
     constexpr bool kBf16 = sizeof(T) == 2;
@@ -747,6 +755,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
         for (int r = 0; r < 16; ++r)
             dk_acc[dt][r] = dv_acc[dt][r] = 0.0f;
 
+    // ---- the chunk's queries, in ascending order, from the cell's masks ----
     const int b0 = (int)(c / cells_per_block) + 1; // first block for which the cell is available
     const u32x4 *mc = masks + (head * M + c) * NB;
     uint16_t *ql = qlist[wave];
@@ -764,131 +773,155 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
                 incl += y;
         }
         const int nw = __shfl(incl, kWave - 1, kWave);
-        if (cum + nw <= lo_q) { // the whole window lies before the chunk
-            cum += nw;
-            continue;
-        }
-        {
-            int pos = incl - cnt;
+        if (cum + nw > lo_q) {
+            int64_t pos = cum + incl - cnt;
             uint32_t b = bits;
-            const int base = (lane >> 2) * 128 + (lane & 3) * 32;
-            while (b) {
+            const int base = bk * 128 + (lane & 3) * 32;
+            while (b && pos < hi_q) {
                 const int bit = __ffs(b) - 1;
                 b &= b - 1u;
-                ql[pos++] = (uint16_t)(base + bit);
+                if (pos >= lo_q)
+                    ql[pos - lo_q] = (uint16_t)(base + bit);
+                ++pos;
             }
+        }
+        cum += nw;
+    }
+    const int n_q = (int)((cum < hi_q ? cum : hi_q) - lo_q); // queries of this chunk (0 for an unselected cell)
+    wave_sync_lds();
+
+    // ---- tiles of 32 queries; the next tile's rows are fetched while this one is on the matrix cores ----
+    const int64_t hN = head * N;
+    constexpr int CQ = kBf16 ? D / 8 : D / 4; // 16-byte chunks per staged row
+    constexpr int PER = 32 * CQ / kWave;      // chunks per lane per staged tensor
+    u32x4 nq[PER], nh[PER], nl[PER];
+    float n_lse = INFINITY, n_delta = 0.0f;
+    auto fetch = [&](int t0) {
+        const int nt = n_q - t0 < 32 ? n_q - t0 : 32;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int ch = lane + kWave * u, row = ch / CQ;
+            nq[u] = nh[u] = nl[u] = u32x4{0u, 0u, 0u, 0u};
+            if (row < nt) {
+                const int64_t at = (hN + ql[t0 + row]) * D;
+                if constexpr (kBf16) {
+                    const uint16_t *uhi = static_cast<const uint16_t *>(du_ws);
+                    const int c8 = (ch % CQ) * 8;
+                    nq[u] = *reinterpret_cast<const u32x4 *>(q + at + c8);
+                    nh[u] = *reinterpret_cast<const u32x4 *>(uhi + at + c8);
+                    nl[u] = *reinterpret_cast<const u32x4 *>(uhi + plane + at + c8);
+                } else {
+                    const int c4 = (ch % CQ) * 4;
+                    nq[u] = *reinterpret_cast<const u32x4 *>(q + at + c4);
+                    nh[u] = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(du_ws) + at + c4);
+                }
+            }
+        }
+        n_lse = INFINITY; // p = 0 for the padding rows
+        n_delta = 0.0f;
+        if (lane < nt) {
+            n_lse = lse_ws[hN + ql[t0 + lane]];
+            n_delta = delta_ws[hN + ql[t0 + lane]];
+        }
+    };
+    if (kBf16 && n_q > 0)
+        fetch(0);
+    for (int t0 = 0; t0 < n_q; t0 += 32) {
+        if constexpr (!kBf16)
+            fetch(t0); // fp32 rows are four times the registers: no fetch ahead
+        // ---- the fetched rows into this wave's staging area ----
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int ch = lane + kWave * u, row = ch / CQ;
+            if constexpr (kBf16) {
+                const int c8 = (ch % CQ) * 8;
+                *reinterpret_cast<u32x4 *>(&sm.qr[wave][row][c8]) = nq[u];
+                *reinterpret_cast<u32x4 *>(&sm.uh[wave][row][c8]) = nh[u];
+                *reinterpret_cast<u32x4 *>(&sm.ul[wave][row][c8]) = nl[u];
+            } else {
+                const int c4 = (ch % CQ) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sm.qr[wave][row][c4 + e] = __uint_as_float(nq[u][e]);
+                    sm.du[wave][row][c4 + e] = __uint_as_float(nh[u][e]);
+                }
+            }
+        }
+        if (lane < 32) {
+            lse_s[wave][lane] = n_lse;
+            delta_s[wave][lane] = n_delta;
         }
         wave_sync_lds();
-        const int a0 = (int)(lo_q > cum ? lo_q - cum : 0);
-        const int a1 = (int)(hi_q - cum < nw ? hi_q - cum : nw);
-        cum += nw;
-        const int64_t qbase = head * N + (int64_t)win * 128;
-        for (int t0 = a0; t0 < a1; t0 += 32) {
-            const int nt = a1 - t0 < 32 ? a1 - t0 : 32;
-            // ---- stage the tile's 32 query rows and du rows (zero past nt) ----
-            if constexpr (kBf16) {
-                constexpr int CQ = D / 8; // 16-byte chunks per bf16 row
-                const uint16_t *uhi = static_cast<const uint16_t *>(du_ws);
-#pragma unroll
-                for (int ch = lane; ch < 32 * CQ; ch += kWave) {
-                    const int row = ch / CQ, c8 = (ch % CQ) * 8;
-                    u32x4 wq = u32x4{0u, 0u, 0u, 0u}, wh = wq, wl = wq;
-                    if (row < nt) {
-                        const int64_t at = (qbase + ql[t0 + row]) * D + c8;
-                        wq = *reinterpret_cast<const u32x4 *>(q + at);
-                        wh = *reinterpret_cast<const u32x4 *>(uhi + at);
-                        wl = *reinterpret_cast<const u32x4 *>(uhi + plane + at);
-                    }
-                    *reinterpret_cast<u32x4 *>(&sm.qr[wave][row][c8]) = wq;
-                    *reinterpret_cast<u32x4 *>(&sm.uh[wave][row][c8]) = wh;
-                    *reinterpret_cast<u32x4 *>(&sm.ul[wave][row][c8]) = wl;
-                }
-            } else {
-                const float *duf = static_cast<const float *>(du_ws);
-                for (int e = lane; e < 32 * D; e += kWave) {
-                    const int row = e / D, f = e % D;
-                    const bool ok = row < nt;
-                    const int64_t src = ok ? (qbase + ql[t0 + row]) * D + f : 0;
-                    sm.qr[wave][row][f] = ok ? q[src] : 0.0f;
-                    sm.du[wave][row][f] = ok ? duf[src] : 0.0f;
-                }
-            }
-            if (lane < 32) {
-                const bool ok = lane < nt;
-                const int64_t qi = ok ? qbase + ql[t0 + lane] : 0;
-                lse_s[wave][lane] = ok ? lse_ws[qi] : INFINITY; // p = 0 for the padding rows
-                delta_s[wave][lane] = ok ? delta_ws[qi] : 0.0f;
-            }
-            wave_sync_lds();
+        if (kBf16 && t0 + 32 < n_q)
+            fetch(t0 + 32);
 
-            // ---- S = Q K^T and dP = du V^T: [query][token], lane col = token ----
-            f32x16 sacc, dp;
+        // ---- S = Q K^T and dP = du V^T: [query][token], lane col = token ----
+        f32x16 sacc, dp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sacc[r] = dp[r] = 0.0f;
-            if constexpr (kBf16) {
+        for (int r = 0; r < 16; ++r)
+            sacc[r] = dp[r] = 0.0f;
+        if constexpr (kBf16) {
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const int f0 = kc * 16 + half * 8;
-                    sacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.qr[wave][col][f0])), kf[kc], sacc);
-                    dp = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.ul[wave][col][f0])), vf[kc], dp);
-                    dp = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.uh[wave][col][f0])), vf[kc], dp);
-                }
-            } else {
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    sacc = mfma_f32(sm.qr[wave][col][kc * 2 + half], kf[kc], sacc);
-                    dp = mfma_f32(sm.du[wave][col][kc * 2 + half], vf[kc], dp);
-                }
+            for (int kc = 0; kc < KC; ++kc) {
+                const int f0 = kc * 16 + half * 8;
+                sacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.qr[wave][col][f0])), kf[kc], sacc);
+                dp = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.ul[wave][col][f0])), vf[kc], dp);
+                dp = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.uh[wave][col][f0])), vf[kc], dp);
             }
-            float p[16], ds[16];
+        } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qs = acc_row(r, half);
-                p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse_s[wave][qs]));
-                ds[r] = p[r] * (dp[r] - delta_s[wave][qs]);
+            for (int kc = 0; kc < KC; ++kc) {
+                sacc = mfma_f32(sm.qr[wave][col][kc * 2 + half], kf[kc], sacc);
+                dp = mfma_f32(sm.du[wave][col][kc * 2 + half], vf[kc], dp);
             }
-
-            // ---- dV += P^T du and dK += dS^T Q: [token][feature], contraction over the tile's queries ----
-            if constexpr (kBf16) {
-                // B operands: 8 queries of one feature (the rows the lane's p and dS belong to)
-                auto gather8 = [&](const uint16_t (*rows)[KeySmem<uint16_t, D>::kStride], int kk, int f) {
-                    u32x4 w;
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        w[x] = (uint32_t)rows[acc_row(8 * kk + 2 * x, half)][f] |
-                               ((uint32_t)rows[acc_row(8 * kk + 2 * x + 1, half)][f] << 16);
-                    return as_bf16x8(w);
-                };
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 ph, pl, sh, sl;
-                    split_bf16x8(&p[8 * kk], ph, pl);
-                    split_bf16x8(&ds[8 * kk], sh, sl);
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const int f = dt * 32 + col;
-                        const bf16x8 uhb = gather8(sm.uh[wave], kk, f), ulb = gather8(sm.ul[wave], kk, f);
-                        const bf16x8 qb = gather8(sm.qr[wave], kk, f);
-                        dv_acc[dt] = mfma_bf16(pl, uhb, dv_acc[dt]);
-                        dv_acc[dt] = mfma_bf16(ph, ulb, dv_acc[dt]);
-                        dv_acc[dt] = mfma_bf16(ph, uhb, dv_acc[dt]);
-                        dk_acc[dt] = mfma_bf16(sl, qb, dk_acc[dt]);
-                        dk_acc[dt] = mfma_bf16(sh, qb, dk_acc[dt]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int qs = acc_row(r, half);
-                        dv_acc[dt] = mfma_f32(p[r], sm.du[wave][qs][dt * 32 + col], dv_acc[dt]);
-                        dk_acc[dt] = mfma_f32(ds[r], sm.qr[wave][qs][dt * 32 + col], dk_acc[dt]);
-                    }
-            }
-            wave_sync_lds(); // the staged rows are read: the next tile may overwrite them
         }
+        float p[16], ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qs = acc_row(r, half);
+            p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse_s[wave][qs]));
+            ds[r] = p[r] * (dp[r] - delta_s[wave][qs]);
+        }
+
+        // ---- dV += P^T du and dK += dS^T Q: [token][feature], contraction over the tile's queries ----
+        if constexpr (kBf16) {
+            // B operands: 8 queries of one feature (the rows the lane's p and dS belong to)
+            auto gather8 = [&](const uint16_t (*rows)[KeySmem<uint16_t, D>::kStride], int kk, int f) {
+                u32x4 w;
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    w[x] = (uint32_t)rows[acc_row(8 * kk + 2 * x, half)][f] |
+                           ((uint32_t)rows[acc_row(8 * kk + 2 * x + 1, half)][f] << 16);
+                return as_bf16x8(w);
+            };
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 ph, pl, sh, sl;
+                split_bf16x8(&p[8 * kk], ph, pl);
+                split_bf16x8(&ds[8 * kk], sh, sl);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int f = dt * 32 + col;
+                    const bf16x8 uhb = gather8(sm.uh[wave], kk, f), ulb = gather8(sm.ul[wave], kk, f);
+                    const bf16x8 qb = gather8(sm.qr[wave], kk, f);
+                    dv_acc[dt] = mfma_bf16(pl, uhb, dv_acc[dt]);
+                    dv_acc[dt] = mfma_bf16(ph, ulb, dv_acc[dt]);
+                    dv_acc[dt] = mfma_bf16(ph, uhb, dv_acc[dt]);
+                    dk_acc[dt] = mfma_bf16(sl, qb, dk_acc[dt]);
+                    dk_acc[dt] = mfma_bf16(sh, qb, dk_acc[dt]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qs = acc_row(r, half);
+                    dv_acc[dt] = mfma_f32(p[r], sm.du[wave][qs][dt * 32 + col], dv_acc[dt]);
+                    dk_acc[dt] = mfma_f32(ds[r], sm.qr[wave][qs][dt * 32 + col], dk_acc[dt]);
+                }
+        }
+        wave_sync_lds(); // the staged rows are read: the next tile may overwrite them
     }
 
     // ---- out: lane (col, half) holds features dt*32 + col of tokens acc_row(r, half) ----
@@ -911,32 +944,36 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
         }
 }
 
-// One workgroup per (sequence, head, cell with rows): the chunk partial sums of
-// a cell of several chunks, added in chunk order; zeros for the tokens of the
+// Workgroup m of a head adds, in chunk order, the partial sums of the head's m-th
+// cell of several chunks; workgroup multi_max writes zeros for the tokens of the
 // incomplete last cell.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ partial,
                                                          const int32_t *__restrict__ item_start,
-                                                         const int32_t *__restrict__ pstart, float *__restrict__ dk,
+                                                         const int32_t *__restrict__ pstart,
+                                                         const int32_t *__restrict__ multi_cell, float *__restrict__ dk,
                                                          float *__restrict__ dv, int64_t N, int64_t M, int D,
-                                                         int64_t p_max)
+                                                         int64_t p_max, int64_t multi_max)
 {
     constexpr int s = 32;
-    const int64_t MC = M + ((N % s) != 0 ? 1 : 0);
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int64_t c = (int64_t)(lb % (uint32_t)MC);
-    const int64_t head = (int64_t)(lb / (uint32_t)MC);
-    if (c == M) { // the incomplete last cell: its tokens are never read
-        const int64_t r0 = M * s;
+    const int64_t m = (int64_t)(lb % (uint32_t)(multi_max + 1));
+    const int64_t head = (int64_t)(lb / (uint32_t)(multi_max + 1));
+    if (m == multi_max) {
+        const int64_t r0 = M * s; // the incomplete last cell: its tokens are never read
         for (int64_t e = threadIdx.x; e < (N - r0) * D; e += blockDim.x) {
             dk[(head * N + r0) * D + e] = 0.0f;
             dv[(head * N + r0) * D + e] = 0.0f;
         }
         return;
     }
+    if (M == 0)
+        return; // no complete cell: the plan did not run
+    const int32_t *mcl = multi_cell + head * (multi_max + 1);
+    if (m >= mcl[0])
+        return;
+    const int64_t c = mcl[1 + m];
     const int32_t *is = item_start + head * (M + 1);
     const int n = is[c + 1] - is[c];
-    if (n <= 1)
-        return; // written by its only chunk
     const float *p0 = partial + (head * p_max + pstart[head * (M + 1) + c]) * 2 * (32 * D);
     float *dkc = dk + (head * N + c * s) * D, *dvc = dv + (head * N + c * s) * D;
     for (int e = threadIdx.x; e < 32 * D; e += blockDim.x) {
@@ -1024,7 +1061,7 @@ hipError_t launch_typed(const Geometry &g, const BwdBuffers &w, const void *q, c
     const u32x4 *masks = reinterpret_cast<const u32x4 *>(w.masks);
     if (g.M > 0) {
         hipLaunchKernelGGL(bwd_plan_kernel, dim3((unsigned)g.bh), dim3(256), 0, st, masks, w.item_start, w.pstart,
-                           w.item_cell, g.M, g.NB, g.B / g.s, z.items_max);
+                           w.item_cell, w.multi_cell, g.M, g.NB, g.B / g.s, z.items_max, z.multi_max);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
         hipLaunchKernelGGL((bwd_key_kernel<T, D>), dim3((unsigned)(((z.items_max + 3) / 4) * g.bh)), dim3(kThreads), 0,
@@ -1034,9 +1071,8 @@ hipError_t launch_typed(const Geometry &g, const BwdBuffers &w, const void *q, c
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
-    const int64_t MC = g.M + ((g.N % g.s) != 0 ? 1 : 0);
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(MC * g.bh)), dim3(256), 0, st, w.partial, w.item_start,
-                       w.pstart, dk, dv, g.N, g.M, g.d, z.p_max);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((z.multi_max + 1) * g.bh)), dim3(256), 0, st, w.partial,
+                       w.item_start, w.pstart, w.multi_cell, dk, dv, g.N, g.M, g.d, z.p_max, z.multi_max);
     if ((e = hipGetLastError()) != hipSuccess || !gain || !dgain)
         return e;
     hipLaunchKernelGGL(bwd_gain_partial_kernel, dim3((unsigned)(g.H * kGainGroups)), dim3(256), 0, st, w.dg_part, w.dg2,

@@ -355,8 +355,9 @@ def test_readout_backward_validation_before_launch(L):
     M, NB, K = N // 32, N // 128, 4
     extra = -(-N * K // 512)  # chunks of 512 queries beyond one per cell
     core = b * H * (N * d * 4 + 2 * N * 4 + M * NB * 16 + NB * d * 4)
-    tables = b * H * (2 * (M + 1) * 4 + (M + extra) * 4 + 2 * extra * 2 * 32 * d * 4) + H * 32 * d * 4
-    assert core + tables <= need < core + tables + 10 * 256
+    tables = b * H * (2 * (M + 1) * 4 + (M + extra) * 4 + (extra + 1) * 4 + 2 * extra * 2 * 32 * d * 4) \
+        + H * 32 * d * 4
+    assert core + tables <= need < core + tables + 11 * 256
 
     def call(sh=sh, q=1, k=1, v=1, sel=1, dout=1, dq=1, dk=1, dv=1, ws=need, wsp=1):
         f = lambda x: vp(x) if x else None
