@@ -127,7 +127,8 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
     float pre_a;
     // the tile bound needs every retained cell's prior and mean-key norm: one
     // load each per block, kept in registers until the first tile is scored
-    const bool bound = kbar_norm != nullptr && nA > 32 && nA <= kThreads;
+    constexpr int kBoundTiles = 256; // the tile bound covers retained lists of up to 8192 cells
+    const bool bound = kbar_norm != nullptr && nA > 32 && nA <= kBoundTiles * 32;
     float b_pr = 0.0f, b_kn = 0.0f;
     if (bound && t < nA) { // lambda is applied where the values are first used, so nothing waits here
         const int64_t id = head * M + (prune ? s_A[t] : t);
@@ -171,8 +172,23 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
     // When it falls below every query's K-th best key so far, no cell of the
     // tile can enter any top-K, and the tile is passed over: the selections are
     // those of scoring every cell.  The first tile is always scored.
-    __shared__ float s_bpr[kThreads], s_bkn[kThreads], s_qn[kThreads / kWave];
+    // per 32-cell tile of the retained list: the largest lambda a_c and the largest |kbar_c|
+    // (NaN or infinite values make the tile's maximum infinite, so it is never passed over)
+    __shared__ float s_tpr[kBoundTiles], s_tkn[kBoundTiles], s_qn[kThreads / kWave];
     __shared__ uint32_t s_tau[2][kThreads / kWave];
+    auto tile_max = [&](int x, float pr, float kn) { // thread's cell x of the list; all threads call it
+        pr = pr <= FLT_MAX ? pr : INFINITY;
+        kn = kn <= FLT_MAX ? kn : INFINITY;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            pr = fmaxf(pr, shfl_xor_f(pr, o));
+            kn = fmaxf(kn, shfl_xor_f(kn, o));
+        }
+        if ((lane & 31) == 0) {
+            s_tpr[x >> 5] = pr;
+            s_tkn[x >> 5] = kn;
+        }
+    };
     int iter = 0;
     for (int t0 = 0; t0 < nA; t0 += 32, ++iter) {
         const int par = iter & 1; // tau slots alternate, so no wave overwrites one still being read
@@ -187,11 +203,7 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
         uint32_t tau = 0;
         float qn = 0.0f;
         auto tile_below = [&](int tb) {
-            const int x = tb + lane;
-            const float pr = lane < 32 && x < nA ? s_bpr[x] : 0.0f; // >= 0 unless NaN
-            const float kn = lane < 32 && x < nA ? s_bkn[x] : 0.0f;
-            const bool bad = __ballot(!(pr <= FLT_MAX) || !(kn <= FLT_MAX)) != 0ull; // NaN or infinite
-            const float pm = bad ? INFINITY : wave_max_f(pr), km = wave_max_f(kn);
+            const float pm = s_tpr[tb >> 5], km = s_tkn[tb >> 5];
             const float ub = (pm + qn * km * inv_sqrt_d * (1.0f + 0x1p-10f)) * (1.0f + 0x1p-10f);
             // ub >= 0: its ranking key's high word is its bits with the sign bit set
             return ub <= FLT_MAX && (__float_as_uint(ub) | 0x80000000u) < tau;
@@ -223,9 +235,18 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
 #pragma unroll
             for (int u = 0; u < SCH; ++u)
                 *reinterpret_cast<u32x4 *>(&sm.kb[part][srow][spart * PER + u * 8]) = pre3[part * SCH + u];
-        if (bound && t0 == 0 && t < nA) { // loaded before the tile, so here already; read after a later barrier
-            s_bpr[t] = lam * b_pr;
-            s_bkn[t] = b_kn;
+        if (bound && t0 == 0) { // loaded before the tile, so here already; read after a later barrier
+            tile_max(t, t < nA ? lam * b_pr : 0.0f, t < nA ? b_kn : 0.0f);
+            for (int x0 = kThreads; x0 < nA; x0 += kThreads) { // lists past 256 cells (FS)
+                const int x = x0 + t;
+                float pr = 0.0f, kn = 0.0f;
+                if (x < nA) {
+                    const int64_t id = head * M + (prune ? s_A[x] : x);
+                    pr = lam * a[id];
+                    kn = kbar_norm[id];
+                }
+                tile_max(x, pr, kn);
+            }
         }
         __syncthreads();
         if (t0 + 32 < nA && !(bound && t0 > 0 && tile_below(t0 + 32)))
