@@ -57,6 +57,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWin = 16; // query blocks whose masks one list window of the key side covers
+// Waves per key-side workgroup.  The waves share nothing, and a workgroup holds its LDS until
+// its slowest wave ends: with one wave per workgroup a wave with a long chunk never keeps
+// the slots of short ones.
+constexpr int kKeyWaves = 1;
 
 __device__ __forceinline__ void wave_sync_lds()
 {
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const u32x4 *__restrict__
             const u32x4 m = mc[bk];
             cnt += __popc(m[0]) + __popc(m[1]) + __popc(m[2]) + __popc(m[3]);
         }
-        const int n = cnt > 0 ? (cnt + kChunk - 1) / kChunk : 1;
+        const int n = cnt > 0 ? (cnt + kChunk - 1) / kChunk : 0; // 0: no query selected the cell
         n_it[c] = n;
         n_p[c] = n > 1 ? n : 0;
     }
@@ -630,7 +634,7 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const u32x4 *__restrict__
     int si = 0, sp = 0, sm_ = 0;
     for (int x = 0; x < per; ++x)
         if (c0 + x < M) {
-            si += n_it[c0 + x];
+            si += n_it[c0 + x] > 0 ? n_it[c0 + x] : 1; // an unselected cell: one chunk that writes zeros
             sp += n_p[c0 + x];
             sm_ += n_p[c0 + x] > 0;
         }
@@ -664,6 +668,8 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const u32x4 *__restrict__
             break;
         is[c] = oi;
         ps[c] = op;
+        if (n_it[c] == 0) // marked: the wave writes the cell's zero rows and nothing else
+            ic[oi++] = -1 - (int32_t)c;
         for (int t = 0; t < n_it[c]; ++t)
             ic[oi + t] = (int32_t)c;
         if (n_p[c] > 0)
@@ -681,27 +687,29 @@ __global__ __launch_bounds__(256) void bwd_plan_kernel(const u32x4 *__restrict__
 template <typename T, int D>
 struct KeySmem;
 
+// bf16: the tile's q, du hi and du lo rows as pair words, word [m][f] = (row 2m, row 2m + 1) at
+// feature f, so an 8-row B operand of one feature is four 4-byte reads
 template <int D>
 struct alignas(16) KeySmem<uint16_t, D> {
-    static constexpr int kStride = D + 8; // bf16 elements per staged row
-    uint16_t qr[4][32][kStride];
-    uint16_t uh[4][32][kStride]; // du, hi parts
-    uint16_t ul[4][32][kStride]; // du, lo parts
+    static constexpr int kStride = D + 4; // words per pair row
+    uint32_t pq[kKeyWaves][16][kStride];
+    uint32_t ph[kKeyWaves][16][kStride];
+    uint32_t pl[kKeyWaves][16][kStride];
 };
 
 template <int D>
 struct alignas(16) KeySmem<float, D> {
     static constexpr int kStride = D + 1;
-    float qr[4][32][kStride];
-    float du[4][32][kStride];
+    float qr[kKeyWaves][32][kStride];
+    float du[kKeyWaves][32][kStride];
 };
 
-// One wave per chunk of a cell's query list (four chunks of a head per
+// One wave per chunk of a cell's query list (kKeyWaves chunks of a head per
 // workgroup, each wave on its own): the chunk's queries from the cell's masks,
 // 32 at a time; the cell's rows are written once, by the wave itself when the
 // cell has one chunk, through the partial sums and bwd_reduce_kernel otherwise.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void bwd_key_kernel(
+__global__ __launch_bounds__(kKeyWaves * kWave, sizeof(T) == 2 && D == 64 ? 2 : 1) void bwd_key_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const void *__restrict__ du_ws,
     const float *__restrict__ lse_ws, const float *__restrict__ delta_ws, const u32x4 *__restrict__ masks,
     const int32_t *__restrict__ item_start, const int32_t *__restrict__ pstart, const int32_t *__restrict__ item_cell,
@@ -709,25 +717,36 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
     int cells_per_block, int64_t items_max, int64_t p_max, int64_t plane)
 {
     __shared__ KeySmem<T, D> sm;
-    __shared__ uint16_t qlist[4][kChunk]; // the chunk's query positions (N <= 65,536)
-    __shared__ float lse_s[4][32], delta_s[4][32];
+    __shared__ uint16_t qlist[kKeyWaves][kChunk]; // the chunk's query positions (N <= 65,536)
+    __shared__ __align__(16) float lse_s[kKeyWaves][32];
+    __shared__ __align__(16) float delta_s[kKeyWaves][32];
 
     constexpr bool kBf16 = sizeof(T) == 2;
     constexpr int s = 32;
     constexpr int DT = D / 32;
-    const int64_t Gq = (items_max + 3) / 4; // workgroups per head
+    const int64_t Gq = (items_max + kKeyWaves - 1) / kKeyWaves; // workgroups per head
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
     const int64_t head = (int64_t)(lb / (uint32_t)Gq);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int half = lane >> 5;
     const int col = lane & 31;
-    const int64_t j = (int64_t)(lb % (uint32_t)Gq) * 4 + wave;
+    const int64_t j = (int64_t)(lb % (uint32_t)Gq) * kKeyWaves + wave;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     const int32_t *is = item_start + head * (M + 1);
     if (j >= is[M])
         return;
-    const int64_t c = item_cell[head * items_max + j];
+    const int32_t cj = item_cell[head * items_max + j];
+    if (cj < 0) { // a cell no query selected: zero rows
+        const int64_t cz = -1 - (int64_t)cj;
+        float *dkc = dk + (head * N + cz * 32) * D, *dvc = dv + (head * N + cz * 32) * D;
+        for (int e = lane * 4; e < 32 * D; e += kWave * 4) {
+            *reinterpret_cast<u32x4 *>(dkc + e) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(dvc + e) = u32x4{0u, 0u, 0u, 0u};
+        }
+        return;
+    }
+    const int64_t c = cj;
     const int n_items = is[c + 1] - is[c];
     const int64_t lo_q = (j - is[c]) * (int64_t)kChunk, hi_q = lo_q + kChunk; // the chunk: list entries [lo_q, hi_q)
 
@@ -790,110 +809,91 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
     const int n_q = (int)((cum < hi_q ? cum : hi_q) - lo_q); // queries of this chunk (0 for an unselected cell)
     wave_sync_lds();
 
-    // ---- tiles of 32 queries; the next tile's rows are fetched while this one is on the matrix cores ----
+    // ---- tiles of 32 queries ----
     const int64_t hN = head * N;
-    constexpr int CQ = kBf16 ? D / 8 : D / 4; // 16-byte chunks per staged row
-    constexpr int PER = 32 * CQ / kWave;      // chunks per lane per staged tensor
-    u32x4 nq[PER], nh[PER], nl[PER];
-    float n_lse = INFINITY, n_delta = 0.0f;
-    auto fetch = [&](int t0) {
-        const int nt = n_q - t0 < 32 ? n_q - t0 : 32;
+    if constexpr (kBf16) {
+        // Lane (col, half) holds query slot col's q, du hi and du lo features kc*16 + half*8 .. +8:
+        // the A operands of S = Q K^T and dP = du V^T as loaded.  A padding slot reads a real row
+        // (the tile's first); its lse = +inf makes p = 0, so it adds nothing.  The next tile's rows
+        // are requested once this tile's products have read the registers.
+        const uint16_t *uhi = static_cast<const uint16_t *>(du_ws);
+        u32x4 aq[KC], ah[KC], al[KC];
+        float n_lse = INFINITY, n_delta = 0.0f;
+        auto fetch = [&](int t0) {
+            const int slot = t0 + col < n_q ? t0 + col : t0;
+            const int64_t r = (hN + ql[slot]) * D + half * 8;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int ch = lane + kWave * u, row = ch / CQ;
-            nq[u] = nh[u] = nl[u] = u32x4{0u, 0u, 0u, 0u};
-            if (row < nt) {
-                const int64_t at = (hN + ql[t0 + row]) * D;
-                if constexpr (kBf16) {
-                    const uint16_t *uhi = static_cast<const uint16_t *>(du_ws);
-                    const int c8 = (ch % CQ) * 8;
-                    nq[u] = *reinterpret_cast<const u32x4 *>(q + at + c8);
-                    nh[u] = *reinterpret_cast<const u32x4 *>(uhi + at + c8);
-                    nl[u] = *reinterpret_cast<const u32x4 *>(uhi + plane + at + c8);
-                } else {
-                    const int c4 = (ch % CQ) * 4;
-                    nq[u] = *reinterpret_cast<const u32x4 *>(q + at + c4);
-                    nh[u] = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(du_ws) + at + c4);
-                }
+            for (int kc = 0; kc < KC; ++kc) {
+                aq[kc] = *reinterpret_cast<const u32x4 *>(q + r + kc * 16);
+                ah[kc] = *reinterpret_cast<const u32x4 *>(uhi + r + kc * 16);
+                al[kc] = *reinterpret_cast<const u32x4 *>(uhi + plane + r + kc * 16);
             }
-        }
-        n_lse = INFINITY; // p = 0 for the padding rows
-        n_delta = 0.0f;
-        if (lane < nt) {
-            n_lse = lse_ws[hN + ql[t0 + lane]];
-            n_delta = delta_ws[hN + ql[t0 + lane]];
-        }
-    };
-    if (kBf16 && n_q > 0)
-        fetch(0);
-    for (int t0 = 0; t0 < n_q; t0 += 32) {
-        if constexpr (!kBf16)
-            fetch(t0); // fp32 rows are four times the registers: no fetch ahead
-        // ---- the fetched rows into this wave's staging area ----
+            n_lse = INFINITY;
+            n_delta = 0.0f;
+            if (lane < 32 && t0 + lane < n_q) {
+                n_lse = lse_ws[hN + ql[t0 + lane]];
+                n_delta = delta_ws[hN + ql[t0 + lane]];
+            }
+        };
+        // the pair words of this lane's 8 features: adjacent lanes (rows 2m, 2m + 1) swap two words;
+        // the even lane then holds features +0..3 of both rows, the odd lane +4..7
+        const bool odd = col & 1;
+        auto put_pairs = [&](uint32_t (*tile)[KeySmem<uint16_t, D>::kStride], const u32x4 &w, int kc) {
+            const uint32_t s0 = odd ? w[0] : w[2], s1 = odd ? w[1] : w[3];
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0xB1, 0xf, 0xf, true);
+            const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0xB1, 0xf, 0xf, true);
+            const uint32_t o0 = odd ? w[2] : w[0], o1 = odd ? w[3] : w[1]; // own words kept
+            const uint32_t lo0 = odd ? r0 : o0, hi0 = odd ? o0 : r0;       // row 2m in the low half
+            const uint32_t lo1 = odd ? r1 : o1, hi1 = odd ? o1 : r1;
+            const u32x4 pw = u32x4{(lo0 & 0xffffu) | (hi0 << 16), (lo0 >> 16) | (hi0 & 0xffff0000u),
+                                   (lo1 & 0xffffu) | (hi1 << 16), (lo1 >> 16) | (hi1 & 0xffff0000u)};
+            *reinterpret_cast<u32x4 *>(&tile[col >> 1][kc * 16 + half * 8 + (odd ? 4 : 0)]) = pw;
+        };
+        auto pairs8 = [&](const uint32_t (*tile)[KeySmem<uint16_t, D>::kStride], int kk, int f) {
+            const int m0 = 8 * kk + 2 * half; // rows acc_row(8kk + e, half): pairs m0, m0+1, m0+4, m0+5
+            return as_bf16x8(u32x4{tile[m0][f], tile[m0 + 1][f], tile[m0 + 4][f], tile[m0 + 5][f]});
+        };
+        if (n_q > 0)
+            fetch(0);
+        for (int t0 = 0; t0 < n_q; t0 += 32) {
+            if (lane < 32) {
+                lse_s[wave][lane] = n_lse;
+                delta_s[wave][lane] = n_delta;
+            }
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int ch = lane + kWave * u, row = ch / CQ;
-            if constexpr (kBf16) {
-                const int c8 = (ch % CQ) * 8;
-                *reinterpret_cast<u32x4 *>(&sm.qr[wave][row][c8]) = nq[u];
-                *reinterpret_cast<u32x4 *>(&sm.uh[wave][row][c8]) = nh[u];
-                *reinterpret_cast<u32x4 *>(&sm.ul[wave][row][c8]) = nl[u];
-            } else {
-                const int c4 = (ch % CQ) * 4;
+            for (int kc = 0; kc < KC; ++kc) {
+                put_pairs(sm.pq[wave], aq[kc], kc);
+                put_pairs(sm.ph[wave], ah[kc], kc);
+                put_pairs(sm.pl[wave], al[kc], kc);
+            }
+            // ---- S = Q K^T and dP = du V^T: [query][token], lane col = token ----
+            f32x16 sacc, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sacc[r] = dp[r] = 0.0f;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                sacc = mfma_bf16(as_bf16x8(aq[kc]), kf[kc], sacc);
+                dp = mfma_bf16(as_bf16x8(al[kc]), vf[kc], dp);
+                dp = mfma_bf16(as_bf16x8(ah[kc]), vf[kc], dp);
+            }
+            if (t0 + 32 < n_q)
+                fetch(t0 + 32);
+            wave_sync_lds(); // pair tiles, lse and Delta visible to the whole wave
+            float p[16], ds[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) { // rows 8g + 4 half + 0..3: one 16-byte read each
+                const float4 l4 = *reinterpret_cast<const float4 *>(&lse_s[wave][8 * g + 4 * half]);
+                const float4 d4 = *reinterpret_cast<const float4 *>(&delta_s[wave][8 * g + 4 * half]);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sm.qr[wave][row][c4 + e] = __uint_as_float(nq[u][e]);
-                    sm.du[wave][row][c4 + e] = __uint_as_float(nh[u][e]);
+                    const int r = 4 * g + e;
+                    p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lv[e]));
+                    ds[r] = p[r] * (dp[r] - dv4[e]);
                 }
             }
-        }
-        if (lane < 32) {
-            lse_s[wave][lane] = n_lse;
-            delta_s[wave][lane] = n_delta;
-        }
-        wave_sync_lds();
-        if (kBf16 && t0 + 32 < n_q)
-            fetch(t0 + 32);
-
-        // ---- S = Q K^T and dP = du V^T: [query][token], lane col = token ----
-        f32x16 sacc, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            sacc[r] = dp[r] = 0.0f;
-        if constexpr (kBf16) {
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const int f0 = kc * 16 + half * 8;
-                sacc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.qr[wave][col][f0])), kf[kc], sacc);
-                dp = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.ul[wave][col][f0])), vf[kc], dp);
-                dp = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.uh[wave][col][f0])), vf[kc], dp);
-            }
-        } else {
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                sacc = mfma_f32(sm.qr[wave][col][kc * 2 + half], kf[kc], sacc);
-                dp = mfma_f32(sm.du[wave][col][kc * 2 + half], vf[kc], dp);
-            }
-        }
-        float p[16], ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qs = acc_row(r, half);
-            p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse_s[wave][qs]));
-            ds[r] = p[r] * (dp[r] - delta_s[wave][qs]);
-        }
-
-        // ---- dV += P^T du and dK += dS^T Q: [token][feature], contraction over the tile's queries ----
-        if constexpr (kBf16) {
-            // B operands: 8 queries of one feature (the rows the lane's p and dS belong to)
-            auto gather8 = [&](const uint16_t (*rows)[KeySmem<uint16_t, D>::kStride], int kk, int f) {
-                u32x4 w;
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    w[x] = (uint32_t)rows[acc_row(8 * kk + 2 * x, half)][f] |
-                           ((uint32_t)rows[acc_row(8 * kk + 2 * x + 1, half)][f] << 16);
-                return as_bf16x8(w);
-            };
+            // ---- dV += P^T du and dK += dS^T Q: [token][feature], contraction over the tile's queries ----
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 ph, pl, sh, sl;
@@ -902,8 +902,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const int f = dt * 32 + col;
-                    const bf16x8 uhb = gather8(sm.uh[wave], kk, f), ulb = gather8(sm.ul[wave], kk, f);
-                    const bf16x8 qb = gather8(sm.qr[wave], kk, f);
+                    const bf16x8 uhb = pairs8(sm.ph[wave], kk, f), ulb = pairs8(sm.pl[wave], kk, f);
+                    const bf16x8 qb = pairs8(sm.pq[wave], kk, f);
                     dv_acc[dt] = mfma_bf16(pl, uhb, dv_acc[dt]);
                     dv_acc[dt] = mfma_bf16(ph, ulb, dv_acc[dt]);
                     dv_acc[dt] = mfma_bf16(ph, uhb, dv_acc[dt]);
@@ -911,7 +911,51 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
                     dk_acc[dt] = mfma_bf16(sh, qb, dk_acc[dt]);
                 }
             }
-        } else {
+            wave_sync_lds(); // the pair tiles are read: the next tile may overwrite them
+        }
+    } else {
+        // fp32: rows staged in LDS, fetched when needed
+        constexpr int CQ = D / 4; // 16-byte chunks per row
+        constexpr int PER = 32 * CQ / kWave;
+        for (int t0 = 0; t0 < n_q; t0 += 32) {
+            const int nt = n_q - t0 < 32 ? n_q - t0 : 32;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int ch = lane + kWave * u, row = ch / CQ, c4 = (ch % CQ) * 4;
+                u32x4 wq = u32x4{0u, 0u, 0u, 0u}, wu = wq;
+                if (row < nt) {
+                    const int64_t at = (hN + ql[t0 + row]) * D + c4;
+                    wq = *reinterpret_cast<const u32x4 *>(q + at);
+                    wu = *reinterpret_cast<const u32x4 *>(static_cast<const float *>(du_ws) + at);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sm.qr[wave][row][c4 + e] = __uint_as_float(wq[e]);
+                    sm.du[wave][row][c4 + e] = __uint_as_float(wu[e]);
+                }
+            }
+            if (lane < 32) {
+                const bool ok = lane < nt;
+                lse_s[wave][lane] = ok ? lse_ws[hN + ql[t0 + lane]] : INFINITY; // p = 0 for padding rows
+                delta_s[wave][lane] = ok ? delta_ws[hN + ql[t0 + lane]] : 0.0f;
+            }
+            wave_sync_lds();
+            f32x16 sacc, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sacc[r] = dp[r] = 0.0f;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                sacc = mfma_f32(sm.qr[wave][col][kc * 2 + half], kf[kc], sacc);
+                dp = mfma_f32(sm.du[wave][col][kc * 2 + half], vf[kc], dp);
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qs = acc_row(r, half);
+                p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse_s[wave][qs]));
+                ds[r] = p[r] * (dp[r] - delta_s[wave][qs]);
+            }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -920,8 +964,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 && D == 64 ? 2 : 1) void b
                     dv_acc[dt] = mfma_f32(p[r], sm.du[wave][qs][dt * 32 + col], dv_acc[dt]);
                     dk_acc[dt] = mfma_f32(ds[r], sm.qr[wave][qs][dt * 32 + col], dk_acc[dt]);
                 }
+            wave_sync_lds(); // the staged rows are read: the next tile may overwrite them
         }
-        wave_sync_lds(); // the staged rows are read: the next tile may overwrite them
     }
 
     // ---- out: lane (col, half) holds features dt*32 + col of tokens acc_row(r, half) ----
@@ -1064,7 +1108,8 @@ hipError_t launch_typed(const Geometry &g, const BwdBuffers &w, const void *q, c
                            w.item_cell, w.multi_cell, g.M, g.NB, g.B / g.s, z.items_max, z.multi_max);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
-        hipLaunchKernelGGL((bwd_key_kernel<T, D>), dim3((unsigned)(((z.items_max + 3) / 4) * g.bh)), dim3(kThreads), 0,
+        hipLaunchKernelGGL((bwd_key_kernel<T, D>), dim3((unsigned)(((z.items_max + kKeyWaves - 1) / kKeyWaves) * g.bh)),
+                           dim3(kKeyWaves * kWave), 0,
                            st, static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), w.du,
                            w.lse, w.delta, masks, w.item_start, w.pstart, w.item_cell, w.partial, dk, dv, g.N, g.M,
                            g.NB, g.B / g.s, z.items_max, z.p_max, (int64_t)g.bh * g.N * g.d);
