@@ -1020,14 +1020,27 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict
     const int n = is[c + 1] - is[c];
     const float *p0 = partial + (head * p_max + pstart[head * (M + 1) + c]) * 2 * (32 * D);
     float *dkc = dk + (head * N + c * s) * D, *dvc = dv + (head * N + c * s) * D;
-    for (int e = threadIdx.x; e < 32 * D; e += blockDim.x) {
-        float tk = 0.0f, tv = 0.0f;
-        for (int x = 0; x < n; ++x) {
-            tk += p0[(int64_t)x * 2 * 32 * D + e];
-            tv += p0[(int64_t)x * 2 * 32 * D + 32 * D + e];
+    // thread: four consecutive floats of dk and of dv; the chunks' loads four at a time, added in chunk order
+    const int64_t stride = 2 * 32 * D;
+    for (int e = threadIdx.x * 4; e < 32 * D; e += blockDim.x * 4) {
+        float4 tk = make_float4(0.0f, 0.0f, 0.0f, 0.0f), tv = tk;
+        for (int x0 = 0; x0 < n; x0 += 4) {
+            float4 a[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (x0 + u < n) {
+                    a[u] = *reinterpret_cast<const float4 *>(p0 + (x0 + u) * stride + e);
+                    b[u] = *reinterpret_cast<const float4 *>(p0 + (x0 + u) * stride + 32 * D + e);
+                }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (x0 + u < n) {
+                    tk.x += a[u].x; tk.y += a[u].y; tk.z += a[u].z; tk.w += a[u].w;
+                    tv.x += b[u].x; tv.y += b[u].y; tv.z += b[u].z; tv.w += b[u].w;
+                }
         }
-        dkc[e] = tk;
-        dvc[e] = tv;
+        *reinterpret_cast<float4 *>(dkc + e) = tk;
+        *reinterpret_cast<float4 *>(dvc + e) = tv;
     }
 }
 
