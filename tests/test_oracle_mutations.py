@@ -109,8 +109,8 @@ FSB_MUTATIONS = [
      "        if (cells[x] > mn)\n            mn = cells[x];"),
     ("priority without the radius term", "const double spread = fb->c * q_norm(q, d) * F->rho[v];",
      "const double spread = 0.0;"),
-    ("priority prior at the node's end", "const double g = erf(((double)i - F->pmin[v]) / (2.0 * cfg->sigma)); /* g_h(i - p_v^min) */",
-     "const double g = erf(((double)i - F->pmin[v] - 64.0 * F->count[v]) / (2.0 * cfg->sigma)); /* g_h(i - p_v^min) */"),
+    ("priority prior taken two cells late", "const double g = erf(((double)i - F->pmin[v]) / (2.0 * cfg->sigma)); /* g_h(i - p_v^min) */",
+     "const double g = erf(((double)i - F->pmin[v] - 2.0 * cfg->s) / (2.0 * cfg->sigma)); /* g_h(i - p_v^min) */"),
     ("leaves compete for their slots", "                leaves[n_leaf++] = beam[x]; /* a leaf keeps its slot */",
      "                kids[n_kid++] = beam[x];"),
     ("second forest admits above the threshold only", "if (a[c] >= fb->tau)", "if (a[c] > fb->tau)"),
