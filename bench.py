@@ -39,6 +39,8 @@ DECODE_METRIC = "long-range FS-L decode query-tokens/s at a 262,144-token contex
 LOCAL_METRIC = "local RoPE window branch + branch combination query-tokens/s at 16k prefill (w=512); % HBM roofline"
 LOCAL_DECODE_METRIC = ("local RoPE window branch + branch combination decode query-tokens/s at a 262,144-token "
                        "context (w=512); % HBM roofline")
+ATTN_DECODE_METRIC = ("attention decode (long-range FS-L + local w=512 + branch combination, one launch) "
+                      "query-tokens/s at a 262,144-token context; % HBM roofline")
 LOCAL_W = 512
 WORKLOADS = {
     "prefill_16k": dict(prune=True),
@@ -53,6 +55,7 @@ WORKLOADS = {
     "fsb_16k": dict(fsb=True),
     "chunk_256k": dict(prune=True, chunk=True),
     "train_4k_bwd": dict(prune=True, backward=True),
+    "attn_decode_256k": dict(prune=True, attn_decode=True),
 }
 DECODE_PREFIX = 262144
 DECODE_LAYER_STATES = 12  # independent states in rotation: 12 x ~26 MB per step exceeds the 256 MB MALL
@@ -198,6 +201,8 @@ def main() -> int:
         return run_decode(args)
     if WORKLOADS[args.workload].get("local_decode"):
         return run_local_decode(args)
+    if WORKLOADS[args.workload].get("attn_decode"):
+        return run_attn_decode(args)
     if WORKLOADS[args.workload].get("local"):
         return run_local(args)
     if WORKLOADS[args.workload].get("fsb"):
@@ -1301,6 +1306,218 @@ def run_local_decode(args) -> int:
         "roofline": roofline, "cpu_baseline": cpu, "us_per_step_and_state": round(per_launch_ms * 1e3, 3),
         "wall_ms": round(wall * 1e3, 3), "settle_replays": settle, "state_build_ms": round(build_ms, 3),
         "state_bytes": int(snap.numel()), "layer_states_agree": same_states, "parity_spot_check": parity,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_attn_decode(args) -> int:
+    """The whole attention decode step in one launch per layer (fs_attention_decode:
+    the long-range step, the local step with w = 512, Eq. 2): b32 H8 d128 bf16
+    sequences with a 262,144-token prefix.  The long-range state comes from a
+    state-only prefill of the prefix, the local state from its last 512 tokens.
+    The timed region replays, as one HIP graph, `steps` token steps over
+    DECODE_LAYER_STATES independent pairs of states (as the layers of a model
+    would); the same steps as two separate launches (fs_longrange_decode, then
+    fs_local_decode) are timed the same way for comparison, and their outputs must
+    match the fused call's bit for bit.  Throughput counts one query-token per
+    sequence, step and layer."""
+    import numpy as np
+    import torch
+
+    import cell_routed_long_amd as fsl
+    import synth
+
+    w = synth.WORKLOADS["decode_256k"]
+    prm = fsl.Params()
+    sigma, lam = 4.0, 1.0
+    dev = torch.device("cuda:0")
+    b, H, d, N0 = w.batch, w.H, w.d, DECODE_PREFIX
+    steps = w.N - N0
+    R = DECODE_LAYER_STATES
+    stream = torch.cuda.current_stream()
+
+    t0 = time.time()
+    dk = torch.empty(b, H, N0, d, dtype=torch.bfloat16, device=dev)
+    dv = torch.empty_like(dk)
+    for bb in range(b):
+        for x, dst in (("k", dk), ("v", dv)):
+            a = synth.tensor(w, x, 0, N0, heads=[(bb, h) for h in range(H)])
+            dst[bb].copy_(torch.from_numpy(a.view(np.int16)).view(torch.bfloat16))
+        if bb % 8 == 7:
+            log(f"[bench] prefix generated for {bb + 1}/{b} sequences ({time.time() - t0:.0f}s)")
+    steps_in = {x: torch.from_numpy(np.ascontiguousarray(np.moveaxis(synth.tensor(w, x, N0, w.N), 2, 0))
+                                    .view(np.int16)).view(torch.bfloat16).to(dev) for x in "qkv"}
+    snap = fsl.new_state(b, H, d, torch.bfloat16, prm)
+    _, _, ws = fsl.prefill(None, dk, dv, prm, sigma=sigma, lam=lam, want_out=False, want_sel=False, state=snap)
+    lsnap = fsl.new_local_state(b, H, d, torch.bfloat16, w=LOCAL_W)
+    lsnap.zero_()
+    fsl.fs_local_state_build(lsnap, dk[:, :, N0 - LOCAL_W:].contiguous(), dv[:, :, N0 - LOCAL_W:].contiguous(),
+                             pos=N0, w=LOCAL_W)
+    torch.cuda.synchronize()
+    del ws, dk, dv
+    torch.cuda.empty_cache()
+    log(f"[bench] states ready in {time.time() - t0:.0f}s")
+    alpha = [0.25 + 0.05 * h for h in range(H)]  # alpha_h is learned; the page gives no values
+    states = [torch.empty_like(snap) for _ in range(R)]
+    lstates = [torch.empty_like(lsnap) for _ in range(R)]
+    outs = torch.empty(R, steps, b, H, d, dtype=torch.bfloat16, device=dev)
+    sels = torch.empty(R, steps, b, H, prm.K, dtype=torch.int32, device=dev)
+    outs2 = torch.empty_like(outs)
+    sels2 = torch.empty_like(sels)
+    o_lr = torch.empty(R, b, H, d, dtype=torch.bfloat16, device=dev)
+
+    def restore():
+        for st, lst in zip(states, lstates):
+            st.copy_(snap)
+            lst.copy_(lsnap)
+
+    def fused():
+        for t in range(steps):
+            q, k, v = steps_in["q"][t], steps_in["k"][t], steps_in["v"][t]
+            for r in range(R):
+                fsl.fs_attention_decode(states[r], lstates[r], q, k, v, outs[r, t], alpha, sel=sels[r, t],
+                                        params=prm, sigma=sigma, lam=lam, w=LOCAL_W)
+
+    def separate():
+        for t in range(steps):
+            q, k, v = steps_in["q"][t], steps_in["k"][t], steps_in["v"][t]
+            for r in range(R):
+                fsl.decode(states[r], q, k, v, prm, sigma=sigma, lam=lam, out=o_lr[r], sel=sels2[r, t])
+                fsl.fs_local_decode(lstates[r], q, k, v, outs2[r, t], w=LOCAL_W, alpha=alpha, o_lr=o_lr[r])
+
+    graphs = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        restore()
+        for _ in range(max(1, args.warmup)):
+            fn()
+            restore()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                fn()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graphs[name] = g
+
+    def timed(name):
+        restore()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graphs[name].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def replay_fused():
+        restore()
+        graphs["fused"].replay()
+
+    settle = settle_clocks(replay_fused)
+    sep_ms = timed("separate")
+    graph_ms = timed("fused")  # last, so that outs holds the fused results
+    per_launch_ms = graph_ms / (steps * R)
+    sep_us = sep_ms / (steps * R) * 1e3
+    matches = bool(torch.equal(outs.view(torch.int16), outs2.view(torch.int16)) and torch.equal(sels, sels2))
+    log(f"[bench] attention decode graph: {graph_ms:.3f} ms for {steps} steps x {R} states = "
+        f"{per_launch_ms * 1e3:.2f} us per step and layer (two launches: {sep_us:.2f} us); bitwise equal: {matches}")
+    out_h = outs[0].float().cpu().numpy()  # [steps, b, H, d]
+    sel_h = sels[0].cpu().numpy()
+
+    if args.copy_calibration:  # a 1 GiB copy whose bytes are known, for HBM counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- algorithmic bytes per launch (one step of every (sequence, head)) ----
+    n_sel = np.count_nonzero(sel_h >= 0, axis=-1)
+    n_ret = min(prm.P + prm.W, N0 // prm.s)
+    per_pair = (n_ret * (d * 4 + 4 + 4)             # long-range: mean keys, norms, slot ids of A
+                + 2 * d * 2 + 16                    # long-range: appended key/value row, position
+                + LOCAL_W * d * 2 * 2 + 2 * d * 2 + 16  # local: the ring's keys and values, appended row, position
+                + 3 * d * 2 + d * 2)                # q, k_new, v_new in (read by both), out
+    alg_bytes = (b * H * per_pair + float(n_sel.mean()) * b * H * prm.s * d * 2 * 2
+                 + (LOCAL_W + 1) * (d // 2) * 8)    # the rotation table, shared by every head
+    achieved = alg_bytes / (per_launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("attn_decode", "attn_decode_256k"), "kernel": "attn_decode",
+                "alg_bytes_per_launch": int(alg_bytes)}
+    value = b * steps * R / (graph_ms * 1e-3)
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from concurrent.futures import ThreadPoolExecutor
+        from tests import parity_utils as pu
+        threads = oracle_threads()
+        pairs = [(0, 0), (b - 1, H - 1)]
+        op = oracle.Params(s=prm.s, B=prm.B, P=prm.P, W=prm.W, K=prm.K, prune=True, sigma=sigma, lam=lam,
+                           eps=prm.eps)
+
+        def inputs(bh):
+            kk = synth.to_f64(synth.tensor(w, "k", heads=[bh], threads=1)[0], w.dtype)
+            vv = synth.to_f64(synth.tensor(w, "v", heads=[bh], threads=1)[0], w.dtype)
+            qq = np.zeros_like(kk)
+            qq[N0:] = synth.to_f64(synth.tensor(w, "q", N0, w.N, heads=[bh], threads=1)[0], w.dtype)
+            return bh, (qq, kk, vv)
+
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            data = dict(ex.map(inputs, pairs))
+
+        def one(bh):
+            # both branches of the oracle over the steps' positions; the local branch reads
+            # the 512 tokens before them (RoPE's relative form makes the frame irrelevant)
+            qq, kk, vv = data[bh]
+            lr = oracle.head(qq, kk, vv, None, op, i_lo=N0, i_hi=N0 + steps, want_summaries=False)
+            lo = N0 - LOCAL_W
+            full = oracle.local(qq[lo:], kk[lo:], vv[lo:], w=LOCAL_W, alpha=alpha[bh[1]], o_lr=lr["out"],
+                                i_lo=LOCAL_W, i_hi=LOCAL_W + steps)
+            return bh, (lr, full)
+
+        t1 = single_thread_seconds(one, pairs[0])
+        refs, passes, cpu_s = time_oracle(one, pairs, threads)
+        model, visible = host_cpu()
+        cpu = {"value": round(passes * len(pairs) / H * steps / cpu_s, 1), "unit": "query-tokens/s",
+               "cores": min(threads, len(pairs)), "kind": "oracle", "cpu_model": model, "host_cpus_visible": visible,
+               "single_thread_s_per_pair": round(t1, 3),
+               "sample": f"{len(pairs)} of {b * H} (sequence, head) pairs, both branches at all {steps} decode "
+                         f"positions each, from the raw 262,144-token prefix, {passes} passes; {cpu_s:.1f}s wall"}
+        worst, invalid = 0.0, []
+        for (bb, hh), (lr, full) in refs.items():
+            pu.attach(lr, data[(bb, hh)] + (None,), op)
+            lr["kbar"], lr["a"] = oracle.cell_summaries(data[(bb, hh)][1], op)
+            try:
+                lr_ref, _ = pu.lr_reference(sel_h[:, bb, hh], lr, prm, N0, f"attention decode b{bb} h{hh}")
+            except AssertionError as e:
+                invalid.append(str(e))
+                lr_ref = lr["out"]
+            qq, kk, vv = data[(bb, hh)]
+            lo = N0 - LOCAL_W
+            ref = oracle.local(qq[lo:], kk[lo:], vv[lo:], w=LOCAL_W, alpha=alpha[hh], o_lr=lr_ref, i_lo=LOCAL_W,
+                               i_hi=LOCAL_W + steps)
+            worst = max(worst, float(np.abs(out_h[:, bb, hh] - ref).max()))
+        parity = {"heads": len(pairs), "steps": steps, "near_ties_invalid": invalid, "max_abs_err": worst}
+        log(f"[bench] oracle {cpu_s:.1f}s on {threads} threads; parity {parity}")
+
+    result = {
+        "metric": ATTN_DECODE_METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(graph_ms / steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": "attention decode (long-range FS-L + local w=512 + Eq. 2) in one launch, b32 H8 "
+                               "d128 bf16 at positions 262,144 onward", "batch": b, "heads": H, "prefix": N0,
+                   "head_dim": d, "s": prm.s, "B": prm.B, "P": prm.P, "W": prm.W, "K": prm.K, "sigma_h": sigma,
+                   "lambda_h": lam, "w": LOCAL_W, "rope_base": 10000.0, "layer_states": R,
+                   "timing": "one HIP graph replay of steps x layer_states fused decode launches"},
+        "roofline": roofline, "cpu_baseline": cpu, "us_per_step_and_layer": round(per_launch_ms * 1e3, 3),
+        "us_per_step_and_layer_two_launches": round(sep_us, 3), "matches_two_launches_bitwise": matches,
+        "settle_replays": settle, "parity_spot_check": parity,
     }
     print(json.dumps(result), flush=True)
     return 0

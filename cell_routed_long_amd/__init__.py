@@ -115,11 +115,13 @@ def lib():
         L.fs_local_state_build.argtypes = [i32, i32, i32, ctypes.c_int, i64, ctypes.c_float, vp, sz, vp, vp, i64,
                                            i64, vp]
         L.fs_local_decode.argtypes = [i32, i32, i32, ctypes.c_int, i64, vp, sz, vp, vp, vp, vp, vp, vp, vp]
+        L.fs_attention_decode.argtypes = [P_prm, i32, i32, i32, ctypes.c_int, vp, sz, i64, vp, sz, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, vp]
         for name in ("fs_cell_summaries", "fs_prune_retained", "fs_score_select", "fs_readout", "fs_readout_backward",
                      "fs_select_readout", "fs_longrange_prefill", "fs_longrange_prefill_noalloc", "fs_fsb_prefill",
                      "fs_longrange_decode", "fs_decode_state_init", "fs_longrange_prefill_chunk",
                      "fs_local_window",
-                     "fs_local_state_build", "fs_local_decode"):
+                     "fs_local_state_build", "fs_local_decode", "fs_attention_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -442,6 +444,20 @@ def fs_local_decode(state, q, k_new, v_new, out, w: int = 512, alpha=None, o_lr=
     _check(lib().fs_local_decode(b, H, d, _dtype_code(q), int(w), _ptr(state), state.numel() * state.element_size(),
                                  _ptr(q), _ptr(k_new), _ptr(v_new), al, _ptr(o_lr), _ptr(out), _stream(stream)),
            "fs_local_decode")
+
+
+def fs_attention_decode(state, local_state, q, k_new, v_new, out, alpha, sel=None, params: Params = Params(),
+                        sigma=4.0, lam=1.0, gain=None, w: int = 512, stream=None):
+    """The whole attention decode step in one launch: out = o_sr + alpha_h * o_lr (Eq. 2)
+    from the long-range state and the local state (window w) for [batch, H, d] inputs."""
+    prm = params.c()
+    b, H, d = q.shape
+    sig, la, al = _floats(sigma, H), _floats(lam, H), _floats(alpha, H)
+    _check(lib().fs_attention_decode(ctypes.byref(prm), b, H, d, _dtype_code(q), _ptr(state),
+                                     state.numel() * state.element_size(), int(w), _ptr(local_state),
+                                     local_state.numel() * local_state.element_size(), _ptr(q), _ptr(k_new),
+                                     _ptr(v_new), sig, la, _ptr(gain), al, _ptr(out), _ptr(sel), _stream(stream)),
+           "fs_attention_decode")
 
 
 def new_local_state(batch: int, H: int, d: int, dtype, w: int = 512, device="cuda"):

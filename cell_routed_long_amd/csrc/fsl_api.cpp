@@ -818,6 +818,40 @@ FSL_EXPORT fs_status fs_local_decode(int32_t batch, int32_t H, int32_t d, fs_dty
                                           v_new, o_lr, out, static_cast<hipStream_t>(stream)));
 }
 
+FSL_EXPORT fs_status fs_attention_decode(const fs_params *prm, int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
+                                        void *state, size_t state_bytes, int64_t w, void *local_state,
+                                        size_t local_state_bytes, const void *q, const void *k_new, const void *v_new,
+                                        const float *sigma_h, const float *lambda_h, const float *gain,
+                                        const float *alpha_h, void *out, int32_t *sel, void *stream)
+{
+    fs_status st = check_local_dims(batch, H, d, dtype, w);
+    if (st != FS_OK)
+        return st;
+    st = check_decode_params(prm);
+    if (st != FS_OK)
+        return st;
+    HeadConsts hc;
+    st = check_heads(H, sigma_h, lambda_h, &hc);
+    if (st != FS_OK)
+        return st;
+    if (!state || !local_state || !q || !k_new || !v_new || !out || !alpha_h)
+        return FS_ERR_INVALID;
+    LocalConsts lc;
+    std::memset(&lc, 0, sizeof(lc));
+    st = local_alpha(H, alpha_h, out, &lc); // out stands for o_lr: alpha is required
+    if (st != FS_OK)
+        return st;
+    const StateLayout L = state_layout(d, dtype, prm);
+    const LocalStateLayout LL = local_layout(d, dtype, w);
+    if (state_bytes != state_bytes_of(batch, H, L) || local_state_bytes != local_state_bytes_of(batch, H, LL))
+        return FS_ERR_STATE;
+    const StateHeader expect = state_header(batch, H, d, dtype, prm, L);
+    const LocalStateHeader lexpect = local_header(batch, H, d, dtype, w, 0.0f, LL);
+    return hip_status(launch_attn_decode(batch * H, H, d, dtype == FS_BF16 ? 1 : 0, prm->K, prm->P, prm->W, prm->eps,
+                                         L, expect, hc, state, LL, lexpect, lc, local_state, q, k_new, v_new, gain,
+                                         out, sel, static_cast<hipStream_t>(stream)));
+}
+
 FSL_EXPORT size_t fs_fsb_workspace_bytes(const fs_shape *shape, const fs_params *prm, const fs_fsb_params *fb)
 {
     if (check_fsb(shape, prm, fb) != FS_OK)

@@ -127,6 +127,15 @@ hipError_t launch_local_decode(int32_t bh, int32_t H, int32_t d, int32_t bf16, c
                                const LocalStateHeader &expect, const LocalConsts &lc, void *state, const void *q,
                                const void *k_new, const void *v_new, const void *o_lr, void *out, hipStream_t st);
 
+// The whole attention decode step in one launch: the long-range step on `state`
+// and the local step on `lstate` (out = o_sr + alpha_h o_lr), bitwise
+// launch_decode_step followed by launch_local_decode with its output as o_lr.
+hipError_t launch_attn_decode(int32_t bh, int32_t H, int32_t d, int32_t bf16, int32_t K, int32_t P, int32_t W,
+                              float eps, const StateLayout &L, const StateHeader &expect, const HeadConsts &hc,
+                              void *state, const LocalStateLayout &LL, const LocalStateHeader &lexpect,
+                              const LocalConsts &lc, void *lstate, const void *q, const void *k_new,
+                              const void *v_new, const float *gain, void *out, int32_t *sel, hipStream_t st);
+
 // ---- FS-B (Sec. 3.4; App. E.1): two causal forests, beam search, token rerank ----
 constexpr int kFsbMaxBeam = 16;          // W^b
 constexpr int64_t kFsbMaxCells = 4096;   // admitted cells per forest (N <= 131,072 at s = 32)

@@ -1,78 +1,15 @@
 // Streaming decode of the local branch (FreeSolo, Sec. 3.2, Eqs. 3-4; the
-// window moves one token per step) with the branch combination of Eq. 2.
-//
-// A step for the token at position i reads the window [max(0, i - w), i]: the
-// step's own k_new, v_new (offset o = 0) and the ring's w slots, which hold
-// the tokens i - w .. i - 1 (offsets w .. 1; those before position 0 are
-// masked).  Logits take the relative form of Eq. 3, q_i . R(-o) k_{i-o} =
-// (R(o) q_i) . k_{i-o}, with R(o) turning feature pair m by o theta_m; the ring
-// holds raw keys, so no angle grows with the position.
-//
-// One workgroup of 512 threads per (sequence, head).  Sixteen lanes share a
-// row (a ring slot) and hold d/16 of its features, so a row is one coalesced
-// read per array; a group of 16 lanes owns kRows consecutive slots per pass,
-// and a pass of the 32 groups covers 32 kRows slots (the whole w = 512 ring
-// for bf16, every load of it in flight together).  The loads go by slot, so
-// they do not wait for the position; the offsets follow once it arrives.
-// Along a group's slots the offset falls by one per slot, with one jump from 1
-// to w where the ring wraps: the group turns the query once with the (cos,
-// sin) table entry of its first offset (built in fp64 with the state), then by
-// -theta_m per slot, and takes R(w) q at the wrap.  Every group runs an online
-// softmax over its rows; the groups meet in LDS, where 512 / d adjacent lanes
-// finish each feature.  The new token then replaces the oldest one, in slot
-// i mod w, after every read of the ring.
-#include "fsl_internal.h"
+// window moves one token per step) with the branch combination of Eq. 2: the
+// state (a rotation table shared by every head and a ring of the last w raw
+// keys and values per (sequence, head)), its construction, and the step
+// kernel.  The step's arithmetic lives in decode_local.h, which the fused
+// attention decode kernel shares.
+#include "decode_local.h"
 
 namespace fsl {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kLanesPerRow = 16;
-constexpr int kGroups = kThreads / kLanesPerRow; // 32 groups of 16 lanes
-
-template <typename T>
-__device__ __forceinline__ float to_f32(T x);
-template <>
-__device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_bits_to_f32(x); }
-template <>
-__device__ __forceinline__ float to_f32<float>(float x) { return x; }
-
-template <typename T>
-__device__ __forceinline__ T from_f32(float x);
-template <>
-__device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return (uint16_t)f32_to_bf16_bits(x); }
-template <>
-__device__ __forceinline__ float from_f32<float>(float x) { return x; }
-
-// NDW consecutive dwords (NDW = 2, 4 or 8; 8-byte aligned, 16-byte for NDW >= 4).
-template <int NDW>
-__device__ __forceinline__ void load_dwords(const char *p, uint32_t (&r)[NDW])
-{
-    if constexpr (NDW == 2) {
-        const u32x2 a = *reinterpret_cast<const u32x2 *>(p);
-        r[0] = a.x;
-        r[1] = a.y;
-    } else {
-#pragma unroll
-        for (int c = 0; c < NDW / 4; ++c) {
-            const u32x4 a = reinterpret_cast<const u32x4 *>(p)[c];
-            r[4 * c] = a.x;
-            r[4 * c + 1] = a.y;
-            r[4 * c + 2] = a.z;
-            r[4 * c + 3] = a.w;
-        }
-    }
-}
-
-// Feature e of a lane's features held as raw dwords.
-template <typename T, int NDW>
-__device__ __forceinline__ float feature(const uint32_t (&r)[NDW], int e)
-{
-    if constexpr (sizeof(T) == 2)
-        return bf16_bits_to_f32((e & 1) ? (r[e >> 1] >> 16) : (r[e >> 1] & 0xffffu));
-    else
-        return __uint_as_float(r[e]);
-}
+using ldec::kThreads;
 
 // ---- rotation table: (cos, sin) of o * theta_m, theta_m = base^(-2m/d) ----
 __global__ __launch_bounds__(256) void local_table_kernel(float2 *__restrict__ table, int64_t R, int NP, int d,
@@ -114,17 +51,7 @@ __global__ __launch_bounds__(256) void local_state_build_kernel(char *__restrict
     }
 }
 
-// Sum over the 16 lanes of a DPP row, in every lane of the row.
-__device__ __forceinline__ float row16_sum(float x)
-{
-    x += dpp_f<0xB1>(x);  // quad_perm [1,0,3,2]
-    x += dpp_f<0x4E>(x);  // quad_perm [2,3,0,1]
-    x += dpp_f<0x141>(x); // row_half_mirror
-    x += dpp_f<0x140>(x); // row_mirror
-    return x;
-}
-
-// ---- one step ----
+// ---- one step: one workgroup of 512 threads per (sequence, head) ----
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict__ state, LocalStateLayout L,
                                                                 LocalStateHeader expect, LocalConsts lc,
@@ -134,258 +61,19 @@ __global__ __launch_bounds__(kThreads) void local_decode_kernel(char *__restrict
                                                                 const T *__restrict__ o_lr, T *__restrict__ out,
                                                                 int H)
 {
-    constexpr int FPL = D / kLanesPerRow;         // features per lane
-    constexpr int NPL = FPL / 2;                  // feature pairs per lane
-    constexpr int NDW = FPL * (int)sizeof(T) / 4; // dwords of a lane's key (or value) features
-    constexpr int NP = D / 2;
-    constexpr int kRows = 32 / (int)sizeof(T);    // slots per group and pass (16 bf16, 8 fp32)
-    constexpr int kPass = kGroups * kRows;        // slots per pass
-    static_assert(FPL % 2 == 0, "whole feature pairs per lane");
-
-    constexpr int TPF = kThreads / D;  // lanes per feature in the final combination: 4 (d = 128) or 8
-    constexpr int GPT = kGroups / TPF; // groups each of them combines
-    __shared__ float s_m[kGroups], s_l[kGroups];
-    __shared__ float s_acc[kGroups][D + 1];
-
+    using S = ldec::Shape<T, D>;
+    __shared__ ldec::Smem<D> sm;
     const int64_t bh = blockIdx.x;
-    const int h = (int)(bh % H);
     const int t = threadIdx.x;
-    const int grp = t / kLanesPerRow, part = t % kLanesPerRow;
-    const int64_t w = L.w;
-    char *rec = state + L.off_rec + bh * L.rec_bytes; // in bounds: the host checked the buffer size
-    const int64_t lane_off = part * FPL * (int64_t)sizeof(T);
-    const char *kring = rec + L.off_k + lane_off;
-    const char *vring = rec + L.off_v + lane_off;
-    const char *tab = state + L.off_table + part * NPL * (int64_t)sizeof(float2);
-    // log2(e) / sqrt(d): the softmax works in the exp2 domain with the hardware exp2 (one
-    // instruction; results below 2^-126 flush to 0, far below any weight that counts next
-    // to the largest, which is 1)
-    const float scale = 1.4426950408889634f / sqrtf((float)D);
-
-    // Nothing waits for memory before a pass's ring rows are requested, and
-    // nothing branches on the header: every address here lies inside the buffer
-    // whatever the header holds, and a foreign header only changes what is
-    // written at the end.
-    const LocalStateHeader hv = *reinterpret_cast<const LocalStateHeader *>(state);
-    const int64_t i = *reinterpret_cast<const int64_t *>(rec);
-    uint32_t qr[NDW], kr0[NDW], vr0[NDW], stp[FPL], cw[FPL];
-    load_dwords<NDW>(reinterpret_cast<const char *>(q + bh * D) + lane_off, qr);
-    load_dwords<NDW>(reinterpret_cast<const char *>(k_new + bh * D) + lane_off, kr0);
-    load_dwords<NDW>(reinterpret_cast<const char *>(v_new + bh * D) + lane_off, vr0);
-    load_dwords<FPL>(tab + (w > 0 ? 1 : 0) * NP * (int64_t)sizeof(float2), stp); // (cos, sin) of theta_m
-    load_dwords<FPL>(tab + w * NP * (int64_t)sizeof(float2), cw);                // of w theta_m
-    // what the epilogue writes or adds for feature te: requested now, not after the
+    const int te = t / S::TPF; // the feature this thread finishes
+    const ldec::Entry<T, D> e = ldec::step_entry<T, D>(state, L, q, k_new, v_new, bh, t % ldec::kLanesPerRow, te);
+    // what the combination adds for feature te: requested now, not after the
     // softmax, and without a branch (a load under a branch is waited for at its end)
-    const int te = t / TPF; // the feature this thread finishes
     const T *olr_src = o_lr ? o_lr : q; // q stands in when there is no o_lr (then unused)
     const T olr_t = olr_src[bh * D + te];
-    const T kn_t = k_new[bh * D + te], vn_t = v_new[bh * D + te];
-
-    // slot of token i - 1 (offset 1); slots of offsets above min(i, w) hold no token yet.
-    // Slots and offsets fit in 32 bits: w <= 65535.
-    const int wi = (int)w;
-    const int64_t i_nn = i > 0 ? i : 0;
-    const int last = (int)((i_nn + w - 1) % L.slots);
-    const int n_valid = (int)(i_nn < w ? i_nn : w);
-    // offset of slot s: last - s + 1, or that plus w past the wrap (always in 1 .. w)
-    auto offset_of = [&](int sl) { return sl <= last ? last - sl + 1 : last - sl + 1 + wi; };
-    constexpr int kHalf = kRows / 2; // rows per softmax update
-
-    // A group adds up to w / 32 rows one after another; a running fp32 sum of n terms
-    // can lose about n * 2^-24 of its value, 1e-4 at the largest window.  Each run of
-    // kRunPasses passes is therefore summed on its own and then added into a second
-    // total (acc_t, l_t): the loss stays near (rows per run + runs) * 2^-24.  Windows
-    // of up to kRunPasses passes never close a run.
-    constexpr int kRunPasses = 8;
-    float m = -INFINITY, l = 0.0f, acc[FPL], l_t = 0.0f, acc_t[FPL];
-#pragma unroll
-    for (int e = 0; e < FPL; ++e) {
-        acc[e] = 0.0f;
-        acc_t[e] = 0.0f;
-    }
-
-    for (int base = 0; base < wi; base += kPass) {
-        // the pass's rows and the angle of the group's first offset are requested
-        // before anything waits for memory
-        const int s0 = base + grp * kRows; // the group's first slot in this pass
-        uint32_t kr[kRows][NDW], vr[kRows][NDW], c0[FPL];
-        // (loads complete in issue order: the angle goes between the two halves, so
-        // the first half's rows can be used while the second half arrives)
-#pragma unroll
-        for (int u = 0; u < kRows; ++u) {
-            if (u == kRows / 2)
-                load_dwords<FPL>(tab + (int64_t)offset_of(s0 < wi ? s0 : 0) * NP * (int64_t)sizeof(float2), c0);
-            const int sc = s0 + u < wi ? s0 + u : 0; // slots past the ring read slot 0 (in bounds, unused)
-            load_dwords<NDW>(kring + (int64_t)sc * D * (int64_t)sizeof(T), kr[u]);
-            load_dwords<NDW>(vring + (int64_t)sc * D * (int64_t)sizeof(T), vr[u]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // q and the angle w theta_m are loop-invariant; these empty asm statements
-        // keep their use (and the wait for them) here, behind the pass's loads,
-        // instead of hoisted in front of the loop
-        uint32_t qv[NDW], cwv[FPL];
-#pragma unroll
-        for (int e = 0; e < NDW; ++e) {
-            qv[e] = qr[e];
-            asm volatile("" : "+v"(qv[e]));
-        }
-#pragma unroll
-        for (int e = 0; e < FPL; ++e) {
-            cwv[e] = cw[e];
-            asm volatile("" : "+v"(cwv[e]));
-        }
-
-        // R(o0) q for the first offset; R(w) q, taken where the slots wrap from offset 1 to w
-        float qx[NPL], qy[NPL], wx[NPL], wy[NPL];
-#pragma unroll
-        for (int p = 0; p < NPL; ++p) {
-            const float q0 = feature<T, NDW>(qv, 2 * p), q1 = feature<T, NDW>(qv, 2 * p + 1);
-            const float c = __uint_as_float(c0[2 * p]), sn = __uint_as_float(c0[2 * p + 1]);
-            qx[p] = fmaf(q0, c, -q1 * sn);
-            qy[p] = fmaf(q0, sn, q1 * c);
-            const float cwc = __uint_as_float(cwv[2 * p]), cws = __uint_as_float(cwv[2 * p + 1]);
-            wx[p] = fmaf(q0, cwc, -q1 * cws);
-            wy[p] = fmaf(q0, cws, q1 * cwc);
-        }
-#pragma unroll
-        for (int hh = 0; hh < kRows; hh += kHalf) {
-            float x[kHalf];
-            float mx = m;
-#pragma unroll
-            for (int uu = 0; uu < kHalf; ++uu) {
-                const int u = hh + uu;
-                const int s = s0 + u;
-                if (u > 0) { // offset of slot s: one less than slot s - 1's, or w at the wrap
-                    const bool wrap = s == last + 1;
-#pragma unroll
-                    for (int p = 0; p < NPL; ++p) {
-                        const float c = __uint_as_float(stp[2 * p]), sn = __uint_as_float(stp[2 * p + 1]);
-                        const float nx = fmaf(qx[p], c, qy[p] * sn); // R(-1)
-                        const float ny = fmaf(-qx[p], sn, qy[p] * c);
-                        qx[p] = wrap ? wx[p] : nx;
-                        qy[p] = wrap ? wy[p] : ny;
-                    }
-                }
-                float dot = 0.0f;
-#pragma unroll
-                for (int p = 0; p < NPL; ++p) {
-                    dot = fmaf(qx[p], feature<T, NDW>(kr[u], 2 * p), dot);
-                    dot = fmaf(qy[p], feature<T, NDW>(kr[u], 2 * p + 1), dot);
-                }
-                dot = row16_sum(dot);
-                x[uu] = (s < wi && offset_of(s) <= n_valid) ? dot * scale : -INFINITY;
-                mx = fmaxf(mx, x[uu]);
-            }
-            if (mx > m) { // the group's running maximum grows: rescale what it holds
-                const float f = __builtin_amdgcn_exp2f(m - mx);
-                l *= f;
-                l_t *= f;
-#pragma unroll
-                for (int e = 0; e < FPL; ++e) {
-                    acc[e] *= f;
-                    acc_t[e] *= f;
-                }
-                m = mx;
-            }
-#pragma unroll
-            for (int uu = 0; uu < kHalf; ++uu) {
-                const float p = x[uu] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[uu] - m);
-                l += p;
-#pragma unroll
-                for (int e = 0; e < FPL; ++e)
-                    acc[e] = fmaf(p, feature<T, NDW>(vr[hh + uu], e), acc[e]);
-            }
-        }
-        if ((base / kPass) % kRunPasses == kRunPasses - 1) { // close the run
-#pragma unroll
-            for (int e = 0; e < FPL; ++e) {
-                acc_t[e] += acc[e];
-                acc[e] = 0.0f;
-            }
-            l_t += l;
-            l = 0.0f;
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < FPL; ++e)
-        acc[e] += acc_t[e];
-    l += l_t;
-
-    // offset 0, the step's own token, joins group 0's softmax
-    {
-        float dot = 0.0f;
-#pragma unroll
-        for (int e = 0; e < FPL; ++e)
-            dot = fmaf(feature<T, NDW>(qr, e), feature<T, NDW>(kr0, e), dot);
-        dot = row16_sum(dot);
-        if (grp == 0) {
-            const float x0 = dot * scale;
-            const float mx = fmaxf(m, x0);
-            const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mx), p0 = __builtin_amdgcn_exp2f(x0 - mx);
-            l = fmaf(l, f, p0);
-#pragma unroll
-            for (int e = 0; e < FPL; ++e)
-                acc[e] = fmaf(acc[e], f, p0 * feature<T, NDW>(vr0, e));
-            m = mx;
-        }
-    }
-
-    // every group's partial softmax goes to LDS (a group without rows has m = -inf and weight 0)
-#pragma unroll
-    for (int e = 0; e < FPL; ++e)
-        s_acc[grp][part * FPL + e] = acc[e];
-    if (part == 0) {
-        s_m[grp] = m;
-        s_l[grp] = l;
-    }
+    ldec::step_group<T, D>(e, L, t / ldec::kLanesPerRow, t % ldec::kLanesPerRow, sm);
     __syncthreads();
-
-    // TPF adjacent lanes finish feature te, each combining GPT groups, then add up by DPP
-    const int sub = t % TPF;
-    float M = s_m[0]; // group 0 holds offset 0, so M is finite
-#pragma unroll
-    for (int g = 1; g < kGroups; ++g)
-        M = fmaxf(M, s_m[g]);
-    float z = 0.0f, u = 0.0f;
-#pragma unroll
-    for (int gg = 0; gg < GPT; ++gg) {
-        const int g = sub * GPT + gg;
-        const float fw = __builtin_amdgcn_exp2f(s_m[g] - M);
-        z = fmaf(s_l[g], fw, z);
-        u = fmaf(s_acc[g][te], fw, u);
-    }
-    z += dpp_f<0xB1>(z); // quad_perm [1,0,3,2]
-    u += dpp_f<0xB1>(u);
-    z += dpp_f<0x4E>(z); // quad_perm [2,3,0,1]
-    u += dpp_f<0x4E>(u);
-    if constexpr (TPF == 8) {
-        z += dpp_f<0x141>(z); // row_half_mirror: the two quads of each 8-lane half
-        u += dpp_f<0x141>(u);
-    }
-
-    const bool bad = hv.magic != kLocalStateMagic || hv.version != kLocalStateVersion || hv.batch != expect.batch ||
-                     hv.H != expect.H || hv.d != D || hv.dtype != expect.dtype || hv.w != expect.w ||
-                     hv.rec_bytes != expect.rec_bytes || i < 0;
-    T *o_row = out + bh * D;
-    if (sub == 0) {
-        u /= z;
-        const float y = o_lr ? fmaf(lc.alpha[h], to_f32<T>(olr_t), u) : u;
-        if (bad) { // not a state of this shape: flag the output, leave the state alone
-            if constexpr (sizeof(T) == 2)
-                o_row[te] = (T)0x7fc0u; // bf16 quiet NaN
-            else
-                o_row[te] = __uint_as_float(0x7fc00000u);
-        } else {
-            o_row[te] = from_f32<T>(y);
-            if (w > 0) { // the new token replaces token i - w, read above for the last time
-                const int64_t slot = i % w;
-                reinterpret_cast<T *>(rec + L.off_k)[slot * D + te] = kn_t;
-                reinterpret_cast<T *>(rec + L.off_v)[slot * D + te] = vn_t;
-            }
-        }
-    }
-    if (t == 0 && !bad)
-        *reinterpret_cast<int64_t *>(rec) = i + 1;
+    ldec::step_finish<T, D>(e, L, expect, sm, t, o_lr != nullptr, lc.alpha[bh % H], ldec::to_f32<T>(olr_t), out, bh);
 }
 
 template <typename T, int D>

@@ -474,6 +474,37 @@ fs_status fs_local_decode(int32_t batch, int32_t H, int32_t d, fs_dtype dtype, i
                           size_t state_bytes, const void *q, const void *k_new, const void *v_new,
                           const float *alpha_h, const void *o_lr, void *out, void *stream);
 
+/*
+ * The whole attention decode step of one token per (sequence, head) in one
+ * launch (Sec. 3.1, Eq. 2: out = o_sr + alpha_h * o_lr): the long-range step
+ * of fs_longrange_decode (Sec. 3.3 "Inference"; App. C "Bounded cache",
+ * Eq. 15) on `state` and the local-branch step of fs_local_decode (Sec. 3.2,
+ * Eqs. 3-4) on `local_state`, both at the records' next position.  The result,
+ * sel and both final states are bitwise those of fs_longrange_decode (output
+ * o_lr) followed by fs_local_decode with that o_lr; the long-range output
+ * itself is not stored.  The ring reads of the local step overlap the
+ * long-range step's chain of dependent phases, so one call takes far less than
+ * the two.
+ *   prm, state, state_bytes, sigma_h, lambda_h, gain, sel   as for fs_longrange_decode
+ *   w, local_state, local_state_bytes   as for fs_local_decode (the state built by
+ *                    fs_local_state_build with this w)                   (in/out)
+ *   q, k_new, v_new  device [batch, H, d] dtype, unrotated: the one query, key
+ *                    and value both branches read                        (input)
+ *   alpha_h          host [H] fp32, finite (required)
+ *   out              device [batch, H, d] dtype, not overlapping q, k_new, v_new (output)
+ * Errors: those of the two calls (FS_ERR_STATE when either size does not
+ * match; batch * H above 65535 is FS_ERR_UNSUPPORTED).  A buffer of the right
+ * size with a foreign header is detected on the device, as by the two calls:
+ * out is NaN, and that state is left untouched (the other one advances).  One
+ * launch, no host synchronisation (capturable in a HIP graph); steps on the
+ * same states must be ordered.
+ */
+fs_status fs_attention_decode(const fs_params *prm, int32_t batch, int32_t H, int32_t d, fs_dtype dtype,
+                              void *state, size_t state_bytes, int64_t w, void *local_state,
+                              size_t local_state_bytes, const void *q, const void *k_new, const void *v_new,
+                              const float *sigma_h, const float *lambda_h, const float *gain,
+                              const float *alpha_h, void *out, int32_t *sel, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -242,6 +242,44 @@ def test_local_decode_validation(L):
     assert call(ww=w + 1) == fsl.FS_ERR_STATE          # a state for another w has another size
 
 
+def test_attention_decode_validation(L):
+    """fs_attention_decode checks both states' sizes and every argument of the two
+    steps it fuses on the host, before any HIP call."""
+    p = fsl.Params()
+    prm_c = p.c()
+    b, H, d, w = 2, 3, 64, 16
+    n = fsl.fs_decode_state_bytes(b, H, d, fsl.FS_F32, p)
+    nl = fsl.fs_local_state_bytes(b, H, d, fsl.FS_F32, w)
+    vp = ctypes.c_void_p
+    sig = (ctypes.c_float * H)(*([4.0] * H))
+    lam = (ctypes.c_float * H)(*([1.0] * H))
+    alpha = (ctypes.c_float * H)(*([0.5] * H))
+    nan_alpha = (ctypes.c_float * H)(0.5, float("nan"), 0.5)
+    bad_sig = (ctypes.c_float * H)(*([0.0] * H))
+
+    def call(prm=prm_c, st=n, lst=nl, ww=w, q=1, out=1, state=1, lstate=1, al=alpha, sigma=sig, dd=d, bb=b):
+        return L.fs_attention_decode(ctypes.byref(prm), bb, H, dd, fsl.FS_F32, vp(state) if state else None, st, ww,
+                                     vp(lstate) if lstate else None, lst, vp(q) if q else None, vp(1), vp(1), sigma,
+                                     lam, None, al, vp(out) if out else None, None, None)
+
+    assert call(st=n + 256) == fsl.FS_ERR_STATE
+    assert call(lst=nl - 1) == fsl.FS_ERR_STATE
+    assert call(ww=w + 1) == fsl.FS_ERR_STATE           # the local state of another window has another size
+    assert call(state=0) == fsl.FS_ERR_INVALID
+    assert call(lstate=0) == fsl.FS_ERR_INVALID
+    assert call(q=0) == fsl.FS_ERR_INVALID
+    assert call(out=0) == fsl.FS_ERR_INVALID
+    assert call(al=None) == fsl.FS_ERR_INVALID          # Eq. 2 needs alpha_h
+    assert call(al=nan_alpha) == fsl.FS_ERR_INVALID
+    assert call(sigma=bad_sig) == fsl.FS_ERR_INVALID
+    assert call(ww=-1) == fsl.FS_ERR_INVALID
+    assert call(ww=65536) == fsl.FS_ERR_UNSUPPORTED
+    assert call(dd=96) == fsl.FS_ERR_UNSUPPORTED
+    assert call(bb=30000) == fsl.FS_ERR_UNSUPPORTED     # batch * H above 65535
+    assert call(prm=fsl.Params(prune=False).c()) == fsl.FS_ERR_UNSUPPORTED
+    assert call(prm=fsl.Params(K=0).c()) == fsl.FS_ERR_INVALID
+
+
 def test_local_window_validation(L):
     sh = shape(b=1, H=2, N=256, d=64)
     vp = ctypes.c_void_p
