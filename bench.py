@@ -712,9 +712,10 @@ CHUNK = 2048
 def run_chunk(args) -> int:
     """Chunked prefill into the bounded cache (App. C): b32 H8 d128 bf16 sequences whose
     state holds a 262,144-token prefix take the next 2048 tokens as one
-    fs_longrange_prefill_chunk call (2048 decode steps in one launch: a merge every 128
-    tokens, a cell completion every 32).  Each timed call starts from a fresh copy of
-    the prefix state (the copy is outside the timed region)."""
+    fs_longrange_prefill_chunk call: one launch that takes the chunk's 16 query blocks in
+    order per (sequence, head), each with its retention merge, the block's routing and
+    readout, and the append of its tokens (cell completions every 32).  Each timed call
+    starts from a fresh copy of the prefix state (the copy is outside the timed region)."""
     import numpy as np
     import torch
 
@@ -767,16 +768,21 @@ def run_chunk(args) -> int:
         times.append(ev0.elapsed_time(ev1))
     ms = float(np.median(times))
     value = b * CHUNK / (ms * 1e-3)
-    # what one chunk must move at the least: the state read and written once, the chunk's q, k, v
-    # read and its output written
-    alg_bytes = 2 * snap.numel() + 4 * b * H * CHUNK * d * 2
-    roofline = {"bound": "latency", "achieved": round(alg_bytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "decode_step (chunk)", "alg_bytes_per_launch": int(alg_bytes),
-                "us_per_token_step": round(ms * 1e3 / CHUNK, 3),
-                "note": "2048 dependent decode steps per (sequence, head) in one launch"}
     sel_h = sel.cpu().numpy()
     out_h = out.float().cpu().numpy()
+    # what one chunk moves by the method's own terms: per (sequence, head) the slot tables and
+    # mean keys once, the K/V of every block's distinct selected cells (U_beta cells of s
+    # rows), the chunk's q, k, v in and its output out, and its k, v rows into the slots
+    S = prm.P + prm.W + prm.B // prm.s
+    U = distinct_cells_per_block(sel_h, prm.B)
+    alg_bytes = (b * H * S * (d * 4 + 16) + float(U.sum()) * prm.s * d * 2 * 2
+                 + b * H * CHUNK * d * 2 * (3 + 1 + 2))
+    roofline = {"bound": "latency", "achieved": round(alg_bytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "chunk_block", "alg_bytes_per_launch": int(alg_bytes),
+                "us_per_block": round(ms * 1e3 / (CHUNK // prm.B), 3),
+                "mean_distinct_cells_per_block": round(float(U.mean()), 3),
+                "note": "the chunk's 16 query blocks one after another per (sequence, head), 256 workgroups"}
 
     cpu = parity = None
     if not args.no_cpu_baseline:

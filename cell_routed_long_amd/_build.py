@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libfsl.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["k_summaries.hip", "k_prune.hip", "k_score.hip", "k_readout.hip", "k_readout_bwd.hip", "k_fused.hip",
-           "k_decode.hip", "k_local.hip", "k_local_decode.hip", "k_attn_decode.hip", "noalloc.hip", "k_fsb.hip",
+           "k_decode.hip", "k_chunk.hip", "k_local.hip", "k_local_decode.hip", "k_attn_decode.hip", "noalloc.hip", "k_fsb.hip",
            "fsl_api.cpp"]
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

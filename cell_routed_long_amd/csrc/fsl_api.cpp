@@ -743,9 +743,11 @@ FSL_EXPORT fs_status fs_longrange_prefill_chunk(const fs_params *prm, int32_t ba
     if (state_bytes != state_bytes_of(batch, H, L))
         return FS_ERR_STATE;
     const StateHeader expect = state_header(batch, H, d, dtype, prm, L);
-    return hip_status(launch_decode_step(batch * H, H, d, dtype == FS_BF16 ? 1 : 0, prm->K, prm->P, prm->W, prm->eps,
-                                         L, expect, hc, state, q, k, v, gain, out, sel,
-                                         static_cast<hipStream_t>(stream), (int)n));
+    if (dtype == FS_BF16) // block by block, as the whole-prompt prefill
+        return hip_status(launch_chunk_blocks(batch * H, H, d, prm->K, prm->P, prm->W, prm->eps, L, expect, hc, state,
+                                              q, k, v, gain, out, sel, n, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_decode_step(batch * H, H, d, 0, prm->K, prm->P, prm->W, prm->eps, L, expect, hc, state, q,
+                                         k, v, gain, out, sel, static_cast<hipStream_t>(stream), (int)n));
 }
 
 FSL_EXPORT fs_status fs_local_window(const fs_shape *shape, int64_t w, float rope_base, const void *q, const void *k,

@@ -105,6 +105,13 @@ hipError_t launch_decode_step(int32_t bh, int32_t H, int32_t d, int32_t bf16, in
                               void *state, const void *q, const void *k_new, const void *v_new,
                               const float *gain, void *out, int32_t *sel, hipStream_t st, int n_tok = 0);
 
+// Chunked prefill of n tokens into bf16 decode states, one query block at a time
+// with the fused prefill's arithmetic (q, k, v, out [bh, n, d]; sel [bh, n, K]).
+hipError_t launch_chunk_blocks(int32_t bh, int32_t H, int32_t d, int32_t K, int32_t P, int32_t W, float eps,
+                               const StateLayout &L, const StateHeader &expect, const HeadConsts &hc, void *state,
+                               const void *q, const void *k, const void *v, const float *gain, void *out,
+                               int32_t *sel, int64_t n, hipStream_t st);
+
 // An empty decode state (position 0) for bh records.
 hipError_t launch_state_init(int32_t bh, const StateLayout &L, const StateHeader &hdr, void *state, hipStream_t st);
 

@@ -373,11 +373,15 @@ fs_status fs_decode_state_init(const fs_params *prm, int32_t batch, int32_t H, i
  * cache is prefilled in fixed-size chunks -- the page uses 2048 tokens -- with
  * the retention update at every block boundary; Sec. 3.3 "Inference").  The n
  * tokens at the state's positions i .. i + n - 1 of every (sequence, head) are
- * processed in order, each exactly as one fs_longrange_decode step (merge at
- * block starts, append and cell summary, Eq. 7 scores over A, top-K, readout
- * with Eq. 17), in one launch: the outputs and the final state are bitwise
- * those of n single steps, and equal the whole-prompt prefill's at the same
- * positions (the same causal operator).
+ * processed in one launch, with the same results as n fs_longrange_decode steps
+ * (merge at block starts, append and cell summary, Eq. 7 scores over A, top-K,
+ * readout with Eq. 17): the same causal operator as the whole-prompt prefill.
+ * bf16: the chunk's query blocks are taken in order, each block's queries at
+ * once with the whole-prompt prefill's arithmetic, so outputs and selections
+ * are bitwise those of fs_longrange_prefill over the whole prompt and the
+ * state's cell summaries are bitwise the summary pass's.  fp32: the tokens are
+ * taken one by one as decode steps, bitwise n single steps.  Either way the
+ * result does not depend on where a prompt is cut into chunks.
  *   state            as for fs_longrange_decode (built by fs_longrange_prefill,
  *                    fs_decode_state_init, or an earlier chunk)            (in/out)
  *   n                tokens per (sequence, head), 1 <= n <= 65536

@@ -6,8 +6,10 @@ decode under one HIP graph.
 The page defines prefill and decode as one causal operator (Sec. 3.3
 "Inference"), so the reference for every chunk position is the oracle's output
 at that position over the whole sequence; see tests/parity_utils.py for the
-rules.  A chunk is n decode steps in one launch, so it must also agree bitwise
-with n single steps, and with itself split at any point.
+rules.  A chunk must also agree bitwise with itself split at any point.  bf16
+chunks are computed block by block with the whole-prompt prefill's arithmetic,
+so they agree with it bitwise; fp32 chunks are n decode steps in one launch,
+bitwise n single steps.
 """
 import numpy as np
 import pytest
@@ -92,34 +94,98 @@ def test_chunked_prompt_from_empty_state(w, p, bounds, extra):
         np.testing.assert_array_equal(sel[b, h][ok], sel_pre[b, h][ok])
 
 
-def test_chunk_equals_single_steps_and_split_chunks():
-    """A chunk is n decode steps: bitwise the outputs, selections and final state of n
-    single steps, and of the same tokens split into two chunks at any point."""
-    w = synth.Workload(batch=2, H=2, N=2600, d=128, dtype="bf16", seed=505, needle_frac=0.01)
-    p = fsl.Params(P=8, W=2)
+@pytest.mark.parametrize("w,p", [
+    (synth.Workload(batch=2, H=2, N=2600, d=128, dtype="bf16", seed=505, needle_frac=0.01), fsl.Params(P=8, W=2)),
+    (synth.Workload(batch=1, H=3, N=1900, d=64, dtype="bf16", seed=507, needle_frac=0.01), fsl.Params(K=6)),
+    (synth.Workload(batch=2, H=2, N=2600, d=128, dtype="f32", seed=508, needle_frac=0.01), fsl.Params(P=8, W=2)),
+], ids=["bf16d128", "bf16d64-K6", "f32d128"])
+def test_chunk_split_anywhere_and_against_prefill(w, p):
+    """The same tokens in one chunk or split into two at any point: bitwise the same
+    outputs, selections and final state.  bf16 chunks run block by block with the
+    fused prefill's arithmetic, so they are bitwise the whole-prompt prefill's rows;
+    fp32 chunks are single decode steps, so they are bitwise n single steps."""
     host = pu.inputs(w)
-    N0, n = 1000, 1300  # a state from a prefill, then positions crossing several block boundaries
+    N0, n = 1000, w.N - 1000 - 300  # a state from a prefill, then positions crossing several block boundaries
     dk, dv = (rows(host, x, 0, N0, w.dtype) for x in "kv")
-    base = fsl.new_state(w.batch, w.H, w.d, torch.bfloat16, p)
+    base = fsl.new_state(w.batch, w.H, w.d, tdtype(w), p)
     base.fill_(0x33)
     fsl.prefill(None, dk, dv, p, want_out=False, want_sel=False, state=base)
     s1, s2, s3 = base.clone(), base.clone(), base.clone()
     o1, c1 = run_chunks(w, host, p, s1, N0, [N0 + n])
     o3, c3 = run_chunks(w, host, p, s3, N0, [N0 + 437, N0 + n])
+    np.testing.assert_array_equal(c1, c3)
+    np.testing.assert_array_equal(o1, o3)
+    assert torch.equal(s1, s3)
+    if w.dtype == "bf16":
+        dq, dk2, dv2 = (rows(host, x, 0, N0 + n, w.dtype) for x in "qkv")
+        print(f"[gpu] whole-prompt prefill {w}", flush=True)
+        o_pre, c_pre, _ = fsl.prefill(dq, dk2, dv2, p)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(c1, c_pre[:, :, N0:].cpu().numpy())
+        np.testing.assert_array_equal(o1, o_pre[:, :, N0:].float().cpu().numpy())
+        return
     steps = {x: pu.to_device(np.ascontiguousarray(np.moveaxis(host[x][:, :, N0:N0 + n], 2, 0)), w.dtype) for x in "qkv"}
-    outs = torch.empty(n, w.batch, w.H, w.d, dtype=torch.bfloat16, device="cuda")
+    outs = torch.empty(n, w.batch, w.H, w.d, dtype=tdtype(w), device="cuda")
     sels = torch.empty(n, w.batch, w.H, p.K, dtype=torch.int32, device="cuda")
     print("[gpu] single steps", flush=True)
     for t in range(n):
         fsl.decode(s2, steps["q"][t], steps["k"][t], steps["v"][t], p, out=outs[t], sel=sels[t])
     torch.cuda.synchronize()
-    o2 = np.moveaxis(outs.float().cpu().numpy(), 0, 2)
-    c2 = np.moveaxis(sels.cpu().numpy(), 0, 2)
-    np.testing.assert_array_equal(c1, c2)
-    np.testing.assert_array_equal(o1, o2)
-    np.testing.assert_array_equal(c1, c3)
-    np.testing.assert_array_equal(o1, o3)
-    assert torch.equal(s1, s2) and torch.equal(s1, s3)
+    np.testing.assert_array_equal(c1, np.moveaxis(sels.cpu().numpy(), 0, 2))
+    np.testing.assert_array_equal(o1, np.moveaxis(outs.float().cpu().numpy(), 0, 2))
+    assert torch.equal(s1, s2)
+
+
+def state_summaries(st, w):
+    """(cell ids [b H, S], fp32 mean keys [b H, S, d], norms [b H, S]) of a decode-state
+    buffer, read in the record layout fs_decode_state_bytes sizes: a 256-byte header
+    (n_slots at byte 40, the record size at byte 48), then per (sequence, head) a
+    32-byte meta block and the slot tables (positions in A, cell ids, flags, a_c,
+    mean keys), each starting on a 256-byte boundary."""
+    raw = st.cpu().numpy()
+    S = int(raw[40:44].view(np.int32)[0])
+    rec = int(raw[48:56].view(np.int64)[0])
+    al = lambda x: (x + 255) // 256 * 256
+    off_cell = al(32) + al(4 * S)
+    off_a = off_cell + 2 * al(4 * S)
+    off_kbar = off_a + al(4 * S)
+    n = w.batch * w.H
+    cells = np.stack([raw[256 + r * rec + off_cell:][:4 * S].view(np.int32) for r in range(n)])
+    a = np.stack([raw[256 + r * rec + off_a:][:4 * S].view(np.float32) for r in range(n)])
+    kbar = np.stack([raw[256 + r * rec + off_kbar:][:4 * S * w.d].view(np.float32).reshape(S, w.d) for r in range(n)])
+    return cells, kbar, a
+
+
+def test_chunks_from_empty_state_equal_prefill_bitwise():
+    """bf16: a whole prompt fed from an empty state in chunks of 2048 (and a ragged
+    last one, and chunks ending mid-cell) gives bitwise the whole-prompt prefill's
+    output rows and selections, and every complete cell the state holds has bitwise
+    the summary pass's mean key and norm (Eq. 5)."""
+    w = synth.Workload(batch=2, H=3, N=5000, d=128, dtype="bf16", seed=509, needle_frac=0.005)
+    p = fsl.Params()
+    host = pu.inputs(w)
+    st = empty_state(w, p)
+    o, c = run_chunks(w, host, p, st, 0, [2048, 2049, 3000, 4096, 4113, 5000])
+    dq, dk, dv = (rows(host, x, 0, w.N, w.dtype) for x in "qkv")
+    o_pre, c_pre, _ = fsl.prefill(dq, dk, dv, p)
+    M = w.N // p.s
+    kbar_ref = torch.empty(w.batch, w.H, M, w.d, dtype=torch.float32, device="cuda")
+    a_ref = torch.empty(w.batch, w.H, M, dtype=torch.float32, device="cuda")
+    fsl.fs_cell_summaries(dk, kbar_ref, a_ref, p)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c, c_pre.cpu().numpy())
+    np.testing.assert_array_equal(o, o_pre.float().cpu().numpy())
+    cells, kbar, a = state_summaries(st, w)
+    kbar_ref = kbar_ref.reshape(w.batch * w.H, M, w.d).cpu().numpy()
+    a_ref = a_ref.reshape(w.batch * w.H, M).cpu().numpy()
+    checked = 0
+    for r in range(w.batch * w.H):
+        for x, cell in enumerate(cells[r]):
+            if 0 <= cell < M:
+                assert np.array_equal(kbar[r, x].view(np.uint32), kbar_ref[r, cell].view(np.uint32)), (r, cell)
+                assert a[r, x].view(np.uint32) == a_ref[r, cell].view(np.uint32), (r, cell)
+                checked += 1
+    assert checked >= w.batch * w.H * p.P
 
 
 def test_chunked_prefill_then_decode_equals_prefill_then_decode():
