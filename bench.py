@@ -770,6 +770,12 @@ def run_chunk(args) -> int:
     value = b * CHUNK / (ms * 1e-3)
     sel_h = sel.cpu().numpy()
     out_h = out.float().cpu().numpy()
+    if args.copy_calibration:  # a 1 GiB copy whose bytes are known, for HBM counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     # what one chunk moves by the method's own terms: per (sequence, head) the slot tables and
     # mean keys once, the K/V of every block's distinct selected cells (U_beta cells of s
     # rows), the chunk's q, k, v in and its output out, and its k, v rows into the slots
@@ -778,8 +784,9 @@ def run_chunk(args) -> int:
     alg_bytes = (b * H * S * (d * 4 + 16) + float(U.sum()) * prm.s * d * 2 * 2
                  + b * H * CHUNK * d * 2 * (3 + 1 + 2))
     roofline = {"bound": "latency", "achieved": round(alg_bytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "chunk_block", "alg_bytes_per_launch": int(alg_bytes),
+                "unit": "GB/s", "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("chunk_block", "chunk_256k"), "kernel": "chunk_block",
+                "alg_bytes_per_launch": int(alg_bytes),
                 "us_per_block": round(ms * 1e3 / (CHUNK // prm.B), 3),
                 "mean_distinct_cells_per_block": round(float(U.mean()), 3),
                 "note": "the chunk's 16 query blocks one after another per (sequence, head), 256 workgroups"}
