@@ -129,6 +129,31 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
     // load each per block, kept in registers until the first tile is scored
     constexpr int kBoundTiles = 256; // the tile bound covers retained lists of up to 8192 cells
     const bool bound = kbar_norm != nullptr && nA > 32 && nA <= kBoundTiles * 32;
+    __shared__ float s_tpr[kBoundTiles], s_tkn[kBoundTiles], s_qn[kThreads / kWave];
+    __shared__ uint32_t s_tau[2][kThreads / kWave];
+    if (bound) { // the largest |q_i| of this wave, for the tile bound (read after a later barrier);
+        // computed before any later load is issued, so it waits for the query fragments only
+        float ss = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const u32x4 w = __builtin_bit_cast(u32x4, qf[kc]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // the element goes through a named copy: hipcc miscompiles a bit cast
+                // of a vector element taken in place (it reads element 0)
+                const uint32_t we = w[e];
+                const bf16x2 x = __builtin_bit_cast(bf16x2, we);
+                ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+            }
+        }
+        ss += shfl_xor_f(ss, 32); // the partner lane holds the other half of the features
+        // + 2^-100: covers subnormal elements, should the dot product flush them
+        const float qn = q_ok ? sqrtf(ss) * (1.0f + 0x1p-10f) + 0x1p-100f : 0.0f;
+        const bool badq = __ballot(!(qn <= FLT_MAX)) != 0ull;
+        const float qm = wave_max_f(qn);
+        if (lane == 0)
+            s_qn[wave] = badq ? INFINITY : qm;
+    }
     float b_pr = 0.0f, b_kn = 0.0f;
     if (bound && t < nA) { // lambda is applied where the values are first used, so nothing waits here
         const int64_t id = head * M + (prune ? s_A[t] : t);
@@ -141,22 +166,18 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
         pre_t0 = t0;
         const int x = t0 + srow;
         pre_id = x < nA ? (prune ? s_A[x] : x) : -1;
-        pre_a = 0.0f;
-        if (pre_id >= 0) {
-            // < 3 d M elements: the offset fits 32 bits
-            const uint16_t *src = kbs_h + (uint32_t)(pre_id * 3 * D + spart * PER);
+        // no branch around the loads: a value merged from two paths would make the wave
+        // wait for the loads right here.  Padding rows read cell 0, and their scores never
+        // count (their id stays -1).
+        const int cid = pre_id >= 0 ? pre_id : 0;
+        // < 3 d M elements: the offset fits 32 bits
+        const uint16_t *src = kbs_h + (uint32_t)(cid * 3 * D + spart * PER);
 #pragma unroll
-            for (int part = 0; part < 3; ++part)
+        for (int part = 0; part < 3; ++part)
 #pragma unroll
-                for (int u = 0; u < SCH; ++u)
-                    pre3[part * SCH + u] = *reinterpret_cast<const u32x4 *>(src + part * D + u * 8);
-            if (spart == 0)
-                pre_a = a[head * M + pre_id];
-        } else {
-#pragma unroll
-            for (int u = 0; u < 3 * SCH; ++u)
-                pre3[u] = u32x4{0, 0, 0, 0};
-        }
+            for (int u = 0; u < SCH; ++u)
+                pre3[part * SCH + u] = *reinterpret_cast<const u32x4 *>(src + part * D + u * 8);
+        pre_a = a[head * M + cid];
     };
     if (nA > 0)
         prefetch(0);
@@ -174,8 +195,6 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
     // those of scoring every cell.  The first tile is always scored.
     // per 32-cell tile of the retained list: the largest lambda a_c and the largest |kbar_c|
     // (NaN or infinite values make the tile's maximum infinite, so it is never passed over)
-    __shared__ float s_tpr[kBoundTiles], s_tkn[kBoundTiles], s_qn[kThreads / kWave];
-    __shared__ uint32_t s_tau[2][kThreads / kWave];
     auto tile_max = [&](int x, float pr, float kn) { // thread's cell x of the list; all threads call it
         pr = pr <= FLT_MAX ? pr : INFINITY;
         kn = kn <= FLT_MAX ? kn : INFINITY;
@@ -249,8 +268,10 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
             }
         }
         __syncthreads();
-        if (t0 + 32 < nA && !(bound && t0 > 0 && tile_below(t0 + 32)))
-            prefetch(t0 + 32); // overlaps the matrix work below
+        // the next tile, in flight under the matrix work below, unless the bound passes over
+        // it; with the bound on, the first tile's keys decide (without them it seldom fails)
+        if (t0 + 32 < nA && !(bound && (t0 == 0 || tile_below(t0 + 32))))
+            prefetch(t0 + 32);
 
         f32x16 acc;
         // three independent accumulators (lo, mid, hi parts) keep the matrix cores busy;
@@ -272,72 +293,54 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             acc[r] = (acc3[2][r] + acc3[1][r]) + acc3[0][r];
-        if (bound && t0 == 0) { // the largest |q_i| of this wave, for the tile bound
-            float ss = 0.0f;
+        // this lane's 16 rows come in 4 runs of 4 consecutive rows; their keys are made and
+        // taken in two halves of 8 rows (fewer registers live at once; the top-K does not
+        // depend on the order in which distinct keys enter it)
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const u32x4 w = __builtin_bit_cast(u32x4, qf[kc]);
+        for (int hh = 0; hh < 2; ++hh) {
+            float prv[8], pcv[8];
+            int idv[8]; // low key halves; -1 on padding rows
+#pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2) {
+                const int r0 = 8 * (2 * hh + g2) + 4 * half;
+                const u32x4 vp = *reinterpret_cast<const u32x4 *>(&sm.prior[r0]);
+                const u32x4 vc = *reinterpret_cast<const u32x4 *>(&sm.pc[r0]);
+                const u32x4 vi = *reinterpret_cast<const u32x4 *>(&sm.id[r0]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    // the element goes through a named copy: hipcc miscompiles a bit cast
-                    // of a vector element taken in place (it reads element 0)
-                    const uint32_t we = w[e];
-                    const bf16x2 x = __builtin_bit_cast(bf16x2, we);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+                    prv[4 * g2 + e] = __uint_as_float(vp[e]);
+                    pcv[4 * g2 + e] = __uint_as_float(vc[e]);
+                    idv[4 * g2 + e] = (int)vi[e];
                 }
             }
-            ss += shfl_xor_f(ss, 32); // the partner lane holds the other half of the features
-            // + 2^-100: covers subnormal elements, should the dot product flush them
-            const float qn = q_ok ? sqrtf(ss) * (1.0f + 0x1p-10f) + 0x1p-100f : 0.0f;
-            const bool badq = __ballot(!(qn <= FLT_MAX)) != 0ull;
-            const float qm = wave_max_f(qn);
-            if (lane == 0)
-                s_qn[wave] = badq ? INFINITY : qm;
-        }
-        // erf only below 4 (above it rounds to 1 in fp32); see the scorer
-        // this lane's 16 rows come in 4 runs of 4 consecutive rows: 12 vector LDS reads
-        float prv[16], pcv[16];
-        int idv[16]; // low key halves; -1 on padding rows
+            // erf only below 4 (from there on it rounds to 1 in fp32, and fmaf(prior,
+            // 1, content) == prior + content); a wave takes the long path only if
+            // one of its queries is that close to one of these cells
+            float pcmax = pcv[0];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int r0 = 8 * g + 4 * half;
-            const u32x4 vp = *reinterpret_cast<const u32x4 *>(&sm.prior[r0]);
-            const u32x4 vc = *reinterpret_cast<const u32x4 *>(&sm.pc[r0]);
-            const u32x4 vi = *reinterpret_cast<const u32x4 *>(&sm.id[r0]);
+            for (int r = 1; r < 8; ++r)
+                pcmax = fmaxf(pcmax, pcv[r]);
+            const bool need_erf = __ballot(q_ok && (qpos - pcmax) * inv2s < 4.0f) != 0ull;
+            uint64_t key[8];
+            if (need_erf) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                prv[4 * g + e] = __uint_as_float(vp[e]);
-                pcv[4 * g + e] = __uint_as_float(vc[e]);
-                idv[4 * g + e] = (int)vi[e];
+                for (int r = 0; r < 8; ++r) {
+                    float g = 1.0f;
+                    const float x = (qpos - pcv[r]) * inv2s; // (i - p_c) / (2 sigma_h), i - p_c exact
+                    if (x < 4.0f)
+                        g = erff(x);
+                    const float score = fmaf(prv[r], g, acc[8 * hh + r] * inv_sqrt_d);
+                    key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float score = fmaf(prv[r], 1.0f, acc[8 * hh + r] * inv_sqrt_d);
+                    key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
+                }
             }
+            take_tile_keys<KT, 8>(kl, key, t0 == 0 && hh == 0);
         }
-        // erf only below 4 (from there on it rounds to 1 in fp32, and fmaf(prior,
-        // 1, content) == prior + content); a wave takes the long path only if
-        // one of its queries is that close to one of its cells
-        float pcmax = pcv[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-            pcmax = fmaxf(pcmax, pcv[r]);
-        const bool need_erf = __ballot(q_ok && (qpos - pcmax) * inv2s < 4.0f) != 0ull;
-        uint64_t key[16];
-        if (need_erf) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float g = 1.0f;
-                const float x = (qpos - pcv[r]) * inv2s; // (i - p_c) / (2 sigma_h), i - p_c exact
-                if (x < 4.0f)
-                    g = erff(x);
-                const float score = fmaf(prv[r], g, acc[r] * inv_sqrt_d);
-                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float score = fmaf(prv[r], 1.0f, acc[r] * inv_sqrt_d);
-                key[r] = (q_ok && idv[r] >= 0) ? rank_key(score, (uint32_t)idv[r]) : 0;
-            }
-        }
-        take_tile_keys<KT>(kl, key, t0 == 0);
     }
     // merge with the partner lane (same query, other 16 rows of every tile)
     {
@@ -481,24 +484,31 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
             // probabilities (16 kk + 4 half + 0..3, then + 8); two transposed 4-row reads
             // from row-major V give them (lane j of a 16-lane group names row j / 4, and
             // features 4 (j % 4) .. +3 of the group's 16)
-            bf16x8 av[DT];
             const int r0 = 16 * kk + 4 * half + ((lane & 15) >> 2);
             const int c0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            // two feature tiles at a time (fewer registers live): lo parts of both, then hi
+            // parts, so no product waits on the one just before it
+            constexpr int DP = DT < 2 ? DT : 2;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)&sm.v[r0][dt * 32 + c0]);
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)&sm.v[r0 + 8][dt * 32 + c0]);
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                av[dt] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+            for (int d0 = 0; d0 < DT; d0 += DP) {
+                bf16x8 av[DP];
+#pragma unroll
+                for (int j = 0; j < DP; ++j) {
+                    const int dt = d0 + j;
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16 *)&sm.v[r0][dt * 32 + c0]);
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16 *)&sm.v[r0 + 8][dt * 32 + c0]);
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    av[j] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+                }
+#pragma unroll
+                for (int j = 0; j < DP; ++j)
+                    o_acc[d0 + j] = mfma_bf16(av[j], bl, o_acc[d0 + j]);
+#pragma unroll
+                for (int j = 0; j < DP; ++j)
+                    o_acc[d0 + j] = mfma_bf16(av[j], bh, o_acc[d0 + j]);
             }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) // lo parts of every tile, then hi parts: no back-to-back chain
-                o_acc[dt] = mfma_bf16(av[dt], bl, o_acc[dt]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                o_acc[dt] = mfma_bf16(av[dt], bh, o_acc[dt]);
         }
     }
 
