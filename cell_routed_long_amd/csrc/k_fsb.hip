@@ -262,6 +262,55 @@ __global__ __launch_bounds__(kBuildThreads) void fsb_build_kernel(const double *
 
 // ---------------------------------------------------------------- search
 
+// Compare-exchange of two 64-bit keys: afterwards hi >= lo.
+__device__ __forceinline__ void cx_desc(uint64_t &hi, uint64_t &lo)
+{
+    const uint64_t a = hi, b = lo;
+    const bool sw = a < b;
+    hi = sw ? b : a;
+    lo = sw ? a : b;
+}
+
+// Bitonic sort of N keys into descending order (N a power of two; every index a
+// compile-time constant after unrolling, so the keys stay in registers).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&x)[N])
+{
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    if ((i & k) == 0)
+                        cx_desc(x[i], x[l]); // this run descending
+                    else
+                        cx_desc(x[l], x[i]); // this run ascending
+                }
+            }
+}
+
+// The N largest of two descending lists a and b, descending, into a: the
+// elementwise larger of a and b reversed is a bitonic sequence that holds them,
+// and a bitonic merge orders it.
+template <int N>
+__device__ __forceinline__ void merge_top_desc(uint64_t (&a)[N], const uint64_t (&b)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        a[i] = a[i] > b[N - 1 - i] ? a[i] : b[N - 1 - i];
+#pragma unroll
+    for (int j = N >> 1; j > 0; j >>= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int l = i ^ j;
+            if (l > i)
+                cx_desc(a[i], a[l]);
+        }
+}
+
 constexpr int kMaxChunksPerForest = kFsbMaxLevels; // popcount of an admitted count below 2^13
 constexpr int kMaxForestNodes = 2 * (int)kFsbMaxCells; // 2M - 1 nodes
 constexpr int kBmWords = kMaxForestNodes / 32;
@@ -551,26 +600,26 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
             }
             // ---- each query keeps its leaves and its best Wb - #leaves children ----
             {
+                // this lane's children (every other one) sorted, then the best kFsbMaxBeam of
+                // its list and the partner lane's (which ranked the others); the keys are
+                // distinct, so this is the order any exact top-kFsbMaxBeam selection gives
+                static_assert(kMaxKids == 2 * kFsbMaxBeam, "each lane of the pair ranks half the children");
                 uint64_t top[kFsbMaxBeam];
-#pragma unroll
-                for (int e = 0; e < kFsbMaxBeam; ++e)
-                    top[e] = 0ull;
                 const int nkq = sm.nk[qs];
-                for (int e = half; e < nkq; e += 2)
-                    insert_key<kFsbMaxBeam>(top, rank_key(sm.ku[qs][e], ((0xffffu - sm.kmin[qs][e]) << 16) | (uint32_t)e));
-                uint64_t mine[kFsbMaxBeam]; // sent as ranked before the partner's keys enter the list
 #pragma unroll
-                for (int e = 0; e < kFsbMaxBeam; ++e)
-                    mine[e] = top[e];
-#pragma unroll
-                for (int e = 0; e < kFsbMaxBeam; ++e) { // the partner lane ranked the other children
-                    const uint64_t o = mine[e];
-                    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)o, 32, kWave);
-                    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(o >> 32), 32, kWave);
-                    const uint64_t other = ((uint64_t)hi << 32) | lo;
-                    if (other)
-                        insert_key<kFsbMaxBeam>(top, other);
+                for (int j = 0; j < kFsbMaxBeam; ++j) {
+                    const int e = 2 * j + half;
+                    top[j] = e < nkq ? rank_key(sm.ku[qs][e], ((0xffffu - sm.kmin[qs][e]) << 16) | (uint32_t)e) : 0ull;
                 }
+                sort_desc<kFsbMaxBeam>(top);
+                uint64_t other[kFsbMaxBeam];
+#pragma unroll
+                for (int j = 0; j < kFsbMaxBeam; ++j) {
+                    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)top[j], 32, kWave);
+                    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(top[j] >> 32), 32, kWave);
+                    other[j] = ((uint64_t)hi << 32) | lo;
+                }
+                merge_top_desc<kFsbMaxBeam>(top, other);
                 if (half == 0 && nkq > 0) {
                     int nb2 = 0;
                     for (int e = 0; e < sm.nb[qs]; ++e)
