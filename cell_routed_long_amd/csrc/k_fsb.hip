@@ -312,34 +312,39 @@ __device__ __forceinline__ void merge_top_desc(uint64_t (&a)[N], const uint64_t 
 }
 
 constexpr int kMaxChunksPerForest = kFsbMaxLevels; // popcount of an admitted count below 2^13
-constexpr int kMaxForestNodes = 2 * (int)kFsbMaxCells; // 2M - 1 nodes
-constexpr int kBmWords = kMaxForestNodes / 32;
 constexpr int kMaxKids = 2 * kFsbMaxBeam;
 constexpr uint32_t kJoinRef = 0x40000000u;
+
+// Dynamic LDS of the search: bm and wb of fsb_search_words(Mu) words each, then the
+// node list of up to 32 words' worth of entries per word; a forest of Mu cells has
+// fewer than 2 Mu nodes (chunk trees and join nodes), and the candidate union at
+// most Mu cells.
+__host__ __device__ inline int fsb_search_words(int64_t Mu) { return (int)((2 * Mu + 63) / 32); }
+inline size_t fsb_search_lds(int64_t Mu)
+{
+    const int nw = fsb_search_words(Mu);
+    return (size_t)nw * 2 * sizeof(uint32_t) + (size_t)nw * 32 * sizeof(uint16_t);
+}
 
 template <typename T, int D>
 struct SearchSmem {
     int32_t beam[128][kFsbMaxBeam]; // node refs of each query's beam
     int32_t nb[128];
     int32_t nk[128], nleaf[128];
-    int32_t kref[128][kMaxKids];   // children being ranked
-    uint16_t kidx[128][kMaxKids];  // their position in the level's node list
-    float ku[128][kMaxKids];       // their priority (Eq. 11)
-    uint16_t kmin[128][kMaxKids];  // their smallest cell id
-    int32_t cand[128][kMaxKids];   // candidate cells (forest 0, then the second forest)
+    int32_t kpar[128][kFsbMaxBeam]; // the beam's internal nodes, whose children 2 j, 2 j + 1 are ranked
+    float ku[128][kMaxKids];        // the children's priority (Eq. 11)
+    uint16_t kmin[128][kMaxKids];   // their smallest cell id
+    uint16_t cand[128][kMaxKids];   // candidate cells (forest 0, then the second forest)
     int32_t ncand[128];
-    uint32_t bm[kBmWords];         // the level's node set (forest-local index), or the candidates' cells
-    int32_t wb[kBmWords];          // prefix counts of bm
-    uint16_t list[kMaxForestNodes]; // the level's nodes (forest-local index), or the candidates' cells
     int32_t nlist;
     union {
-        float mu[32][D + 1]; // a tile of node means
+        float mu[32][D + 1];      // a tile of node means
+        float ut[kWaves][32][33]; // then the tile's priorities: [wave][node row][query column]
         uint16_t kt16[32][D + 8];
         float kt32[32][D + 1];
     };
     float trho[32], tA[32];
     int32_t tmin[32];
-    float ut[kWaves][32][33]; // priorities of the tile: [wave][node row][query column]
     float jmu[kMaxChunksPerForest][D];
     FsbNodeMeta jmeta[kMaxChunksPerForest];
     int32_t jcount[kMaxChunksPerForest];
@@ -364,6 +369,12 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
 {
     constexpr bool kBf16 = sizeof(T) == 2;
     __shared__ SearchSmem<T, D> sm;
+    // sized by the launch for this forest size (fsb_search_lds): bm and wb of nw words, then list
+    extern __shared__ uint32_t dyn[];
+    const int nw = fsb_search_words(L.Mu);
+    uint32_t *const bm = dyn;                                  // the level's node set, or the candidates' cells
+    int32_t *const wb = reinterpret_cast<int32_t *>(dyn + nw); // prefix counts of bm
+    uint16_t *const list = reinterpret_cast<uint16_t *>(dyn + 2 * nw); // the level's nodes, or the candidates' cells
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
     const int beta = (int)(lb % (uint32_t)NB);
     const int64_t bh = (int64_t)(lb / (uint32_t)NB);
@@ -473,6 +484,16 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
         auto local_of = [&](int32_t ref) {
             return (ref & kJoinRef) ? lj + (ref & 0xffff) : sm.lbase[ref >> 16] + (ref & 0xffff) - 1;
         };
+        // child c (0 or 1) of internal node ref
+        auto child_of = [&](int32_t ref, int c) -> int32_t {
+            if (ref & kJoinRef) {
+                const int jt = ref & 0xffff;
+                if (c == 0)
+                    return (jt << 16) | 1;
+                return jt + 1 <= r - 2 ? (int32_t)(kJoinRef | (jt + 1)) : (int32_t)(((r - 1) << 16) | 1);
+            }
+            return ref + (ref & 0xffff) + c; // heap 2h, 2h + 1
+        };
         const int32_t root = r == 1 ? (int32_t)((0 << 16) | 1) : (int32_t)(kJoinRef | 0);
         if (t < 128) {
             sm.beam[t][0] = root;
@@ -483,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
         // ---- beam search, level by level ----
         for (;;) {
             for (int x = t; x < nwords; x += kThreads)
-                sm.bm[x] = 0u;
+                bm[x] = 0u;
             __syncthreads();
             int nk = 0;
             if (half == 0) { // expand this query's internal nodes; leaves keep their slots
@@ -494,20 +515,12 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
                         ++nleaf;
                         continue;
                     }
-                    int32_t c0, c1;
-                    if (ref & kJoinRef) {
-                        const int jt = ref & 0xffff;
-                        c0 = (jt << 16) | 1;
-                        c1 = jt + 1 <= r - 2 ? (int32_t)(kJoinRef | (jt + 1)) : (int32_t)(((r - 1) << 16) | 1);
-                    } else {
-                        c0 = ref + (ref & 0xffff);     // heap 2h
-                        c1 = ref + (ref & 0xffff) + 1; // heap 2h + 1
-                    }
-                    sm.kref[qs][nk++] = c0;
-                    sm.kref[qs][nk++] = c1;
+                    const int32_t c0 = child_of(ref, 0), c1 = child_of(ref, 1);
+                    sm.kpar[qs][nk >> 1] = ref;
+                    nk += 2;
                     const int l0 = local_of(c0), l1 = local_of(c1);
-                    atomicOr(&sm.bm[l0 >> 5], 1u << (l0 & 31));
-                    atomicOr(&sm.bm[l1 >> 5], 1u << (l1 & 31));
+                    atomicOr(&bm[l0 >> 5], 1u << (l0 & 31));
+                    atomicOr(&bm[l1 >> 5], 1u << (l1 & 31));
                 }
                 sm.nk[qs] = nk;
                 sm.nleaf[qs] = nleaf;
@@ -518,25 +531,19 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
             if (t == 0) {
                 int32_t run = 0;
                 for (int x = 0; x < nwords; ++x) {
-                    sm.wb[x] = run;
-                    run += __popc(sm.bm[x]);
+                    wb[x] = run;
+                    run += __popc(bm[x]);
                 }
                 sm.nlist = run;
             }
             __syncthreads();
             for (int x = t; x < nwords; x += kThreads) {
-                uint32_t bits = sm.bm[x];
-                int32_t pos = sm.wb[x];
+                uint32_t bits = bm[x];
+                int32_t pos = wb[x];
                 while (bits) {
                     const int b = __ffs(bits) - 1;
                     bits &= bits - 1;
-                    sm.list[pos++] = (uint16_t)(x * 32 + b);
-                }
-            }
-            if (half == 0) {
-                for (int e = 0; e < sm.nk[qs]; ++e) {
-                    const int l = local_of(sm.kref[qs][e]);
-                    sm.kidx[qs][e] = (uint16_t)(sm.wb[l >> 5] + __popc(sm.bm[l >> 5] & ((1u << (l & 31)) - 1u)));
+                    list[pos++] = (uint16_t)(x * 32 + b);
                 }
             }
             __syncthreads();
@@ -550,7 +557,7 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
                     const float *src = nullptr;
                     FsbNodeMeta meta{0.0f, 0.0f, 0, -1};
                     if (u < Z) {
-                        const int l = sm.list[u];
+                        const int l = list[u];
                         if (l >= lj) {
                             src = sm.jmu[l - lj];
                             meta = sm.jmeta[l - lj];
@@ -580,6 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
 #pragma unroll
                 for (int kc = 0; kc < D / 2; ++kc)
                     acc = mfma_f32(sm.mu[col][2 * kc + half], qf[kc], acc); // node row col, query column col
+                __syncthreads(); // every wave has read the means: the area takes the priorities
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
                     const int row = acc_row(rr, half);
@@ -590,7 +598,9 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
                 }
                 wave_lds_sync();
                 for (int e = half; e < sm.nk[qs]; e += 2) {
-                    const int u = sm.kidx[qs][e] - t0;
+                    // the child's position in the level's node list
+                    const int l = local_of(child_of(sm.kpar[qs][e >> 1], e & 1));
+                    const int u = wb[l >> 5] + __popc(bm[l >> 5] & ((1u << (l & 31)) - 1u)) - t0;
                     if (u >= 0 && u < 32) {
                         sm.ku[qs][e] = sm.ut[wave][u][col];
                         sm.kmin[qs][e] = (uint16_t)sm.tmin[u];
@@ -629,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
 #pragma unroll
                     for (int e = 0; e < kFsbMaxBeam; ++e)
                         if (e < keep && top[e] != 0ull)
-                            sm.beam[qs][nb2++] = sm.kref[qs][(int)(top[e] & 0xffffu)];
+                            sm.beam[qs][nb2++] = child_of(sm.kpar[qs][(int)(top[e] & 0xffffu) >> 1], (int)(top[e] & 1u));
                     sm.nb[qs] = nb2;
                 }
             }
@@ -644,9 +654,9 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
                 const int32_t cell = node_meta[sm.cbase[ct] + (ref & 0xffff) - 1].cell;
                 bool dup = false;
                 for (int x = 0; x < nc; ++x)
-                    dup |= sm.cand[qs][x] == cell;
+                    dup |= (int32_t)sm.cand[qs][x] == cell;
                 if (!dup)
-                    sm.cand[qs][nc++] = cell;
+                    sm.cand[qs][nc++] = (uint16_t)cell; // cell ids < kFsbMaxCells
             }
             sm.ncand[qs] = nc;
         }
@@ -656,12 +666,12 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
     // ---- candidates in ascending id order; their union over the block ----
     const int mwords = (int)((n_avail + 31) / 32);
     for (int x = t; x < mwords; x += kThreads)
-        sm.bm[x] = 0u;
+        bm[x] = 0u;
     __syncthreads();
     if (half == 0) {
         const int nc = sm.ncand[qs];
         for (int x = 1; x < nc; ++x) {
-            const int32_t v = sm.cand[qs][x];
+            const uint16_t v = sm.cand[qs][x];
             int y = x - 1;
             while (y >= 0 && sm.cand[qs][y] > v) {
                 sm.cand[qs][y + 1] = sm.cand[qs][y];
@@ -670,25 +680,25 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
             sm.cand[qs][y + 1] = v;
         }
         for (int x = 0; x < nc; ++x)
-            atomicOr(&sm.bm[sm.cand[qs][x] >> 5], 1u << (sm.cand[qs][x] & 31));
+            atomicOr(&bm[sm.cand[qs][x] >> 5], 1u << (sm.cand[qs][x] & 31));
     }
     __syncthreads();
     if (t == 0) {
         int32_t run = 0;
         for (int x = 0; x < mwords; ++x) {
-            sm.wb[x] = run;
-            run += __popc(sm.bm[x]);
+            wb[x] = run;
+            run += __popc(bm[x]);
         }
         sm.nlist = run;
     }
     __syncthreads();
     for (int x = t; x < mwords; x += kThreads) {
-        uint32_t bits = sm.bm[x];
-        int32_t pos = sm.wb[x];
+        uint32_t bits = bm[x];
+        int32_t pos = wb[x];
         while (bits) {
             const int b = __ffs(bits) - 1;
             bits &= bits - 1;
-            sm.list[pos++] = (uint16_t)(x * 32 + b);
+            list[pos++] = (uint16_t)(x * 32 + b);
         }
     }
     __syncthreads();
@@ -710,7 +720,7 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
     const int Zc = sm.nlist;
     const T *kh = k + bh * N * D;
     for (int u = 0; u < Zc; ++u) {
-        const int32_t c = sm.list[u];
+        const int32_t c = list[u];
         if constexpr (kBf16) { // the cell's 32 token keys, 16 bytes per thread
             const uint16_t *src = reinterpret_cast<const uint16_t *>(kh) + (int64_t)c * 32 * D;
             for (int x = t; x < 32 * D / 8; x += kThreads) {
@@ -741,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
         // is c one of this query's candidates? (sorted list, at most 2 Wb)
         bool mine = false;
         for (int x = 0; x < nc; ++x)
-            mine |= sm.cand[qs][x] == c;
+            mine |= (int32_t)sm.cand[qs][x] == c;
         float m = -INFINITY;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
@@ -768,7 +778,7 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
         if (cand) {
             int32_t *cd = cand + (bh * N + i) * 2 * Wb;
             for (int x = 0; x < 2 * Wb; ++x)
-                cd[x] = x < nc ? sm.cand[qs][x] : -1;
+                cd[x] = x < nc ? (int32_t)sm.cand[qs][x] : -1;
         }
     }
 }
@@ -784,7 +794,8 @@ hipError_t launch_t(const Geometry &g, const FsbLayout &L, const HeadConsts &hc,
     if (L.Mu > 0)
         hipLaunchKernelGGL((fsb_build_kernel<D>), dim3((unsigned)((int64_t)g.bh * 2 * L.chunks)),
                            dim3(kBuildThreads), 0, st, kbar64, a, adm, adm_count, node_mu, node_meta, g.M, L);
-    hipLaunchKernelGGL((fsb_search_kernel<T, D>), dim3((unsigned)((int64_t)g.bh * g.NB)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((fsb_search_kernel<T, D>), dim3((unsigned)((int64_t)g.bh * g.NB)), dim3(kThreads),
+                       fsb_search_lds(L.Mu), st,
                        static_cast<const T *>(q), static_cast<const T *>(k), a, adm_count, node_mu, node_meta, sel,
                        cand, hc, fc, L, g.N, g.M, g.NB, g.H, g.K);
     return hipGetLastError();
