@@ -328,6 +328,9 @@ inline size_t fsb_search_lds(int64_t Mu)
 
 template <typename T, int D>
 struct SearchSmem {
+    // bf16 queries read a node mean 8 features at a time (16-byte aligned rows; 4 words
+    // of pad put 16 consecutive rows on distinct banks); fp32 ones one feature per lane
+    static constexpr int kMuStride = sizeof(T) == 2 ? D + 4 : D + 1;
     int32_t beam[128][kFsbMaxBeam]; // node refs of each query's beam
     int32_t nb[128];
     int32_t nk[128], nleaf[128];
@@ -338,7 +341,7 @@ struct SearchSmem {
     int32_t ncand[128];
     int32_t nlist;
     union {
-        float mu[32][D + 1];      // a tile of node means
+        float mu[32][kMuStride];  // a tile of node means
         float ut[kWaves][32][33]; // then the tile's priorities: [wave][node row][query column]
         uint16_t kt16[32][D + 8];
         float kt32[32][D + 1];
@@ -357,8 +360,12 @@ struct SearchSmem {
     int32_t r;
 };
 
+// bf16 queries: two workgroups per CU (at most 256 VGPRs, 80 KB of LDS at 16k tokens)
+template <typename T>
+constexpr int kSearchWavesPerSimd = sizeof(T) == 2 ? 2 : 1;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                               const float *__restrict__ a,
                                                               const int32_t *__restrict__ cnt,
                                                               const float *__restrict__ node_mu,
@@ -388,20 +395,33 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
     const int Wb = fc.Wb;
     const int64_t n_avail = ((int64_t)beta * 128 / 32) < L.Mu ? ((int64_t)beta * 128 / 32) : L.Mu;
 
-    // ---- the query in the layouts of the two products ----
+    // ---- the query as the B operand of the products: bf16, features 16 kc + 8 half .. + 7
+    // (32x32x16); fp32, feature 2 kc + half (32x32x2) ----
     const T *qrow = q + (bh * N + (q_ok ? i : 0)) * D;
-    float qf[D / 2]; // fp32 32x32x2 B operand: feature 2 kc + half
-#pragma unroll
-    for (int kc = 0; kc < D / 2; ++kc) {
-        if constexpr (kBf16)
-            qf[kc] = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(qrow)[2 * kc + half]);
-        else
-            qf[kc] = qrow[2 * kc + half];
-    }
+    constexpr int KB = kBf16 ? D / 16 : 1;
+    constexpr int KF = kBf16 ? 1 : D / 2;
+    bf16x8 qb[KB];
+    float qf[KF];
     float qsq = 0.0f;
+    if constexpr (kBf16) {
 #pragma unroll
-    for (int kc = 0; kc < D / 2; ++kc)
-        qsq = fmaf(qf[kc], qf[kc], qsq);
+        for (int kc = 0; kc < KB; ++kc) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qrow) + kc * 16 + half * 8);
+            qb[kc] = as_bf16x8(w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t we = w[e];
+                const float x0 = bf16_bits_to_f32(we & 0xffffu), x1 = bf16_bits_to_f32(we >> 16);
+                qsq = fmaf(x1, x1, fmaf(x0, x0, qsq));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kc = 0; kc < KF; ++kc) {
+            qf[kc] = qrow[2 * kc + half];
+            qsq = fmaf(qf[kc], qf[kc], qsq);
+        }
+    }
     qsq += shfl_xor_f(qsq, 32);
     const float qnorm = sqrtf(qsq);
 
@@ -584,9 +604,35 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr)
                     acc[rr] = 0.0f;
+                if constexpr (kBf16) {
+                    // q . mu with mu as bf16 hi + mid + lo parts (exactly the fp32 mean) and the
+                    // products added in one fp32 accumulator, smallest part first in each step
 #pragma unroll
-                for (int kc = 0; kc < D / 2; ++kc)
-                    acc = mfma_f32(sm.mu[col][2 * kc + half], qf[kc], acc); // node row col, query column col
+                    for (int kc = 0; kc < KB; ++kc) {
+                        const float *mrow = &sm.mu[col][kc * 16 + half * 8]; // node row col
+                        const u32x4 m0 = *reinterpret_cast<const u32x4 *>(mrow);
+                        const u32x4 m1 = *reinterpret_cast<const u32x4 *>(mrow + 4);
+                        u32x4 ph, pm, pl;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const float x0 = __uint_as_float(w < 2 ? m0[2 * w] : m1[2 * w - 4]);
+                            const float x1 = __uint_as_float(w < 2 ? m0[2 * w + 1] : m1[2 * w - 3]);
+                            const uint32_t hp = cvt_pk_bf16(x0, x1);
+                            const float r0 = x0 - __uint_as_float(hp << 16), r1 = x1 - __uint_as_float(hp & 0xffff0000u);
+                            const uint32_t mp = cvt_pk_bf16(r0, r1);
+                            ph[w] = hp;
+                            pm[w] = mp;
+                            pl[w] = cvt_pk_bf16(r0 - __uint_as_float(mp << 16), r1 - __uint_as_float(mp & 0xffff0000u));
+                        }
+                        acc = mfma_bf16(as_bf16x8(pl), qb[kc], acc);
+                        acc = mfma_bf16(as_bf16x8(pm), qb[kc], acc);
+                        acc = mfma_bf16(as_bf16x8(ph), qb[kc], acc);
+                    }
+                } else {
+#pragma unroll
+                    for (int kc = 0; kc < KF; ++kc)
+                        acc = mfma_f32(sm.mu[col][2 * kc + half], qf[kc], acc); // node row col, query column col
+                }
                 __syncthreads(); // every wave has read the means: the area takes the priorities
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
@@ -704,14 +750,6 @@ __global__ __launch_bounds__(kThreads, 1) void fsb_search_kernel(const T *__rest
     __syncthreads();
 
     // ---- rerank (Eq. 12): one candidate cell at a time, all queries on the matrix cores ----
-    constexpr int KB = kBf16 ? D / 16 : 1;
-    bf16x8 qb[KB];
-    if constexpr (kBf16) {
-#pragma unroll
-        for (int kc = 0; kc < KB; ++kc)
-            qb[kc] = as_bf16x8(*reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(qrow) + kc * 16 +
-                                                                half * 8));
-    }
     uint64_t topk[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
