@@ -515,11 +515,15 @@ def run_fsb(args) -> int:
     flop = search_flop + rerank_flop + read_flop
     M = N // prm.s
     alg_bytes = 4 * b * H * N * d * 2 + b * H * M * d * (4 + 8) * 2 + b * H * 2 * (2 * M) * (d * 4 + 16) * 2
-    roofline = {"bound": "mfma", "achieved": round(flop / (ms * 1e-3) / 1e12, 2), "peak": 157.3, "unit": "TFLOP/s",
-                "frac": round(flop / (ms * 1e-3) / 1e12 / 157.3, 4), "traffic": None, "kernel": "fs_fsb_prefill",
+    # bf16 inputs: node priorities (three bf16 products per mean), the rerank and the readout
+    # all run on the bf16 matrix cores, so the bf16 dense peak bounds the call
+    peak = MFMA_BF16_PEAK_TFLOPS
+    roofline = {"bound": "mfma", "achieved": round(flop / (ms * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(flop / (ms * 1e-3) / 1e12 / peak, 4), "traffic": None, "kernel": "fs_fsb_prefill",
                 "alg_flop_per_launch": flop, "alg_bytes_per_launch": int(alg_bytes),
                 "hbm_frac_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "note": "fp32 matrix-core peak (node priorities); all kernels of the call"}
+                "note": "bf16 dense matrix-core peak on the page's algorithmic FLOPs; all kernels of the call; "
+                        "the search is latency-bound (serial steps per level, two workgroups per CU)"}
 
     cpu = parity = None
     if not args.no_cpu_baseline:
