@@ -111,16 +111,21 @@ __global__ __launch_bounds__(kBuildThreads) void fsb_build_kernel(const double *
     __shared__ int32_t perm[kFsbMaxCells];
     __shared__ double key[kFsbMaxCells];
 
+    // the largest chunks first: a chunk's build is a chain that grows with its size (the
+    // 2^k-cell root alone takes 2^k cells through every pass), so the longest chains start
+    // at once and the many small chunks fill the CUs around them
+    const int64_t groups = (int64_t)gridDim.x / L.chunks; // (sequence, head, forest) triples
     int64_t w = blockIdx.x;
-    const int64_t per = 2 * L.chunks;
-    const int64_t bh = w / per;
-    w -= bh * per;
-    const int f = (int)(w / L.chunks);
-    w -= (int64_t)f * L.chunks;
-    int k = 0;
-    while (k + 1 < L.levels && w >= L.chunk_base[k + 1])
-        ++k;
-    const int64_t jj = w - L.chunk_base[k];
+    int k = L.levels - 1;
+    int64_t ck = L.chunk_base[k + 1] - L.chunk_base[k]; // chunks of 2^k cells per forest
+    while (w >= ck * groups) {
+        w -= ck * groups;
+        --k;
+        ck = L.chunk_base[k + 1] - L.chunk_base[k];
+    }
+    const int64_t grp = w / ck, jj = w - grp * ck;
+    const int64_t bh = grp / 2;
+    const int f = (int)(grp - bh * 2);
     const int64_t n = (int64_t)1 << k, start = 2 * jj * n;
     const int64_t Mf = f == 0 ? L.Mu : cnt[bh * (M + 1) + L.Mu];
     if (start + n > Mf)
