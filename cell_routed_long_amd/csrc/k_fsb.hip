@@ -17,13 +17,18 @@
 //     node: fp64 mean, farthest cell, two power iterations (Eq. 19), then the
 //     node's cells are sorted by their projection in LDS (bitonic) and halved;
 //     node summaries (Eq. 20) are written heap-ordered, mean keys as fp32.
+//     The chunks are taken largest first (the longest chains start at once).
 //   * fsb_search_kernel: one workgroup per (sequence, head, 128-query block).
 //     It forms the block's join nodes (Eq. 21) from its chunks' roots and runs
 //     the 128 beams level-synchronously: each level the children of every
 //     query's internal beam nodes are collected into one list (an LDS bitmap
 //     over the block's forest nodes dedupes them), scored for all 128 queries
-//     32 nodes at a time on the fp32 matrix cores (the q . mu term of Eq. 11),
-//     and each query keeps its leaves plus its best W^b - #leaves children.
+//     32 nodes at a time on the matrix cores (the q . mu term of Eq. 11: bf16
+//     queries against each fp32 mean's bf16 hi + mid + lo parts, fp32 queries
+//     on the fp32 products), and each query keeps its leaves plus its best
+//     W^b - #leaves children (a bitonic sort and merge over the query's lane
+//     pair).  The level's node list is dynamic LDS sized by the forest, so a
+//     bf16 search fits two workgroups on a CU at moderate lengths.
 //     The union of the leaves reached is then reranked cell by cell: a cell's
 //     32 token keys are staged once and the logits of all 128 queries come
 //     from the matrix cores; each query that has the cell as a candidate takes

@@ -10,8 +10,10 @@
 //             |A_beta| and the retained list are requested together;
 //   routing   the retained mean keys (bf16 hi/mid/lo parts from the summary
 //             pass) are staged 32 cells at a time, the next tile in flight
-//             while the matrix cores score the current one; each lane keeps its
-//             query's top-K in registers, exactly as fs_score_select does;
+//             while the matrix cores score the current one (once the first
+//             tile's keys show that the tile bound will not pass over it);
+//             each lane keeps its query's top-K in registers, exactly as
+//             fs_score_select does;
 //   union     the selections go to LDS (and, if asked, to global memory) and
 //             the block's distinct selected cells are listed in id order;
 //   readout   each listed cell's keys and values are gathered once into LDS
