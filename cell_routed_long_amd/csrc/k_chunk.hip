@@ -91,6 +91,9 @@ __global__ __launch_bounds__(kThreads) void chunk_block_kernel(char *__restrict_
     __shared__ int32_t n_u, s_cur, s_newslot[kCpb];
     __shared__ double s_rowmax[kCpb][kWaves];
     __shared__ __attribute__((aligned(16))) uint16_t s_kbs[kMaxSlots * 3 * kPartStride<D>]; // the slots' parts
+    // the tile bound: every slot's |kbar| (and by scoring row), and per 32-row tile the
+    // largest lambda a_c and |kbar_c| (infinite where a value is not finite)
+    __shared__ float s_kn[kMaxSlots], s_knr[kMaxSlots], s_tpr[kMaxSlots / 32], s_tkn[kMaxSlots / 32];
 
     constexpr int KC = D / 16;   // k-steps of the bf16 matrix products
     constexpr int PS = kPartStride<D>;
@@ -141,6 +144,16 @@ __global__ __launch_bounds__(kThreads) void chunk_block_kernel(char *__restrict_
         *reinterpret_cast<uint32_t *>(s_kbs + (3 * x + 0) * PS + f) = hi;
         *reinterpret_cast<uint32_t *>(s_kbs + (3 * x + 1) * PS + f) = mid;
         *reinterpret_cast<uint32_t *>(s_kbs + (3 * x + 2) * PS + f) = lo;
+    }
+    if (t < L.S) { // the slot's |kbar| (slots without a summary yet: stale, unread until it completes)
+        float ss = 0.0f;
+        for (int f = 0; f < D; f += 4) {
+            const u32x4 m4 = *reinterpret_cast<const u32x4 *>(R.kbar + (int64_t)t * D + f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ss = fmaf(__uint_as_float(m4[e]), __uint_as_float(m4[e]), ss);
+        }
+        s_kn[t] = sqrtf(ss);
     }
     const int64_t i0 = mv.pos;
     int n_ret = mv.n_ret < 0 ? 0 : (mv.n_ret > L.S ? L.S : mv.n_ret);
@@ -207,31 +220,93 @@ __global__ __launch_bounds__(kThreads) void chunk_block_kernel(char *__restrict_
         }
         __syncthreads();
         const int nA = n_ret;
-        if (t < kMaxSlots) { // position t of A, or a padding row of the last tile
-            const bool in = t < nA;
-            const int slot = in ? s_Aslot[t] : 0;
-            sm.prior[t] = in ? lam * s_a[slot] : 0.0f;
-            // (padding rows sit far before the block: they never call for erf)
-            sm.pc[t] = in ? (float)((int64_t)s_Acell[t] * kS + kS / 2 - q0) : -1.0e9f;
-            sm.id[t] = in ? 0x7fffffff - t : -1;
-            sm.pslot[t] = slot;
-        }
-        __syncthreads();
         const int64_t qi = q0 + wave * 32 + col; // this lane's query position
         const bool q_ok = qi >= seg && qi < seg_end;
         const float qrel = (float)(qi - q0); // positions relative to the block start: exact
-        bf16x8 qf[KC];
+        bf16x8 qf[KC]; // requested here: the loads are in flight while A is ordered below
         {
             const uint16_t *qrow = q + (bh * n + ((q_ok ? qi : seg) - i0)) * D;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
                 qf[kc] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + kc * 16 + half * 8));
         }
+        // Scoring takes A in priority order (a_c desc, id asc: the order of the prefill's
+        // retained lists), so that the first tile holds the largest priors and the tile
+        // bound below can pass over the rest.  A row keeps its position in A (ascending
+        // id) as the low half of its ranking key, so selections, the union and the readout
+        // are exactly those of scoring in position order (a score does not depend on the
+        // tile its row sits in).
+        if (t < kMaxSlots)
+            s_key[t] = t < nA ? norm_key(s_a[s_Aslot[t]], s_Acell[t]) : 0ull;
+        __syncthreads();
+        if (t < kMaxSlots) { // position t of A, or a padding row of the last tile
+            const bool in = t < nA;
+            const int slot = in ? s_Aslot[t] : 0;
+            const int row = in ? count_greater(s_key, (nA + 7) & ~7, s_key[t]) : t; // its priority rank
+            sm.prior[row] = in ? lam * s_a[slot] : 0.0f;
+            // (padding rows sit far before the block: they never call for erf)
+            sm.pc[row] = in ? (float)((int64_t)s_Acell[t] * kS + kS / 2 - q0) : -1.0e9f;
+            sm.id[row] = in ? 0x7fffffff - t : -1;
+            sm.pslot[row] = slot;
+            s_knr[row] = in ? s_kn[slot] : 0.0f;
+        }
+        __syncthreads();
+        if (t < kMaxSlots) { // per 32-row tile: the largest lambda a_c and |kbar_c|
+            float pr = sm.prior[t], kn = s_knr[t];
+            pr = pr <= FLT_MAX ? pr : INFINITY; // NaN or infinite: the tile is never passed over
+            kn = kn <= FLT_MAX ? kn : INFINITY;
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) {
+                pr = fmaxf(pr, shfl_xor_f(pr, o));
+                kn = fmaxf(kn, shfl_xor_f(kn, o));
+            }
+            if ((t & 31) == 0) {
+                s_tpr[t >> 5] = pr;
+                s_tkn[t >> 5] = kn;
+            }
+        }
+        __syncthreads();
         uint64_t kl[KT]; // this lane's best keys so far
 #pragma unroll
         for (int j = 0; j < KT; ++j)
             kl[j] = 0;
+        // Tile bound, per wave: every score in a tile is at most
+        //   max_c (lambda a_c) + max_i |q_i| max_c |kbar_c| / sqrt(d)
+        // (lambda a_c >= 0 and 0 < g <= 1 for every available cell, Cauchy-Schwarz on the
+        // content term), widened for rounding.  Once it falls below the smallest K-th best
+        // key of the wave's queries so far, no cell of the tile can enter any of their
+        // top-K lists and the wave passes over the tile: the selections are those of
+        // scoring every tile.  The first tile is always scored.
+        float qn_w;
+        {
+            float ss = 0.0f;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const u32x4 w4 = __builtin_bit_cast(u32x4, qf[kc]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // the element goes through a named copy: hipcc miscompiles a bit cast
+                    // of a vector element taken in place (it reads element 0)
+                    const uint32_t we = w4[e];
+                    const bf16x2 x2 = __builtin_bit_cast(bf16x2, we);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, ss, false);
+                }
+            }
+            ss += shfl_xor_f(ss, 32); // the partner lane holds the other half of the features
+            // + 2^-100: covers subnormal elements, should the dot product flush them
+            const float qn = q_ok ? sqrtf(ss) * (1.0f + 0x1p-10f) + 0x1p-100f : 0.0f;
+            const bool badq = __ballot(!(qn <= FLT_MAX)) != 0ull;
+            qn_w = badq ? INFINITY : wave_max_f(qn);
+        }
+        uint32_t tau_w = 0; // the wave's smallest K-th best key (high word) so far
         for (int t0 = 0; t0 < nA; t0 += 32) {
+            if (t0 > 0) {
+                const float ub = (s_tpr[t0 >> 5] + qn_w * s_tkn[t0 >> 5] * inv_sqrt_d * (1.0f + 0x1p-10f)) *
+                                 (1.0f + 0x1p-10f);
+                // ub >= 0: its ranking key's high word is its bits with the sign bit set
+                if (ub <= FLT_MAX && (__float_as_uint(ub) | 0x80000000u) < tau_w)
+                    continue; // wave-uniform
+            }
             const uint16_t *kbrow = s_kbs + 3 * sm.pslot[t0 + col] * PS; // the tile row this lane's operand reads
             f32x16 acc;
             f32x16 acc3[3];
@@ -292,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void chunk_block_kernel(char *__restrict_
                 }
             }
             take_tile_keys<KT>(kl, key, t0 == 0);
+            tau_w = wave_min_u32(q_ok ? (uint32_t)(kl[KT - 1] >> 32) : 0xffffffffu);
         }
         { // merge with the partner lane (same query, other 16 rows of every tile)
             uint64_t pk[KT];
@@ -601,6 +677,27 @@ __global__ __launch_bounds__(kThreads) void chunk_block_kernel(char *__restrict_
                                                       fmax(s_rowmax[t][2], s_rowmax[t][3])));
                     R.a[slot] = av;
                     s_a[slot] = av;
+                }
+            }
+            __syncthreads();
+            // the completed cells' |kbar|, one wave per cell, from its parts (hi + mid + lo =
+            // the mean; the tile bound only needs it to about 2^-10)
+            static_assert(kCpb <= kWaves, "a wave per completed cell");
+            if (wave < n_done) {
+                const int slot = slot_of(cdone[wave]);
+                if (slot >= 0 && slot < L.S) {
+                    float ss = 0.0f;
+                    for (int f = lane; f < D; f += kWave) {
+                        const float m = (bf16_bits_to_f32(s_kbs[(3 * slot + 0) * PS + f]) +
+                                         bf16_bits_to_f32(s_kbs[(3 * slot + 1) * PS + f])) +
+                                        bf16_bits_to_f32(s_kbs[(3 * slot + 2) * PS + f]);
+                        ss = fmaf(m, m, ss);
+                    }
+#pragma unroll
+                    for (int o = 1; o < kWave; o <<= 1)
+                        ss += shfl_xor_f(ss, o);
+                    if (lane == 0)
+                        s_kn[slot] = sqrtf(ss);
                 }
             }
             __syncthreads();
