@@ -503,6 +503,18 @@ __global__ __launch_bounds__(kThreads) void chunk_block_kernel(char *__restrict_
             }
         }
 
+        // the block's key and value rows for the state, requested now so that they arrive
+        // while the output goes out; stored into their slots below
+        constexpr int kIt = (kB * CPR) / kThreads;
+        u32x4 rk[kIt], rv[kIt];
+#pragma unroll
+        for (int u = 0; u < kIt; ++u) {
+            const int e = t + u * kThreads;
+            const int64_t tok = seg + e / CPR < seg_end ? seg + e / CPR : seg_end - 1;
+            const int64_t src = (bh * n + (tok - i0)) * D + (e % CPR) * 8;
+            rk[u] = *reinterpret_cast<const u32x4 *>(kin + src);
+            rv[u] = *reinterpret_cast<const u32x4 *>(vin + src);
+        }
         // normalise, RMSNorm over d (Eq. 17), the chunk's rows out through LDS
         const float c = rms_factor<DT>(o_acc, l_run, eps);
         __syncthreads(); // the last cell's LDS reads are done: the tile area takes the output
@@ -574,17 +586,7 @@ __global__ __launch_bounds__(kThreads) void chunk_block_kernel(char *__restrict_
         auto slot_of = [&](int64_t cell) { // -1 when the state had no free slot (a corrupted state)
             return cell >= c_first ? s_newslot[(int)(cell - c_first)] : cur_before;
         };
-        { // the rows: every load first, then the stores
-            constexpr int kIt = (kB * CPR) / kThreads;
-            u32x4 rk[kIt], rv[kIt];
-#pragma unroll
-            for (int u = 0; u < kIt; ++u) {
-                const int e = t + u * kThreads;
-                const int64_t tok = seg + e / CPR < seg_end ? seg + e / CPR : seg_end - 1;
-                const int64_t src = (bh * n + (tok - i0)) * D + (e % CPR) * 8;
-                rk[u] = *reinterpret_cast<const u32x4 *>(kin + src);
-                rv[u] = *reinterpret_cast<const u32x4 *>(vin + src);
-            }
+        { // the rows (requested before the output tile, above): the stores
 #pragma unroll
             for (int u = 0; u < kIt; ++u) {
                 const int e = t + u * kThreads;
