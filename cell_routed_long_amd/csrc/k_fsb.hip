@@ -358,7 +358,7 @@ struct SearchSmem {
     };
     float trho[32], tA[32];
     int32_t tmin[32];
-    float jmu[kMaxChunksPerForest][D];
+    alignas(16) float jmu[kMaxChunksPerForest][D];
     FsbNodeMeta jmeta[kMaxChunksPerForest];
     int32_t jcount[kMaxChunksPerForest];
     double red[2][kThreads / kWave];
@@ -600,9 +600,16 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                             meta = node_meta[gi];
                         }
                     }
+                    // 16-byte loads (node and join means are rows of D floats, 16-byte aligned)
 #pragma unroll
-                    for (int e = 0; e < FP; ++e)
-                        sm.mu[row][part * FP + e] = src ? src[part * FP + e] : 0.0f;
+                    for (int e = 0; e < FP; e += 4) {
+                        const float4 v4 = src ? *reinterpret_cast<const float4 *>(src + part * FP + e)
+                                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                        sm.mu[row][part * FP + e] = v4.x;
+                        sm.mu[row][part * FP + e + 1] = v4.y;
+                        sm.mu[row][part * FP + e + 2] = v4.z;
+                        sm.mu[row][part * FP + e + 3] = v4.w;
+                    }
                     if (part == 0) {
                         sm.trho[row] = meta.rho;
                         sm.tA[row] = meta.A;
