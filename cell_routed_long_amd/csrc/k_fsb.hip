@@ -774,14 +774,30 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
     const int nc = sm.ncand[qs];
     const int Zc = sm.nlist;
     const T *kh = k + bh * N * D;
+    // bf16: a cell's 32 token keys, 16 bytes per thread, the next cell's in flight while the
+    // current one is on the matrix cores
+    constexpr int KR = kBf16 ? (32 * D / 8 + kThreads - 1) / kThreads : 1;
+    u32x4 pre[KR];
+    auto fetch_keys = [&](int32_t c) {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(kh) + (int64_t)c * 32 * D;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            const int x = t + r * kThreads;
+            if (x < 32 * D / 8)
+                pre[r] = *reinterpret_cast<const u32x4 *>(src + (int64_t)(x / (D / 8)) * D + (x % (D / 8)) * 8);
+        }
+    };
+    if (kBf16 && Zc > 0)
+        fetch_keys(list[0]);
+    int cp = 0; // this lane's place in its candidates (both lists ascend)
     for (int u = 0; u < Zc; ++u) {
         const int32_t c = list[u];
-        if constexpr (kBf16) { // the cell's 32 token keys, 16 bytes per thread
-            const uint16_t *src = reinterpret_cast<const uint16_t *>(kh) + (int64_t)c * 32 * D;
-            for (int x = t; x < 32 * D / 8; x += kThreads) {
-                const int row = x / (D / 8), c8 = (x % (D / 8)) * 8;
-                *reinterpret_cast<u32x4 *>(&sm.kt16[row][c8]) =
-                    *reinterpret_cast<const u32x4 *>(src + (int64_t)row * D + c8);
+        if constexpr (kBf16) {
+#pragma unroll
+            for (int r = 0; r < KR; ++r) {
+                const int x = t + r * kThreads;
+                if (x < 32 * D / 8)
+                    *reinterpret_cast<u32x4 *>(&sm.kt16[x / (D / 8)][(x % (D / 8)) * 8]) = pre[r];
             }
         } else {
             const float *src = reinterpret_cast<const float *>(kh) + (int64_t)c * 32 * D;
@@ -789,6 +805,8 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                 sm.kt32[x / D][x % D] = src[x];
         }
         __syncthreads();
+        if (kBf16 && u + 1 < Zc)
+            fetch_keys(list[u + 1]);
         f32x16 acc;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
@@ -803,10 +821,10 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
             for (int kc = 0; kc < D / 2; ++kc)
                 acc = mfma_f32(sm.kt32[col][2 * kc + half], qf[kc], acc);
         }
-        // is c one of this query's candidates? (sorted list, at most 2 Wb)
-        bool mine = false;
-        for (int x = 0; x < nc; ++x)
-            mine |= (int32_t)sm.cand[qs][x] == c;
+        // is c one of this query's candidates? (sorted, at most 2 Wb; the cells come ascending)
+        while (cp < nc && (int32_t)sm.cand[qs][cp] < c)
+            ++cp;
+        const bool mine = cp < nc && (int32_t)sm.cand[qs][cp] == c;
         float m = -INFINITY;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
