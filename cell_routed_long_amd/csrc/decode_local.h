@@ -103,24 +103,28 @@ struct Shape {
     static_assert(FPL % 2 == 0, "whole feature pairs per lane");
 };
 
-// The groups' softmax partials (a group without rows has m = -inf and weight 0).
+// The groups' softmax partials (a group without rows has m = -inf and weight 0)
+// and the logit of offset 0, the step's own token (exp2 domain).
 template <int D>
 struct Smem {
     float m[kGroups], l[kGroups];
     float acc[kGroups][D + 1];
+    float x0;
 };
 
 // What a thread loads at the start of its part of a step: the header, the
-// position, its lane's features of q, k_new and v_new, the (cos, sin) of
-// theta_m and of w theta_m for its feature pairs, and the new key and value of
-// the feature te it finishes in the combination.  Nothing here waits for memory.
+// position, its lane's features of q and k_new, the (cos, sin) of theta_m and
+// of w theta_m for its feature pairs, and the new key and value of the feature
+// te it finishes in the combination.  Nothing here waits for memory.  (The new
+// token's value enters only in the combination, through vn_t, so no value row
+// stays live across a group's ring loop.)
 template <typename T, int D>
 struct Entry {
     LocalStateHeader hv;
     int64_t i;
     char *rec;
     const char *tab;
-    uint32_t qr[Shape<T, D>::NDW], kr0[Shape<T, D>::NDW], vr0[Shape<T, D>::NDW];
+    uint32_t qr[Shape<T, D>::NDW], kr0[Shape<T, D>::NDW];
     uint32_t stp[Shape<T, D>::FPL], cw[Shape<T, D>::FPL];
     T kn_t, vn_t;
 };
@@ -142,7 +146,6 @@ __device__ __forceinline__ Entry<T, D> step_entry(char *__restrict__ state, cons
     e.i = *reinterpret_cast<const int64_t *>(e.rec);
     load_dwords<S::NDW>(reinterpret_cast<const char *>(q + bh * D) + lane_off, e.qr);
     load_dwords<S::NDW>(reinterpret_cast<const char *>(k_new + bh * D) + lane_off, e.kr0);
-    load_dwords<S::NDW>(reinterpret_cast<const char *>(v_new + bh * D) + lane_off, e.vr0);
     load_dwords<S::FPL>(e.tab + (w > 0 ? 1 : 0) * S::NP * (int64_t)sizeof(float2), e.stp); // (cos, sin) of theta_m
     load_dwords<S::FPL>(e.tab + w * S::NP * (int64_t)sizeof(float2), e.cw);                // of w theta_m
     e.kn_t = k_new[bh * D + te];
@@ -296,23 +299,15 @@ __device__ __forceinline__ void step_group(const Entry<T, D> &e, const LocalStat
         acc[y] += acc_t[y];
     l += l_t;
 
-    // offset 0, the step's own token, joins group 0's softmax
-    {
+    // offset 0, the step's own token: group 0 leaves its logit for the combination
+    if (grp == 0) {
         float dot = 0.0f;
 #pragma unroll
         for (int y = 0; y < FPL; ++y)
             dot = fmaf(feature<T, NDW>(e.qr, y), feature<T, NDW>(e.kr0, y), dot);
         dot = row16_sum(dot);
-        if (grp == 0) {
-            const float x0 = dot * scale;
-            const float mx = fmaxf(m, x0);
-            const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mx), p0 = __builtin_amdgcn_exp2f(x0 - mx);
-            l = fmaf(l, f, p0);
-#pragma unroll
-            for (int y = 0; y < FPL; ++y)
-                acc[y] = fmaf(acc[y], f, p0 * feature<T, NDW>(e.vr0, y));
-            m = mx;
-        }
+        if (part == 0)
+            sm.x0 = dot * scale;
     }
 
 #pragma unroll
@@ -326,9 +321,10 @@ __device__ __forceinline__ void step_group(const Entry<T, D> &e, const LocalStat
 
 // After every group's partials are in sm: thread c of the step's 512 (TPF
 // adjacent lanes per feature te = c / TPF, each combining GPT groups, then
-// added up by DPP) finishes feature te: out = o_sr + alpha * olr when combine
-// is set, else o_sr; then the new token enters the ring and the position
-// advances.  A header that does not match `expect` gives NaN and leaves the
+// added up by DPP) finishes feature te, the step's own token joining as one
+// more term (logit sm.x0, value v_new[te]): out = o_sr + alpha * olr when
+// combine is set, else o_sr; then the new token enters the ring and the
+// position advances.  A header that does not match `expect` gives NaN and leaves the
 // record alone.
 template <typename T, int D>
 __device__ __forceinline__ void step_finish(const Entry<T, D> &e, const LocalStateLayout &L,
@@ -338,9 +334,10 @@ __device__ __forceinline__ void step_finish(const Entry<T, D> &e, const LocalSta
     using S = Shape<T, D>;
     constexpr int TPF = S::TPF, GPT = S::GPT;
     const int te = c / TPF, sub = c % TPF;
-    float M = sm.m[0]; // group 0 holds offset 0, so M is finite
+    const float x0 = sm.x0;
+    float M = x0; // offset 0 is always in the window, so M is finite
 #pragma unroll
-    for (int g = 1; g < kGroups; ++g)
+    for (int g = 0; g < kGroups; ++g)
         M = fmaxf(M, sm.m[g]);
     float z = 0.0f, u = 0.0f;
 #pragma unroll
@@ -358,6 +355,9 @@ __device__ __forceinline__ void step_finish(const Entry<T, D> &e, const LocalSta
         z += dpp_f<0x141>(z); // row_half_mirror: the two quads of each 8-lane half
         u += dpp_f<0x141>(u);
     }
+    const float p0 = __builtin_amdgcn_exp2f(x0 - M);
+    z += p0;
+    u = fmaf(p0, to_f32<T>(e.vn_t), u);
 
     const LocalStateHeader &hv = e.hv;
     const int64_t w = L.w, i = e.i;
