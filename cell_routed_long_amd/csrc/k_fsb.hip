@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void fsb_admit_kernel(const double *__res
 constexpr int kBuildThreads = 512;
 
 template <int D>
-__global__ __launch_bounds__(kBuildThreads) void fsb_build_kernel(const double *__restrict__ kbar64,
+__global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const double *__restrict__ kbar64,
                                                                const float *__restrict__ a,
                                                                const int32_t *__restrict__ adm,
                                                                const int32_t *__restrict__ cnt,
@@ -159,26 +159,66 @@ __global__ __launch_bounds__(kBuildThreads) void fsb_build_kernel(const double *
                     node_meta[node] = FsbNodeMeta{0.0f, ah[c], c, c};
                 continue;
             }
+            // Every pass below walks the node's cells in order, kBatch at a time: the
+            // batch's ids, then all of its rows requested together, then the arithmetic
+            // in cell order (each sum keeps its order of additions), so a pass waits for
+            // memory once per batch instead of once per cell.  nv is a power of two.
+            constexpr int kBatch = 4;
+            const int64_t nb_full = nv / kBatch * kBatch;
+            double rows[kBatch][FPL];
+            int32_t ids[kBatch];
+            auto fetch = [&](int64_t x0, int cnt) {
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    ids[j] = j < cnt ? cells[x0 + j] : cells[x0];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        rows[j][e] = kb[(int64_t)ids[j] * D + lane + kWave * e];
+            };
+            // apply body(x, j) to cells x = 0 .. nv - 1 in order, the rows in rows[j]
+            auto walk = [&](auto &&body) {
+                for (int64_t x0 = 0; x0 < nb_full; x0 += kBatch) {
+                    fetch(x0, kBatch);
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j)
+                        body(x0 + j, j);
+                }
+                for (int64_t x0 = nb_full; x0 < nv; x0 += kBatch) {
+                    const int cnt = (int)(nv - x0 < kBatch ? nv - x0 : kBatch);
+                    fetch(x0, cnt);
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j)
+                        if (j < cnt)
+                            body(x0 + j, j);
+                }
+            };
+
             // mean of the cells' mean keys, summed in the node's cell order
             double mu[FPL];
 #pragma unroll
-            for (int e = 0; e < FPL; ++e) {
-                double sum = 0.0;
-                for (int64_t x = 0; x < nv; ++x)
-                    sum += kb[(int64_t)cells[x] * D + lane + kWave * e];
-                mu[e] = sum / (double)nv;
-            }
+            for (int e = 0; e < FPL; ++e)
+                mu[e] = 0.0;
+            walk([&](int64_t, int j) {
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    mu[e] += rows[j][e];
+            });
+#pragma unroll
+            for (int e = 0; e < FPL; ++e)
+                mu[e] = mu[e] / (double)nv;
             // distances from the mean: the farthest cell (smaller id on ties) starts the
             // power iteration and gives the radius; the largest norm and the earliest cell
             double best = -1.0;
             int32_t bestc = INT_MAX, mn = INT_MAX;
             float A = -INFINITY;
-            for (int64_t x = 0; x < nv; ++x) {
-                const int32_t c = cells[x];
+            walk([&](int64_t, int j) {
+                const int32_t c = ids[j];
                 double sq = 0.0;
 #pragma unroll
                 for (int e = 0; e < FPL; ++e) {
-                    const double xv = kb[(int64_t)c * D + lane + kWave * e] - mu[e];
+                    const double xv = rows[j][e] - mu[e];
                     sq += xv * xv;
                 }
                 const double nrm = sqrt(wave_sum_d(sq));
@@ -186,9 +226,11 @@ __global__ __launch_bounds__(kBuildThreads) void fsb_build_kernel(const double *
                     best = nrm;
                     bestc = c;
                 }
-                A = fmaxf(A, ah[c]);
                 mn = min(mn, c);
-            }
+            });
+            for (int64_t x = lane; x < nv; x += kWave) // the largest norm: order-free
+                A = fmaxf(A, ah[cells[x]]);
+            A = wave_max_f(A);
             double u[FPL];
             auto normalise = [&]() {
                 double sq = 0.0;
@@ -212,34 +254,32 @@ __global__ __launch_bounds__(kBuildThreads) void fsb_build_kernel(const double *
 #pragma unroll
                 for (int e = 0; e < FPL; ++e)
                     wv[e] = 0.0;
-                for (int64_t x = 0; x < nv; ++x) {
-                    const int32_t c = cells[x];
+                walk([&](int64_t, int j) {
                     double xv[FPL], p = 0.0;
 #pragma unroll
                     for (int e = 0; e < FPL; ++e) {
-                        xv[e] = kb[(int64_t)c * D + lane + kWave * e] - mu[e];
+                        xv[e] = rows[j][e] - mu[e];
                         p += xv[e] * u[e];
                     }
                     p = wave_sum_d(p);
 #pragma unroll
                     for (int e = 0; e < FPL; ++e)
                         wv[e] += p * xv[e];
-                }
+                });
 #pragma unroll
                 for (int e = 0; e < FPL; ++e)
                     u[e] = wv[e];
                 normalise();
             }
-            for (int64_t x = 0; x < nv; ++x) { // projections on u^(2)
-                const int32_t c = cells[x];
+            walk([&](int64_t x, int j) { // projections on u^(2)
                 double p = 0.0;
 #pragma unroll
                 for (int e = 0; e < FPL; ++e)
-                    p += (kb[(int64_t)c * D + lane + kWave * e] - mu[e]) * u[e];
+                    p += (rows[j][e] - mu[e]) * u[e];
                 p = wave_sum_d(p);
                 if (lane == 0)
                     keys[x] = p;
-            }
+            });
 #pragma unroll
             for (int e = 0; e < FPL; ++e)
                 mu_out[lane + kWave * e] = (float)mu[e];
