@@ -578,19 +578,28 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
             __syncthreads();
             int nk = 0;
             if (half == 0) { // expand this query's internal nodes; leaves keep their slots
+                // the beam is read whole first (slots past nb hold stale refs, never used)
+                const int nbq = sm.nb[qs];
+                int32_t refs[kFsbMaxBeam];
+#pragma unroll
+                for (int e = 0; e < kFsbMaxBeam; ++e)
+                    refs[e] = sm.beam[qs][e];
                 int nleaf = 0;
-                for (int e = 0; e < sm.nb[qs]; ++e) {
-                    const int32_t ref = sm.beam[qs][e];
-                    if (is_leaf(ref)) {
-                        ++nleaf;
-                        continue;
+#pragma unroll
+                for (int e = 0; e < kFsbMaxBeam; ++e) {
+                    if (e < nbq) {
+                        const int32_t ref = refs[e];
+                        if (is_leaf(ref)) {
+                            ++nleaf;
+                        } else {
+                            const int32_t c0 = child_of(ref, 0), c1 = child_of(ref, 1);
+                            sm.kpar[qs][nk >> 1] = ref;
+                            nk += 2;
+                            const int l0 = local_of(c0), l1 = local_of(c1);
+                            atomicOr(&bm[l0 >> 5], 1u << (l0 & 31));
+                            atomicOr(&bm[l1 >> 5], 1u << (l1 & 31));
+                        }
                     }
-                    const int32_t c0 = child_of(ref, 0), c1 = child_of(ref, 1);
-                    sm.kpar[qs][nk >> 1] = ref;
-                    nk += 2;
-                    const int l0 = local_of(c0), l1 = local_of(c1);
-                    atomicOr(&bm[l0 >> 5], 1u << (l0 & 31));
-                    atomicOr(&bm[l1 >> 5], 1u << (l1 & 31));
                 }
                 sm.nk[qs] = nk;
                 sm.nleaf[qs] = nleaf;
@@ -734,15 +743,24 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                 }
                 merge_top_desc<kFsbMaxBeam>(top, other);
                 if (half == 0 && nkq > 0) {
+                    // the old beam and the kept children's parents are read before any write
+                    const int nbq = sm.nb[qs];
+                    int32_t refs[kFsbMaxBeam], par[kFsbMaxBeam];
+#pragma unroll
+                    for (int e = 0; e < kFsbMaxBeam; ++e) {
+                        refs[e] = sm.beam[qs][e];
+                        par[e] = sm.kpar[qs][(int)(top[e] & 0xffffu) >> 1]; // in bounds for every key
+                    }
                     int nb2 = 0;
-                    for (int e = 0; e < sm.nb[qs]; ++e)
-                        if (is_leaf(sm.beam[qs][e]))
-                            sm.beam[qs][nb2++] = sm.beam[qs][e];
+#pragma unroll
+                    for (int e = 0; e < kFsbMaxBeam; ++e)
+                        if (e < nbq && is_leaf(refs[e]))
+                            sm.beam[qs][nb2++] = refs[e];
                     const int keep = Wb - sm.nleaf[qs];
 #pragma unroll
                     for (int e = 0; e < kFsbMaxBeam; ++e)
                         if (e < keep && top[e] != 0ull)
-                            sm.beam[qs][nb2++] = child_of(sm.kpar[qs][(int)(top[e] & 0xffffu) >> 1], (int)(top[e] & 1u));
+                            sm.beam[qs][nb2++] = child_of(par[e], (int)(top[e] & 1u));
                     sm.nb[qs] = nb2;
                 }
             }
@@ -750,16 +768,29 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
         }
         // ---- the leaves reached join the query's candidates (deduplicated) ----
         if (half == 0) {
+            // every beam node is a leaf now: all their cells are requested at once,
+            // then taken in beam order
+            const int nbq = sm.nb[qs];
+            int32_t leaf_cell[kFsbMaxBeam];
+#pragma unroll
+            for (int e = 0; e < kFsbMaxBeam; ++e) {
+                leaf_cell[e] = -1;
+                if (e < nbq) {
+                    const int32_t ref = sm.beam[qs][e];
+                    leaf_cell[e] = node_meta[sm.cbase[ref >> 16] + (ref & 0xffff) - 1].cell;
+                }
+            }
             int nc = sm.ncand[qs];
-            for (int e = 0; e < sm.nb[qs]; ++e) {
-                const int32_t ref = sm.beam[qs][e];
-                const int ct = ref >> 16;
-                const int32_t cell = node_meta[sm.cbase[ct] + (ref & 0xffff) - 1].cell;
-                bool dup = false;
-                for (int x = 0; x < nc; ++x)
-                    dup |= (int32_t)sm.cand[qs][x] == cell;
-                if (!dup)
-                    sm.cand[qs][nc++] = (uint16_t)cell; // cell ids < kFsbMaxCells
+#pragma unroll
+            for (int e = 0; e < kFsbMaxBeam; ++e) {
+                if (e < nbq) {
+                    const int32_t cell = leaf_cell[e];
+                    bool dup = false;
+                    for (int x = 0; x < nc; ++x)
+                        dup |= (int32_t)sm.cand[qs][x] == cell;
+                    if (!dup)
+                        sm.cand[qs][nc++] = (uint16_t)cell; // cell ids < kFsbMaxCells
+                }
             }
             sm.ncand[qs] = nc;
         }
