@@ -606,14 +606,26 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
             }
             if (!__syncthreads_or(nk > 0))
                 break; // every beam holds only leaves
-            // the level's node list: prefix counts over the bitmap words
-            if (t == 0) {
-                int32_t run = 0;
-                for (int x = 0; x < nwords; ++x) {
-                    wb[x] = run;
-                    run += __popc(bm[x]);
+            // the level's node list: prefix counts over the bitmap words, one word per lane
+            // of wave 0 (64 words a round, the total carried)
+            if (wave == 0) {
+                int32_t carry = 0;
+                for (int x0 = 0; x0 < nwords; x0 += kWave) {
+                    const int x = x0 + lane;
+                    const int32_t c = x < nwords ? __popc(bm[x]) : 0;
+                    int32_t incl = c;
+#pragma unroll
+                    for (int off = 1; off < kWave; off <<= 1) {
+                        const int32_t y = __shfl_up(incl, off, kWave);
+                        if (lane >= off)
+                            incl += y;
+                    }
+                    if (x < nwords)
+                        wb[x] = carry + incl - c;
+                    carry += __shfl(incl, kWave - 1, kWave);
                 }
-                sm.nlist = run;
+                if (lane == 0)
+                    sm.nlist = carry;
             }
             __syncthreads();
             for (int x = t; x < nwords; x += kThreads) {
