@@ -554,6 +554,15 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
         auto local_of = [&](int32_t ref) {
             return (ref & kJoinRef) ? lj + (ref & 0xffff) : sm.lbase[ref >> 16] + (ref & 0xffff) - 1;
         };
+        // the node of local id lp (the inverse of local_of)
+        auto ref_of = [&](int lp) -> int32_t {
+            if (lp >= lj)
+                return (int32_t)(kJoinRef | (lp - lj));
+            int ct = 0;
+            while (ct + 1 < r && lp >= sm.lbase[ct + 1])
+                ++ct;
+            return (int32_t)((ct << 16) | (lp - sm.lbase[ct] + 1));
+        };
         // child c (0 or 1) of internal node ref
         auto child_of = [&](int32_t ref, int c) -> int32_t {
             if (ref & kJoinRef) {
@@ -591,13 +600,11 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                         const int32_t ref = refs[e];
                         if (is_leaf(ref)) {
                             ++nleaf;
-                        } else {
-                            const int32_t c0 = child_of(ref, 0), c1 = child_of(ref, 1);
+                        } else { // the node is marked; the list takes both its children
                             sm.kpar[qs][nk >> 1] = ref;
                             nk += 2;
-                            const int l0 = local_of(c0), l1 = local_of(c1);
-                            atomicOr(&bm[l0 >> 5], 1u << (l0 & 31));
-                            atomicOr(&bm[l1 >> 5], 1u << (l1 & 31));
+                            const int lp = local_of(ref);
+                            atomicOr(&bm[lp >> 5], 1u << (lp & 31));
                         }
                     }
                 }
@@ -606,8 +613,10 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
             }
             if (!__syncthreads_or(nk > 0))
                 break; // every beam holds only leaves
-            // the level's node list: prefix counts over the bitmap words, one word per lane
-            // of wave 0 (64 words a round, the total carried)
+            // the level's node list, two entries (children 0 and 1) per marked node: prefix
+            // counts of marked nodes over the bitmap words, one word per lane of wave 0 (64
+            // words a round, the total carried).  Children of different nodes are different
+            // nodes, so the list never holds more entries than the forest has nodes.
             if (wave == 0) {
                 int32_t carry = 0;
                 for (int x0 = 0; x0 < nwords; x0 += kWave) {
@@ -625,16 +634,18 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                     carry += __shfl(incl, kWave - 1, kWave);
                 }
                 if (lane == 0)
-                    sm.nlist = carry;
+                    sm.nlist = 2 * carry;
             }
             __syncthreads();
             for (int x = t; x < nwords; x += kThreads) {
                 uint32_t bits = bm[x];
-                int32_t pos = wb[x];
+                int32_t pos = 2 * wb[x];
                 while (bits) {
                     const int b = __ffs(bits) - 1;
                     bits &= bits - 1;
-                    list[pos++] = (uint16_t)(x * 32 + b);
+                    const int32_t pref = ref_of(x * 32 + b);
+                    list[pos++] = (uint16_t)local_of(child_of(pref, 0));
+                    list[pos++] = (uint16_t)local_of(child_of(pref, 1));
                 }
             }
             __syncthreads();
@@ -722,9 +733,10 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                 }
                 wave_lds_sync();
                 for (int e = half; e < sm.nk[qs]; e += 2) {
-                    // the child's position in the level's node list
-                    const int l = local_of(child_of(sm.kpar[qs][e >> 1], e & 1));
-                    const int u = wb[l >> 5] + __popc(bm[l >> 5] & ((1u << (l & 31)) - 1u)) - t0;
+                    // the child's position in the level's node list: after both children of
+                    // every node marked before its parent
+                    const int lp = local_of(sm.kpar[qs][e >> 1]);
+                    const int u = 2 * (wb[lp >> 5] + __popc(bm[lp >> 5] & ((1u << (lp & 31)) - 1u))) + (e & 1) - t0;
                     if (u >= 0 && u < 32) {
                         sm.ku[qs][e] = sm.ut[wave][u][col];
                         sm.kmin[qs][e] = (uint16_t)sm.tmin[u];
