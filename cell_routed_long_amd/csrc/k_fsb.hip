@@ -38,6 +38,8 @@
 // smallest cell id below, which names one node among disjoint subtrees).
 #include "fsl_internal.h"
 
+#include <type_traits>
+
 #include <climits>
 
 namespace fsl {
@@ -135,7 +137,8 @@ __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const doubl
     const int64_t Mf = f == 0 ? L.Mu : cnt[bh * (M + 1) + L.Mu];
     if (start + n > Mf)
         return; // not a complete chunk of this forest: never read
-    const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
+    const int t = threadIdx.x, lane = t & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave); // uniform: node and slice values stay scalar
     for (int64_t p = t; p < n; p += kBuildThreads)
         perm[p] = f == 0 ? (int32_t)(start + p) : adm[bh * M + start + p];
     __syncthreads();
@@ -143,9 +146,33 @@ __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const doubl
     const double *kb = kbar64 + bh * M * D;
     const float *ah = a + bh * M;
 
+    // Levels with fewer nodes than waves (and at least kCoopCells cells a node) take
+    // every wave: wpn waves share a node, each walking a contiguous slice of its cells;
+    // their sums meet in LDS (added in slice order) and the node's sort steps on
+    // workgroup barriers.  Other levels take one wave per node.
+    constexpr int kCoopCells = 16;
+    constexpr int kBatch = 4; // cells per memory round trip in the node passes
+    __shared__ double s_best[NW];
+    __shared__ int32_t s_bestc[NW], s_mn[NW];
+    __shared__ float s_A[NW];
+    // the slices' partial sums (one D-vector per wave) use the first NW * D entries of
+    // key: the level's projections are written only after the last partial is read
+    static_assert(NW * D <= kFsbMaxCells, "the partial sums fit in the key area");
+    double(*const s_part)[D] = reinterpret_cast<double(*)[D]>(key);
+
     for (int l = 0; l <= k; ++l) {
         const int64_t nv = n >> l, nodes = (int64_t)1 << l;
-        for (int64_t s = wave; s < nodes; s += NW) {
+        const int wpn = (nodes < NW && nv >= kCoopCells) ? NW / (int)nodes : 1; // waves per node
+        const bool coop = wpn > 1; // then nodes * wpn == NW: every wave takes one node, once
+        auto node_sync = [&]() {
+            if (coop)
+                __syncthreads();
+            else
+                wave_lds_sync();
+        };
+        for (int64_t s = wave / wpn; s < nodes; s += NW / wpn) {
+            const int sp = wave % wpn;                     // this wave's slice of the node
+            const int64_t xb = sp * (nv / wpn), xe = xb + nv / wpn; // its cells (all of them if wpn = 1)
             int32_t *cells = perm + s * nv;
             double *keys = key + s * nv;
             const int64_t node = out0 + nodes + s - 1; // heap index nodes + s
@@ -159,152 +186,230 @@ __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const doubl
                     node_meta[node] = FsbNodeMeta{0.0f, ah[c], c, c};
                 continue;
             }
-            // Every pass below walks the node's cells in order, kBatch at a time: the
-            // batch's ids, then all of its rows requested together, then the arithmetic
-            // in cell order (each sum keeps its order of additions), so a pass waits for
-            // memory once per batch instead of once per cell.  nv is a power of two.
-            constexpr int kBatch = 4;
-            const int64_t nb_full = nv / kBatch * kBatch;
-            double rows[kBatch][FPL];
-            int32_t ids[kBatch];
-            auto fetch = [&](int64_t x0, int cnt) {
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j)
-                    ids[j] = j < cnt ? cells[x0 + j] : cells[x0];
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j)
-#pragma unroll
-                    for (int e = 0; e < FPL; ++e)
-                        rows[j][e] = kb[(int64_t)ids[j] * D + lane + kWave * e];
-            };
-            // apply body(x, j) to cells x = 0 .. nv - 1 in order, the rows in rows[j]
-            auto walk = [&](auto &&body) {
-                for (int64_t x0 = 0; x0 < nb_full; x0 += kBatch) {
-                    fetch(x0, kBatch);
+            // the node's passes, with its slice resident in registers or streamed in batches
+            auto node_passes = [&](auto mode) {
+                // Every pass below walks the wave's cells in order, kBatch at a time: the
+                // batch's ids, then all of its rows (and norms) requested together, then the
+                // arithmetic in cell order (each sum keeps its order of additions), so a pass
+                // waits for memory once per batch instead of once per cell.  A slice of at
+                // most kBatch cells (every node of the two lowest levels, small chunks) is
+                // fetched once and every pass runs on the registers.  Slices are powers of two.
+                const int64_t nb_full = xb + (xe - xb) / kBatch * kBatch;
+                constexpr bool resident = decltype(mode)::value;
+                double rows[kBatch][FPL];
+                int32_t ids[kBatch];
+                float an[kBatch];
+                auto fetch = [&](int64_t x0, int cnt) {
 #pragma unroll
                     for (int j = 0; j < kBatch; ++j)
-                        body(x0 + j, j);
-                }
-                for (int64_t x0 = nb_full; x0 < nv; x0 += kBatch) {
-                    const int cnt = (int)(nv - x0 < kBatch ? nv - x0 : kBatch);
-                    fetch(x0, cnt);
+                        ids[j] = j < cnt ? cells[x0 + j] : cells[x0];
 #pragma unroll
-                    for (int j = 0; j < kBatch; ++j)
-                        if (j < cnt)
+                    for (int j = 0; j < kBatch; ++j) {
+#pragma unroll
+                        for (int e = 0; e < FPL; ++e)
+                            rows[j][e] = kb[(int64_t)ids[j] * D + lane + kWave * e];
+                        an[j] = ah[ids[j]];
+                    }
+                };
+                if constexpr (resident)
+                    fetch(xb, (int)(xe - xb));
+                // apply body(x, j) to cells x = xb .. xe - 1 in order, the rows in rows[j]
+                auto walk = [&](auto &&body) {
+                    if constexpr (resident) {
+#pragma unroll
+                        for (int j = 0; j < kBatch; ++j)
+                            if (j < xe - xb)
+                                body(xb + j, j);
+                        return;
+                    }
+                    for (int64_t x0 = xb; x0 < nb_full; x0 += kBatch) {
+                        fetch(x0, kBatch);
+#pragma unroll
+                        for (int j = 0; j < kBatch; ++j)
                             body(x0 + j, j);
-                }
-            };
-
-            // mean of the cells' mean keys, summed in the node's cell order
-            double mu[FPL];
+                    }
+                    for (int64_t x0 = nb_full; x0 < xe; x0 += kBatch) {
+                        const int cnt = (int)(xe - x0 < kBatch ? xe - x0 : kBatch);
+                        fetch(x0, cnt);
 #pragma unroll
-            for (int e = 0; e < FPL; ++e)
-                mu[e] = 0.0;
-            walk([&](int64_t, int j) {
-#pragma unroll
-                for (int e = 0; e < FPL; ++e)
-                    mu[e] += rows[j][e];
-            });
-#pragma unroll
-            for (int e = 0; e < FPL; ++e)
-                mu[e] = mu[e] / (double)nv;
-            // distances from the mean: the farthest cell (smaller id on ties) starts the
-            // power iteration and gives the radius; the largest norm and the earliest cell
-            double best = -1.0;
-            int32_t bestc = INT_MAX, mn = INT_MAX;
-            float A = -INFINITY;
-            walk([&](int64_t, int j) {
-                const int32_t c = ids[j];
-                double sq = 0.0;
-#pragma unroll
-                for (int e = 0; e < FPL; ++e) {
-                    const double xv = rows[j][e] - mu[e];
-                    sq += xv * xv;
-                }
-                const double nrm = sqrt(wave_sum_d(sq));
-                if (nrm > best || (nrm == best && c < bestc)) {
-                    best = nrm;
-                    bestc = c;
-                }
-                mn = min(mn, c);
-            });
-            for (int64_t x = lane; x < nv; x += kWave) // the largest norm: order-free
-                A = fmaxf(A, ah[cells[x]]);
-            A = wave_max_f(A);
-            double u[FPL];
-            auto normalise = [&]() {
-                double sq = 0.0;
-#pragma unroll
-                for (int e = 0; e < FPL; ++e)
-                    sq += u[e] * u[e];
-                sq = wave_sum_d(sq);
-                if (sq > 0.0) {
-                    const double inv = 1.0 / sqrt(sq);
+                        for (int j = 0; j < kBatch; ++j)
+                            if (j < cnt)
+                                body(x0 + j, j);
+                    }
+                };
+                // a D-vector summed over the node's slices, in slice order (every wave of the
+                // node gets the same sum); then the barrier that frees s_part
+                auto slices_sum = [&](double (&v)[FPL]) {
+                    if (!coop)
+                        return;
 #pragma unroll
                     for (int e = 0; e < FPL; ++e)
-                        u[e] *= inv;
-                }
-            };
-#pragma unroll
-            for (int e = 0; e < FPL; ++e)
-                u[e] = kb[(int64_t)bestc * D + lane + kWave * e] - mu[e];
-            normalise();
-            for (int it = 0; it < 2; ++it) { // u <- sum_c (x_c . u) x_c, normalised (Eq. 19)
-                double wv[FPL];
-#pragma unroll
-                for (int e = 0; e < FPL; ++e)
-                    wv[e] = 0.0;
-                walk([&](int64_t, int j) {
-                    double xv[FPL], p = 0.0;
+                        s_part[wave][lane + kWave * e] = v[e];
+                    __syncthreads();
 #pragma unroll
                     for (int e = 0; e < FPL; ++e) {
-                        xv[e] = rows[j][e] - mu[e];
-                        p += xv[e] * u[e];
+                        double sum = 0.0;
+                        for (int j = 0; j < wpn; ++j)
+                            sum += s_part[s * wpn + j][lane + kWave * e];
+                        v[e] = sum;
                     }
-                    p = wave_sum_d(p);
+                    __syncthreads();
+                };
+
+                // mean of the cells' mean keys, summed in the node's cell order (one wave) or
+                // in slice order of the slices' sums (several)
+                double mu[FPL];
+#pragma unroll
+                for (int e = 0; e < FPL; ++e)
+                    mu[e] = 0.0;
+                walk([&](int64_t, int j) {
 #pragma unroll
                     for (int e = 0; e < FPL; ++e)
-                        wv[e] += p * xv[e];
+                        mu[e] += rows[j][e];
                 });
+                slices_sum(mu);
 #pragma unroll
                 for (int e = 0; e < FPL; ++e)
-                    u[e] = wv[e];
-                normalise();
-            }
-            walk([&](int64_t x, int j) { // projections on u^(2)
-                double p = 0.0;
+                    mu[e] = mu[e] / (double)nv;
+                // distances from the mean: the farthest cell (smaller id on ties) starts the
+                // power iteration and gives the radius; the largest norm and the earliest cell
+                double best = -1.0;
+                int32_t bestc = INT_MAX, mn = INT_MAX;
+                float A = -INFINITY;
+                walk([&](int64_t, int j) {
+                    const int32_t c = ids[j];
+                    double sq = 0.0;
 #pragma unroll
-                for (int e = 0; e < FPL; ++e)
-                    p += (rows[j][e] - mu[e]) * u[e];
-                p = wave_sum_d(p);
-                if (lane == 0)
-                    keys[x] = p;
-            });
-#pragma unroll
-            for (int e = 0; e < FPL; ++e)
-                mu_out[lane + kWave * e] = (float)mu[e];
-            if (lane == 0)
-                node_meta[node] = FsbNodeMeta{(float)best, A, mn, -1};
-            wave_lds_sync();
-            // sort the node's cells by (projection asc, id asc); the first half goes left
-            for (int64_t size = 2; size <= nv; size <<= 1) {
-                for (int64_t stride = size >> 1; stride > 0; stride >>= 1) {
-                    for (int64_t p = lane; p < nv / 2; p += kWave) {
-                        const int64_t i1 = 2 * p - (p & (stride - 1)), i2 = i1 + stride;
-                        const bool asc = (i1 & size) == 0;
-                        const double k1 = keys[i1], k2 = keys[i2];
-                        const int32_t c1 = cells[i1], c2 = cells[i2];
-                        const bool gt = k1 > k2 || (k1 == k2 && c1 > c2);
-                        if (gt == asc) {
-                            keys[i1] = k2;
-                            keys[i2] = k1;
-                            cells[i1] = c2;
-                            cells[i2] = c1;
-                        }
+                    for (int e = 0; e < FPL; ++e) {
+                        const double xv = rows[j][e] - mu[e];
+                        sq += xv * xv;
                     }
-                    wave_lds_sync();
+                    const double nrm = sqrt(wave_sum_d(sq));
+                    if (nrm > best || (nrm == best && c < bestc)) {
+                        best = nrm;
+                        bestc = c;
+                    }
+                    mn = min(mn, c);
+                    A = fmaxf(A, an[j]);
+                });
+                if (coop) { // the slices' results, combined by the same rules (order-free)
+                    if (lane == 0) {
+                        s_best[wave] = best;
+                        s_bestc[wave] = bestc;
+                        s_A[wave] = A;
+                        s_mn[wave] = mn;
+                    }
+                    __syncthreads();
+                    best = -1.0;
+                    bestc = INT_MAX;
+                    mn = INT_MAX;
+                    A = -INFINITY;
+                    for (int j = 0; j < wpn; ++j) {
+                        const int w2 = (int)s * wpn + j;
+                        const double nb = s_best[w2];
+                        const int32_t cb = s_bestc[w2];
+                        if (nb > best || (nb == best && cb < bestc)) {
+                            best = nb;
+                            bestc = cb;
+                        }
+                        A = fmaxf(A, s_A[w2]);
+                        mn = min(mn, s_mn[w2]);
+                    }
                 }
-            }
+                double u[FPL];
+                auto normalise = [&]() {
+                    double sq = 0.0;
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        sq += u[e] * u[e];
+                    sq = wave_sum_d(sq);
+                    if (sq > 0.0) {
+                        const double inv = 1.0 / sqrt(sq);
+#pragma unroll
+                        for (int e = 0; e < FPL; ++e)
+                            u[e] *= inv;
+                    }
+                };
+                if (resident && !coop) { // the farthest cell's row is one of the registers
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        u[e] = 0.0;
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j)
+                        if (j < xe - xb && ids[j] == bestc)
+#pragma unroll
+                            for (int e = 0; e < FPL; ++e)
+                                u[e] = rows[j][e] - mu[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        u[e] = kb[(int64_t)bestc * D + lane + kWave * e] - mu[e];
+                }
+                normalise();
+                for (int it = 0; it < 2; ++it) { // u <- sum_c (x_c . u) x_c, normalised (Eq. 19)
+                    double wv[FPL];
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        wv[e] = 0.0;
+                    walk([&](int64_t, int j) {
+                        double xv[FPL], p = 0.0;
+#pragma unroll
+                        for (int e = 0; e < FPL; ++e) {
+                            xv[e] = rows[j][e] - mu[e];
+                            p += xv[e] * u[e];
+                        }
+                        p = wave_sum_d(p);
+#pragma unroll
+                        for (int e = 0; e < FPL; ++e)
+                            wv[e] += p * xv[e];
+                    });
+                    slices_sum(wv);
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        u[e] = wv[e];
+                    normalise();
+                }
+                walk([&](int64_t x, int j) { // projections on u^(2)
+                    double p = 0.0;
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        p += (rows[j][e] - mu[e]) * u[e];
+                    p = wave_sum_d(p);
+                    if (lane == 0)
+                        keys[x] = p;
+                });
+                if (sp == 0) {
+#pragma unroll
+                    for (int e = 0; e < FPL; ++e)
+                        mu_out[lane + kWave * e] = (float)mu[e];
+                    if (lane == 0)
+                        node_meta[node] = FsbNodeMeta{(float)best, A, mn, -1};
+                }
+                node_sync();
+                // sort the node's cells by (projection asc, id asc); the first half goes left
+                for (int64_t size = 2; size <= nv; size <<= 1) {
+                    for (int64_t stride = size >> 1; stride > 0; stride >>= 1) {
+                        for (int64_t p = sp * kWave + lane; p < nv / 2; p += wpn * kWave) {
+                            const int64_t i1 = 2 * p - (p & (stride - 1)), i2 = i1 + stride;
+                            const bool asc = (i1 & size) == 0;
+                            const double k1 = keys[i1], k2 = keys[i2];
+                            const int32_t c1 = cells[i1], c2 = cells[i2];
+                            const bool gt = k1 > k2 || (k1 == k2 && c1 > c2);
+                            if (gt == asc) {
+                                keys[i1] = k2;
+                                keys[i2] = k1;
+                                cells[i1] = c2;
+                                cells[i2] = c1;
+                            }
+                        }
+                        node_sync();
+                    }
+                }
+            };
+            if (xe - xb <= kBatch)
+                node_passes(std::true_type{});
+            else
+                node_passes(std::false_type{});
         }
         __syncthreads();
     }
