@@ -663,9 +663,10 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
         auto ref_of = [&](int lp) -> int32_t {
             if (lp >= lj)
                 return (int32_t)(kJoinRef | (lp - lj));
-            int ct = 0;
-            while (ct + 1 < r && lp >= sm.lbase[ct + 1])
-                ++ct;
+            int ct = 0; // chunk bases ascend: count those at or below lp
+#pragma unroll
+            for (int c = 1; c < kMaxChunksPerForest; ++c)
+                ct += (c < r && lp >= sm.lbase[c]) ? 1 : 0;
             return (int32_t)((ct << 16) | (lp - sm.lbase[ct] + 1));
         };
         // child c (0 or 1) of internal node ref
@@ -742,15 +743,13 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                     sm.nlist = 2 * carry;
             }
             __syncthreads();
-            for (int x = t; x < nwords; x += kThreads) {
-                uint32_t bits = bm[x];
-                int32_t pos = 2 * wb[x];
-                while (bits) {
-                    const int b = __ffs(bits) - 1;
-                    bits &= bits - 1;
-                    const int32_t pref = ref_of(x * 32 + b);
-                    list[pos++] = (uint16_t)local_of(child_of(pref, 0));
-                    list[pos++] = (uint16_t)local_of(child_of(pref, 1));
+            for (int lp = t; lp < nwords * 32; lp += kThreads) { // one local id per thread
+                const uint32_t word = bm[lp >> 5];
+                if ((word >> (lp & 31)) & 1u) {
+                    const int32_t pos = 2 * (wb[lp >> 5] + __popc(word & ((1u << (lp & 31)) - 1u)));
+                    const int32_t pref = ref_of(lp);
+                    list[pos] = (uint16_t)local_of(child_of(pref, 0));
+                    list[pos + 1] = (uint16_t)local_of(child_of(pref, 1));
                 }
             }
             __syncthreads();
@@ -828,11 +827,24 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                         acc = mfma_f32(sm.mu[col][2 * kc + half], qf[kc], acc); // node row col, query column col
                 }
                 __syncthreads(); // every wave has read the means: the area takes the priorities
+                // erf only below 4 (from there on it rounds to 1 in fp32); a wave takes it
+                // only if one of its queries is that close to a node's earliest cell
+                float pm[16], pmax = -INFINITY;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    pm[rr] = ((float)sm.tmin[acc_row(rr, half)] + 0.5f) * 32.0f;
+                    pmax = fmaxf(pmax, pm[rr]);
+                }
+                const bool need_erf = __ballot(((float)i - pmax) * its < 4.0f) != 0ull;
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
                     const int row = acc_row(rr, half);
-                    const float pmin = ((float)sm.tmin[row] + 0.5f) * 32.0f;
-                    const float g = erff(((float)i - pmin) * its);
+                    float g = 1.0f;
+                    if (need_erf) {
+                        const float x = ((float)i - pm[rr]) * its;
+                        if (x < 4.0f)
+                            g = erff(x);
+                    }
                     sm.ut[wave][row][col] =
                         fmaf(fmaf(fc.c * qnorm, sm.trho[row], acc[rr]), inv_sqrt_d, lam * sm.tA[row] * g);
                 }
