@@ -486,13 +486,16 @@ struct SearchSmem {
     // bf16 queries read a node mean 8 features at a time (16-byte aligned rows; 4 words
     // of pad put 16 consecutive rows on distinct banks); fp32 ones one feature per lane
     static constexpr int kMuStride = sizeof(T) == 2 ? D + 4 : D + 1;
-    int32_t beam[128][kFsbMaxBeam]; // node refs of each query's beam
+    // Per-query rows: the lanes of a wave each take their own query's row at the same
+    // index, so rows are an odd number of words long (one word of pad) and the lanes'
+    // words fall on distinct banks.
+    int32_t beam[128][kFsbMaxBeam + 1]; // node refs of each query's beam
     int32_t nb[128];
     int32_t nk[128], nleaf[128];
-    int32_t kpar[128][kFsbMaxBeam]; // the beam's internal nodes, whose children 2 j, 2 j + 1 are ranked
-    float ku[128][kMaxKids];        // the children's priority (Eq. 11)
-    uint16_t kmin[128][kMaxKids];   // their smallest cell id
-    uint16_t cand[128][kMaxKids];   // candidate cells (forest 0, then the second forest)
+    int32_t kpar[128][kFsbMaxBeam + 1]; // the beam's internal nodes, whose children 2 j, 2 j + 1 are ranked
+    float ku[128][kMaxKids + 1];        // the children's priority (Eq. 11)
+    uint16_t kmin[128][kMaxKids + 2];   // their smallest cell id
+    uint16_t cand[128][kMaxKids + 2];   // candidate cells (forest 0, then the second forest)
     int32_t ncand[128];
     int32_t nlist;
     union {
