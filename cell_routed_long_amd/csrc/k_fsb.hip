@@ -924,14 +924,22 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                     leaf_cell[e] = node_meta[sm.cbase[ref >> 16] + (ref & 0xffff) - 1].cell;
                 }
             }
+            // one forest's leaves are distinct cells: a leaf can repeat only a candidate
+            // of the forest before, at most kFsbMaxBeam of them, compared in registers
             int nc = sm.ncand[qs];
+            const int nc0 = nc;
+            int32_t prev[kFsbMaxBeam];
+#pragma unroll
+            for (int x = 0; x < kFsbMaxBeam; ++x)
+                prev[x] = x < nc0 ? (int32_t)sm.cand[qs][x] : -1;
 #pragma unroll
             for (int e = 0; e < kFsbMaxBeam; ++e) {
                 if (e < nbq) {
                     const int32_t cell = leaf_cell[e];
                     bool dup = false;
-                    for (int x = 0; x < nc; ++x)
-                        dup |= (int32_t)sm.cand[qs][x] == cell;
+#pragma unroll
+                    for (int x = 0; x < kFsbMaxBeam; ++x)
+                        dup |= prev[x] == cell;
                     if (!dup)
                         sm.cand[qs][nc++] = (uint16_t)cell; // cell ids < kFsbMaxCells
                 }
@@ -947,37 +955,50 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
         bm[x] = 0u;
     __syncthreads();
     if (half == 0) {
+        // the query's candidates (distinct ids) in ascending order: each one's rank is
+        // the number of smaller ones, counted in registers
         const int nc = sm.ncand[qs];
-        for (int x = 1; x < nc; ++x) {
-            const uint16_t v = sm.cand[qs][x];
-            int y = x - 1;
-            while (y >= 0 && sm.cand[qs][y] > v) {
-                sm.cand[qs][y + 1] = sm.cand[qs][y];
-                --y;
+        int32_t cv[kMaxKids];
+#pragma unroll
+        for (int x = 0; x < kMaxKids; ++x)
+            cv[x] = x < nc ? (int32_t)sm.cand[qs][x] : INT_MAX;
+#pragma unroll
+        for (int x = 0; x < kMaxKids; ++x) {
+            if (x < nc) {
+                int rank = 0;
+#pragma unroll
+                for (int y = 0; y < kMaxKids; ++y)
+                    rank += cv[y] < cv[x] ? 1 : 0;
+                sm.cand[qs][rank] = (uint16_t)cv[x];
+                atomicOr(&bm[cv[x] >> 5], 1u << (cv[x] & 31));
             }
-            sm.cand[qs][y + 1] = v;
         }
-        for (int x = 0; x < nc; ++x)
-            atomicOr(&bm[sm.cand[qs][x] >> 5], 1u << (sm.cand[qs][x] & 31));
     }
     __syncthreads();
-    if (t == 0) {
-        int32_t run = 0;
-        for (int x = 0; x < mwords; ++x) {
-            wb[x] = run;
-            run += __popc(bm[x]);
+    if (wave == 0) { // prefix counts over the words, one word per lane (as for a level)
+        int32_t carry = 0;
+        for (int x0 = 0; x0 < mwords; x0 += kWave) {
+            const int x = x0 + lane;
+            const int32_t c = x < mwords ? __popc(bm[x]) : 0;
+            int32_t incl = c;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int32_t y = __shfl_up(incl, off, kWave);
+                if (lane >= off)
+                    incl += y;
+            }
+            if (x < mwords)
+                wb[x] = carry + incl - c;
+            carry += __shfl(incl, kWave - 1, kWave);
         }
-        sm.nlist = run;
+        if (lane == 0)
+            sm.nlist = carry;
     }
     __syncthreads();
-    for (int x = t; x < mwords; x += kThreads) {
-        uint32_t bits = bm[x];
-        int32_t pos = wb[x];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            list[pos++] = (uint16_t)(x * 32 + b);
-        }
+    for (int c = t; c < mwords * 32; c += kThreads) { // one cell id per thread
+        const uint32_t word = bm[c >> 5];
+        if ((word >> (c & 31)) & 1u)
+            list[wb[c >> 5] + __popc(word & ((1u << (c & 31)) - 1u))] = (uint16_t)c;
     }
     __syncthreads();
 
