@@ -498,6 +498,7 @@ struct SearchSmem {
     uint16_t cand[128][kMaxKids + 2];   // candidate cells (forest 0, then the second forest)
     int32_t ncand[128];
     int32_t nlist;
+    int32_t need_sel; // some query of the level has more children than free beam slots
     union {
         float mu[32][kMuStride];  // a tile of node means
         float ut[kWaves][32][33]; // then the tile's priorities: [wave][node row][query column]
@@ -693,6 +694,8 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
         for (;;) {
             for (int x = t; x < nwords; x += kThreads)
                 bm[x] = 0u;
+            if (t == 0)
+                sm.need_sel = 0;
             __syncthreads();
             int nk = 0;
             if (half == 0) { // expand this query's internal nodes; leaves keep their slots
@@ -719,9 +722,40 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                 }
                 sm.nk[qs] = nk;
                 sm.nleaf[qs] = nleaf;
+                if (nk > Wb - nleaf)
+                    sm.need_sel = 1;
             }
             if (!__syncthreads_or(nk > 0))
                 break; // every beam holds only leaves
+            if (sm.need_sel == 0) {
+                // every query keeps all its children (the beams are not full yet): no
+                // priorities are needed.  The beam takes its leaves, then the children in
+                // the parents' order; the kept set is the one a ranking would keep, and no
+                // later step depends on the order of a beam's nodes.
+                if (half == 0 && nk > 0) {
+                    const int nbq = sm.nb[qs];
+                    int32_t refs[kFsbMaxBeam], par[kFsbMaxBeam];
+#pragma unroll
+                    for (int e = 0; e < kFsbMaxBeam; ++e) {
+                        refs[e] = sm.beam[qs][e];
+                        par[e] = sm.kpar[qs][e];
+                    }
+                    int nb2 = 0;
+#pragma unroll
+                    for (int e = 0; e < kFsbMaxBeam; ++e)
+                        if (e < nbq && is_leaf(refs[e]))
+                            sm.beam[qs][nb2++] = refs[e];
+#pragma unroll
+                    for (int j = 0; j < kFsbMaxBeam; ++j)
+                        if (2 * j < nk) {
+                            sm.beam[qs][nb2++] = child_of(par[j], 0);
+                            sm.beam[qs][nb2++] = child_of(par[j], 1);
+                        }
+                    sm.nb[qs] = nb2;
+                }
+                __syncthreads();
+                continue;
+            }
             // the level's node list, two entries (children 0 and 1) per marked node: prefix
             // counts of marked nodes over the bitmap words, one word per lane of wave 0 (64
             // words a round, the total carried).  Children of different nodes are different
