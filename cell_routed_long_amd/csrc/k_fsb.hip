@@ -103,6 +103,14 @@ __global__ __launch_bounds__(kThreads) void fsb_admit_kernel(const double *__res
 // ---------------------------------------------------------------- construction
 
 constexpr int kBuildThreads = 512;
+constexpr int kBuildWaves = kBuildThreads / kWave;
+constexpr int kWaveChunkK = 3; // chunks of at most 2^3 cells: one wave each, kBuildWaves to a workgroup
+
+// workgroups for the chunks of 2^k cells (ck per forest, over `groups` forests)
+__host__ __device__ inline int64_t build_span(int64_t ck, int64_t groups, int k)
+{
+    return k > kWaveChunkK ? ck * groups : (ck * groups + kBuildWaves - 1) / kBuildWaves;
+}
 
 template <int D>
 __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const double *__restrict__ kbar64,
@@ -111,37 +119,52 @@ __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const doubl
                                                                const int32_t *__restrict__ cnt,
                                                                float *__restrict__ node_mu,
                                                                FsbNodeMeta *__restrict__ node_meta, int64_t M,
-                                                               FsbLayout L)
+                                                               FsbLayout L, int64_t groups)
 {
     constexpr int FPL = D / kWave; // features per lane
-    constexpr int NW = kBuildThreads / kWave;
+    constexpr int NW = kBuildWaves;
     __shared__ int32_t perm[kFsbMaxCells];
     __shared__ double key[kFsbMaxCells];
 
     // the largest chunks first: a chunk's build is a chain that grows with its size (the
     // 2^k-cell root alone takes 2^k cells through every pass), so the longest chains start
-    // at once and the many small chunks fill the CUs around them
-    const int64_t groups = (int64_t)gridDim.x / L.chunks; // (sequence, head, forest) triples
+    // at once and the many small chunks fill the CUs around them.  A chunk of at most
+    // 2^kWaveChunkK cells is built by one wave alone (its team), kBuildWaves of them to a
+    // workgroup; a larger one by the whole workgroup.  `groups`: (sequence, head, forest)
+    // triples.
     int64_t w = blockIdx.x;
     int k = L.levels - 1;
     int64_t ck = L.chunk_base[k + 1] - L.chunk_base[k]; // chunks of 2^k cells per forest
-    while (w >= ck * groups) {
-        w -= ck * groups;
+    while (k > 0 && w >= build_span(ck, groups, k)) {
+        w -= build_span(ck, groups, k);
         --k;
         ck = L.chunk_base[k + 1] - L.chunk_base[k];
     }
-    const int64_t grp = w / ck, jj = w - grp * ck;
+    const bool wm = k <= kWaveChunkK; // one wave per chunk
+    const int t = threadIdx.x, lane = t & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave); // uniform: node and slice values stay scalar
+    const int64_t cw = wm ? w * NW + wave : w; // the chunk among the ck * groups of this size
+    if (cw >= ck * groups)
+        return; // a spare wave of the last workgroup of small chunks
+    const int64_t grp = cw / ck, jj = cw - grp * ck;
     const int64_t bh = grp / 2;
     const int f = (int)(grp - bh * 2);
     const int64_t n = (int64_t)1 << k, start = 2 * jj * n;
     const int64_t Mf = f == 0 ? L.Mu : cnt[bh * (M + 1) + L.Mu];
     if (start + n > Mf)
         return; // not a complete chunk of this forest: never read
-    const int t = threadIdx.x, lane = t & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(t / kWave); // uniform: node and slice values stay scalar
-    for (int64_t p = t; p < n; p += kBuildThreads)
-        perm[p] = f == 0 ? (int32_t)(start + p) : adm[bh * M + start + p];
-    __syncthreads();
+    const int team_waves = wm ? 1 : NW, team_wave = wm ? 0 : wave;
+    int32_t *const perm_t = wm ? perm + wave * (1 << kWaveChunkK) : perm; // the team's cells
+    double *const key_t = wm ? key + wave * (1 << kWaveChunkK) : key;
+    auto team_sync = [&]() {
+        if (wm)
+            wave_lds_sync();
+        else
+            __syncthreads();
+    };
+    for (int64_t p = wm ? lane : t; p < n; p += wm ? kWave : kBuildThreads)
+        perm_t[p] = f == 0 ? (int32_t)(start + p) : adm[bh * M + start + p];
+    team_sync();
     const int64_t out0 = (bh * 2 + f) * L.nodes + L.node_base[k] + jj * (2 * n - 1);
     const double *kb = kbar64 + bh * M * D;
     const float *ah = a + bh * M;
@@ -162,7 +185,8 @@ __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const doubl
 
     for (int l = 0; l <= k; ++l) {
         const int64_t nv = n >> l, nodes = (int64_t)1 << l;
-        const int wpn = (nodes < NW && nv >= kCoopCells) ? NW / (int)nodes : 1; // waves per node
+        // waves per node; coop only when the team is the whole workgroup
+        const int wpn = (nodes < team_waves && nv >= kCoopCells) ? team_waves / (int)nodes : 1;
         const bool coop = wpn > 1; // then nodes * wpn == NW: every wave takes one node, once
         auto node_sync = [&]() {
             if (coop)
@@ -170,11 +194,11 @@ __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const doubl
             else
                 wave_lds_sync();
         };
-        for (int64_t s = wave / wpn; s < nodes; s += NW / wpn) {
-            const int sp = wave % wpn;                     // this wave's slice of the node
+        for (int64_t s = team_wave / wpn; s < nodes; s += team_waves / wpn) {
+            const int sp = team_wave % wpn;                     // this wave's slice of the node
             const int64_t xb = sp * (nv / wpn), xe = xb + nv / wpn; // its cells (all of them if wpn = 1)
-            int32_t *cells = perm + s * nv;
-            double *keys = key + s * nv;
+            int32_t *cells = perm_t + s * nv;
+            double *keys = key_t + s * nv;
             const int64_t node = out0 + nodes + s - 1; // heap index nodes + s
             float *mu_out = node_mu + node * D;
             if (nv == 1) { // a leaf: the cell itself
@@ -411,7 +435,7 @@ __global__ __launch_bounds__(kBuildThreads, 6) void fsb_build_kernel(const doubl
             else
                 node_passes(std::false_type{});
         }
-        __syncthreads();
+        team_sync();
     }
 }
 
@@ -1134,9 +1158,14 @@ hipError_t launch_t(const Geometry &g, const FsbLayout &L, const HeadConsts &hc,
 {
     hipLaunchKernelGGL(fsb_admit_kernel, dim3((unsigned)g.bh), dim3(kThreads), 0, st, a64, adm, adm_count, g.M, g.H,
                        fc);
-    if (L.Mu > 0)
-        hipLaunchKernelGGL((fsb_build_kernel<D>), dim3((unsigned)((int64_t)g.bh * 2 * L.chunks)),
-                           dim3(kBuildThreads), 0, st, kbar64, a, adm, adm_count, node_mu, node_meta, g.M, L);
+    if (L.Mu > 0) {
+        const int64_t groups = (int64_t)g.bh * 2; // (sequence, head, forest) triples
+        int64_t blocks = 0;
+        for (int k = 0; k < L.levels; ++k)
+            blocks += build_span(L.chunk_base[k + 1] - L.chunk_base[k], groups, k);
+        hipLaunchKernelGGL((fsb_build_kernel<D>), dim3((unsigned)blocks), dim3(kBuildThreads), 0, st, kbar64, a,
+                           adm, adm_count, node_mu, node_meta, g.M, L, groups);
+    }
     hipLaunchKernelGGL((fsb_search_kernel<T, D>), dim3((unsigned)((int64_t)g.bh * g.NB)), dim3(kThreads),
                        fsb_search_lds(L.Mu), st,
                        static_cast<const T *>(q), static_cast<const T *>(k), a, adm_count, node_mu, node_meta, sel,
