@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void fsb_admit_kernel(const double *__res
 
 constexpr int kBuildThreads = 512;
 constexpr int kBuildWaves = kBuildThreads / kWave;
-constexpr int kWaveChunkK = 3; // chunks of at most 2^3 cells: one wave each, kBuildWaves to a workgroup
+constexpr int kWaveChunkK = 4; // chunks of at most 2^4 cells: one wave each, kBuildWaves to a workgroup
 
 // workgroups for the chunks of 2^k cells (ck per forest, over `groups` forests)
 __host__ __device__ inline int64_t build_span(int64_t ck, int64_t groups, int k)
