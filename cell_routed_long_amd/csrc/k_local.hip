@@ -99,8 +99,12 @@ __global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(co
     constexpr int NP = D / 2; // feature pairs
     __shared__ LocalSmem<T, D> sm;
     __shared__ double s_theta[NP];
+    // s_row and s_base keep pair m = 4 j + e at tab_ix(m) = e (NP / 4) + j: a lane rotates
+    // the pairs 4 j .. 4 j + 3 of a 16-byte chunk, so for each e the 16 lanes of a row
+    // read consecutive entries (distinct banks) instead of entries 4 apart
     __shared__ float2 s_row[32][NP];  // (cos, sin) of b theta_m, b < 32
     __shared__ float2 s_base[2][NP];  // (cos, sin) of a tile's offset times theta_m (double-buffered)
+    auto tab_ix = [](int m) { return (m & 3) * (NP / 4) + (m >> 2); };
     __shared__ float2 s_step[NP];     // (cos, sin) of 32 theta_m: one tile further
     __shared__ float2 s_qbase[4][NP]; // (cos, sin) of 32 a theta_m for the block's 128 query rows
 
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(co
         s_theta[t] = pow((double)lc.rope_base, -2.0 * (double)t / (double)D);
     __syncthreads();
     for (int e = t; e < 32 * NP; e += kThreads)
-        s_row[e / NP][e % NP] = sincos_pair((double)(e / NP) * s_theta[e % NP]);
+        s_row[e / NP][tab_ix(e % NP)] = sincos_pair((double)(e / NP) * s_theta[e % NP]);
     for (int e = t; e < 4 * NP; e += kThreads)
         s_qbase[e / NP][e % NP] = sincos_pair((double)(32 * (e / NP)) * s_theta[e % NP]);
     // tile x starts 32 x tokens after tile 0: its angles are the previous tile's turned by
@@ -137,15 +141,15 @@ __global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(co
     // at most 37 tiles; the long form takes the angles afresh from fp64 every kRun tiles,
     // so the stepped angles never carry more than kRun additions however long the window.
     if (t < NP) {
-        s_base[0][t] = sincos_pair((double)(t_lo - q0) * s_theta[t]);
+        s_base[0][tab_ix(t)] = sincos_pair((double)(t_lo - q0) * s_theta[t]);
         s_step[t] = sincos_pair(32.0 * s_theta[t]);
     }
     auto tile_base = [&](int x, int buf) { // tile x, from tile x - 1 whose angles are in buf ^ 1
         if (t < NP) {
             if (LONG && x % kRun == 0)
-                s_base[buf][t] = sincos_pair((double)(t_lo - q0 + 32 * (int64_t)x) * s_theta[t]);
+                s_base[buf][tab_ix(t)] = sincos_pair((double)(t_lo - q0 + 32 * (int64_t)x) * s_theta[t]);
             else
-                s_base[buf][t] = cs_add(s_base[buf ^ 1][t], s_step[t]);
+                s_base[buf][tab_ix(t)] = cs_add(s_base[buf ^ 1][tab_ix(t)], s_step[t]);
         }
     };
     __syncthreads();
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(co
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = f8 / 2 + e;
-                const float2 cs = cs_add(s_qbase[r >> 5][m], s_row[r & 31][m]);
+                const float2 cs = cs_add(s_qbase[r >> 5][m], s_row[r & 31][tab_ix(m)]);
                 const uint32_t xe = x[e];
                 const float2 y = rotate(bf16_bits_to_f32(xe & 0xffffu), bf16_bits_to_f32(xe >> 16), cs);
                 const uint32_t hp = cvt_pk_bf16(y.x, y.y);
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(co
         const int r = wave * 32 + col;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) { // this lane keeps element 2 kc + half of the rotated pair kc
-            const float2 cs = cs_add(s_qbase[r >> 5][kc], s_row[r & 31][kc]);
+            const float2 cs = cs_add(s_qbase[r >> 5][kc], s_row[r & 31][tab_ix(kc)]);
             const float2 y = q_ok ? rotate(qrow[2 * kc], qrow[2 * kc + 1], cs) : make_float2(0.0f, 0.0f);
             qf[kc] = half ? y.y : y.x;
         }
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(co
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int m = f8 / 2 + e;
-                    const float2 cs = cs_add(s_base[buf][m], s_row[row][m]);
+                    const float2 cs = cs_add(s_base[buf][tab_ix(m)], s_row[row][tab_ix(m)]);
                     const uint32_t xe = pk[u][e];
                     const float2 y = rotate(bf16_bits_to_f32(xe & 0xffffu), bf16_bits_to_f32(xe >> 16), cs);
                     const uint32_t hp = cvt_pk_bf16(y.x, y.y);
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(kThreads, LONG ? 1 : 2) void local_window_kernel(co
                 const int row = e / NP, m = e % NP;
                 const int64_t j = ts + row < N ? ts + row : N - 1;
                 const float2 y = rotate(kc_src[j * D + 2 * m], kc_src[j * D + 2 * m + 1],
-                                        cs_add(s_base[buf][m], s_row[row][m]));
+                                        cs_add(s_base[buf][tab_ix(m)], s_row[row][tab_ix(m)]));
                 sm.k[row][2 * m] = y.x;
                 sm.k[row][2 * m + 1] = y.y;
                 sm.v[row][2 * m] = vc_src[j * D + 2 * m];
