@@ -722,32 +722,43 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                 sm.need_sel = 0;
             __syncthreads();
             int nk = 0;
-            if (half == 0) { // expand this query's internal nodes; leaves keep their slots
-                // the beam is read whole first (slots past nb hold stale refs, never used)
+            { // expand this query's internal nodes, the pair's lanes taking half the beam each
+              // (entries 8 half .. 8 half + 7; the parents in beam order, the second lane's after
+              // the first's); leaves keep their slots.  Slots past nb hold stale refs, never used.
+                constexpr int kHalfBeam = kFsbMaxBeam / 2;
                 const int nbq = sm.nb[qs];
-                int32_t refs[kFsbMaxBeam];
+                int32_t refs[kHalfBeam];
 #pragma unroll
-                for (int e = 0; e < kFsbMaxBeam; ++e)
-                    refs[e] = sm.beam[qs][e];
-                int nleaf = 0;
+                for (int e = 0; e < kHalfBeam; ++e)
+                    refs[e] = sm.beam[qs][kHalfBeam * half + e];
+                bool internal[kHalfBeam];
+                int ni = 0, nl = 0;
 #pragma unroll
-                for (int e = 0; e < kFsbMaxBeam; ++e) {
-                    if (e < nbq) {
-                        const int32_t ref = refs[e];
-                        if (is_leaf(ref)) {
-                            ++nleaf;
-                        } else { // the node is marked; the list takes both its children
-                            sm.kpar[qs][nk >> 1] = ref;
-                            nk += 2;
-                            const int lp = local_of(ref);
-                            atomicOr(&bm[lp >> 5], 1u << (lp & 31));
-                        }
+                for (int e = 0; e < kHalfBeam; ++e) {
+                    const bool here = kHalfBeam * half + e < nbq;
+                    const bool leaf = here && is_leaf(refs[e]);
+                    internal[e] = here && !leaf;
+                    ni += internal[e] ? 1 : 0;
+                    nl += leaf ? 1 : 0;
+                }
+                const int ni_other = __shfl_xor(ni, 32, kWave), nl_other = __shfl_xor(nl, 32, kWave);
+                int pos = half ? ni_other : 0;
+#pragma unroll
+                for (int e = 0; e < kHalfBeam; ++e) {
+                    if (internal[e]) { // the node is marked; the list takes both its children
+                        sm.kpar[qs][pos++] = refs[e];
+                        const int lp = local_of(refs[e]);
+                        atomicOr(&bm[lp >> 5], 1u << (lp & 31));
                     }
                 }
-                sm.nk[qs] = nk;
-                sm.nleaf[qs] = nleaf;
-                if (nk > Wb - nleaf)
-                    sm.need_sel = 1;
+                nk = 2 * (ni + ni_other);
+                const int nleaf = nl + nl_other;
+                if (half == 0) {
+                    sm.nk[qs] = nk;
+                    sm.nleaf[qs] = nleaf;
+                    if (nk > Wb - nleaf)
+                        sm.need_sel = 1;
+                }
             }
             if (!__syncthreads_or(nk > 0))
                 break; // every beam holds only leaves
