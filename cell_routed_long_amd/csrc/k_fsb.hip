@@ -955,26 +955,47 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
                     other[j] = ((uint64_t)hi << 32) | lo;
                 }
                 merge_top_desc<kFsbMaxBeam>(top, other);
-                if (half == 0 && nkq > 0) {
-                    // the old beam and the kept children's parents are read before any write
+                if (nkq > 0) {
+                    // both lanes of the pair hold the same top list; each takes half of the
+                    // old beam (its leaves, at an offset from the partner's count) and half of
+                    // the kept children, which are a prefix of the list (zero keys sort last).
+                    // The old beam and the parents are read before any write.
+                    constexpr int kHalfBeam = kFsbMaxBeam / 2;
                     const int nbq = sm.nb[qs];
-                    int32_t refs[kFsbMaxBeam], par[kFsbMaxBeam];
+                    int32_t refs[kHalfBeam], par[kHalfBeam];
 #pragma unroll
-                    for (int e = 0; e < kFsbMaxBeam; ++e) {
-                        refs[e] = sm.beam[qs][e];
-                        par[e] = sm.kpar[qs][(int)(top[e] & 0xffffu) >> 1]; // in bounds for every key
+                    for (int e = 0; e < kHalfBeam; ++e) {
+                        refs[e] = sm.beam[qs][kHalfBeam * half + e];
+                        // in bounds for every key
+                        par[e] = sm.kpar[qs][(int)(top[kHalfBeam * half + e] & 0xffffu) >> 1];
                     }
-                    int nb2 = 0;
+                    bool leaf[kHalfBeam];
+                    int nl = 0;
+#pragma unroll
+                    for (int e = 0; e < kHalfBeam; ++e) {
+                        leaf[e] = kHalfBeam * half + e < nbq && is_leaf(refs[e]);
+                        nl += leaf[e] ? 1 : 0;
+                    }
+                    const int nl_other = __shfl_xor(nl, 32, kWave);
+                    const int NL = nl + nl_other; // the beam's leaves (sm.nleaf)
+                    int pos = half ? nl_other : 0;
+#pragma unroll
+                    for (int e = 0; e < kHalfBeam; ++e)
+                        if (leaf[e])
+                            sm.beam[qs][pos++] = refs[e];
+                    const int keep = Wb - NL;
+                    int nkept = 0;
 #pragma unroll
                     for (int e = 0; e < kFsbMaxBeam; ++e)
-                        if (e < nbq && is_leaf(refs[e]))
-                            sm.beam[qs][nb2++] = refs[e];
-                    const int keep = Wb - sm.nleaf[qs];
+                        nkept += (e < keep && top[e] != 0ull) ? 1 : 0;
 #pragma unroll
-                    for (int e = 0; e < kFsbMaxBeam; ++e)
-                        if (e < keep && top[e] != 0ull)
-                            sm.beam[qs][nb2++] = child_of(par[e], (int)(top[e] & 1u));
-                    sm.nb[qs] = nb2;
+                    for (int e = 0; e < kHalfBeam; ++e) {
+                        const int ee = kHalfBeam * half + e;
+                        if (ee < nkept)
+                            sm.beam[qs][NL + ee] = child_of(par[e], (int)(top[ee] & 1u));
+                    }
+                    if (half == 0)
+                        sm.nb[qs] = NL + nkept;
                 }
             }
             __syncthreads();
