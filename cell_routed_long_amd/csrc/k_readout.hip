@@ -60,8 +60,13 @@ struct alignas(16) ReadoutSmem<float, D> {
     float v[32][kStride];
 };
 
+// bf16 with K <= 4: three workgroups per CU (168 VGPRs) hide more of each cell's memory
+// latency; otherwise two
 template <typename T, int D, int KT>
-__global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restrict__ q, const T *__restrict__ k,
+constexpr int kReadoutBlocksPerCU = (sizeof(T) == 2 && KT <= 4) ? 3 : 2;
+
+template <typename T, int D, int KT>
+__global__ __launch_bounds__(kThreads, (kReadoutBlocksPerCU<T, D, KT>)) void readout_kernel(const T *__restrict__ q, const T *__restrict__ k,
                                                            const T *__restrict__ v,
                                                            const int32_t *__restrict__ sel,
                                                            const float *__restrict__ gain, T *__restrict__ out,
@@ -273,16 +278,22 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(const T *__restric
             for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 bh, bl;
                 split_bf16x8(&p[8 * kk], bh, bl);
-                bf16x8 av[DT];
+                // two feature tiles at a time (fewer registers live): lo parts of both, then
+                // hi parts, so no product waits on the one just before it
+                constexpr int DP = DT < 2 ? DT : 2;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    av[dt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.vt[dt * 32 + col][16 * kk + 8 * half]));
+                for (int d0 = 0; d0 < DT; d0 += DP) {
+                    bf16x8 av[DP];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) // lo parts of every tile, then hi parts: no back-to-back chain
-                    o_acc[dt] = mfma_bf16(av[dt], bl, o_acc[dt]);
+                    for (int j = 0; j < DP; ++j)
+                        av[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&sm.vt[(d0 + j) * 32 + col][16 * kk + 8 * half]));
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    o_acc[dt] = mfma_bf16(av[dt], bh, o_acc[dt]);
+                    for (int j = 0; j < DP; ++j)
+                        o_acc[d0 + j] = mfma_bf16(av[j], bl, o_acc[d0 + j]);
+#pragma unroll
+                    for (int j = 0; j < DP; ++j)
+                        o_acc[d0 + j] = mfma_bf16(av[j], bh, o_acc[d0 + j]);
+                }
             }
         } else {
 #pragma unroll
