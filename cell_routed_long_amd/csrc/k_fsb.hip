@@ -9,26 +9,30 @@
 //   * fsb_admit_kernel: per head, the second forest's admitted cells in arrival
 //     order and their running count (a_c in fp64, so the admission equals an
 //     fp64 evaluation exactly).
-//   * fsb_build_kernel: one workgroup per aligned chunk of 2^k admitted cells
-//     that starts at an even multiple of 2^k (the only chunks a binary
-//     decomposition of the admitted count uses, App. E.1 "Chunks"), for both
-//     forests of every head.  A chunk never changes once complete, so its tree
-//     is built once and serves every block whose forest holds it.  One wave per
-//     node: fp64 mean, farthest cell, two power iterations (Eq. 19), then the
-//     node's cells are sorted by their projection in LDS (bitonic) and halved;
-//     node summaries (Eq. 20) are written heap-ordered, mean keys as fp32.
-//     The chunks are taken largest first (the longest chains start at once).
+//   * fsb_build_kernel: the aligned chunks of 2^k admitted cells that start at
+//     an even multiple of 2^k (the only chunks a binary decomposition of the
+//     admitted count uses, App. E.1 "Chunks"), for both forests of every head:
+//     a workgroup per chunk of more than sixteen cells, a wave per smaller one.
+//     A chunk never changes once complete, so its tree is built once and
+//     serves every block whose forest holds it.  Per node: fp64 mean, farthest
+//     cell, two power iterations (Eq. 19), then the node's cells are sorted by
+//     their projection in LDS (bitonic) and halved; node summaries (Eq. 20) are
+//     written heap-ordered, mean keys as fp32.  A wave takes a node where a
+//     level has at least as many nodes as waves; above that every wave takes a
+//     slice of a node.  The chunks are taken largest first (the longest chains
+//     start at once).
 //   * fsb_search_kernel: one workgroup per (sequence, head, 128-query block).
 //     It forms the block's join nodes (Eq. 21) from its chunks' roots and runs
-//     the 128 beams level-synchronously: each level the children of every
-//     query's internal beam nodes are collected into one list (an LDS bitmap
-//     over the block's forest nodes dedupes them), scored for all 128 queries
+//     the 128 beams level-synchronously: each level every query's internal
+//     beam nodes are marked in an LDS bitmap over the block's forest nodes and
+//     their children collected into one list, scored for all 128 queries
 //     32 nodes at a time on the matrix cores (the q . mu term of Eq. 11: bf16
 //     queries against each fp32 mean's bf16 hi + mid + lo parts, fp32 queries
 //     on the fp32 products), and each query keeps its leaves plus its best
 //     W^b - #leaves children (a bitonic sort and merge over the query's lane
-//     pair).  The level's node list is dynamic LDS sized by the forest, so a
-//     bf16 search fits two workgroups on a CU at moderate lengths.
+//     pair); a level where every query keeps all its children skips the
+//     priorities.  The level's node list is dynamic LDS sized by the forest, so
+//     a bf16 search fits two workgroups on a CU at moderate lengths.
 //     The union of the leaves reached is then reranked cell by cell: a cell's
 //     32 token keys are staged once and the logits of all 128 queries come
 //     from the matrix cores; each query that has the cell as a candidate takes
