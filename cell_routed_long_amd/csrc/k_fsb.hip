@@ -570,7 +570,9 @@ __global__ __launch_bounds__(kThreads, kSearchWavesPerSimd<T>) void fsb_search_k
     int32_t *const wb = reinterpret_cast<int32_t *>(dyn + nw); // prefix counts of bm
     uint16_t *const list = reinterpret_cast<uint16_t *>(dyn + 2 * nw); // the level's nodes, or the candidates' cells
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int beta = (int)(lb % (uint32_t)NB);
+    // a head's blocks from the last: later blocks search larger forests, so the longest start
+    // first and the kernel ends on short ones
+    const int beta = NB - 1 - (int)(lb % (uint32_t)NB);
     const int64_t bh = (int64_t)(lb / (uint32_t)NB);
     const int h = (int)(bh % H);
     const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1), half = lane >> 5, col = lane & 31;
