@@ -84,7 +84,9 @@ __global__ __launch_bounds__(kThreads, (kFusedBlocksPerCU<D, KT>)) void route_re
     constexpr int SCH = PER / 8; // 16-byte chunks per part and thread
     constexpr int KC = D / 16;  // k-steps of the bf16 matrix products
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int beta = (int)(lb % (uint32_t)NB);
+    // a head's blocks from the last: without pruning (FS) a later block scores more cells,
+    // so the longest start first and the kernel ends on short ones
+    const int beta = NB - 1 - (int)(lb % (uint32_t)NB);
     const int64_t head = (int64_t)(lb / (uint32_t)NB);
     const int h = (int)(head % H);
     const int t = threadIdx.x;
